@@ -1,0 +1,155 @@
+/*
+ * tm.h -- C ABI of the Titans neural long-term memory on MI355X (gfx950).
+ *
+ * The memory M is a small MLP without biases (depth weight matrices, SiLU
+ * between them) whose weights are written at test time.  Sources: the pages
+ * on Titans; "Titans, explained" (vibeengines.com) method steps 1-6 and its
+ * extremes paragraph; "Attack of the Titans" (synthesis.ai), Technical
+ * Details / Parallel training; the titans-pytorch analysis (hysenlabs.com),
+ * section "NeuralMemory as a standalone module".
+ *
+ *   store   : per chunk of b tokens, every token's surprise (the gradient of
+ *             ||M(k_t) - v_t||^2 w.r.t. the weights, taken at the weights the
+ *             chunk started with) goes into the momentum
+ *             S_t = eta_t S_{t-1} - theta_t grad, then M_t = (1 - alpha_t) M_{t-1} + S_t.
+ *   retrieve: y = M(q), a forward pass that writes nothing.
+ *   forward : store and retrieve together; the queries of chunk c are read
+ *             through the weights after chunk c has been written.  This is the
+ *             (retrieved, mem_state) call of NeuralMemory.
+ *
+ * Conventions shared by every call
+ *   - All buffers are device memory allocated by the caller; the library
+ *     never allocates device memory.  Every call is asynchronous on `stream`
+ *     (a hipStream_t; NULL is the null stream) unless stated otherwise.
+ *   - Streams of memory: s = batch_index * heads + head; every stream owns an
+ *     independent memory (one copy per sequence and head).
+ *   - Token arrays k, v, q, y: [batch][n_tokens][heads][dim], contiguous,
+ *     16-byte aligned.  k, v, q are bf16 (TM_BF16) or fp32 (TM_F32); y is fp32.
+ *   - Gates theta, eta, alpha: [batch][n_tokens][heads] fp32, 4-byte aligned,
+ *     values in [0, 1].
+ *   - Weights: row-vector convention y = x W; W_l is [d_in][d_out] row-major.
+ *     Layer widths: dim -> hidden -> ... -> hidden -> dim with
+ *     hidden = dim * expansion (depth 1: one dim x dim matrix).  P is the
+ *     total weight count per stream.
+ *   - Precision: TM_BF16 rounds weights, activations and theta-scaled deltas
+ *     to bf16 for the matrix cores and accumulates in fp32; TM_F32 runs the
+ *     same steps with fp32 operands.  M and S are always kept in fp32.
+ *   - Errors: every function returns a tm_status and never throws.  All
+ *     argument checks run on the host before anything is launched, so a call
+ *     that returns an error has not touched the state.  Non-finite values are
+ *     not call errors: they set a sticky flag read by tm_state_check.
+ *   - A state blob may be used by one stream at a time; a ctx is immutable
+ *     and may be shared between threads.
+ */
+#ifndef TM_H
+#define TM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TM_OK = 0,
+    TM_ERR_INVALID = -1,  /* null/misaligned pointer, non-positive or unsupported size */
+    TM_ERR_SHAPE = -2,    /* n_tokens not a multiple of the chunk size */
+    TM_ERR_DTYPE = -3,    /* unknown tm_dtype */
+    TM_ERR_STATE = -4,    /* state header does not match the ctx / batch / heads */
+    TM_ERR_HIP = -5       /* a HIP runtime call or launch failed */
+} tm_status;
+
+typedef enum { TM_F32 = 0, TM_BF16 = 1 } tm_dtype;
+
+typedef struct tm_ctx tm_ctx;
+
+/* Memory configuration.  dim: per-head width, a multiple of 32 (>= 32);
+ * depth: number of weight matrices, 1..8; expansion: hidden = dim*expansion
+ * (>= 1, ignored for depth 1); chunk: tokens per mini-batch b, 1..64 ("Titans,
+ * explained" step 6: within a chunk every gradient is taken at the chunk-start
+ * weights).  On success *out owns a ctx to release with tm_destroy. */
+tm_status tm_create(int dim, int depth, int expansion, int chunk, tm_ctx** out);
+void tm_destroy(tm_ctx* ctx);
+
+/* Weights per stream (P). */
+size_t tm_param_count(const tm_ctx* ctx);
+
+/* Size in bytes of the opaque state blob for batch*heads streams (fp32 M and
+ * S, a bf16 copy of M for the matrix cores, and a header).  0 on bad args. */
+size_t tm_state_bytes(const tm_ctx* ctx, int batch, int heads);
+
+/* Scratch bytes tm_store / tm_retrieve / tm_forward need for a call of
+ * n_tokens tokens per stream.  The workspace holds no data between calls. */
+size_t tm_workspace_bytes(const tm_ctx* ctx, int batch, int heads, int n_tokens);
+
+/* M = init_weights (device fp32 [heads][P], canonical layer order, broadcast
+ * over the batch), S = 0, position = 0, flag cleared.  state: 256-byte
+ * aligned, tm_state_bytes(ctx, batch, heads) bytes. */
+tm_status tm_state_init(const tm_ctx* ctx, void* state, int batch, int heads,
+                        const float* init_weights, void* stream);
+
+/* Store n_tokens tokens per stream ("Titans, explained" steps 2-4 in the
+ * chunked form of step 6).  n_tokens must be a multiple of the chunk
+ * (TM_ERR_SHAPE otherwise); chunk boundaries are counted from the start of
+ * every call, so calls must stay chunk-aligned.  n_tokens == 0 is a no-op. */
+tm_status tm_store(const tm_ctx* ctx, void* state, const void* k, const void* v,
+                   const float* theta, const float* eta, const float* alpha,
+                   int batch, int heads, int n_tokens, tm_dtype dtype,
+                   void* workspace, void* stream);
+
+/* y = M(q) for every query through the current weights (step 5).  The state
+ * is not written.  Any n_tokens >= 0. */
+tm_status tm_retrieve(const tm_ctx* ctx, const void* state, const void* q, float* y,
+                      int batch, int heads, int n_tokens, tm_dtype dtype,
+                      void* workspace, void* stream);
+
+/* Store and retrieve: for each chunk c, store chunk c, then read chunk c's
+ * queries through the written memory.  Equivalent to alternating tm_store and
+ * tm_retrieve chunk by chunk. */
+tm_status tm_forward(const tm_ctx* ctx, void* state, const void* k, const void* v,
+                     const void* q, const float* theta, const float* eta,
+                     const float* alpha, float* y, int batch, int heads,
+                     int n_tokens, tm_dtype dtype, void* workspace, void* stream);
+
+/* Canonical fp32 copy of the state: dst is [batch*heads][2P], per stream
+ * M_1..M_L then S_1..S_L, each W_l row-major [d_in][d_out]. */
+tm_status tm_state_export(const tm_ctx* ctx, const void* state, int batch, int heads,
+                          float* dst, void* stream);
+
+/* Inverse of tm_state_export (rebuilds the bf16 copy, position = 0, flag
+ * cleared). */
+tm_status tm_state_import(const tm_ctx* ctx, void* state, int batch, int heads,
+                          const float* src, void* stream);
+
+/* Synchronous: waits for `stream`, then checks the state header against the
+ * ctx, batch and heads (TM_ERR_STATE on mismatch) and reports the sticky
+ * non-finite flag and the number of tokens stored since init/import. */
+tm_status tm_state_check(const tm_ctx* ctx, const void* state, int batch, int heads,
+                         int* nonfinite, long long* position, void* stream);
+
+const char* tm_status_str(tm_status status);
+
+/* Graph replay (on by default, process-wide).  A tm_state_init / tm_store /
+ * tm_retrieve / tm_forward call whose device, pointers and sizes repeat an
+ * earlier call's is captured once into a HIP graph (on a private stream of
+ * the ctx) and from then on replayed on the caller's stream, which removes
+ * most of the per-kernel launch cost of the chunk loop.  Each ctx keeps its
+ * 16 most recent call shapes.  on = 0 launches every call directly. */
+tm_status tm_graphs_enable(int on);
+
+/* Instrumentation for measuring kernels in place (not part of the method).
+ * Kernel classes: 0 coefficient scan, 1 chunk forward product, 2 chunk
+ * backward product, 3 gradient reduction + state update.  While bit c of
+ * class_mask is set, every launch of class c is bracketed by a pair of HIP
+ * events recorded on its launch stream (mask 0 turns timing off).
+ * tm_timing_read waits for the recorded launches and returns, for one class,
+ * the summed duration in milliseconds and the number of launches since its
+ * last read, then forgets them.  Process-wide. */
+tm_status tm_timing_enable(int class_mask);
+tm_status tm_timing_read(int kernel_class, double* total_ms, long long* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TM_H */

@@ -1,0 +1,276 @@
+"""Titans neural long-term memory on MI355X: Python binding of ``libtm.so``.
+
+Argument marshalling only: every step of the store / retrieve path runs in
+the HIP kernels behind the C ABI declared in ``include/tm.h``.  PyTorch
+supplies device memory (tensors) and the HIP stream.  The functions carry the
+C names; batch, heads and n_tokens are read off the [batch][n_tokens][heads]
+[dim] token tensors, and the dtype off their element type (bfloat16 or
+float32).  ``NeuralMemory`` wraps them into the pages' call
+``retrieved, mem_state = memory(...)``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtm.so")
+
+TM_OK, TM_ERR_INVALID, TM_ERR_SHAPE, TM_ERR_DTYPE, TM_ERR_STATE, TM_ERR_HIP = 0, -1, -2, -3, -4, -5
+TM_F32, TM_BF16 = 0, 1
+
+EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_workspace_bytes",
+            "tm_state_init", "tm_store", "tm_retrieve", "tm_forward", "tm_state_export",
+            "tm_state_import", "tm_state_check", "tm_status_str", "tm_timing_enable", "tm_timing_read",
+            "tm_graphs_enable")
+
+# kernel classes of tm_timing_enable / tm_timing_read
+K_SCAN, K_FWD, K_BWD, K_UPDATE = 0, 1, 2, 3
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+
+class TMError(RuntimeError):
+    def __init__(self, fn, code):
+        msg = lib().tm_status_str(code).decode() if _lib is not None else str(code)
+        super().__init__("%s failed: %s (%d)" % (fn, msg, code))
+        self.code = code
+
+
+def lib():
+    """Load libtm.so.  Raises if it has not been built: there is no other
+    implementation to fall back to."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libtm.so is not built (run __graft_entry__.build() or "
+                              "python -m test_trained_neural_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.tm_create.restype = _i
+        L.tm_create.argtypes = [_i, _i, _i, _i, ctypes.POINTER(_vp)]
+        L.tm_destroy.restype = None
+        L.tm_destroy.argtypes = [_vp]
+        L.tm_param_count.restype = ctypes.c_size_t
+        L.tm_param_count.argtypes = [_vp]
+        L.tm_state_bytes.restype = ctypes.c_size_t
+        L.tm_state_bytes.argtypes = [_vp, _i, _i]
+        L.tm_workspace_bytes.restype = ctypes.c_size_t
+        L.tm_workspace_bytes.argtypes = [_vp, _i, _i, _i]
+        L.tm_state_init.restype = _i
+        L.tm_state_init.argtypes = [_vp, _vp, _i, _i, _vp, _vp]
+        L.tm_store.restype = _i
+        L.tm_store.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
+        L.tm_retrieve.restype = _i
+        L.tm_retrieve.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
+        L.tm_forward.restype = _i
+        L.tm_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
+        L.tm_state_export.restype = _i
+        L.tm_state_export.argtypes = [_vp, _vp, _i, _i, _vp, _vp]
+        L.tm_state_import.restype = _i
+        L.tm_state_import.argtypes = [_vp, _vp, _i, _i, _vp, _vp]
+        L.tm_state_check.restype = _i
+        L.tm_state_check.argtypes = [_vp, _vp, _i, _i, ctypes.POINTER(_i),
+                                     ctypes.POINTER(ctypes.c_longlong), _vp]
+        L.tm_timing_enable.restype = _i
+        L.tm_timing_enable.argtypes = [_i]
+        L.tm_timing_read.restype = _i
+        L.tm_timing_read.argtypes = [_i, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong)]
+        L.tm_graphs_enable.restype = _i
+        L.tm_graphs_enable.argtypes = [_i]
+        L.tm_status_str.restype = ctypes.c_char_p
+        L.tm_status_str.argtypes = [_i]
+        _lib = L
+    return _lib
+
+
+def _check(fn, rc):
+    if rc != TM_OK:
+        raise TMError(fn, rc)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _vp(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return TM_BF16
+    if t.dtype == torch.float32:
+        return TM_F32
+    raise TypeError("token tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _tok(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("token and gate tensors must be contiguous device tensors")
+
+
+# ---------------------------------------------------------------------------
+# the C calls, one to one
+
+def tm_create(dim, depth, expansion, chunk):
+    h = _vp()
+    _check("tm_create", lib().tm_create(dim, depth, expansion, chunk, ctypes.byref(h)))
+    return h
+
+
+def tm_destroy(ctx):
+    lib().tm_destroy(ctx)
+
+
+def tm_param_count(ctx):
+    return lib().tm_param_count(ctx)
+
+
+def tm_state_bytes(ctx, batch, heads):
+    return lib().tm_state_bytes(ctx, batch, heads)
+
+
+def tm_workspace_bytes(ctx, batch, heads, n_tokens):
+    return lib().tm_workspace_bytes(ctx, batch, heads, n_tokens)
+
+
+def tm_state_init(ctx, state, batch, heads, init_weights, stream=None):
+    _tok(init_weights)
+    assert init_weights.dtype == torch.float32
+    _check("tm_state_init", lib().tm_state_init(ctx, _ptr(state), batch, heads, _ptr(init_weights),
+                                                _stream(stream)))
+
+
+def tm_store(ctx, state, k, v, theta, eta, alpha, workspace, stream=None):
+    _tok(k, v, theta, eta, alpha)
+    B, T, H, _ = k.shape
+    _check("tm_store", lib().tm_store(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta),
+                                      _ptr(alpha), B, H, T, _dtype_code(k), _ptr(workspace),
+                                      _stream(stream)))
+
+
+def tm_retrieve(ctx, state, q, y, workspace, stream=None):
+    _tok(q, y)
+    B, T, H, _ = q.shape
+    _check("tm_retrieve", lib().tm_retrieve(ctx, _ptr(state), _ptr(q), _ptr(y), B, H, T,
+                                            _dtype_code(q), _ptr(workspace), _stream(stream)))
+
+
+def tm_forward(ctx, state, k, v, q, theta, eta, alpha, y, workspace, stream=None):
+    _tok(k, v, q, theta, eta, alpha, y)
+    B, T, H, _ = k.shape
+    _check("tm_forward", lib().tm_forward(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(q), _ptr(theta),
+                                          _ptr(eta), _ptr(alpha), _ptr(y), B, H, T, _dtype_code(k),
+                                          _ptr(workspace), _stream(stream)))
+
+
+def tm_state_export(ctx, state, batch, heads, dst, stream=None):
+    _check("tm_state_export", lib().tm_state_export(ctx, _ptr(state), batch, heads, _ptr(dst),
+                                                    _stream(stream)))
+
+
+def tm_state_import(ctx, state, batch, heads, src, stream=None):
+    _check("tm_state_import", lib().tm_state_import(ctx, _ptr(state), batch, heads, _ptr(src),
+                                                    _stream(stream)))
+
+
+def tm_state_check(ctx, state, batch, heads, stream=None):
+    nf = _i(0)
+    pos = ctypes.c_longlong(0)
+    _check("tm_state_check", lib().tm_state_check(ctx, _ptr(state), batch, heads, ctypes.byref(nf),
+                                                  ctypes.byref(pos), _stream(stream)))
+    return bool(nf.value), int(pos.value)
+
+
+def tm_graphs_enable(on):
+    _check("tm_graphs_enable", lib().tm_graphs_enable(1 if on else 0))
+
+
+def tm_timing_enable(class_mask):
+    _check("tm_timing_enable", lib().tm_timing_enable(class_mask))
+
+
+def tm_timing_read(kernel_class):
+    """(summed milliseconds, launches) of one kernel class since its last read."""
+    ms = ctypes.c_double(0)
+    n = ctypes.c_longlong(0)
+    _check("tm_timing_read", lib().tm_timing_read(kernel_class, ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)
+
+
+# ---------------------------------------------------------------------------
+# convenience wrapper: retrieved, mem_state = memory(...)
+
+class MemState:
+    """Opaque memory state of batch*heads streams (device bytes)."""
+
+    def __init__(self, mem, batch, heads, device):
+        self.batch, self.heads = batch, heads
+        self.buf = torch.empty(tm_state_bytes(mem.ctx, batch, heads), dtype=torch.uint8, device=device)
+
+
+class NeuralMemory:
+    def __init__(self, dim, depth=2, expansion=4, chunk=64, device="cuda"):
+        self.dim, self.depth, self.expansion, self.chunk = dim, depth, expansion, chunk
+        self.device = torch.device(device)
+        self.ctx = tm_create(dim, depth, expansion, chunk)
+        self.params = tm_param_count(self.ctx)
+        self._ws = None
+
+    def __del__(self):
+        try:
+            if self.ctx is not None and _lib is not None:
+                tm_destroy(self.ctx)
+        except Exception:
+            pass
+
+    def workspace(self, batch, heads, n_tokens):
+        need = tm_workspace_bytes(self.ctx, batch, heads, n_tokens)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def init_state(self, batch, heads, init_weights):
+        st = MemState(self, batch, heads, self.device)
+        w = init_weights.to(self.device, torch.float32).contiguous()
+        assert w.numel() == heads * self.params
+        tm_state_init(self.ctx, st.buf, batch, heads, w)
+        return st
+
+    def store(self, state, k, v, theta, eta, alpha):
+        B, T, H, _ = k.shape
+        tm_store(self.ctx, state.buf, k, v, theta, eta, alpha, self.workspace(B, H, T))
+        return state
+
+    def retrieve(self, state, q):
+        B, T, H, d = q.shape
+        y = torch.empty((B, T, H, d), dtype=torch.float32, device=self.device)
+        tm_retrieve(self.ctx, state.buf, q, y, self.workspace(B, H, T))
+        return y
+
+    def __call__(self, state, k, v, q, theta, eta, alpha):
+        B, T, H, d = k.shape
+        y = torch.empty((B, T, H, d), dtype=torch.float32, device=self.device)
+        tm_forward(self.ctx, state.buf, k, v, q, theta, eta, alpha, y, self.workspace(B, H, T))
+        return y, state
+
+    def export(self, state):
+        out = torch.empty((state.batch * state.heads, 2 * self.params), dtype=torch.float32,
+                          device=self.device)
+        tm_state_export(self.ctx, state.buf, state.batch, state.heads, out)
+        return out
+
+    def import_(self, state, src):
+        tm_state_import(self.ctx, state.buf, state.batch, state.heads, src.contiguous())
+        return state
+
+    def check(self, state):
+        return tm_state_check(self.ctx, state.buf, state.batch, state.heads)

@@ -1,0 +1,730 @@
+// C-ABI runtime of the neural-memory library: argument checks, the state
+// and workspace layouts, and the per-call launch sequence (the chunk loop).
+//
+// State blob: [header 256 B][M fp32 ns*P][S fp32 ns*P][Wt bf16 ns*P], each
+// region 256-byte aligned; per stream the layers follow each other, W_l is
+// row-major [d_in][d_out] in M and S and transposed ([d_out][d_in]) in Wt.
+#include <mutex>
+#include <new>
+#include <string.h>
+#include <vector>
+
+#include "../../include/tm.h"
+#include "tm_internal.h"
+
+using namespace tmk;
+
+// A call's launch sequence replayed as a HIP graph: keyed by everything the
+// kernels' arguments depend on (device, every pointer and every size).
+struct GraphEntry {
+    int dev, kind, batch, heads, n_tokens, dtype;
+    const void* p[10];
+    int seen;                    // sightings before capture
+    hipGraphExec_t exec;
+    unsigned long long last;     // LRU stamp
+};
+
+struct tm_ctx {
+    std::mutex* gmu;
+    std::vector<GraphEntry>* graphs;
+    std::vector<std::pair<int, hipStream_t>>* capture_streams;
+    unsigned long long stamp;
+    int dim, depth, expansion, chunk, hidden, L;
+    int din[MAXL], dout[MAXL];
+    long off[MAXL + 1];
+    long P;
+    int tj[MAXL];
+    int tbase[MAXL + 1];
+    uint64_t hash;
+};
+
+namespace {
+
+constexpr long RET_ROWS = 2048;   // query rows per stream per retrieve pass
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct StateLayout {
+    size_t M, S, Wt, total;
+};
+
+StateLayout state_layout(const tm_ctx* c, long ns) {
+    StateLayout s;
+    s.M = sizeof(StateHeader);
+    s.S = s.M + al256((size_t)ns * c->P * 4);
+    s.Wt = s.S + al256((size_t)ns * c->P * 4);
+    s.total = s.Wt + al256((size_t)ns * c->P * 2);
+    return s;
+}
+
+struct WsLayout {
+    size_t cc, dc, cs, act[MAXL], dsl[MAXL], dlt[MAXL], ret[2], total;
+    long coef_ss, cs_ss, act_ss, dsl_ss, dlt_ss[MAXL], ret_ss, ret_rows;
+};
+
+WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
+    WsLayout w;
+    memset(&w, 0, sizeof(w));
+    const long b = c->chunk, C = (T + b - 1) / b, h = c->hidden;
+    size_t o = 0;
+    w.coef_ss = T;
+    w.cc = o; o += al256((size_t)ns * T * 4);
+    w.dc = o; o += al256((size_t)ns * T * 4);
+    w.cs_ss = C * 4;
+    w.cs = o; o += al256((size_t)ns * C * 16);
+    w.act_ss = 2 * b * h;
+    w.dsl_ss = b * h;
+    for (int l = 0; l + 1 < c->L; ++l) {
+        w.act[l] = o; o += al256((size_t)ns * w.act_ss * 4);
+        w.dsl[l] = o; o += al256((size_t)ns * w.dsl_ss * 4);
+    }
+    for (int l = 0; l < c->L; ++l) {
+        w.dlt_ss[l] = b * c->dout[l];
+        w.dlt[l] = o; o += al256((size_t)ns * w.dlt_ss[l] * 4);
+    }
+    size_t fwd_total = o;
+    w.ret_rows = T < RET_ROWS ? T : RET_ROWS;
+    w.ret_ss = w.ret_rows * h;
+    size_t r = 0;
+    if (c->L > 1) {
+        w.ret[0] = r; r += al256((size_t)ns * w.ret_ss * 4);
+        w.ret[1] = r; r += al256((size_t)ns * w.ret_ss * 4);
+    }
+    w.total = fwd_total > r ? fwd_total : r;
+    if (w.total == 0) w.total = 256;
+    return w;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+uint64_t fnv(uint64_t h, uint64_t x) {
+    for (int i = 0; i < 8; ++i) { h ^= (x >> (8 * i)) & 0xff; h *= 1099511628211ull; }
+    return h;
+}
+
+tm_status hip_status(hipError_t e) { return e == hipSuccess ? TM_OK : TM_ERR_HIP; }
+
+// ---- optional per-launch timing (tm_timing_enable / tm_timing_read) ----
+enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_UPD = 3, K_CLASSES = 4 };
+struct Timed {
+    hipEvent_t a, b;
+    int kind;
+};
+std::mutex g_tmu;
+int g_timing = 0;   // bit mask of timed kernel classes
+std::vector<Timed> g_pending;
+std::vector<hipEvent_t> g_pool;
+double g_ms[K_CLASSES];
+long long g_n[K_CLASSES];
+
+hipEvent_t pool_get() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class F>
+hipError_t timed(int kind, hipStream_t st, F&& launch) {
+    bool on;
+    {
+        std::lock_guard<std::mutex> g(g_tmu);
+        on = (g_timing >> kind) & 1;
+    }
+    if (!on) return launch();
+    hipEvent_t a, b;
+    {
+        std::lock_guard<std::mutex> g(g_tmu);
+        a = pool_get();
+        b = pool_get();
+    }
+    if (!a || !b) return hipErrorOutOfMemory;
+    hipError_t e = hipEventRecord(a, st);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(b, st);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> g(g_tmu);
+    g_pending.push_back(Timed{a, b, kind});
+    return hipSuccess;
+}
+
+// ---- graph replay of repeated calls ----
+bool g_graphs = true;
+constexpr size_t MAX_GRAPHS = 16;
+
+// Runs `launch(stream)`.  A call whose key has been seen before is captured
+// once into a graph on a private stream and from then on replayed on the
+// caller's stream; first sightings and timed runs launch directly.
+template <class F>
+tm_status with_graph(const tm_ctx* cc, GraphEntry key, hipStream_t st, F&& launch) {
+    tm_ctx* c = const_cast<tm_ctx*>(cc);
+    bool timing;
+    {
+        std::lock_guard<std::mutex> g(g_tmu);
+        timing = g_timing != 0;
+    }
+    if (!g_graphs || timing) return launch(st);
+    if (hipGetDevice(&key.dev) != hipSuccess) return TM_ERR_HIP;
+    std::unique_lock<std::mutex> lk(*c->gmu);
+    GraphEntry* hit = nullptr;
+    for (GraphEntry& e : *c->graphs) {
+        if (e.dev == key.dev && e.kind == key.kind && e.batch == key.batch && e.heads == key.heads &&
+            e.n_tokens == key.n_tokens && e.dtype == key.dtype && memcmp(e.p, key.p, sizeof(key.p)) == 0) {
+            hit = &e;
+            break;
+        }
+    }
+    if (!hit) {
+        if (c->graphs->size() >= MAX_GRAPHS) {
+            size_t lru = 0;
+            for (size_t i = 1; i < c->graphs->size(); ++i)
+                if ((*c->graphs)[i].last < (*c->graphs)[lru].last) lru = i;
+            if ((*c->graphs)[lru].exec) (void)hipGraphExecDestroy((*c->graphs)[lru].exec);
+            c->graphs->erase(c->graphs->begin() + lru);
+        }
+        key.seen = 1;
+        key.exec = nullptr;
+        key.last = ++c->stamp;
+        c->graphs->push_back(key);
+        lk.unlock();
+        return launch(st);
+    }
+    hit->last = ++c->stamp;
+    if (!hit->exec) {
+        hipStream_t cs = nullptr;
+        for (auto& pr : *c->capture_streams)
+            if (pr.first == key.dev) cs = pr.second;
+        if (!cs) {
+            if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return TM_ERR_HIP;
+            c->capture_streams->push_back({key.dev, cs});
+        }
+        hipGraph_t graph = nullptr;
+        if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) return TM_ERR_HIP;
+        tm_status rc = launch(cs);
+        hipError_t e = hipStreamEndCapture(cs, &graph);
+        if (rc != TM_OK || e != hipSuccess) {
+            if (graph) (void)hipGraphDestroy(graph);
+            return rc != TM_OK ? rc : TM_ERR_HIP;
+        }
+        hipGraphExec_t exec = nullptr;
+        e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(graph);
+        if (e != hipSuccess) return TM_ERR_HIP;
+        hit->exec = exec;
+    }
+    return hipGraphLaunch(hit->exec, st) == hipSuccess ? TM_OK : TM_ERR_HIP;
+}
+
+GraphEntry make_key(int kind, int batch, int heads, int n_tokens, int dtype,
+                    std::initializer_list<const void*> ptrs) {
+    GraphEntry k;
+    memset(&k, 0, sizeof(k));
+    k.kind = kind;
+    k.batch = batch;
+    k.heads = heads;
+    k.n_tokens = n_tokens;
+    k.dtype = dtype;
+    int i = 0;
+    for (const void* p : ptrs) k.p[i++] = p;
+    return k;
+}
+
+// Layer / tile fields shared by the update and the bf16-copy kernels.
+UpdArgs base_upd(const tm_ctx* c, char* state, long ns) {
+    UpdArgs u;
+    memset(&u, 0, sizeof(u));
+    StateLayout sl = state_layout(c, ns);
+    u.L = c->L;
+    u.b = c->chunk;
+    for (int l = 0; l < c->L; ++l) {
+        u.din[l] = c->din[l];
+        u.dout[l] = c->dout[l];
+        u.off[l] = c->off[l];
+        u.tj[l] = c->tj[l];
+    }
+    for (int l = 0; l <= c->L; ++l) u.tbase[l] = c->tbase[l];
+    u.P = c->P;
+    u.M = reinterpret_cast<float*>(state + sl.M);
+    u.S = reinterpret_cast<float*>(state + sl.S);
+    u.Wt = state + sl.Wt;
+    u.flag = &reinterpret_cast<StateHeader*>(state)->nonfinite;
+    return u;
+}
+
+tm_status check_common(const tm_ctx* c, const void* state, int batch, int heads, int n_tokens,
+                       tm_dtype dtype, const void* ws) {
+    if (!c || !state || !ws) return TM_ERR_INVALID;
+    if (batch <= 0 || heads <= 0 || n_tokens < 0) return TM_ERR_INVALID;
+    if ((long)batch * heads > 65535) return TM_ERR_INVALID;   // grid.y / grid.z limit
+    if (dtype != TM_F32 && dtype != TM_BF16) return TM_ERR_DTYPE;
+    if (!aligned(state, 256) || !aligned(ws, 256)) return TM_ERR_INVALID;
+    return TM_OK;
+}
+
+bool tok_ok(const void* p) { return p && aligned(p, 16); }
+bool gate_ok(const void* p) { return p && aligned(p, 4); }
+
+// Forward of `rows` rows (q rows first, then k rows) of one chunk step, or of
+// a retrieve pass, through every layer at the current weights.
+struct FwdRows {
+    int nq, nk;        // q rows, k rows
+    const void* q;     // q token array (input layout) or nullptr
+    int tq;            // first q token
+    const void* k;
+    int tk;
+    const void* v;
+    float* y;
+};
+
+tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayout& w, char* ws,
+                             const TokLayout& tl, const FwdRows& fr, bool f32, bool retrieve,
+                             hipStream_t st) {
+    StateLayout sl = state_layout(c, ns);
+    const int rows = fr.nq + fr.nk;
+    if (rows == 0) return TM_OK;
+    const int esz = f32 ? 4 : 2;
+    for (int l = 0; l < c->L; ++l) {
+        GemmArgs g;
+        memset(&g, 0, sizeof(g));
+        g.nrows = rows;
+        g.N = c->dout[l];
+        g.K = c->din[l];
+        g.tl = tl;
+        g.n0 = fr.nq;
+        if (l == 0) {
+            g.amode = 0;
+            g.a0 = fr.q;
+            g.at0 = fr.tq;
+            g.a1 = fr.k;
+            g.at1 = fr.tk;
+        } else {
+            g.amode = 1;
+            if (retrieve) {
+                g.a0 = ws + w.ret[(l - 1) & 1];
+                g.a_ss = w.ret_ss;
+            } else {
+                g.a0 = ws + w.act[l - 1];
+                g.a_ss = w.act_ss;
+            }
+            g.a_ld = c->hidden;
+        }
+        if (f32) {
+            g.b = state + sl.M + (size_t)c->off[l] * 4;
+            g.b_ss = c->P;
+            g.b_ldn = 1;
+            g.b_ldk = c->dout[l];
+        } else {
+            g.b = state + sl.Wt + (size_t)c->off[l] * 2;
+            g.b_ss = c->P;
+            g.b_ldn = c->din[l];
+            g.b_ldk = 1;
+        }
+        if (l + 1 < c->L) {
+            g.epi = EPI_HIDDEN;
+            if (retrieve) {
+                g.act = ws + w.ret[l & 1];
+                g.act_ss = w.ret_ss;
+                // retrieve rows are all q rows: no SiLU' is stored
+                g.dsl = nullptr;
+            } else {
+                g.act = ws + w.act[l];
+                g.act_ss = w.act_ss;
+                g.dsl = reinterpret_cast<float*>(ws + w.dsl[l]);
+                g.dsl_ss = w.dsl_ss;
+                g.dsl_ld = c->hidden;
+            }
+            g.act_ld = c->hidden;
+        } else {
+            g.epi = EPI_OUT;
+            g.y = fr.y;
+            g.yt0 = fr.tq;
+            g.v = fr.v;
+            g.vt0 = fr.tk;
+            if (!retrieve) {
+                g.dlt = reinterpret_cast<float*>(ws + w.dlt[l]);
+                g.dlt_ss = w.dlt_ss[l];
+                g.dlt_ld = c->dout[l];
+            }
+        }
+        (void)esz;
+        hipError_t e = timed(K_FWD, st, [&] { return launch_fwd(g, (int)ns, f32 ? 1 : 0, st); });
+        if (e != hipSuccess) return TM_ERR_HIP;
+    }
+    return TM_OK;
+}
+
+// One chunk: forward (with the previous chunk's queries), backward, update.
+tm_status run_chunk(const tm_ctx* c, char* state, long ns, const WsLayout& w, char* ws,
+                    const TokLayout& tl, const void* k, const void* v, const void* q, float* y,
+                    int chunk_idx, bool f32, hipStream_t st) {
+    const int b = c->chunk;
+    StateLayout sl = state_layout(c, ns);
+    FwdRows fr;
+    fr.nq = (q && chunk_idx > 0) ? b : 0;
+    fr.q = q;
+    fr.tq = (chunk_idx - 1) * b;
+    fr.nk = b;
+    fr.k = k;
+    fr.tk = chunk_idx * b;
+    fr.v = v;
+    fr.y = y;
+    tm_status rc = run_forward_layers(c, state, ns, w, ws, tl, fr, f32, false, st);
+    if (rc != TM_OK) return rc;
+    // backward: delta_{l-1} = (delta_l W_l^T) * SiLU'(z_{l-1})
+    for (int l = c->L - 1; l >= 1; --l) {
+        GemmArgs g;
+        memset(&g, 0, sizeof(g));
+        g.nrows = b;
+        g.N = c->din[l];
+        g.K = c->dout[l];
+        g.tl = tl;
+        g.amode = 1;
+        g.a0 = ws + w.dlt[l];
+        g.a_ss = w.dlt_ss[l];
+        g.a_ld = c->dout[l];
+        g.n0 = b;
+        g.b = state + sl.M + (size_t)c->off[l] * 4;
+        g.b_ss = c->P;
+        g.b_ldn = c->dout[l];
+        g.b_ldk = 1;
+        g.epi = EPI_BWD;
+        g.dsl = reinterpret_cast<float*>(ws + w.dsl[l - 1]);
+        g.dsl_ss = w.dsl_ss;
+        g.dsl_ld = c->hidden;
+        g.dlt = reinterpret_cast<float*>(ws + w.dlt[l - 1]);
+        g.dlt_ss = w.dlt_ss[l - 1];
+        g.dlt_ld = c->din[l];
+        hipError_t e = timed(K_BWD, st, [&] { return launch_bwd(g, (int)ns, f32 ? 1 : 0, st); });
+        if (e != hipSuccess) return TM_ERR_HIP;
+    }
+    UpdArgs u = base_upd(c, state, ns);
+    u.kin = k;
+    u.tl = tl;
+    u.tk0 = chunk_idx * b;
+    for (int l = 0; l + 1 < c->L; ++l) u.act[l] = ws + w.act[l];
+    u.act_ss = w.act_ss;
+    u.act_ld = c->hidden;
+    u.act_r0 = fr.nq;
+    for (int l = 0; l < c->L; ++l) {
+        u.dlt[l] = reinterpret_cast<const float*>(ws + w.dlt[l]);
+        u.dlt_ss[l] = w.dlt_ss[l];
+    }
+    u.cc = reinterpret_cast<const float*>(ws + w.cc);
+    u.dc = reinterpret_cast<const float*>(ws + w.dc);
+    u.coef_ss = w.coef_ss;
+    u.ct0 = chunk_idx * b;
+    u.cs = reinterpret_cast<const float*>(ws + w.cs);
+    u.cs_ss = w.cs_ss;
+    u.chunk = chunk_idx;
+    return hip_status(timed(K_UPD, st, [&] { return launch_update(u, c->tbase[c->L], (int)ns, f32 ? 1 : 0, st); }));
+}
+
+tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v, const void* q,
+                    const float* theta, const float* eta, const float* alpha, float* y, int batch,
+                    int heads, int n_tokens, tm_dtype dtype, void* ws_v, hipStream_t st) {
+    char* state = static_cast<char*>(state_v);
+    char* ws = static_cast<char*>(ws_v);
+    const long ns = (long)batch * heads;
+    const int b = c->chunk, C = n_tokens / b;
+    const bool f32 = dtype == TM_F32;
+    WsLayout w = ws_layout(c, ns, n_tokens);
+    TokLayout tl{n_tokens, heads, c->dim};
+
+    ScanArgs sa;
+    memset(&sa, 0, sizeof(sa));
+    sa.theta = theta;
+    sa.eta = eta;
+    sa.alpha = alpha;
+    sa.tl = TokLayout{n_tokens, heads, 1};
+    sa.b = b;
+    sa.C = C;
+    sa.ns = (int)ns;
+    sa.cc = reinterpret_cast<float*>(ws + w.cc);
+    sa.dc = reinterpret_cast<float*>(ws + w.dc);
+    sa.coef_ss = w.coef_ss;
+    sa.cs = reinterpret_cast<float*>(ws + w.cs);
+    sa.cs_ss = w.cs_ss;
+    sa.position = &reinterpret_cast<StateHeader*>(state)->position;
+    sa.add = n_tokens;
+    if (timed(K_SCAN, st, [&] { return launch_scan(sa, st); }) != hipSuccess) return TM_ERR_HIP;
+
+    for (int ci = 0; ci < C; ++ci) {
+        tm_status rc = run_chunk(c, state, ns, w, ws, tl, k, v, q, y, ci, f32, st);
+        if (rc != TM_OK) return rc;
+    }
+    if (q) {
+        // the last chunk's queries, through the weights it wrote
+        FwdRows fr;
+        fr.nq = b;
+        fr.q = q;
+        fr.tq = (C - 1) * b;
+        fr.nk = 0;
+        fr.k = nullptr;
+        fr.tk = 0;
+        fr.v = nullptr;
+        fr.y = y;
+        tm_status rc = run_forward_layers(c, state, ns, w, ws, tl, fr, f32, false, st);
+        if (rc != TM_OK) return rc;
+    }
+    return TM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tm_status tm_create(int dim, int depth, int expansion, int chunk, tm_ctx** out) {
+    if (!out) return TM_ERR_INVALID;
+    *out = nullptr;
+    if (dim < 32 || dim % 32 != 0 || dim > 16384) return TM_ERR_INVALID;
+    if (depth < 1 || depth > MAXL) return TM_ERR_INVALID;
+    if (expansion < 1 || (long)dim * expansion > 65536) return TM_ERR_INVALID;
+    if (chunk < 1 || chunk > MAX_CHUNK) return TM_ERR_INVALID;
+    tm_ctx* c = new (std::nothrow) tm_ctx;
+    if (!c) return TM_ERR_INVALID;
+    memset(c, 0, sizeof(*c));
+    c->gmu = new (std::nothrow) std::mutex;
+    c->graphs = new (std::nothrow) std::vector<GraphEntry>;
+    c->capture_streams = new (std::nothrow) std::vector<std::pair<int, hipStream_t>>;
+    if (!c->gmu || !c->graphs || !c->capture_streams) {
+        delete c->gmu;
+        delete c->graphs;
+        delete c->capture_streams;
+        delete c;
+        return TM_ERR_INVALID;
+    }
+    c->dim = dim;
+    c->depth = depth;
+    c->expansion = depth > 1 ? expansion : 1;
+    c->chunk = chunk;
+    c->hidden = depth > 1 ? dim * expansion : dim;
+    c->L = depth;
+    c->off[0] = 0;
+    c->tbase[0] = 0;
+    for (int l = 0; l < depth; ++l) {
+        c->din[l] = l == 0 ? dim : c->hidden;
+        c->dout[l] = l == depth - 1 ? dim : c->hidden;
+        c->off[l + 1] = c->off[l] + (long)c->din[l] * c->dout[l];
+        c->tj[l] = (c->dout[l] + 63) / 64;
+        c->tbase[l + 1] = c->tbase[l] + ((c->din[l] + 63) / 64) * c->tj[l];
+    }
+    c->P = c->off[depth];
+    uint64_t h = 1469598103934665603ull;
+    h = fnv(h, (uint64_t)dim);
+    h = fnv(h, (uint64_t)depth);
+    h = fnv(h, (uint64_t)c->expansion);
+    h = fnv(h, (uint64_t)chunk);
+    c->hash = h;
+    *out = c;
+    return TM_OK;
+}
+
+void tm_destroy(tm_ctx* ctx) {
+    if (!ctx) return;
+    for (GraphEntry& e : *ctx->graphs)
+        if (e.exec) (void)hipGraphExecDestroy(e.exec);
+    for (auto& pr : *ctx->capture_streams) (void)hipStreamDestroy(pr.second);
+    delete ctx->graphs;
+    delete ctx->capture_streams;
+    delete ctx->gmu;
+    delete ctx;
+}
+
+size_t tm_param_count(const tm_ctx* c) { return c ? (size_t)c->P : 0; }
+
+size_t tm_state_bytes(const tm_ctx* c, int batch, int heads) {
+    if (!c || batch <= 0 || heads <= 0) return 0;
+    return state_layout(c, (long)batch * heads).total;
+}
+
+size_t tm_workspace_bytes(const tm_ctx* c, int batch, int heads, int n_tokens) {
+    if (!c || batch <= 0 || heads <= 0 || n_tokens < 0) return 0;
+    return ws_layout(c, (long)batch * heads, n_tokens > 0 ? n_tokens : 1).total;
+}
+
+tm_status tm_state_init(const tm_ctx* c, void* state, int batch, int heads, const float* init,
+                        void* stream) {
+    if (!c || !state || !init || batch <= 0 || heads <= 0) return TM_ERR_INVALID;
+    if ((long)batch * heads > 65535) return TM_ERR_INVALID;
+    if (!aligned(state, 256) || !aligned(init, 4)) return TM_ERR_INVALID;
+    const long ns = (long)batch * heads;
+    char* s = static_cast<char*>(state);
+    return with_graph(c, make_key(0, batch, heads, 0, 0, {state, init}), static_cast<hipStream_t>(stream),
+                      [&](hipStream_t st) {
+        UpdArgs u = base_upd(c, s, ns);
+        if (launch_header(reinterpret_cast<StateHeader*>(s), c->hash, batch, heads, st) != hipSuccess)
+            return TM_ERR_HIP;
+        if (launch_init(u.M, u.S, init, c->P, heads, (int)ns, st) != hipSuccess) return TM_ERR_HIP;
+        return hip_status(launch_shadow(u, c->tbase[c->L], (int)ns, st));
+    });
+}
+
+tm_status tm_store(const tm_ctx* c, void* state, const void* k, const void* v, const float* theta,
+                   const float* eta, const float* alpha, int batch, int heads, int n_tokens,
+                   tm_dtype dtype, void* ws, void* stream) {
+    tm_status rc = check_common(c, state, batch, heads, n_tokens, dtype, ws);
+    if (rc != TM_OK) return rc;
+    if (!tok_ok(k) || !tok_ok(v) || !gate_ok(theta) || !gate_ok(eta) || !gate_ok(alpha))
+        return TM_ERR_INVALID;
+    if (n_tokens % c->chunk != 0) return TM_ERR_SHAPE;
+    if (n_tokens == 0) return TM_OK;
+    return with_graph(c, make_key(1, batch, heads, n_tokens, dtype, {state, k, v, theta, eta, alpha, ws}),
+                      static_cast<hipStream_t>(stream), [&](hipStream_t st) {
+        return run_store(c, state, k, v, nullptr, theta, eta, alpha, nullptr, batch, heads, n_tokens,
+                         dtype, ws, st);
+    });
+}
+
+tm_status tm_forward(const tm_ctx* c, void* state, const void* k, const void* v, const void* q,
+                     const float* theta, const float* eta, const float* alpha, float* y, int batch,
+                     int heads, int n_tokens, tm_dtype dtype, void* ws, void* stream) {
+    tm_status rc = check_common(c, state, batch, heads, n_tokens, dtype, ws);
+    if (rc != TM_OK) return rc;
+    if (!tok_ok(k) || !tok_ok(v) || !tok_ok(q) || !tok_ok(y) || !gate_ok(theta) || !gate_ok(eta) ||
+        !gate_ok(alpha))
+        return TM_ERR_INVALID;
+    if (n_tokens % c->chunk != 0) return TM_ERR_SHAPE;
+    if (n_tokens == 0) return TM_OK;
+    return with_graph(c, make_key(2, batch, heads, n_tokens, dtype, {state, k, v, q, theta, eta, alpha, y, ws}),
+                      static_cast<hipStream_t>(stream), [&](hipStream_t st) {
+        return run_store(c, state, k, v, q, theta, eta, alpha, y, batch, heads, n_tokens, dtype, ws, st);
+    });
+}
+
+tm_status tm_retrieve(const tm_ctx* c, const void* state_v, const void* q, float* y, int batch,
+                      int heads, int n_tokens, tm_dtype dtype, void* ws_v, void* stream) {
+    tm_status rc = check_common(c, state_v, batch, heads, n_tokens, dtype, ws_v);
+    if (rc != TM_OK) return rc;
+    if (!tok_ok(q) || !tok_ok(y)) return TM_ERR_INVALID;
+    if (n_tokens == 0) return TM_OK;
+    char* state = const_cast<char*>(static_cast<const char*>(state_v));   // read only below
+    char* ws = static_cast<char*>(ws_v);
+    const long ns = (long)batch * heads;
+    return with_graph(c, make_key(3, batch, heads, n_tokens, dtype, {state_v, q, y, ws_v}),
+                      static_cast<hipStream_t>(stream), [&](hipStream_t st) {
+        WsLayout w = ws_layout(c, ns, n_tokens);
+        TokLayout tl{n_tokens, heads, c->dim};
+        for (long p0 = 0; p0 < n_tokens; p0 += w.ret_rows) {
+            FwdRows fr;
+            fr.nq = (int)((n_tokens - p0) < w.ret_rows ? (n_tokens - p0) : w.ret_rows);
+            fr.q = q;
+            fr.tq = (int)p0;
+            fr.nk = 0;
+            fr.k = nullptr;
+            fr.tk = 0;
+            fr.v = nullptr;
+            fr.y = y;
+            tm_status r2 = run_forward_layers(c, state, ns, w, ws, tl, fr, dtype == TM_F32, true, st);
+            if (r2 != TM_OK) return r2;
+        }
+        return TM_OK;
+    });
+}
+
+tm_status tm_state_export(const tm_ctx* c, const void* state, int batch, int heads, float* dst,
+                          void* stream) {
+    if (!c || !state || !dst || batch <= 0 || heads <= 0) return TM_ERR_INVALID;
+    if (!aligned(state, 256) || !aligned(dst, 4)) return TM_ERR_INVALID;
+    const long ns = (long)batch * heads;
+    StateLayout sl = state_layout(c, ns);
+    const char* s = static_cast<const char*>(state);
+    return hip_status(launch_export(reinterpret_cast<const float*>(s + sl.M),
+                                    reinterpret_cast<const float*>(s + sl.S), dst, c->P, (int)ns,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+tm_status tm_state_import(const tm_ctx* c, void* state, int batch, int heads, const float* src,
+                          void* stream) {
+    if (!c || !state || !src || batch <= 0 || heads <= 0) return TM_ERR_INVALID;
+    if ((long)batch * heads > 65535) return TM_ERR_INVALID;
+    if (!aligned(state, 256) || !aligned(src, 4)) return TM_ERR_INVALID;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const long ns = (long)batch * heads;
+    char* s = static_cast<char*>(state);
+    UpdArgs u = base_upd(c, s, ns);
+    if (launch_header(reinterpret_cast<StateHeader*>(s), c->hash, batch, heads, st) != hipSuccess)
+        return TM_ERR_HIP;
+    if (launch_import(u.M, u.S, src, c->P, (int)ns, st) != hipSuccess) return TM_ERR_HIP;
+    return hip_status(launch_shadow(u, c->tbase[c->L], (int)ns, st));
+}
+
+tm_status tm_state_check(const tm_ctx* c, const void* state, int batch, int heads, int* nonfinite,
+                         long long* position, void* stream) {
+    if (!c || !state || batch <= 0 || heads <= 0) return TM_ERR_INVALID;
+    StateHeader h;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(&h, state, sizeof(h), hipMemcpyDeviceToHost, st) != hipSuccess) return TM_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return TM_ERR_HIP;
+    if (h.magic != STATE_MAGIC || h.version != STATE_VERSION || h.cfg_hash != c->hash ||
+        h.batch != batch || h.heads != heads)
+        return TM_ERR_STATE;
+    if (nonfinite) *nonfinite = h.nonfinite;
+    if (position) *position = h.position;
+    return TM_OK;
+}
+
+tm_status tm_graphs_enable(int on) {
+    g_graphs = on != 0;
+    return TM_OK;
+}
+
+tm_status tm_timing_enable(int class_mask) {
+    std::lock_guard<std::mutex> g(g_tmu);
+    g_timing = class_mask & ((1 << K_CLASSES) - 1);
+    return TM_OK;
+}
+
+tm_status tm_timing_read(int kind, double* total_ms, long long* launches) {
+    if (kind < 0 || kind >= K_CLASSES) return TM_ERR_INVALID;
+    std::vector<Timed> todo;
+    {
+        std::lock_guard<std::mutex> g(g_tmu);
+        todo.swap(g_pending);
+    }
+    tm_status rc = TM_OK;
+    double ms[K_CLASSES] = {0};
+    long long n[K_CLASSES] = {0};
+    for (const Timed& t : todo) {
+        float x = 0.f;
+        if (hipEventSynchronize(t.b) != hipSuccess || hipEventElapsedTime(&x, t.a, t.b) != hipSuccess) {
+            rc = TM_ERR_HIP;
+            continue;
+        }
+        ms[t.kind] += x;
+        n[t.kind] += 1;
+    }
+    std::lock_guard<std::mutex> g(g_tmu);
+    for (const Timed& t : todo) {
+        g_pool.push_back(t.a);
+        g_pool.push_back(t.b);
+    }
+    for (int i = 0; i < K_CLASSES; ++i) {
+        g_ms[i] += ms[i];
+        g_n[i] += n[i];
+    }
+    if (total_ms) *total_ms = g_ms[kind];
+    if (launches) *launches = g_n[kind];
+    g_ms[kind] = 0;
+    g_n[kind] = 0;
+    return rc;
+}
+
+const char* tm_status_str(tm_status s) {
+    switch (s) {
+        case TM_OK: return "ok";
+        case TM_ERR_INVALID: return "invalid argument";
+        case TM_ERR_SHAPE: return "n_tokens is not a multiple of the chunk size";
+        case TM_ERR_DTYPE: return "unknown dtype";
+        case TM_ERR_STATE: return "state header does not match the memory configuration";
+        case TM_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,633 @@
+// HIP kernels for the Titans neural-memory store / retrieve on CDNA4 (gfx950).
+//
+// Per chunk of b tokens and per memory stream (one memory per sequence and
+// head), the store is ("Titans, explained", steps 2-4 and 6; "Attack of the
+// Titans", Parallel training):
+//   1. forward of the keys through the chunk-start weights, with the queries
+//      of the previous chunk riding along as extra rows (both read the same
+//      weights),                                            -> gemm_kernel
+//   2. backward of ||M(k) - v||^2 to every hidden layer,    -> gemm_kernel
+//   3. the per-token gradients, weighted by coefficients of theta, eta and
+//      alpha, reduced over the chunk and folded into S and M in one pass over
+//      the state                                            -> update_kernel
+// The coefficients come from a wave-level scan over the gates of each chunk
+// (scan_kernel): the momentum is a linear recurrence and the forgetting a
+// running product, and unrolling both over a chunk whose gradients all sit at
+// the chunk-start weights gives
+//     S_end = p_eta S_0 - sum_i d_i G_i,
+//     M_end = p_alpha M_0 + s0 S_0 - sum_i c_i G_i,
+// with A_i = prod_{j>i} (1 - alpha_j), E_i = prod_{j>i} eta_j,
+// r_i = A_i + eta_{i+1} r_{i+1} (r_b = 1), c_i = theta_i r_i, d_i = theta_i E_i,
+// p_alpha = prod (1 - alpha), p_eta = prod eta, s0 = eta_1 r_1.  Only products
+// and sums appear (no ratios of running products, which underflow).
+//
+// Matrix products run on MFMA: v_mfma_f32_16x16x32_bf16 for the bf16 path
+// and v_mfma_f32_16x16x4_f32 for the fp32 path, fp32 accumulation in both.
+#include "tm_internal.h"
+
+namespace tmk {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+template <class OP> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 T; };
+template <> struct Frag<float> { typedef f32x8 T; };   // also: 8 raw values of a storage type
+
+// ---------------------------------------------------------------------------
+// small helpers
+
+__device__ __forceinline__ f32x8 ld8(const float* p) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x8 ld8(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16(f32x8 v) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (bf16)v[j];
+    return r;
+}
+__device__ __forceinline__ f32x8 to_f32(bf16x8 v) {
+    f32x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (float)v[j];
+    return r;
+}
+
+template <class OP> __device__ __forceinline__ typename Frag<OP>::T cvt(f32x8 v);
+template <> __device__ __forceinline__ bf16x8 cvt<bf16>(f32x8 v) { return to_bf16(v); }
+template <> __device__ __forceinline__ f32x8 cvt<float>(f32x8 v) { return v; }
+template <class OP> __device__ __forceinline__ typename Frag<OP>::T cvt(bf16x8 v);
+template <> __device__ __forceinline__ bf16x8 cvt<bf16>(bf16x8 v) { return v; }
+template <> __device__ __forceinline__ f32x8 cvt<float>(bf16x8 v) { return to_f32(v); }
+
+template <class OP> __device__ __forceinline__ typename Frag<OP>::T zero_frag() {
+    typename Frag<OP>::T z;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) z[j] = (OP)0.0f;
+    return z;
+}
+
+// C += A B over one 32-deep slice of K.  Each lane supplies 8 consecutive K
+// values of its A row and of its B column; A and B use the same K order, so
+// how the instruction maps register slots to K does not matter.
+__device__ __forceinline__ void mma(f32x4& c, bf16x8 a, bf16x8 b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, f32x8 a, f32x8 b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ long tok_off(const TokLayout& tl, int s, int t) {
+    int bi = s / tl.H, hi = s - bi * tl.H;
+    return ((long)bi * tl.Tc + t) * tl.H * (long)tl.d + (long)hi * tl.d;
+}
+
+template <class T> __device__ __forceinline__ void store1(void* p, long i, float x) {
+    reinterpret_cast<T*>(p)[i] = (T)x;
+}
+template <class T> __device__ __forceinline__ float load1(const void* p, long i) {
+    return (float)reinterpret_cast<const T*>(p)[i];
+}
+
+// ---------------------------------------------------------------------------
+// Chunk forward / backward product.  A workgroup of W waves owns one tile of
+// 64 rows x 16*NR columns and splits its K range over the waves (wave w takes
+// the w-th contiguous slice of 32-deep steps); the W partial tiles are summed
+// in LDS in a fixed order, so results are deterministic and no workgroup ever
+// waits for another (cross-workgroup handoffs need device-scope fences, which
+// serialise across the whole chip).  Each lane feeds the matrix cores from
+// registers loaded straight from global memory (activations hit L2) through
+// a PF-deep prefetch ring; the ring has no branches, steps past the end of a
+// slice re-load a valid address and contribute zeros.
+// OP: operand type; AT / BT: storage types of A / B; BKC: B contiguous in K.
+
+constexpr int GEMM_RT = 64;   // rows per tile (4 row blocks of 16)
+
+template <class OP>
+__device__ __forceinline__ void gemm_store(const GemmArgs& g, int s, int r, int c, float z) {
+    if (g.epi == EPI_HIDDEN) {
+        const float sg = sigmoid(z);
+        store1<OP>(g.act, (long)s * g.act_ss + (long)r * g.act_ld + c, z * sg);
+        if (r >= g.n0)
+            g.dsl[(long)s * g.dsl_ss + (long)(r - g.n0) * g.dsl_ld + c] = sg * (1.0f + z * (1.0f - sg));
+    } else if (g.epi == EPI_OUT) {
+        if (r < g.n0) {
+            g.y[tok_off(g.tl, s, g.yt0 + r) + c] = z;
+        } else {
+            const float vv = load1<OP>(g.v, tok_off(g.tl, s, g.vt0 + r - g.n0) + c);
+            g.dlt[(long)s * g.dlt_ss + (long)(r - g.n0) * g.dlt_ld + c] = 2.0f * (z - vv);
+        }
+    } else {
+        g.dlt[(long)s * g.dlt_ss + (long)r * g.dlt_ld + c] =
+            z * g.dsl[(long)s * g.dsl_ss + (long)r * g.dsl_ld + c];
+    }
+}
+
+template <class OP, class AT, class BT, bool BKC, int NR, int W, int PF>
+__global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
+    typedef typename Frag<OP>::T F;
+    constexpr int MR = GEMM_RT / 16;
+    constexpr int NT = NR * 16;
+    constexpr int NTP = NT + 1;            // padded LDS row
+    extern __shared__ float red[];          // [W][GEMM_RT][NTP]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int s = blockIdx.z;
+    const int row0 = blockIdx.y * GEMM_RT;
+    const int col0 = blockIdx.x * NT;
+    const int nsteps = g.K >> 5;
+    const int spw = (nsteps + W - 1) / W;   // steps per wave
+    const int kb = wave * spw;
+    const int ke = min(nsteps, kb + spw);   // may be <= kb: the wave adds zeros
+    const int klast = max(min(ke, nsteps) - 1, 0);
+
+    f32x4 acc[MR][NR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) acc[m][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    const int kofs = 8 * (lane >> 4);
+    const AT* arow[MR];
+    bool aok[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        int r = row0 + m * 16 + (lane & 15);
+        aok[m] = r < g.nrows;
+        if (!aok[m]) r = g.nrows - 1;   // valid address; the value is dropped
+        long off;
+        const void* base = g.a0;
+        if (g.amode == 0) {
+            if (r < g.n0) { off = tok_off(g.tl, s, g.at0 + r); }
+            else { base = g.a1; off = tok_off(g.tl, s, g.at1 + r - g.n0); }
+        } else {
+            off = (long)s * g.a_ss + (long)r * g.a_ld;
+        }
+        arow[m] = reinterpret_cast<const AT*>(base) + off + kofs;
+    }
+    const BT* bcol[NR];
+    bool bok[NR];
+#pragma unroll
+    for (int n = 0; n < NR; ++n) {
+        int c = col0 + n * 16 + (lane & 15);
+        bok[n] = c < g.N;
+        bcol[n] = reinterpret_cast<const BT*>(g.b) + (long)s * g.b_ss + (long)(bok[n] ? c : 0) * g.b_ldn +
+                  (long)kofs * g.b_ldk;
+    }
+    // the ring holds raw storage vectors; conversion to the operand type
+    // happens right before the matrix instruction, so loads stay in flight
+    typedef typename Frag<AT>::T RA;
+    typedef typename Frag<BT>::T RB;
+    RA a[PF][MR];
+    RB bb[PF][NR];
+    auto load_step = [&](int p, int k) {
+        const int k0 = k << 5;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) a[p][m] = ld8(arow[m] + k0);
+#pragma unroll
+        for (int n = 0; n < NR; ++n) {
+            if (BKC) {
+                bb[p][n] = ld8(bcol[n] + k0);
+            } else {
+                RB u;
+                const BT* q = bcol[n] + (long)k0 * g.b_ldk;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) u[j] = q[(long)j * g.b_ldk];
+                bb[p][n] = u;
+            }
+        }
+    };
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load_step(p, min(kb + p, klast));
+    for (int k = kb; k < kb + spw; k += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const bool live = k + p < ke;   // wave-uniform
+            F av[MR], bv[NR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) av[m] = aok[m] ? cvt<OP>(a[p][m]) : zero_frag<OP>();
+#pragma unroll
+            for (int n = 0; n < NR; ++n) bv[n] = (live && bok[n]) ? cvt<OP>(bb[p][n]) : zero_frag<OP>();
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+#pragma unroll
+                for (int n = 0; n < NR; ++n) mma(acc[m][n], av[m], bv[n]);
+            load_step(p, min(k + p + PF, klast));
+        }
+    }
+
+    // sum the W partial tiles in LDS, in wave order
+    float* mine = red + wave * (GEMM_RT * NTP);
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int n = 0; n < NR; ++n)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                mine[(m * 16 + 4 * (lane >> 4) + e) * NTP + n * 16 + (lane & 15)] = acc[m][n][e];
+    __syncthreads();
+    for (int idx = tid; idx < GEMM_RT * NT; idx += W * 64) {
+        const int rr = idx / NT, cc = idx - rr * NT;
+        const int r = row0 + rr, c = col0 + cc;
+        if (r >= g.nrows || c >= g.N) continue;
+        float z = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) z += red[w * (GEMM_RT * NTP) + rr * NTP + cc];
+        gemm_store<OP>(g, s, r, c, z);
+    }
+}
+
+// Pick the column width and wave count of one product: enough workgroups to
+// cover the chip (about 192 tiles of 64 rows, ideally at least 3 steps per
+// wave), wider tiles first so the activations are re-read from L2 less often.
+static void pick(const GemmArgs& g, int ns, int& nr, int& w) {
+    const int nsteps = g.K >> 5;
+    const long nrt = (g.nrows + GEMM_RT - 1) / GEMM_RT;
+    nr = 4;
+    w = 4;
+    auto wgs = [&](int nr_) { return (long)((g.N + 16 * nr_ - 1) / (16 * nr_)) * nrt * ns; };
+    if (nsteps >= 8 * 4) w = 8;
+    while (wgs(nr) < 192 && nr > 1) nr >>= 1;
+}
+
+template <class OP, class AT, class BT, bool BKC, int NR, int W, int PF>
+static void launch_one(const GemmArgs& g, int ns, hipStream_t st) {
+    dim3 grid((g.N + NR * 16 - 1) / (NR * 16), (g.nrows + GEMM_RT - 1) / GEMM_RT, ns);
+    const size_t lds = (size_t)W * GEMM_RT * (NR * 16 + 1) * 4;
+    hipLaunchKernelGGL((gemm_kernel<OP, AT, BT, BKC, NR, W, PF>), grid, dim3(W * 64), lds, st, g);
+}
+
+template <class OP, class AT, class BT, bool BKC, int PF>
+static hipError_t launch_gemm(const GemmArgs& g, int ns, hipStream_t st) {
+    if (g.nrows <= 0 || g.N <= 0) return hipSuccess;
+    int nr, w;
+    pick(g, ns, nr, w);
+    if (w == 8) {
+        if (nr == 4) launch_one<OP, AT, BT, BKC, 4, 8, PF>(g, ns, st);
+        else if (nr == 2) launch_one<OP, AT, BT, BKC, 2, 8, PF>(g, ns, st);
+        else launch_one<OP, AT, BT, BKC, 1, 8, PF>(g, ns, st);
+    } else {
+        if (nr == 4) launch_one<OP, AT, BT, BKC, 4, 4, PF>(g, ns, st);
+        else if (nr == 2) launch_one<OP, AT, BT, BKC, 2, 4, PF>(g, ns, st);
+        else launch_one<OP, AT, BT, BKC, 1, 4, PF>(g, ns, st);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd(const GemmArgs& g, int ns, int f32, hipStream_t st) {
+    if (f32) return launch_gemm<float, float, float, false, 2>(g, ns, st);
+    return launch_gemm<bf16, bf16, bf16, true, 3>(g, ns, st);
+}
+
+hipError_t launch_bwd(const GemmArgs& g, int ns, int f32, hipStream_t st) {
+    if (f32) return launch_gemm<float, float, float, true, 2>(g, ns, st);
+    return launch_gemm<bf16, float, float, true, 2>(g, ns, st);
+}
+
+// ---------------------------------------------------------------------------
+// Coefficient scan: one wave per (stream, chunk), lane i = token i of the chunk.
+
+__device__ __forceinline__ float shdown(float x, int off) { return __shfl_down(x, off, 64); }
+
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+    const int lane = threadIdx.x & 63;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && a.position) *a.position += a.add;
+    const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= (long)a.ns * a.C) return;
+    const int s = (int)(w / a.C), c = (int)(w - (long)s * a.C);
+    const int b = a.b;
+    const bool on = lane < b;
+    const int t = c * b + lane;
+    float th = 0.f, e = 1.f, oa = 1.f;
+    if (on) {
+        const long gi = tok_off(a.tl, s, t);
+        th = a.theta[gi];
+        e = a.eta[gi];
+        oa = 1.0f - a.alpha[gi];
+    }
+    // inclusive suffix products over lanes i..63 (idle lanes contribute 1)
+    float po = oa, pe = e;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float o2 = shdown(po, off), e2 = shdown(pe, off);
+        if (lane + off < 64) { po *= o2; pe *= e2; }
+    }
+    float A = shdown(po, 1), E = shdown(pe, 1);
+    if (lane == 63) { A = 1.f; E = 1.f; }
+    // r_i = A_i + eta_{i+1} r_{i+1}: suffix composition of x -> A_i + en_i x,
+    // with en = 0 on the chunk's last token (r_{b-1} = 1) and beyond.
+    float en = shdown(e, 1);
+    if (lane + 1 >= b) en = 0.f;
+    float fa = A, fm = en;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float a2 = shdown(fa, off), m2 = shdown(fm, off);
+        if (lane + off < 64) { fa = fa + fm * a2; fm = fm * m2; }
+    }
+    const float r = fa;
+    if (on) {
+        a.cc[(long)s * a.coef_ss + t] = th * r;
+        a.dc[(long)s * a.coef_ss + t] = th * E;
+    }
+    if (lane == 0) {
+        float* o = a.cs + (long)s * a.cs_ss + (long)c * 4;
+        o[0] = oa * A;   // p_alpha
+        o[1] = e * E;    // p_eta
+        o[2] = e * r;    // s0
+        o[3] = 0.f;
+    }
+}
+
+hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
+    long waves = (long)a.ns * a.C;
+    if (waves == 0) return hipSuccess;
+    dim3 grid((unsigned)((waves + 3) / 4));
+    hipLaunchKernelGGL(scan_kernel, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Gradient reduction over the chunk + fused momentum / forgetting write.
+// One workgroup per 64 x 64 tile of one layer's W (per stream):
+//   U_M = H^T diag(c) Delta,  U_S = H^T diag(d) Delta   (K = b tokens)
+//   S' = p_eta S - U_S,  M' = p_alpha M + s0 S - U_M,  Wt = bf16(M')^T.
+// H and Delta arrive token-major; they are staged transposed in LDS so that
+// each lane reads 8 consecutive tokens for the MFMA operands.
+
+constexpr int UPAD = 8;                 // LDS row padding (elements)
+constexpr int UK = MAX_CHUNK + UPAD;    // LDS row pitch of the operand tiles
+
+template <class OP>
+__global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
+    typedef typename Frag<OP>::T F;
+    // operand tiles and result tiles share the LDS (a barrier separates them)
+    constexpr int OPB = 3 * 64 * UK * (int)sizeof(OP);
+    constexpr int UB = 2 * 64 * 65 * 4;
+    __shared__ __attribute__((aligned(16))) char lds[OPB > UB ? OPB : UB];
+    OP (*HT)[UK] = reinterpret_cast<OP (*)[UK]>(lds);
+    OP (*DcT)[UK] = reinterpret_cast<OP (*)[UK]>(lds + 64 * UK * sizeof(OP));
+    OP (*DdT)[UK] = reinterpret_cast<OP (*)[UK]>(lds + 2 * 64 * UK * sizeof(OP));
+    float (*UM)[65] = reinterpret_cast<float (*)[65]>(lds);
+    float (*US)[65] = reinterpret_cast<float (*)[65]>(lds + 64 * 65 * 4);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int s = blockIdx.y;
+    int tile = blockIdx.x;
+    int l = 0;
+    while (l + 1 < u.L && tile >= u.tbase[l + 1]) ++l;
+    tile -= u.tbase[l];
+    const int ti = tile / u.tj[l], tj = tile - ti * u.tj[l];
+    const int din = u.din[l], dout = u.dout[l];
+    const int i0 = ti * 64, j0 = tj * 64;
+    const int b = u.b, KP = (b + 31) & ~31;
+
+    // issue this tile's M and S loads first: their HBM latency overlaps the
+    // staging and the matrix-core work below
+    float* Mp = u.M + (long)s * u.P + u.off[l];
+    float* Sp = u.S + (long)s * u.P + u.off[l];
+    f32x4 mreg[4], sreg[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int idx = tid + 256 * q;
+        const int gi = i0 + (idx >> 4), gj = j0 + (idx & 15) * 4;
+        if (gi < din && gj < dout) {
+            const long o = (long)gi * dout + gj;
+            mreg[q] = *reinterpret_cast<const f32x4*>(Mp + o);
+            sreg[q] = *reinterpret_cast<const f32x4*>(Sp + o);
+        } else {
+            mreg[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            sreg[q] = mreg[q];
+        }
+    }
+
+    // stage H^T: HT[i][t] = H[t][i0 + i]
+    for (int idx = tid; idx < KP * 8; idx += 256) {
+        const int t = idx >> 3, i = (idx & 7) * 8;
+        f32x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        if (t < b && i0 + i < din) {
+            if (l == 0) {
+                const OP* p = reinterpret_cast<const OP*>(u.kin) + tok_off(u.tl, s, u.tk0 + t) + i0 + i;
+                v = (sizeof(OP) == 2) ? to_f32(ld8(reinterpret_cast<const bf16*>(p)))
+                                      : ld8(reinterpret_cast<const float*>(p));
+            } else {
+                const OP* p = reinterpret_cast<const OP*>(u.act[l - 1]) + (long)s * u.act_ss +
+                              (long)(u.act_r0 + t) * u.act_ld + i0 + i;
+                v = (sizeof(OP) == 2) ? to_f32(ld8(reinterpret_cast<const bf16*>(p)))
+                                      : ld8(reinterpret_cast<const float*>(p));
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) HT[i + e][t] = (OP)v[e];
+    }
+    // stage (c_t Delta[t][j]) and (d_t Delta[t][j]) transposed
+    for (int idx = tid; idx < KP * 8; idx += 256) {
+        const int t = idx >> 3, j = (idx & 7) * 8;
+        f32x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        float ct = 0.f, dt = 0.f;
+        if (t < b && j0 + j < dout) {
+            v = ld8(u.dlt[l] + (long)s * u.dlt_ss[l] + (long)t * dout + j0 + j);
+            ct = u.cc[(long)s * u.coef_ss + u.ct0 + t];
+            dt = u.dc[(long)s * u.coef_ss + u.ct0 + t];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            DcT[j + e][t] = (OP)(ct * v[e]);
+            DdT[j + e][t] = (OP)(dt * v[e]);
+        }
+    }
+    __syncthreads();
+
+    const int wi = wave & 1, wj = wave >> 1;
+    f32x4 am[2][2], as[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) { am[m][n] = (f32x4){0.f, 0.f, 0.f, 0.f}; as[m][n] = am[m][n]; }
+    const int kofs = 8 * (lane >> 4);
+    for (int k0 = 0; k0 < KP; k0 += 32) {
+        F a[2], bc[2], bd[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            a[m] = *reinterpret_cast<const F*>(&HT[wi * 32 + m * 16 + (lane & 15)][k0 + kofs]);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            bc[n] = *reinterpret_cast<const F*>(&DcT[wj * 32 + n * 16 + (lane & 15)][k0 + kofs]);
+            bd[n] = *reinterpret_cast<const F*>(&DdT[wj * 32 + n * 16 + (lane & 15)][k0 + kofs]);
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) { mma(am[m][n], a[m], bc[n]); mma(as[m][n], a[m], bd[n]); }
+    }
+    __syncthreads();   // operand tiles are dead from here; the LDS now holds U
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = wi * 32 + m * 16 + 4 * (lane >> 4) + e;
+                const int c = wj * 32 + n * 16 + (lane & 15);
+                UM[r][c] = am[m][n][e];
+                US[r][c] = as[m][n][e];
+            }
+    __syncthreads();
+
+    const float* csp = u.cs + (long)s * u.cs_ss + (long)u.chunk * 4;
+    const float pa = csp[0], pe = csp[1], s0 = csp[2];
+    bool bad = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int idx = tid + 256 * q;
+        const int i = idx >> 4, j = (idx & 15) * 4;
+        const int gi = i0 + i, gj = j0 + j;
+        if (gi < din && gj < dout) {
+            const long o = (long)gi * dout + gj;
+            const f32x4 m = mreg[q], sv = sreg[q];
+            f32x4 mn, sn;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sn[e] = pe * sv[e] - US[i][j + e];
+                mn[e] = pa * m[e] + s0 * sv[e] - UM[i][j + e];
+                bad |= !__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn[e]);
+                UM[i][j + e] = mn[e];
+            }
+            *reinterpret_cast<f32x4*>(Mp + o) = mn;
+            *reinterpret_cast<f32x4*>(Sp + o) = sn;
+        }
+    }
+    __syncthreads();
+    bf16* Wp = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P + u.off[l];
+    for (int idx = tid; idx < 64 * 8; idx += 256) {
+        const int j = idx >> 3, i = (idx & 7) * 8;
+        const int gj = j0 + j, gi = i0 + i;
+        if (gj < dout && gi < din) {
+            bf16x8 w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = (bf16)UM[i + e][j];
+            *reinterpret_cast<bf16x8*>(Wp + (long)gj * din + gi) = w;
+        }
+    }
+    if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
+}
+
+hipError_t launch_update(const UpdArgs& u, int ntiles, int ns, int f32, hipStream_t st) {
+    dim3 grid(ntiles, ns);
+    if (f32) hipLaunchKernelGGL(update_kernel<float>, grid, dim3(256), 0, st, u);
+    else hipLaunchKernelGGL(update_kernel<bf16>, grid, dim3(256), 0, st, u);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// State set-up, bf16 copy, export / import.
+
+__global__ void init_kernel(float* M, float* S, const float* init, long P, int H, int ns) {
+    const long n = (long)ns * P;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+        const long s = i / P, p = i - s * P;
+        M[i] = init[(s % H) * P + p];
+        S[i] = 0.f;
+    }
+}
+
+hipError_t launch_init(float* M, float* S, const float* init, long P, int H, int ns, hipStream_t st) {
+    hipLaunchKernelGGL(init_kernel, dim3(2048), dim3(256), 0, st, M, S, init, P, H, ns);
+    return hipGetLastError();
+}
+
+// Wt = bf16(M)^T per 64 x 64 tile (uses the layer / tile fields of UpdArgs).
+__global__ __launch_bounds__(256) void shadow_kernel(UpdArgs u) {
+    __shared__ float T[64][65];
+    const int tid = threadIdx.x;
+    const int s = blockIdx.y;
+    int tile = blockIdx.x;
+    int l = 0;
+    while (l + 1 < u.L && tile >= u.tbase[l + 1]) ++l;
+    tile -= u.tbase[l];
+    const int ti = tile / u.tj[l], tj = tile - ti * u.tj[l];
+    const int din = u.din[l], dout = u.dout[l];
+    const int i0 = ti * 64, j0 = tj * 64;
+    const float* Mp = u.M + (long)s * u.P + u.off[l];
+    for (int idx = tid; idx < 64 * 64; idx += 256) {
+        const int i = idx >> 6, j = idx & 63;
+        T[i][j] = (i0 + i < din && j0 + j < dout) ? Mp[(long)(i0 + i) * dout + j0 + j] : 0.f;
+    }
+    __syncthreads();
+    bf16* Wp = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P + u.off[l];
+    for (int idx = tid; idx < 64 * 8; idx += 256) {
+        const int j = idx >> 3, i = (idx & 7) * 8;
+        if (j0 + j < dout && i0 + i < din) {
+            bf16x8 w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = (bf16)T[i + e][j];
+            *reinterpret_cast<bf16x8*>(Wp + (long)(j0 + j) * din + i0 + i) = w;
+        }
+    }
+}
+
+hipError_t launch_shadow(const UpdArgs& u, int ntiles, int ns, hipStream_t st) {
+    hipLaunchKernelGGL(shadow_kernel, dim3(ntiles, ns), dim3(256), 0, st, u);
+    return hipGetLastError();
+}
+
+__global__ void export_kernel(const float* M, const float* S, float* dst, long P, int ns) {
+    const long n = (long)ns * P;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+        const long s = i / P, p = i - s * P;
+        dst[s * 2 * P + p] = M[i];
+        dst[s * 2 * P + P + p] = S[i];
+    }
+}
+
+__global__ void import_kernel(float* M, float* S, const float* src, long P, int ns) {
+    const long n = (long)ns * P;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+        const long s = i / P, p = i - s * P;
+        M[i] = src[s * 2 * P + p];
+        S[i] = src[s * 2 * P + P + p];
+    }
+}
+
+hipError_t launch_export(const float* M, const float* S, float* dst, long P, int ns, hipStream_t st) {
+    hipLaunchKernelGGL(export_kernel, dim3(2048), dim3(256), 0, st, M, S, dst, P, ns);
+    return hipGetLastError();
+}
+
+hipError_t launch_import(float* M, float* S, const float* src, long P, int ns, hipStream_t st) {
+    hipLaunchKernelGGL(import_kernel, dim3(2048), dim3(256), 0, st, M, S, src, P, ns);
+    return hipGetLastError();
+}
+
+__global__ void header_kernel(StateHeader* h, uint64_t hash, int batch, int heads) {
+    if (threadIdx.x == 0) {
+        h->magic = STATE_MAGIC;
+        h->version = STATE_VERSION;
+        h->cfg_hash = hash;
+        h->batch = batch;
+        h->heads = heads;
+        h->nonfinite = 0;
+        h->reserved0 = 0;
+        h->position = 0;
+    }
+}
+
+hipError_t launch_header(StateHeader* h, uint64_t hash, int batch, int heads, hipStream_t st) {
+    hipLaunchKernelGGL(header_kernel, dim3(1), dim3(64), 0, st, h, hash, batch, heads);
+    return hipGetLastError();
+}
+
+}  // namespace tmk

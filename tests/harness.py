@@ -1,0 +1,115 @@
+"""Test harness: run a workload through the HIP library (via the C ABI) and
+through the fp64 oracle on the same seeded host arrays."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import torch
+
+from oracle import tmref
+from test_trained_neural_amd import inputs as I
+import test_trained_neural_amd as T
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def relerr(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def dev_inputs(ci: I.CallInputs, dtype: str):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {}
+    for name in ("k", "v", "q"):
+        out[name] = torch.from_numpy(np.ascontiguousarray(getattr(ci, name))).to("cuda").to(tdt).contiguous()
+    for name in ("theta", "eta", "alpha"):
+        out[name] = torch.from_numpy(np.ascontiguousarray(getattr(ci, name))).to("cuda").contiguous()
+    return out
+
+
+class GpuMemory:
+    """A memory of batch*heads streams held in a device state blob."""
+
+    def __init__(self, wl: I.Workload, params: I.Params, batch=None, init_weights=None):
+        self.wl = wl
+        self.B = wl.batch if batch is None else batch
+        self.H = wl.heads
+        self.ctx = T.tm_create(wl.dim, wl.depth, wl.expansion, wl.chunk)
+        self.P = T.tm_param_count(self.ctx)
+        assert self.P == wl.params
+        self.state = torch.empty(T.tm_state_bytes(self.ctx, self.B, self.H), dtype=torch.uint8, device="cuda")
+        w = params.init_weights if init_weights is None else init_weights
+        self.init = torch.from_numpy(np.ascontiguousarray(w, np.float32)).to("cuda")
+        T.tm_state_init(self.ctx, self.state, self.B, self.H, self.init)
+        self.ws = None
+
+    def _ws(self, n):
+        need = T.tm_workspace_bytes(self.ctx, self.B, self.H, n)
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        return self.ws
+
+    def forward(self, d):
+        B, Tn, H, dim = d["k"].shape
+        y = torch.empty((B, Tn, H, dim), dtype=torch.float32, device="cuda")
+        T.tm_forward(self.ctx, self.state, d["k"], d["v"], d["q"], d["theta"], d["eta"], d["alpha"], y,
+                     self._ws(Tn))
+        return y
+
+    def store(self, d):
+        T.tm_store(self.ctx, self.state, d["k"], d["v"], d["theta"], d["eta"], d["alpha"],
+                   self._ws(d["k"].shape[1]))
+
+    def retrieve(self, q):
+        B, Tn, H, dim = q.shape
+        y = torch.empty((B, Tn, H, dim), dtype=torch.float32, device="cuda")
+        T.tm_retrieve(self.ctx, self.state, q, y, self._ws(Tn))
+        return y
+
+    def export(self):
+        out = torch.empty((self.B * self.H, 2 * self.P), dtype=torch.float32, device="cuda")
+        T.tm_state_export(self.ctx, self.state, self.B, self.H, out)
+        return out.cpu().numpy()
+
+    def import_(self, arr):
+        src = torch.from_numpy(np.ascontiguousarray(arr, np.float32)).to("cuda")
+        T.tm_state_import(self.ctx, self.state, self.B, self.H, src)
+        torch.cuda.synchronize()
+
+    def check(self):
+        return T.tm_state_check(self.ctx, self.state, self.B, self.H)
+
+    def close(self):
+        T.tm_destroy(self.ctx)
+        self.ctx = None
+
+
+def oracle_forward(wl: I.Workload, state: np.ndarray, ci: I.CallInputs, with_q=True, threads=None):
+    return tmref.forward(wl.dim, wl.depth, wl.expansion, wl.chunk, state, ci.k, ci.v, ci.theta, ci.eta,
+                         ci.alpha, q=ci.q if with_q else None, n_threads=threads)
+
+
+def compare_state(wl: I.Workload, gpu_state, ref_state):
+    """(rel err of M, rel err of S): the worst over streams and layers of
+    ||X_gpu - X_ref||_F / ||X_ref||_F per weight matrix."""
+    P = wl.params
+    em = es = 0.0
+    for s in range(ref_state.shape[0]):
+        off = 0
+        for din, dout in wl.layer_dims():
+            n = din * dout
+            em = max(em, relerr(gpu_state[s, off:off + n], ref_state[s, off:off + n]))
+            es = max(es, relerr(gpu_state[s, P + off:P + off + n], ref_state[s, P + off:P + off + n]))
+            off += n
+    return em, es
+
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}

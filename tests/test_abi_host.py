@@ -1,0 +1,84 @@
+"""Host side of the C ABI, no GPU needed: the library loads, exports every
+entry point include/tm.h declares, and rejects bad arguments on the host
+before anything is launched (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import test_trained_neural_amd as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "tm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tm_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert len(syms) == 16
+    assert set(syms) == set(T.EXPORTED)
+    L = ctypes.CDLL(T.LIB_PATH)
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_create_validation():
+    for args in [(48, 2, 4, 64), (0, 2, 4, 64), (64, 0, 4, 64), (64, 9, 4, 64), (64, 2, 0, 64),
+                 (64, 2, 4, 0), (64, 2, 4, 65)]:
+        with pytest.raises(T.TMError) as e:
+            T.tm_create(*args)
+        assert e.value.code == T.TM_ERR_INVALID
+    assert T.lib().tm_create(64, 1, 1, 16, None) == T.TM_ERR_INVALID
+
+
+def test_sizes():
+    c = T.tm_create(384, 2, 4, 64)
+    P = 2 * 384 * 1536
+    assert T.tm_param_count(c) == P
+    # header + M + S (fp32) + bf16 copy, each 256-aligned
+    assert T.tm_state_bytes(c, 2, 1) == 256 + 2 * P * 4 * 2 + 2 * P * 2
+    assert T.tm_state_bytes(c, 0, 1) == 0
+    c1 = T.tm_create(64, 1, 7, 16)   # depth 1 ignores the expansion
+    assert T.tm_param_count(c1) == 64 * 64
+    c4 = T.tm_create(512, 4, 4, 32)
+    assert T.tm_param_count(c4) == 512 * 2048 * 2 + 2048 * 2048 * 2
+    assert T.tm_workspace_bytes(c, 2, 1, 1024) > 0
+    for h in (c, c1, c4):
+        T.tm_destroy(h)
+
+
+def test_call_validation_before_launch():
+    # fake, aligned "device" addresses: every call below must be rejected on
+    # the host, so nothing is dereferenced or launched
+    L = T.lib()
+    c = T.tm_create(64, 2, 2, 16)
+    A = ctypes.c_void_p(1 << 20)
+    G = ctypes.c_void_p((1 << 20) + 4096)
+    st = ctypes.c_void_p(None)
+    # n_tokens not a multiple of the chunk
+    assert L.tm_store(c, A, A, A, G, G, G, 1, 1, 24, T.TM_BF16, A, st) == T.TM_ERR_SHAPE
+    assert L.tm_forward(c, A, A, A, A, G, G, G, A, 1, 1, 17, T.TM_F32, A, st) == T.TM_ERR_SHAPE
+    # bad dtype
+    assert L.tm_store(c, A, A, A, G, G, G, 1, 1, 16, 7, A, st) == T.TM_ERR_DTYPE
+    # null / misaligned pointers, bad sizes
+    assert L.tm_store(c, None, A, A, G, G, G, 1, 1, 16, T.TM_BF16, A, st) == T.TM_ERR_INVALID
+    assert L.tm_store(c, A, ctypes.c_void_p((1 << 20) + 2), A, G, G, G, 1, 1, 16, T.TM_BF16, A, st) == \
+        T.TM_ERR_INVALID
+    assert L.tm_store(c, ctypes.c_void_p((1 << 20) + 16), A, A, G, G, G, 1, 1, 16, T.TM_BF16, A, st) == \
+        T.TM_ERR_INVALID
+    assert L.tm_store(c, A, A, A, G, G, G, 0, 1, 16, T.TM_BF16, A, st) == T.TM_ERR_INVALID
+    assert L.tm_store(c, A, A, A, G, G, G, 1, 1, -16, T.TM_BF16, A, st) == T.TM_ERR_INVALID
+    assert L.tm_retrieve(c, A, None, A, 1, 1, 16, T.TM_BF16, A, st) == T.TM_ERR_INVALID
+    assert L.tm_forward(c, A, A, A, None, G, G, G, A, 1, 1, 16, T.TM_BF16, A, st) == T.TM_ERR_INVALID
+    assert L.tm_state_init(c, None, 1, 1, A, st) == T.TM_ERR_INVALID
+    assert L.tm_state_export(c, A, 0, 1, A, st) == T.TM_ERR_INVALID
+    # empty calls are no-ops that succeed without touching anything
+    assert L.tm_store(c, A, A, A, G, G, G, 1, 1, 0, T.TM_BF16, A, st) == T.TM_OK
+    assert L.tm_retrieve(c, A, A, A, 1, 1, 0, T.TM_BF16, A, st) == T.TM_OK
+    assert L.tm_status_str(T.TM_ERR_SHAPE).decode().startswith("n_tokens")
+    T.tm_destroy(c)
