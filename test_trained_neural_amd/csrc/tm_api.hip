@@ -58,8 +58,9 @@ StateLayout state_layout(const tm_ctx* c, long ns) {
 }
 
 struct WsLayout {
-    size_t cc, dc, cs, act[MAXL], dsl[MAXL], dlt[MAXL], ret[2], total;
-    long coef_ss, cs_ss, act_ss, dsl_ss, dlt_ss[MAXL], ret_ss, ret_rows;
+    size_t cc, dc, cs, act[MAXL], dsl[MAXL], dlt[MAXL], kt, ht[MAXL], dct[MAXL], ddt[MAXL], ret[2], total;
+    long coef_ss, cs_ss, act_ss, dsl_ss, dlt_ss[MAXL], kt_ss, ht_ss, dt_ss[MAXL], ret_ss, ret_rows;
+    int bp, C;
 };
 
 WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
@@ -81,6 +82,21 @@ WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
     for (int l = 0; l < c->L; ++l) {
         w.dlt_ss[l] = b * c->dout[l];
         w.dlt[l] = o; o += al256((size_t)ns * w.dlt_ss[l] * 4);
+    }
+    // transposed operands of the update: rows of bp tokens (fp32-sized so
+    // either operand type fits)
+    w.bp = (int)((b + 31) / 32 * 32);
+    w.C = (int)C;
+    w.kt_ss = C * c->dim * w.bp;
+    w.kt = o; o += al256((size_t)ns * w.kt_ss * 4);
+    w.ht_ss = h * w.bp;
+    for (int l = 0; l + 1 < c->L; ++l) {
+        w.ht[l] = o; o += al256((size_t)ns * w.ht_ss * 4);
+    }
+    for (int l = 0; l < c->L; ++l) {
+        w.dt_ss[l] = (long)c->dout[l] * w.bp;
+        w.dct[l] = o; o += al256((size_t)ns * w.dt_ss[l] * 4);
+        w.ddt[l] = o; o += al256((size_t)ns * w.dt_ss[l] * 4);
     }
     size_t fwd_total = o;
     w.ret_rows = T < RET_ROWS ? T : RET_ROWS;
@@ -338,6 +354,9 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
                 g.dsl = reinterpret_cast<float*>(ws + w.dsl[l]);
                 g.dsl_ss = w.dsl_ss;
                 g.dsl_ld = c->hidden;
+                g.ht = ws + w.ht[l];
+                g.tr_ss = w.ht_ss;
+                g.bp = w.bp;
             }
             g.act_ld = c->hidden;
         } else {
@@ -350,6 +369,15 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
                 g.dlt = reinterpret_cast<float*>(ws + w.dlt[l]);
                 g.dlt_ss = w.dlt_ss[l];
                 g.dlt_ld = c->dout[l];
+                if (fr.nk > 0) {
+                    g.dct = ws + w.dct[l];
+                    g.ddt = ws + w.ddt[l];
+                    g.tr_ss = w.dt_ss[l];
+                    g.bp = w.bp;
+                    g.cc = reinterpret_cast<const float*>(ws + w.cc) + fr.tk;
+                    g.dc = reinterpret_cast<const float*>(ws + w.dc) + fr.tk;
+                    g.coef_ss = w.coef_ss;
+                }
             }
         }
         (void)esz;
@@ -388,7 +416,7 @@ tm_status run_chunk(const tm_ctx* c, char* state, long ns, const WsLayout& w, ch
         g.a0 = ws + w.dlt[l];
         g.a_ss = w.dlt_ss[l];
         g.a_ld = c->dout[l];
-        g.n0 = b;
+        g.n0 = 0;   // key rows only
         g.b = state + sl.M + (size_t)c->off[l] * 4;
         g.b_ss = c->P;
         g.b_ldn = c->dout[l];
@@ -400,25 +428,30 @@ tm_status run_chunk(const tm_ctx* c, char* state, long ns, const WsLayout& w, ch
         g.dlt = reinterpret_cast<float*>(ws + w.dlt[l - 1]);
         g.dlt_ss = w.dlt_ss[l - 1];
         g.dlt_ld = c->din[l];
+        g.dct = ws + w.dct[l - 1];
+        g.ddt = ws + w.ddt[l - 1];
+        g.tr_ss = w.dt_ss[l - 1];
+        g.bp = w.bp;
+        g.cc = reinterpret_cast<const float*>(ws + w.cc) + chunk_idx * b;
+        g.dc = reinterpret_cast<const float*>(ws + w.dc) + chunk_idx * b;
+        g.coef_ss = w.coef_ss;
         hipError_t e = timed(K_BWD, st, [&] { return launch_bwd(g, (int)ns, f32 ? 1 : 0, st); });
         if (e != hipSuccess) return TM_ERR_HIP;
     }
     UpdArgs u = base_upd(c, state, ns);
-    u.kin = k;
-    u.tl = tl;
-    u.tk0 = chunk_idx * b;
-    for (int l = 0; l + 1 < c->L; ++l) u.act[l] = ws + w.act[l];
-    u.act_ss = w.act_ss;
-    u.act_ld = c->hidden;
-    u.act_r0 = fr.nq;
-    for (int l = 0; l < c->L; ++l) {
-        u.dlt[l] = reinterpret_cast<const float*>(ws + w.dlt[l]);
-        u.dlt_ss[l] = w.dlt_ss[l];
+    const size_t esz = f32 ? 4 : 2;
+    u.bp = w.bp;
+    u.at[0] = ws + w.kt + (size_t)chunk_idx * c->dim * w.bp * esz;
+    u.at_ss[0] = w.kt_ss;
+    for (int l = 1; l < c->L; ++l) {
+        u.at[l] = ws + w.ht[l - 1];
+        u.at_ss[l] = w.ht_ss;
     }
-    u.cc = reinterpret_cast<const float*>(ws + w.cc);
-    u.dc = reinterpret_cast<const float*>(ws + w.dc);
-    u.coef_ss = w.coef_ss;
-    u.ct0 = chunk_idx * b;
+    for (int l = 0; l < c->L; ++l) {
+        u.dct[l] = ws + w.dct[l];
+        u.ddt[l] = ws + w.ddt[l];
+        u.dt_ss[l] = w.dt_ss[l];
+    }
     u.cs = reinterpret_cast<const float*>(ws + w.cs);
     u.cs_ss = w.cs_ss;
     u.chunk = chunk_idx;
@@ -452,6 +485,12 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     sa.cs_ss = w.cs_ss;
     sa.position = &reinterpret_cast<StateHeader*>(state)->position;
     sa.add = n_tokens;
+    sa.k = k;
+    sa.ktl = tl;
+    sa.kt = ws + w.kt;
+    sa.bp = w.bp;
+    sa.kt_f32 = f32 ? 1 : 0;
+    sa.scan_blocks = (int)(((long)ns * C + 3) / 4);
     if (timed(K_SCAN, st, [&] { return launch_scan(sa, st); }) != hipSuccess) return TM_ERR_HIP;
 
     for (int ci = 0; ci < C; ++ci) {

@@ -36,6 +36,8 @@ enum { EPI_HIDDEN = 0, EPI_OUT = 1, EPI_BWD = 2 };
 
 // One matrix product of the chunk forward / backward, per stream s
 // (blockIdx.z):  Z[r][n] = sum_k A[r][k] B[k][n], r < nrows, n < N, k < K.
+// Rows r < n0 are queries, rows r >= n0 keys (t = r - n0 is the key's token
+// inside the chunk); the backward has key rows only (n0 = 0).
 struct GemmArgs {
     int nrows, N, K;
     // A rows.  amode 0: rows r < n0 are tokens (at0 + r) of a0, rows r >= n0
@@ -50,11 +52,14 @@ struct GemmArgs {
     long b_ss, b_ldn, b_ldk;
     TokLayout tl;
     int epi;
-    // EPI_HIDDEN: act[r][n] = SiLU(z) (operand type); rows r >= n0 also
-    //             dsl[r - n0][n] = SiLU'(z).
-    // EPI_OUT   : rows r < n0: y at token (yt0 + r) = z; rows r >= n0:
-    //             dlt[r - n0][n] = 2 (z - v at token (vt0 + r - n0)).
-    // EPI_BWD   : dlt[r][n] = z * dsl[r][n].
+    // EPI_HIDDEN: act[r][n] = SiLU(z) (operand type); key rows also
+    //             dsl[t][n] = SiLU'(z) and the transposed copy ht[n][t] = act.
+    // EPI_OUT   : query rows: y at token (yt0 + r) = z; key rows:
+    //             dlt[t][n] = Delta = 2 (z - v at token (vt0 + t)).
+    // EPI_BWD   : dlt[t][n] = Delta = z * dsl[t][n].
+    // OUT / BWD also write the theta-weighted transposed deltas
+    //             dct[n][t] = c_t Delta,  ddt[n][t] = d_t Delta  (operand type).
+    // Transposed arrays have rows of bp (>= chunk, multiple of 32) tokens.
     void* act;
     long act_ss, act_ld;
     float* dsl;
@@ -64,13 +69,22 @@ struct GemmArgs {
     float* y;
     const void* v;
     int yt0, vt0;
+    void* ht;
+    void* dct;
+    void* ddt;
+    long tr_ss;               // per-stream stride of ht / dct / ddt
+    int bp;
+    const float* cc;          // c_t of the chunk's tokens: cc[s*coef_ss + t]
+    const float* dc;
+    long coef_ss;
 };
 
 // The theta-weighted gradient reduction of one chunk and the fused
 // momentum / forgetting write, for every layer.  Grid: (tiles of all layers,
-// streams); tiles are 64 x 64 blocks of W_l.
+// streams); tiles are 64 x 64 blocks of W_l.  Operands arrive transposed
+// (token-contiguous rows of bp tokens, valid below b).
 struct UpdArgs {
-    int L, b;
+    int L, b, bp;
     int din[MAXL], dout[MAXL];
     long off[MAXL];
     int tj[MAXL];
@@ -79,24 +93,19 @@ struct UpdArgs {
     float* M;
     float* S;
     void* Wt;                 // bf16 transposed copy, [d_out][d_in] per layer
-    const void* kin;          // layer 0 input rows: keys at token (tk0 + t)
-    TokLayout tl;
-    int tk0;
-    const void* act[MAXL];    // act[l]: output rows of hidden layer l
-    long act_ss, act_ld;
-    int act_r0;               // first key row inside act[l]
-    const float* dlt[MAXL];   // dlt[l]: [b][dout[l]] per stream
-    long dlt_ss[MAXL];
-    const float* cc;          // per-token momentum-into-memory coefficient
-    const float* dc;          // per-token momentum coefficient
-    long coef_ss;
-    int ct0;
+    const void* at[MAXL];     // at[l]: layer l's input rows transposed, [d_in][bp]
+    long at_ss[MAXL];
+    const void* dct[MAXL];    // (c Delta_l)^T, [d_out][bp]
+    const void* ddt[MAXL];    // (d Delta_l)^T
+    long dt_ss[MAXL];
     const float* cs;          // per-chunk scalars (p_alpha, p_eta, s0, 0)
     long cs_ss;
     int chunk;
     int* flag;
 };
 
+// Per call: the coefficient scan of every (stream, chunk) and the keys of
+// every chunk transposed to kt[s][chunk][d][bp].
 struct ScanArgs {
     const float* theta;
     const float* eta;
@@ -110,6 +119,11 @@ struct ScanArgs {
     long cs_ss;
     long long* position;
     long long add;
+    const void* k;            // keys, token layout ktl
+    TokLayout ktl;
+    void* kt;
+    int bp, kt_f32;
+    int scan_blocks;          // blocks [0, scan_blocks) scan, the rest transpose
 };
 
 // ---- launchers (tm_kernels.hip) ----

@@ -114,24 +114,30 @@ template <class T> __device__ __forceinline__ float load1(const void* p, long i)
 
 constexpr int GEMM_RT = 64;   // rows per tile (4 row blocks of 16)
 
+// Row-major outputs of one element; returns the value the transposed copy
+// carries for key rows (the rounded activation, or Delta).
 template <class OP>
-__device__ __forceinline__ void gemm_store(const GemmArgs& g, int s, int r, int c, float z) {
+__device__ __forceinline__ float gemm_store(const GemmArgs& g, int s, int r, int c, float z) {
     if (g.epi == EPI_HIDDEN) {
         const float sg = sigmoid(z);
-        store1<OP>(g.act, (long)s * g.act_ss + (long)r * g.act_ld + c, z * sg);
+        const OP h = (OP)(z * sg);
+        reinterpret_cast<OP*>(g.act)[(long)s * g.act_ss + (long)r * g.act_ld + c] = h;
         if (r >= g.n0)
             g.dsl[(long)s * g.dsl_ss + (long)(r - g.n0) * g.dsl_ld + c] = sg * (1.0f + z * (1.0f - sg));
+        return (float)h;
     } else if (g.epi == EPI_OUT) {
         if (r < g.n0) {
             g.y[tok_off(g.tl, s, g.yt0 + r) + c] = z;
-        } else {
-            const float vv = load1<OP>(g.v, tok_off(g.tl, s, g.vt0 + r - g.n0) + c);
-            g.dlt[(long)s * g.dlt_ss + (long)(r - g.n0) * g.dlt_ld + c] = 2.0f * (z - vv);
+            return 0.f;
         }
-    } else {
-        g.dlt[(long)s * g.dlt_ss + (long)r * g.dlt_ld + c] =
-            z * g.dsl[(long)s * g.dsl_ss + (long)r * g.dsl_ld + c];
+        const float vv = load1<OP>(g.v, tok_off(g.tl, s, g.vt0 + r - g.n0) + c);
+        const float dl = 2.0f * (z - vv);
+        g.dlt[(long)s * g.dlt_ss + (long)(r - g.n0) * g.dlt_ld + c] = dl;
+        return dl;
     }
+    const float dl = z * g.dsl[(long)s * g.dsl_ss + (long)r * g.dsl_ld + c];
+    g.dlt[(long)s * g.dlt_ss + (long)r * g.dlt_ld + c] = dl;
+    return dl;
 }
 
 template <class OP, class AT, class BT, bool BKC, int NR, int W, int PF>
@@ -236,6 +242,8 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
             for (int e = 0; e < 4; ++e)
                 mine[(m * 16 + 4 * (lane >> 4) + e) * NTP + n * 16 + (lane & 15)] = acc[m][n][e];
     __syncthreads();
+    // pass 1, row-major (coalesced row outputs): each element is owned by one
+    // thread, which leaves the value for the transposed copy in slot 0
     for (int idx = tid; idx < GEMM_RT * NT; idx += W * 64) {
         const int rr = idx / NT, cc = idx - rr * NT;
         const int r = row0 + rr, c = col0 + cc;
@@ -243,7 +251,24 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
         float z = 0.f;
 #pragma unroll
         for (int w = 0; w < W; ++w) z += red[w * (GEMM_RT * NTP) + rr * NTP + cc];
-        gemm_store<OP>(g, s, r, c, z);
+        red[rr * NTP + cc] = gemm_store<OP>(g, s, r, c, z);
+    }
+    if (!g.ht && !g.dct) return;   // uniform: no transposed outputs (retrieve)
+    __syncthreads();
+    // pass 2, column-major (coalesced transposed outputs) over the key rows
+    for (int idx = tid; idx < GEMM_RT * NT; idx += W * 64) {
+        const int cc = idx / GEMM_RT, rr = idx - cc * GEMM_RT;
+        const int r = row0 + rr, c = col0 + cc;
+        if (r >= g.nrows || r < g.n0 || c >= g.N) continue;
+        const int t = r - g.n0;
+        const float x = red[rr * NTP + cc];
+        const long o = (long)s * g.tr_ss + (long)c * g.bp + t;
+        if (g.epi == EPI_HIDDEN) {
+            reinterpret_cast<OP*>(g.ht)[o] = (OP)x;
+        } else {
+            reinterpret_cast<OP*>(g.dct)[o] = (OP)(g.cc[(long)s * g.coef_ss + t] * x);
+            reinterpret_cast<OP*>(g.ddt)[o] = (OP)(g.dc[(long)s * g.coef_ss + t] * x);
+        }
     }
 }
 
@@ -299,7 +324,37 @@ hipError_t launch_bwd(const GemmArgs& g, int ns, int f32, hipStream_t st) {
 
 __device__ __forceinline__ float shdown(float x, int off) { return __shfl_down(x, off, 64); }
 
+// Keys of one chunk, 64 features at a time, transposed through LDS into
+// kt[s][chunk][feature][bp] (token-contiguous rows for the update's operands).
+template <class T>
+__device__ void transpose_keys(const ScanArgs& a, long blk) {
+    __shared__ float tile[64][65];
+    const int d = a.ktl.d, ib = (d + 63) / 64;
+    const int s = (int)(blk / ((long)a.C * ib));
+    const long rem = blk - (long)s * a.C * ib;
+    const int c = (int)(rem / ib), i0 = (int)(rem - (long)c * ib) * 64;
+    const int tid = threadIdx.x;
+    const T* k = reinterpret_cast<const T*>(a.k);
+    for (int idx = tid; idx < 64 * 64; idx += 256) {
+        const int t = idx >> 6, i = idx & 63;
+        tile[t][i] = (t < a.b && i0 + i < d) ? (float)k[tok_off(a.ktl, s, c * a.b + t) + i0 + i] : 0.f;
+    }
+    __syncthreads();
+    T* kt = reinterpret_cast<T*>(a.kt) + ((long)s * a.C + c) * (long)d * a.bp;
+    for (int idx = tid; idx < 64 * a.bp; idx += 256) {
+        const int i = idx / a.bp, t = idx - i * a.bp;
+        if (i0 + i < d && t < 64) kt[(long)(i0 + i) * a.bp + t] = (T)tile[t][i];
+    }
+}
+
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+    if ((int)blockIdx.x >= a.scan_blocks) {
+        const long blk = (long)blockIdx.x - a.scan_blocks;
+        if (a.kt_f32) transpose_keys<float>(a, blk);
+        else transpose_keys<bf16>(a, blk);
+        return;
+    }
+
     const int lane = threadIdx.x & 63;
     if (blockIdx.x == 0 && threadIdx.x == 0 && a.position) *a.position += a.add;
     const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -351,7 +406,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
     long waves = (long)a.ns * a.C;
     if (waves == 0) return hipSuccess;
-    dim3 grid((unsigned)((waves + 3) / 4));
+    const long tr = (long)a.ns * a.C * ((a.ktl.d + 63) / 64);
+    dim3 grid((unsigned)(a.scan_blocks + tr));
     hipLaunchKernelGGL(scan_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
@@ -359,26 +415,31 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // Gradient reduction over the chunk + fused momentum / forgetting write.
 // One workgroup per 64 x 64 tile of one layer's W (per stream):
-//   U_M = H^T diag(c) Delta,  U_S = H^T diag(d) Delta   (K = b tokens)
+//   U_M = H^T diag(c) Delta,  U_S = H^T diag(d) Delta   (K = the chunk's tokens)
 //   S' = p_eta S - U_S,  M' = p_alpha M + s0 S - U_M,  Wt = bf16(M')^T.
-// H and Delta arrive token-major; they are staged transposed in LDS so that
-// each lane reads 8 consecutive tokens for the MFMA operands.
+// The producers left H^T, (c Delta)^T and (d Delta)^T token-contiguous, so
+// each lane loads its 8 consecutive tokens straight from L2; the tile's M and
+// S loads are issued first and overlap that work.  The results go through
+// LDS once to switch from the matrix-core layout to row-contiguous float4
+// accesses for M and S, and once more for the transposed bf16 copy.
 
-constexpr int UPAD = 8;                 // LDS row padding (elements)
-constexpr int UK = MAX_CHUNK + UPAD;    // LDS row pitch of the operand tiles
+template <class OP>
+__device__ __forceinline__ typename Frag<OP>::T tok8(const OP* p, int t0, int b, bool full) {
+    typedef typename Frag<OP>::T F;
+    F v = cvt<OP>(ld8(p));
+    if (!full) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (t0 + e >= b) v[e] = (OP)0.0f;
+    }
+    return v;
+}
 
 template <class OP>
 __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
     typedef typename Frag<OP>::T F;
-    // operand tiles and result tiles share the LDS (a barrier separates them)
-    constexpr int OPB = 3 * 64 * UK * (int)sizeof(OP);
-    constexpr int UB = 2 * 64 * 65 * 4;
-    __shared__ __attribute__((aligned(16))) char lds[OPB > UB ? OPB : UB];
-    OP (*HT)[UK] = reinterpret_cast<OP (*)[UK]>(lds);
-    OP (*DcT)[UK] = reinterpret_cast<OP (*)[UK]>(lds + 64 * UK * sizeof(OP));
-    OP (*DdT)[UK] = reinterpret_cast<OP (*)[UK]>(lds + 2 * 64 * UK * sizeof(OP));
-    float (*UM)[65] = reinterpret_cast<float (*)[65]>(lds);
-    float (*US)[65] = reinterpret_cast<float (*)[65]>(lds + 64 * 65 * 4);
+    __shared__ float UM[64][65];
+    __shared__ float US[64][65];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = blockIdx.y;
@@ -389,10 +450,9 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
     const int ti = tile / u.tj[l], tj = tile - ti * u.tj[l];
     const int din = u.din[l], dout = u.dout[l];
     const int i0 = ti * 64, j0 = tj * 64;
-    const int b = u.b, KP = (b + 31) & ~31;
+    const int b = u.b, bp = u.bp;
 
-    // issue this tile's M and S loads first: their HBM latency overlaps the
-    // staging and the matrix-core work below
+    // this tile's M and S first: their latency overlaps the work below
     float* Mp = u.M + (long)s * u.P + u.off[l];
     float* Sp = u.S + (long)s * u.P + u.off[l];
     f32x4 mreg[4], sreg[4];
@@ -410,70 +470,48 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
         }
     }
 
-    // stage H^T: HT[i][t] = H[t][i0 + i]
-    for (int idx = tid; idx < KP * 8; idx += 256) {
-        const int t = idx >> 3, i = (idx & 7) * 8;
-        f32x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
-        if (t < b && i0 + i < din) {
-            if (l == 0) {
-                const OP* p = reinterpret_cast<const OP*>(u.kin) + tok_off(u.tl, s, u.tk0 + t) + i0 + i;
-                v = (sizeof(OP) == 2) ? to_f32(ld8(reinterpret_cast<const bf16*>(p)))
-                                      : ld8(reinterpret_cast<const float*>(p));
-            } else {
-                const OP* p = reinterpret_cast<const OP*>(u.act[l - 1]) + (long)s * u.act_ss +
-                              (long)(u.act_r0 + t) * u.act_ld + i0 + i;
-                v = (sizeof(OP) == 2) ? to_f32(ld8(reinterpret_cast<const bf16*>(p)))
-                                      : ld8(reinterpret_cast<const float*>(p));
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) HT[i + e][t] = (OP)v[e];
-    }
-    // stage (c_t Delta[t][j]) and (d_t Delta[t][j]) transposed
-    for (int idx = tid; idx < KP * 8; idx += 256) {
-        const int t = idx >> 3, j = (idx & 7) * 8;
-        f32x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
-        float ct = 0.f, dt = 0.f;
-        if (t < b && j0 + j < dout) {
-            v = ld8(u.dlt[l] + (long)s * u.dlt_ss[l] + (long)t * dout + j0 + j);
-            ct = u.cc[(long)s * u.coef_ss + u.ct0 + t];
-            dt = u.dc[(long)s * u.coef_ss + u.ct0 + t];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            DcT[j + e][t] = (OP)(ct * v[e]);
-            DdT[j + e][t] = (OP)(dt * v[e]);
-        }
-    }
-    __syncthreads();
-
+    // U_M, U_S on the matrix cores: 4 waves as 2 x 2, 32 x 32 each
     const int wi = wave & 1, wj = wave >> 1;
+    const int kofs = 8 * (lane >> 4);
+    const OP* A = reinterpret_cast<const OP*>(u.at[l]) + (long)s * u.at_ss[l];
+    const OP* Bc = reinterpret_cast<const OP*>(u.dct[l]) + (long)s * u.dt_ss[l];
+    const OP* Bd = reinterpret_cast<const OP*>(u.ddt[l]) + (long)s * u.dt_ss[l];
+    int ai[2], bj[2];
+    bool aok[2], bok[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        ai[m] = i0 + wi * 32 + m * 16 + (lane & 15);
+        aok[m] = ai[m] < din;
+        if (!aok[m]) ai[m] = 0;
+        bj[m] = j0 + wj * 32 + m * 16 + (lane & 15);
+        bok[m] = bj[m] < dout;
+        if (!bok[m]) bj[m] = 0;
+    }
     f32x4 am[2][2], as[2][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int n = 0; n < 2; ++n) { am[m][n] = (f32x4){0.f, 0.f, 0.f, 0.f}; as[m][n] = am[m][n]; }
-    const int kofs = 8 * (lane >> 4);
-    for (int k0 = 0; k0 < KP; k0 += 32) {
+    for (int k0 = 0; k0 < bp; k0 += 32) {
+        const int t0 = k0 + kofs;
+        const bool full = t0 + 8 <= b;
         F a[2], bc[2], bd[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-            a[m] = *reinterpret_cast<const F*>(&HT[wi * 32 + m * 16 + (lane & 15)][k0 + kofs]);
+        for (int m = 0; m < 2; ++m) {
+            a[m] = tok8<OP>(A + (long)ai[m] * bp + t0, t0, b, full);
+            if (!aok[m]) a[m] = zero_frag<OP>();
+        }
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-            bc[n] = *reinterpret_cast<const F*>(&DcT[wj * 32 + n * 16 + (lane & 15)][k0 + kofs]);
-            bd[n] = *reinterpret_cast<const F*>(&DdT[wj * 32 + n * 16 + (lane & 15)][k0 + kofs]);
+            bc[n] = tok8<OP>(Bc + (long)bj[n] * bp + t0, t0, b, full);
+            bd[n] = tok8<OP>(Bd + (long)bj[n] * bp + t0, t0, b, full);
+            if (!bok[n]) { bc[n] = zero_frag<OP>(); bd[n] = zero_frag<OP>(); }
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int n = 0; n < 2; ++n) { mma(am[m][n], a[m], bc[n]); mma(as[m][n], a[m], bd[n]); }
     }
-    __syncthreads();   // operand tiles are dead from here; the LDS now holds U
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
