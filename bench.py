@@ -127,8 +127,8 @@ def main():
 
     # the same steps again with HIP events around every launch (events force
     # direct launches): per-kernel durations for the roofline
-    T.tm_timing_enable(0xF)
-    for c in range(4):
+    T.tm_timing_enable(0x1F)
+    for c in range(5):
         T.tm_timing_read(c)
     torch.cuda.synchronize()
     e0 = time.perf_counter()
@@ -137,7 +137,7 @@ def main():
     torch.cuda.synchronize()
     e1 = time.perf_counter()
     T.tm_timing_enable(0)
-    names = {T.K_SCAN: "scan", T.K_FWD: "fwd", T.K_BWD: "bwd", T.K_UPDATE: "update"}
+    names = {T.K_SCAN: "scan", T.K_FWD: "fwd", T.K_BWD: "bwd", T.K_UPDATE: "update", T.K_FIRST: "first"}
     per = {}
     for c, nm in names.items():
         per[nm] = T.tm_timing_read(c)

@@ -63,7 +63,7 @@ typedef enum { TM_F32 = 0, TM_BF16 = 1 } tm_dtype;
 
 typedef struct tm_ctx tm_ctx;
 
-/* Memory configuration.  dim: per-head width, a multiple of 32 (>= 32);
+/* Memory configuration.  dim: per-head width, a multiple of 32, 32..1024;
  * depth: number of weight matrices, 1..8; expansion: hidden = dim*expansion
  * (>= 1, ignored for depth 1); chunk: tokens per mini-batch b, 1..64 ("Titans,
  * explained" step 6: within a chunk every gradient is taken at the chunk-start
@@ -138,8 +138,10 @@ const char* tm_status_str(tm_status status);
 tm_status tm_graphs_enable(int on);
 
 /* Instrumentation for measuring kernels in place (not part of the method).
- * Kernel classes: 0 coefficient scan, 1 chunk forward product, 2 chunk
- * backward product, 3 gradient reduction + state update.  While bit c of
+ * Kernel classes: 0 coefficient scan (and key transpose), 1 chunk forward
+ * products of layers 1.., 2 chunk backward products, 3 gradient reduction +
+ * state update of layers 1.., 4 first-layer step (the first layer's update,
+ * its in-place backward, and its forward).  While bit c of
  * class_mask is set, every launch of class c is bracketed by a pair of HIP
  * events recorded on its launch stream (mask 0 turns timing off).
  * tm_timing_read waits for the recorded launches and returns, for one class,

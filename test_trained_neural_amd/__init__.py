@@ -27,7 +27,7 @@ EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_w
             "tm_graphs_enable")
 
 # kernel classes of tm_timing_enable / tm_timing_read
-K_SCAN, K_FWD, K_BWD, K_UPDATE = 0, 1, 2, 3
+K_SCAN, K_FWD, K_BWD, K_UPDATE, K_FIRST = 0, 1, 2, 3, 4
 
 _lib = None
 _vp = ctypes.c_void_p

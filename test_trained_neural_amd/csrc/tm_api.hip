@@ -28,6 +28,14 @@ struct tm_ctx {
     std::mutex* gmu;
     std::vector<GraphEntry>* graphs;
     std::vector<std::pair<int, hipStream_t>>* capture_streams;
+    // per device: a second capture stream and two events, used to fork the
+    // independent kernels of a chunk step into parallel graph branches
+    struct Fork {
+        int dev;
+        hipStream_t side;
+        hipEvent_t fork, join;
+    };
+    std::vector<Fork>* forks;
     unsigned long long stamp;
     int dim, depth, expansion, chunk, hidden, L;
     int din[MAXL], dout[MAXL];
@@ -41,6 +49,7 @@ struct tm_ctx {
 namespace {
 
 constexpr long RET_ROWS = 2048;   // query rows per stream per retrieve pass
+constexpr bool kForkChunkStep = false;
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -58,7 +67,7 @@ StateLayout state_layout(const tm_ctx* c, long ns) {
 }
 
 struct WsLayout {
-    size_t cc, dc, cs, act[MAXL], dsl[MAXL], dlt[MAXL], kt, ht[MAXL], dct[MAXL], ddt[MAXL], ret[2], total;
+    size_t cc, dc, cs, act[MAXL], dsl[MAXL], dlt[MAXL], dltb, kt, ht[MAXL], dct[MAXL], ddt[MAXL], ht1[2], wr[2], ret[2], total;
     long coef_ss, cs_ss, act_ss, dsl_ss, dlt_ss[MAXL], kt_ss, ht_ss, dt_ss[MAXL], ret_ss, ret_rows;
     int bp, C;
 };
@@ -98,6 +107,18 @@ WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
         w.dct[l] = o; o += al256((size_t)ns * w.dt_ss[l] * 4);
         w.ddt[l] = o; o += al256((size_t)ns * w.dt_ss[l] * 4);
     }
+    // first layer's transposed key-row activations, alternating between the
+    // chunk being written and the chunk being reduced; and two row-major
+    // copies of layer 1's weights (chunk start of the chunk being reduced,
+    // and its result), both with stream stride P
+    for (int i = 0; i < 2; ++i) {
+        w.ht1[i] = o; o += al256((size_t)ns * w.ht_ss * 4);
+    }
+    for (int i = 0; i < 2; ++i) {
+        w.wr[i] = o; o += al256((size_t)ns * c->P * 4);
+    }
+    // operand-type copy of layer 1's Delta (the first layer's in-place backward)
+    w.dltb = o; o += al256((size_t)ns * w.dlt_ss[c->L > 1 ? 1 : 0] * 4);
     size_t fwd_total = o;
     w.ret_rows = T < RET_ROWS ? T : RET_ROWS;
     w.ret_ss = w.ret_rows * h;
@@ -121,7 +142,7 @@ uint64_t fnv(uint64_t h, uint64_t x) {
 tm_status hip_status(hipError_t e) { return e == hipSuccess ? TM_OK : TM_ERR_HIP; }
 
 // ---- optional per-launch timing (tm_timing_enable / tm_timing_read) ----
-enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_UPD = 3, K_CLASSES = 4 };
+enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_UPD = 3, K_FIRST = 4, K_CLASSES = 5 };
 struct Timed {
     hipEvent_t a, b;
     int kind;
@@ -300,12 +321,12 @@ struct FwdRows {
 
 tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayout& w, char* ws,
                              const TokLayout& tl, const FwdRows& fr, bool f32, bool retrieve,
-                             hipStream_t st) {
+                             hipStream_t st, int l_begin = 0) {
     StateLayout sl = state_layout(c, ns);
     const int rows = fr.nq + fr.nk;
     if (rows == 0) return TM_OK;
     const int esz = f32 ? 4 : 2;
-    for (int l = 0; l < c->L; ++l) {
+    for (int l = l_begin; l < c->L; ++l) {
         GemmArgs g;
         memset(&g, 0, sizeof(g));
         g.nrows = rows;
@@ -370,6 +391,7 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
                 g.dlt_ss = w.dlt_ss[l];
                 g.dlt_ld = c->dout[l];
                 if (fr.nk > 0) {
+                    if (l == 1 && !f32) g.dltb = ws + w.dltb;
                     g.dct = ws + w.dct[l];
                     g.ddt = ws + w.ddt[l];
                     g.tr_ss = w.dt_ss[l];
@@ -387,25 +409,13 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
     return TM_OK;
 }
 
-// One chunk: forward (with the previous chunk's queries), backward, update.
-tm_status run_chunk(const tm_ctx* c, char* state, long ns, const WsLayout& w, char* ws,
-                    const TokLayout& tl, const void* k, const void* v, const void* q, float* y,
-                    int chunk_idx, bool f32, hipStream_t st) {
+// Backward of chunk ci through layers L-1 .. 2: Delta_{l-1} from Delta_l
+// (the first layer's Delta is formed inside the next step kernel).
+tm_status run_backward(const tm_ctx* c, char* state, long ns, const WsLayout& w, char* ws,
+                       const TokLayout& tl, int ci, bool f32, hipStream_t st) {
     const int b = c->chunk;
     StateLayout sl = state_layout(c, ns);
-    FwdRows fr;
-    fr.nq = (q && chunk_idx > 0) ? b : 0;
-    fr.q = q;
-    fr.tq = (chunk_idx - 1) * b;
-    fr.nk = b;
-    fr.k = k;
-    fr.tk = chunk_idx * b;
-    fr.v = v;
-    fr.y = y;
-    tm_status rc = run_forward_layers(c, state, ns, w, ws, tl, fr, f32, false, st);
-    if (rc != TM_OK) return rc;
-    // backward: delta_{l-1} = (delta_l W_l^T) * SiLU'(z_{l-1})
-    for (int l = c->L - 1; l >= 1; --l) {
+    for (int l = c->L - 1; l >= 2; --l) {
         GemmArgs g;
         memset(&g, 0, sizeof(g));
         g.nrows = b;
@@ -428,36 +438,26 @@ tm_status run_chunk(const tm_ctx* c, char* state, long ns, const WsLayout& w, ch
         g.dlt = reinterpret_cast<float*>(ws + w.dlt[l - 1]);
         g.dlt_ss = w.dlt_ss[l - 1];
         g.dlt_ld = c->din[l];
+        if (l - 1 == 1 && !f32) g.dltb = ws + w.dltb;
         g.dct = ws + w.dct[l - 1];
         g.ddt = ws + w.ddt[l - 1];
         g.tr_ss = w.dt_ss[l - 1];
         g.bp = w.bp;
-        g.cc = reinterpret_cast<const float*>(ws + w.cc) + chunk_idx * b;
-        g.dc = reinterpret_cast<const float*>(ws + w.dc) + chunk_idx * b;
+        g.cc = reinterpret_cast<const float*>(ws + w.cc) + ci * b;
+        g.dc = reinterpret_cast<const float*>(ws + w.dc) + ci * b;
         g.coef_ss = w.coef_ss;
         hipError_t e = timed(K_BWD, st, [&] { return launch_bwd(g, (int)ns, f32 ? 1 : 0, st); });
         if (e != hipSuccess) return TM_ERR_HIP;
     }
-    UpdArgs u = base_upd(c, state, ns);
-    const size_t esz = f32 ? 4 : 2;
-    u.bp = w.bp;
-    u.at[0] = ws + w.kt + (size_t)chunk_idx * c->dim * w.bp * esz;
-    u.at_ss[0] = w.kt_ss;
-    for (int l = 1; l < c->L; ++l) {
-        u.at[l] = ws + w.ht[l - 1];
-        u.at_ss[l] = w.ht_ss;
-    }
-    for (int l = 0; l < c->L; ++l) {
-        u.dct[l] = ws + w.dct[l];
-        u.ddt[l] = ws + w.ddt[l];
-        u.dt_ss[l] = w.dt_ss[l];
-    }
-    u.cs = reinterpret_cast<const float*>(ws + w.cs);
-    u.cs_ss = w.cs_ss;
-    u.chunk = chunk_idx;
-    return hip_status(timed(K_UPD, st, [&] { return launch_update(u, c->tbase[c->L], (int)ns, f32 ? 1 : 0, st); }));
+    return TM_OK;
 }
 
+// The call's chunk loop.  Step c (0..C) is one launch of the step kernel:
+// chunk c-1's update of every layer (the first layer's Delta formed in
+// place) and chunk c's first-layer forward of [queries of chunk c-1; keys of
+// chunk c]; then the forward of layers 1.. for the same rows (their last
+// layer writes y for the queries and Delta for the keys) and, for depth >= 3,
+// the backward down to layer 1.  Step C only finishes chunk C-1.
 tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v, const void* q,
                     const float* theta, const float* eta, const float* alpha, float* y, int batch,
                     int heads, int n_tokens, tm_dtype dtype, void* ws_v, hipStream_t st) {
@@ -466,8 +466,10 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     const long ns = (long)batch * heads;
     const int b = c->chunk, C = n_tokens / b;
     const bool f32 = dtype == TM_F32;
+    const size_t esz = f32 ? 4 : 2;
     WsLayout w = ws_layout(c, ns, n_tokens);
     TokLayout tl{n_tokens, heads, c->dim};
+    StateLayout sl = state_layout(c, ns);
 
     ScanArgs sa;
     memset(&sa, 0, sizeof(sa));
@@ -491,25 +493,134 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     sa.bp = w.bp;
     sa.kt_f32 = f32 ? 1 : 0;
     sa.scan_blocks = (int)(((long)ns * C + 3) / 4);
+    sa.tr_blocks = (int)(ns * C * ((c->dim + 63) / 64));
+    if (c->L >= 2) {
+        sa.w1_master = reinterpret_cast<const float*>(state + sl.M) + c->off[1];
+        sa.w1_copy = ws + w.wr[0];
+        sa.w1_ss = c->P;
+        sa.w1_n = (long)c->din[1] * c->dout[1];
+    }
     if (timed(K_SCAN, st, [&] { return launch_scan(sa, st); }) != hipSuccess) return TM_ERR_HIP;
 
-    for (int ci = 0; ci < C; ++ci) {
-        tm_status rc = run_chunk(c, state, ns, w, ws, tl, k, v, q, y, ci, f32, st);
-        if (rc != TM_OK) return rc;
+    FirstArgs a;
+    memset(&a, 0, sizeof(a));
+    a.u = base_upd(c, state, ns);
+    a.u.bp = w.bp;
+    a.u.cs = reinterpret_cast<const float*>(ws + w.cs);
+    a.u.cs_ss = w.cs_ss;
+    for (int l = 2; l < c->L; ++l) {
+        a.u.at[l] = ws + w.ht[l - 1];
+        a.u.at_ss[l] = w.ht_ss;
     }
-    if (q) {
-        // the last chunk's queries, through the weights it wrote
-        FwdRows fr;
-        fr.nq = b;
-        fr.q = q;
-        fr.tq = (C - 1) * b;
-        fr.nk = 0;
-        fr.k = nullptr;
-        fr.tk = 0;
-        fr.v = nullptr;
-        fr.y = y;
-        tm_status rc = run_forward_layers(c, state, ns, w, ws, tl, fr, f32, false, st);
-        if (rc != TM_OK) return rc;
+    if (c->L >= 2) a.u.at_ss[1] = w.ht_ss;
+    for (int l = 0; l < c->L; ++l) {
+        a.u.dct[l] = ws + w.dct[l];
+        a.u.ddt[l] = ws + w.ddt[l];
+        a.u.dt_ss[l] = w.dt_ss[l];
+    }
+    a.u.wr_ss = c->P;
+    a.dim = c->dim;
+    a.h1 = c->dout[0];
+    a.nb1 = (a.h1 + JW - 1) / JW;
+    a.kt_ss = w.kt_ss;
+    a.dlt2_ss = c->L >= 2 ? w.dlt_ss[1] : 0;
+    a.dlt2 = c->L >= 2 ? (f32 ? (const void*)(ws + w.dlt[1]) : (const void*)(ws + w.dltb)) : nullptr;
+    a.wr_ss = c->P;
+    a.dsl1 = c->L >= 2 ? reinterpret_cast<float*>(ws + w.dsl[0]) : nullptr;
+    a.dsl1_ss = w.dsl_ss;
+    a.coef_ss = w.coef_ss;
+    a.xq = q;
+    a.xk = k;
+    a.tl = tl;
+    a.act = c->L >= 2 ? ws + w.act[0] : nullptr;
+    a.act_ss = w.act_ss;
+    a.ht_ss = w.ht_ss;
+    a.y = y;
+    a.v = v;
+    a.dct1 = ws + w.dct[0];
+    a.ddt1 = ws + w.ddt[0];
+    a.dt1_ss = w.dt_ss[0];
+    const int tile1 = c->tbase[c->L > 1 ? 1 : c->L];
+    const int ntile_rest = c->tbase[c->L] - tile1;
+
+    // while this call is being captured into a graph, the first-layer
+    // blocks and the other layers' update tiles become parallel branches
+    tm_ctx::Fork* fk = nullptr;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    // (measured: joining two hardware queues inside a graph costs ~10 us, more
+    // than running the two kernels back to back, so the fork stays off)
+    if (kForkChunkStep && ntile_rest > 0 && hipStreamIsCapturing(st, &cap) == hipSuccess &&
+        cap == hipStreamCaptureStatusActive) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return TM_ERR_HIP;
+        tm_ctx* mc = const_cast<tm_ctx*>(c);
+        for (auto& f : *mc->forks)
+            if (f.dev == dev) fk = &f;
+        if (!fk) {
+            tm_ctx::Fork f{dev, nullptr, nullptr, nullptr};
+            if (hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking) != hipSuccess) return TM_ERR_HIP;
+            if (hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess) return TM_ERR_HIP;
+            if (hipEventCreateWithFlags(&f.join, hipEventDisableTiming) != hipSuccess) return TM_ERR_HIP;
+            mc->forks->push_back(f);
+            fk = &mc->forks->back();
+        }
+    }
+
+    for (int ci = 0; ci <= C; ++ci) {
+        a.do_update = ci >= 1;
+        a.nq = (q && ci >= 1) ? b : 0;
+        a.nk = ci < C ? b : 0;
+        a.do_fwd = a.nq + a.nk > 0;
+        a.chunk_prev = ci - 1;
+        a.u.chunk = ci - 1;
+        a.tq0 = (ci - 1) * b;
+        a.tk0 = ci * b;
+        if (ci >= 1) {
+            a.kt_prev = ws + w.kt + (size_t)(ci - 1) * c->dim * w.bp * esz;
+            a.cc_prev = reinterpret_cast<const float*>(ws + w.cc) + (ci - 1) * b;
+            a.dc_prev = reinterpret_cast<const float*>(ws + w.dc) + (ci - 1) * b;
+        }
+        a.cc_cur = reinterpret_cast<const float*>(ws + w.cc) + (ci < C ? ci : 0) * b;
+        a.dc_cur = reinterpret_cast<const float*>(ws + w.dc) + (ci < C ? ci : 0) * b;
+        if (c->L >= 2) {
+            a.wr_prev = ws + w.wr[(ci - 1) & 1];
+            a.u.wr_next = ws + w.wr[ci & 1];
+            a.u.at[1] = ws + w.ht1[(ci - 1) & 1];
+            a.ht1 = ws + w.ht1[ci & 1];
+        }
+        if (!a.do_update && !a.do_fwd) continue;
+        const bool upd_rest = a.do_update && ntile_rest > 0;
+        if (upd_rest && fk) {
+            if (hipEventRecord(fk->fork, st) != hipSuccess) return TM_ERR_HIP;
+            if (hipStreamWaitEvent(fk->side, fk->fork, 0) != hipSuccess) return TM_ERR_HIP;
+            if (launch_update_range(a.u, tile1, ntile_rest, (int)ns, f32 ? 1 : 0, fk->side) != hipSuccess)
+                return TM_ERR_HIP;
+            if (hipEventRecord(fk->join, fk->side) != hipSuccess) return TM_ERR_HIP;
+        } else if (upd_rest) {
+            if (timed(K_UPD, st, [&] { return launch_update_range(a.u, tile1, ntile_rest, (int)ns, f32 ? 1 : 0, st); }) !=
+                hipSuccess)
+                return TM_ERR_HIP;
+        }
+        if (timed(K_FIRST, st, [&] { return launch_first(a, (int)ns, f32 ? 1 : 0, st); }) != hipSuccess)
+            return TM_ERR_HIP;
+        if (upd_rest && fk && hipStreamWaitEvent(st, fk->join, 0) != hipSuccess) return TM_ERR_HIP;
+        if (a.do_fwd && c->L >= 2) {
+            FwdRows fr;
+            fr.nq = a.nq;
+            fr.q = q;
+            fr.tq = a.tq0;
+            fr.nk = a.nk;
+            fr.k = k;
+            fr.tk = a.tk0;
+            fr.v = v;
+            fr.y = y;
+            tm_status rc = run_forward_layers(c, state, ns, w, ws, tl, fr, f32, false, st, 1);
+            if (rc != TM_OK) return rc;
+        }
+        if (ci < C && c->L >= 3) {
+            tm_status rc = run_backward(c, state, ns, w, ws, tl, ci, f32, st);
+            if (rc != TM_OK) return rc;
+        }
     }
     return TM_OK;
 }
@@ -521,7 +632,7 @@ extern "C" {
 tm_status tm_create(int dim, int depth, int expansion, int chunk, tm_ctx** out) {
     if (!out) return TM_ERR_INVALID;
     *out = nullptr;
-    if (dim < 32 || dim % 32 != 0 || dim > 16384) return TM_ERR_INVALID;
+    if (dim < 32 || dim % 32 != 0 || dim > 1024) return TM_ERR_INVALID;
     if (depth < 1 || depth > MAXL) return TM_ERR_INVALID;
     if (expansion < 1 || (long)dim * expansion > 65536) return TM_ERR_INVALID;
     if (chunk < 1 || chunk > MAX_CHUNK) return TM_ERR_INVALID;
@@ -531,10 +642,12 @@ tm_status tm_create(int dim, int depth, int expansion, int chunk, tm_ctx** out) 
     c->gmu = new (std::nothrow) std::mutex;
     c->graphs = new (std::nothrow) std::vector<GraphEntry>;
     c->capture_streams = new (std::nothrow) std::vector<std::pair<int, hipStream_t>>;
-    if (!c->gmu || !c->graphs || !c->capture_streams) {
+    c->forks = new (std::nothrow) std::vector<tm_ctx::Fork>;
+    if (!c->gmu || !c->graphs || !c->capture_streams || !c->forks) {
         delete c->gmu;
         delete c->graphs;
         delete c->capture_streams;
+        delete c->forks;
         delete c;
         return TM_ERR_INVALID;
     }
@@ -569,6 +682,12 @@ void tm_destroy(tm_ctx* ctx) {
     for (GraphEntry& e : *ctx->graphs)
         if (e.exec) (void)hipGraphExecDestroy(e.exec);
     for (auto& pr : *ctx->capture_streams) (void)hipStreamDestroy(pr.second);
+    for (auto& f : *ctx->forks) {
+        (void)hipStreamDestroy(f.side);
+        (void)hipEventDestroy(f.fork);
+        (void)hipEventDestroy(f.join);
+    }
+    delete ctx->forks;
     delete ctx->graphs;
     delete ctx->capture_streams;
     delete ctx->gmu;

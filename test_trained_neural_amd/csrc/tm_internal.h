@@ -66,6 +66,7 @@ struct GemmArgs {
     long dsl_ss, dsl_ld;
     float* dlt;
     long dlt_ss, dlt_ld;
+    void* dltb;               // optional operand-type copy of dlt (same layout)
     float* y;
     const void* v;
     int yt0, vt0;
@@ -102,6 +103,57 @@ struct UpdArgs {
     long cs_ss;
     int chunk;
     int* flag;
+    void* wr_next;            // if set: row-major copy (operand type) of layer 1's new weights
+    long wr_ss;
+};
+
+// First-layer part of chunk step c (one launch; it runs concurrently with
+// the update tiles of layers 1.. for chunk c-1).  One workgroup per JW-wide
+// column block of the first weight matrix W_0 (full height):
+//   * if do_update: chunk c-1's update of those columns.  The first layer's
+//     Delta for the columns is formed in place (depth >= 2) from layer 1's
+//     Delta and a row-major copy of layer 1's chunk-start weights, or read
+//     back (depth 1); theta-weighted, reduced against the chunk's keys and
+//     folded into M and S (and the bf16 copy of W_0);
+//   * if do_fwd: chunk c's first-layer forward of [queries of chunk c-1;
+//     keys of chunk c] through the freshly written columns.
+// K is split over the workgroup's 4 waves for the backward and the forward
+// products (partial tiles summed in LDS), so no wave walks a long chain of
+// dependent loads.
+constexpr int JW = 16;
+
+struct FirstArgs {
+    UpdArgs u;                // layers, state, chunk scalars, flag
+    int dim, h1, nb1;
+    int do_update, do_fwd, nq, nk;
+    int chunk_prev;
+    const void* kt_prev;      // keys of chunk c-1 transposed, [dim][bp]
+    long kt_ss;
+    const void* dlt2;         // Delta of layer 1 for chunk c-1 (operand type), [b][dout1]
+    long dlt2_ss;
+    const void* wr_prev;      // layer 1's weights at chunk c-1's start, [h1][dout1]
+    long wr_ss;
+    float* dsl1;              // SiLU'(z) of layer 0: read (chunk c-1), then written (chunk c)
+    long dsl1_ss;
+    const float* cc_prev;     // coefficients of chunk c-1's tokens
+    const float* dc_prev;
+    const float* cc_cur;      // coefficients of chunk c's tokens
+    const float* dc_cur;
+    long coef_ss;
+    const void* xq;           // queries (rows r < nq are tokens tq0 + r)
+    const void* xk;           // keys (rows r >= nq are tokens tk0 + r - nq)
+    TokLayout tl;
+    int tq0, tk0;
+    void* act;                // layer-0 activations of the rows, [2b][h1]
+    long act_ss;
+    void* ht1;                // key rows of act transposed, [h1][bp]
+    long ht_ss;
+    // depth 1: the first layer is the last one
+    float* y;
+    const void* v;
+    void* dct1;               // (c Delta)^T, (d Delta)^T of layer 0, [h1][bp]
+    void* ddt1;
+    long dt1_ss;
 };
 
 // Per call: the coefficient scan of every (stream, chunk) and the keys of
@@ -124,6 +176,11 @@ struct ScanArgs {
     void* kt;
     int bp, kt_f32;
     int scan_blocks;          // blocks [0, scan_blocks) scan, the rest transpose
+    // refresh of the row-major copy of layer 1's weights (depth >= 2)
+    const float* w1_master;   // M of layer 1, stream stride w1_ss
+    void* w1_copy;            // operand-type copy, same layout
+    long w1_ss, w1_n;         // per-stream stride, elements per stream
+    int tr_blocks;            // transpose blocks; copy blocks follow them
 };
 
 // ---- launchers (tm_kernels.hip) ----
@@ -133,6 +190,9 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
 hipError_t launch_fwd(const GemmArgs& g, int ns, int f32, hipStream_t st);
 hipError_t launch_bwd(const GemmArgs& g, int ns, int f32, hipStream_t st);
 hipError_t launch_update(const UpdArgs& u, int ntiles, int ns, int f32, hipStream_t st);
+hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st);
+// update tiles [tile0, tile0 + ntiles) of every stream
+hipError_t launch_update_range(const UpdArgs& u, int tile0, int ntiles, int ns, int f32, hipStream_t st);
 hipError_t launch_init(float* M, float* S, const float* init, long P, int H, int ns,
                        hipStream_t st);
 hipError_t launch_shadow(const UpdArgs& u, int ntiles, int ns, hipStream_t st);

@@ -132,11 +132,15 @@ __device__ __forceinline__ float gemm_store(const GemmArgs& g, int s, int r, int
         }
         const float vv = load1<OP>(g.v, tok_off(g.tl, s, g.vt0 + r - g.n0) + c);
         const float dl = 2.0f * (z - vv);
-        g.dlt[(long)s * g.dlt_ss + (long)(r - g.n0) * g.dlt_ld + c] = dl;
+        const long o = (long)s * g.dlt_ss + (long)(r - g.n0) * g.dlt_ld + c;
+        g.dlt[o] = dl;
+        if (g.dltb) reinterpret_cast<OP*>(g.dltb)[o] = (OP)dl;
         return dl;
     }
     const float dl = z * g.dsl[(long)s * g.dsl_ss + (long)r * g.dsl_ld + c];
-    g.dlt[(long)s * g.dlt_ss + (long)r * g.dlt_ld + c] = dl;
+    const long o = (long)s * g.dlt_ss + (long)r * g.dlt_ld + c;
+    g.dlt[o] = dl;
+    if (g.dltb) reinterpret_cast<OP*>(g.dltb)[o] = (OP)dl;
     return dl;
 }
 
@@ -275,14 +279,15 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
 // Pick the column width and wave count of one product: enough workgroups to
 // cover the chip (about 192 tiles of 64 rows, ideally at least 3 steps per
 // wave), wider tiles first so the activations are re-read from L2 less often.
-static void pick(const GemmArgs& g, int ns, int& nr, int& w) {
+static void pick(const GemmArgs& g, int ns, int& nr, int& w, bool allow16) {
     const int nsteps = g.K >> 5;
     const long nrt = (g.nrows + GEMM_RT - 1) / GEMM_RT;
     nr = 4;
     w = 4;
     auto wgs = [&](int nr_) { return (long)((g.N + 16 * nr_ - 1) / (16 * nr_)) * nrt * ns; };
-    if (nsteps >= 8 * 4) w = 8;
+    if (nsteps >= 8 * 3) w = 8;
     while (wgs(nr) < 192 && nr > 1) nr >>= 1;
+    (void)allow16;
 }
 
 template <class OP, class AT, class BT, bool BKC, int NR, int W, int PF>
@@ -296,8 +301,12 @@ template <class OP, class AT, class BT, bool BKC, int PF>
 static hipError_t launch_gemm(const GemmArgs& g, int ns, hipStream_t st) {
     if (g.nrows <= 0 || g.N <= 0) return hipSuccess;
     int nr, w;
-    pick(g, ns, nr, w);
-    if (w == 8) {
+    // 16-wave workgroups cap a wave at 128 registers: only the narrowest
+    // tile with 16-bit operands in storage fits the prefetch ring there
+    pick(g, ns, nr, w, sizeof(AT) == 2 && sizeof(BT) == 2);
+    if (w == 16) {
+        launch_one<OP, AT, BT, BKC, 1, 16, PF>(g, ns, st);
+    } else if (w == 8) {
         if (nr == 4) launch_one<OP, AT, BT, BKC, 4, 8, PF>(g, ns, st);
         else if (nr == 2) launch_one<OP, AT, BT, BKC, 2, 8, PF>(g, ns, st);
         else launch_one<OP, AT, BT, BKC, 1, 8, PF>(g, ns, st);
@@ -311,7 +320,7 @@ static hipError_t launch_gemm(const GemmArgs& g, int ns, hipStream_t st) {
 
 hipError_t launch_fwd(const GemmArgs& g, int ns, int f32, hipStream_t st) {
     if (f32) return launch_gemm<float, float, float, false, 2>(g, ns, st);
-    return launch_gemm<bf16, bf16, bf16, true, 3>(g, ns, st);
+    return launch_gemm<bf16, bf16, bf16, true, 4>(g, ns, st);
 }
 
 hipError_t launch_bwd(const GemmArgs& g, int ns, int f32, hipStream_t st) {
@@ -347,7 +356,22 @@ __device__ void transpose_keys(const ScanArgs& a, long blk) {
     }
 }
 
+template <class T>
+__device__ void copy_layer1(const ScanArgs& a, long blk) {
+    const long n = a.w1_n;
+    for (long e = blk * 256 + threadIdx.x; e < n * a.ns; e += 1024L * 256) {
+        const long s = e / n, i = e - s * n;
+        reinterpret_cast<T*>(a.w1_copy)[s * a.w1_ss + i] = (T)a.w1_master[s * a.w1_ss + i];
+    }
+}
+
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+    if ((int)blockIdx.x >= a.scan_blocks + a.tr_blocks) {
+        const long blk = (long)blockIdx.x - a.scan_blocks - a.tr_blocks;
+        if (a.kt_f32) copy_layer1<float>(a, blk);
+        else copy_layer1<bf16>(a, blk);
+        return;
+    }
     if ((int)blockIdx.x >= a.scan_blocks) {
         const long blk = (long)blockIdx.x - a.scan_blocks;
         if (a.kt_f32) transpose_keys<float>(a, blk);
@@ -406,8 +430,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
     long waves = (long)a.ns * a.C;
     if (waves == 0) return hipSuccess;
-    const long tr = (long)a.ns * a.C * ((a.ktl.d + 63) / 64);
-    dim3 grid((unsigned)(a.scan_blocks + tr));
+    const long cp = a.w1_copy ? 1024 : 0;
+    dim3 grid((unsigned)(a.scan_blocks + a.tr_blocks + cp));
     hipLaunchKernelGGL(scan_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
@@ -436,14 +460,9 @@ __device__ __forceinline__ typename Frag<OP>::T tok8(const OP* p, int t0, int b,
 }
 
 template <class OP>
-__global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
+__device__ void update_tile(const UpdArgs& u, int s, int tile, float (*UM)[65], float (*US)[65]) {
     typedef typename Frag<OP>::T F;
-    __shared__ float UM[64][65];
-    __shared__ float US[64][65];
-
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int s = blockIdx.y;
-    int tile = blockIdx.x;
     int l = 0;
     while (l + 1 < u.L && tile >= u.tbase[l + 1]) ++l;
     tile -= u.tbase[l];
@@ -451,24 +470,6 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
     const int din = u.din[l], dout = u.dout[l];
     const int i0 = ti * 64, j0 = tj * 64;
     const int b = u.b, bp = u.bp;
-
-    // this tile's M and S first: their latency overlaps the work below
-    float* Mp = u.M + (long)s * u.P + u.off[l];
-    float* Sp = u.S + (long)s * u.P + u.off[l];
-    f32x4 mreg[4], sreg[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int idx = tid + 256 * q;
-        const int gi = i0 + (idx >> 4), gj = j0 + (idx & 15) * 4;
-        if (gi < din && gj < dout) {
-            const long o = (long)gi * dout + gj;
-            mreg[q] = *reinterpret_cast<const f32x4*>(Mp + o);
-            sreg[q] = *reinterpret_cast<const f32x4*>(Sp + o);
-        } else {
-            mreg[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            sreg[q] = mreg[q];
-        }
-    }
 
     // U_M, U_S on the matrix cores: 4 waves as 2 x 2, 32 x 32 each
     const int wi = wave & 1, wj = wave >> 1;
@@ -487,30 +488,59 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
         bok[m] = bj[m] < dout;
         if (!bok[m]) bj[m] = 0;
     }
+    // operand fragments first (vector loads complete in issue order, so
+    // the matrix work below waits only for these), then this tile's M and
+    // S, whose latency overlaps the matrix work and the LDS exchange
+    F fa[2][2], fc[2][2], fd[2][2];   // [k step][block]
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int t0 = ks * 32 + kofs;
+        const bool full = t0 + 8 <= b;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            fa[ks][m] = zero_frag<OP>();
+            fc[ks][m] = zero_frag<OP>();
+            fd[ks][m] = zero_frag<OP>();
+            if (ks * 32 < bp) {
+                fa[ks][m] = tok8<OP>(A + (long)ai[m] * bp + t0, t0, b, full);
+                fc[ks][m] = tok8<OP>(Bc + (long)bj[m] * bp + t0, t0, b, full);
+                fd[ks][m] = tok8<OP>(Bd + (long)bj[m] * bp + t0, t0, b, full);
+            }
+        }
+    }
+    float* Mp = u.M + (long)s * u.P + u.off[l];
+    float* Sp = u.S + (long)s * u.P + u.off[l];
+    f32x4 mreg[4], sreg[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int idx = tid + 256 * q;
+        const int gi = i0 + (idx >> 4), gj = j0 + (idx & 15) * 4;
+        if (gi < din && gj < dout) {
+            const long o = (long)gi * dout + gj;
+            mreg[q] = *reinterpret_cast<const f32x4*>(Mp + o);
+            sreg[q] = *reinterpret_cast<const f32x4*>(Sp + o);
+        } else {
+            mreg[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            sreg[q] = mreg[q];
+        }
+    }
     f32x4 am[2][2], as[2][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int n = 0; n < 2; ++n) { am[m][n] = (f32x4){0.f, 0.f, 0.f, 0.f}; as[m][n] = am[m][n]; }
-    for (int k0 = 0; k0 < bp; k0 += 32) {
-        const int t0 = k0 + kofs;
-        const bool full = t0 + 8 <= b;
-        F a[2], bc[2], bd[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        if (ks * 32 >= bp) break;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            a[m] = tok8<OP>(A + (long)ai[m] * bp + t0, t0, b, full);
-            if (!aok[m]) a[m] = zero_frag<OP>();
+            const F av = aok[m] ? fa[ks][m] : zero_frag<OP>();
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                mma(am[m][n], av, bok[n] ? fc[ks][n] : zero_frag<OP>());
+                mma(as[m][n], av, bok[n] ? fd[ks][n] : zero_frag<OP>());
+            }
         }
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            bc[n] = tok8<OP>(Bc + (long)bj[n] * bp + t0, t0, b, full);
-            bd[n] = tok8<OP>(Bd + (long)bj[n] * bp + t0, t0, b, full);
-            if (!bok[n]) { bc[n] = zero_frag<OP>(); bd[n] = zero_frag<OP>(); }
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int n = 0; n < 2; ++n) { mma(am[m][n], a[m], bc[n]); mma(as[m][n], a[m], bd[n]); }
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -546,6 +576,11 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
             }
             *reinterpret_cast<f32x4*>(Mp + o) = mn;
             *reinterpret_cast<f32x4*>(Sp + o) = sn;
+            if (l == 1 && u.wr_next) {
+                OP* wr = reinterpret_cast<OP*>(u.wr_next) + (long)s * u.wr_ss + o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wr[e] = (OP)mn[e];
+            }
         }
     }
     __syncthreads();
@@ -563,10 +598,353 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
     if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
 }
 
+template <class OP>
+__global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
+    __shared__ float UM[64][65];
+    __shared__ float US[64][65];
+    update_tile<OP>(u, blockIdx.y, blockIdx.x, UM, US);
+}
+
 hipError_t launch_update(const UpdArgs& u, int ntiles, int ns, int f32, hipStream_t st) {
     dim3 grid(ntiles, ns);
     if (f32) hipLaunchKernelGGL(update_kernel<float>, grid, dim3(256), 0, st, u);
     else hipLaunchKernelGGL(update_kernel<bf16>, grid, dim3(256), 0, st, u);
+    return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// First-layer part of a chunk step (see FirstArgs).
+
+constexpr int WPAD = 8;     // LDS row padding (elements)
+constexpr int RPAD = 1;     // LDS row padding of the partial-sum tiles (floats)
+constexpr int FW = 8;       // waves of a first-layer workgroup
+
+static size_t first_lds_bytes(int dim, int bp, int f32) {
+    const size_t e = f32 ? 4 : 2;
+    return (size_t)JW * (dim + WPAD) * e + 2 * (size_t)JW * (bp + WPAD) * e +
+           (size_t)FW * 128 * (JW + RPAD) * 4;
+}
+
+// Prefetch depths (in K steps or row blocks) of the first-layer workgroup:
+// everything a wave needs is requested at kernel start when it fits the
+// register file, so each phase waits for at most one round of memory.
+template <class OP> struct FirstDepth;
+template <> struct FirstDepth<bf16> { static constexpr int A = 2, B = 4, C = 2; };
+template <> struct FirstDepth<float> { static constexpr int A = 1, B = 2, C = 1; };
+
+template <class OP>
+__global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
+    typedef typename Frag<OP>::T F;
+    constexpr int PA = FirstDepth<OP>::A, PB = FirstDepth<OP>::B, PC = FirstDepth<OP>::C;
+    constexpr int NT = FW * 64;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const UpdArgs& u = a.u;
+    const int s = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kofs = 8 * (lane >> 4), g4 = 4 * (lane >> 4);
+    const int d = a.dim, h1 = a.h1, b = u.b, bp = u.bp;
+    const int j0 = blockIdx.x * JW;
+    const int jl = lane & 15, j = j0 + jl;   // the lane's column in B fragments / results
+    const bool jok = j < h1;
+    const int WP = d + WPAD, DP = bp + WPAD, RP = JW + RPAD;
+    OP* Wn = reinterpret_cast<OP*>(lds);   // [JW][WP]: the block's columns of W_0, K-contiguous
+    OP* DcT = Wn + JW * WP;                 // [JW][DP]: (c Delta_0)^T of chunk c-1
+    OP* DdT = DcT + JW * DP;
+    float* red = reinterpret_cast<float*>(DdT + JW * DP);   // [FW][rows][RP] partial tiles
+    float* M0 = u.M + (long)s * u.P;
+    float* S0 = u.S + (long)s * u.P;
+    bf16* Wt0 = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P;
+    const OP* kt = reinterpret_cast<const OP*>(a.kt_prev) + (long)s * a.kt_ss;
+    const bool upd = a.do_update;
+    const bool bwd = upd && u.L >= 2;
+    bool bad = false;
+
+    // ================= every load of the kernel, in consumption order =================
+    // (1) the in-place backward's operands: Delta_1 rows (4 token blocks) and
+    //     the lane's column of W_1, K split over the waves
+    const int K1 = bwd ? u.dout[1] : 32;
+    const int nsA = K1 >> 5, qA = (nsA + FW - 1) / FW;
+    const int kbA = wave * qA, keA = min(nsA, kbA + qA), klA = max(keA - 1, 0);
+    const OP* Ad[4];
+    bool tok[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int t = 16 * m + (lane & 15);
+        tok[m] = t < b;
+        Ad[m] = bwd ? reinterpret_cast<const OP*>(a.dlt2) + (long)s * a.dlt2_ss + (long)(tok[m] ? t : 0) * K1 + kofs
+                    : nullptr;
+    }
+    const OP* Bw = bwd ? reinterpret_cast<const OP*>(a.wr_prev) + (long)s * a.wr_ss + (long)(jok ? j : 0) * K1 + kofs
+                       : nullptr;
+    F ra[PA][4], rb[PA];
+    if (bwd) {
+#pragma unroll
+        for (int p = 0; p < PA; ++p) {
+            const int k0 = min(kbA + p, klA) << 5;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) ra[p][m] = cvt<OP>(ld8(Ad[m] + k0));
+            rb[p] = cvt<OP>(ld8(Bw + k0));
+        }
+    }
+    // (2) the backward epilogue's SiLU' and coefficients (2 elements per thread)
+    constexpr int EA = 64 * JW / NT;
+    float sl[EA], cv[EA], dv[EA];
+    if (bwd) {
+#pragma unroll
+        for (int q = 0; q < EA; ++q) {
+            const int idx = tid + NT * q, t = idx / JW, jj = j0 + idx % JW;
+            const bool ok = t < b && jj < h1;
+            sl[q] = ok ? a.dsl1[(long)s * a.dsl1_ss + (long)t * h1 + jj] : 0.f;
+            cv[q] = ok ? a.cc_prev[(long)s * a.coef_ss + t] : 0.f;
+            dv[q] = ok ? a.dc_prev[(long)s * a.coef_ss + t] : 0.f;
+        }
+    }
+    // (3) the update's row blocks of this wave: keys^T fragments, M and S
+    const int nrb = d >> 4;
+    const int mineB = upd ? (nrb - wave + FW - 1) / FW : 0;
+    F kf[PB][2];
+    float mr[PB][4], sr[PB][4];
+    auto load_rb = [&](int p, int n) {
+        const int ib = 16 * (wave + FW * min(n, mineB - 1));
+        const int ia = ib + (lane & 15);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            kf[p][ks] = (ks * 32 < bp) ? cvt<OP>(ld8(kt + (long)ia * bp + ks * 32 + kofs)) : zero_frag<OP>();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const long o = (long)(ib + g4 + e) * h1 + (jok ? j : 0);
+            mr[p][e] = M0[o];
+            sr[p][e] = S0[o];
+        }
+    };
+    if (mineB > 0) {
+#pragma unroll
+        for (int p = 0; p < PB; ++p) load_rb(p, p);
+    }
+    // (4) the forward's rows (all 16-row blocks), K = dim split over the waves
+    const int R = a.nq + a.nk;
+    const int nrow = (R + 15) >> 4;
+    const int nsC = d >> 5, qC = (nsC + FW - 1) / FW;
+    const int kbC = wave * qC, keC = min(nsC, kbC + qC), klC = max(keC - 1, 0);
+    const OP* Ax[8];
+    bool rok[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        int r = 16 * m + (lane & 15);
+        rok[m] = r < R;
+        if (!rok[m]) r = R > 0 ? R - 1 : 0;
+        Ax[m] = nullptr;
+        if (R > 0) {
+            const long off = r < a.nq ? tok_off(a.tl, s, a.tq0 + r) : tok_off(a.tl, s, a.tk0 + r - a.nq);
+            Ax[m] = reinterpret_cast<const OP*>(r < a.nq ? a.xq : a.xk) + off + kofs;
+        }
+    }
+    F rx[PC][8];
+    if (a.do_fwd) {
+#pragma unroll
+        for (int p = 0; p < PC; ++p)
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+                if (m < nrow) rx[p][m] = cvt<OP>(ld8(Ax[m] + (min(kbC + p, klC) << 5)));
+    }
+
+    // ================= chunk c-1's update of the block's columns =================
+    if (upd) {
+        if (bwd) {
+            // Delta_0 = (Delta_1 W_1^T) * SiLU'(z_0): 64 tokens x JW columns
+            f32x4 acc[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            for (int k = kbA; k < kbA + qA; k += PA) {
+#pragma unroll
+                for (int p = 0; p < PA; ++p) {
+                    const bool live = k + p < keA && k + p < kbA + qA;
+                    const F bv = (live && jok) ? rb[p] : zero_frag<OP>();
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) mma(acc[m], tok[m] ? ra[p][m] : zero_frag<OP>(), bv);
+                    if (k + PA < kbA + qA) {   // wave-uniform: ring refill for long K
+                        const int kn = min(k + p + PA, klA) << 5;
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) ra[p][m] = cvt<OP>(ld8(Ad[m] + kn));
+                        rb[p] = cvt<OP>(ld8(Bw + kn));
+                    }
+                }
+            }
+            float* mine = red + wave * 64 * RP;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mine[(16 * m + g4 + e) * RP + jl] = acc[m][e];
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < EA; ++q) {
+                const int idx = tid + NT * q, t = idx / JW, cl = idx % JW;
+                if (t >= bp) continue;
+                float z = 0.f;
+#pragma unroll
+                for (int w = 0; w < FW; ++w) z += red[(w * 64 + t) * RP + cl];
+                const float dl = z * sl[q];
+                DcT[cl * DP + t] = (OP)(cv[q] * dl);
+                DdT[cl * DP + t] = (OP)(dv[q] * dl);
+            }
+        } else {
+            // depth 1: the previous chunk's forward left them in memory (tokens
+            // past the chunk are padding nobody wrote: zero them here)
+            for (int idx = tid; idx < JW * bp; idx += NT) {
+                const int cl = idx / bp, t = idx - cl * bp;
+                const int jj = j0 + cl;
+                const bool ok = jj < h1 && t < b;
+                const long o = (long)s * a.dt1_ss + (long)(ok ? jj : 0) * bp + (ok ? t : 0);
+                DcT[cl * DP + t] = ok ? reinterpret_cast<const OP*>(a.dct1)[o] : (OP)0.0f;
+                DdT[cl * DP + t] = ok ? reinterpret_cast<const OP*>(a.ddt1)[o] : (OP)0.0f;
+            }
+        }
+        __syncthreads();
+
+        // U = K^T diag(c) Delta_0 and the momentum / forgetting write, 16-row
+        // blocks (block w, w+FW, ... for wave w)
+        const float* csp = u.cs + (long)s * u.cs_ss + (long)a.chunk_prev * 4;
+        const float pa = csp[0], pe = csp[1], s0 = csp[2];
+        F bc[2], bd[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bool on = ks * 32 < bp;
+            bc[ks] = on ? *reinterpret_cast<const F*>(&DcT[jl * DP + ks * 32 + kofs]) : zero_frag<OP>();
+            bd[ks] = on ? *reinterpret_cast<const F*>(&DdT[jl * DP + ks * 32 + kofs]) : zero_frag<OP>();
+        }
+        for (int n = 0; n < mineB; n += PB) {
+#pragma unroll
+            for (int p = 0; p < PB; ++p) {
+                if (n + p < mineB) {   // wave-uniform
+                    const int ib = 16 * (wave + FW * (n + p));
+                    f32x4 um = (f32x4){0.f, 0.f, 0.f, 0.f}, us = um;
+                    mma(um, kf[p][0], bc[0]);
+                    mma(us, kf[p][0], bd[0]);
+                    mma(um, kf[p][1], bc[1]);
+                    mma(us, kf[p][1], bd[1]);
+                    float mn[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float sn = pe * sr[p][e] - us[e];
+                        mn[e] = pa * mr[p][e] + s0 * sr[p][e] - um[e];
+                        bad |= jok && (!__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn));
+                        if (jok) {
+                            const long o = (long)(ib + g4 + e) * h1 + j;
+                            M0[o] = mn[e];
+                            S0[o] = sn;
+                        }
+                        Wn[jl * WP + ib + g4 + e] = (OP)mn[e];
+                    }
+                    if (jok) {
+                        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                        *reinterpret_cast<bf16x4*>(Wt0 + (long)j * d + ib + g4) =
+                            (bf16x4){(bf16)mn[0], (bf16)mn[1], (bf16)mn[2], (bf16)mn[3]};
+                    }
+                }
+                if (n + PB < mineB) load_rb(p, n + p + PB);   // wave-uniform refill
+            }
+        }
+    } else if (a.do_fwd) {
+        // first chunk of the call: the block's columns of the current W_0
+        if (sizeof(OP) == 2) {
+            for (int idx = tid; idx < JW * (d >> 3); idx += NT) {
+                const int cl = idx / (d >> 3), i = (idx - cl * (d >> 3)) * 8;
+                const int jj = j0 + cl;
+                bf16x8 w = jj < h1 ? *reinterpret_cast<const bf16x8*>(Wt0 + (long)jj * d + i) : zero_frag<bf16>();
+                *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(Wn) + cl * WP + i) = w;
+            }
+        } else {
+            for (int idx = tid; idx < JW * d; idx += NT) {
+                const int i = idx / JW, cl = idx - i * JW;
+                const int jj = j0 + cl;
+                Wn[cl * WP + i] = jj < h1 ? (OP)M0[(long)i * h1 + jj] : (OP)0.0f;
+            }
+        }
+    }
+    if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
+    if (!a.do_fwd) return;
+    __syncthreads();
+
+    // ================= chunk c's first-layer forward =================
+    {
+        f32x4 acc[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int k = kbC; k < kbC + qC; k += PC) {
+#pragma unroll
+            for (int p = 0; p < PC; ++p) {
+                const bool live = k + p < keC && k + p < kbC + qC;
+                const int k0 = min(k + p, klC) << 5;
+                F bv = *reinterpret_cast<const F*>(&Wn[jl * WP + k0 + kofs]);
+                if (!live) bv = zero_frag<OP>();
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    if (m < nrow) mma(acc[m], rok[m] ? rx[p][m] : zero_frag<OP>(), bv);
+                if (k + PC < kbC + qC) {   // wave-uniform ring refill
+                    const int kn = min(k + p + PC, klC) << 5;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m)
+                        if (m < nrow) rx[p][m] = cvt<OP>(ld8(Ax[m] + kn));
+                }
+            }
+        }
+        float* mine = red + wave * 128 * RP;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            if (m < nrow)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mine[(16 * m + g4 + e) * RP + jl] = acc[m][e];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < R * JW; idx += NT) {
+        const int r = idx / JW, cl = idx - r * JW, jj = j0 + cl;
+        if (jj >= h1) continue;
+        float z = 0.f;
+#pragma unroll
+        for (int w = 0; w < FW; ++w) z += red[(w * 128 + r) * RP + cl];
+        if (u.L >= 2) {
+            const float sg = sigmoid(z);
+            const OP hv = (OP)(z * sg);
+            reinterpret_cast<OP*>(a.act)[(long)s * a.act_ss + (long)r * h1 + jj] = hv;
+            if (r >= a.nq) {
+                const int t = r - a.nq;
+                a.dsl1[(long)s * a.dsl1_ss + (long)t * h1 + jj] = sg * (1.0f + z * (1.0f - sg));
+                reinterpret_cast<OP*>(a.ht1)[(long)s * a.ht_ss + (long)jj * bp + t] = hv;
+            }
+        } else if (r < a.nq) {
+            a.y[tok_off(a.tl, s, a.tq0 + r) + jj] = z;
+        } else {
+            const int t = r - a.nq;
+            const float vv = load1<OP>(a.v, tok_off(a.tl, s, a.tk0 + t) + jj);
+            const float dl = 2.0f * (z - vv);
+            const long o = (long)s * a.dt1_ss + (long)jj * bp + t;
+            reinterpret_cast<OP*>(a.dct1)[o] = (OP)(a.cc_cur[(long)s * a.coef_ss + t] * dl);
+            reinterpret_cast<OP*>(a.ddt1)[o] = (OP)(a.dc_cur[(long)s * a.coef_ss + t] * dl);
+        }
+    }
+}
+
+hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st) {
+    dim3 grid(a.nb1, ns);
+    const size_t lds = first_lds_bytes(a.dim, a.u.bp, f32);
+    if (f32) hipLaunchKernelGGL(first_layer_kernel<float>, grid, dim3(FW * 64), lds, st, a);
+    else hipLaunchKernelGGL(first_layer_kernel<bf16>, grid, dim3(FW * 64), lds, st, a);
+    return hipGetLastError();
+}
+
+template <class OP>
+__global__ __launch_bounds__(256) void update_range_kernel(UpdArgs u, int tile0) {
+    __shared__ float UM[64][65];
+    __shared__ float US[64][65];
+    update_tile<OP>(u, blockIdx.y, tile0 + blockIdx.x, UM, US);
+}
+
+hipError_t launch_update_range(const UpdArgs& u, int tile0, int ntiles, int ns, int f32, hipStream_t st) {
+    if (ntiles <= 0) return hipSuccess;
+    dim3 grid(ntiles, ns);
+    if (f32) hipLaunchKernelGGL(update_range_kernel<float>, grid, dim3(256), 0, st, u, tile0);
+    else hipLaunchKernelGGL(update_range_kernel<bf16>, grid, dim3(256), 0, st, u, tile0);
     return hipGetLastError();
 }
 

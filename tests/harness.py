@@ -101,15 +101,16 @@ def compare_state(wl: I.Workload, gpu_state, ref_state):
     """(rel err of M, rel err of S): the worst over streams and layers of
     ||X_gpu - X_ref||_F / ||X_ref||_F per weight matrix."""
     P = wl.params
-    em = es = 0.0
+    em, es = [], []
     for s in range(ref_state.shape[0]):
         off = 0
         for din, dout in wl.layer_dims():
             n = din * dout
-            em = max(em, relerr(gpu_state[s, off:off + n], ref_state[s, off:off + n]))
-            es = max(es, relerr(gpu_state[s, P + off:P + off + n], ref_state[s, P + off:P + off + n]))
+            em.append(relerr(gpu_state[s, off:off + n], ref_state[s, off:off + n]))
+            es.append(relerr(gpu_state[s, P + off:P + off + n], ref_state[s, P + off:P + off + n]))
             off += n
-    return em, es
+    # np.max propagates NaN (a NaN anywhere must fail the comparison)
+    return float(np.max(em)), float(np.max(es))
 
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_create_validation():
-    for args in [(48, 2, 4, 64), (0, 2, 4, 64), (64, 0, 4, 64), (64, 9, 4, 64), (64, 2, 0, 64),
+    for args in [(48, 2, 4, 64), (2048, 2, 4, 64), (0, 2, 4, 64), (64, 0, 4, 64), (64, 9, 4, 64), (64, 2, 0, 64),
                  (64, 2, 4, 0), (64, 2, 4, 65)]:
         with pytest.raises(T.TMError) as e:
             T.tm_create(*args)
