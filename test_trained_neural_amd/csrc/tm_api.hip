@@ -66,9 +66,13 @@ StateLayout state_layout(const tm_ctx* c, long ns) {
     return s;
 }
 
+// Workspace of one call.  Every matrix-instruction operand that one kernel
+// leaves for another is stored fragment-packed (pk() in tm_internal.h),
+// sized in 4-byte elements so either operand type fits.
 struct WsLayout {
-    size_t cc, dc, cs, act[MAXL], dsl[MAXL], dlt[MAXL], dltb, kt, ht[MAXL], dct[MAXL], ddt[MAXL], ht1[2], wr[2], ret[2], total;
-    long coef_ss, cs_ss, act_ss, dsl_ss, dlt_ss[MAXL], kt_ss, ht_ss, dt_ss[MAXL], ret_ss, ret_rows;
+    size_t cc, dc, cs, act[MAXL], dsl[MAXL], dlp[MAXL], kt, xk, xq, ht[MAXL], dct[MAXL], ddt[MAXL], ht1[2],
+        wr[2], ret[2], total;
+    long coef_ss, cs_ss, act_ss, dsl_ss, dlp_ss[MAXL], kt_ss, x_ss, xc, ht_ss, dt_ss[MAXL], wr_ss, ret_ss, ret_rows;
     int bp, C;
 };
 
@@ -82,22 +86,29 @@ WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
     w.dc = o; o += al256((size_t)ns * T * 4);
     w.cs_ss = C * 4;
     w.cs = o; o += al256((size_t)ns * C * 16);
-    w.act_ss = 2 * b * h;
+    // hidden layers: activations of [queries of chunk c-1; keys of chunk c]
+    // (packed [2b][h]) and SiLU'(z) of the key rows (row-major [b][h])
+    w.act_ss = pk_size(2 * b, h);
     w.dsl_ss = b * h;
     for (int l = 0; l + 1 < c->L; ++l) {
         w.act[l] = o; o += al256((size_t)ns * w.act_ss * 4);
         w.dsl[l] = o; o += al256((size_t)ns * w.dsl_ss * 4);
     }
-    for (int l = 0; l < c->L; ++l) {
-        w.dlt_ss[l] = b * c->dout[l];
-        w.dlt[l] = o; o += al256((size_t)ns * w.dlt_ss[l] * 4);
+    // Delta of layers 1.. (packed [b][dout]; layer 0's is formed in place)
+    for (int l = 1; l < c->L; ++l) {
+        w.dlp_ss[l] = pk_size(b, c->dout[l]);
+        w.dlp[l] = o; o += al256((size_t)ns * w.dlp_ss[l] * 4);
     }
-    // transposed operands of the update: rows of bp tokens (fp32-sized so
-    // either operand type fits)
+    // transposed operands of the update: packed [rows][bp]
     w.bp = (int)((b + 31) / 32 * 32);
     w.C = (int)C;
     w.kt_ss = C * c->dim * w.bp;
     w.kt = o; o += al256((size_t)ns * w.kt_ss * 4);
+    // every chunk's key and query rows, packed [b][dim]
+    w.xc = pk_size(b, c->dim);
+    w.x_ss = C * w.xc;
+    w.xk = o; o += al256((size_t)ns * w.x_ss * 4);
+    w.xq = o; o += al256((size_t)ns * w.x_ss * 4);
     w.ht_ss = h * w.bp;
     for (int l = 0; l + 1 < c->L; ++l) {
         w.ht[l] = o; o += al256((size_t)ns * w.ht_ss * 4);
@@ -107,21 +118,21 @@ WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
         w.dct[l] = o; o += al256((size_t)ns * w.dt_ss[l] * 4);
         w.ddt[l] = o; o += al256((size_t)ns * w.dt_ss[l] * 4);
     }
-    // first layer's transposed key-row activations, alternating between the
-    // chunk being written and the chunk being reduced; and two row-major
+    // the first layer's transposed key-row activations, alternating between
+    // the chunk being written and the chunk being reduced; and two packed
     // copies of layer 1's weights (chunk start of the chunk being reduced,
-    // and its result), both with stream stride P
+    // and its result)
     for (int i = 0; i < 2; ++i) {
         w.ht1[i] = o; o += al256((size_t)ns * w.ht_ss * 4);
     }
+    w.wr_ss = c->L > 1 ? (long)c->din[1] * c->dout[1] : 0;
     for (int i = 0; i < 2; ++i) {
-        w.wr[i] = o; o += al256((size_t)ns * c->P * 4);
+        w.wr[i] = o; o += al256((size_t)ns * w.wr_ss * 4);
     }
-    // operand-type copy of layer 1's Delta (the first layer's in-place backward)
-    w.dltb = o; o += al256((size_t)ns * w.dlt_ss[c->L > 1 ? 1 : 0] * 4);
     size_t fwd_total = o;
+    // retrieve: ping-pong activations of up to RET_ROWS query rows (packed)
     w.ret_rows = T < RET_ROWS ? T : RET_ROWS;
-    w.ret_ss = w.ret_rows * h;
+    w.ret_ss = pk_size(w.ret_rows, h);
     size_t r = 0;
     if (c->L > 1) {
         w.ret[0] = r; r += al256((size_t)ns * w.ret_ss * 4);
@@ -325,7 +336,6 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
     StateLayout sl = state_layout(c, ns);
     const int rows = fr.nq + fr.nk;
     if (rows == 0) return TM_OK;
-    const int esz = f32 ? 4 : 2;
     for (int l = l_begin; l < c->L; ++l) {
         GemmArgs g;
         memset(&g, 0, sizeof(g));
@@ -335,13 +345,13 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
         g.tl = tl;
         g.n0 = fr.nq;
         if (l == 0) {
-            g.amode = 0;
+            g.amode = A_TOKENS;
             g.a0 = fr.q;
             g.at0 = fr.tq;
             g.a1 = fr.k;
             g.at1 = fr.tk;
         } else {
-            g.amode = 1;
+            g.amode = A_PACKED;
             if (retrieve) {
                 g.a0 = ws + w.ret[(l - 1) & 1];
                 g.a_ss = w.ret_ss;
@@ -349,18 +359,17 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
                 g.a0 = ws + w.act[l - 1];
                 g.a_ss = w.act_ss;
             }
-            g.a_ld = c->hidden;
         }
         if (f32) {
+            // fp32 operands straight from the fp32 master, row-major [din][dout]
+            g.bmode = B_STRIDED;
             g.b = state + sl.M + (size_t)c->off[l] * 4;
             g.b_ss = c->P;
-            g.b_ldn = 1;
-            g.b_ldk = c->dout[l];
+            g.b_ld = c->dout[l];
         } else {
+            g.bmode = B_PACKED;
             g.b = state + sl.Wt + (size_t)c->off[l] * 2;
             g.b_ss = c->P;
-            g.b_ldn = c->din[l];
-            g.b_ldk = 1;
         }
         if (l + 1 < c->L) {
             g.epi = EPI_HIDDEN;
@@ -379,30 +388,26 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
                 g.tr_ss = w.ht_ss;
                 g.bp = w.bp;
             }
-            g.act_ld = c->hidden;
         } else {
             g.epi = EPI_OUT;
             g.y = fr.y;
             g.yt0 = fr.tq;
             g.v = fr.v;
             g.vt0 = fr.tk;
-            if (!retrieve) {
-                g.dlt = reinterpret_cast<float*>(ws + w.dlt[l]);
-                g.dlt_ss = w.dlt_ss[l];
-                g.dlt_ld = c->dout[l];
-                if (fr.nk > 0) {
-                    if (l == 1 && !f32) g.dltb = ws + w.dltb;
-                    g.dct = ws + w.dct[l];
-                    g.ddt = ws + w.ddt[l];
-                    g.tr_ss = w.dt_ss[l];
-                    g.bp = w.bp;
-                    g.cc = reinterpret_cast<const float*>(ws + w.cc) + fr.tk;
-                    g.dc = reinterpret_cast<const float*>(ws + w.dc) + fr.tk;
-                    g.coef_ss = w.coef_ss;
+            if (!retrieve && fr.nk > 0) {
+                if (l >= 1) {
+                    g.dlp = ws + w.dlp[l];
+                    g.dlp_ss = w.dlp_ss[l];
                 }
+                g.dct = ws + w.dct[l];
+                g.ddt = ws + w.ddt[l];
+                g.tr_ss = w.dt_ss[l];
+                g.bp = w.bp;
+                g.cc = reinterpret_cast<const float*>(ws + w.cc) + fr.tk;
+                g.dc = reinterpret_cast<const float*>(ws + w.dc) + fr.tk;
+                g.coef_ss = w.coef_ss;
             }
         }
-        (void)esz;
         hipError_t e = timed(K_FWD, st, [&] { return launch_fwd(g, (int)ns, f32 ? 1 : 0, st); });
         if (e != hipSuccess) return TM_ERR_HIP;
     }
@@ -422,23 +427,21 @@ tm_status run_backward(const tm_ctx* c, char* state, long ns, const WsLayout& w,
         g.N = c->din[l];
         g.K = c->dout[l];
         g.tl = tl;
-        g.amode = 1;
-        g.a0 = ws + w.dlt[l];
-        g.a_ss = w.dlt_ss[l];
-        g.a_ld = c->dout[l];
+        g.amode = A_PACKED;
+        g.a0 = ws + w.dlp[l];
+        g.a_ss = w.dlp_ss[l];
         g.n0 = 0;   // key rows only
+        // B[k][n] = W_l[n][k]: row n of the fp32 master, contiguous in K
+        g.bmode = B_ROWS;
         g.b = state + sl.M + (size_t)c->off[l] * 4;
         g.b_ss = c->P;
-        g.b_ldn = c->dout[l];
-        g.b_ldk = 1;
+        g.b_ld = c->dout[l];
         g.epi = EPI_BWD;
         g.dsl = reinterpret_cast<float*>(ws + w.dsl[l - 1]);
         g.dsl_ss = w.dsl_ss;
         g.dsl_ld = c->hidden;
-        g.dlt = reinterpret_cast<float*>(ws + w.dlt[l - 1]);
-        g.dlt_ss = w.dlt_ss[l - 1];
-        g.dlt_ld = c->din[l];
-        if (l - 1 == 1 && !f32) g.dltb = ws + w.dltb;
+        g.dlp = ws + w.dlp[l - 1];
+        g.dlp_ss = w.dlp_ss[l - 1];
         g.dct = ws + w.dct[l - 1];
         g.ddt = ws + w.ddt[l - 1];
         g.tr_ss = w.dt_ss[l - 1];
@@ -488,17 +491,24 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     sa.position = &reinterpret_cast<StateHeader*>(state)->position;
     sa.add = n_tokens;
     sa.k = k;
+    sa.q = q;
     sa.ktl = tl;
     sa.kt = ws + w.kt;
+    sa.xk = ws + w.xk;
+    sa.xq = ws + w.xq;
+    sa.xc = w.xc;
     sa.bp = w.bp;
     sa.kt_f32 = f32 ? 1 : 0;
     sa.scan_blocks = (int)(((long)ns * C + 3) / 4);
     sa.tr_blocks = (int)(ns * C * ((c->dim + 63) / 64));
+    sa.pack_blocks = (int)(ns * C * ((b + 15) / 16) * (q ? 2 : 1));
     if (c->L >= 2) {
         sa.w1_master = reinterpret_cast<const float*>(state + sl.M) + c->off[1];
         sa.w1_copy = ws + w.wr[0];
         sa.w1_ss = c->P;
-        sa.w1_n = (long)c->din[1] * c->dout[1];
+        sa.w1c_ss = w.wr_ss;
+        sa.w1_din = c->din[1];
+        sa.w1_dout = c->dout[1];
     }
     if (timed(K_SCAN, st, [&] { return launch_scan(sa, st); }) != hipSuccess) return TM_ERR_HIP;
 
@@ -518,19 +528,18 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         a.u.ddt[l] = ws + w.ddt[l];
         a.u.dt_ss[l] = w.dt_ss[l];
     }
-    a.u.wr_ss = c->P;
+    a.u.wr_ss = w.wr_ss;
     a.dim = c->dim;
     a.h1 = c->dout[0];
     a.nb1 = (a.h1 + JW - 1) / JW;
     a.kt_ss = w.kt_ss;
-    a.dlt2_ss = c->L >= 2 ? w.dlt_ss[1] : 0;
-    a.dlt2 = c->L >= 2 ? (f32 ? (const void*)(ws + w.dlt[1]) : (const void*)(ws + w.dltb)) : nullptr;
-    a.wr_ss = c->P;
+    a.dlt2_ss = c->L >= 2 ? w.dlp_ss[1] : 0;
+    a.dlt2 = c->L >= 2 ? (const void*)(ws + w.dlp[1]) : nullptr;
+    a.wr_ss = w.wr_ss;
     a.dsl1 = c->L >= 2 ? reinterpret_cast<float*>(ws + w.dsl[0]) : nullptr;
     a.dsl1_ss = w.dsl_ss;
     a.coef_ss = w.coef_ss;
-    a.xq = q;
-    a.xk = k;
+    a.x_ss = w.x_ss;
     a.tl = tl;
     a.act = c->L >= 2 ? ws + w.act[0] : nullptr;
     a.act_ss = w.act_ss;
@@ -575,6 +584,8 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         a.u.chunk = ci - 1;
         a.tq0 = (ci - 1) * b;
         a.tk0 = ci * b;
+        a.xq = (q && ci >= 1) ? ws + w.xq + (size_t)(ci - 1) * w.xc * esz : nullptr;
+        a.xk = ci < C ? ws + w.xk + (size_t)ci * w.xc * esz : nullptr;
         if (ci >= 1) {
             a.kt_prev = ws + w.kt + (size_t)(ci - 1) * c->dim * w.bp * esz;
             a.cc_prev = reinterpret_cast<const float*>(ws + w.cc) + (ci - 1) * b;

@@ -27,6 +27,27 @@ struct StateHeader {
 };
 static_assert(sizeof(StateHeader) == 256, "header is 256 bytes");
 
+// Fragment-packed matrices ("packed" below).  An operand of the 16x16x32
+// matrix instruction is fed as 16-row x 32-deep fragments in which lane l
+// supplies row l % 16 and the 8 consecutive K values 8 * (l / 16) .. + 7.
+// Packed storage puts those 8 values of the 64 lanes next to each other:
+// element (r, k) of an R x K matrix (R padded to 16, K to 32) lives at
+// pk(r, k, K / 32), and the fragment (row block rb, K step ks) of lane l
+// starts at pkf(rb, ks, K / 32, l).  A wave's fragment load is then one
+// contiguous 1 KB (2 KB for fp32) instead of 16 rows x 64 B: measured on
+// MI355X, 59 vs 18.5 bytes per clock per CU.  Every operand the kernels
+// produce for another kernel's matrix instructions is stored packed; for a
+// B operand the "row" is the output column.
+__host__ __device__ inline long pk(int r, int k, int nks) {
+    return ((((long)(r >> 4) * nks + (k >> 5)) * 64 + (r & 15) + 16 * ((k & 31) >> 3)) << 3) + (k & 7);
+}
+__host__ __device__ inline long pkf(int rb, int ks, int nks, int lane) {
+    return (((long)rb * nks + ks) * 64 + lane) << 3;
+}
+__host__ __device__ inline long pk_size(long rows, long cols) {
+    return ((rows + 15) / 16 * 16) * ((cols + 31) / 32 * 32);
+}
+
 // Token-major arrays [batch][Tc][H][d]; gates use d = 1.
 struct TokLayout {
     int Tc, H, d;
@@ -38,35 +59,40 @@ enum { EPI_HIDDEN = 0, EPI_OUT = 1, EPI_BWD = 2 };
 // (blockIdx.z):  Z[r][n] = sum_k A[r][k] B[k][n], r < nrows, n < N, k < K.
 // Rows r < n0 are queries, rows r >= n0 keys (t = r - n0 is the key's token
 // inside the chunk); the backward has key rows only (n0 = 0).
+enum { A_TOKENS = 0, A_ROWS = 1, A_PACKED = 2 };
+enum { B_STRIDED = 0, B_ROWS = 1, B_PACKED = 2 };
 struct GemmArgs {
     int nrows, N, K;
-    // A rows.  amode 0: rows r < n0 are tokens (at0 + r) of a0, rows r >= n0
-    // tokens (at1 + r - n0) of a1, both in the token layout tl.  amode 1:
-    // row r at a0 + s*a_ss + r*a_ld.
+    // A.  A_TOKENS: rows r < n0 are tokens (at0 + r) of a0, rows r >= n0
+    // tokens (at1 + r - n0) of a1, both in the token layout tl.  A_ROWS: row
+    // r at a0 + s*a_ss + r*a_ld.  A_PACKED: packed [rows][K] at a0 + s*a_ss.
     const void* a0;
     const void* a1;
     int n0, at0, at1, amode;
     long a_ss, a_ld;
-    // B element (k, n) at b + s*b_ss + n*b_ldn + k*b_ldk.
+    // B.  B_STRIDED: element (k, n) at b + s*b_ss + n + k*b_ld (row-major
+    // [K][N]); B_ROWS: at b + s*b_ss + n*b_ld + k (row n contiguous in K);
+    // B_PACKED: packed [N][K] at b + s*b_ss.
     const void* b;
-    long b_ss, b_ldn, b_ldk;
+    long b_ss, b_ld;
+    int bmode;
     TokLayout tl;
     int epi;
-    // EPI_HIDDEN: act[r][n] = SiLU(z) (operand type); key rows also
-    //             dsl[t][n] = SiLU'(z) and the transposed copy ht[n][t] = act.
+    // EPI_HIDDEN: act = SiLU(z) (operand type, packed [rows][N]); key rows
+    //             also dsl[t][n] = SiLU'(z) and ht = act transposed (packed
+    //             [N][bp]).
     // EPI_OUT   : query rows: y at token (yt0 + r) = z; key rows:
-    //             dlt[t][n] = Delta = 2 (z - v at token (vt0 + t)).
-    // EPI_BWD   : dlt[t][n] = Delta = z * dsl[t][n].
-    // OUT / BWD also write the theta-weighted transposed deltas
-    //             dct[n][t] = c_t Delta,  ddt[n][t] = d_t Delta  (operand type).
-    // Transposed arrays have rows of bp (>= chunk, multiple of 32) tokens.
+    //             Delta = 2 (z - v at token (vt0 + t)).
+    // EPI_BWD   : Delta = z * dsl[t][n].
+    // OUT / BWD write Delta (operand type, packed [b][N]) to dlp if set, and
+    //             the theta-weighted transposed deltas dct = (c_t Delta)^T,
+    //             ddt = (d_t Delta)^T (packed [N][bp]).
     void* act;
-    long act_ss, act_ld;
+    long act_ss;
     float* dsl;
     long dsl_ss, dsl_ld;
-    float* dlt;
-    long dlt_ss, dlt_ld;
-    void* dltb;               // optional operand-type copy of dlt (same layout)
+    void* dlp;
+    long dlp_ss;
     float* y;
     const void* v;
     int yt0, vt0;
@@ -93,17 +119,17 @@ struct UpdArgs {
     long P;
     float* M;
     float* S;
-    void* Wt;                 // bf16 transposed copy, [d_out][d_in] per layer
-    const void* at[MAXL];     // at[l]: layer l's input rows transposed, [d_in][bp]
+    void* Wt;                 // bf16 copy of M for the forward, packed [d_out][d_in] per layer
+    const void* at[MAXL];     // at[l]: layer l's input key rows transposed, packed [d_in][bp]
     long at_ss[MAXL];
-    const void* dct[MAXL];    // (c Delta_l)^T, [d_out][bp]
+    const void* dct[MAXL];    // (c Delta_l)^T, packed [d_out][bp]
     const void* ddt[MAXL];    // (d Delta_l)^T
     long dt_ss[MAXL];
     const float* cs;          // per-chunk scalars (p_alpha, p_eta, s0, 0)
     long cs_ss;
     int chunk;
     int* flag;
-    void* wr_next;            // if set: row-major copy (operand type) of layer 1's new weights
+    void* wr_next;            // if set: layer 1's new weights, operand type, packed [d_in][d_out]
     long wr_ss;
 };
 
@@ -127,11 +153,11 @@ struct FirstArgs {
     int dim, h1, nb1;
     int do_update, do_fwd, nq, nk;
     int chunk_prev;
-    const void* kt_prev;      // keys of chunk c-1 transposed, [dim][bp]
+    const void* kt_prev;      // keys of chunk c-1 transposed, packed [dim][bp]
     long kt_ss;
-    const void* dlt2;         // Delta of layer 1 for chunk c-1 (operand type), [b][dout1]
+    const void* dlt2;         // Delta of layer 1 for chunk c-1 (operand type), packed [b][dout1]
     long dlt2_ss;
-    const void* wr_prev;      // layer 1's weights at chunk c-1's start, [h1][dout1]
+    const void* wr_prev;      // layer 1's weights at chunk c-1's start, packed [h1][dout1]
     long wr_ss;
     float* dsl1;              // SiLU'(z) of layer 0: read (chunk c-1), then written (chunk c)
     long dsl1_ss;
@@ -140,24 +166,27 @@ struct FirstArgs {
     const float* cc_cur;      // coefficients of chunk c's tokens
     const float* dc_cur;
     long coef_ss;
-    const void* xq;           // queries (rows r < nq are tokens tq0 + r)
-    const void* xk;           // keys (rows r >= nq are tokens tk0 + r - nq)
-    TokLayout tl;
+    const void* xq;           // queries of chunk c-1, packed [b][dim] (rows r < nq)
+    const void* xk;           // keys of chunk c, packed [b][dim] (rows r >= nq)
+    long x_ss;
+    TokLayout tl;             // token layout of y and v
     int tq0, tk0;
-    void* act;                // layer-0 activations of the rows, [2b][h1]
+    void* act;                // layer-0 activations of the rows, packed [2b][h1]
     long act_ss;
-    void* ht1;                // key rows of act transposed, [h1][bp]
+    void* ht1;                // key rows of act transposed, packed [h1][bp]
     long ht_ss;
     // depth 1: the first layer is the last one
     float* y;
     const void* v;
-    void* dct1;               // (c Delta)^T, (d Delta)^T of layer 0, [h1][bp]
+    void* dct1;               // (c Delta)^T, (d Delta)^T of layer 0, packed [h1][bp]
     void* ddt1;
     long dt1_ss;
 };
 
-// Per call: the coefficient scan of every (stream, chunk) and the keys of
-// every chunk transposed to kt[s][chunk][d][bp].
+// Per call: the coefficient scan of every (stream, chunk); every chunk's
+// keys transposed (packed [d][bp] per chunk) and its key and query rows
+// packed ([b][d] per chunk); and the packed operand-type copy of layer 1's
+// weights.
 struct ScanArgs {
     const float* theta;
     const float* eta;
@@ -172,15 +201,21 @@ struct ScanArgs {
     long long* position;
     long long add;
     const void* k;            // keys, token layout ktl
+    const void* q;            // queries (may be null)
     TokLayout ktl;
-    void* kt;
+    void* kt;                 // [s][chunk] packed [d][bp]
+    void* xk;                 // [s][chunk] packed [b][d]
+    void* xq;
+    long xc;                  // elements of one chunk's packed rows
     int bp, kt_f32;
-    int scan_blocks;          // blocks [0, scan_blocks) scan, the rest transpose
-    // refresh of the row-major copy of layer 1's weights (depth >= 2)
-    const float* w1_master;   // M of layer 1, stream stride w1_ss
-    void* w1_copy;            // operand-type copy, same layout
-    long w1_ss, w1_n;         // per-stream stride, elements per stream
-    int tr_blocks;            // transpose blocks; copy blocks follow them
+    int scan_blocks;          // blocks [0, scan_blocks) scan, then transposes, packs, copy
+    int pack_blocks;
+    // refresh of the packed copy of layer 1's weights (depth >= 2)
+    const float* w1_master;   // M of layer 1 (row-major [din1][dout1]), stream stride w1_ss
+    void* w1_copy;            // operand type, packed [din1][dout1], stream stride w1c_ss
+    long w1_ss, w1c_ss;
+    int w1_din, w1_dout;
+    int tr_blocks;
 };
 
 // ---- launchers (tm_kernels.hip) ----

@@ -68,6 +68,9 @@ template <class OP> __device__ __forceinline__ typename Frag<OP>::T cvt(bf16x8 v
 template <> __device__ __forceinline__ bf16x8 cvt<bf16>(bf16x8 v) { return v; }
 template <> __device__ __forceinline__ f32x8 cvt<float>(bf16x8 v) { return to_f32(v); }
 
+__device__ __forceinline__ f32x8 to_f32v(f32x8 v) { return v; }
+__device__ __forceinline__ f32x8 to_f32v(bf16x8 v) { return to_f32(v); }
+
 template <class OP> __device__ __forceinline__ typename Frag<OP>::T zero_frag() {
     typename Frag<OP>::T z;
 #pragma unroll
@@ -114,34 +117,54 @@ template <class T> __device__ __forceinline__ float load1(const void* p, long i)
 
 constexpr int GEMM_RT = 64;   // rows per tile (4 row blocks of 16)
 
-// Row-major outputs of one element; returns the value the transposed copy
-// carries for key rows (the rounded activation, or Delta).
+template <class OP> __device__ __forceinline__ void st8(OP* p, typename Frag<OP>::T v) {
+    *reinterpret_cast<typename Frag<OP>::T*>(p) = v;
+}
+__device__ __forceinline__ void st8f(float* p, const float* v) {
+    *reinterpret_cast<f32x4*>(p) = (f32x4){v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = (f32x4){v[4], v[5], v[6], v[7]};
+}
+
+// Row outputs of 8 consecutive columns c .. c+7 of row r; z becomes the
+// value the transposed copy carries for key rows (the rounded activation,
+// or Delta).
 template <class OP>
-__device__ __forceinline__ float gemm_store(const GemmArgs& g, int s, int r, int c, float z) {
+__device__ __forceinline__ void gemm_store8(const GemmArgs& g, int s, int r, int c, float* z) {
+    typedef typename Frag<OP>::T F;
+    F o;
     if (g.epi == EPI_HIDDEN) {
-        const float sg = sigmoid(z);
-        const OP h = (OP)(z * sg);
-        reinterpret_cast<OP*>(g.act)[(long)s * g.act_ss + (long)r * g.act_ld + c] = h;
-        if (r >= g.n0)
-            g.dsl[(long)s * g.dsl_ss + (long)(r - g.n0) * g.dsl_ld + c] = sg * (1.0f + z * (1.0f - sg));
-        return (float)h;
-    } else if (g.epi == EPI_OUT) {
-        if (r < g.n0) {
-            g.y[tok_off(g.tl, s, g.yt0 + r) + c] = z;
-            return 0.f;
+        float sl[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float sg = sigmoid(z[e]);
+            o[e] = (OP)(z[e] * sg);
+            sl[e] = sg * (1.0f + z[e] * (1.0f - sg));
+            z[e] = (float)o[e];
         }
-        const float vv = load1<OP>(g.v, tok_off(g.tl, s, g.vt0 + r - g.n0) + c);
-        const float dl = 2.0f * (z - vv);
-        const long o = (long)s * g.dlt_ss + (long)(r - g.n0) * g.dlt_ld + c;
-        g.dlt[o] = dl;
-        if (g.dltb) reinterpret_cast<OP*>(g.dltb)[o] = (OP)dl;
-        return dl;
+        st8<OP>(reinterpret_cast<OP*>(g.act) + (long)s * g.act_ss + pk(r, c, g.N >> 5), o);
+        if (r >= g.n0 && g.dsl) st8f(g.dsl + (long)s * g.dsl_ss + (long)(r - g.n0) * g.dsl_ld + c, sl);
+        return;
     }
-    const float dl = z * g.dsl[(long)s * g.dsl_ss + (long)r * g.dsl_ld + c];
-    const long o = (long)s * g.dlt_ss + (long)r * g.dlt_ld + c;
-    g.dlt[o] = dl;
-    if (g.dltb) reinterpret_cast<OP*>(g.dltb)[o] = (OP)dl;
-    return dl;
+    int t = r;
+    if (g.epi == EPI_OUT) {
+        if (r < g.n0) {
+            st8f(g.y + tok_off(g.tl, s, g.yt0 + r) + c, z);
+            return;
+        }
+        t = r - g.n0;
+        const f32x8 vv = to_f32v(ld8(reinterpret_cast<const OP*>(g.v) + tok_off(g.tl, s, g.vt0 + t) + c));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = 2.0f * (z[e] - vv[e]);
+    } else {
+        const f32x8 sl = ld8(g.dsl + (long)s * g.dsl_ss + (long)r * g.dsl_ld + c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = z[e] * sl[e];
+    }
+    if (g.dlp) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (OP)z[e];
+        st8<OP>(reinterpret_cast<OP*>(g.dlp) + (long)s * g.dlp_ss + pk(t, c, g.N >> 5), o);
+    }
 }
 
 template <class OP, class AT, class BT, bool BKC, int NR, int W, int PF>
@@ -167,17 +190,27 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int n = 0; n < NR; ++n) acc[m][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+    // per-lane operand addresses at K step 0 and the distance of one step:
+    // packed operands advance by one 64-lane fragment (512 elements)
     const int kofs = 8 * (lane >> 4);
     const AT* arow[MR];
     bool aok[MR];
+    long astep = 32;
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-        int r = row0 + m * 16 + (lane & 15);
-        aok[m] = r < g.nrows;
-        if (!aok[m]) r = g.nrows - 1;   // valid address; the value is dropped
+        int rb = (row0 >> 4) + m;
+        aok[m] = rb * 16 + (lane & 15) < g.nrows;
+        if (g.amode == A_PACKED) {
+            if (rb * 16 >= g.nrows) rb = 0;   // a block past the rows: valid address, values dropped
+            arow[m] = reinterpret_cast<const AT*>(g.a0) + (long)s * g.a_ss + pkf(rb, 0, nsteps, lane);
+            astep = 512;
+            continue;
+        }
+        int r = rb * 16 + (lane & 15);
+        if (!aok[m]) r = g.nrows - 1;
         long off;
         const void* base = g.a0;
-        if (g.amode == 0) {
+        if (g.amode == A_TOKENS) {
             if (r < g.n0) { off = tok_off(g.tl, s, g.at0 + r); }
             else { base = g.a1; off = tok_off(g.tl, s, g.at1 + r - g.n0); }
         } else {
@@ -187,12 +220,22 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     }
     const BT* bcol[NR];
     bool bok[NR];
+    long bstep = 32;
 #pragma unroll
     for (int n = 0; n < NR; ++n) {
-        int c = col0 + n * 16 + (lane & 15);
+        int cb = (col0 >> 4) + n;
+        const int c = cb * 16 + (lane & 15);
         bok[n] = c < g.N;
-        bcol[n] = reinterpret_cast<const BT*>(g.b) + (long)s * g.b_ss + (long)(bok[n] ? c : 0) * g.b_ldn +
-                  (long)kofs * g.b_ldk;
+        const BT* base = reinterpret_cast<const BT*>(g.b) + (long)s * g.b_ss;
+        if (g.bmode == B_PACKED) {
+            if (cb * 16 >= g.N) cb = 0;
+            bcol[n] = base + pkf(cb, 0, nsteps, lane);
+            bstep = 512;
+        } else if (g.bmode == B_ROWS) {
+            bcol[n] = base + (long)(bok[n] ? c : 0) * g.b_ld + kofs;
+        } else {
+            bcol[n] = base + (bok[n] ? c : 0) + (long)kofs * g.b_ld;
+        }
     }
     // the ring holds raw storage vectors; conversion to the operand type
     // happens right before the matrix instruction, so loads stay in flight
@@ -201,18 +244,17 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     RA a[PF][MR];
     RB bb[PF][NR];
     auto load_step = [&](int p, int k) {
-        const int k0 = k << 5;
 #pragma unroll
-        for (int m = 0; m < MR; ++m) a[p][m] = ld8(arow[m] + k0);
+        for (int m = 0; m < MR; ++m) a[p][m] = ld8(arow[m] + k * astep);
 #pragma unroll
         for (int n = 0; n < NR; ++n) {
             if (BKC) {
-                bb[p][n] = ld8(bcol[n] + k0);
+                bb[p][n] = ld8(bcol[n] + k * bstep);
             } else {
                 RB u;
-                const BT* q = bcol[n] + (long)k0 * g.b_ldk;
+                const BT* q = bcol[n] + (long)(k << 5) * g.b_ld;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) u[j] = q[(long)j * g.b_ldk];
+                for (int j = 0; j < 8; ++j) u[j] = q[(long)j * g.b_ld];
                 bb[p][n] = u;
             }
         }
@@ -246,32 +288,81 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
             for (int e = 0; e < 4; ++e)
                 mine[(m * 16 + 4 * (lane >> 4) + e) * NTP + n * 16 + (lane & 15)] = acc[m][n][e];
     __syncthreads();
-    // pass 1, row-major (coalesced row outputs): each element is owned by one
-    // thread, which leaves the value for the transposed copy in slot 0
-    for (int idx = tid; idx < GEMM_RT * NT; idx += W * 64) {
-        const int rr = idx / NT, cc = idx - rr * NT;
+    // pass 1: row outputs, 8 consecutive columns per thread (N is a multiple
+    // of 32); the value for the transposed copy is left in slot 0
+    for (int idx = tid; idx < GEMM_RT * (NT / 8); idx += W * 64) {
+        const int rr = idx / (NT / 8), cc = (idx - rr * (NT / 8)) * 8;
         const int r = row0 + rr, c = col0 + cc;
         if (r >= g.nrows || c >= g.N) continue;
-        float z = 0.f;
+        float z[8];
 #pragma unroll
-        for (int w = 0; w < W; ++w) z += red[w * (GEMM_RT * NTP) + rr * NTP + cc];
-        red[rr * NTP + cc] = gemm_store<OP>(g, s, r, c, z);
+        for (int e = 0; e < 8; ++e) {
+            float x = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) x += red[w * (GEMM_RT * NTP) + rr * NTP + cc + e];
+            z[e] = x;
+        }
+        gemm_store8<OP>(g, s, r, c, z);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[rr * NTP + cc + e] = z[e];
     }
     if (!g.ht && !g.dct) return;   // uniform: no transposed outputs (retrieve)
     __syncthreads();
-    // pass 2, column-major (coalesced transposed outputs) over the key rows
-    for (int idx = tid; idx < GEMM_RT * NT; idx += W * 64) {
-        const int cc = idx / GEMM_RT, rr = idx - cc * GEMM_RT;
-        const int r = row0 + rr, c = col0 + cc;
-        if (r >= g.nrows || r < g.n0 || c >= g.N) continue;
-        const int t = r - g.n0;
-        const float x = red[rr * NTP + cc];
-        const long o = (long)s * g.tr_ss + (long)c * g.bp + t;
+    // pass 2: the key rows' transposed copies, packed [N][bp]: 8 tokens of
+    // one column per thread, whole vectors where all 8 tokens are this
+    // tile's rows (a group cut by the tile edge is stored element-wise)
+    const int tlo = max(row0, g.n0) - g.n0, thi = min(row0 + GEMM_RT, g.nrows) - g.n0;
+    if (thi <= tlo) return;
+    const int g0 = tlo >> 3, ng = ((thi - 1) >> 3) - g0 + 1;
+    const int nkb = g.bp >> 5;
+    for (int idx = tid; idx < NT * ng; idx += W * 64) {
+        const int cc = idx % NT, t8 = (g0 + idx / NT) * 8;
+        const int c = col0 + cc;
+        if (c >= g.N) continue;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = t8 + e;
+            x[e] = (t >= tlo && t < thi) ? red[(t + g.n0 - row0) * NTP + cc] : 0.f;
+        }
+        const long o = (long)s * g.tr_ss + pk(c, t8, nkb);
+        const bool whole = t8 >= tlo && t8 + 8 <= thi;
         if (g.epi == EPI_HIDDEN) {
-            reinterpret_cast<OP*>(g.ht)[o] = (OP)x;
+            OP* h = reinterpret_cast<OP*>(g.ht) + o;
+            if (whole) {
+                F v;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (OP)x[e];
+                st8<OP>(h, v);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (t8 + e >= tlo && t8 + e < thi) h[e] = (OP)x[e];
+            }
         } else {
-            reinterpret_cast<OP*>(g.dct)[o] = (OP)(g.cc[(long)s * g.coef_ss + t] * x);
-            reinterpret_cast<OP*>(g.ddt)[o] = (OP)(g.dc[(long)s * g.coef_ss + t] * x);
+            OP* pc = reinterpret_cast<OP*>(g.dct) + o;
+            OP* pd = reinterpret_cast<OP*>(g.ddt) + o;
+            const float* cf = g.cc + (long)s * g.coef_ss;
+            const float* df = g.dc + (long)s * g.coef_ss;
+            if (whole) {
+                F vc, vd;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    vc[e] = (OP)(cf[t8 + e] * x[e]);
+                    vd[e] = (OP)(df[t8 + e] * x[e]);
+                }
+                st8<OP>(pc, vc);
+                st8<OP>(pd, vd);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int t = t8 + e;
+                    if (t >= tlo && t < thi) {
+                        pc[e] = (OP)(cf[t] * x[e]);
+                        pd[e] = (OP)(df[t] * x[e]);
+                    }
+                }
+            }
         }
     }
 }
@@ -325,7 +416,7 @@ hipError_t launch_fwd(const GemmArgs& g, int ns, int f32, hipStream_t st) {
 
 hipError_t launch_bwd(const GemmArgs& g, int ns, int f32, hipStream_t st) {
     if (f32) return launch_gemm<float, float, float, true, 2>(g, ns, st);
-    return launch_gemm<bf16, float, float, true, 2>(g, ns, st);
+    return launch_gemm<bf16, bf16, float, true, 2>(g, ns, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -334,9 +425,11 @@ hipError_t launch_bwd(const GemmArgs& g, int ns, int f32, hipStream_t st) {
 __device__ __forceinline__ float shdown(float x, int off) { return __shfl_down(x, off, 64); }
 
 // Keys of one chunk, 64 features at a time, transposed through LDS into
-// kt[s][chunk][feature][bp] (token-contiguous rows for the update's operands).
+// kt[s][chunk] (packed [d][bp]: rows are features, K runs over the chunk's
+// tokens, zero past the chunk).
 template <class T>
 __device__ void transpose_keys(const ScanArgs& a, long blk) {
+    typedef typename Frag<T>::T V;
     __shared__ float tile[64][65];
     const int d = a.ktl.d, ib = (d + 63) / 64;
     const int s = (int)(blk / ((long)a.C * ib));
@@ -349,31 +442,84 @@ __device__ void transpose_keys(const ScanArgs& a, long blk) {
         tile[t][i] = (t < a.b && i0 + i < d) ? (float)k[tok_off(a.ktl, s, c * a.b + t) + i0 + i] : 0.f;
     }
     __syncthreads();
+    const int nkb = a.bp >> 5;
     T* kt = reinterpret_cast<T*>(a.kt) + ((long)s * a.C + c) * (long)d * a.bp;
-    for (int idx = tid; idx < 64 * a.bp; idx += 256) {
-        const int i = idx / a.bp, t = idx - i * a.bp;
-        if (i0 + i < d && t < 64) kt[(long)(i0 + i) * a.bp + t] = (T)tile[t][i];
+    for (int idx = tid; idx < 4 * nkb * 64; idx += 256) {
+        const int ln = idx & 63, ks = (idx >> 6) % nkb, rb = (idx >> 6) / nkb;
+        const int i = rb * 16 + (ln & 15), t8 = ks * 32 + 8 * (ln >> 4);
+        if (i0 + i >= d) continue;
+        V v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (T)tile[t8 + e][i];
+        *reinterpret_cast<V*>(kt + pkf((i0 >> 4) + rb, ks, nkb, ln)) = v;
     }
 }
 
+// One 16-token block of one chunk's keys or queries, packed ([b][d] per
+// chunk: rows are tokens, K runs over the features; zero past the chunk).
+template <class T>
+__device__ void pack_rows(const ScanArgs& a, long blk) {
+    typedef typename Frag<T>::T V;
+    const int d = a.ktl.d, nbt = (a.b + 15) >> 4, nks = d >> 5;
+    const int nkq = a.q ? 2 : 1;
+    const int kq = (int)(blk % nkq);
+    blk /= nkq;
+    const int tb = (int)(blk % nbt);
+    blk /= nbt;
+    const int c = (int)(blk % a.C), s = (int)(blk / a.C);
+    const T* src = reinterpret_cast<const T*>(kq ? a.q : a.k);
+    T* dst = reinterpret_cast<T*>(kq ? a.xq : a.xk) + ((long)s * a.C + c) * a.xc;
+    for (int idx = threadIdx.x; idx < nks * 64; idx += 256) {
+        const int ln = idx & 63, ks = idx >> 6;
+        const int t = tb * 16 + (ln & 15), i = ks * 32 + 8 * (ln >> 4);
+        V v;
+        if (t < a.b) {
+            v = ld8(src + tok_off(a.ktl, s, c * a.b + t) + i);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (T)0.0f;
+        }
+        *reinterpret_cast<V*>(dst + pkf(tb, ks, nks, ln)) = v;
+    }
+}
+
+// Layer 1's weights at the call start, in operand type and packed
+// [din1][dout1] (rows are layer 1's inputs, K runs over its outputs).
 template <class T>
 __device__ void copy_layer1(const ScanArgs& a, long blk) {
-    const long n = a.w1_n;
-    for (long e = blk * 256 + threadIdx.x; e < n * a.ns; e += 1024L * 256) {
-        const long s = e / n, i = e - s * n;
-        reinterpret_cast<T*>(a.w1_copy)[s * a.w1_ss + i] = (T)a.w1_master[s * a.w1_ss + i];
+    typedef typename Frag<T>::T V;
+    const int nks = a.w1_dout >> 5;
+    const long per = (long)(a.w1_din >> 4) * nks * 64;   // vectors per stream
+    for (long e = blk * 256 + threadIdx.x; e < per * a.ns; e += 1024L * 256) {
+        const long s = e / per, v = e - s * per;
+        const int ln = (int)(v & 63);
+        const long f = v >> 6;
+        const int ks = (int)(f % nks), rb = (int)(f / nks);
+        const int i = rb * 16 + (ln & 15), j = ks * 32 + 8 * (ln >> 4);
+        const f32x8 w = ld8(a.w1_master + s * a.w1_ss + (long)i * a.w1_dout + j);
+        V o;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = (T)w[q];
+        *reinterpret_cast<V*>(reinterpret_cast<T*>(a.w1_copy) + s * a.w1c_ss + (v << 3)) = o;
     }
 }
 
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
-    if ((int)blockIdx.x >= a.scan_blocks + a.tr_blocks) {
-        const long blk = (long)blockIdx.x - a.scan_blocks - a.tr_blocks;
+    const int x = (int)blockIdx.x;
+    if (x >= a.scan_blocks + a.tr_blocks + a.pack_blocks) {
+        const long blk = (long)x - a.scan_blocks - a.tr_blocks - a.pack_blocks;
         if (a.kt_f32) copy_layer1<float>(a, blk);
         else copy_layer1<bf16>(a, blk);
         return;
     }
-    if ((int)blockIdx.x >= a.scan_blocks) {
-        const long blk = (long)blockIdx.x - a.scan_blocks;
+    if (x >= a.scan_blocks + a.tr_blocks) {
+        const long blk = (long)x - a.scan_blocks - a.tr_blocks;
+        if (a.kt_f32) pack_rows<float>(a, blk);
+        else pack_rows<bf16>(a, blk);
+        return;
+    }
+    if (x >= a.scan_blocks) {
+        const long blk = (long)x - a.scan_blocks;
         if (a.kt_f32) transpose_keys<float>(a, blk);
         else transpose_keys<bf16>(a, blk);
         return;
@@ -431,7 +577,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
     long waves = (long)a.ns * a.C;
     if (waves == 0) return hipSuccess;
     const long cp = a.w1_copy ? 1024 : 0;
-    dim3 grid((unsigned)(a.scan_blocks + a.tr_blocks + cp));
+    dim3 grid((unsigned)(a.scan_blocks + a.tr_blocks + a.pack_blocks + cp));
     hipLaunchKernelGGL(scan_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
@@ -474,19 +620,20 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, float (*UM)[65], 
     // U_M, U_S on the matrix cores: 4 waves as 2 x 2, 32 x 32 each
     const int wi = wave & 1, wj = wave >> 1;
     const int kofs = 8 * (lane >> 4);
+    const int nkb = bp >> 5;
     const OP* A = reinterpret_cast<const OP*>(u.at[l]) + (long)s * u.at_ss[l];
     const OP* Bc = reinterpret_cast<const OP*>(u.dct[l]) + (long)s * u.dt_ss[l];
     const OP* Bd = reinterpret_cast<const OP*>(u.ddt[l]) + (long)s * u.dt_ss[l];
-    int ai[2], bj[2];
+    int ab[2], bb[2];
     bool aok[2], bok[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-        ai[m] = i0 + wi * 32 + m * 16 + (lane & 15);
-        aok[m] = ai[m] < din;
-        if (!aok[m]) ai[m] = 0;
-        bj[m] = j0 + wj * 32 + m * 16 + (lane & 15);
-        bok[m] = bj[m] < dout;
-        if (!bok[m]) bj[m] = 0;
+        ab[m] = (i0 >> 4) + wi * 2 + m;     // 16-row blocks of W (packed operand rows)
+        aok[m] = ab[m] * 16 < din;
+        if (!aok[m]) ab[m] = 0;
+        bb[m] = (j0 >> 4) + wj * 2 + m;
+        bok[m] = bb[m] * 16 < dout;
+        if (!bok[m]) bb[m] = 0;
     }
     // operand fragments first (vector loads complete in issue order, so
     // the matrix work below waits only for these), then this tile's M and
@@ -501,10 +648,10 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, float (*UM)[65], 
             fa[ks][m] = zero_frag<OP>();
             fc[ks][m] = zero_frag<OP>();
             fd[ks][m] = zero_frag<OP>();
-            if (ks * 32 < bp) {
-                fa[ks][m] = tok8<OP>(A + (long)ai[m] * bp + t0, t0, b, full);
-                fc[ks][m] = tok8<OP>(Bc + (long)bj[m] * bp + t0, t0, b, full);
-                fd[ks][m] = tok8<OP>(Bd + (long)bj[m] * bp + t0, t0, b, full);
+            if (ks < nkb) {
+                fa[ks][m] = tok8<OP>(A + pkf(ab[m], ks, nkb, lane), t0, b, full);
+                fc[ks][m] = tok8<OP>(Bc + pkf(bb[m], ks, nkb, lane), t0, b, full);
+                fd[ks][m] = tok8<OP>(Bd + pkf(bb[m], ks, nkb, lane), t0, b, full);
             }
         }
     }
@@ -576,23 +723,35 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, float (*UM)[65], 
             }
             *reinterpret_cast<f32x4*>(Mp + o) = mn;
             *reinterpret_cast<f32x4*>(Sp + o) = sn;
-            if (l == 1 && u.wr_next) {
-                OP* wr = reinterpret_cast<OP*>(u.wr_next) + (long)s * u.wr_ss + o;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) wr[e] = (OP)mn[e];
-            }
         }
     }
     __syncthreads();
+    // the tile of the bf16 forward copy Wt (packed [dout][din]): 4 column
+    // blocks x 2 K steps x 64 lanes of 8 consecutive inputs, in memory order
     bf16* Wp = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P + u.off[l];
-    for (int idx = tid; idx < 64 * 8; idx += 256) {
-        const int j = idx >> 3, i = (idx & 7) * 8;
-        const int gj = j0 + j, gi = i0 + i;
-        if (gj < dout && gi < din) {
+    for (int idx = tid; idx < 512; idx += 256) {
+        const int ln = idx & 63, kk = (idx >> 6) & 1, jb = idx >> 7;
+        const int jl = jb * 16 + (ln & 15), il = kk * 32 + 8 * (ln >> 4);
+        if (j0 + jl < dout && i0 + il < din) {
             bf16x8 w;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = (bf16)UM[i + e][j];
-            *reinterpret_cast<bf16x8*>(Wp + (long)gj * din + gi) = w;
+            for (int e = 0; e < 8; ++e) w[e] = (bf16)UM[il + e][jl];
+            *reinterpret_cast<bf16x8*>(Wp + pkf((j0 >> 4) + jb, (i0 >> 5) + kk, din >> 5, ln)) = w;
+        }
+    }
+    // layer 1's operand-type copy (packed [din][dout]) for the next chunk's
+    // in-place backward of the first layer
+    if (l == 1 && u.wr_next) {
+        OP* wr = reinterpret_cast<OP*>(u.wr_next) + (long)s * u.wr_ss;
+        for (int idx = tid; idx < 512; idx += 256) {
+            const int ln = idx & 63, kk = (idx >> 6) & 1, ib = idx >> 7;
+            const int il = ib * 16 + (ln & 15), jl = kk * 32 + 8 * (ln >> 4);
+            if (i0 + il < din && j0 + jl < dout) {
+                F w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e] = (OP)UM[il][jl + e];
+                st8<OP>(wr + pkf((i0 >> 4) + ib, (j0 >> 5) + kk, dout >> 5, ln), w);
+            }
         }
     }
     if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
@@ -670,18 +829,17 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     bool tok[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const int t = 16 * m + (lane & 15);
-        tok[m] = t < b;
-        Ad[m] = bwd ? reinterpret_cast<const OP*>(a.dlt2) + (long)s * a.dlt2_ss + (long)(tok[m] ? t : 0) * K1 + kofs
-                    : nullptr;
+        tok[m] = 16 * m + (lane & 15) < b;
+        const int mb = 16 * m < b ? m : 0;   // token blocks past the chunk: valid address, dropped
+        Ad[m] = bwd ? reinterpret_cast<const OP*>(a.dlt2) + (long)s * a.dlt2_ss + pkf(mb, 0, nsA, lane) : nullptr;
     }
-    const OP* Bw = bwd ? reinterpret_cast<const OP*>(a.wr_prev) + (long)s * a.wr_ss + (long)(jok ? j : 0) * K1 + kofs
+    const OP* Bw = bwd ? reinterpret_cast<const OP*>(a.wr_prev) + (long)s * a.wr_ss + pkf(j0 >> 4, 0, nsA, lane)
                        : nullptr;
     F ra[PA][4], rb[PA];
     if (bwd) {
 #pragma unroll
         for (int p = 0; p < PA; ++p) {
-            const int k0 = min(kbA + p, klA) << 5;
+            const long k0 = (long)min(kbA + p, klA) << 9;
 #pragma unroll
             for (int m = 0; m < 4; ++m) ra[p][m] = cvt<OP>(ld8(Ad[m] + k0));
             rb[p] = cvt<OP>(ld8(Bw + k0));
@@ -702,15 +860,16 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     }
     // (3) the update's row blocks of this wave: keys^T fragments, M and S
     const int nrb = d >> 4;
+    const int nkb = bp >> 5;
     const int mineB = upd ? (nrb - wave + FW - 1) / FW : 0;
     F kf[PB][2];
     float mr[PB][4], sr[PB][4];
     auto load_rb = [&](int p, int n) {
-        const int ib = 16 * (wave + FW * min(n, mineB - 1));
-        const int ia = ib + (lane & 15);
+        const int rbk = wave + FW * min(n, mineB - 1);
+        const int ib = 16 * rbk;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            kf[p][ks] = (ks * 32 < bp) ? cvt<OP>(ld8(kt + (long)ia * bp + ks * 32 + kofs)) : zero_frag<OP>();
+            kf[p][ks] = ks < nkb ? cvt<OP>(ld8(kt + pkf(rbk, ks, nkb, lane))) : zero_frag<OP>();
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const long o = (long)(ib + g4 + e) * h1 + (jok ? j : 0);
@@ -727,6 +886,8 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     const int nrow = (R + 15) >> 4;
     const int nsC = d >> 5, qC = (nsC + FW - 1) / FW;
     const int kbC = wave * qC, keC = min(nsC, kbC + qC), klC = max(keC - 1, 0);
+    // each lane's row: query rows of chunk c-1 first, then key rows of chunk
+    // c, both packed per chunk
     const OP* Ax[8];
     bool rok[8];
 #pragma unroll
@@ -736,8 +897,8 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
         if (!rok[m]) r = R > 0 ? R - 1 : 0;
         Ax[m] = nullptr;
         if (R > 0) {
-            const long off = r < a.nq ? tok_off(a.tl, s, a.tq0 + r) : tok_off(a.tl, s, a.tk0 + r - a.nq);
-            Ax[m] = reinterpret_cast<const OP*>(r < a.nq ? a.xq : a.xk) + off + kofs;
+            const bool isq = r < a.nq;
+            Ax[m] = reinterpret_cast<const OP*>(isq ? a.xq : a.xk) + (long)s * a.x_ss + pk(isq ? r : r - a.nq, kofs, nsC);
         }
     }
     F rx[PC][8];
@@ -746,7 +907,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
         for (int p = 0; p < PC; ++p)
 #pragma unroll
             for (int m = 0; m < 8; ++m)
-                if (m < nrow) rx[p][m] = cvt<OP>(ld8(Ax[m] + (min(kbC + p, klC) << 5)));
+                if (m < nrow) rx[p][m] = cvt<OP>(ld8(Ax[m] + ((long)min(kbC + p, klC) << 9)));
     }
 
     // ================= chunk c-1's update of the block's columns =================
@@ -764,7 +925,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
 #pragma unroll
                     for (int m = 0; m < 4; ++m) mma(acc[m], tok[m] ? ra[p][m] : zero_frag<OP>(), bv);
                     if (k + PA < kbA + qA) {   // wave-uniform: ring refill for long K
-                        const int kn = min(k + p + PA, klA) << 5;
+                        const long kn = (long)min(k + p + PA, klA) << 9;
 #pragma unroll
                         for (int m = 0; m < 4; ++m) ra[p][m] = cvt<OP>(ld8(Ad[m] + kn));
                         rb[p] = cvt<OP>(ld8(Bw + kn));
@@ -789,15 +950,18 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
                 DdT[cl * DP + t] = (OP)(dv[q] * dl);
             }
         } else {
-            // depth 1: the previous chunk's forward left them in memory (tokens
-            // past the chunk are padding nobody wrote: zero them here)
-            for (int idx = tid; idx < JW * bp; idx += NT) {
-                const int cl = idx / bp, t = idx - cl * bp;
-                const int jj = j0 + cl;
-                const bool ok = jj < h1 && t < b;
-                const long o = (long)s * a.dt1_ss + (long)(ok ? jj : 0) * bp + (ok ? t : 0);
-                DcT[cl * DP + t] = ok ? reinterpret_cast<const OP*>(a.dct1)[o] : (OP)0.0f;
-                DdT[cl * DP + t] = ok ? reinterpret_cast<const OP*>(a.ddt1)[o] : (OP)0.0f;
+            // depth 1: the previous chunk's forward left them in memory
+            // (packed [h1][bp]; tokens past the chunk are zeroed here)
+            for (int idx = tid; idx < JW * (bp >> 3); idx += NT) {
+                const int cl = idx % JW, t8 = (idx / JW) * 8;
+                const long o = (long)s * a.dt1_ss + pk(j0 + cl, t8, nkb);
+                F vc = cvt<OP>(ld8(reinterpret_cast<const OP*>(a.dct1) + o));
+                F vd = cvt<OP>(ld8(reinterpret_cast<const OP*>(a.ddt1) + o));
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (t8 + e >= b) { vc[e] = (OP)0.0f; vd[e] = (OP)0.0f; }
+                *reinterpret_cast<F*>(&DcT[cl * DP + t8]) = vc;
+                *reinterpret_cast<F*>(&DdT[cl * DP + t8]) = vd;
             }
         }
         __syncthreads();
@@ -809,7 +973,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
         F bc[2], bd[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const bool on = ks * 32 < bp;
+            const bool on = ks < nkb;
             bc[ks] = on ? *reinterpret_cast<const F*>(&DcT[jl * DP + ks * 32 + kofs]) : zero_frag<OP>();
             bd[ks] = on ? *reinterpret_cast<const F*>(&DdT[jl * DP + ks * 32 + kofs]) : zero_frag<OP>();
         }
@@ -837,8 +1001,9 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
                         Wn[jl * WP + ib + g4 + e] = (OP)mn[e];
                     }
                     if (jok) {
+                        // 4 consecutive inputs of output j: 8 contiguous bytes of packed Wt
                         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                        *reinterpret_cast<bf16x4*>(Wt0 + (long)j * d + ib + g4) =
+                        *reinterpret_cast<bf16x4*>(Wt0 + pk(j, ib + g4, d >> 5)) =
                             (bf16x4){(bf16)mn[0], (bf16)mn[1], (bf16)mn[2], (bf16)mn[3]};
                     }
                 }
@@ -849,9 +1014,9 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
         // first chunk of the call: the block's columns of the current W_0
         if (sizeof(OP) == 2) {
             for (int idx = tid; idx < JW * (d >> 3); idx += NT) {
-                const int cl = idx / (d >> 3), i = (idx - cl * (d >> 3)) * 8;
+                const int cl = idx % JW, i = (idx / JW) * 8;
                 const int jj = j0 + cl;
-                bf16x8 w = jj < h1 ? *reinterpret_cast<const bf16x8*>(Wt0 + (long)jj * d + i) : zero_frag<bf16>();
+                bf16x8 w = jj < h1 ? *reinterpret_cast<const bf16x8*>(Wt0 + pk(jj, i, d >> 5)) : zero_frag<bf16>();
                 *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(Wn) + cl * WP + i) = w;
             }
         } else {
@@ -882,7 +1047,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
                 for (int m = 0; m < 8; ++m)
                     if (m < nrow) mma(acc[m], rok[m] ? rx[p][m] : zero_frag<OP>(), bv);
                 if (k + PC < kbC + qC) {   // wave-uniform ring refill
-                    const int kn = min(k + p + PC, klC) << 5;
+                    const long kn = (long)min(k + p + PC, klC) << 9;
 #pragma unroll
                     for (int m = 0; m < 8; ++m)
                         if (m < nrow) rx[p][m] = cvt<OP>(ld8(Ax[m] + kn));
@@ -897,30 +1062,79 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
                 for (int e = 0; e < 4; ++e) mine[(16 * m + g4 + e) * RP + jl] = acc[m][e];
     }
     __syncthreads();
+    // z of every (row, column): the waves' partial tiles summed into slot 0
     for (int idx = tid; idx < R * JW; idx += NT) {
-        const int r = idx / JW, cl = idx - r * JW, jj = j0 + cl;
-        if (jj >= h1) continue;
+        const int r = idx / JW, cl = idx - r * JW;
         float z = 0.f;
 #pragma unroll
         for (int w = 0; w < FW; ++w) z += red[(w * 128 + r) * RP + cl];
-        if (u.L >= 2) {
-            const float sg = sigmoid(z);
-            const OP hv = (OP)(z * sg);
-            reinterpret_cast<OP*>(a.act)[(long)s * a.act_ss + (long)r * h1 + jj] = hv;
-            if (r >= a.nq) {
-                const int t = r - a.nq;
-                a.dsl1[(long)s * a.dsl1_ss + (long)t * h1 + jj] = sg * (1.0f + z * (1.0f - sg));
-                reinterpret_cast<OP*>(a.ht1)[(long)s * a.ht_ss + (long)jj * bp + t] = hv;
+        red[r * RP + cl] = z;
+    }
+    __syncthreads();
+    if (u.L >= 2) {
+        // activations (packed [rows][h1]) and, for key rows, SiLU'(z)
+        for (int idx = tid; idx < R * (JW / 8); idx += NT) {
+            const int r = idx / (JW / 8), c8 = (idx % (JW / 8)) * 8, jj = j0 + c8;
+            F hv;
+            float sl[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float z = red[r * RP + c8 + e];
+                const float sg = sigmoid(z);
+                hv[e] = (OP)(z * sg);
+                sl[e] = sg * (1.0f + z * (1.0f - sg));
             }
-        } else if (r < a.nq) {
-            a.y[tok_off(a.tl, s, a.tq0 + r) + jj] = z;
-        } else {
-            const int t = r - a.nq;
-            const float vv = load1<OP>(a.v, tok_off(a.tl, s, a.tk0 + t) + jj);
-            const float dl = 2.0f * (z - vv);
-            const long o = (long)s * a.dt1_ss + (long)jj * bp + t;
-            reinterpret_cast<OP*>(a.dct1)[o] = (OP)(a.cc_cur[(long)s * a.coef_ss + t] * dl);
-            reinterpret_cast<OP*>(a.ddt1)[o] = (OP)(a.dc_cur[(long)s * a.coef_ss + t] * dl);
+            st8<OP>(reinterpret_cast<OP*>(a.act) + (long)s * a.act_ss + pk(r, jj, h1 >> 5), hv);
+            if (r >= a.nq) st8f(a.dsl1 + (long)s * a.dsl1_ss + (long)(r - a.nq) * h1 + jj, sl);
+        }
+        // the key rows' activations transposed (packed [h1][bp], zero past the chunk)
+        if (a.nk > 0) {
+            for (int idx = tid; idx < JW * (bp >> 3); idx += NT) {
+                const int cl = idx % JW, t8 = (idx / JW) * 8;
+                F hv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int t = t8 + e;
+                    float h = 0.f;
+                    if (t < a.nk) {
+                        const float z = red[(a.nq + t) * RP + cl];
+                        h = z * sigmoid(z);
+                    }
+                    hv[e] = (OP)h;
+                }
+                st8<OP>(reinterpret_cast<OP*>(a.ht1) + (long)s * a.ht_ss + pk(j0 + cl, t8, nkb), hv);
+            }
+        }
+    } else {
+        // depth 1: the first layer is the output layer
+        for (int idx = tid; idx < a.nq * (JW / 8); idx += NT) {
+            const int r = idx / (JW / 8), c8 = (idx % (JW / 8)) * 8;
+            float z[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[e] = red[r * RP + c8 + e];
+            st8f(a.y + tok_off(a.tl, s, a.tq0 + r) + j0 + c8, z);
+        }
+        if (a.nk > 0) {
+            for (int idx = tid; idx < JW * (bp >> 3); idx += NT) {
+                const int cl = idx % JW, t8 = (idx / JW) * 8, jj = j0 + cl;
+                F vc, vd;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int t = t8 + e;
+                    float xc = 0.f, xd = 0.f;
+                    if (t < a.nk) {
+                        const float z = red[(a.nq + t) * RP + cl];
+                        const float dl = 2.0f * (z - load1<OP>(a.v, tok_off(a.tl, s, a.tk0 + t) + jj));
+                        xc = a.cc_cur[(long)s * a.coef_ss + t] * dl;
+                        xd = a.dc_cur[(long)s * a.coef_ss + t] * dl;
+                    }
+                    vc[e] = (OP)xc;
+                    vd[e] = (OP)xd;
+                }
+                const long o = (long)s * a.dt1_ss + pk(jj, t8, nkb);
+                st8<OP>(reinterpret_cast<OP*>(a.dct1) + o, vc);
+                st8<OP>(reinterpret_cast<OP*>(a.ddt1) + o, vd);
+            }
         }
     }
 }
@@ -965,7 +1179,8 @@ hipError_t launch_init(float* M, float* S, const float* init, long P, int H, int
     return hipGetLastError();
 }
 
-// Wt = bf16(M)^T per 64 x 64 tile (uses the layer / tile fields of UpdArgs).
+// Wt = bf16(M) packed [dout][din], per 64 x 64 tile (uses the layer / tile
+// fields of UpdArgs).
 __global__ __launch_bounds__(256) void shadow_kernel(UpdArgs u) {
     __shared__ float T[64][65];
     const int tid = threadIdx.x;
@@ -984,13 +1199,14 @@ __global__ __launch_bounds__(256) void shadow_kernel(UpdArgs u) {
     }
     __syncthreads();
     bf16* Wp = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P + u.off[l];
-    for (int idx = tid; idx < 64 * 8; idx += 256) {
-        const int j = idx >> 3, i = (idx & 7) * 8;
-        if (j0 + j < dout && i0 + i < din) {
+    for (int idx = tid; idx < 512; idx += 256) {
+        const int ln = idx & 63, kk = (idx >> 6) & 1, jb = idx >> 7;
+        const int jl = jb * 16 + (ln & 15), il = kk * 32 + 8 * (ln >> 4);
+        if (j0 + jl < dout && i0 + il < din) {
             bf16x8 w;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = (bf16)T[i + e][j];
-            *reinterpret_cast<bf16x8*>(Wp + (long)(j0 + j) * din + i0 + i) = w;
+            for (int e = 0; e < 8; ++e) w[e] = (bf16)T[il + e][jl];
+            *reinterpret_cast<bf16x8*>(Wp + pkf((j0 >> 4) + jb, (i0 >> 5) + kk, din >> 5, ln)) = w;
         }
     }
 }
