@@ -11,60 +11,139 @@ resident in HBM before timing starts.  Prints one JSON line.
 The timed region runs the steps as a caller would (same buffers every step,
 so the library replays each call as a HIP graph).  The same steps then run
 once more with HIP events recorded around every kernel launch on the launch
-stream (events force direct launches); ``roofline.achieved`` = the dominant
-kernel's (the gradient-reduction + state-update kernel) algorithmic bytes per
-launch / its mean event-timed duration.  The fp64 CPU oracle is timed on the
-host as ``cpu_baseline``.
+stream (events force direct launches), which gives each kernel class's mean
+duration.  ``roofline`` describes the class that takes the most time:
+algorithmic bytes (or flops) per launch / its mean event-timed duration.
+``roofline.traffic`` is the HBM traffic per launch from the committed
+rocprofv3 counter summary of that kernel, used only while the kernel source
+still hashes to the value recorded there.  The fp64 CPU oracle is timed on
+the host as ``cpu_baseline``.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "memory tokens/sec (store+retrieve) at dim 384, chunk 64; MFMA util %"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
+KERNEL_SOURCE = os.path.join(ROOT, "test_trained_neural_amd", "csrc", "tm_kernels.hip")
 
 
-def algorithmic(wl, ns):
-    """Per-launch algorithmic work of each kernel class for one chunk step."""
-    P = wl.params
-    b = wl.chunk
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work of each launch (bytes a kernel must move at least once, and
+# the flops of its products), for one tm_forward call of T tokens.
+
+def first_layer_launches(wl, ns, T):
+    """Bytes of every launch of the first-layer step kernel (chunk steps 0..C).
+
+    Step c updates W_0 for chunk c-1 (M_0, S_0 read and written in fp32, its
+    bf16 forward copy written; the keys of chunk c-1, layer 1's Delta and its
+    packed weight copy, SiLU' of chunk c-1 read) and runs chunk c's first-layer
+    forward of [queries of chunk c-1; keys of chunk c] (input rows read;
+    activations, SiLU' and the transposed activations written)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    b, d = wl.chunk, wl.dim
     dims = wl.layer_dims()
-    # update: M, S read + written in fp32, bf16 copy of M written; plus the
-    # chunk's activations (bf16) and deltas (fp32) read once
-    upd_bytes = ns * (18 * P + sum(b * (din * 2 + dout * 4) for din, dout in dims))
-    upd_flops = ns * 4 * b * P                      # two K=b reductions
-    fwd_flops = ns * 2 * (2 * b) * P                # q rows of the previous chunk + k rows
-    bwd_flops = ns * 2 * b * sum(din * dout for din, dout in dims[1:])
-    return dict(upd_bytes=upd_bytes, upd_flops=upd_flops, fwd_flops=fwd_flops, bwd_flops=bwd_flops)
+    h1 = dims[0][1]
+    C = T // b
+    out = []
+    for c in range(C + 1):
+        upd, nq, nk = c >= 1, (b if c >= 1 else 0), (b if c < C else 0)
+        x = 0
+        if upd:
+            x += 18 * d * h1 + d * b * e + 8 * b
+            if wl.depth >= 2:
+                x += b * dims[1][1] * e + h1 * dims[1][1] * e + b * h1 * 4
+            else:
+                x += 2 * h1 * b * e
+        else:
+            x += (2 if wl.dtype == "bf16" else 4) * d * h1      # the layer's weights, read once
+        x += (nq + nk) * d * e
+        if wl.depth >= 2:
+            x += (nq + nk) * h1 * e + nk * h1 * 4 + nk * h1 * e
+        else:
+            x += nq * d * 4 + nk * d * e + 2 * h1 * nk * e
+        out.append(ns * x)
+    return out
 
 
-def cpu_baseline(wl, params, ci, seconds_hint):
-    """The fp64 oracle on a bounded sample of the same workload."""
+def update_launch_bytes(wl, ns):
+    """Bytes of one launch of the update tiles of layers 1..L-1: M, S read and
+    written, the bf16 copy written, the transposed activations and the two
+    theta-weighted delta operands read, layer 1's packed copy written."""
+    e = 2 if wl.dtype == "bf16" else 4
+    b = wl.chunk
+    x = 0
+    for l, (din, dout) in enumerate(wl.layer_dims()):
+        if l == 0:
+            continue
+        x += 18 * din * dout + din * b * e + 2 * dout * b * e
+        if l == 1:
+            x += din * dout * e
+    return ns * x
+
+
+def fwd_flops(wl, ns, T):
+    """Flops of the forward products of layers 1.. (the first layer's run in
+    the step kernel): every key row once and every query row once."""
+    return 2 * 2 * ns * T * sum(a * b for a, b in wl.layer_dims()[1:])
+
+
+def bwd_flops(wl, ns, T):
+    return 2 * ns * T * sum(a * b for a, b in wl.layer_dims()[2:])
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_pmc.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel source sha256\[:16\]: `([0-9a-f]+)`", text)
+    t = re.search(r"HBM bytes per launch: ([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(wl, params, ci, min_seconds=10.0):
+    """The fp64 oracle on a bounded sample of the same workload: the whole
+    step (store + retrieve of every stream's tokens from the initial state),
+    repeated until at least min_seconds of host time have been spent."""
     from oracle import tmref
     from test_trained_neural_amd import inputs as I
-    import numpy as np
     streams = wl.batch * wl.heads
-    # ~12 ms per token per stream for this memory: the whole workload
-    # (2 streams x 1024 tokens) is ~10-15 s on 2 threads
     tokens = wl.tokens_per_call
-    st = I.initial_state(wl, params)
     threads = min(os.cpu_count() or 1, streams)
+    reps = 0
     t0 = time.perf_counter()
-    tmref.forward(wl.dim, wl.depth, wl.expansion, wl.chunk, st, ci.k[:, :tokens], ci.v[:, :tokens],
-                  ci.theta[:, :tokens], ci.eta[:, :tokens], ci.alpha[:, :tokens], q=ci.q[:, :tokens],
-                  n_threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": wl.batch * tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%s: %d streams x %d tokens (the whole step), fp64 C oracle, %.1f s"
-                      % (wl.name, streams, tokens, dt)}
+    while True:
+        st = I.initial_state(wl, params)
+        tmref.forward(wl.dim, wl.depth, wl.expansion, wl.chunk, st, ci.k[:, :tokens], ci.v[:, :tokens],
+                      ci.theta[:, :tokens], ci.eta[:, :tokens], ci.alpha[:, :tokens], q=ci.q[:, :tokens],
+                      n_threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": reps * wl.batch * tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%s: %d x the whole step (%d streams x %d tokens, store + retrieve from the initial "
+                      "state), fp64 C oracle, one thread per stream, %.1f s" % (wl.name, reps, streams, tokens, dt)}
 
 
 def main():
@@ -74,13 +153,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mlp384")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="finish with a plain 256 MiB device copy (scale reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the memory streams of this workload are independent "
               "and a multi-GPU run would only shard them; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     import test_trained_neural_amd as T
     from test_trained_neural_amd import inputs as I
@@ -122,8 +202,7 @@ def main():
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
+    elapsed = time.perf_counter() - t0
 
     # the same steps again with HIP events around every launch (events force
     # direct launches): per-kernel durations for the roofline
@@ -138,34 +217,59 @@ def main():
     e1 = time.perf_counter()
     T.tm_timing_enable(0)
     names = {T.K_SCAN: "scan", T.K_FWD: "fwd", T.K_BWD: "bwd", T.K_UPDATE: "update", T.K_FIRST: "first"}
-    per = {}
-    for c, nm in names.items():
-        per[nm] = T.tm_timing_read(c)
-    upd_ms, upd_n = per["update"]
+    per = {nm: T.tm_timing_read(c) for c, nm in names.items()}
 
-    tokens = Bn * Tn * args.steps
-    work = algorithmic(wl, ns)
-    upd_avg_s = upd_ms / 1e3 / max(upd_n, 1)
-    achieved = work["upd_bytes"] / upd_avg_s / 1e9
+    # algorithmic work per step of each class
+    fl = first_layer_launches(wl, ns, Tn)
+    C = Tn // wl.chunk
+    work = {
+        "first": ("hbm", sum(fl)),
+        "update": ("hbm", update_launch_bytes(wl, ns) * (C if wl.depth >= 2 else 0)),
+        "fwd": ("mfma", fwd_flops(wl, ns, Tn)),
+        "bwd": ("mfma", bwd_flops(wl, ns, Tn)),
+    }
+    kernel_names = {"first": "first_layer_kernel", "update": "update_range_kernel", "fwd": "gemm_kernel",
+                    "bwd": "gemm_kernel", "scan": "scan_kernel"}
     kernels = {}
     for nm, (ms, n) in per.items():
-        kernels[nm] = {"launches_per_step": n / args.steps, "us_per_launch": ms * 1e3 / max(n, 1),
-                       "ms_per_step": ms / args.steps}
-    fwd_s = per["fwd"][0] / 1e3 / args.steps
-    bwd_s = per["bwd"][0] / 1e3 / args.steps
-    # forward: every token row goes through the weights twice per call (as a
-    # key of its chunk and as a query of the same chunk); backward: key rows
-    # through layers 2..L
-    fwd_flops = 2 * 2 * Bn * H * Tn * wl.params
-    bwd_flops = 2 * Bn * H * Tn * sum(a * b for a, b in wl.layer_dims()[1:])
-    kernels["fwd"]["tflops"] = fwd_flops / fwd_s / 1e12
-    kernels["fwd"]["mfma_util"] = kernels["fwd"]["tflops"] / BF16_PEAK_TFLOPS
-    if bwd_s > 0:
-        kernels["bwd"]["tflops"] = bwd_flops / bwd_s / 1e12
-        kernels["bwd"]["mfma_util"] = kernels["bwd"]["tflops"] / BF16_PEAK_TFLOPS
+        kd = {"kernel": kernel_names[nm], "launches_per_step": n / args.steps,
+              "us_per_launch": ms * 1e3 / max(n, 1), "ms_per_step": ms / args.steps}
+        if nm in work and n > 0:
+            kind, amount = work[nm]
+            s_per_step = ms / 1e3 / args.steps
+            if kind == "hbm":
+                kd["GB_per_s"] = amount / s_per_step / 1e9
+                kd["hbm_frac"] = kd["GB_per_s"] / HBM_PEAK_GBS
+            else:
+                peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+                kd["tflops"] = amount / s_per_step / 1e12
+                kd["mfma_util"] = kd["tflops"] / peak
+        kernels[nm] = kd
     kernels["direct_launch_ms_per_step"] = (e1 - e0) / args.steps * 1e3
+
+    dom = max((nm for nm in work if per[nm][1] > 0), key=lambda nm: per[nm][0])
+    kind, amount = work[dom]
+    dms, dn = per[dom]
+    avg_s = dms / 1e3 / dn
+    per_launch = amount / (dn / args.steps)
+    if kind == "hbm":
+        achieved = per_launch / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+        achieved = per_launch / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+    roof["traffic"] = read_traffic(kernel_names[dom], wl.name)
+    roof.update({"kernel": kernel_names[dom], "launches": dn, "avg_us": avg_s * 1e6,
+                 ("bytes_per_launch" if kind == "hbm" else "flops_per_launch"): per_launch,
+                 "timing": "HIP events around each launch on its stream, second pass of the same steps",
+                 "kernel_source_sha256_16": kernel_source_hash()})
+
+    tokens = Bn * Tn * args.steps
     out = {
-        "metric": "memory tokens/sec (store+retrieve) at dim 384, chunk 64; MFMA util %",
+        "metric": METRIC,
         "value": tokens / elapsed,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -176,22 +280,24 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded; shapes of the README example)",
+        "data": "synthetic (seeded; shapes of the README example, gates with fixed logit offsets)",
         "config": {"workload": wl.name, "batch": Bn, "seq": Tn, "heads": H, "dim": d,
                    "hidden": wl.hidden, "depth": wl.depth, "chunk": wl.chunk,
-                   "step": "tm_state_init + tm_forward"},
-        "roofline": {"bound": "hbm", "kernel": "update_kernel (gradient reduction + state update)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "launches": upd_n, "avg_us": upd_avg_s * 1e6,
-                     "bytes_per_launch": work["upd_bytes"],
-                     "timing": "HIP events around each launch, second pass of the same steps"},
+                   "step": "tm_state_init + tm_forward (store + retrieve)"},
+        "roofline": roof,
         "kernels": kernels,
     }
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, params, ci, 15.0)
-        out["cpu_baseline"]["vs_gpu"] = out["value"] / out["cpu_baseline"]["value"]
+        out["cpu_baseline"] = cpu_baseline(wl, params, ci)
+        out["cpu_baseline"]["gpu_over_cpu"] = out["value"] / out["cpu_baseline"]["value"]
+    if args.calib_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(json.dumps(out), flush=True)
 
 
