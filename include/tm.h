@@ -91,21 +91,22 @@ tm_status tm_state_init(const tm_ctx* ctx, void* state, int batch, int heads,
 /* Store n_tokens tokens per stream ("Titans, explained" steps 2-4 in the
  * chunked form of step 6).  n_tokens must be a multiple of the chunk
  * (TM_ERR_SHAPE otherwise); chunk boundaries are counted from the start of
- * every call, so calls must stay chunk-aligned.  n_tokens == 0 is a no-op. */
+ * every call, so calls must stay chunk-aligned.  n_tokens == 0 is a no-op
+ * that returns TM_OK without examining the token and gate pointers. */
 tm_status tm_store(const tm_ctx* ctx, void* state, const void* k, const void* v,
                    const float* theta, const float* eta, const float* alpha,
                    int batch, int heads, int n_tokens, tm_dtype dtype,
                    void* workspace, void* stream);
 
 /* y = M(q) for every query through the current weights (step 5).  The state
- * is not written.  Any n_tokens >= 0. */
+ * is not written.  Any n_tokens >= 0 (0: a no-op, as for tm_store). */
 tm_status tm_retrieve(const tm_ctx* ctx, const void* state, const void* q, float* y,
                       int batch, int heads, int n_tokens, tm_dtype dtype,
                       void* workspace, void* stream);
 
 /* Store and retrieve: for each chunk c, store chunk c, then read chunk c's
  * queries through the written memory.  Equivalent to alternating tm_store and
- * tm_retrieve chunk by chunk. */
+ * tm_retrieve chunk by chunk.  n_tokens == 0 is a no-op, as for tm_store. */
 tm_status tm_forward(const tm_ctx* ctx, void* state, const void* k, const void* v,
                      const void* q, const float* theta, const float* eta,
                      const float* alpha, float* y, int batch, int heads,

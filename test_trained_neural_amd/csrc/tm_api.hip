@@ -739,10 +739,10 @@ tm_status tm_store(const tm_ctx* c, void* state, const void* k, const void* v, c
                    tm_dtype dtype, void* ws, void* stream) {
     tm_status rc = check_common(c, state, batch, heads, n_tokens, dtype, ws);
     if (rc != TM_OK) return rc;
+    if (n_tokens == 0) return TM_OK;   // nothing to store: the token pointers are not examined
     if (!tok_ok(k) || !tok_ok(v) || !gate_ok(theta) || !gate_ok(eta) || !gate_ok(alpha))
         return TM_ERR_INVALID;
     if (n_tokens % c->chunk != 0) return TM_ERR_SHAPE;
-    if (n_tokens == 0) return TM_OK;
     return with_graph(c, make_key(1, batch, heads, n_tokens, dtype, {state, k, v, theta, eta, alpha, ws}),
                       static_cast<hipStream_t>(stream), [&](hipStream_t st) {
         return run_store(c, state, k, v, nullptr, theta, eta, alpha, nullptr, batch, heads, n_tokens,
@@ -755,11 +755,11 @@ tm_status tm_forward(const tm_ctx* c, void* state, const void* k, const void* v,
                      int heads, int n_tokens, tm_dtype dtype, void* ws, void* stream) {
     tm_status rc = check_common(c, state, batch, heads, n_tokens, dtype, ws);
     if (rc != TM_OK) return rc;
+    if (n_tokens == 0) return TM_OK;
     if (!tok_ok(k) || !tok_ok(v) || !tok_ok(q) || !tok_ok(y) || !gate_ok(theta) || !gate_ok(eta) ||
         !gate_ok(alpha))
         return TM_ERR_INVALID;
     if (n_tokens % c->chunk != 0) return TM_ERR_SHAPE;
-    if (n_tokens == 0) return TM_OK;
     return with_graph(c, make_key(2, batch, heads, n_tokens, dtype, {state, k, v, q, theta, eta, alpha, y, ws}),
                       static_cast<hipStream_t>(stream), [&](hipStream_t st) {
         return run_store(c, state, k, v, q, theta, eta, alpha, y, batch, heads, n_tokens, dtype, ws, st);
@@ -770,8 +770,8 @@ tm_status tm_retrieve(const tm_ctx* c, const void* state_v, const void* q, float
                       int heads, int n_tokens, tm_dtype dtype, void* ws_v, void* stream) {
     tm_status rc = check_common(c, state_v, batch, heads, n_tokens, dtype, ws_v);
     if (rc != TM_OK) return rc;
-    if (!tok_ok(q) || !tok_ok(y)) return TM_ERR_INVALID;
     if (n_tokens == 0) return TM_OK;
+    if (!tok_ok(q) || !tok_ok(y)) return TM_ERR_INVALID;
     char* state = const_cast<char*>(static_cast<const char*>(state_v));   // read only below
     char* ws = static_cast<char*>(ws_v);
     const long ns = (long)batch * heads;

@@ -80,5 +80,9 @@ def test_call_validation_before_launch():
     # empty calls are no-ops that succeed without touching anything
     assert L.tm_store(c, A, A, A, G, G, G, 1, 1, 0, T.TM_BF16, A, st) == T.TM_OK
     assert L.tm_retrieve(c, A, A, A, 1, 1, 0, T.TM_BF16, A, st) == T.TM_OK
+    # ... also with the (empty) token arrays given as null pointers
+    assert L.tm_store(c, A, None, None, None, None, None, 1, 1, 0, T.TM_BF16, A, st) == T.TM_OK
+    assert L.tm_forward(c, A, None, None, None, None, None, None, None, 1, 1, 0, T.TM_BF16, A, st) == T.TM_OK
+    assert L.tm_retrieve(c, A, None, None, 1, 1, 0, T.TM_F32, A, st) == T.TM_OK
     assert L.tm_status_str(T.TM_ERR_SHAPE).decode().startswith("n_tokens")
     T.tm_destroy(c)
