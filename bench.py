@@ -49,13 +49,15 @@ def kernel_source_hash():
 # the flops of its products), for one tm_forward call of T tokens.
 
 def first_layer_launches(wl, ns, T):
-    """Bytes of every launch of the first-layer step kernel (chunk steps 0..C).
+    """Bytes of every launch of the chunk-step kernel (chunk steps 0..C).
 
     Step c updates W_0 for chunk c-1 (M_0, S_0 read and written in fp32, its
     bf16 forward copy written; the keys of chunk c-1, layer 1's Delta and its
     packed weight copy, SiLU' of chunk c-1 read) and runs chunk c's first-layer
     forward of [queries of chunk c-1; keys of chunk c] (input rows read;
-    activations, SiLU' and the transposed activations written)."""
+    activations, SiLU' and the transposed activations written).  The same
+    launch carries chunk c-1's update tiles of layers 1..L-1
+    (update_launch_bytes)."""
     e = 2 if wl.dtype == "bf16" else 4
     b, d = wl.chunk, wl.dim
     dims = wl.layer_dims()
@@ -78,7 +80,7 @@ def first_layer_launches(wl, ns, T):
             x += (nq + nk) * h1 * e + nk * h1 * 4 + nk * h1 * e
         else:
             x += nq * d * 4 + nk * d * e + 2 * h1 * nk * e
-        out.append(ns * x)
+        out.append(ns * x + (update_launch_bytes(wl, ns) if upd and wl.depth >= 2 else 0))
     return out
 
 
@@ -228,7 +230,7 @@ def main():
         "fwd": ("mfma", fwd_flops(wl, ns, Tn)),
         "bwd": ("mfma", bwd_flops(wl, ns, Tn)),
     }
-    kernel_names = {"first": "first_layer_kernel", "update": "update_range_kernel", "fwd": "gemm_kernel",
+    kernel_names = {"first": "first_layer_kernel", "update": "update_kernel", "fwd": "gemm_kernel",
                     "bwd": "gemm_kernel", "scan": "scan_kernel"}
     kernels = {}
     for nm, (ms, n) in per.items():

@@ -28,14 +28,6 @@ struct tm_ctx {
     std::mutex* gmu;
     std::vector<GraphEntry>* graphs;
     std::vector<std::pair<int, hipStream_t>>* capture_streams;
-    // per device: a second capture stream and two events, used to fork the
-    // independent kernels of a chunk step into parallel graph branches
-    struct Fork {
-        int dev;
-        hipStream_t side;
-        hipEvent_t fork, join;
-    };
-    std::vector<Fork>* forks;
     unsigned long long stamp;
     int dim, depth, expansion, chunk, hidden, L;
     int din[MAXL], dout[MAXL];
@@ -49,7 +41,6 @@ struct tm_ctx {
 namespace {
 
 constexpr long RET_ROWS = 2048;   // query rows per stream per retrieve pass
-constexpr bool kForkChunkStep = false;
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -552,29 +543,6 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     const int tile1 = c->tbase[c->L > 1 ? 1 : c->L];
     const int ntile_rest = c->tbase[c->L] - tile1;
 
-    // while this call is being captured into a graph, the first-layer
-    // blocks and the other layers' update tiles become parallel branches
-    tm_ctx::Fork* fk = nullptr;
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    // (measured: joining two hardware queues inside a graph costs ~10 us, more
-    // than running the two kernels back to back, so the fork stays off)
-    if (kForkChunkStep && ntile_rest > 0 && hipStreamIsCapturing(st, &cap) == hipSuccess &&
-        cap == hipStreamCaptureStatusActive) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return TM_ERR_HIP;
-        tm_ctx* mc = const_cast<tm_ctx*>(c);
-        for (auto& f : *mc->forks)
-            if (f.dev == dev) fk = &f;
-        if (!fk) {
-            tm_ctx::Fork f{dev, nullptr, nullptr, nullptr};
-            if (hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking) != hipSuccess) return TM_ERR_HIP;
-            if (hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess) return TM_ERR_HIP;
-            if (hipEventCreateWithFlags(&f.join, hipEventDisableTiming) != hipSuccess) return TM_ERR_HIP;
-            mc->forks->push_back(f);
-            fk = &mc->forks->back();
-        }
-    }
-
     for (int ci = 0; ci <= C; ++ci) {
         a.do_update = ci >= 1;
         a.nq = (q && ci >= 1) ? b : 0;
@@ -584,13 +552,14 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         a.u.chunk = ci - 1;
         a.tq0 = (ci - 1) * b;
         a.tk0 = ci * b;
+        // steps that skip a part still get valid addresses for its operands
+        // (the step kernel loads them unconditionally and drops the values)
+        const int cprev = ci >= 1 ? ci - 1 : 0;
         a.xq = (q && ci >= 1) ? ws + w.xq + (size_t)(ci - 1) * w.xc * esz : nullptr;
-        a.xk = ci < C ? ws + w.xk + (size_t)ci * w.xc * esz : nullptr;
-        if (ci >= 1) {
-            a.kt_prev = ws + w.kt + (size_t)(ci - 1) * c->dim * w.bp * esz;
-            a.cc_prev = reinterpret_cast<const float*>(ws + w.cc) + (ci - 1) * b;
-            a.dc_prev = reinterpret_cast<const float*>(ws + w.dc) + (ci - 1) * b;
-        }
+        a.xk = ws + w.xk + (size_t)(ci < C ? ci : 0) * w.xc * esz;
+        a.kt_prev = ws + w.kt + (size_t)cprev * c->dim * w.bp * esz;
+        a.cc_prev = reinterpret_cast<const float*>(ws + w.cc) + cprev * b;
+        a.dc_prev = reinterpret_cast<const float*>(ws + w.dc) + cprev * b;
         a.cc_cur = reinterpret_cast<const float*>(ws + w.cc) + (ci < C ? ci : 0) * b;
         a.dc_cur = reinterpret_cast<const float*>(ws + w.dc) + (ci < C ? ci : 0) * b;
         if (c->L >= 2) {
@@ -600,21 +569,12 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
             a.ht1 = ws + w.ht1[ci & 1];
         }
         if (!a.do_update && !a.do_fwd) continue;
-        const bool upd_rest = a.do_update && ntile_rest > 0;
-        if (upd_rest && fk) {
-            if (hipEventRecord(fk->fork, st) != hipSuccess) return TM_ERR_HIP;
-            if (hipStreamWaitEvent(fk->side, fk->fork, 0) != hipSuccess) return TM_ERR_HIP;
-            if (launch_update_range(a.u, tile1, ntile_rest, (int)ns, f32 ? 1 : 0, fk->side) != hipSuccess)
-                return TM_ERR_HIP;
-            if (hipEventRecord(fk->join, fk->side) != hipSuccess) return TM_ERR_HIP;
-        } else if (upd_rest) {
-            if (timed(K_UPD, st, [&] { return launch_update_range(a.u, tile1, ntile_rest, (int)ns, f32 ? 1 : 0, st); }) !=
-                hipSuccess)
-                return TM_ERR_HIP;
-        }
+        // one launch: the first-layer blocks plus chunk c-1's update tiles of
+        // the other layers (independent of each other)
+        a.upd_tile0 = tile1;
+        a.upd_ntiles = a.do_update ? ntile_rest : 0;
         if (timed(K_FIRST, st, [&] { return launch_first(a, (int)ns, f32 ? 1 : 0, st); }) != hipSuccess)
             return TM_ERR_HIP;
-        if (upd_rest && fk && hipStreamWaitEvent(st, fk->join, 0) != hipSuccess) return TM_ERR_HIP;
         if (a.do_fwd && c->L >= 2) {
             FwdRows fr;
             fr.nq = a.nq;
@@ -653,12 +613,10 @@ tm_status tm_create(int dim, int depth, int expansion, int chunk, tm_ctx** out) 
     c->gmu = new (std::nothrow) std::mutex;
     c->graphs = new (std::nothrow) std::vector<GraphEntry>;
     c->capture_streams = new (std::nothrow) std::vector<std::pair<int, hipStream_t>>;
-    c->forks = new (std::nothrow) std::vector<tm_ctx::Fork>;
-    if (!c->gmu || !c->graphs || !c->capture_streams || !c->forks) {
+    if (!c->gmu || !c->graphs || !c->capture_streams) {
         delete c->gmu;
         delete c->graphs;
         delete c->capture_streams;
-        delete c->forks;
         delete c;
         return TM_ERR_INVALID;
     }
@@ -693,12 +651,6 @@ void tm_destroy(tm_ctx* ctx) {
     for (GraphEntry& e : *ctx->graphs)
         if (e.exec) (void)hipGraphExecDestroy(e.exec);
     for (auto& pr : *ctx->capture_streams) (void)hipStreamDestroy(pr.second);
-    for (auto& f : *ctx->forks) {
-        (void)hipStreamDestroy(f.side);
-        (void)hipEventDestroy(f.fork);
-        (void)hipEventDestroy(f.join);
-    }
-    delete ctx->forks;
     delete ctx->graphs;
     delete ctx->capture_streams;
     delete ctx->gmu;

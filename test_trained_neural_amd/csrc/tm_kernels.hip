@@ -605,10 +605,14 @@ __device__ __forceinline__ typename Frag<OP>::T tok8(const OP* p, int t0, int b,
     return v;
 }
 
+// tid: the thread's index among the tile's 256 threads.  A tile that is
+// not live (padding of a workgroup that carries two tiles) computes on a
+// valid tile and stores nothing; it still takes part in every barrier.
 template <class OP>
-__device__ void update_tile(const UpdArgs& u, int s, int tile, float (*UM)[65], float (*US)[65]) {
+__device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool live, float (*UM)[65],
+                            float (*US)[65]) {
     typedef typename Frag<OP>::T F;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = tid >> 6;
     int l = 0;
     while (l + 1 < u.L && tile >= u.tbase[l + 1]) ++l;
     tile -= u.tbase[l];
@@ -638,21 +642,20 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, float (*UM)[65], 
     // operand fragments first (vector loads complete in issue order, so
     // the matrix work below waits only for these), then this tile's M and
     // S, whose latency overlaps the matrix work and the LDS exchange
+    // (every load is unconditional, from a clamped address, so the compiler
+    // can wait for exactly the loads each step needs; unused values are
+    // replaced by zeros)
     F fa[2][2], fc[2][2], fd[2][2];   // [k step][block]
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int t0 = ks * 32 + kofs;
         const bool full = t0 + 8 <= b;
+        const int kc = min(ks, nkb - 1);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            fa[ks][m] = zero_frag<OP>();
-            fc[ks][m] = zero_frag<OP>();
-            fd[ks][m] = zero_frag<OP>();
-            if (ks < nkb) {
-                fa[ks][m] = tok8<OP>(A + pkf(ab[m], ks, nkb, lane), t0, b, full);
-                fc[ks][m] = tok8<OP>(Bc + pkf(bb[m], ks, nkb, lane), t0, b, full);
-                fd[ks][m] = tok8<OP>(Bd + pkf(bb[m], ks, nkb, lane), t0, b, full);
-            }
+            fa[ks][m] = tok8<OP>(A + pkf(ab[m], kc, nkb, lane), t0, b, full);
+            fc[ks][m] = tok8<OP>(Bc + pkf(bb[m], kc, nkb, lane), t0, b, full);
+            fd[ks][m] = tok8<OP>(Bd + pkf(bb[m], kc, nkb, lane), t0, b, full);
         }
     }
     float* Mp = u.M + (long)s * u.P + u.off[l];
@@ -661,15 +664,10 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, float (*UM)[65], 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int idx = tid + 256 * q;
-        const int gi = i0 + (idx >> 4), gj = j0 + (idx & 15) * 4;
-        if (gi < din && gj < dout) {
-            const long o = (long)gi * dout + gj;
-            mreg[q] = *reinterpret_cast<const f32x4*>(Mp + o);
-            sreg[q] = *reinterpret_cast<const f32x4*>(Sp + o);
-        } else {
-            mreg[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            sreg[q] = mreg[q];
-        }
+        const int gi = min(i0 + (idx >> 4), din - 1), gj = min(j0 + (idx & 15) * 4, dout - 4);
+        const long o = (long)gi * dout + gj;
+        mreg[q] = *reinterpret_cast<const f32x4*>(Mp + o);   // outside the layer: not used
+        sreg[q] = *reinterpret_cast<const f32x4*>(Sp + o);
     }
     f32x4 am[2][2], as[2][2];
 #pragma unroll
@@ -678,7 +676,7 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, float (*UM)[65], 
         for (int n = 0; n < 2; ++n) { am[m][n] = (f32x4){0.f, 0.f, 0.f, 0.f}; as[m][n] = am[m][n]; }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        if (ks * 32 >= bp) break;
+        if (ks >= nkb) break;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const F av = aok[m] ? fa[ks][m] : zero_frag<OP>();
@@ -710,7 +708,7 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, float (*UM)[65], 
         const int idx = tid + 256 * q;
         const int i = idx >> 4, j = (idx & 15) * 4;
         const int gi = i0 + i, gj = j0 + j;
-        if (gi < din && gj < dout) {
+        if (live && gi < din && gj < dout) {
             const long o = (long)gi * dout + gj;
             const f32x4 m = mreg[q], sv = sreg[q];
             f32x4 mn, sn;
@@ -732,7 +730,7 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, float (*UM)[65], 
     for (int idx = tid; idx < 512; idx += 256) {
         const int ln = idx & 63, kk = (idx >> 6) & 1, jb = idx >> 7;
         const int jl = jb * 16 + (ln & 15), il = kk * 32 + 8 * (ln >> 4);
-        if (j0 + jl < dout && i0 + il < din) {
+        if (live && j0 + jl < dout && i0 + il < din) {
             bf16x8 w;
 #pragma unroll
             for (int e = 0; e < 8; ++e) w[e] = (bf16)UM[il + e][jl];
@@ -741,7 +739,7 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, float (*UM)[65], 
     }
     // layer 1's operand-type copy (packed [din][dout]) for the next chunk's
     // in-place backward of the first layer
-    if (l == 1 && u.wr_next) {
+    if (live && l == 1 && u.wr_next) {
         OP* wr = reinterpret_cast<OP*>(u.wr_next) + (long)s * u.wr_ss;
         for (int idx = tid; idx < 512; idx += 256) {
             const int ln = idx & 63, kk = (idx >> 6) & 1, ib = idx >> 7;
@@ -754,14 +752,14 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, float (*UM)[65], 
             }
         }
     }
-    if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
+    if (__ballot(bad) != 0 && lane == 0 && live) atomicOr(u.flag, 1);
 }
 
 template <class OP>
 __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
     __shared__ float UM[64][65];
     __shared__ float US[64][65];
-    update_tile<OP>(u, blockIdx.y, blockIdx.x, UM, US);
+    update_tile<OP>(u, blockIdx.y, blockIdx.x, threadIdx.x, true, UM, US);
 }
 
 hipError_t launch_update(const UpdArgs& u, int ntiles, int ns, int f32, hipStream_t st) {
@@ -779,10 +777,39 @@ constexpr int WPAD = 8;     // LDS row padding (elements)
 constexpr int RPAD = 1;     // LDS row padding of the partial-sum tiles (floats)
 constexpr int FW = 8;       // waves of a first-layer workgroup
 
+constexpr int FRED = FW / 2;   // partial tiles kept in LDS (two-round reduction)
+constexpr size_t UPD_PAIR_LDS = 2 * 2 * 64 * 65 * 4;   // two update tiles: U_M, U_S each
+
 static size_t first_lds_bytes(int dim, int bp, int f32) {
     const size_t e = f32 ? 4 : 2;
     return (size_t)JW * (dim + WPAD) * e + 2 * (size_t)JW * (bp + WPAD) * e +
-           (size_t)FW * 128 * (JW + RPAD) * 4;
+           (size_t)FRED * 128 * (JW + RPAD) * 4;
+}
+
+// The waves' partial tiles acc (nb row blocks of 16 x JW) summed into FRED
+// LDS slots in two rounds: waves FRED.. store theirs, waves 0..FRED-1 add
+// their own.  Ends with a barrier; the caller sums the FRED slots.
+template <int NB>
+__device__ __forceinline__ void partial_tiles(float* red, const f32x4* acc, int nb, int rows, int wave, int lane,
+                                              int RP) {
+    const int g4 = 4 * (lane >> 4), jl = lane & 15;
+    float* slot = red + (wave % FRED) * rows * RP;
+    if (wave >= FRED) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+            if (m < nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) slot[(16 * m + g4 + e) * RP + jl] = acc[m][e];
+    }
+    __syncthreads();
+    if (wave < FRED) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+            if (m < nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) slot[(16 * m + g4 + e) * RP + jl] += acc[m][e];
+    }
+    __syncthreads();
 }
 
 // Prefetch depths (in K steps or row blocks) of the first-layer workgroup:
@@ -798,6 +825,18 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     constexpr int PA = FirstDepth<OP>::A, PB = FirstDepth<OP>::B, PC = FirstDepth<OP>::C;
     constexpr int NT = FW * 64;
     extern __shared__ __attribute__((aligned(16))) char lds[];
+    if ((int)blockIdx.x >= a.nb1) {
+        // the other layers' update tiles of chunk c-1, two per workgroup
+        // (threads 0..255 and 256..511, each half with its own LDS tiles);
+        // they touch nothing the first-layer blocks read or write
+        const int half = threadIdx.x >> 8;
+        int t = 2 * ((int)blockIdx.x - a.nb1) + half;
+        const bool live = t < a.upd_ntiles;
+        if (!live) t = a.upd_ntiles - 1;
+        float(*UM)[65] = reinterpret_cast<float(*)[65]>(lds) + half * 128;
+        update_tile<OP>(a.u, blockIdx.y, a.upd_tile0 + t, threadIdx.x & 255, live, UM, UM + 64);
+        return;
+    }
     const UpdArgs& u = a.u;
     const int s = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -810,7 +849,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     OP* Wn = reinterpret_cast<OP*>(lds);   // [JW][WP]: the block's columns of W_0, K-contiguous
     OP* DcT = Wn + JW * WP;                 // [JW][DP]: (c Delta_0)^T of chunk c-1
     OP* DdT = DcT + JW * DP;
-    float* red = reinterpret_cast<float*>(DdT + JW * DP);   // [FW][rows][RP] partial tiles
+    float* red = reinterpret_cast<float*>(DdT + JW * DP);   // [FRED][rows][RP] partial tiles
     float* M0 = u.M + (long)s * u.P;
     float* S0 = u.S + (long)s * u.P;
     bf16* Wt0 = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P;
@@ -831,32 +870,32 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     for (int m = 0; m < 4; ++m) {
         tok[m] = 16 * m + (lane & 15) < b;
         const int mb = 16 * m < b ? m : 0;   // token blocks past the chunk: valid address, dropped
-        Ad[m] = bwd ? reinterpret_cast<const OP*>(a.dlt2) + (long)s * a.dlt2_ss + pkf(mb, 0, nsA, lane) : nullptr;
+        // without the backward: a harmless read of the first 2 KB of M
+        Ad[m] = bwd ? reinterpret_cast<const OP*>(a.dlt2) + (long)s * a.dlt2_ss + pkf(mb, 0, nsA, lane)
+                    : reinterpret_cast<const OP*>(M0) + lane * 8;
     }
     const OP* Bw = bwd ? reinterpret_cast<const OP*>(a.wr_prev) + (long)s * a.wr_ss + pkf(j0 >> 4, 0, nsA, lane)
-                       : nullptr;
+                       : reinterpret_cast<const OP*>(M0) + lane * 8;
+    // (every load below is unconditional and from a valid address, whether
+    // or not this step uses it, so that the compiler waits for exactly the
+    // loads each phase needs; the host points unused operands at valid memory)
     F ra[PA][4], rb[PA];
-    if (bwd) {
 #pragma unroll
-        for (int p = 0; p < PA; ++p) {
-            const long k0 = (long)min(kbA + p, klA) << 9;
+    for (int p = 0; p < PA; ++p) {
+        const long k0 = (long)min(kbA + p, klA) << 9;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) ra[p][m] = cvt<OP>(ld8(Ad[m] + k0));
-            rb[p] = cvt<OP>(ld8(Bw + k0));
-        }
+        for (int m = 0; m < 4; ++m) ra[p][m] = cvt<OP>(ld8(Ad[m] + k0));
+        rb[p] = cvt<OP>(ld8(Bw + k0));
     }
     // (2) the backward epilogue's SiLU' and coefficients (2 elements per thread)
     constexpr int EA = 64 * JW / NT;
     float sl[EA], cv[EA], dv[EA];
-    if (bwd) {
 #pragma unroll
-        for (int q = 0; q < EA; ++q) {
-            const int idx = tid + NT * q, t = idx / JW, jj = j0 + idx % JW;
-            const bool ok = t < b && jj < h1;
-            sl[q] = ok ? a.dsl1[(long)s * a.dsl1_ss + (long)t * h1 + jj] : 0.f;
-            cv[q] = ok ? a.cc_prev[(long)s * a.coef_ss + t] : 0.f;
-            dv[q] = ok ? a.dc_prev[(long)s * a.coef_ss + t] : 0.f;
-        }
+    for (int q = 0; q < EA; ++q) {
+        const int idx = tid + NT * q, t = min(idx / JW, b - 1), jj = j0 + idx % JW;
+        sl[q] = *(bwd ? a.dsl1 + (long)s * a.dsl1_ss + (long)t * h1 + jj : M0 + (tid & 63));
+        cv[q] = a.cc_prev[(long)s * a.coef_ss + t];
+        dv[q] = a.dc_prev[(long)s * a.coef_ss + t];
     }
     // (3) the update's row blocks of this wave: keys^T fragments, M and S
     const int nrb = d >> 4;
@@ -865,7 +904,8 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     F kf[PB][2];
     float mr[PB][4], sr[PB][4];
     auto load_rb = [&](int p, int n) {
-        const int rbk = wave + FW * min(n, mineB - 1);
+        // a wave without row blocks (mineB == 0) still loads a valid block
+        const int rbk = min(wave + FW * max(min(n, mineB - 1), 0), nrb - 1);
         const int ib = 16 * rbk;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -877,10 +917,8 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             sr[p][e] = S0[o];
         }
     };
-    if (mineB > 0) {
 #pragma unroll
-        for (int p = 0; p < PB; ++p) load_rb(p, p);
-    }
+    for (int p = 0; p < PB; ++p) load_rb(p, p);
     // (4) the forward's rows (all 16-row blocks), K = dim split over the waves
     const int R = a.nq + a.nk;
     const int nrow = (R + 15) >> 4;
@@ -895,20 +933,14 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
         int r = 16 * m + (lane & 15);
         rok[m] = r < R;
         if (!rok[m]) r = R > 0 ? R - 1 : 0;
-        Ax[m] = nullptr;
-        if (R > 0) {
-            const bool isq = r < a.nq;
-            Ax[m] = reinterpret_cast<const OP*>(isq ? a.xq : a.xk) + (long)s * a.x_ss + pk(isq ? r : r - a.nq, kofs, nsC);
-        }
+        const bool isq = r < a.nq;
+        Ax[m] = reinterpret_cast<const OP*>(isq ? a.xq : a.xk) + (long)s * a.x_ss + pk(isq ? r : r - a.nq, kofs, nsC);
     }
     F rx[PC][8];
-    if (a.do_fwd) {
 #pragma unroll
-        for (int p = 0; p < PC; ++p)
+    for (int p = 0; p < PC; ++p)
 #pragma unroll
-            for (int m = 0; m < 8; ++m)
-                if (m < nrow) rx[p][m] = cvt<OP>(ld8(Ax[m] + ((long)min(kbC + p, klC) << 9)));
-    }
+        for (int m = 0; m < 8; ++m) rx[p][m] = cvt<OP>(ld8(Ax[m] + ((long)min(kbC + p, klC) << 9)));
 
     // ================= chunk c-1's update of the block's columns =================
     if (upd) {
@@ -932,20 +964,15 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
                     }
                 }
             }
-            float* mine = red + wave * 64 * RP;
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mine[(16 * m + g4 + e) * RP + jl] = acc[m][e];
-            __syncthreads();
+            partial_tiles<4>(red, acc, 4, 64, wave, lane, RP);
 #pragma unroll
             for (int q = 0; q < EA; ++q) {
                 const int idx = tid + NT * q, t = idx / JW, cl = idx % JW;
                 if (t >= bp) continue;
                 float z = 0.f;
 #pragma unroll
-                for (int w = 0; w < FW; ++w) z += red[(w * 64 + t) * RP + cl];
-                const float dl = z * sl[q];
+                for (int w = 0; w < FRED; ++w) z += red[(w * 64 + t) * RP + cl];
+                const float dl = t < b ? z * sl[q] : 0.f;   // padding tokens: zero
                 DcT[cl * DP + t] = (OP)(cv[q] * dl);
                 DdT[cl * DP + t] = (OP)(dv[q] * dl);
             }
@@ -1054,20 +1081,14 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
                 }
             }
         }
-        float* mine = red + wave * 128 * RP;
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-            if (m < nrow)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mine[(16 * m + g4 + e) * RP + jl] = acc[m][e];
+        partial_tiles<8>(red, acc, nrow, 128, wave, lane, RP);
     }
-    __syncthreads();
-    // z of every (row, column): the waves' partial tiles summed into slot 0
+    // z of every (row, column): the partial tiles summed into slot 0
     for (int idx = tid; idx < R * JW; idx += NT) {
         const int r = idx / JW, cl = idx - r * JW;
         float z = 0.f;
 #pragma unroll
-        for (int w = 0; w < FW; ++w) z += red[(w * 128 + r) * RP + cl];
+        for (int w = 0; w < FRED; ++w) z += red[(w * 128 + r) * RP + cl];
         red[r * RP + cl] = z;
     }
     __syncthreads();
@@ -1140,8 +1161,10 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
 }
 
 hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st) {
-    dim3 grid(a.nb1, ns);
-    const size_t lds = first_lds_bytes(a.dim, a.u.bp, f32);
+    const int pairs = (a.upd_ntiles + 1) / 2;
+    dim3 grid(a.nb1 + pairs, ns);
+    size_t lds = first_lds_bytes(a.dim, a.u.bp, f32);
+    if (pairs > 0 && lds < UPD_PAIR_LDS) lds = UPD_PAIR_LDS;
     if (f32) hipLaunchKernelGGL(first_layer_kernel<float>, grid, dim3(FW * 64), lds, st, a);
     else hipLaunchKernelGGL(first_layer_kernel<bf16>, grid, dim3(FW * 64), lds, st, a);
     return hipGetLastError();
@@ -1151,7 +1174,7 @@ template <class OP>
 __global__ __launch_bounds__(256) void update_range_kernel(UpdArgs u, int tile0) {
     __shared__ float UM[64][65];
     __shared__ float US[64][65];
-    update_tile<OP>(u, blockIdx.y, tile0 + blockIdx.x, UM, US);
+    update_tile<OP>(u, blockIdx.y, tile0 + blockIdx.x, threadIdx.x, true, UM, US);
 }
 
 hipError_t launch_update_range(const UpdArgs& u, int tile0, int ntiles, int ns, int f32, hipStream_t st) {
