@@ -2,8 +2,11 @@
 // and workspace layouts, and the per-call launch sequence (the chunk loop).
 //
 // State blob: [header 256 B][M fp32 ns*P][S fp32 ns*P][Wt bf16 ns*P], each
-// region 256-byte aligned; per stream the layers follow each other, W_l is
-// row-major [d_in][d_out] in M and S and transposed ([d_out][d_in]) in Wt.
+// region 256-byte aligned; per stream the layers follow each other.  In M and
+// S, W_0 is in the matrix instruction's accumulator order (cf0) and the other
+// layers row-major [d_in][d_out]; Wt holds every layer fragment-packed
+// [d_out][d_in].  Export and import convert to and from the canonical
+// row-major form.
 #include <mutex>
 #include <new>
 #include <string.h>
@@ -352,8 +355,9 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
             }
         }
         if (f32) {
-            // fp32 operands straight from the fp32 master, row-major [din][dout]
-            g.bmode = B_STRIDED;
+            // fp32 operands straight from the fp32 master: row-major [din][dout],
+            // layer 0 in accumulator order
+            g.bmode = l == 0 ? B_CFRAG : B_STRIDED;
             g.b = state + sl.M + (size_t)c->off[l] * 4;
             g.b_ss = c->P;
             g.b_ld = c->dout[l];
@@ -681,7 +685,8 @@ tm_status tm_state_init(const tm_ctx* c, void* state, int batch, int heads, cons
         UpdArgs u = base_upd(c, s, ns);
         if (launch_header(reinterpret_cast<StateHeader*>(s), c->hash, batch, heads, st) != hipSuccess)
             return TM_ERR_HIP;
-        if (launch_init(u.M, u.S, init, c->P, heads, (int)ns, st) != hipSuccess) return TM_ERR_HIP;
+        if (launch_init(u.M, u.S, init, c->P, heads, (int)ns, c->din[0], c->dout[0], st) != hipSuccess)
+            return TM_ERR_HIP;
         return hip_status(launch_shadow(u, c->tbase[c->L], (int)ns, st));
     });
 }
@@ -756,8 +761,8 @@ tm_status tm_state_export(const tm_ctx* c, const void* state, int batch, int hea
     StateLayout sl = state_layout(c, ns);
     const char* s = static_cast<const char*>(state);
     return hip_status(launch_export(reinterpret_cast<const float*>(s + sl.M),
-                                    reinterpret_cast<const float*>(s + sl.S), dst, c->P, (int)ns,
-                                    static_cast<hipStream_t>(stream)));
+                                    reinterpret_cast<const float*>(s + sl.S), dst, c->P, (int)ns, c->din[0],
+                                    c->dout[0], static_cast<hipStream_t>(stream)));
 }
 
 tm_status tm_state_import(const tm_ctx* c, void* state, int batch, int heads, const float* src,
@@ -771,7 +776,7 @@ tm_status tm_state_import(const tm_ctx* c, void* state, int batch, int heads, co
     UpdArgs u = base_upd(c, s, ns);
     if (launch_header(reinterpret_cast<StateHeader*>(s), c->hash, batch, heads, st) != hipSuccess)
         return TM_ERR_HIP;
-    if (launch_import(u.M, u.S, src, c->P, (int)ns, st) != hipSuccess) return TM_ERR_HIP;
+    if (launch_import(u.M, u.S, src, c->P, (int)ns, c->din[0], c->dout[0], st) != hipSuccess) return TM_ERR_HIP;
     return hip_status(launch_shadow(u, c->tbase[c->L], (int)ns, st));
 }
 

@@ -48,6 +48,16 @@ __host__ __device__ inline long pk_size(long rows, long cols) {
     return ((rows + 15) / 16 * 16) * ((cols + 31) / 32 * 32);
 }
 
+// Layer 0's M and S (d x h1) are stored in the matrix instruction's
+// accumulator order: per 16-column block, per 16-row block, the 16 x 16 tile
+// as 64 lanes x 4 consecutive rows (lane l: rows 4 * (l / 16) .. + 3 of
+// column l % 16).  The first-layer workgroup that owns a column block then
+// moves a wave's 16 x 16 block of M or S as one contiguous 1 KB float4
+// access.  nrb = d / 16.
+__host__ __device__ inline long cf0(int i, int j, int nrb) {
+    return ((((long)(j >> 4) * nrb + (i >> 4)) * 64 + (j & 15) + 16 * ((i & 15) >> 2)) << 2) + (i & 3);
+}
+
 // Token-major arrays [batch][Tc][H][d]; gates use d = 1.
 struct TokLayout {
     int Tc, H, d;
@@ -60,7 +70,7 @@ enum { EPI_HIDDEN = 0, EPI_OUT = 1, EPI_BWD = 2 };
 // Rows r < n0 are queries, rows r >= n0 keys (t = r - n0 is the key's token
 // inside the chunk); the backward has key rows only (n0 = 0).
 enum { A_TOKENS = 0, A_ROWS = 1, A_PACKED = 2 };
-enum { B_STRIDED = 0, B_ROWS = 1, B_PACKED = 2 };
+enum { B_STRIDED = 0, B_ROWS = 1, B_PACKED = 2, B_CFRAG = 3 };
 struct GemmArgs {
     int nrows, N, K;
     // A.  A_TOKENS: rows r < n0 are tokens (at0 + r) of a0, rows r >= n0
@@ -72,7 +82,8 @@ struct GemmArgs {
     long a_ss, a_ld;
     // B.  B_STRIDED: element (k, n) at b + s*b_ss + n + k*b_ld (row-major
     // [K][N]); B_ROWS: at b + s*b_ss + n*b_ld + k (row n contiguous in K);
-    // B_PACKED: packed [N][K] at b + s*b_ss.
+    // B_PACKED: packed [N][K] at b + s*b_ss; B_CFRAG: layer 0's fp32 master
+    // in accumulator order, cf0(k, n, K / 16), at b + s*b_ss.
     const void* b;
     long b_ss, b_ld;
     int bmode;
@@ -231,12 +242,14 @@ hipError_t launch_update(const UpdArgs& u, int ntiles, int ns, int f32, hipStrea
 hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st);
 // update tiles [tile0, tile0 + ntiles) of every stream
 hipError_t launch_update_range(const UpdArgs& u, int tile0, int ntiles, int ns, int f32, hipStream_t st);
-hipError_t launch_init(float* M, float* S, const float* init, long P, int H, int ns,
+// init / export / import convert between the canonical row-major layers and
+// the state layout (layer 0 of d0 x h1 in accumulator order)
+hipError_t launch_init(float* M, float* S, const float* init, long P, int H, int ns, int d0, int h1,
                        hipStream_t st);
 hipError_t launch_shadow(const UpdArgs& u, int ntiles, int ns, hipStream_t st);
-hipError_t launch_export(const float* M, const float* S, float* dst, long P, int ns,
+hipError_t launch_export(const float* M, const float* S, float* dst, long P, int ns, int d0, int h1,
                          hipStream_t st);
-hipError_t launch_import(float* M, float* S, const float* src, long P, int ns,
+hipError_t launch_import(float* M, float* S, const float* src, long P, int ns, int d0, int h1,
                          hipStream_t st);
 hipError_t launch_header(StateHeader* h, uint64_t hash, int batch, int heads,
                          hipStream_t st);

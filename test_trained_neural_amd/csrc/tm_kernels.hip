@@ -105,17 +105,18 @@ template <class T> __device__ __forceinline__ float load1(const void* p, long i)
 
 // ---------------------------------------------------------------------------
 // Chunk forward / backward product.  A workgroup of W waves owns one tile of
-// 64 rows x 16*NR columns and splits its K range over the waves (wave w takes
+// RT rows x 16*NR columns and splits its K range over the waves (wave w takes
 // the w-th contiguous slice of 32-deep steps); the W partial tiles are summed
 // in LDS in a fixed order, so results are deterministic and no workgroup ever
 // waits for another (cross-workgroup handoffs need device-scope fences, which
 // serialise across the whole chip).  Each lane feeds the matrix cores from
-// registers loaded straight from global memory (activations hit L2) through
-// a PF-deep prefetch ring; the ring has no branches, steps past the end of a
-// slice re-load a valid address and contribute zeros.
-// OP: operand type; AT / BT: storage types of A / B; BKC: B contiguous in K.
-
-constexpr int GEMM_RT = 64;   // rows per tile (4 row blocks of 16)
+// registers loaded straight from global memory through a prefetch ring of PF
+// steps, sized to the register budget; when a wave's slice fits the ring,
+// all its loads are in flight at once.  The ring has no branches: steps past
+// the end of a slice re-load a valid address and contribute zeros.  The
+// epilogue's own operands (v or SiLU', the theta coefficients) are requested
+// at kernel start too.
+// OP: operand type; AT / BT: storage types of A / B; BM: B layout (B_*).
 
 template <class OP> __device__ __forceinline__ void st8(OP* p, typename Frag<OP>::T v) {
     *reinterpret_cast<typename Frag<OP>::T*>(p) = v;
@@ -125,58 +126,25 @@ __device__ __forceinline__ void st8f(float* p, const float* v) {
     *reinterpret_cast<f32x4*>(p + 4) = (f32x4){v[4], v[5], v[6], v[7]};
 }
 
-// Row outputs of 8 consecutive columns c .. c+7 of row r; z becomes the
-// value the transposed copy carries for key rows (the rounded activation,
-// or Delta).
-template <class OP>
-__device__ __forceinline__ void gemm_store8(const GemmArgs& g, int s, int r, int c, float* z) {
-    typedef typename Frag<OP>::T F;
-    F o;
-    if (g.epi == EPI_HIDDEN) {
-        float sl[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float sg = sigmoid(z[e]);
-            o[e] = (OP)(z[e] * sg);
-            sl[e] = sg * (1.0f + z[e] * (1.0f - sg));
-            z[e] = (float)o[e];
-        }
-        st8<OP>(reinterpret_cast<OP*>(g.act) + (long)s * g.act_ss + pk(r, c, g.N >> 5), o);
-        if (r >= g.n0 && g.dsl) st8f(g.dsl + (long)s * g.dsl_ss + (long)(r - g.n0) * g.dsl_ld + c, sl);
-        return;
-    }
-    int t = r;
-    if (g.epi == EPI_OUT) {
-        if (r < g.n0) {
-            st8f(g.y + tok_off(g.tl, s, g.yt0 + r) + c, z);
-            return;
-        }
-        t = r - g.n0;
-        const f32x8 vv = to_f32v(ld8(reinterpret_cast<const OP*>(g.v) + tok_off(g.tl, s, g.vt0 + t) + c));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = 2.0f * (z[e] - vv[e]);
-    } else {
-        const f32x8 sl = ld8(g.dsl + (long)s * g.dsl_ss + (long)r * g.dsl_ld + c);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = z[e] * sl[e];
-    }
-    if (g.dlp) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (OP)z[e];
-        st8<OP>(reinterpret_cast<OP*>(g.dlp) + (long)s * g.dlp_ss + pk(t, c, g.N >> 5), o);
-    }
+// prefetch depth for a tile: about 96 registers of operand ring (8 values
+// of each fragment per lane; a register holds 4 bytes)
+constexpr int gemm_pf(int mr, int nr, int asz, int bsz) {
+    const int per = (mr * asz + nr * bsz) * 2;   // registers per K step
+    return 96 / per < 2 ? 2 : (96 / per > 8 ? 8 : 96 / per);
 }
 
-template <class OP, class AT, class BT, bool BKC, int NR, int W, int PF>
+template <class OP, class AT, class BT, int BM, int RT, int NR, int W>
 __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     typedef typename Frag<OP>::T F;
-    constexpr int MR = GEMM_RT / 16;
+    constexpr int MR = RT / 16;
     constexpr int NT = NR * 16;
     constexpr int NTP = NT + 1;            // padded LDS row
-    extern __shared__ float red[];          // [W][GEMM_RT][NTP]
+    constexpr int PF = gemm_pf(MR, NR, (int)sizeof(AT), (int)sizeof(BT));
+    extern __shared__ float red[];          // [W][RT][NTP], then the tile's c, d coefficients
+    float* coefs = red + W * RT * NTP;      // [2][RT]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = blockIdx.z;
-    const int row0 = blockIdx.y * GEMM_RT;
+    const int row0 = blockIdx.y * RT;
     const int col0 = blockIdx.x * NT;
     const int nsteps = g.K >> 5;
     const int spw = (nsteps + W - 1) / W;   // steps per wave
@@ -220,22 +188,18 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     }
     const BT* bcol[NR];
     bool bok[NR];
-    long bstep = 32;
+    constexpr long bstep = (BM == B_PACKED || BM == B_CFRAG) ? 512 : 32;
 #pragma unroll
     for (int n = 0; n < NR; ++n) {
         int cb = (col0 >> 4) + n;
-        const int c = cb * 16 + (lane & 15);
+        int c = cb * 16 + (lane & 15);
         bok[n] = c < g.N;
+        if (!bok[n]) { cb = 0; c = lane & 15; }
         const BT* base = reinterpret_cast<const BT*>(g.b) + (long)s * g.b_ss;
-        if (g.bmode == B_PACKED) {
-            if (cb * 16 >= g.N) cb = 0;
-            bcol[n] = base + pkf(cb, 0, nsteps, lane);
-            bstep = 512;
-        } else if (g.bmode == B_ROWS) {
-            bcol[n] = base + (long)(bok[n] ? c : 0) * g.b_ld + kofs;
-        } else {
-            bcol[n] = base + (bok[n] ? c : 0) + (long)kofs * g.b_ld;
-        }
+        if constexpr (BM == B_PACKED) bcol[n] = base + pkf(cb, 0, nsteps, lane);
+        else if constexpr (BM == B_ROWS) bcol[n] = base + (long)c * g.b_ld + kofs;
+        else if constexpr (BM == B_CFRAG) bcol[n] = base + cf0(kofs, c, g.K >> 4);
+        else bcol[n] = base + c + (long)kofs * g.b_ld;
     }
     // the ring holds raw storage vectors; conversion to the operand type
     // happens right before the matrix instruction, so loads stay in flight
@@ -248,8 +212,15 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
         for (int m = 0; m < MR; ++m) a[p][m] = ld8(arow[m] + k * astep);
 #pragma unroll
         for (int n = 0; n < NR; ++n) {
-            if (BKC) {
+            if constexpr (BM == B_PACKED || BM == B_ROWS) {
                 bb[p][n] = ld8(bcol[n] + k * bstep);
+            } else if constexpr (BM == B_CFRAG) {
+                // rows kofs..kofs+3 and kofs+4..kofs+7 of the column: two
+                // float4 one 16-lane group apart
+                const BT* q = bcol[n] + k * bstep;
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(q);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(q + 64);
+                bb[p][n] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             } else {
                 RB u;
                 const BT* q = bcol[n] + (long)(k << 5) * g.b_ld;
@@ -261,6 +232,33 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     };
 #pragma unroll
     for (int p = 0; p < PF; ++p) load_step(p, min(kb + p, klast));
+
+    // the epilogue's operands, requested now (unused ones read a valid
+    // address): pass 1's first item (v or SiLU' of 8 columns of one row) and
+    // the c, d coefficient of token (this thread's row) for pass 2
+    typedef typename Frag<OP>::T RV;
+    RV vpre;
+    f32x8 spre;
+    float cpre = 0.f, dpre = 0.f;
+    {
+        const int rr = tid / (NT / 8), cc = (tid % (NT / 8)) * 8;
+        const int r = min(row0 + rr, g.nrows - 1), c = min(col0 + cc, g.N - 8);
+        const int t = max(r - g.n0, 0);
+        // v only where the product has key rows (their tokens vt0 .. vt0 + nk - 1)
+        const bool keys = g.epi == EPI_OUT && g.v && g.nrows > g.n0;
+        const OP* vp = keys ? reinterpret_cast<const OP*>(g.v) + tok_off(g.tl, s, g.vt0 + t) + c
+                            : reinterpret_cast<const OP*>(g.b);
+        vpre = ld8(vp);
+        const float* sp = g.epi == EPI_BWD ? g.dsl + (long)s * g.dsl_ss + (long)r * g.dsl_ld + c
+                                           : reinterpret_cast<const float*>(g.b);
+        spre = ld8(sp);
+        if (g.dct) {
+            const int tt = min(max(row0 + (tid % RT) - g.n0, 0), g.nrows - g.n0 - 1);
+            cpre = g.cc[(long)s * g.coef_ss + tt];
+            dpre = g.dc[(long)s * g.coef_ss + tt];
+        }
+    }
+
     for (int k = kb; k < kb + spw; k += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
@@ -279,7 +277,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     }
 
     // sum the W partial tiles in LDS, in wave order
-    float* mine = red + wave * (GEMM_RT * NTP);
+    float* mine = red + wave * (RT * NTP);
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
@@ -287,10 +285,14 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 mine[(m * 16 + 4 * (lane >> 4) + e) * NTP + n * 16 + (lane & 15)] = acc[m][n][e];
+    if (tid < RT) {
+        coefs[tid] = cpre;
+        coefs[RT + tid] = dpre;
+    }
     __syncthreads();
     // pass 1: row outputs, 8 consecutive columns per thread (N is a multiple
     // of 32); the value for the transposed copy is left in slot 0
-    for (int idx = tid; idx < GEMM_RT * (NT / 8); idx += W * 64) {
+    for (int idx = tid; idx < RT * (NT / 8); idx += W * 64) {
         const int rr = idx / (NT / 8), cc = (idx - rr * (NT / 8)) * 8;
         const int r = row0 + rr, c = col0 + cc;
         if (r >= g.nrows || c >= g.N) continue;
@@ -299,10 +301,41 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
         for (int e = 0; e < 8; ++e) {
             float x = 0.f;
 #pragma unroll
-            for (int w = 0; w < W; ++w) x += red[w * (GEMM_RT * NTP) + rr * NTP + cc + e];
+            for (int w = 0; w < W; ++w) x += red[w * (RT * NTP) + rr * NTP + cc + e];
             z[e] = x;
         }
-        gemm_store8<OP>(g, s, r, c, z);
+        typename Frag<OP>::T o;
+        if (g.epi == EPI_HIDDEN) {
+            float sl[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float sg = sigmoid(z[e]);
+                o[e] = (OP)(z[e] * sg);
+                sl[e] = sg * (1.0f + z[e] * (1.0f - sg));
+                z[e] = (float)o[e];
+            }
+            st8<OP>(reinterpret_cast<OP*>(g.act) + (long)s * g.act_ss + pk(r, c, g.N >> 5), o);
+            if (r >= g.n0 && g.dsl) st8f(g.dsl + (long)s * g.dsl_ss + (long)(r - g.n0) * g.dsl_ld + c, sl);
+        } else if (g.epi == EPI_OUT && r < g.n0) {
+            st8f(g.y + tok_off(g.tl, s, g.yt0 + r) + c, z);
+        } else {
+            const int t = r - g.n0;
+            if (g.epi == EPI_OUT) {
+                const f32x8 vv = to_f32v(idx == tid ? vpre : ld8(reinterpret_cast<const OP*>(g.v) +
+                                                              tok_off(g.tl, s, g.vt0 + t) + c));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) z[e] = 2.0f * (z[e] - vv[e]);
+            } else {
+                const f32x8 sl = idx == tid ? spre : ld8(g.dsl + (long)s * g.dsl_ss + (long)r * g.dsl_ld + c);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) z[e] = z[e] * sl[e];
+            }
+            if (g.dlp) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = (OP)z[e];
+                st8<OP>(reinterpret_cast<OP*>(g.dlp) + (long)s * g.dlp_ss + pk(t, c, g.N >> 5), o);
+            }
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) red[rr * NTP + cc + e] = z[e];
     }
@@ -311,7 +344,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     // pass 2: the key rows' transposed copies, packed [N][bp]: 8 tokens of
     // one column per thread, whole vectors where all 8 tokens are this
     // tile's rows (a group cut by the tile edge is stored element-wise)
-    const int tlo = max(row0, g.n0) - g.n0, thi = min(row0 + GEMM_RT, g.nrows) - g.n0;
+    const int tlo = max(row0, g.n0) - g.n0, thi = min(row0 + RT, g.nrows) - g.n0;
     if (thi <= tlo) return;
     const int g0 = tlo >> 3, ng = ((thi - 1) >> 3) - g0 + 1;
     const int nkb = g.bp >> 5;
@@ -320,10 +353,12 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
         const int c = col0 + cc;
         if (c >= g.N) continue;
         float x[8];
+        bool in[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int t = t8 + e;
-            x[e] = (t >= tlo && t < thi) ? red[(t + g.n0 - row0) * NTP + cc] : 0.f;
+            in[e] = t >= tlo && t < thi;
+            x[e] = in[e] ? red[(t + g.n0 - row0) * NTP + cc] : 0.f;
         }
         const long o = (long)s * g.tr_ss + pk(c, t8, nkb);
         const bool whole = t8 >= tlo && t8 + 8 <= thi;
@@ -337,86 +372,105 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    if (t8 + e >= tlo && t8 + e < thi) h[e] = (OP)x[e];
+                    if (in[e]) h[e] = (OP)x[e];
             }
         } else {
+            // the tile's coefficients, staged in LDS by row
             OP* pc = reinterpret_cast<OP*>(g.dct) + o;
             OP* pd = reinterpret_cast<OP*>(g.ddt) + o;
-            const float* cf = g.cc + (long)s * g.coef_ss;
-            const float* df = g.dc + (long)s * g.coef_ss;
-            if (whole) {
-                F vc, vd;
+            F vc, vd;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    vc[e] = (OP)(cf[t8 + e] * x[e]);
-                    vd[e] = (OP)(df[t8 + e] * x[e]);
-                }
+            for (int e = 0; e < 8; ++e) {
+                const int rr = min(max(t8 + e + g.n0 - row0, 0), RT - 1);
+                vc[e] = (OP)(coefs[rr] * x[e]);
+                vd[e] = (OP)(coefs[RT + rr] * x[e]);
+            }
+            if (whole) {
                 st8<OP>(pc, vc);
                 st8<OP>(pd, vd);
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int t = t8 + e;
-                    if (t >= tlo && t < thi) {
-                        pc[e] = (OP)(cf[t] * x[e]);
-                        pd[e] = (OP)(df[t] * x[e]);
+                for (int e = 0; e < 8; ++e)
+                    if (in[e]) {
+                        pc[e] = vc[e];
+                        pd[e] = vd[e];
                     }
-                }
             }
         }
     }
 }
 
-// Pick the column width and wave count of one product: enough workgroups to
-// cover the chip (about 192 tiles of 64 rows, ideally at least 3 steps per
-// wave), wider tiles first so the activations are re-read from L2 less often.
-static void pick(const GemmArgs& g, int ns, int& nr, int& w, bool allow16) {
+// The tile shape and wave count of one product: prefer tiles whose K slice
+// per wave fits the prefetch ring (one memory round trip) and enough
+// workgroups to cover the chip, then the widest tile (activations re-read
+// from L2 by fewer workgroups).
+struct GemmShape {
+    int rt, nr, w;
+};
+
+template <class AT, class BT>
+static GemmShape pick(const GemmArgs& g, int ns) {
     const int nsteps = g.K >> 5;
-    const long nrt = (g.nrows + GEMM_RT - 1) / GEMM_RT;
-    nr = 4;
-    w = 4;
-    auto wgs = [&](int nr_) { return (long)((g.N + 16 * nr_ - 1) / (16 * nr_)) * nrt * ns; };
-    if (nsteps >= 8 * 3) w = 8;
-    while (wgs(nr) < 192 && nr > 1) nr >>= 1;
-    (void)allow16;
+    static const int cand[5][2] = {{64, 4}, {64, 2}, {32, 2}, {64, 1}, {32, 1}};
+    GemmShape best{64, 1, 8};
+    long best_score = -1;
+    for (const auto& cd : cand) {
+        const int rt = cd[0], nr = cd[1];
+        const int pf = gemm_pf(rt / 16, nr, (int)sizeof(AT), (int)sizeof(BT));
+        const int w = nsteps >= 16 ? 8 : 4;
+        const int spw = (nsteps + w - 1) / w;
+        const long wgs = (long)((g.N + 16 * nr - 1) / (16 * nr)) * ((g.nrows + rt - 1) / rt) * ns;
+        // one round trip and a full chip first; then more workgroups; then
+        // the wider tile (earlier candidates)
+        const long score = (spw <= pf ? 4000000 : 0) + (wgs >= 192 ? 2000000 : 0) + (wgs < 192 ? wgs * 1000 : 0) +
+                           (5 - (&cd - cand));
+        if (score > best_score) {
+            best_score = score;
+            best = GemmShape{rt, nr, w};
+        }
+    }
+    return best;
 }
 
-template <class OP, class AT, class BT, bool BKC, int NR, int W, int PF>
+template <class OP, class AT, class BT, int BM, int RT, int NR, int W>
 static void launch_one(const GemmArgs& g, int ns, hipStream_t st) {
-    dim3 grid((g.N + NR * 16 - 1) / (NR * 16), (g.nrows + GEMM_RT - 1) / GEMM_RT, ns);
-    const size_t lds = (size_t)W * GEMM_RT * (NR * 16 + 1) * 4;
-    hipLaunchKernelGGL((gemm_kernel<OP, AT, BT, BKC, NR, W, PF>), grid, dim3(W * 64), lds, st, g);
+    dim3 grid((g.N + NR * 16 - 1) / (NR * 16), (g.nrows + RT - 1) / RT, ns);
+    const size_t lds = ((size_t)W * RT * (NR * 16 + 1) + 2 * RT) * 4;
+    hipLaunchKernelGGL((gemm_kernel<OP, AT, BT, BM, RT, NR, W>), grid, dim3(W * 64), lds, st, g);
 }
 
-template <class OP, class AT, class BT, bool BKC, int PF>
+template <class OP, class AT, class BT, int BM, int RT, int W>
+static void launch_nr(const GemmArgs& g, int ns, int nr, hipStream_t st) {
+    if (nr == 4) launch_one<OP, AT, BT, BM, RT, 4, W>(g, ns, st);
+    else if (nr == 2) launch_one<OP, AT, BT, BM, RT, 2, W>(g, ns, st);
+    else launch_one<OP, AT, BT, BM, RT, 1, W>(g, ns, st);
+}
+
+template <class OP, class AT, class BT, int BM>
 static hipError_t launch_gemm(const GemmArgs& g, int ns, hipStream_t st) {
     if (g.nrows <= 0 || g.N <= 0) return hipSuccess;
-    int nr, w;
-    // 16-wave workgroups cap a wave at 128 registers: only the narrowest
-    // tile with 16-bit operands in storage fits the prefetch ring there
-    pick(g, ns, nr, w, sizeof(AT) == 2 && sizeof(BT) == 2);
-    if (w == 16) {
-        launch_one<OP, AT, BT, BKC, 1, 16, PF>(g, ns, st);
-    } else if (w == 8) {
-        if (nr == 4) launch_one<OP, AT, BT, BKC, 4, 8, PF>(g, ns, st);
-        else if (nr == 2) launch_one<OP, AT, BT, BKC, 2, 8, PF>(g, ns, st);
-        else launch_one<OP, AT, BT, BKC, 1, 8, PF>(g, ns, st);
+    const GemmShape sh = pick<AT, BT>(g, ns);
+    if (sh.rt == 64) {
+        if (sh.w == 8) launch_nr<OP, AT, BT, BM, 64, 8>(g, ns, sh.nr, st);
+        else launch_nr<OP, AT, BT, BM, 64, 4>(g, ns, sh.nr, st);
     } else {
-        if (nr == 4) launch_one<OP, AT, BT, BKC, 4, 4, PF>(g, ns, st);
-        else if (nr == 2) launch_one<OP, AT, BT, BKC, 2, 4, PF>(g, ns, st);
-        else launch_one<OP, AT, BT, BKC, 1, 4, PF>(g, ns, st);
+        if (sh.w == 8) launch_nr<OP, AT, BT, BM, 32, 8>(g, ns, sh.nr, st);
+        else launch_nr<OP, AT, BT, BM, 32, 4>(g, ns, sh.nr, st);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_fwd(const GemmArgs& g, int ns, int f32, hipStream_t st) {
-    if (f32) return launch_gemm<float, float, float, false, 2>(g, ns, st);
-    return launch_gemm<bf16, bf16, bf16, true, 4>(g, ns, st);
+    if (f32) {
+        if (g.bmode == B_CFRAG) return launch_gemm<float, float, float, B_CFRAG>(g, ns, st);
+        return launch_gemm<float, float, float, B_STRIDED>(g, ns, st);
+    }
+    return launch_gemm<bf16, bf16, bf16, B_PACKED>(g, ns, st);
 }
 
 hipError_t launch_bwd(const GemmArgs& g, int ns, int f32, hipStream_t st) {
-    if (f32) return launch_gemm<float, float, float, true, 2>(g, ns, st);
-    return launch_gemm<bf16, bf16, float, true, 2>(g, ns, st);
+    if (f32) return launch_gemm<float, float, float, B_ROWS>(g, ns, st);
+    return launch_gemm<bf16, bf16, float, B_ROWS>(g, ns, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -593,15 +647,15 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
 // LDS once to switch from the matrix-core layout to row-contiguous float4
 // accesses for M and S, and once more for the transposed bf16 copy.
 
+// 8 consecutive tokens t0 .. t0+7 of a transposed operand, zero past the
+// chunk (selects, no branch: a branch here would make the compiler wait for
+// every load in flight)
 template <class OP>
-__device__ __forceinline__ typename Frag<OP>::T tok8(const OP* p, int t0, int b, bool full) {
+__device__ __forceinline__ typename Frag<OP>::T tok8(const OP* p, int t0, int b) {
     typedef typename Frag<OP>::T F;
     F v = cvt<OP>(ld8(p));
-    if (!full) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (t0 + e >= b) v[e] = (OP)0.0f;
-    }
+    for (int e = 0; e < 8; ++e) v[e] = t0 + e < b ? v[e] : (OP)0.0f;
     return v;
 }
 
@@ -613,21 +667,47 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
                             float (*US)[65]) {
     typedef typename Frag<OP>::T F;
     const int lane = tid & 63, wave = tid >> 6;
+    // the tile's layer and its parameters, picked by compare and select (an
+    // index computed at run time into the kernel arguments would become a
+    // chain of dependent memory loads)
     int l = 0;
-    while (l + 1 < u.L && tile >= u.tbase[l + 1]) ++l;
-    tile -= u.tbase[l];
-    const int ti = tile / u.tj[l], tj = tile - ti * u.tj[l];
-    const int din = u.din[l], dout = u.dout[l];
+#pragma unroll
+    for (int q = 1; q < MAXL; ++q)
+        if (q < u.L && tile >= u.tbase[q]) l = q;
+    int tb = 0, tjn = 1, din = 32, dout = 32;
+    long off = 0, at_ss = 0, dt_ss = 0;
+    const void* atp = nullptr;
+    const void* dcp = nullptr;
+    const void* ddp = nullptr;
+#pragma unroll
+    for (int q = 0; q < MAXL; ++q)
+        if (q == l) {
+            tb = u.tbase[q];
+            tjn = u.tj[q];
+            din = u.din[q];
+            dout = u.dout[q];
+            off = u.off[q];
+            atp = u.at[q];
+            at_ss = u.at_ss[q];
+            dcp = u.dct[q];
+            ddp = u.ddt[q];
+            dt_ss = u.dt_ss[q];
+        }
+    tile -= tb;
+    const int ti = tile / tjn, tj = tile - ti * tjn;
     const int i0 = ti * 64, j0 = tj * 64;
     const int b = u.b, bp = u.bp;
+    // the chunk scalars first: every load below is consumed in issue order
+    const float* csp = u.cs + (long)s * u.cs_ss + (long)u.chunk * 4;
+    const float pa = csp[0], pe = csp[1], s0 = csp[2];
 
     // U_M, U_S on the matrix cores: 4 waves as 2 x 2, 32 x 32 each
     const int wi = wave & 1, wj = wave >> 1;
     const int kofs = 8 * (lane >> 4);
     const int nkb = bp >> 5;
-    const OP* A = reinterpret_cast<const OP*>(u.at[l]) + (long)s * u.at_ss[l];
-    const OP* Bc = reinterpret_cast<const OP*>(u.dct[l]) + (long)s * u.dt_ss[l];
-    const OP* Bd = reinterpret_cast<const OP*>(u.ddt[l]) + (long)s * u.dt_ss[l];
+    const OP* A = reinterpret_cast<const OP*>(atp) + (long)s * at_ss;
+    const OP* Bc = reinterpret_cast<const OP*>(dcp) + (long)s * dt_ss;
+    const OP* Bd = reinterpret_cast<const OP*>(ddp) + (long)s * dt_ss;
     int ab[2], bb[2];
     bool aok[2], bok[2];
 #pragma unroll
@@ -649,17 +729,16 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int t0 = ks * 32 + kofs;
-        const bool full = t0 + 8 <= b;
         const int kc = min(ks, nkb - 1);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            fa[ks][m] = tok8<OP>(A + pkf(ab[m], kc, nkb, lane), t0, b, full);
-            fc[ks][m] = tok8<OP>(Bc + pkf(bb[m], kc, nkb, lane), t0, b, full);
-            fd[ks][m] = tok8<OP>(Bd + pkf(bb[m], kc, nkb, lane), t0, b, full);
+            fa[ks][m] = tok8<OP>(A + pkf(ab[m], kc, nkb, lane), t0, b);
+            fc[ks][m] = tok8<OP>(Bc + pkf(bb[m], kc, nkb, lane), t0, b);
+            fd[ks][m] = tok8<OP>(Bd + pkf(bb[m], kc, nkb, lane), t0, b);
         }
     }
-    float* Mp = u.M + (long)s * u.P + u.off[l];
-    float* Sp = u.S + (long)s * u.P + u.off[l];
+    float* Mp = u.M + (long)s * u.P + off;
+    float* Sp = u.S + (long)s * u.P + off;
     f32x4 mreg[4], sreg[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -700,8 +779,6 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
             }
     __syncthreads();
 
-    const float* csp = u.cs + (long)s * u.cs_ss + (long)u.chunk * 4;
-    const float pa = csp[0], pe = csp[1], s0 = csp[2];
     bool bad = false;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -726,7 +803,7 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
     __syncthreads();
     // the tile of the bf16 forward copy Wt (packed [dout][din]): 4 column
     // blocks x 2 K steps x 64 lanes of 8 consecutive inputs, in memory order
-    bf16* Wp = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P + u.off[l];
+    bf16* Wp = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P + off;
     for (int idx = tid; idx < 512; idx += 256) {
         const int ln = idx & 63, kk = (idx >> 6) & 1, jb = idx >> 7;
         const int jl = jb * 16 + (ln & 15), il = kk * 32 + 8 * (ln >> 4);
@@ -782,7 +859,8 @@ constexpr size_t UPD_PAIR_LDS = 2 * 2 * 64 * 65 * 4;   // two update tiles: U_M,
 
 static size_t first_lds_bytes(int dim, int bp, int f32) {
     const size_t e = f32 ? 4 : 2;
-    return (size_t)JW * (dim + WPAD) * e + 2 * (size_t)JW * (bp + WPAD) * e +
+    (void)bp;
+    return (size_t)JW * (dim + WPAD) * e + 2 * (size_t)JW * (MAX_CHUNK + WPAD) * e +
            (size_t)FRED * 128 * (JW + RPAD) * 4;
 }
 
@@ -819,11 +897,18 @@ template <class OP> struct FirstDepth;
 template <> struct FirstDepth<bf16> { static constexpr int A = 2, B = 4, C = 2; };
 template <> struct FirstDepth<float> { static constexpr int A = 1, B = 2, C = 1; };
 
-template <class OP>
+// UPD: chunk c-1's update runs (steps 1..C); FWD: chunk c's forward runs (a
+// step with rows to push); DEEP: depth >= 2.  The phases a launch runs are
+// compile-time, so every load of a phase is unconditional and issued at the
+// top in consumption order: a load whose only use sits behind a run-time
+// branch would be moved down to that use, and a branch or loop around a use
+// makes the compiler wait for every load in flight.
+template <class OP, bool UPD, bool FWD, bool DEEP>
 __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     typedef typename Frag<OP>::T F;
     constexpr int PA = FirstDepth<OP>::A, PB = FirstDepth<OP>::B, PC = FirstDepth<OP>::C;
     constexpr int NT = FW * 64;
+    constexpr bool BWD = UPD && DEEP;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     if ((int)blockIdx.x >= a.nb1) {
         // the other layers' update tiles of chunk c-1, two per workgroup
@@ -843,9 +928,9 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     const int kofs = 8 * (lane >> 4), g4 = 4 * (lane >> 4);
     const int d = a.dim, h1 = a.h1, b = u.b, bp = u.bp;
     const int j0 = blockIdx.x * JW;
-    const int jl = lane & 15, j = j0 + jl;   // the lane's column in B fragments / results
-    const bool jok = j < h1;
-    const int WP = d + WPAD, DP = bp + WPAD, RP = JW + RPAD;
+    const int jl = lane & 15, j = j0 + jl;   // the lane's column (h1 is a multiple of 16)
+    const int WP = d + WPAD, RP = JW + RPAD;
+    constexpr int DP = MAX_CHUNK + WPAD;     // rows hold every token slot of a chunk
     OP* Wn = reinterpret_cast<OP*>(lds);   // [JW][WP]: the block's columns of W_0, K-contiguous
     OP* DcT = Wn + JW * WP;                 // [JW][DP]: (c Delta_0)^T of chunk c-1
     OP* DdT = DcT + JW * DP;
@@ -854,125 +939,142 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     float* S0 = u.S + (long)s * u.P;
     bf16* Wt0 = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P;
     const OP* kt = reinterpret_cast<const OP*>(a.kt_prev) + (long)s * a.kt_ss;
-    const bool upd = a.do_update;
-    const bool bwd = upd && u.L >= 2;
+    const int nrb = d >> 4;
+    const int nkb = bp >> 5;
     bool bad = false;
 
     // ================= every load of the kernel, in consumption order =================
+    // (0) the chunk scalars of chunk c-1
+    float pa = 0.f, pe = 0.f, s0 = 0.f;
+    if constexpr (UPD) {
+        const float* csp = u.cs + (long)s * u.cs_ss + (long)a.chunk_prev * 4;
+        pa = csp[0];
+        pe = csp[1];
+        s0 = csp[2];
+    }
     // (1) the in-place backward's operands: Delta_1 rows (4 token blocks) and
     //     the lane's column of W_1, K split over the waves
-    const int K1 = bwd ? u.dout[1] : 32;
-    const int nsA = K1 >> 5, qA = (nsA + FW - 1) / FW;
+    const int nsA = BWD ? u.dout[1] >> 5 : 1, qA = (nsA + FW - 1) / FW;
     const int kbA = wave * qA, keA = min(nsA, kbA + qA), klA = max(keA - 1, 0);
     const OP* Ad[4];
+    const OP* Bw = nullptr;
     bool tok[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        tok[m] = 16 * m + (lane & 15) < b;
-        const int mb = 16 * m < b ? m : 0;   // token blocks past the chunk: valid address, dropped
-        // without the backward: a harmless read of the first 2 KB of M
-        Ad[m] = bwd ? reinterpret_cast<const OP*>(a.dlt2) + (long)s * a.dlt2_ss + pkf(mb, 0, nsA, lane)
-                    : reinterpret_cast<const OP*>(M0) + lane * 8;
-    }
-    const OP* Bw = bwd ? reinterpret_cast<const OP*>(a.wr_prev) + (long)s * a.wr_ss + pkf(j0 >> 4, 0, nsA, lane)
-                       : reinterpret_cast<const OP*>(M0) + lane * 8;
-    // (every load below is unconditional and from a valid address, whether
-    // or not this step uses it, so that the compiler waits for exactly the
-    // loads each phase needs; the host points unused operands at valid memory)
     F ra[PA][4], rb[PA];
+    if constexpr (BWD) {
 #pragma unroll
-    for (int p = 0; p < PA; ++p) {
-        const long k0 = (long)min(kbA + p, klA) << 9;
+        for (int m = 0; m < 4; ++m) {
+            tok[m] = 16 * m + (lane & 15) < b;
+            const int mb = 16 * m < b ? m : 0;   // token blocks past the chunk: valid address, dropped
+            Ad[m] = reinterpret_cast<const OP*>(a.dlt2) + (long)s * a.dlt2_ss + pkf(mb, 0, nsA, lane);
+        }
+        Bw = reinterpret_cast<const OP*>(a.wr_prev) + (long)s * a.wr_ss + pkf(j0 >> 4, 0, nsA, lane);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) ra[p][m] = cvt<OP>(ld8(Ad[m] + k0));
-        rb[p] = cvt<OP>(ld8(Bw + k0));
+        for (int p = 0; p < PA; ++p) {
+            const long k0 = (long)min(kbA + p, klA) << 9;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) ra[p][m] = cvt<OP>(ld8(Ad[m] + k0));
+            rb[p] = cvt<OP>(ld8(Bw + k0));
+        }
     }
     // (2) the backward epilogue's SiLU' and coefficients (2 elements per thread)
-    constexpr int EA = 64 * JW / NT;
+    constexpr int EA = MAX_CHUNK * JW / NT;
     float sl[EA], cv[EA], dv[EA];
+    if constexpr (BWD) {
 #pragma unroll
-    for (int q = 0; q < EA; ++q) {
-        const int idx = tid + NT * q, t = min(idx / JW, b - 1), jj = j0 + idx % JW;
-        sl[q] = *(bwd ? a.dsl1 + (long)s * a.dsl1_ss + (long)t * h1 + jj : M0 + (tid & 63));
-        cv[q] = a.cc_prev[(long)s * a.coef_ss + t];
-        dv[q] = a.dc_prev[(long)s * a.coef_ss + t];
-    }
-    // (3) the update's row blocks of this wave: keys^T fragments, M and S
-    const int nrb = d >> 4;
-    const int nkb = bp >> 5;
-    const int mineB = upd ? (nrb - wave + FW - 1) / FW : 0;
-    F kf[PB][2];
-    float mr[PB][4], sr[PB][4];
-    auto load_rb = [&](int p, int n) {
-        // a wave without row blocks (mineB == 0) still loads a valid block
-        const int rbk = min(wave + FW * max(min(n, mineB - 1), 0), nrb - 1);
-        const int ib = 16 * rbk;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            kf[p][ks] = ks < nkb ? cvt<OP>(ld8(kt + pkf(rbk, ks, nkb, lane))) : zero_frag<OP>();
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const long o = (long)(ib + g4 + e) * h1 + (jok ? j : 0);
-            mr[p][e] = M0[o];
-            sr[p][e] = S0[o];
+        for (int q = 0; q < EA; ++q) {
+            const int idx = tid + NT * q, t = min(idx / JW, b - 1), jj = j0 + idx % JW;
+            sl[q] = a.dsl1[(long)s * a.dsl1_ss + (long)t * h1 + jj];
+            cv[q] = a.cc_prev[(long)s * a.coef_ss + t];
+            dv[q] = a.dc_prev[(long)s * a.coef_ss + t];
         }
-    };
+    }
+    // (3) the update's row blocks of this wave (block wave + FW * p): keys^T
+    //     fragments, M and S; blocks past the matrix are clamped and dropped
+    const int mineB = (nrb - wave + FW - 1) / FW;
+    // (the lane's 4 values of a 16 x 16 block of M or S are one float4 at
+    // mso(rbk), the wave's block 1 KB contiguous)
+    auto mso = [&](int rbk) { return ((long)(blockIdx.x * nrb + rbk) * 64 + lane) * 4; };
+    F kf[PB][2];
+    f32x4 mr[PB], sr[PB];
+    auto load_rb = [&](int p, int n) {
+        const int rbk = min(wave + FW * n, nrb - 1);
 #pragma unroll
-    for (int p = 0; p < PB; ++p) load_rb(p, p);
-    // (4) the forward's rows (all 16-row blocks), K = dim split over the waves
+        for (int ks = 0; ks < 2; ++ks) {
+            const F v = cvt<OP>(ld8(kt + pkf(rbk, min(ks, nkb - 1), nkb, lane)));
+            kf[p][ks] = ks < nkb ? v : zero_frag<OP>();
+        }
+        mr[p] = *reinterpret_cast<const f32x4*>(M0 + mso(rbk));
+        sr[p] = *reinterpret_cast<const f32x4*>(S0 + mso(rbk));
+    };
+    if constexpr (UPD) {
+#pragma unroll
+        for (int p = 0; p < PB; ++p) load_rb(p, p);
+    }
+    // (4) the forward's rows (all 16-row blocks), K = dim split over the
+    //     waves; each lane's row: query rows of chunk c-1 first, then key rows
+    //     of chunk c, both packed per chunk.  With a backward these loads are
+    //     issued right after its products, once its operand registers are
+    //     free (issued earlier, the prefetched set would not fit the register
+    //     file), and still have the whole update phase to arrive.
     const int R = a.nq + a.nk;
-    const int nrow = (R + 15) >> 4;
     const int nsC = d >> 5, qC = (nsC + FW - 1) / FW;
     const int kbC = wave * qC, keC = min(nsC, kbC + qC), klC = max(keC - 1, 0);
-    // each lane's row: query rows of chunk c-1 first, then key rows of chunk
-    // c, both packed per chunk
     const OP* Ax[8];
     bool rok[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        int r = 16 * m + (lane & 15);
-        rok[m] = r < R;
-        if (!rok[m]) r = R > 0 ? R - 1 : 0;
-        const bool isq = r < a.nq;
-        Ax[m] = reinterpret_cast<const OP*>(isq ? a.xq : a.xk) + (long)s * a.x_ss + pk(isq ? r : r - a.nq, kofs, nsC);
-    }
     F rx[PC][8];
+    auto issue_rows = [&]() {
+        if constexpr (FWD) {
 #pragma unroll
-    for (int p = 0; p < PC; ++p)
+            for (int m = 0; m < 8; ++m) {
+                int r = 16 * m + (lane & 15);
+                rok[m] = r < R;
+                if (!rok[m]) r = R - 1;
+                const bool isq = r < a.nq;
+                Ax[m] = reinterpret_cast<const OP*>(isq ? a.xq : a.xk) + (long)s * a.x_ss +
+                        pk(isq ? r : r - a.nq, kofs, nsC);
+            }
 #pragma unroll
-        for (int m = 0; m < 8; ++m) rx[p][m] = cvt<OP>(ld8(Ax[m] + ((long)min(kbC + p, klC) << 9)));
+            for (int p = 0; p < PC; ++p)
+#pragma unroll
+                for (int m = 0; m < 8; ++m) rx[p][m] = cvt<OP>(ld8(Ax[m] + ((long)min(kbC + p, klC) << 9)));
+        }
+    };
+    if constexpr (!BWD) issue_rows();
 
     // ================= chunk c-1's update of the block's columns =================
-    if (upd) {
-        if (bwd) {
-            // Delta_0 = (Delta_1 W_1^T) * SiLU'(z_0): 64 tokens x JW columns
+    if constexpr (UPD) {
+        if constexpr (BWD) {
+            // Delta_0 = (Delta_1 W_1^T) * SiLU'(z_0): 64 tokens x JW columns.
+            // The prefetched K steps straight-line, then (long K only) the
+            // rest, each loaded and used
             f32x4 acc[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            for (int k = kbA; k < kbA + qA; k += PA) {
 #pragma unroll
-                for (int p = 0; p < PA; ++p) {
-                    const bool live = k + p < keA && k + p < kbA + qA;
-                    const F bv = (live && jok) ? rb[p] : zero_frag<OP>();
+            for (int p = 0; p < PA; ++p) {
+                const F bv = kbA + p < keA ? rb[p] : zero_frag<OP>();
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) mma(acc[m], tok[m] ? ra[p][m] : zero_frag<OP>(), bv);
-                    if (k + PA < kbA + qA) {   // wave-uniform: ring refill for long K
-                        const long kn = (long)min(k + p + PA, klA) << 9;
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) ra[p][m] = cvt<OP>(ld8(Ad[m] + kn));
-                        rb[p] = cvt<OP>(ld8(Bw + kn));
-                    }
-                }
+                for (int m = 0; m < 4; ++m) mma(acc[m], tok[m] ? ra[p][m] : zero_frag<OP>(), bv);
             }
+            for (int k = kbA + PA; k < keA; ++k) {
+                const long kn = (long)k << 9;
+                F av[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) av[m] = cvt<OP>(ld8(Ad[m] + kn));
+                const F bv = cvt<OP>(ld8(Bw + kn));
+#pragma unroll
+                for (int m = 0; m < 4; ++m) mma(acc[m], tok[m] ? av[m] : zero_frag<OP>(), bv);
+            }
+            issue_rows();
             partial_tiles<4>(red, acc, 4, 64, wave, lane, RP);
+            // theta-weighted, into LDS (token slots past the chunk get zeros)
 #pragma unroll
             for (int q = 0; q < EA; ++q) {
                 const int idx = tid + NT * q, t = idx / JW, cl = idx % JW;
-                if (t >= bp) continue;
                 float z = 0.f;
 #pragma unroll
                 for (int w = 0; w < FRED; ++w) z += red[(w * 64 + t) * RP + cl];
-                const float dl = t < b ? z * sl[q] : 0.f;   // padding tokens: zero
+                const float dl = t < b ? z * sl[q] : 0.f;
                 DcT[cl * DP + t] = (OP)(cv[q] * dl);
                 DdT[cl * DP + t] = (OP)(dv[q] * dl);
             }
@@ -985,8 +1087,10 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
                 F vc = cvt<OP>(ld8(reinterpret_cast<const OP*>(a.dct1) + o));
                 F vd = cvt<OP>(ld8(reinterpret_cast<const OP*>(a.ddt1) + o));
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (t8 + e >= b) { vc[e] = (OP)0.0f; vd[e] = (OP)0.0f; }
+                for (int e = 0; e < 8; ++e) {
+                    vc[e] = t8 + e < b ? vc[e] : (OP)0.0f;
+                    vd[e] = t8 + e < b ? vd[e] : (OP)0.0f;
+                }
                 *reinterpret_cast<F*>(&DcT[cl * DP + t8]) = vc;
                 *reinterpret_cast<F*>(&DdT[cl * DP + t8]) = vd;
             }
@@ -995,8 +1099,6 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
 
         // U = K^T diag(c) Delta_0 and the momentum / forgetting write, 16-row
         // blocks (block w, w+FW, ... for wave w)
-        const float* csp = u.cs + (long)s * u.cs_ss + (long)a.chunk_prev * 4;
-        const float pa = csp[0], pe = csp[1], s0 = csp[2];
         F bc[2], bd[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -1004,58 +1106,58 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             bc[ks] = on ? *reinterpret_cast<const F*>(&DcT[jl * DP + ks * 32 + kofs]) : zero_frag<OP>();
             bd[ks] = on ? *reinterpret_cast<const F*>(&DdT[jl * DP + ks * 32 + kofs]) : zero_frag<OP>();
         }
-        for (int n = 0; n < mineB; n += PB) {
+        auto update_rb = [&](int p, int n, bool live) {
+            const int rbk = min(wave + FW * n, nrb - 1), ib = 16 * rbk;
+            f32x4 um = (f32x4){0.f, 0.f, 0.f, 0.f}, us = um;
+            mma(um, kf[p][0], bc[0]);
+            mma(us, kf[p][0], bd[0]);
+            mma(um, kf[p][1], bc[1]);
+            mma(us, kf[p][1], bd[1]);
+            f32x4 mn, sn;
 #pragma unroll
-            for (int p = 0; p < PB; ++p) {
-                if (n + p < mineB) {   // wave-uniform
-                    const int ib = 16 * (wave + FW * (n + p));
-                    f32x4 um = (f32x4){0.f, 0.f, 0.f, 0.f}, us = um;
-                    mma(um, kf[p][0], bc[0]);
-                    mma(us, kf[p][0], bd[0]);
-                    mma(um, kf[p][1], bc[1]);
-                    mma(us, kf[p][1], bd[1]);
-                    float mn[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float sn = pe * sr[p][e] - us[e];
-                        mn[e] = pa * mr[p][e] + s0 * sr[p][e] - um[e];
-                        bad |= jok && (!__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn));
-                        if (jok) {
-                            const long o = (long)(ib + g4 + e) * h1 + j;
-                            M0[o] = mn[e];
-                            S0[o] = sn;
-                        }
-                        Wn[jl * WP + ib + g4 + e] = (OP)mn[e];
-                    }
-                    if (jok) {
-                        // 4 consecutive inputs of output j: 8 contiguous bytes of packed Wt
-                        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                        *reinterpret_cast<bf16x4*>(Wt0 + pk(j, ib + g4, d >> 5)) =
-                            (bf16x4){(bf16)mn[0], (bf16)mn[1], (bf16)mn[2], (bf16)mn[3]};
-                    }
-                }
-                if (n + PB < mineB) load_rb(p, n + p + PB);   // wave-uniform refill
+            for (int e = 0; e < 4; ++e) {
+                sn[e] = pe * sr[p][e] - us[e];
+                mn[e] = pa * mr[p][e] + s0 * sr[p][e] - um[e];
             }
+            if (live) {   // wave-uniform
+                *reinterpret_cast<f32x4*>(M0 + mso(rbk)) = mn;
+                *reinterpret_cast<f32x4*>(S0 + mso(rbk)) = sn;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bad |= !__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn[e]);
+                    Wn[jl * WP + ib + g4 + e] = (OP)mn[e];
+                }
+                // 4 consecutive inputs of output j: 8 contiguous bytes of packed Wt
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                *reinterpret_cast<bf16x4*>(Wt0 + pk(j, ib + g4, d >> 5)) =
+                    (bf16x4){(bf16)mn[0], (bf16)mn[1], (bf16)mn[2], (bf16)mn[3]};
+            }
+        };
+        // the prefetched row blocks, then (dim above 16 * FW * PB only) the
+        // rest, each loaded and used
+#pragma unroll
+        for (int p = 0; p < PB; ++p) update_rb(p, p, p < mineB);
+        for (int n = PB; n < mineB; ++n) {
+            load_rb(0, n);
+            update_rb(0, n, true);
         }
-    } else if (a.do_fwd) {
+    } else if constexpr (FWD) {
         // first chunk of the call: the block's columns of the current W_0
-        if (sizeof(OP) == 2) {
+        if constexpr (sizeof(OP) == 2) {
             for (int idx = tid; idx < JW * (d >> 3); idx += NT) {
                 const int cl = idx % JW, i = (idx / JW) * 8;
-                const int jj = j0 + cl;
-                bf16x8 w = jj < h1 ? *reinterpret_cast<const bf16x8*>(Wt0 + pk(jj, i, d >> 5)) : zero_frag<bf16>();
-                *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(Wn) + cl * WP + i) = w;
+                *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(Wn) + cl * WP + i) =
+                    *reinterpret_cast<const bf16x8*>(Wt0 + pk(j0 + cl, i, d >> 5));
             }
         } else {
             for (int idx = tid; idx < JW * d; idx += NT) {
                 const int i = idx / JW, cl = idx - i * JW;
-                const int jj = j0 + cl;
-                Wn[cl * WP + i] = jj < h1 ? (OP)M0[(long)i * h1 + jj] : (OP)0.0f;
+                Wn[cl * WP + i] = (OP)M0[cf0(i, j0 + cl, nrb)];
             }
         }
     }
     if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
-    if (!a.do_fwd) return;
+    if constexpr (!FWD) return;
     __syncthreads();
 
     // ================= chunk c's first-layer forward =================
@@ -1063,25 +1165,25 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
         f32x4 acc[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        for (int k = kbC; k < kbC + qC; k += PC) {
+        // prefetched steps straight-line, then (long K only) load and use;
+        // row blocks past the rows multiply zeros
 #pragma unroll
-            for (int p = 0; p < PC; ++p) {
-                const bool live = k + p < keC && k + p < kbC + qC;
-                const int k0 = min(k + p, klC) << 5;
-                F bv = *reinterpret_cast<const F*>(&Wn[jl * WP + k0 + kofs]);
-                if (!live) bv = zero_frag<OP>();
+        for (int p = 0; p < PC; ++p) {
+            const int k0 = min(kbC + p, klC) << 5;
+            F bv = *reinterpret_cast<const F*>(&Wn[jl * WP + k0 + kofs]);
+            if (kbC + p >= keC) bv = zero_frag<OP>();
 #pragma unroll
-                for (int m = 0; m < 8; ++m)
-                    if (m < nrow) mma(acc[m], rok[m] ? rx[p][m] : zero_frag<OP>(), bv);
-                if (k + PC < kbC + qC) {   // wave-uniform ring refill
-                    const long kn = (long)min(k + p + PC, klC) << 9;
-#pragma unroll
-                    for (int m = 0; m < 8; ++m)
-                        if (m < nrow) rx[p][m] = cvt<OP>(ld8(Ax[m] + kn));
-                }
-            }
+            for (int m = 0; m < 8; ++m) mma(acc[m], rok[m] ? rx[p][m] : zero_frag<OP>(), bv);
         }
-        partial_tiles<8>(red, acc, nrow, 128, wave, lane, RP);
+        for (int k = kbC + PC; k < keC; ++k) {
+            F xv[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) xv[m] = cvt<OP>(ld8(Ax[m] + ((long)k << 9)));
+            const F bv = *reinterpret_cast<const F*>(&Wn[jl * WP + (k << 5) + kofs]);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) mma(acc[m], rok[m] ? xv[m] : zero_frag<OP>(), bv);
+        }
+        partial_tiles<8>(red, acc, 8, 128, wave, lane, RP);
     }
     // z of every (row, column): the partial tiles summed into slot 0
     for (int idx = tid; idx < R * JW; idx += NT) {
@@ -1092,21 +1194,21 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
         red[r * RP + cl] = z;
     }
     __syncthreads();
-    if (u.L >= 2) {
+    if constexpr (DEEP) {
         // activations (packed [rows][h1]) and, for key rows, SiLU'(z)
         for (int idx = tid; idx < R * (JW / 8); idx += NT) {
             const int r = idx / (JW / 8), c8 = (idx % (JW / 8)) * 8, jj = j0 + c8;
             F hv;
-            float sl[8];
+            float sd[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float z = red[r * RP + c8 + e];
                 const float sg = sigmoid(z);
                 hv[e] = (OP)(z * sg);
-                sl[e] = sg * (1.0f + z * (1.0f - sg));
+                sd[e] = sg * (1.0f + z * (1.0f - sg));
             }
             st8<OP>(reinterpret_cast<OP*>(a.act) + (long)s * a.act_ss + pk(r, jj, h1 >> 5), hv);
-            if (r >= a.nq) st8f(a.dsl1 + (long)s * a.dsl1_ss + (long)(r - a.nq) * h1 + jj, sl);
+            if (r >= a.nq) st8f(a.dsl1 + (long)s * a.dsl1_ss + (long)(r - a.nq) * h1 + jj, sd);
         }
         // the key rows' activations transposed (packed [h1][bp], zero past the chunk)
         if (a.nk > 0) {
@@ -1160,13 +1262,27 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     }
 }
 
+template <class OP, bool UPD, bool FWD>
+static void launch_first_as(const FirstArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+    if (a.u.L >= 2) hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, true>), grid, dim3(FW * 64), lds, st, a);
+    else hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, false>), grid, dim3(FW * 64), lds, st, a);
+}
+
+template <class OP>
+static void launch_first_op(const FirstArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+    if (a.do_update && a.do_fwd) launch_first_as<OP, true, true>(a, grid, lds, st);
+    else if (a.do_update) launch_first_as<OP, true, false>(a, grid, lds, st);
+    else launch_first_as<OP, false, true>(a, grid, lds, st);
+}
+
 hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st) {
+    if (!a.do_update && !a.do_fwd) return hipSuccess;
     const int pairs = (a.upd_ntiles + 1) / 2;
     dim3 grid(a.nb1 + pairs, ns);
     size_t lds = first_lds_bytes(a.dim, a.u.bp, f32);
     if (pairs > 0 && lds < UPD_PAIR_LDS) lds = UPD_PAIR_LDS;
-    if (f32) hipLaunchKernelGGL(first_layer_kernel<float>, grid, dim3(FW * 64), lds, st, a);
-    else hipLaunchKernelGGL(first_layer_kernel<bf16>, grid, dim3(FW * 64), lds, st, a);
+    if (f32) launch_first_op<float>(a, grid, lds, st);
+    else launch_first_op<bf16>(a, grid, lds, st);
     return hipGetLastError();
 }
 
@@ -1188,17 +1304,26 @@ hipError_t launch_update_range(const UpdArgs& u, int tile0, int ntiles, int ns, 
 // ---------------------------------------------------------------------------
 // State set-up, bf16 copy, export / import.
 
-__global__ void init_kernel(float* M, float* S, const float* init, long P, int H, int ns) {
+// Position in the state of canonical element p (row-major layers) of one
+// stream: layer 0 (d0 x h1, the first d0 * h1 elements) in accumulator order.
+__device__ __forceinline__ long state_pos(long p, int d0, int h1) {
+    if (p >= (long)d0 * h1) return p;
+    const int i = (int)(p / h1), j = (int)(p - (long)i * h1);
+    return cf0(i, j, d0 >> 4);
+}
+
+__global__ void init_kernel(float* M, float* S, const float* init, long P, int H, int ns, int d0, int h1) {
     const long n = (long)ns * P;
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
         const long s = i / P, p = i - s * P;
-        M[i] = init[(s % H) * P + p];
+        M[s * P + state_pos(p, d0, h1)] = init[(s % H) * P + p];
         S[i] = 0.f;
     }
 }
 
-hipError_t launch_init(float* M, float* S, const float* init, long P, int H, int ns, hipStream_t st) {
-    hipLaunchKernelGGL(init_kernel, dim3(2048), dim3(256), 0, st, M, S, init, P, H, ns);
+hipError_t launch_init(float* M, float* S, const float* init, long P, int H, int ns, int d0, int h1,
+                       hipStream_t st) {
+    hipLaunchKernelGGL(init_kernel, dim3(2048), dim3(256), 0, st, M, S, init, P, H, ns, d0, h1);
     return hipGetLastError();
 }
 
@@ -1218,7 +1343,8 @@ __global__ __launch_bounds__(256) void shadow_kernel(UpdArgs u) {
     const float* Mp = u.M + (long)s * u.P + u.off[l];
     for (int idx = tid; idx < 64 * 64; idx += 256) {
         const int i = idx >> 6, j = idx & 63;
-        T[i][j] = (i0 + i < din && j0 + j < dout) ? Mp[(long)(i0 + i) * dout + j0 + j] : 0.f;
+        const long o = l == 0 ? cf0(i0 + i, j0 + j, din >> 4) : (long)(i0 + i) * dout + j0 + j;
+        T[i][j] = (i0 + i < din && j0 + j < dout) ? Mp[o] : 0.f;
     }
     __syncthreads();
     bf16* Wp = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P + u.off[l];
@@ -1239,31 +1365,33 @@ hipError_t launch_shadow(const UpdArgs& u, int ntiles, int ns, hipStream_t st) {
     return hipGetLastError();
 }
 
-__global__ void export_kernel(const float* M, const float* S, float* dst, long P, int ns) {
+__global__ void export_kernel(const float* M, const float* S, float* dst, long P, int ns, int d0, int h1) {
     const long n = (long)ns * P;
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-        const long s = i / P, p = i - s * P;
-        dst[s * 2 * P + p] = M[i];
-        dst[s * 2 * P + P + p] = S[i];
+        const long s = i / P, p = i - s * P, q = s * P + state_pos(p, d0, h1);
+        dst[s * 2 * P + p] = M[q];
+        dst[s * 2 * P + P + p] = S[q];
     }
 }
 
-__global__ void import_kernel(float* M, float* S, const float* src, long P, int ns) {
+__global__ void import_kernel(float* M, float* S, const float* src, long P, int ns, int d0, int h1) {
     const long n = (long)ns * P;
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-        const long s = i / P, p = i - s * P;
-        M[i] = src[s * 2 * P + p];
-        S[i] = src[s * 2 * P + P + p];
+        const long s = i / P, p = i - s * P, q = s * P + state_pos(p, d0, h1);
+        M[q] = src[s * 2 * P + p];
+        S[q] = src[s * 2 * P + P + p];
     }
 }
 
-hipError_t launch_export(const float* M, const float* S, float* dst, long P, int ns, hipStream_t st) {
-    hipLaunchKernelGGL(export_kernel, dim3(2048), dim3(256), 0, st, M, S, dst, P, ns);
+hipError_t launch_export(const float* M, const float* S, float* dst, long P, int ns, int d0, int h1,
+                         hipStream_t st) {
+    hipLaunchKernelGGL(export_kernel, dim3(2048), dim3(256), 0, st, M, S, dst, P, ns, d0, h1);
     return hipGetLastError();
 }
 
-hipError_t launch_import(float* M, float* S, const float* src, long P, int ns, hipStream_t st) {
-    hipLaunchKernelGGL(import_kernel, dim3(2048), dim3(256), 0, st, M, S, src, P, ns);
+hipError_t launch_import(float* M, float* S, const float* src, long P, int ns, int d0, int h1,
+                         hipStream_t st) {
+    hipLaunchKernelGGL(import_kernel, dim3(2048), dim3(256), 0, st, M, S, src, P, ns, d0, h1);
     return hipGetLastError();
 }
 
