@@ -3,8 +3,8 @@
 //
 // State blob: [header 256 B][M fp32 ns*P][S fp32 ns*P][Wt bf16 ns*P], each
 // region 256-byte aligned; per stream the layers follow each other.  In M and
-// S, W_0 is in the matrix instruction's accumulator order (cf0) and the other
-// layers row-major [d_in][d_out]; Wt holds every layer fragment-packed
+// S, W_0 and W_1 are in matrix-instruction accumulator orders (cf0, cf1) and
+// the other layers row-major [d_in][d_out]; Wt holds every layer fragment-packed
 // [d_out][d_in].  Export and import convert to and from the canonical
 // row-major form.
 #include <mutex>
@@ -356,8 +356,8 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
         }
         if (f32) {
             // fp32 operands straight from the fp32 master: row-major [din][dout],
-            // layer 0 in accumulator order
-            g.bmode = l == 0 ? B_CFRAG : B_STRIDED;
+            // layers 0 and 1 in accumulator order
+            g.bmode = l == 0 ? B_CFRAG : l == 1 ? B_CF1 : B_STRIDED;
             g.b = state + sl.M + (size_t)c->off[l] * 4;
             g.b_ss = c->P;
             g.b_ld = c->dout[l];
@@ -544,8 +544,10 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     a.dct1 = ws + w.dct[0];
     a.ddt1 = ws + w.ddt[0];
     a.dt1_ss = w.dt_ss[0];
-    const int tile1 = c->tbase[c->L > 1 ? 1 : c->L];
-    const int ntile_rest = c->tbase[c->L] - tile1;
+    // layers 0 and 1 are updated by the first-layer blocks; layers 2.. by
+    // update tiles in the same launch
+    const int tile2 = c->tbase[c->L > 2 ? 2 : c->L];
+    const int ntile_rest = c->tbase[c->L] - tile2;
 
     for (int ci = 0; ci <= C; ++ci) {
         a.do_update = ci >= 1;
@@ -575,7 +577,7 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         if (!a.do_update && !a.do_fwd) continue;
         // one launch: the first-layer blocks plus chunk c-1's update tiles of
         // the other layers (independent of each other)
-        a.upd_tile0 = tile1;
+        a.upd_tile0 = tile2;
         a.upd_ntiles = a.do_update ? ntile_rest : 0;
         if (timed(K_FIRST, st, [&] { return launch_first(a, (int)ns, f32 ? 1 : 0, st); }) != hipSuccess)
             return TM_ERR_HIP;
@@ -685,7 +687,8 @@ tm_status tm_state_init(const tm_ctx* c, void* state, int batch, int heads, cons
         UpdArgs u = base_upd(c, s, ns);
         if (launch_header(reinterpret_cast<StateHeader*>(s), c->hash, batch, heads, st) != hipSuccess)
             return TM_ERR_HIP;
-        if (launch_init(u.M, u.S, init, c->P, heads, (int)ns, c->din[0], c->dout[0], st) != hipSuccess)
+        if (launch_init(u.M, u.S, init, c->P, heads, (int)ns, c->din[0], c->dout[0], c->L > 1 ? c->dout[1] : 0,
+                        st) != hipSuccess)
             return TM_ERR_HIP;
         return hip_status(launch_shadow(u, c->tbase[c->L], (int)ns, st));
     });
@@ -762,7 +765,7 @@ tm_status tm_state_export(const tm_ctx* c, const void* state, int batch, int hea
     const char* s = static_cast<const char*>(state);
     return hip_status(launch_export(reinterpret_cast<const float*>(s + sl.M),
                                     reinterpret_cast<const float*>(s + sl.S), dst, c->P, (int)ns, c->din[0],
-                                    c->dout[0], static_cast<hipStream_t>(stream)));
+                                    c->dout[0], c->L > 1 ? c->dout[1] : 0, static_cast<hipStream_t>(stream)));
 }
 
 tm_status tm_state_import(const tm_ctx* c, void* state, int batch, int heads, const float* src,
@@ -776,7 +779,9 @@ tm_status tm_state_import(const tm_ctx* c, void* state, int batch, int heads, co
     UpdArgs u = base_upd(c, s, ns);
     if (launch_header(reinterpret_cast<StateHeader*>(s), c->hash, batch, heads, st) != hipSuccess)
         return TM_ERR_HIP;
-    if (launch_import(u.M, u.S, src, c->P, (int)ns, c->din[0], c->dout[0], st) != hipSuccess) return TM_ERR_HIP;
+    if (launch_import(u.M, u.S, src, c->P, (int)ns, c->din[0], c->dout[0], c->L > 1 ? c->dout[1] : 0, st) !=
+        hipSuccess)
+        return TM_ERR_HIP;
     return hip_status(launch_shadow(u, c->tbase[c->L], (int)ns, st));
 }
 

@@ -58,6 +58,16 @@ __host__ __device__ inline long cf0(int i, int j, int nrb) {
     return ((((long)(j >> 4) * nrb + (i >> 4)) * 64 + (j & 15) + 16 * ((i & 15) >> 2)) << 2) + (i & 3);
 }
 
+// Layer 1's M and S (h1 x d1) are stored in the accumulator order of its
+// update computed transposed (rows: layer 1's outputs n, columns: its inputs
+// j): per 16-row block of j, per 16-column block of n, lane l holds the 4
+// consecutive outputs n = 4 * (l / 16) .. + 3 of input j = l % 16.  The
+// first-layer workgroup that owns inputs j .. j+15 then moves each 16 x 16
+// block as one contiguous 1 KB float4 access.  ncb = d1 / 16.
+__host__ __device__ inline long cf1(int j, int n, int ncb) {
+    return ((((long)(j >> 4) * ncb + (n >> 4)) * 64 + (j & 15) + 16 * ((n & 15) >> 2)) << 2) + (n & 3);
+}
+
 // Token-major arrays [batch][Tc][H][d]; gates use d = 1.
 struct TokLayout {
     int Tc, H, d;
@@ -70,7 +80,7 @@ enum { EPI_HIDDEN = 0, EPI_OUT = 1, EPI_BWD = 2 };
 // Rows r < n0 are queries, rows r >= n0 keys (t = r - n0 is the key's token
 // inside the chunk); the backward has key rows only (n0 = 0).
 enum { A_TOKENS = 0, A_ROWS = 1, A_PACKED = 2 };
-enum { B_STRIDED = 0, B_ROWS = 1, B_PACKED = 2, B_CFRAG = 3 };
+enum { B_STRIDED = 0, B_ROWS = 1, B_PACKED = 2, B_CFRAG = 3, B_CF1 = 4 };
 struct GemmArgs {
     int nrows, N, K;
     // A.  A_TOKENS: rows r < n0 are tokens (at0 + r) of a0, rows r >= n0
@@ -83,7 +93,8 @@ struct GemmArgs {
     // B.  B_STRIDED: element (k, n) at b + s*b_ss + n + k*b_ld (row-major
     // [K][N]); B_ROWS: at b + s*b_ss + n*b_ld + k (row n contiguous in K);
     // B_PACKED: packed [N][K] at b + s*b_ss; B_CFRAG: layer 0's fp32 master
-    // in accumulator order, cf0(k, n, K / 16), at b + s*b_ss.
+    // in accumulator order, cf0(k, n, K / 16), at b + s*b_ss; B_CF1: layer
+    // 1's, cf1(k, n, N / 16).
     const void* b;
     long b_ss, b_ld;
     int bmode;
@@ -144,17 +155,19 @@ struct UpdArgs {
     long wr_ss;
 };
 
-// First-layer part of chunk step c (one launch; it runs concurrently with
-// the update tiles of layers 1.. for chunk c-1).  One workgroup per JW-wide
-// column block of the first weight matrix W_0 (full height):
+// First-layer part of chunk step c, one launch (the update tiles of layers
+// 2.. for chunk c-1 ride in the same launch).  One workgroup per JW = 16
+// hidden units j: columns j of W_0 (full height) and rows j of W_1:
 //   * if do_update: chunk c-1's update of those columns.  The first layer's
 //     Delta for the columns is formed in place (depth >= 2) from layer 1's
-//     Delta and a row-major copy of layer 1's chunk-start weights, or read
-//     back (depth 1); theta-weighted, reduced against the chunk's keys and
-//     folded into M and S (and the bf16 copy of W_0);
+//     Delta and the packed operand-type copy of layer 1's chunk-start
+//     weights, or read back (depth 1); theta-weighted, reduced against the
+//     chunk's keys and folded into M and S (and the bf16 copy of W_0);
 //   * if do_fwd: chunk c's first-layer forward of [queries of chunk c-1;
-//     keys of chunk c] through the freshly written columns.
-// K is split over the workgroup's 4 waves for the backward and the forward
+//     keys of chunk c] through the freshly written columns;
+//   * if do_update and depth >= 2: chunk c-1's update of rows j of W_1 (and
+//     of their bf16 copy and operand-type copy).
+// K is split over the workgroup's 8 waves for the backward and the forward
 // products (partial tiles summed in LDS), so no wave walks a long chain of
 // dependent loads.
 constexpr int JW = 16;
@@ -243,13 +256,14 @@ hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st);
 // update tiles [tile0, tile0 + ntiles) of every stream
 hipError_t launch_update_range(const UpdArgs& u, int tile0, int ntiles, int ns, int f32, hipStream_t st);
 // init / export / import convert between the canonical row-major layers and
-// the state layout (layer 0 of d0 x h1 in accumulator order)
+// the state layout (layer 0 of d0 x h1 and layer 1 of h1 x d1 in accumulator
+// order; d1 = 0 for depth 1)
 hipError_t launch_init(float* M, float* S, const float* init, long P, int H, int ns, int d0, int h1,
-                       hipStream_t st);
+                       int d1, hipStream_t st);
 hipError_t launch_shadow(const UpdArgs& u, int ntiles, int ns, hipStream_t st);
 hipError_t launch_export(const float* M, const float* S, float* dst, long P, int ns, int d0, int h1,
-                         hipStream_t st);
-hipError_t launch_import(float* M, float* S, const float* src, long P, int ns, int d0, int h1,
+                         int d1, hipStream_t st);
+hipError_t launch_import(float* M, float* S, const float* src, long P, int ns, int d0, int h1, int d1,
                          hipStream_t st);
 hipError_t launch_header(StateHeader* h, uint64_t hash, int batch, int heads,
                          hipStream_t st);

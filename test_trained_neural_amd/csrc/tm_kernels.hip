@@ -91,6 +91,14 @@ __device__ __forceinline__ void mma(f32x4& c, f32x8 a, f32x8 b) {
 
 __device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// The chunk's momentum / forgetting write of one element, with explicit
+// fused multiply-adds, so that every kernel (and every instantiation of one)
+// rounds it the same way:  S' = p_eta S - U_S,  M' = p_alpha M + s0 S - U_M.
+__device__ __forceinline__ float mom_s(float pe, float s, float us) { return __builtin_fmaf(pe, s, -us); }
+__device__ __forceinline__ float mom_m(float pa, float m, float s0, float s, float um) {
+    return __builtin_fmaf(pa, m, __builtin_fmaf(s0, s, -um));
+}
+
 __device__ __forceinline__ long tok_off(const TokLayout& tl, int s, int t) {
     int bi = s / tl.H, hi = s - bi * tl.H;
     return ((long)bi * tl.Tc + t) * tl.H * (long)tl.d + (long)hi * tl.d;
@@ -199,6 +207,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
         if constexpr (BM == B_PACKED) bcol[n] = base + pkf(cb, 0, nsteps, lane);
         else if constexpr (BM == B_ROWS) bcol[n] = base + (long)c * g.b_ld + kofs;
         else if constexpr (BM == B_CFRAG) bcol[n] = base + cf0(kofs, c, g.K >> 4);
+        else if constexpr (BM == B_CF1) bcol[n] = base + cf1(kofs, c, g.N >> 4);
         else bcol[n] = base + c + (long)kofs * g.b_ld;
     }
     // the ring holds raw storage vectors; conversion to the operand type
@@ -214,6 +223,13 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
         for (int n = 0; n < NR; ++n) {
             if constexpr (BM == B_PACKED || BM == B_ROWS) {
                 bb[p][n] = ld8(bcol[n] + k * bstep);
+            } else if constexpr (BM == B_CF1) {
+                // inputs kofs .. kofs+7 of output c: 8 lanes' slots, 4 floats apart
+                const BT* q = bcol[n] + k * (2L * (g.N >> 4) * 256);
+                RB u;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u[e] = q[4 * e];
+                bb[p][n] = u;
             } else if constexpr (BM == B_CFRAG) {
                 // rows kofs..kofs+3 and kofs+4..kofs+7 of the column: two
                 // float4 one 16-lane group apart
@@ -463,6 +479,7 @@ static hipError_t launch_gemm(const GemmArgs& g, int ns, hipStream_t st) {
 hipError_t launch_fwd(const GemmArgs& g, int ns, int f32, hipStream_t st) {
     if (f32) {
         if (g.bmode == B_CFRAG) return launch_gemm<float, float, float, B_CFRAG>(g, ns, st);
+        if (g.bmode == B_CF1) return launch_gemm<float, float, float, B_CF1>(g, ns, st);
         return launch_gemm<float, float, float, B_STRIDED>(g, ns, st);
     }
     return launch_gemm<bf16, bf16, bf16, B_PACKED>(g, ns, st);
@@ -550,10 +567,17 @@ __device__ void copy_layer1(const ScanArgs& a, long blk) {
         const long f = v >> 6;
         const int ks = (int)(f % nks), rb = (int)(f / nks);
         const int i = rb * 16 + (ln & 15), j = ks * 32 + 8 * (ln >> 4);
-        const f32x8 w = ld8(a.w1_master + s * a.w1_ss + (long)i * a.w1_dout + j);
+        // outputs j .. j+3 and j+4 .. j+7 of input i: two float4 of layer 1's
+        // accumulator-order master, one 16-lane group apart
+        const float* m = a.w1_master + s * a.w1_ss + cf1(i, j, a.w1_dout >> 4);
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(m);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(m + 64);
         V o;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = (T)w[q];
+        for (int q = 0; q < 4; ++q) {
+            o[q] = (T)lo[q];
+            o[q + 4] = (T)hi[q];
+        }
         *reinterpret_cast<V*>(reinterpret_cast<T*>(a.w1_copy) + s * a.w1c_ss + (v << 3)) = o;
     }
 }
@@ -791,8 +815,8 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
             f32x4 mn, sn;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                sn[e] = pe * sv[e] - US[i][j + e];
-                mn[e] = pa * m[e] + s0 * sv[e] - UM[i][j + e];
+                sn[e] = mom_s(pe, sv[e], US[i][j + e]);
+                mn[e] = mom_m(pa, m[e], s0, sv[e], UM[i][j + e]);
                 bad |= !__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn[e]);
                 UM[i][j + e] = mn[e];
             }
@@ -894,7 +918,7 @@ __device__ __forceinline__ void partial_tiles(float* red, const f32x4* acc, int 
 // everything a wave needs is requested at kernel start when it fits the
 // register file, so each phase waits for at most one round of memory.
 template <class OP> struct FirstDepth;
-template <> struct FirstDepth<bf16> { static constexpr int A = 2, B = 4, C = 2; };
+template <> struct FirstDepth<bf16> { static constexpr int A = 2, B = 3, C = 2; };
 template <> struct FirstDepth<float> { static constexpr int A = 1, B = 2, C = 1; };
 
 // UPD: chunk c-1's update runs (steps 1..C); FWD: chunk c's forward runs (a
@@ -938,6 +962,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     float* M0 = u.M + (long)s * u.P;
     float* S0 = u.S + (long)s * u.P;
     bf16* Wt0 = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P;
+    bf16* Wt1 = Wt0 + (DEEP ? u.off[1] : 0);
     const OP* kt = reinterpret_cast<const OP*>(a.kt_prev) + (long)s * a.kt_ss;
     const int nrb = d >> 4;
     const int nkb = bp >> 5;
@@ -1041,6 +1066,84 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     };
     if constexpr (!BWD) issue_rows();
 
+    // (5) chunk c-1's update of rows j0 .. j0+15 of W_1 (depth >= 2), its
+    //     operands requested once the forward's registers are free.  It is
+    //     computed transposed, U^T = (c Delta_1)^T H_1 (rows: layer 1's
+    //     outputs n in 16-blocks nb = wave, wave + FW, ...; columns: the
+    //     block's inputs j; K: tokens), so a lane's 4 results are outputs
+    //     n .. n+3 of one input j: one float4 of M and S in their accumulator
+    //     order, 8 contiguous bytes of the packed operand-type copy.
+    constexpr bool W1 = UPD && DEEP;
+    constexpr int PN = 3;                   // n-blocks per wave held in registers
+    const int d1 = DEEP ? u.dout[1] : 16, ncb1 = d1 >> 4;
+    const int mine1 = (ncb1 - wave + FW - 1) / FW;
+    F h1f[2], c1f[PN][2], d1f[PN][2];
+    f32x4 m1r[PN], s1r[PN];
+    const OP* at1 = DEEP ? reinterpret_cast<const OP*>(u.at[1]) + (long)s * u.at_ss[1] : nullptr;
+    const OP* dc1 = DEEP ? reinterpret_cast<const OP*>(u.dct[1]) + (long)s * u.dt_ss[1] : nullptr;
+    const OP* dd1 = DEEP ? reinterpret_cast<const OP*>(u.ddt[1]) + (long)s * u.dt_ss[1] : nullptr;
+    float* M1 = u.M + (long)s * u.P + (DEEP ? u.off[1] : 0);
+    float* S1 = u.S + (long)s * u.P + (DEEP ? u.off[1] : 0);
+    auto mso1 = [&](int nb) { return ((long)(blockIdx.x * ncb1 + nb) * 64 + lane) * 4; };
+    auto load_w1 = [&](int p, int n) {
+        const int nb = min(wave + FW * n, ncb1 - 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int kc = min(ks, nkb - 1), t0 = ks * 32 + kofs;
+            const F vc = tok8<OP>(dc1 + pkf(nb, kc, nkb, lane), t0, b);   // padding tokens: zero
+            const F vd = tok8<OP>(dd1 + pkf(nb, kc, nkb, lane), t0, b);
+            c1f[p][ks] = ks < nkb ? vc : zero_frag<OP>();
+            d1f[p][ks] = ks < nkb ? vd : zero_frag<OP>();
+        }
+        m1r[p] = *reinterpret_cast<const f32x4*>(M1 + mso1(nb));
+        s1r[p] = *reinterpret_cast<const f32x4*>(S1 + mso1(nb));
+    };
+    auto issue1 = [&]() {
+        if constexpr (W1) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) h1f[ks] = cvt<OP>(ld8(at1 + pkf(blockIdx.x, min(ks, nkb - 1), nkb, lane)));
+#pragma unroll
+            for (int p = 0; p < PN; ++p) load_w1(p, p);
+        }
+    };
+    auto update1 = [&](int p, int n, bool live) {
+        const int nb = min(wave + FW * n, ncb1 - 1);
+        f32x4 um = (f32x4){0.f, 0.f, 0.f, 0.f}, us = um;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            mma(um, c1f[p][ks], h1f[ks]);
+            mma(us, d1f[p][ks], h1f[ks]);
+        }
+        f32x4 mn, sn;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sn[e] = mom_s(pe, s1r[p][e], us[e]);
+            mn[e] = mom_m(pa, m1r[p][e], s0, s1r[p][e], um[e]);
+        }
+        if (live) {   // wave-uniform
+            *reinterpret_cast<f32x4*>(M1 + mso1(nb)) = mn;
+            *reinterpret_cast<f32x4*>(S1 + mso1(nb)) = sn;
+            const int n0 = nb * 16 + g4;   // outputs n0 .. n0+3 of input j
+            OP* wr = reinterpret_cast<OP*>(u.wr_next) + (long)s * u.wr_ss + pk(j, n0, d1 >> 5);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bad |= !__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn[e]);
+                wr[e] = (OP)mn[e];
+                Wt1[pk(n0 + e, j, h1 >> 5)] = (bf16)mn[e];
+            }
+        }
+    };
+    auto run1 = [&]() {
+        if constexpr (W1) {
+#pragma unroll
+            for (int p = 0; p < PN; ++p) update1(p, p, p < mine1);
+            for (int n = PN; n < mine1; ++n) {
+                load_w1(0, n);
+                update1(0, n, true);
+            }
+        }
+    };
+
     // ================= chunk c-1's update of the block's columns =================
     if constexpr (UPD) {
         if constexpr (BWD) {
@@ -1116,8 +1219,8 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             f32x4 mn, sn;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                sn[e] = pe * sr[p][e] - us[e];
-                mn[e] = pa * mr[p][e] + s0 * sr[p][e] - um[e];
+                sn[e] = mom_s(pe, sr[p][e], us[e]);
+                mn[e] = mom_m(pa, mr[p][e], s0, sr[p][e], um[e]);
             }
             if (live) {   // wave-uniform
                 *reinterpret_cast<f32x4*>(M0 + mso(rbk)) = mn;
@@ -1141,6 +1244,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             load_rb(0, n);
             update_rb(0, n, true);
         }
+
     } else if constexpr (FWD) {
         // first chunk of the call: the block's columns of the current W_0
         if constexpr (sizeof(OP) == 2) {
@@ -1156,8 +1260,12 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             }
         }
     }
-    if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
-    if constexpr (!FWD) return;
+    if constexpr (!FWD) {
+        issue1();
+        run1();
+        if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
+        return;
+    }
     __syncthreads();
 
     // ================= chunk c's first-layer forward =================
@@ -1183,6 +1291,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) mma(acc[m], rok[m] ? xv[m] : zero_frag<OP>(), bv);
         }
+        issue1();   // layer 1's rows: operands now, the update after the epilogue
         partial_tiles<8>(red, acc, 8, 128, wave, lane, RP);
     }
     // z of every (row, column): the partial tiles summed into slot 0
@@ -1260,6 +1369,8 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             }
         }
     }
+    run1();
+    if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
 }
 
 template <class OP, bool UPD, bool FWD>
@@ -1305,25 +1416,35 @@ hipError_t launch_update_range(const UpdArgs& u, int tile0, int ntiles, int ns, 
 // State set-up, bf16 copy, export / import.
 
 // Position in the state of canonical element p (row-major layers) of one
-// stream: layer 0 (d0 x h1, the first d0 * h1 elements) in accumulator order.
-__device__ __forceinline__ long state_pos(long p, int d0, int h1) {
-    if (p >= (long)d0 * h1) return p;
-    const int i = (int)(p / h1), j = (int)(p - (long)i * h1);
-    return cf0(i, j, d0 >> 4);
+// stream: layer 0 (d0 x h1) and layer 1 (h1 x d1, d1 = 0 for depth 1) in
+// accumulator order, the other layers row-major.
+__device__ __forceinline__ long state_pos(long p, int d0, int h1, int d1) {
+    const long p0 = (long)d0 * h1;
+    if (p < p0) {
+        const int i = (int)(p / h1), j = (int)(p - (long)i * h1);
+        return cf0(i, j, d0 >> 4);
+    }
+    if (p < p0 + (long)h1 * d1) {
+        const long q = p - p0;
+        const int j = (int)(q / d1), n = (int)(q - (long)j * d1);
+        return p0 + cf1(j, n, d1 >> 4);
+    }
+    return p;
 }
 
-__global__ void init_kernel(float* M, float* S, const float* init, long P, int H, int ns, int d0, int h1) {
+__global__ void init_kernel(float* M, float* S, const float* init, long P, int H, int ns, int d0, int h1,
+                            int d1) {
     const long n = (long)ns * P;
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
         const long s = i / P, p = i - s * P;
-        M[s * P + state_pos(p, d0, h1)] = init[(s % H) * P + p];
+        M[s * P + state_pos(p, d0, h1, d1)] = init[(s % H) * P + p];
         S[i] = 0.f;
     }
 }
 
-hipError_t launch_init(float* M, float* S, const float* init, long P, int H, int ns, int d0, int h1,
+hipError_t launch_init(float* M, float* S, const float* init, long P, int H, int ns, int d0, int h1, int d1,
                        hipStream_t st) {
-    hipLaunchKernelGGL(init_kernel, dim3(2048), dim3(256), 0, st, M, S, init, P, H, ns, d0, h1);
+    hipLaunchKernelGGL(init_kernel, dim3(2048), dim3(256), 0, st, M, S, init, P, H, ns, d0, h1, d1);
     return hipGetLastError();
 }
 
@@ -1343,7 +1464,8 @@ __global__ __launch_bounds__(256) void shadow_kernel(UpdArgs u) {
     const float* Mp = u.M + (long)s * u.P + u.off[l];
     for (int idx = tid; idx < 64 * 64; idx += 256) {
         const int i = idx >> 6, j = idx & 63;
-        const long o = l == 0 ? cf0(i0 + i, j0 + j, din >> 4) : (long)(i0 + i) * dout + j0 + j;
+        const long o = l == 0 ? cf0(i0 + i, j0 + j, din >> 4)
+                     : l == 1 ? cf1(i0 + i, j0 + j, dout >> 4) : (long)(i0 + i) * dout + j0 + j;
         T[i][j] = (i0 + i < din && j0 + j < dout) ? Mp[o] : 0.f;
     }
     __syncthreads();
@@ -1365,33 +1487,35 @@ hipError_t launch_shadow(const UpdArgs& u, int ntiles, int ns, hipStream_t st) {
     return hipGetLastError();
 }
 
-__global__ void export_kernel(const float* M, const float* S, float* dst, long P, int ns, int d0, int h1) {
+__global__ void export_kernel(const float* M, const float* S, float* dst, long P, int ns, int d0, int h1,
+                              int d1) {
     const long n = (long)ns * P;
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-        const long s = i / P, p = i - s * P, q = s * P + state_pos(p, d0, h1);
+        const long s = i / P, p = i - s * P, q = s * P + state_pos(p, d0, h1, d1);
         dst[s * 2 * P + p] = M[q];
         dst[s * 2 * P + P + p] = S[q];
     }
 }
 
-__global__ void import_kernel(float* M, float* S, const float* src, long P, int ns, int d0, int h1) {
+__global__ void import_kernel(float* M, float* S, const float* src, long P, int ns, int d0, int h1,
+                              int d1) {
     const long n = (long)ns * P;
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-        const long s = i / P, p = i - s * P, q = s * P + state_pos(p, d0, h1);
+        const long s = i / P, p = i - s * P, q = s * P + state_pos(p, d0, h1, d1);
         M[q] = src[s * 2 * P + p];
         S[q] = src[s * 2 * P + P + p];
     }
 }
 
-hipError_t launch_export(const float* M, const float* S, float* dst, long P, int ns, int d0, int h1,
+hipError_t launch_export(const float* M, const float* S, float* dst, long P, int ns, int d0, int h1, int d1,
                          hipStream_t st) {
-    hipLaunchKernelGGL(export_kernel, dim3(2048), dim3(256), 0, st, M, S, dst, P, ns, d0, h1);
+    hipLaunchKernelGGL(export_kernel, dim3(2048), dim3(256), 0, st, M, S, dst, P, ns, d0, h1, d1);
     return hipGetLastError();
 }
 
-hipError_t launch_import(float* M, float* S, const float* src, long P, int ns, int d0, int h1,
+hipError_t launch_import(float* M, float* S, const float* src, long P, int ns, int d0, int h1, int d1,
                          hipStream_t st) {
-    hipLaunchKernelGGL(import_kernel, dim3(2048), dim3(256), 0, st, M, S, src, P, ns, d0, h1);
+    hipLaunchKernelGGL(import_kernel, dim3(2048), dim3(256), 0, st, M, S, src, P, ns, d0, h1, d1);
     return hipGetLastError();
 }
 
