@@ -685,12 +685,8 @@ tm_status tm_state_init(const tm_ctx* c, void* state, int batch, int heads, cons
     return with_graph(c, make_key(0, batch, heads, 0, 0, {state, init}), static_cast<hipStream_t>(stream),
                       [&](hipStream_t st) {
         UpdArgs u = base_upd(c, s, ns);
-        if (launch_header(reinterpret_cast<StateHeader*>(s), c->hash, batch, heads, st) != hipSuccess)
-            return TM_ERR_HIP;
-        if (launch_init(u.M, u.S, init, c->P, heads, (int)ns, c->din[0], c->dout[0], c->L > 1 ? c->dout[1] : 0,
-                        st) != hipSuccess)
-            return TM_ERR_HIP;
-        return hip_status(launch_shadow(u, c->tbase[c->L], (int)ns, st));
+        return hip_status(launch_state_init(u, c->tbase[c->L], (int)ns, init, heads,
+                                            reinterpret_cast<StateHeader*>(s), c->hash, batch, heads, st));
     });
 }
 

@@ -251,16 +251,14 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
 // B = fp32 master read with stride).  bwd: A fp32 deltas, B fp32 master.
 hipError_t launch_fwd(const GemmArgs& g, int ns, int f32, hipStream_t st);
 hipError_t launch_bwd(const GemmArgs& g, int ns, int f32, hipStream_t st);
-hipError_t launch_update(const UpdArgs& u, int ntiles, int ns, int f32, hipStream_t st);
 hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st);
-// update tiles [tile0, tile0 + ntiles) of every stream
-hipError_t launch_update_range(const UpdArgs& u, int tile0, int ntiles, int ns, int f32, hipStream_t st);
-// init / export / import convert between the canonical row-major layers and
-// the state layout (layer 0 of d0 x h1 and layer 1 of h1 x d1 in accumulator
+// export / import convert between the canonical row-major layers and the
+// state layout (layer 0 of d0 x h1 and layer 1 of h1 x d1 in accumulator
 // order; d1 = 0 for depth 1)
-hipError_t launch_init(float* M, float* S, const float* init, long P, int H, int ns, int d0, int h1,
-                       int d1, hipStream_t st);
 hipError_t launch_shadow(const UpdArgs& u, int ntiles, int ns, hipStream_t st);
+// header + M = init (head s % H), S = 0, and the bf16 copy, in one pass
+hipError_t launch_state_init(const UpdArgs& u, int ntiles, int ns, const float* init, int H, StateHeader* h,
+                             uint64_t hash, int batch, int heads, hipStream_t st);
 hipError_t launch_export(const float* M, const float* S, float* dst, long P, int ns, int d0, int h1,
                          int d1, hipStream_t st);
 hipError_t launch_import(float* M, float* S, const float* src, long P, int ns, int d0, int h1, int d1,

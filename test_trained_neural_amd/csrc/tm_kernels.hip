@@ -2,18 +2,25 @@
 //
 // Per chunk of b tokens and per memory stream (one memory per sequence and
 // head), the store is ("Titans, explained", steps 2-4 and 6; "Attack of the
-// Titans", Parallel training):
-//   1. forward of the keys through the chunk-start weights, with the queries
-//      of the previous chunk riding along as extra rows (both read the same
-//      weights),                                            -> gemm_kernel
-//   2. backward of ||M(k) - v||^2 to every hidden layer,    -> gemm_kernel
-//   3. the per-token gradients, weighted by coefficients of theta, eta and
-//      alpha, reduced over the chunk and folded into S and M in one pass over
-//      the state                                            -> update_kernel
-// The coefficients come from a wave-level scan over the gates of each chunk
-// (scan_kernel): the momentum is a linear recurrence and the forgetting a
-// running product, and unrolling both over a chunk whose gradients all sit at
-// the chunk-start weights gives
+// Titans", Parallel training): the forward of the keys through the
+// chunk-start weights (with the queries of the previous chunk riding along as
+// extra rows: both read the same weights), the backward of ||M(k) - v||^2 to
+// every hidden layer, and the per-token gradients, weighted by coefficients
+// of theta, eta and alpha, reduced over the chunk and folded into S and M in
+// one pass over the state.  Per chunk step c the kernels are
+//   first_layer_kernel  one workgroup per 16 hidden units j (per stream):
+//                       chunk c-1's backward to layer 0 for the units (in
+//                       place), the update of columns j of W_0 and rows j of
+//                       W_1, and chunk c's layer-0 forward; update tiles of
+//                       layers 2.. ride in the same launch (update_tile)
+//   gemm_kernel         layers 1.. of chunk c's forward (the last one's
+//                       epilogue gives y for the queries and Delta for the
+//                       keys) and, for depth >= 3, the backward to layer 1
+// and once per call scan_kernel (coefficients, packed operands).
+// The coefficients come from a wave-level scan over the gates of each chunk:
+// the momentum is a linear recurrence and the forgetting a running product,
+// and unrolling both over a chunk whose gradients all sit at the chunk-start
+// weights gives
 //     S_end = p_eta S_0 - sum_i d_i G_i,
 //     M_end = p_alpha M_0 + s0 S_0 - sum_i c_i G_i,
 // with A_i = prod_{j>i} (1 - alpha_j), E_i = prod_{j>i} eta_j,
@@ -856,21 +863,6 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
     if (__ballot(bad) != 0 && lane == 0 && live) atomicOr(u.flag, 1);
 }
 
-template <class OP>
-__global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
-    __shared__ float UM[64][65];
-    __shared__ float US[64][65];
-    update_tile<OP>(u, blockIdx.y, blockIdx.x, threadIdx.x, true, UM, US);
-}
-
-hipError_t launch_update(const UpdArgs& u, int ntiles, int ns, int f32, hipStream_t st) {
-    dim3 grid(ntiles, ns);
-    if (f32) hipLaunchKernelGGL(update_kernel<float>, grid, dim3(256), 0, st, u);
-    else hipLaunchKernelGGL(update_kernel<bf16>, grid, dim3(256), 0, st, u);
-    return hipGetLastError();
-}
-
-
 // ---------------------------------------------------------------------------
 // First-layer part of a chunk step (see FirstArgs).
 
@@ -1397,21 +1389,6 @@ hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <class OP>
-__global__ __launch_bounds__(256) void update_range_kernel(UpdArgs u, int tile0) {
-    __shared__ float UM[64][65];
-    __shared__ float US[64][65];
-    update_tile<OP>(u, blockIdx.y, tile0 + blockIdx.x, threadIdx.x, true, UM, US);
-}
-
-hipError_t launch_update_range(const UpdArgs& u, int tile0, int ntiles, int ns, int f32, hipStream_t st) {
-    if (ntiles <= 0) return hipSuccess;
-    dim3 grid(ntiles, ns);
-    if (f32) hipLaunchKernelGGL(update_range_kernel<float>, grid, dim3(256), 0, st, u, tile0);
-    else hipLaunchKernelGGL(update_range_kernel<bf16>, grid, dim3(256), 0, st, u, tile0);
-    return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // State set-up, bf16 copy, export / import.
 
@@ -1430,22 +1407,6 @@ __device__ __forceinline__ long state_pos(long p, int d0, int h1, int d1) {
         return p0 + cf1(j, n, d1 >> 4);
     }
     return p;
-}
-
-__global__ void init_kernel(float* M, float* S, const float* init, long P, int H, int ns, int d0, int h1,
-                            int d1) {
-    const long n = (long)ns * P;
-    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-        const long s = i / P, p = i - s * P;
-        M[s * P + state_pos(p, d0, h1, d1)] = init[(s % H) * P + p];
-        S[i] = 0.f;
-    }
-}
-
-hipError_t launch_init(float* M, float* S, const float* init, long P, int H, int ns, int d0, int h1, int d1,
-                       hipStream_t st) {
-    hipLaunchKernelGGL(init_kernel, dim3(2048), dim3(256), 0, st, M, S, init, P, H, ns, d0, h1, d1);
-    return hipGetLastError();
 }
 
 // Wt = bf16(M) packed [dout][din], per 64 x 64 tile (uses the layer / tile
@@ -1480,6 +1441,94 @@ __global__ __launch_bounds__(256) void shadow_kernel(UpdArgs u) {
             *reinterpret_cast<bf16x8*>(Wp + pkf((j0 >> 4) + jb, (i0 >> 5) + kk, din >> 5, ln)) = w;
         }
     }
+}
+
+// A fresh state in one pass: per 64 x 64 tile of one layer of one stream,
+// the canonical init weights (head s % H) are read once through LDS and
+// written to M in the layer's layout, to S as zeros and to the packed bf16
+// copy; block (0, 0) also writes the header.
+__global__ __launch_bounds__(256) void state_init_kernel(UpdArgs u, const float* init, int H, StateHeader* h,
+                                                         uint64_t hash, int batch, int heads) {
+    __shared__ float T[64][65];
+    const int tid = threadIdx.x;
+    const int s = blockIdx.y;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+        h->magic = STATE_MAGIC;
+        h->version = STATE_VERSION;
+        h->cfg_hash = hash;
+        h->batch = batch;
+        h->heads = heads;
+        h->nonfinite = 0;
+        h->reserved0 = 0;
+        h->position = 0;
+    }
+    int tile = blockIdx.x;
+    int l = 0;
+#pragma unroll
+    for (int q = 1; q < MAXL; ++q)
+        if (q < u.L && tile >= u.tbase[q]) l = q;
+    int tb = 0, tjn = 1, din = 32, dout = 32;
+    long off = 0;
+#pragma unroll
+    for (int q = 0; q < MAXL; ++q)
+        if (q == l) {
+            tb = u.tbase[q];
+            tjn = u.tj[q];
+            din = u.din[q];
+            dout = u.dout[q];
+            off = u.off[q];
+        }
+    tile -= tb;
+    const int ti = tile / tjn, tj = tile - ti * tjn;
+    const int i0 = ti * 64, j0 = tj * 64;
+    const float* src = init + (long)(s % H) * u.P + off;
+    for (int idx = tid; idx < 64 * 64; idx += 256) {
+        const int i = idx >> 6, j = idx & 63;
+        T[i][j] = (i0 + i < din && j0 + j < dout) ? src[(long)(i0 + i) * dout + j0 + j] : 0.f;
+    }
+    __syncthreads();
+    float* Mp = u.M + (long)s * u.P + off;
+    float* Sp = u.S + (long)s * u.P + off;
+    // 1024 float4 of the tile, each at 4 consecutive positions of the
+    // layer's layout: 4 rows of one column (layer 0), 4 outputs of one input
+    // (layer 1, and the row-major layers)
+    for (int k = tid; k < 1024; k += 256) {
+        int i, j;
+        f32x4 v;
+        long o;
+        if (l == 0) {
+            j = k & 63;
+            i = (k >> 6) * 4;
+            v = (f32x4){T[i][j], T[i + 1][j], T[i + 2][j], T[i + 3][j]};
+            o = cf0(i0 + i, j0 + j, din >> 4);
+        } else {
+            i = k & 63;
+            j = (k >> 6) * 4;
+            v = (f32x4){T[i][j], T[i][j + 1], T[i][j + 2], T[i][j + 3]};
+            o = l == 1 ? cf1(i0 + i, j0 + j, dout >> 4) : (long)(i0 + i) * dout + j0 + j;
+        }
+        if (i0 + i < din && j0 + j < dout) {
+            *reinterpret_cast<f32x4*>(Mp + o) = v;
+            *reinterpret_cast<f32x4*>(Sp + o) = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    bf16* Wp = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P + off;
+    for (int idx = tid; idx < 512; idx += 256) {
+        const int ln = idx & 63, kk = (idx >> 6) & 1, jb = idx >> 7;
+        const int jl = jb * 16 + (ln & 15), il = kk * 32 + 8 * (ln >> 4);
+        if (j0 + jl < dout && i0 + il < din) {
+            bf16x8 w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = (bf16)T[il + e][jl];
+            *reinterpret_cast<bf16x8*>(Wp + pkf((j0 >> 4) + jb, (i0 >> 5) + kk, din >> 5, ln)) = w;
+        }
+    }
+}
+
+hipError_t launch_state_init(const UpdArgs& u, int ntiles, int ns, const float* init, int H, StateHeader* h,
+                             uint64_t hash, int batch, int heads, hipStream_t st) {
+    hipLaunchKernelGGL(state_init_kernel, dim3(ntiles, ns), dim3(256), 0, st, u, init, H, h, hash, batch, heads);
+    return hipGetLastError();
 }
 
 hipError_t launch_shadow(const UpdArgs& u, int ntiles, int ns, hipStream_t st) {
