@@ -51,13 +51,14 @@ def kernel_source_hash():
 def first_layer_launches(wl, ns, T):
     """Bytes of every launch of the chunk-step kernel (chunk steps 0..C).
 
-    Step c updates W_0 for chunk c-1 (M_0, S_0 read and written in fp32, its
-    bf16 forward copy written; the keys of chunk c-1, layer 1's Delta and its
-    packed weight copy, SiLU' of chunk c-1 read) and runs chunk c's first-layer
-    forward of [queries of chunk c-1; keys of chunk c] (input rows read;
-    activations, SiLU' and the transposed activations written).  The same
-    launch carries chunk c-1's update tiles of layers 1..L-1
-    (update_launch_bytes)."""
+    Step c updates W_0 for chunk c-1 (M_0, S_0 read and written in fp32; its
+    bf16 forward copy written on the call's last update only; the keys of
+    chunk c-1, layer 1's Delta and SiLU' of chunk c-1 read; the in-place
+    backward's rows of W_1 are the ones the same launch updates, counted
+    there) and runs chunk c's first-layer forward of [queries of chunk c-1;
+    keys of chunk c] (input rows read; activations, SiLU' and the transposed
+    activations written).  The same launch carries chunk c-1's update of
+    layers 1..L-1 (update_launch_bytes)."""
     e = 2 if wl.dtype == "bf16" else 4
     b, d = wl.chunk, wl.dim
     dims = wl.layer_dims()
@@ -68,9 +69,11 @@ def first_layer_launches(wl, ns, T):
         upd, nq, nk = c >= 1, (b if c >= 1 else 0), (b if c < C else 0)
         x = 0
         if upd:
-            x += 18 * d * h1 + d * b * e + 8 * b
+            x += 16 * d * h1 + d * b * e + 8 * b
+            if c == C:
+                x += 2 * d * h1
             if wl.depth >= 2:
-                x += b * dims[1][1] * e + h1 * dims[1][1] * e + b * h1 * 4
+                x += b * dims[1][1] * e + b * h1 * 4
             else:
                 x += 2 * h1 * b * e
         else:
@@ -85,9 +88,9 @@ def first_layer_launches(wl, ns, T):
 
 
 def update_launch_bytes(wl, ns):
-    """Bytes of one launch of the update tiles of layers 1..L-1: M, S read and
-    written, the bf16 copy written, the transposed activations and the two
-    theta-weighted delta operands read, layer 1's packed copy written."""
+    """Bytes of chunk c-1's update of layers 1..L-1 in one step launch: M, S
+    read and written and the bf16 copy written (18 B per weight), the
+    transposed activations and the two theta-weighted delta operands read."""
     e = 2 if wl.dtype == "bf16" else 4
     b = wl.chunk
     x = 0
@@ -95,8 +98,6 @@ def update_launch_bytes(wl, ns):
         if l == 0:
             continue
         x += 18 * din * dout + din * b * e + 2 * dout * b * e
-        if l == 1:
-            x += din * dout * e
     return ns * x
 
 
@@ -148,6 +149,51 @@ def cpu_baseline(wl, params, ci, min_seconds=10.0):
                       "state), fp64 C oracle, one thread per stream, %.1f s" % (wl.name, reps, streams, tokens, dt)}
 
 
+def other_workload(name, steps, calls=None):
+    """Throughput of another workload (tokens/s): state init + its calls in
+    order, inputs resident in HBM, graph replay (each call's buffers repeat
+    across steps).  calls: how many of the workload's calls to run (a prefix
+    of the stream; None = all)."""
+    import torch
+    import test_trained_neural_amd as T
+    from test_trained_neural_amd import inputs as I
+    wl = I.WORKLOADS[name]
+    n_calls = wl.calls if calls is None else calls
+    Bn, Tn, H, d = wl.batch, wl.tokens_per_call, wl.heads, wl.dim
+    params = I.make_params(wl, 0)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    bufs = []
+    for j in range(n_calls):
+        ci = I.make_call(wl, params, j, 0)
+        bufs.append([torch.from_numpy(x).to(dev).to(tdt) for x in (ci.k, ci.v, ci.q)] +
+                    [torch.from_numpy(x).to(dev) for x in (ci.theta, ci.eta, ci.alpha)])
+    init = torch.from_numpy(params.init_weights).to(dev)
+    ctx = T.tm_create(d, wl.depth, wl.expansion, wl.chunk)
+    state = torch.empty(T.tm_state_bytes(ctx, Bn, H), dtype=torch.uint8, device=dev)
+    ws = torch.empty(T.tm_workspace_bytes(ctx, Bn, H, Tn), dtype=torch.uint8, device=dev)
+    y = torch.empty((Bn, Tn, H, d), dtype=torch.float32, device=dev)
+
+    def step():
+        T.tm_state_init(ctx, state, Bn, H, init)
+        for (k, v, q, th, et, al) in bufs:
+            T.tm_forward(ctx, state, k, v, q, th, et, al, y, ws)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    T.tm_destroy(ctx)
+    tokens = Bn * Tn * n_calls
+    return {"tokens_per_s": tokens / dt, "ms_per_step": dt * 1e3, "steps": steps,
+            "step": "tm_state_init + %d tm_forward calls of (%d, %d) tokens, %d heads" % (n_calls, Bn, Tn, H),
+            "sample": "whole workload" if n_calls == wl.calls else "first %d of %d calls" % (n_calls, wl.calls)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +201,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mlp384")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the other workloads' throughput")
     ap.add_argument("--calib-copy", action="store_true",
                     help="finish with a plain 256 MiB device copy (scale reference for HBM counters)")
     args = ap.parse_args()
@@ -290,6 +337,14 @@ def main():
         "kernels": kernels,
     }
 
+    if not args.no_other:
+        # the other workloads of the pages' shapes, a few steps each (context;
+        # the headline value is the workload above)
+        out["other_workloads"] = {
+            "mlp384_stream": other_workload("mlp384_stream", 3),
+            "multihead1024": other_workload("multihead1024", 3),
+            "deep512": other_workload("deep512", 2, calls=16),
+        }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, params, ci)
         out["cpu_baseline"]["gpu_over_cpu"] = out["value"] / out["cpu_baseline"]["value"]

@@ -65,8 +65,8 @@ StateLayout state_layout(const tm_ctx* c, long ns) {
 // sized in 4-byte elements so either operand type fits.
 struct WsLayout {
     size_t cc, dc, cs, act[MAXL], dsl[MAXL], dlp[MAXL], kt, xk, xq, ht[MAXL], dct[MAXL], ddt[MAXL], ht1[2],
-        wr[2], ret[2], total;
-    long coef_ss, cs_ss, act_ss, dsl_ss, dlp_ss[MAXL], kt_ss, x_ss, xc, ht_ss, dt_ss[MAXL], wr_ss, ret_ss, ret_rows;
+        ret[2], total;
+    long coef_ss, cs_ss, act_ss, dsl_ss, dlp_ss[MAXL], kt_ss, x_ss, xc, ht_ss, dt_ss[MAXL], ret_ss, ret_rows;
     int bp, C;
 };
 
@@ -113,15 +113,9 @@ WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
         w.ddt[l] = o; o += al256((size_t)ns * w.dt_ss[l] * 4);
     }
     // the first layer's transposed key-row activations, alternating between
-    // the chunk being written and the chunk being reduced; and two packed
-    // copies of layer 1's weights (chunk start of the chunk being reduced,
-    // and its result)
+    // the chunk being written and the chunk being reduced
     for (int i = 0; i < 2; ++i) {
         w.ht1[i] = o; o += al256((size_t)ns * w.ht_ss * 4);
-    }
-    w.wr_ss = c->L > 1 ? (long)c->din[1] * c->dout[1] : 0;
-    for (int i = 0; i < 2; ++i) {
-        w.wr[i] = o; o += al256((size_t)ns * w.wr_ss * 4);
     }
     size_t fwd_total = o;
     // retrieve: ping-pong activations of up to RET_ROWS query rows (packed)
@@ -467,7 +461,6 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     const size_t esz = f32 ? 4 : 2;
     WsLayout w = ws_layout(c, ns, n_tokens);
     TokLayout tl{n_tokens, heads, c->dim};
-    StateLayout sl = state_layout(c, ns);
 
     ScanArgs sa;
     memset(&sa, 0, sizeof(sa));
@@ -497,14 +490,6 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     sa.scan_blocks = (int)(((long)ns * C + 3) / 4);
     sa.tr_blocks = (int)(ns * C * ((c->dim + 63) / 64));
     sa.pack_blocks = (int)(ns * C * ((b + 15) / 16) * (q ? 2 : 1));
-    if (c->L >= 2) {
-        sa.w1_master = reinterpret_cast<const float*>(state + sl.M) + c->off[1];
-        sa.w1_copy = ws + w.wr[0];
-        sa.w1_ss = c->P;
-        sa.w1c_ss = w.wr_ss;
-        sa.w1_din = c->din[1];
-        sa.w1_dout = c->dout[1];
-    }
     if (timed(K_SCAN, st, [&] { return launch_scan(sa, st); }) != hipSuccess) return TM_ERR_HIP;
 
     FirstArgs a;
@@ -523,14 +508,12 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         a.u.ddt[l] = ws + w.ddt[l];
         a.u.dt_ss[l] = w.dt_ss[l];
     }
-    a.u.wr_ss = w.wr_ss;
     a.dim = c->dim;
     a.h1 = c->dout[0];
     a.nb1 = (a.h1 + JW - 1) / JW;
     a.kt_ss = w.kt_ss;
     a.dlt2_ss = c->L >= 2 ? w.dlp_ss[1] : 0;
     a.dlt2 = c->L >= 2 ? (const void*)(ws + w.dlp[1]) : nullptr;
-    a.wr_ss = w.wr_ss;
     a.dsl1 = c->L >= 2 ? reinterpret_cast<float*>(ws + w.dsl[0]) : nullptr;
     a.dsl1_ss = w.dsl_ss;
     a.coef_ss = w.coef_ss;
@@ -551,6 +534,7 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
 
     for (int ci = 0; ci <= C; ++ci) {
         a.do_update = ci >= 1;
+        a.last_update = ci == C;
         a.nq = (q && ci >= 1) ? b : 0;
         a.nk = ci < C ? b : 0;
         a.do_fwd = a.nq + a.nk > 0;
@@ -569,8 +553,6 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         a.cc_cur = reinterpret_cast<const float*>(ws + w.cc) + (ci < C ? ci : 0) * b;
         a.dc_cur = reinterpret_cast<const float*>(ws + w.dc) + (ci < C ? ci : 0) * b;
         if (c->L >= 2) {
-            a.wr_prev = ws + w.wr[(ci - 1) & 1];
-            a.u.wr_next = ws + w.wr[ci & 1];
             a.u.at[1] = ws + w.ht1[(ci - 1) & 1];
             a.ht1 = ws + w.ht1[ci & 1];
         }

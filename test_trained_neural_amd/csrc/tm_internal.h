@@ -151,8 +151,6 @@ struct UpdArgs {
     long cs_ss;
     int chunk;
     int* flag;
-    void* wr_next;            // if set: layer 1's new weights, operand type, packed [d_in][d_out]
-    long wr_ss;
 };
 
 // First-layer part of chunk step c, one launch (the update tiles of layers
@@ -160,13 +158,14 @@ struct UpdArgs {
 // hidden units j: columns j of W_0 (full height) and rows j of W_1:
 //   * if do_update: chunk c-1's update of those columns.  The first layer's
 //     Delta for the columns is formed in place (depth >= 2) from layer 1's
-//     Delta and the packed operand-type copy of layer 1's chunk-start
-//     weights, or read back (depth 1); theta-weighted, reduced against the
-//     chunk's keys and folded into M and S (and the bf16 copy of W_0);
+//     Delta and rows j of layer 1's weights (still at chunk c-1's start:
+//     this workgroup updates them later in the launch), or read back
+//     (depth 1); theta-weighted, reduced against the chunk's keys and folded
+//     into M and S (and, on the call's last update, the bf16 copy of W_0);
 //   * if do_fwd: chunk c's first-layer forward of [queries of chunk c-1;
 //     keys of chunk c] through the freshly written columns;
 //   * if do_update and depth >= 2: chunk c-1's update of rows j of W_1 (and
-//     of their bf16 copy and operand-type copy).
+//     of their bf16 copy).
 // K is split over the workgroup's 8 waves for the backward and the forward
 // products (partial tiles summed in LDS), so no wave walks a long chain of
 // dependent loads.
@@ -184,8 +183,7 @@ struct FirstArgs {
     long kt_ss;
     const void* dlt2;         // Delta of layer 1 for chunk c-1 (operand type), packed [b][dout1]
     long dlt2_ss;
-    const void* wr_prev;      // layer 1's weights at chunk c-1's start, packed [h1][dout1]
-    long wr_ss;
+    int last_update;          // the call's last update: also write W_0's bf16 copy
     float* dsl1;              // SiLU'(z) of layer 0: read (chunk c-1), then written (chunk c)
     long dsl1_ss;
     const float* cc_prev;     // coefficients of chunk c-1's tokens
@@ -212,8 +210,7 @@ struct FirstArgs {
 
 // Per call: the coefficient scan of every (stream, chunk); every chunk's
 // keys transposed (packed [d][bp] per chunk) and its key and query rows
-// packed ([b][d] per chunk); and the packed operand-type copy of layer 1's
-// weights.
+// packed ([b][d] per chunk).
 struct ScanArgs {
     const float* theta;
     const float* eta;
@@ -235,13 +232,8 @@ struct ScanArgs {
     void* xq;
     long xc;                  // elements of one chunk's packed rows
     int bp, kt_f32;
-    int scan_blocks;          // blocks [0, scan_blocks) scan, then transposes, packs, copy
+    int scan_blocks;          // blocks [0, scan_blocks) scan, then transposes, then packs
     int pack_blocks;
-    // refresh of the packed copy of layer 1's weights (depth >= 2)
-    const float* w1_master;   // M of layer 1 (row-major [din1][dout1]), stream stride w1_ss
-    void* w1_copy;            // operand type, packed [din1][dout1], stream stride w1c_ss
-    long w1_ss, w1c_ss;
-    int w1_din, w1_dout;
     int tr_blocks;
 };
 

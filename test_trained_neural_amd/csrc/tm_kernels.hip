@@ -54,6 +54,12 @@ __device__ __forceinline__ f32x8 ld8(const float* p) {
 __device__ __forceinline__ bf16x8 ld8(const bf16* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
+// 8 consecutive outputs of one input of W_1's accumulator-order master
+__device__ __forceinline__ f32x8 ld8w1(const float* p) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 64);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 __device__ __forceinline__ bf16x8 to_bf16(f32x8 v) {
     bf16x8 r;
@@ -561,42 +567,8 @@ __device__ void pack_rows(const ScanArgs& a, long blk) {
     }
 }
 
-// Layer 1's weights at the call start, in operand type and packed
-// [din1][dout1] (rows are layer 1's inputs, K runs over its outputs).
-template <class T>
-__device__ void copy_layer1(const ScanArgs& a, long blk) {
-    typedef typename Frag<T>::T V;
-    const int nks = a.w1_dout >> 5;
-    const long per = (long)(a.w1_din >> 4) * nks * 64;   // vectors per stream
-    for (long e = blk * 256 + threadIdx.x; e < per * a.ns; e += 1024L * 256) {
-        const long s = e / per, v = e - s * per;
-        const int ln = (int)(v & 63);
-        const long f = v >> 6;
-        const int ks = (int)(f % nks), rb = (int)(f / nks);
-        const int i = rb * 16 + (ln & 15), j = ks * 32 + 8 * (ln >> 4);
-        // outputs j .. j+3 and j+4 .. j+7 of input i: two float4 of layer 1's
-        // accumulator-order master, one 16-lane group apart
-        const float* m = a.w1_master + s * a.w1_ss + cf1(i, j, a.w1_dout >> 4);
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(m);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(m + 64);
-        V o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            o[q] = (T)lo[q];
-            o[q + 4] = (T)hi[q];
-        }
-        *reinterpret_cast<V*>(reinterpret_cast<T*>(a.w1_copy) + s * a.w1c_ss + (v << 3)) = o;
-    }
-}
-
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     const int x = (int)blockIdx.x;
-    if (x >= a.scan_blocks + a.tr_blocks + a.pack_blocks) {
-        const long blk = (long)x - a.scan_blocks - a.tr_blocks - a.pack_blocks;
-        if (a.kt_f32) copy_layer1<float>(a, blk);
-        else copy_layer1<bf16>(a, blk);
-        return;
-    }
     if (x >= a.scan_blocks + a.tr_blocks) {
         const long blk = (long)x - a.scan_blocks - a.tr_blocks;
         if (a.kt_f32) pack_rows<float>(a, blk);
@@ -661,8 +633,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
     long waves = (long)a.ns * a.C;
     if (waves == 0) return hipSuccess;
-    const long cp = a.w1_copy ? 1024 : 0;
-    dim3 grid((unsigned)(a.scan_blocks + a.tr_blocks + a.pack_blocks + cp));
+    dim3 grid((unsigned)(a.scan_blocks + a.tr_blocks + a.pack_blocks));
     hipLaunchKernelGGL(scan_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
@@ -845,21 +816,6 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
             *reinterpret_cast<bf16x8*>(Wp + pkf((j0 >> 4) + jb, (i0 >> 5) + kk, din >> 5, ln)) = w;
         }
     }
-    // layer 1's operand-type copy (packed [din][dout]) for the next chunk's
-    // in-place backward of the first layer
-    if (live && l == 1 && u.wr_next) {
-        OP* wr = reinterpret_cast<OP*>(u.wr_next) + (long)s * u.wr_ss;
-        for (int idx = tid; idx < 512; idx += 256) {
-            const int ln = idx & 63, kk = (idx >> 6) & 1, ib = idx >> 7;
-            const int il = ib * 16 + (ln & 15), jl = kk * 32 + 8 * (ln >> 4);
-            if (i0 + il < din && j0 + jl < dout) {
-                F w;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) w[e] = (OP)UM[il][jl + e];
-                st8<OP>(wr + pkf((i0 >> 4) + ib, (j0 >> 5) + kk, dout >> 5, ln), w);
-            }
-        }
-    }
     if (__ballot(bad) != 0 && lane == 0 && live) atomicOr(u.flag, 1);
 }
 
@@ -974,7 +930,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     const int nsA = BWD ? u.dout[1] >> 5 : 1, qA = (nsA + FW - 1) / FW;
     const int kbA = wave * qA, keA = min(nsA, kbA + qA), klA = max(keA - 1, 0);
     const OP* Ad[4];
-    const OP* Bw = nullptr;
+    const float* Bm = nullptr;
     bool tok[4];
     F ra[PA][4], rb[PA];
     if constexpr (BWD) {
@@ -984,13 +940,17 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             const int mb = 16 * m < b ? m : 0;   // token blocks past the chunk: valid address, dropped
             Ad[m] = reinterpret_cast<const OP*>(a.dlt2) + (long)s * a.dlt2_ss + pkf(mb, 0, nsA, lane);
         }
-        Bw = reinterpret_cast<const OP*>(a.wr_prev) + (long)s * a.wr_ss + pkf(j0 >> 4, 0, nsA, lane);
+        // W_1's rows j (this block's own, not yet updated in this launch) from
+        // the fp32 master in accumulator order: outputs n .. n+3 and
+        // n+4 .. n+7 of input j are two float4 one 16-lane group apart, and a
+        // K step (32 outputs) is two 16-column blocks further on
+        Bm = u.M + (long)s * u.P + u.off[1] + cf1(j, kofs, u.dout[1] >> 4);
 #pragma unroll
         for (int p = 0; p < PA; ++p) {
             const long k0 = (long)min(kbA + p, klA) << 9;
 #pragma unroll
             for (int m = 0; m < 4; ++m) ra[p][m] = cvt<OP>(ld8(Ad[m] + k0));
-            rb[p] = cvt<OP>(ld8(Bw + k0));
+            rb[p] = cvt<OP>(ld8w1(Bm + k0));
         }
     }
     // (2) the backward epilogue's SiLU' and coefficients (2 elements per thread)
@@ -1064,7 +1024,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     //     outputs n in 16-blocks nb = wave, wave + FW, ...; columns: the
     //     block's inputs j; K: tokens), so a lane's 4 results are outputs
     //     n .. n+3 of one input j: one float4 of M and S in their accumulator
-    //     order, 8 contiguous bytes of the packed operand-type copy.
+    //     order.
     constexpr bool W1 = UPD && DEEP;
     constexpr int PN = 3;                   // n-blocks per wave held in registers
     const int d1 = DEEP ? u.dout[1] : 16, ncb1 = d1 >> 4;
@@ -1116,11 +1076,9 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             *reinterpret_cast<f32x4*>(M1 + mso1(nb)) = mn;
             *reinterpret_cast<f32x4*>(S1 + mso1(nb)) = sn;
             const int n0 = nb * 16 + g4;   // outputs n0 .. n0+3 of input j
-            OP* wr = reinterpret_cast<OP*>(u.wr_next) + (long)s * u.wr_ss + pk(j, n0, d1 >> 5);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 bad |= !__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn[e]);
-                wr[e] = (OP)mn[e];
                 Wt1[pk(n0 + e, j, h1 >> 5)] = (bf16)mn[e];
             }
         }
@@ -1156,7 +1114,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
                 F av[4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) av[m] = cvt<OP>(ld8(Ad[m] + kn));
-                const F bv = cvt<OP>(ld8(Bw + kn));
+                const F bv = cvt<OP>(ld8w1(Bm + kn));
 #pragma unroll
                 for (int m = 0; m < 4; ++m) mma(acc[m], tok[m] ? av[m] : zero_frag<OP>(), bv);
             }
@@ -1222,10 +1180,15 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
                     bad |= !__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn[e]);
                     Wn[jl * WP + ib + g4 + e] = (OP)mn[e];
                 }
-                // 4 consecutive inputs of output j: 8 contiguous bytes of packed Wt
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                *reinterpret_cast<bf16x4*>(Wt0 + pk(j, ib + g4, d >> 5)) =
-                    (bf16x4){(bf16)mn[0], (bf16)mn[1], (bf16)mn[2], (bf16)mn[3]};
+                // W_0's bf16 copy is read only by the next call's first step
+                // and by retrieval (the forward here uses the columns in
+                // LDS): written on the call's last update only.  4
+                // consecutive inputs of output j: 8 contiguous bytes.
+                if (a.last_update) {
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    *reinterpret_cast<bf16x4*>(Wt0 + pk(j, ib + g4, d >> 5)) =
+                        (bf16x4){(bf16)mn[0], (bf16)mn[1], (bf16)mn[2], (bf16)mn[3]};
+                }
             }
         };
         // the prefetched row blocks, then (dim above 16 * FW * PB only) the
