@@ -104,6 +104,14 @@ __device__ __forceinline__ void mma(f32x4& c, f32x8 a, f32x8 b) {
 
 __device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// The new M and S of a chunk: stored non-temporally.  Each launch rewrites
+// the whole state and the next launch reads it from other XCDs, so it is
+// streamed out as it is produced rather than left dirty in the L2 (whose
+// write-back would otherwise be paid after the last workgroup).
+__device__ __forceinline__ void st_state(float* p, f32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
 // The chunk's momentum / forgetting write of one element, with explicit
 // fused multiply-adds, so that every kernel (and every instantiation of one)
 // rounds it the same way:  S' = p_eta S - U_S,  M' = p_alpha M + s0 S - U_M.
@@ -798,8 +806,8 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
                 bad |= !__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn[e]);
                 UM[i][j + e] = mn[e];
             }
-            *reinterpret_cast<f32x4*>(Mp + o) = mn;
-            *reinterpret_cast<f32x4*>(Sp + o) = sn;
+            st_state(Mp + o, mn);
+            st_state(Sp + o, sn);
         }
     }
     __syncthreads();
@@ -1073,8 +1081,8 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             mn[e] = mom_m(pa, m1r[p][e], s0, s1r[p][e], um[e]);
         }
         if (live) {   // wave-uniform
-            *reinterpret_cast<f32x4*>(M1 + mso1(nb)) = mn;
-            *reinterpret_cast<f32x4*>(S1 + mso1(nb)) = sn;
+            st_state(M1 + mso1(nb), mn);
+            st_state(S1 + mso1(nb), sn);
             const int n0 = nb * 16 + g4;   // outputs n0 .. n0+3 of input j
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1173,8 +1181,8 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
                 mn[e] = mom_m(pa, mr[p][e], s0, sr[p][e], um[e]);
             }
             if (live) {   // wave-uniform
-                *reinterpret_cast<f32x4*>(M0 + mso(rbk)) = mn;
-                *reinterpret_cast<f32x4*>(S0 + mso(rbk)) = sn;
+                st_state(M0 + mso(rbk), mn);
+                st_state(S0 + mso(rbk), sn);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     bad |= !__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn[e]);
@@ -1445,9 +1453,19 @@ __global__ __launch_bounds__(256) void state_init_kernel(UpdArgs u, const float*
     const int ti = tile / tjn, tj = tile - ti * tjn;
     const int i0 = ti * 64, j0 = tj * 64;
     const float* src = init + (long)(s % H) * u.P + off;
-    for (int idx = tid; idx < 64 * 64; idx += 256) {
-        const int i = idx >> 6, j = idx & 63;
-        T[i][j] = (i0 + i < din && j0 + j < dout) ? src[(long)(i0 + i) * dout + j0 + j] : 0.f;
+    f32x4 g[4];   // the tile's rows as float4 (dims are multiples of 32)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int idx = tid + 256 * q, i = idx >> 4, j = (idx & 15) * 4;
+        const bool in = i0 + i < din && j0 + j < dout;
+        g[q] = *reinterpret_cast<const f32x4*>(src + (in ? (long)(i0 + i) * dout + j0 + j : 0));
+        if (!in) g[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int idx = tid + 256 * q, i = idx >> 4, j = (idx & 15) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) T[i][j + e] = g[q][e];
     }
     __syncthreads();
     float* Mp = u.M + (long)s * u.P + off;
