@@ -138,6 +138,16 @@ const char* tm_status_str(tm_status status);
  * 16 most recent call shapes.  on = 0 launches every call directly. */
 tm_status tm_graphs_enable(int on);
 
+/* Placement of W_1's update for depth-2 memories; the results are bitwise
+ * identical either way (the same products, in the same order).  With
+ * on = 1 (the default), when the step launch leaves compute units free, W_1's
+ * update runs in workgroups of its own beside the first-layer blocks, and M_1
+ * alternates with a second buffer in the workspace over a call's updates; the
+ * state holds the final M_1 when the call ends.  on = 0 keeps it in the
+ * first-layer blocks, in place.  Process-wide; calls captured into graphs
+ * before a change keep the setting they were captured with. */
+tm_status tm_w1_split_enable(int on);
+
 /* Instrumentation for measuring kernels in place (not part of the method).
  * Kernel classes: 0 coefficient scan (and key transpose), 1 chunk forward
  * products of layers 1.., 2 chunk backward products, 3 gradient reduction +

@@ -24,7 +24,7 @@ TM_F32, TM_BF16 = 0, 1
 EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_workspace_bytes",
             "tm_state_init", "tm_store", "tm_retrieve", "tm_forward", "tm_state_export",
             "tm_state_import", "tm_state_check", "tm_status_str", "tm_timing_enable", "tm_timing_read",
-            "tm_graphs_enable")
+            "tm_graphs_enable", "tm_w1_split_enable")
 
 # kernel classes of tm_timing_enable / tm_timing_read
 K_SCAN, K_FWD, K_BWD, K_UPDATE, K_FIRST = 0, 1, 2, 3, 4
@@ -81,6 +81,8 @@ def lib():
         L.tm_timing_read.argtypes = [_i, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong)]
         L.tm_graphs_enable.restype = _i
         L.tm_graphs_enable.argtypes = [_i]
+        L.tm_w1_split_enable.restype = _i
+        L.tm_w1_split_enable.argtypes = [_i]
         L.tm_status_str.restype = ctypes.c_char_p
         L.tm_status_str.argtypes = [_i]
         _lib = L
@@ -192,6 +194,10 @@ def tm_state_check(ctx, state, batch, heads, stream=None):
 
 def tm_graphs_enable(on):
     _check("tm_graphs_enable", lib().tm_graphs_enable(1 if on else 0))
+
+
+def tm_w1_split_enable(on):
+    _check("tm_w1_split_enable", lib().tm_w1_split_enable(1 if on else 0))
 
 
 def tm_timing_enable(class_mask):

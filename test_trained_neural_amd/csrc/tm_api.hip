@@ -20,7 +20,7 @@ using namespace tmk;
 // A call's launch sequence replayed as a HIP graph: keyed by everything the
 // kernels' arguments depend on (device, every pointer and every size).
 struct GraphEntry {
-    int dev, kind, batch, heads, n_tokens, dtype;
+    int dev, kind, batch, heads, n_tokens, dtype, opt;
     const void* p[10];
     int seen;                    // sightings before capture
     hipGraphExec_t exec;
@@ -65,7 +65,7 @@ StateLayout state_layout(const tm_ctx* c, long ns) {
 // sized in 4-byte elements so either operand type fits.
 struct WsLayout {
     size_t cc, dc, cs, act[MAXL], dsl[MAXL], dlp[MAXL], kt, xk, xq, ht[MAXL], dct[MAXL], ddt[MAXL], ht1[2],
-        ret[2], total;
+        m1x, ret[2], total;
     long coef_ss, cs_ss, act_ss, dsl_ss, dlp_ss[MAXL], kt_ss, x_ss, xc, ht_ss, dt_ss[MAXL], ret_ss, ret_rows;
     int bp, C;
 };
@@ -117,6 +117,11 @@ WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
     for (int i = 0; i < 2; ++i) {
         w.ht1[i] = o; o += al256((size_t)ns * w.ht_ss * 4);
     }
+    // depth 2: W_1's M in the other buffer of an update in workgroups of
+    // its own (the state's layout, stream stride P_1)
+    if (c->L == 2) {
+        w.m1x = o; o += al256((size_t)ns * c->din[1] * c->dout[1] * 4);
+    }
     size_t fwd_total = o;
     // retrieve: ping-pong activations of up to RET_ROWS query rows (packed)
     w.ret_rows = T < RET_ROWS ? T : RET_ROWS;
@@ -139,6 +144,23 @@ uint64_t fnv(uint64_t h, uint64_t x) {
 }
 
 tm_status hip_status(hipError_t e) { return e == hipSuccess ? TM_OK : TM_ERR_HIP; }
+
+// compute units of the current device (queried once per device)
+hipError_t compute_units(int* out) {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> g(mu);
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (cache[dev] == 0) {
+        e = hipDeviceGetAttribute(&cache[dev], hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
+    *out = cache[dev];
+    return hipSuccess;
+}
 
 // ---- optional per-launch timing (tm_timing_enable / tm_timing_read) ----
 enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_UPD = 3, K_FIRST = 4, K_CLASSES = 5 };
@@ -192,6 +214,7 @@ hipError_t timed(int kind, hipStream_t st, F&& launch) {
 
 // ---- graph replay of repeated calls ----
 bool g_graphs = true;
+bool g_w1_split = true;   // tm_w1_split_enable
 constexpr size_t MAX_GRAPHS = 16;
 
 // Runs `launch(stream)`.  A call whose key has been seen before is captured
@@ -211,7 +234,8 @@ tm_status with_graph(const tm_ctx* cc, GraphEntry key, hipStream_t st, F&& launc
     GraphEntry* hit = nullptr;
     for (GraphEntry& e : *c->graphs) {
         if (e.dev == key.dev && e.kind == key.kind && e.batch == key.batch && e.heads == key.heads &&
-            e.n_tokens == key.n_tokens && e.dtype == key.dtype && memcmp(e.p, key.p, sizeof(key.p)) == 0) {
+            e.n_tokens == key.n_tokens && e.dtype == key.dtype && e.opt == key.opt &&
+            memcmp(e.p, key.p, sizeof(key.p)) == 0) {
             hit = &e;
             break;
         }
@@ -266,6 +290,7 @@ GraphEntry make_key(int kind, int batch, int heads, int n_tokens, int dtype,
     k.heads = heads;
     k.n_tokens = n_tokens;
     k.dtype = dtype;
+    k.opt = g_w1_split ? 1 : 0;
     int i = 0;
     for (const void* p : ptrs) k.p[i++] = p;
     return k;
@@ -316,6 +341,8 @@ struct FwdRows {
     int tk;
     const void* v;
     float* y;
+    const float* m1;   // fp32 path: layer 1's master if not the state's (stream stride m1_ss)
+    long m1_ss;
 };
 
 tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayout& w, char* ws,
@@ -355,6 +382,10 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
             g.b = state + sl.M + (size_t)c->off[l] * 4;
             g.b_ss = c->P;
             g.b_ld = c->dout[l];
+            if (l == 1 && fr.m1) {
+                g.b = fr.m1;
+                g.b_ss = fr.m1_ss;
+            }
         } else {
             g.bmode = B_PACKED;
             g.b = state + sl.Wt + (size_t)c->off[l] * 2;
@@ -531,6 +562,22 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     // update tiles in the same launch
     const int tile2 = c->tbase[c->L > 2 ? 2 : c->L];
     const int ntile_rest = c->tbase[c->L] - tile2;
+    // depth 2: W_1's update in workgroups of its own when every workgroup
+    // of the launch has a compute unit.  Those steps read M_1 from one buffer
+    // and write the other; the buffers alternate so that the call's last
+    // update writes the state's (with an odd number of updates, the first
+    // one runs in place in the first-layer blocks).
+    float* m1_state = c->L >= 2 ? a.u.M + c->off[1] : nullptr;
+    float* m1_ws = c->L == 2 ? reinterpret_cast<float*>(ws + w.m1x) : nullptr;
+    const long p1 = c->L >= 2 ? (long)c->din[1] * c->dout[1] : 0;
+    int nw1 = 0;
+    if (c->L == 2 && g_w1_split) {
+        // a multiple of 8 workgroups, W1_JPW row blocks each per XCD residue
+        const int n1 = 8 * (((a.nb1 + 7) / 8 + W1_JPW - 1) / W1_JPW);
+        int cus = 0;
+        if (compute_units(&cus) != hipSuccess) return TM_ERR_HIP;
+        if (ns * (a.nb1 + n1) <= cus) nw1 = n1;
+    }
 
     for (int ci = 0; ci <= C; ++ci) {
         a.do_update = ci >= 1;
@@ -561,10 +608,22 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         // the other layers (independent of each other)
         a.upd_tile0 = tile2;
         a.upd_ntiles = a.do_update ? ntile_rest : 0;
+        a.m1_rd = m1_state;
+        a.m1_wr = m1_state;
+        a.m1_rd_ss = a.m1_wr_ss = c->P;
+        a.nw1 = 0;
+        if (nw1 > 0 && a.do_update && (ci >= 2 || C % 2 == 0)) {
+            const bool to_ws = (C - ci + 1) % 2 == 0;   // updates left, this one included
+            a.nw1 = nw1;
+            a.m1_rd = to_ws ? m1_state : m1_ws;
+            a.m1_rd_ss = to_ws ? c->P : p1;
+            a.m1_wr = to_ws ? m1_ws : m1_state;
+            a.m1_wr_ss = to_ws ? p1 : c->P;
+        }
         if (timed(K_FIRST, st, [&] { return launch_first(a, (int)ns, f32 ? 1 : 0, st); }) != hipSuccess)
             return TM_ERR_HIP;
         if (a.do_fwd && c->L >= 2) {
-            FwdRows fr;
+            FwdRows fr{};
             fr.nq = a.nq;
             fr.q = q;
             fr.tq = a.tq0;
@@ -573,6 +632,8 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
             fr.tk = a.tk0;
             fr.v = v;
             fr.y = y;
+            fr.m1 = a.m1_wr;   // M_1 after this step's update (wherever it was written)
+            fr.m1_ss = a.m1_wr_ss;
             tm_status rc = run_forward_layers(c, state, ns, w, ws, tl, fr, f32, false, st, 1);
             if (rc != TM_OK) return rc;
         }
@@ -718,7 +779,7 @@ tm_status tm_retrieve(const tm_ctx* c, const void* state_v, const void* q, float
         WsLayout w = ws_layout(c, ns, n_tokens);
         TokLayout tl{n_tokens, heads, c->dim};
         for (long p0 = 0; p0 < n_tokens; p0 += w.ret_rows) {
-            FwdRows fr;
+            FwdRows fr{};
             fr.nq = (int)((n_tokens - p0) < w.ret_rows ? (n_tokens - p0) : w.ret_rows);
             fr.q = q;
             fr.tq = (int)p0;
@@ -780,6 +841,11 @@ tm_status tm_state_check(const tm_ctx* c, const void* state, int batch, int head
 
 tm_status tm_graphs_enable(int on) {
     g_graphs = on != 0;
+    return TM_OK;
+}
+
+tm_status tm_w1_split_enable(int on) {
+    g_w1_split = on != 0;
     return TM_OK;
 }
 

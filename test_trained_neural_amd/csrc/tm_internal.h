@@ -169,7 +169,15 @@ struct UpdArgs {
 // K is split over the workgroup's 8 waves for the backward and the forward
 // products (partial tiles summed in LDS), so no wave walks a long chain of
 // dependent loads.
+// Depth 2 with workgroups to spare: W_1's update moves to nw1 workgroups
+// per stream of its own (a multiple of 8), after the nb1 first-layer blocks,
+// each updating W1_JPW blocks of 16 rows.  They run beside the first-layer blocks, which
+// still read W_1's rows at chunk c-1's start for the backward, so M_1 is read
+// from m1_rd and its new value written to m1_wr, a second buffer (the two
+// alternate over a call's updates).  Otherwise m1_rd == m1_wr, the state's
+// own M_1, updated in place by the first-layer blocks.
 constexpr int JW = 16;
+constexpr int W1_JPW = 3;                // row blocks per W_1-update workgroup
 
 struct FirstArgs {
     UpdArgs u;                // layers, state, chunk scalars, flag
@@ -206,6 +214,13 @@ struct FirstArgs {
     void* dct1;               // (c Delta)^T, (d Delta)^T of layer 0, packed [h1][bp]
     void* ddt1;
     long dt1_ss;
+    // W_1 (depth >= 2): where its M is read and written (layer 1's first
+    // element of stream 0, and the stream stride)
+    const float* m1_rd;
+    long m1_rd_ss;
+    float* m1_wr;
+    long m1_wr_ss;
+    int nw1;                  // > 0: W_1's update in workgroups of its own
 };
 
 // Per call: the coefficient scan of every (stream, chunk); every chunk's

@@ -91,6 +91,16 @@ template <class OP> __device__ __forceinline__ typename Frag<OP>::T zero_frag() 
     return z;
 }
 
+// v where `on`, else zeros, by a bit mask the optimizer cannot see through:
+// written as `on ? v : 0`, the load behind v is moved into a branch on `on`
+// and issued late, behind a wait for every load before it.
+template <class F> __device__ __forceinline__ F keep_if(F v, bool on) {
+    typedef int IV __attribute__((ext_vector_type(sizeof(F) / 4)));
+    int m = on ? -1 : 0;
+    asm volatile("" : "+v"(m));
+    return __builtin_bit_cast(F, __builtin_bit_cast(IV, v) & m);
+}
+
 // C += A B over one 32-deep slice of K.  Each lane supplies 8 consecutive K
 // values of its A row and of its B column; A and B use the same K order, so
 // how the instruction maps register slots to K does not matter.
@@ -877,13 +887,125 @@ template <class OP> struct FirstDepth;
 template <> struct FirstDepth<bf16> { static constexpr int A = 2, B = 3, C = 2; };
 template <> struct FirstDepth<float> { static constexpr int A = 1, B = 2, C = 1; };
 
+// W_1's update as a workgroup role of its own (depth 2, with workgroups to
+// spare): workgroup wg of stream s updates W1_JPW row blocks of W_1 for
+// chunk c-1.  Workgroups go to the 8 XCDs round-robin by linear id, and a
+// row block is given to a workgroup on the XCD of the first-layer block that
+// reads those rows in the next launch, so that the rows are still in that
+// XCD's L2: block jb sits at x = jb and this workgroup at x = nb1 + wg of the
+// same grid row, so the row blocks jb = r, r + 8, ... with r = (nb1 + wg) mod 8
+// are the candidates, W1_JPW of them per workgroup of that residue (nw1 is
+// a multiple of 8).  Each block is computed transposed as in the first-layer
+// blocks, U^T = (c Delta_1)^T H_1 (rows: layer 1's outputs n in 16-blocks
+// nb = wave, wave + FW, ...; columns: the block's 16 inputs j; K: tokens).
+// The (c Delta_1)^T fragments depend on the outputs only, so a wave loads
+// them once for all its row blocks, and every row block's H_1 fragments and
+// M / S values are requested at once, before any is used.  M_1 is read from
+// m1_rd and written to m1_wr, never the buffer the first-layer blocks of the
+// same launch read.  Row blocks past h1 re-read the last one and are dropped.
+constexpr int W1_PN = 3;   // output blocks per wave held in registers
+
+template <class OP>
+__device__ void w1_rows(const FirstArgs& a, int s, int wg) {
+    typedef typename Frag<OP>::T F;
+    const UpdArgs& u = a.u;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kofs = 8 * (lane >> 4), g4 = 4 * (lane >> 4), jl = lane & 15;
+    const int b = u.b, nkb = u.bp >> 5, h1 = a.h1;
+    const int ncb1 = u.dout[1] >> 4;
+    const int mine1 = (ncb1 - wave + FW - 1) / FW;
+    const float* csp = u.cs + (long)s * u.cs_ss + (long)a.chunk_prev * 4;
+    const float pa = csp[0], pe = csp[1], s0 = csp[2];
+    const OP* at1 = reinterpret_cast<const OP*>(u.at[1]) + (long)s * u.at_ss[1];
+    const OP* dc1 = reinterpret_cast<const OP*>(u.dct[1]) + (long)s * u.dt_ss[1];
+    const OP* dd1 = reinterpret_cast<const OP*>(u.ddt[1]) + (long)s * u.dt_ss[1];
+    const float* Mr = a.m1_rd + (long)s * a.m1_rd_ss;
+    float* Mw = a.m1_wr + (long)s * a.m1_wr_ss;
+    float* S1 = u.S + (long)s * u.P + u.off[1];
+    bf16* Wt1 = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P + u.off[1];
+    const int xr = (a.nb1 + wg) & 7, jb0 = xr + 8 * W1_JPW * (wg >> 3);   // row blocks jb0 + 8q
+    bool bad = false;
+    auto mso1 = [&](int jb, int nb) { return ((long)(jb * ncb1 + nb) * 64 + lane) * 4; };
+    auto nbp = [&](int n) { return min(wave + FW * n, ncb1 - 1); };
+    auto load_cd = [&](F* cf, F* df, int nb) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int kc = min(ks, nkb - 1), t0 = ks * 32 + kofs;
+            const F vc = tok8<OP>(dc1 + pkf(nb, kc, nkb, lane), t0, b);   // padding tokens: zero
+            const F vd = tok8<OP>(dd1 + pkf(nb, kc, nkb, lane), t0, b);
+            cf[ks] = keep_if(vc, ks < nkb);
+            df[ks] = keep_if(vd, ks < nkb);
+        }
+    };
+    auto fold = [&](int jb, int nb, const F* cf, const F* df, const F* hf, f32x4 m, f32x4 sv, bool live) {
+        f32x4 um = (f32x4){0.f, 0.f, 0.f, 0.f}, us = um;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            mma(um, cf[ks], hf[ks]);
+            mma(us, df[ks], hf[ks]);
+        }
+        f32x4 mn, sn;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sn[e] = mom_s(pe, sv[e], us[e]);
+            mn[e] = mom_m(pa, m[e], s0, sv[e], um[e]);
+        }
+        if (live) {   // wave-uniform
+            st_state(Mw + mso1(jb, nb), mn);
+            st_state(S1 + mso1(jb, nb), sn);
+            const int n0 = nb * 16 + g4;   // outputs n0 .. n0+3 of input j
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bad |= !__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn[e]);
+                Wt1[pk(n0 + e, jb * 16 + jl, h1 >> 5)] = (bf16)mn[e];
+            }
+        }
+    };
+    // every load of the first two row blocks, in consumption order
+    F c1f[W1_PN][2], d1f[W1_PN][2];
+#pragma unroll
+    for (int p = 0; p < W1_PN; ++p) load_cd(c1f[p], d1f[p], nbp(p));
+    F hf[W1_JPW][2];
+    f32x4 mr[W1_JPW][W1_PN], sr[W1_JPW][W1_PN];
+    auto load_q = [&](int slot, int q) {
+        const int jb = min(jb0 + 8 * q, a.nb1 - 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) hf[slot][ks] = cvt<OP>(ld8(at1 + pkf(jb, min(ks, nkb - 1), nkb, lane)));
+#pragma unroll
+        for (int p = 0; p < W1_PN; ++p) {
+            mr[slot][p] = *reinterpret_cast<const f32x4*>(Mr + mso1(jb, nbp(p)));
+            sr[slot][p] = *reinterpret_cast<const f32x4*>(S1 + mso1(jb, nbp(p)));
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < W1_JPW; ++q) load_q(q, q);
+#pragma unroll
+    for (int q = 0; q < W1_JPW; ++q) {
+        const int slot = q, jb = min(jb0 + 8 * q, a.nb1 - 1);
+        const bool on = jb0 + 8 * q < a.nb1;
+#pragma unroll
+        for (int p = 0; p < W1_PN; ++p)
+            fold(jb, nbp(p), c1f[p], d1f[p], hf[slot], mr[slot][p], sr[slot][p], on && p < mine1);
+        for (int n = W1_PN; n < mine1; ++n) {   // layer 1 wider than 16 * FW * W1_PN outputs
+            F cf[2], df[2];
+            const int nb = nbp(n);
+            load_cd(cf, df, nb);
+            const f32x4 m = *reinterpret_cast<const f32x4*>(Mr + mso1(jb, nb));
+            const f32x4 sv = *reinterpret_cast<const f32x4*>(S1 + mso1(jb, nb));
+            fold(jb, nb, cf, df, hf[slot], m, sv, on);
+        }
+    }
+    if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
+}
+
 // UPD: chunk c-1's update runs (steps 1..C); FWD: chunk c's forward runs (a
-// step with rows to push); DEEP: depth >= 2.  The phases a launch runs are
+// step with rows to push); DEEP: depth >= 2; SPLIT: W_1's update runs in
+// workgroups of its own (w1_rows) instead of in the first-layer blocks.  The phases a launch runs are
 // compile-time, so every load of a phase is unconditional and issued at the
 // top in consumption order: a load whose only use sits behind a run-time
 // branch would be moved down to that use, and a branch or loop around a use
 // makes the compiler wait for every load in flight.
-template <class OP, bool UPD, bool FWD, bool DEEP>
+template <class OP, bool UPD, bool FWD, bool DEEP, bool SPLIT>
 __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     typedef typename Frag<OP>::T F;
     constexpr int PA = FirstDepth<OP>::A, PB = FirstDepth<OP>::B, PC = FirstDepth<OP>::C;
@@ -891,6 +1013,10 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     constexpr bool BWD = UPD && DEEP;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     if ((int)blockIdx.x >= a.nb1) {
+        if constexpr (SPLIT) {
+            w1_rows<OP>(a, blockIdx.y, (int)blockIdx.x - a.nb1);
+            return;
+        }
         // the other layers' update tiles of chunk c-1, two per workgroup
         // (threads 0..255 and 256..511, each half with its own LDS tiles);
         // they touch nothing the first-layer blocks read or write
@@ -948,11 +1074,11 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             const int mb = 16 * m < b ? m : 0;   // token blocks past the chunk: valid address, dropped
             Ad[m] = reinterpret_cast<const OP*>(a.dlt2) + (long)s * a.dlt2_ss + pkf(mb, 0, nsA, lane);
         }
-        // W_1's rows j (this block's own, not yet updated in this launch) from
-        // the fp32 master in accumulator order: outputs n .. n+3 and
+        // W_1's rows j at chunk c-1's start (not yet updated in this launch)
+        // from the fp32 master in accumulator order: outputs n .. n+3 and
         // n+4 .. n+7 of input j are two float4 one 16-lane group apart, and a
         // K step (32 outputs) is two 16-column blocks further on
-        Bm = u.M + (long)s * u.P + u.off[1] + cf1(j, kofs, u.dout[1] >> 4);
+        Bm = a.m1_rd + (long)s * a.m1_rd_ss + cf1(j, kofs, u.dout[1] >> 4);
 #pragma unroll
         for (int p = 0; p < PA; ++p) {
             const long k0 = (long)min(kbA + p, klA) << 9;
@@ -985,8 +1111,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
         const int rbk = min(wave + FW * n, nrb - 1);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const F v = cvt<OP>(ld8(kt + pkf(rbk, min(ks, nkb - 1), nkb, lane)));
-            kf[p][ks] = ks < nkb ? v : zero_frag<OP>();
+            kf[p][ks] = keep_if(cvt<OP>(ld8(kt + pkf(rbk, min(ks, nkb - 1), nkb, lane))), ks < nkb);
         }
         mr[p] = *reinterpret_cast<const f32x4*>(M0 + mso(rbk));
         sr[p] = *reinterpret_cast<const f32x4*>(S0 + mso(rbk));
@@ -1033,7 +1158,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     //     block's inputs j; K: tokens), so a lane's 4 results are outputs
     //     n .. n+3 of one input j: one float4 of M and S in their accumulator
     //     order.
-    constexpr bool W1 = UPD && DEEP;
+    constexpr bool W1 = UPD && DEEP && !SPLIT;
     constexpr int PN = 3;                   // n-blocks per wave held in registers
     const int d1 = DEEP ? u.dout[1] : 16, ncb1 = d1 >> 4;
     const int mine1 = (ncb1 - wave + FW - 1) / FW;
@@ -1042,7 +1167,8 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     const OP* at1 = DEEP ? reinterpret_cast<const OP*>(u.at[1]) + (long)s * u.at_ss[1] : nullptr;
     const OP* dc1 = DEEP ? reinterpret_cast<const OP*>(u.dct[1]) + (long)s * u.dt_ss[1] : nullptr;
     const OP* dd1 = DEEP ? reinterpret_cast<const OP*>(u.ddt[1]) + (long)s * u.dt_ss[1] : nullptr;
-    float* M1 = u.M + (long)s * u.P + (DEEP ? u.off[1] : 0);
+    const float* M1r = DEEP ? a.m1_rd + (long)s * a.m1_rd_ss : nullptr;
+    float* M1w = DEEP ? a.m1_wr + (long)s * a.m1_wr_ss : nullptr;
     float* S1 = u.S + (long)s * u.P + (DEEP ? u.off[1] : 0);
     auto mso1 = [&](int nb) { return ((long)(blockIdx.x * ncb1 + nb) * 64 + lane) * 4; };
     auto load_w1 = [&](int p, int n) {
@@ -1052,10 +1178,10 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             const int kc = min(ks, nkb - 1), t0 = ks * 32 + kofs;
             const F vc = tok8<OP>(dc1 + pkf(nb, kc, nkb, lane), t0, b);   // padding tokens: zero
             const F vd = tok8<OP>(dd1 + pkf(nb, kc, nkb, lane), t0, b);
-            c1f[p][ks] = ks < nkb ? vc : zero_frag<OP>();
-            d1f[p][ks] = ks < nkb ? vd : zero_frag<OP>();
+            c1f[p][ks] = keep_if(vc, ks < nkb);
+            d1f[p][ks] = keep_if(vd, ks < nkb);
         }
-        m1r[p] = *reinterpret_cast<const f32x4*>(M1 + mso1(nb));
+        m1r[p] = *reinterpret_cast<const f32x4*>(M1r + mso1(nb));
         s1r[p] = *reinterpret_cast<const f32x4*>(S1 + mso1(nb));
     };
     auto issue1 = [&]() {
@@ -1081,7 +1207,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             mn[e] = mom_m(pa, m1r[p][e], s0, s1r[p][e], um[e]);
         }
         if (live) {   // wave-uniform
-            st_state(M1 + mso1(nb), mn);
+            st_state(M1w + mso1(nb), mn);
             st_state(S1 + mso1(nb), sn);
             const int n0 = nb * 16 + g4;   // outputs n0 .. n0+3 of input j
 #pragma unroll
@@ -1113,7 +1239,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
             for (int m = 0; m < 4; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int p = 0; p < PA; ++p) {
-                const F bv = kbA + p < keA ? rb[p] : zero_frag<OP>();
+                const F bv = keep_if(rb[p], kbA + p < keA);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) mma(acc[m], tok[m] ? ra[p][m] : zero_frag<OP>(), bv);
             }
@@ -1338,8 +1464,16 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
 
 template <class OP, bool UPD, bool FWD>
 static void launch_first_as(const FirstArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-    if (a.u.L >= 2) hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, true>), grid, dim3(FW * 64), lds, st, a);
-    else hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, false>), grid, dim3(FW * 64), lds, st, a);
+    if constexpr (UPD) {
+        if (a.nw1 > 0) {
+            hipLaunchKernelGGL((first_layer_kernel<OP, true, FWD, true, true>), grid, dim3(FW * 64), lds, st, a);
+            return;
+        }
+    }
+    if (a.u.L >= 2)
+        hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, true, false>), grid, dim3(FW * 64), lds, st, a);
+    else
+        hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, false, false>), grid, dim3(FW * 64), lds, st, a);
 }
 
 template <class OP>
@@ -1351,8 +1485,11 @@ static void launch_first_op(const FirstArgs& a, dim3 grid, size_t lds, hipStream
 
 hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st) {
     if (!a.do_update && !a.do_fwd) return hipSuccess;
+    if (a.nw1 > 0 && (!a.do_update || a.u.L != 2 || a.upd_ntiles != 0 || a.nw1 % 8 != 0 ||
+                      (long)(a.nw1 / 8) * W1_JPW < (a.nb1 + 7) / 8 || a.m1_rd == a.m1_wr))
+        return hipErrorInvalidValue;
     const int pairs = (a.upd_ntiles + 1) / 2;
-    dim3 grid(a.nb1 + pairs, ns);
+    dim3 grid(a.nb1 + (a.nw1 > 0 ? a.nw1 : pairs), ns);
     size_t lds = first_lds_bytes(a.dim, a.u.bp, f32);
     if (pairs > 0 && lds < UPD_PAIR_LDS) lds = UPD_PAIR_LDS;
     if (f32) launch_first_op<float>(a, grid, lds, st);

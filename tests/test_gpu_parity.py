@@ -282,3 +282,44 @@ def test_graph_replay_matches_direct_launches():
     finally:
         T.tm_graphs_enable(True)
         g.close()
+
+
+# depth 2: W_1's update in workgroups of its own (M_1 alternating with a
+# workspace buffer) against the update in place in the first-layer blocks;
+# even and odd numbers of chunks per call, forward and store-only, fp32 and
+# bf16, and a second call carrying the state
+SPLIT_CASES = [
+    (small("w1s_even", 96, 2, 3, 24, 2, 1, 96, "f32"), (96,), "forward"),
+    (small("w1s_odd", 96, 2, 3, 24, 2, 1, 72, "f32"), (72,), "forward"),
+    (small("w1s_bf16", 64, 2, 2, 16, 1, 2, 80, "bf16"), (48, 32), "forward"),
+    (small("w1s_store", 64, 2, 2, 16, 2, 1, 80, "bf16"), (80, 48), "store"),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: c[0].name)
+def test_w1_split_matches_in_place(case):
+    import test_trained_neural_amd as T
+    wl, calls, mode = case
+    say("case", wl, calls, mode)
+    p = I.make_params(wl)
+    out = []
+    try:
+        for split in (True, False):
+            T.tm_w1_split_enable(split)
+            g = GpuMemory(wl, p)
+            ys = []
+            for j, n in enumerate(calls):
+                d = {k: v[:, :n].contiguous() for k, v in dev_inputs(I.make_call(wl, p, j), wl.dtype).items()}
+                if mode == "forward":
+                    ys.append(g.forward(d).cpu().numpy())
+                else:
+                    g.store(d)
+            out.append((ys, g.export(), g.check()))
+            g.close()
+    finally:
+        T.tm_w1_split_enable(True)
+    (ya, sa, ca), (yb, sb, cb) = out
+    assert ca == cb == (False, sum(calls))
+    assert np.array_equal(sa, sb)
+    for u, v in zip(ya, yb):
+        assert np.array_equal(u, v)
