@@ -114,12 +114,11 @@ __device__ __forceinline__ void mma(f32x4& c, f32x8 a, f32x8 b) {
 
 __device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
 
-// The new M and S of a chunk: stored non-temporally.  Each launch rewrites
-// the whole state and the next launch reads it from other XCDs, so it is
-// streamed out as it is produced rather than left dirty in the L2 (whose
-// write-back would otherwise be paid after the last workgroup).
+// The new M and S of a chunk (one float4 of the accumulator-order layout).
+// Plain stores: measured against non-temporal and write-through (sc1)
+// stores, which both made the chunk step slower.
 __device__ __forceinline__ void st_state(float* p, f32x4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+    *reinterpret_cast<f32x4*>(p) = v;
 }
 
 // The chunk's momentum / forgetting write of one element, with explicit
@@ -996,6 +995,12 @@ __device__ void w1_rows(const FirstArgs& a, int s, int wg) {
         }
     }
     if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
+    // The end of a launch writes every dirty L2 line back before the next
+    // launch starts, after the last workgroup.  This role ends well before
+    // the first-layer blocks, so one of its waves per XCD (workgroups 0..7 of
+    // stream 0 sit on the 8 XCDs) starts that write-back now, for the state
+    // written so far.  Only 8 waves: the write-back serialises chip-wide.
+    if (wg < 8 && s == 0 && wave == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 }
 
 // UPD: chunk c-1's update runs (steps 1..C); FWD: chunk c's forward runs (a
