@@ -112,7 +112,9 @@ __device__ __forceinline__ void mma(f32x4& c, f32x8 a, f32x8 b) {
     for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
+// sigma(z) = 1 / (1 + e^-z) with the hardware exponential and reciprocal
+// (each about 1 ulp): saturates to 0 and 1, propagates NaN
+__device__ __forceinline__ float sigmoid(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // The new M and S of a chunk (one float4 of the accumulator-order layout).
 // Plain stores: measured against non-temporal and write-through (sc1)
@@ -903,9 +905,10 @@ template <> struct FirstDepth<float> { static constexpr int A = 1, B = 2, C = 1;
 // m1_rd and written to m1_wr, never the buffer the first-layer blocks of the
 // same launch read.  Row blocks past h1 re-read the last one and are dropped.
 constexpr int W1_PN = 3;   // output blocks per wave held in registers
+constexpr size_t W1_LDS = (size_t)FW * 16 * W1_PN * 24 * 2;   // the waves' bf16 tiles
 
 template <class OP>
-__device__ void w1_rows(const FirstArgs& a, int s, int wg) {
+__device__ void w1_rows(const FirstArgs& a, int s, int wg, char* lds) {
     typedef typename Frag<OP>::T F;
     const UpdArgs& u = a.u;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -936,7 +939,13 @@ __device__ void w1_rows(const FirstArgs& a, int s, int wg) {
             df[ks] = keep_if(vd, ks < nkb);
         }
     };
-    auto fold = [&](int jb, int nb, const F* cf, const F* df, const F* hf, f32x4 m, f32x4 sv, bool live) {
+    // W_1's bf16 copy (packed: 8 consecutive inputs of one output per 16
+    // bytes) goes out through a tile of the wave in LDS, since a lane holds 4
+    // outputs of one input: 16 W1_PN rows (outputs) x 16 inputs per row block
+    constexpr int TR = 24;   // tile row pitch (elements): rows stay 16-byte aligned
+    bf16* tile = reinterpret_cast<bf16*>(lds) + wave * (16 * W1_PN * TR);
+    // p >= 0: the fold's copy into tile rows 16p.., else straight to memory
+    auto fold = [&](int jb, int nb, const F* cf, const F* df, const F* hf, f32x4 m, f32x4 sv, bool live, int p) {
         f32x4 um = (f32x4){0.f, 0.f, 0.f, 0.f}, us = um;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -949,6 +958,10 @@ __device__ void w1_rows(const FirstArgs& a, int s, int wg) {
             sn[e] = mom_s(pe, sv[e], us[e]);
             mn[e] = mom_m(pa, m[e], s0, sv[e], um[e]);
         }
+        if (p >= 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tile[(16 * p + g4 + e) * TR + jl] = (bf16)mn[e];
+        }
         if (live) {   // wave-uniform
             st_state(Mw + mso1(jb, nb), mn);
             st_state(S1 + mso1(jb, nb), sn);
@@ -956,7 +969,7 @@ __device__ void w1_rows(const FirstArgs& a, int s, int wg) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 bad |= !__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn[e]);
-                Wt1[pk(n0 + e, jb * 16 + jl, h1 >> 5)] = (bf16)mn[e];
+                if (p < 0) Wt1[pk(n0 + e, jb * 16 + jl, h1 >> 5)] = (bf16)mn[e];
             }
         }
     };
@@ -984,23 +997,25 @@ __device__ void w1_rows(const FirstArgs& a, int s, int wg) {
         const bool on = jb0 + 8 * q < a.nb1;
 #pragma unroll
         for (int p = 0; p < W1_PN; ++p)
-            fold(jb, nbp(p), c1f[p], d1f[p], hf[slot], mr[slot][p], sr[slot][p], on && p < mine1);
+            fold(jb, nbp(p), c1f[p], d1f[p], hf[slot], mr[slot][p], sr[slot][p], on && p < mine1, p);
+        // the tile's rows as whole 16-byte pieces (LDS operations of one wave
+        // complete in order: no barrier)
+        for (int c = lane; c < W1_PN * 32; c += 64) {
+            const int row = c >> 1, half = c & 1, p = row >> 4;
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(&tile[row * TR + 8 * half]);
+            if (on && p < mine1)
+                *reinterpret_cast<bf16x8*>(Wt1 + pk(nbp(p) * 16 + (row & 15), jb * 16 + 8 * half, h1 >> 5)) = v;
+        }
         for (int n = W1_PN; n < mine1; ++n) {   // layer 1 wider than 16 * FW * W1_PN outputs
             F cf[2], df[2];
             const int nb = nbp(n);
             load_cd(cf, df, nb);
             const f32x4 m = *reinterpret_cast<const f32x4*>(Mr + mso1(jb, nb));
             const f32x4 sv = *reinterpret_cast<const f32x4*>(S1 + mso1(jb, nb));
-            fold(jb, nb, cf, df, hf[slot], m, sv, on);
+            fold(jb, nb, cf, df, hf[slot], m, sv, on, -1);
         }
     }
     if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
-    // The end of a launch writes every dirty L2 line back before the next
-    // launch starts, after the last workgroup.  This role ends well before
-    // the first-layer blocks, so one of its waves per XCD (workgroups 0..7 of
-    // stream 0 sit on the 8 XCDs) starts that write-back now, for the state
-    // written so far.  Only 8 waves: the write-back serialises chip-wide.
-    if (wg < 8 && s == 0 && wave == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 }
 
 // UPD: chunk c-1's update runs (steps 1..C); FWD: chunk c's forward runs (a
@@ -1019,7 +1034,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     if ((int)blockIdx.x >= a.nb1) {
         if constexpr (SPLIT) {
-            w1_rows<OP>(a, blockIdx.y, (int)blockIdx.x - a.nb1);
+            w1_rows<OP>(a, blockIdx.y, (int)blockIdx.x - a.nb1, lds);
             return;
         }
         // the other layers' update tiles of chunk c-1, two per workgroup
@@ -1388,51 +1403,55 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
         issue1();   // layer 1's rows: operands now, the update after the epilogue
         partial_tiles<8>(red, acc, 8, 128, wave, lane, RP);
     }
-    // z of every (row, column): the partial tiles summed into slot 0
-    for (int idx = tid; idx < R * JW; idx += NT) {
-        const int r = idx / JW, cl = idx - r * JW;
-        float z = 0.f;
-#pragma unroll
-        for (int w = 0; w < FRED; ++w) z += red[(w * 128 + r) * RP + cl];
-        red[r * RP + cl] = z;
-    }
-    __syncthreads();
     if constexpr (DEEP) {
-        // activations (packed [rows][h1]) and, for key rows, SiLU'(z)
-        for (int idx = tid; idx < R * (JW / 8); idx += NT) {
-            const int r = idx / (JW / 8), c8 = (idx % (JW / 8)) * 8, jj = j0 + c8;
-            F hv;
-            float sd[8];
+        // z of every (row, column), summed from the partial tiles (slot
+        // order), 4 columns of one row per thread: the activations (packed
+        // [rows][h1]), SiLU'(z) of the key rows, and the key rows'
+        // activations transposed into LDS (the (c Delta_0)^T area, free since
+        // the update) for their packed [h1][bp] copy
+        typedef OP OP4 __attribute__((ext_vector_type(4)));
+        OP* hT = DcT;   // [JW][DP]
+        for (int idx = tid; idx < R * (JW / 4); idx += NT) {
+            const int r = idx / (JW / 4), c4 = (idx % (JW / 4)) * 4, jj = j0 + c4;
+            OP4 hv;
+            f32x4 sd;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float z = red[r * RP + c8 + e];
+            for (int e = 0; e < 4; ++e) {
+                float z = 0.f;
+#pragma unroll
+                for (int w = 0; w < FRED; ++w) z += red[(w * 128 + r) * RP + c4 + e];
                 const float sg = sigmoid(z);
                 hv[e] = (OP)(z * sg);
                 sd[e] = sg * (1.0f + z * (1.0f - sg));
             }
-            st8<OP>(reinterpret_cast<OP*>(a.act) + (long)s * a.act_ss + pk(r, jj, h1 >> 5), hv);
-            if (r >= a.nq) st8f(a.dsl1 + (long)s * a.dsl1_ss + (long)(r - a.nq) * h1 + jj, sd);
+            *reinterpret_cast<OP4*>(reinterpret_cast<OP*>(a.act) + (long)s * a.act_ss + pk(r, jj, h1 >> 5)) = hv;
+            if (r >= a.nq) {
+                *reinterpret_cast<f32x4*>(a.dsl1 + (long)s * a.dsl1_ss + (long)(r - a.nq) * h1 + jj) = sd;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hT[(c4 + e) * DP + r - a.nq] = hv[e];
+            }
         }
-        // the key rows' activations transposed (packed [h1][bp], zero past the chunk)
-        if (a.nk > 0) {
+        if (a.nk > 0) {   // uniform
+            __syncthreads();
             for (int idx = tid; idx < JW * (bp >> 3); idx += NT) {
                 const int cl = idx % JW, t8 = (idx / JW) * 8;
-                F hv;
+                F hv = *reinterpret_cast<const F*>(&hT[cl * DP + t8]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int t = t8 + e;
-                    float h = 0.f;
-                    if (t < a.nk) {
-                        const float z = red[(a.nq + t) * RP + cl];
-                        h = z * sigmoid(z);
-                    }
-                    hv[e] = (OP)h;
-                }
+                for (int e = 0; e < 8; ++e) hv[e] = t8 + e < a.nk ? hv[e] : (OP)0.0f;   // zero past the chunk
                 st8<OP>(reinterpret_cast<OP*>(a.ht1) + (long)s * a.ht_ss + pk(j0 + cl, t8, nkb), hv);
             }
         }
     } else {
-        // depth 1: the first layer is the output layer
+        // depth 1: the first layer is the output layer.  z of every (row,
+        // column): the partial tiles summed into slot 0
+        for (int idx = tid; idx < R * JW; idx += NT) {
+            const int r = idx / JW, cl = idx - r * JW;
+            float z = 0.f;
+#pragma unroll
+            for (int w = 0; w < FRED; ++w) z += red[(w * 128 + r) * RP + cl];
+            red[r * RP + cl] = z;
+        }
+        __syncthreads();
         for (int idx = tid; idx < a.nq * (JW / 8); idx += NT) {
             const int r = idx / (JW / 8), c8 = (idx % (JW / 8)) * 8;
             float z[8];
@@ -1497,6 +1516,7 @@ hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st) {
     dim3 grid(a.nb1 + (a.nw1 > 0 ? a.nw1 : pairs), ns);
     size_t lds = first_lds_bytes(a.dim, a.u.bp, f32);
     if (pairs > 0 && lds < UPD_PAIR_LDS) lds = UPD_PAIR_LDS;
+    if (a.nw1 > 0 && lds < W1_LDS) lds = W1_LDS;
     if (f32) launch_first_op<float>(a, grid, lds, st);
     else launch_first_op<bf16>(a, grid, lds, st);
     return hipGetLastError();
