@@ -562,8 +562,9 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     // update tiles in the same launch
     const int tile2 = c->tbase[c->L > 2 ? 2 : c->L];
     const int ntile_rest = c->tbase[c->L] - tile2;
-    // depth 2: W_1's update in workgroups of its own when every workgroup
-    // of the launch has a compute unit.  Those steps read M_1 from one buffer
+    // depth 2: W_1's update in workgroups of its own when they add no round
+    // of workgroups to the launch (one workgroup per compute unit: the
+    // first-layer blocks are register-bound).  Those steps read M_1 from one buffer
     // and write the other; the buffers alternate so that the call's last
     // update writes the state's (with an odd number of updates, the first
     // one runs in place in the first-layer blocks).
@@ -576,7 +577,7 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         const int n1 = 8 * (((a.nb1 + 7) / 8 + W1_JPW - 1) / W1_JPW);
         int cus = 0;
         if (compute_units(&cus) != hipSuccess) return TM_ERR_HIP;
-        if (ns * (a.nb1 + n1) <= cus) nw1 = n1;
+        if ((ns * (a.nb1 + n1) + cus - 1) / cus <= (ns * a.nb1 + cus - 1) / cus) nw1 = n1;
     }
 
     for (int ci = 0; ci <= C; ++ci) {
