@@ -884,9 +884,14 @@ __device__ __forceinline__ void partial_tiles(float* red, const f32x4* acc, int 
 // Prefetch depths (in K steps or row blocks) of the first-layer workgroup:
 // everything a wave needs is requested at kernel start when it fits the
 // register file, so each phase waits for at most one round of memory.
-template <class OP> struct FirstDepth;
-template <> struct FirstDepth<bf16> { static constexpr int A = 2, B = 3, C = 2; };
-template <> struct FirstDepth<float> { static constexpr int A = 1, B = 2, C = 1; };
+// SMALL (dim and layer 1's outputs at most 128): every wave has one K step
+// or row block per phase, so depth 1 everywhere and two workgroups per
+// compute unit (the register budget halves).
+template <class OP, bool SMALL> struct FirstDepth;
+template <> struct FirstDepth<bf16, false> { static constexpr int A = 2, B = 3, C = 2, N = 3; };
+template <> struct FirstDepth<float, false> { static constexpr int A = 1, B = 2, C = 1, N = 3; };
+template <class OP> struct FirstDepth<OP, true> { static constexpr int A = 1, B = 1, C = 1, N = 1; };
+constexpr int SMALL_DIM = 128;
 
 // W_1's update as a workgroup role of its own (depth 2, with workgroups to
 // spare): workgroup wg of stream s updates W1_JPW row blocks of W_1 for
@@ -1025,10 +1030,11 @@ __device__ void w1_rows(const FirstArgs& a, int s, int wg, char* lds) {
 // top in consumption order: a load whose only use sits behind a run-time
 // branch would be moved down to that use, and a branch or loop around a use
 // makes the compiler wait for every load in flight.
-template <class OP, bool UPD, bool FWD, bool DEEP, bool SPLIT>
-__global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
+template <class OP, bool UPD, bool FWD, bool DEEP, bool SPLIT, bool SMALL>
+__global__ __launch_bounds__(FW * 64) __attribute__((amdgpu_waves_per_eu(SMALL ? 4 : 1)))
+void first_layer_kernel(FirstArgs a) {
     typedef typename Frag<OP>::T F;
-    constexpr int PA = FirstDepth<OP>::A, PB = FirstDepth<OP>::B, PC = FirstDepth<OP>::C;
+    constexpr int PA = FirstDepth<OP, SMALL>::A, PB = FirstDepth<OP, SMALL>::B, PC = FirstDepth<OP, SMALL>::C;
     constexpr int NT = FW * 64;
     constexpr bool BWD = UPD && DEEP;
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -1179,7 +1185,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
     //     n .. n+3 of one input j: one float4 of M and S in their accumulator
     //     order.
     constexpr bool W1 = UPD && DEEP && !SPLIT;
-    constexpr int PN = 3;                   // n-blocks per wave held in registers
+    constexpr int PN = FirstDepth<OP, SMALL>::N;   // n-blocks per wave held in registers
     const int d1 = DEEP ? u.dout[1] : 16, ncb1 = d1 >> 4;
     const int mine1 = (ncb1 - wave + FW - 1) / FW;
     F h1f[2], c1f[PN][2], d1f[PN][2];
@@ -1241,6 +1247,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
         if constexpr (W1) {
 #pragma unroll
             for (int p = 0; p < PN; ++p) update1(p, p, p < mine1);
+            if constexpr (!SMALL)   // (SMALL: one output block per wave)
             for (int n = PN; n < mine1; ++n) {
                 load_w1(0, n);
                 update1(0, n, true);
@@ -1263,6 +1270,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) mma(acc[m], tok[m] ? ra[p][m] : zero_frag<OP>(), bv);
             }
+            if constexpr (!SMALL)   // (SMALL: one K step per wave)
             for (int k = kbA + PA; k < keA; ++k) {
                 const long kn = (long)k << 9;
                 F av[4];
@@ -1349,6 +1357,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
         // rest, each loaded and used
 #pragma unroll
         for (int p = 0; p < PB; ++p) update_rb(p, p, p < mineB);
+        if constexpr (!SMALL)   // (SMALL: one row block per wave)
         for (int n = PB; n < mineB; ++n) {
             load_rb(0, n);
             update_rb(0, n, true);
@@ -1392,6 +1401,7 @@ __global__ __launch_bounds__(FW * 64) void first_layer_kernel(FirstArgs a) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) mma(acc[m], rok[m] ? rx[p][m] : zero_frag<OP>(), bv);
         }
+        if constexpr (!SMALL)   // (SMALL: one K step per wave)
         for (int k = kbC + PC; k < keC; ++k) {
             F xv[8];
 #pragma unroll
@@ -1490,14 +1500,25 @@ template <class OP, bool UPD, bool FWD>
 static void launch_first_as(const FirstArgs& a, dim3 grid, size_t lds, hipStream_t st) {
     if constexpr (UPD) {
         if (a.nw1 > 0) {
-            hipLaunchKernelGGL((first_layer_kernel<OP, true, FWD, true, true>), grid, dim3(FW * 64), lds, st, a);
+            hipLaunchKernelGGL((first_layer_kernel<OP, true, FWD, true, true, false>), grid, dim3(FW * 64), lds, st, a);
+            return;
+        }
+    }
+    // (the fp32 operand set does not fit half the register file)
+    const bool small = sizeof(OP) == 2 && a.dim <= SMALL_DIM && (a.u.L < 2 || a.u.dout[1] <= SMALL_DIM);
+    if constexpr (sizeof(OP) == 2) {
+        if (small) {
+            if (a.u.L >= 2)
+                hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, true, false, true>), grid, dim3(FW * 64), lds, st, a);
+            else
+                hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, false, false, true>), grid, dim3(FW * 64), lds, st, a);
             return;
         }
     }
     if (a.u.L >= 2)
-        hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, true, false>), grid, dim3(FW * 64), lds, st, a);
+        hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, true, false, false>), grid, dim3(FW * 64), lds, st, a);
     else
-        hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, false, false>), grid, dim3(FW * 64), lds, st, a);
+        hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, false, false, false>), grid, dim3(FW * 64), lds, st, a);
 }
 
 template <class OP>
