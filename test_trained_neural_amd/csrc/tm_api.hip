@@ -518,9 +518,6 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     sa.xc = w.xc;
     sa.bp = w.bp;
     sa.kt_f32 = f32 ? 1 : 0;
-    sa.scan_blocks = (int)(((long)ns * C + 3) / 4);
-    sa.tr_blocks = (int)(ns * C * ((c->dim + 63) / 64));
-    sa.pack_blocks = (int)(ns * C * ((b + 15) / 16) * (q ? 2 : 1));
     if (timed(K_SCAN, st, [&] { return launch_scan(sa, st); }) != hipSuccess) return TM_ERR_HIP;
 
     FirstArgs a;

@@ -158,10 +158,11 @@ struct UpdArgs {
 // hidden units j: columns j of W_0 (full height) and rows j of W_1:
 //   * if do_update: chunk c-1's update of those columns.  The first layer's
 //     Delta for the columns is formed in place (depth >= 2) from layer 1's
-//     Delta and rows j of layer 1's weights (still at chunk c-1's start:
-//     this workgroup updates them later in the launch), or read back
-//     (depth 1); theta-weighted, reduced against the chunk's keys and folded
-//     into M and S (and, on the call's last update, the bf16 copy of W_0);
+//     Delta and rows j of layer 1's weights (at chunk c-1's start: their
+//     update in this launch comes later or goes to the other buffer), or
+//     read back (depth 1); theta-weighted, reduced against the chunk's keys
+//     and folded into M and S (and, on the call's last update, the bf16 copy
+//     of W_0);
 //   * if do_fwd: chunk c's first-layer forward of [queries of chunk c-1;
 //     keys of chunk c] through the freshly written columns;
 //   * if do_update and depth >= 2: chunk c-1's update of rows j of W_1 (and
@@ -247,9 +248,6 @@ struct ScanArgs {
     void* xq;
     long xc;                  // elements of one chunk's packed rows
     int bp, kt_f32;
-    int scan_blocks;          // blocks [0, scan_blocks) scan, then transposes, then packs
-    int pack_blocks;
-    int tr_blocks;
 };
 
 // ---- launchers (tm_kernels.hip) ----

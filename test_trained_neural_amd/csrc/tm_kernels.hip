@@ -527,85 +527,10 @@ hipError_t launch_bwd(const GemmArgs& g, int ns, int f32, hipStream_t st) {
 
 __device__ __forceinline__ float shdown(float x, int off) { return __shfl_down(x, off, 64); }
 
-// Keys of one chunk, 64 features at a time, transposed through LDS into
-// kt[s][chunk] (packed [d][bp]: rows are features, K runs over the chunk's
-// tokens, zero past the chunk).
-template <class T>
-__device__ void transpose_keys(const ScanArgs& a, long blk) {
-    typedef typename Frag<T>::T V;
-    __shared__ float tile[64][65];
-    const int d = a.ktl.d, ib = (d + 63) / 64;
-    const int s = (int)(blk / ((long)a.C * ib));
-    const long rem = blk - (long)s * a.C * ib;
-    const int c = (int)(rem / ib), i0 = (int)(rem - (long)c * ib) * 64;
-    const int tid = threadIdx.x;
-    const T* k = reinterpret_cast<const T*>(a.k);
-    for (int idx = tid; idx < 64 * 64; idx += 256) {
-        const int t = idx >> 6, i = idx & 63;
-        tile[t][i] = (t < a.b && i0 + i < d) ? (float)k[tok_off(a.ktl, s, c * a.b + t) + i0 + i] : 0.f;
-    }
-    __syncthreads();
-    const int nkb = a.bp >> 5;
-    T* kt = reinterpret_cast<T*>(a.kt) + ((long)s * a.C + c) * (long)d * a.bp;
-    for (int idx = tid; idx < 4 * nkb * 64; idx += 256) {
-        const int ln = idx & 63, ks = (idx >> 6) % nkb, rb = (idx >> 6) / nkb;
-        const int i = rb * 16 + (ln & 15), t8 = ks * 32 + 8 * (ln >> 4);
-        if (i0 + i >= d) continue;
-        V v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (T)tile[t8 + e][i];
-        *reinterpret_cast<V*>(kt + pkf((i0 >> 4) + rb, ks, nkb, ln)) = v;
-    }
-}
-
-// One 16-token block of one chunk's keys or queries, packed ([b][d] per
-// chunk: rows are tokens, K runs over the features; zero past the chunk).
-template <class T>
-__device__ void pack_rows(const ScanArgs& a, long blk) {
-    typedef typename Frag<T>::T V;
-    const int d = a.ktl.d, nbt = (a.b + 15) >> 4, nks = d >> 5;
-    const int nkq = a.q ? 2 : 1;
-    const int kq = (int)(blk % nkq);
-    blk /= nkq;
-    const int tb = (int)(blk % nbt);
-    blk /= nbt;
-    const int c = (int)(blk % a.C), s = (int)(blk / a.C);
-    const T* src = reinterpret_cast<const T*>(kq ? a.q : a.k);
-    T* dst = reinterpret_cast<T*>(kq ? a.xq : a.xk) + ((long)s * a.C + c) * a.xc;
-    for (int idx = threadIdx.x; idx < nks * 64; idx += 256) {
-        const int ln = idx & 63, ks = idx >> 6;
-        const int t = tb * 16 + (ln & 15), i = ks * 32 + 8 * (ln >> 4);
-        V v;
-        if (t < a.b) {
-            v = ld8(src + tok_off(a.ktl, s, c * a.b + t) + i);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (T)0.0f;
-        }
-        *reinterpret_cast<V*>(dst + pkf(tb, ks, nks, ln)) = v;
-    }
-}
-
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
-    const int x = (int)blockIdx.x;
-    if (x >= a.scan_blocks + a.tr_blocks) {
-        const long blk = (long)x - a.scan_blocks - a.tr_blocks;
-        if (a.kt_f32) pack_rows<float>(a, blk);
-        else pack_rows<bf16>(a, blk);
-        return;
-    }
-    if (x >= a.scan_blocks) {
-        const long blk = (long)x - a.scan_blocks;
-        if (a.kt_f32) transpose_keys<float>(a, blk);
-        else transpose_keys<bf16>(a, blk);
-        return;
-    }
-
+// The chunk's coefficients, one wave, lane i = token i (idle lanes past the
+// chunk contribute the identity).
+__device__ void scan_gates(const ScanArgs& a, int s, int c) {
     const int lane = threadIdx.x & 63;
-    if (blockIdx.x == 0 && threadIdx.x == 0 && a.position) *a.position += a.add;
-    const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (w >= (long)a.ns * a.C) return;
-    const int s = (int)(w / a.C), c = (int)(w - (long)s * a.C);
     const int b = a.b;
     const bool on = lane < b;
     const int t = c * b + lane;
@@ -649,11 +574,78 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     }
 }
 
+// One workgroup per (stream, chunk, slice of SCAN_SLICE features): the
+// slice's key and query rows of the chunk packed ([b][d] per chunk: rows are
+// tokens, K runs over the features), its keys also transposed through LDS
+// ([d][bp] per chunk: rows are features, K runs over the chunk's tokens), and
+// in slice 0 the chunk's coefficients.  Every row is read once, 8 features
+// (16 or 32 bytes) per lane; tokens past the chunk are zero.
+constexpr int SCAN_SLICE = 128;
+
+constexpr int SCAN_TP = SCAN_SLICE + 8;   // tile row pitch (elements)
+
+template <class T>
+__device__ void scan_rows(const ScanArgs& a, int s, int c, int f0, char* lds) {
+    typedef typename Frag<T>::T V;
+    T(*tile)[SCAN_TP] = reinterpret_cast<T(*)[SCAN_TP]>(lds);   // [token][feature of the slice]
+    const int d = a.ktl.d, b = a.b, nks = d >> 5, nkb = a.bp >> 5;
+    const int nf = min(SCAN_SLICE, d - f0), nbt = (b + 15) >> 4;
+    const int items = nbt * (nf >> 5) * 64;   // 16 B pieces per tensor (fragment order)
+    for (int kq = 0; kq < (a.q ? 2 : 1); ++kq) {
+        const T* src = reinterpret_cast<const T*>(kq ? a.q : a.k);
+        T* dst = reinterpret_cast<T*>(kq ? a.xq : a.xk) + ((long)s * a.C + c) * a.xc;
+        for (int idx = threadIdx.x; idx < items; idx += 256) {
+            const int ln = idx & 63, f = idx >> 6, ksl = f % (nf >> 5), tb = f / (nf >> 5);
+            const int t = tb * 16 + (ln & 15), fl = ksl * 32 + 8 * (ln >> 4);
+            V v;
+            if (t < b) {
+                v = ld8(src + tok_off(a.ktl, s, c * b + t) + f0 + fl);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (T)0.0f;
+            }
+            *reinterpret_cast<V*>(dst + pkf(tb, (f0 >> 5) + ksl, nks, ln)) = v;
+            if (kq == 0 && t < MAX_CHUNK) *reinterpret_cast<V*>(&tile[t][fl]) = v;
+        }
+    }
+    // rows of the tile past the packed ones (tokens up to bp) are zero
+    for (int idx = threadIdx.x; idx < (a.bp - nbt * 16) * (nf >> 3); idx += 256) {
+        const int t = nbt * 16 + idx / (nf >> 3), fl = (idx % (nf >> 3)) * 8;
+        V z;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = (T)0.0f;
+        *reinterpret_cast<V*>(&tile[t][fl]) = z;
+    }
+    __syncthreads();
+    T* kt = reinterpret_cast<T*>(a.kt) + ((long)s * a.C + c) * (long)d * a.bp;
+    for (int idx = threadIdx.x; idx < (nf >> 4) * nkb * 64; idx += 256) {
+        const int ln = idx & 63, ks = (idx >> 6) % nkb, rb = (idx >> 6) / nkb;
+        const int i = rb * 16 + (ln & 15), t8 = ks * 32 + 8 * (ln >> 4);
+        V v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = tile[t8 + e][i];
+        *reinterpret_cast<V*>(kt + pkf((f0 >> 4) + rb, ks, nkb, ln)) = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+    const int nsl = (a.ktl.d + SCAN_SLICE - 1) / SCAN_SLICE;
+    const long x = blockIdx.x;
+    const int sl = (int)(x % nsl);
+    const long sc = x / nsl;
+    const int c = (int)(sc % a.C), s = (int)(sc / a.C);
+    if (x == 0 && threadIdx.x == 0 && a.position) *a.position += a.add;
+    if (sl == 0 && threadIdx.x < 64) scan_gates(a, s, c);
+    __shared__ __attribute__((aligned(16))) char lds[MAX_CHUNK * SCAN_TP * 4];
+    if (a.kt_f32) scan_rows<float>(a, s, c, sl * SCAN_SLICE, lds);
+    else scan_rows<bf16>(a, s, c, sl * SCAN_SLICE, lds);
+}
+
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
-    long waves = (long)a.ns * a.C;
-    if (waves == 0) return hipSuccess;
-    dim3 grid((unsigned)(a.scan_blocks + a.tr_blocks + a.pack_blocks));
-    hipLaunchKernelGGL(scan_kernel, grid, dim3(256), 0, st, a);
+    const long blocks = (long)a.ns * a.C * ((a.ktl.d + SCAN_SLICE - 1) / SCAN_SLICE);
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffL || a.b > MAX_CHUNK || a.bp > MAX_CHUNK || a.ktl.d % 32 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
