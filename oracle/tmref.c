@@ -26,7 +26,10 @@
  *    still run token by token; this file never uses a closed form for them.
  *  - Retrieval y = M(q) is a forward pass with no write (step 5).  In a
  *    combined store+retrieve call the queries of chunk c are read through the
- *    weights after chunk c has been written.
+ *    weights after chunk c has been written (read mode 0), or, the variant in
+ *    which the queries read the memory before the chunk writes to it ("Attack
+ *    of the Titans", the memory-as-context architecture), through the weights
+ *    chunk c started with (read mode 1).
  *
  * Everything is fp64.  Inputs arrive as float32 arrays (bf16 inputs are passed
  * already widened, which is exact) and are widened to double on use.
@@ -179,6 +182,7 @@ typedef struct {
     double* state;
     double* y;            /* NULL: store only */
     int retrieve_only;
+    int read;                 /* 0: queries after the chunk's write; 1: before */
     int tid, nthreads;
     int err;
 } job_t;
@@ -223,6 +227,15 @@ static void* run_streams(void* arg) {
             /* weights at the start of the chunk: every gradient of the chunk
              * is taken here */
             memcpy(M0, M, sizeof(double) * (size_t)P);
+            if (J->y && J->read == 1) {
+                /* read the chunk's queries before the chunk writes */
+                for (int t = c0; t < c0 + b; t++) {
+                    size_t row = ((size_t)bi * T + t) * H + hi;
+                    widen(kk, J->q + row * d, d);
+                    mlp_row_forward(m, M, kk, act, pre, out);
+                    memcpy(J->y + row * d, out, sizeof(double) * d);
+                }
+            }
             for (int t = c0; t < c0 + b; t++) {
                 size_t row = ((size_t)bi * T + t) * H + hi;
                 widen(kk, J->k + row * d, d);
@@ -232,7 +245,7 @@ static void* run_streams(void* arg) {
                 for (long p = 0; p < P; p++) S[p] = et * S[p] - th * G[p];
                 for (long p = 0; p < P; p++) M[p] = (1.0 - al) * M[p] + S[p];
             }
-            if (J->y) {
+            if (J->y && J->read == 0) {
                 /* read the chunk's queries through the freshly written memory */
                 for (int t = c0; t < c0 + b; t++) {
                     size_t row = ((size_t)bi * T + t) * H + hi;
@@ -252,7 +265,7 @@ done:
 static int run(int dim, int depth, int expansion, int chunk, int batch, int heads,
                int n_tokens, const float* k, const float* v, const float* q,
                const float* theta, const float* eta, const float* alpha,
-               double* state, double* y, int retrieve_only, int n_threads) {
+               double* state, double* y, int retrieve_only, int read, int n_threads) {
     mlp_t m;
     if (mlp_setup(&m, dim, depth, expansion)) return -1;
     if (batch <= 0 || heads <= 0 || n_tokens < 0 || chunk <= 0) return -1;
@@ -265,7 +278,7 @@ static int run(int dim, int depth, int expansion, int chunk, int batch, int head
     if (!jobs || !th) { free(jobs); free(th); return -2; }
     for (int i = 0; i < n_threads; i++) {
         job_t J = {&m, chunk, batch, heads, n_tokens, k, v, q, theta, eta, alpha,
-                   state, y, retrieve_only, i, n_threads, 0};
+                   state, y, retrieve_only, read, i, n_threads, 0};
         jobs[i] = J;
     }
     for (int i = 1; i < n_threads; i++) pthread_create(&th[i], NULL, run_streams, &jobs[i]);
@@ -278,16 +291,26 @@ static int run(int dim, int depth, int expansion, int chunk, int batch, int head
 }
 
 /* Store the call's n_tokens into the memory (and, if y != NULL, read the
- * queries chunk by chunk through the written memory).  state is updated in
- * place.  Returns 0, -1 (bad sizes), -2 (out of memory), -3 (n_tokens not a
- * multiple of chunk). */
+ * queries chunk by chunk: read = 0 through the memory after the chunk's
+ * write, read = 1 through the memory the chunk started with).  state is
+ * updated in place.  Returns 0, -1 (bad sizes or mode), -2 (out of memory),
+ * -3 (n_tokens not a multiple of chunk). */
+int tmref_forward_read(int dim, int depth, int expansion, int chunk, int batch, int heads,
+                       int n_tokens, const float* k, const float* v, const float* q,
+                       const float* theta, const float* eta, const float* alpha,
+                       double* state, double* y, int read, int n_threads) {
+    if (y && !q) return -1;
+    if (read != 0 && read != 1) return -1;
+    return run(dim, depth, expansion, chunk, batch, heads, n_tokens, k, v, q,
+               theta, eta, alpha, state, y, 0, read, n_threads);
+}
+
 int tmref_forward(int dim, int depth, int expansion, int chunk, int batch, int heads,
                   int n_tokens, const float* k, const float* v, const float* q,
                   const float* theta, const float* eta, const float* alpha,
                   double* state, double* y, int n_threads) {
-    if (y && !q) return -1;
-    return run(dim, depth, expansion, chunk, batch, heads, n_tokens, k, v, q,
-               theta, eta, alpha, state, y, 0, n_threads);
+    return tmref_forward_read(dim, depth, expansion, chunk, batch, heads, n_tokens, k, v, q,
+                              theta, eta, alpha, state, y, 0, n_threads);
 }
 
 /* Read only: y = M(q) for every query, the state untouched. */
@@ -295,5 +318,5 @@ int tmref_retrieve(int dim, int depth, int expansion, int batch, int heads,
                    int n_tokens, const double* state, const float* q, double* y,
                    int n_threads) {
     return run(dim, depth, expansion, 1, batch, heads, n_tokens, NULL, NULL, q,
-               NULL, NULL, NULL, (double*)state, y, 1, n_threads);
+               NULL, NULL, NULL, (double*)state, y, 1, 0, n_threads);
 }

@@ -42,6 +42,7 @@ def lib():
         L.tmref_mlp_forward.argtypes = [ctypes.c_int] * 3 + [_dp, _dp, _dp]
         L.tmref_mlp_grad.argtypes = [ctypes.c_int] * 3 + [_dp, _dp, _dp, _dp, _dp]
         L.tmref_forward.argtypes = ([ctypes.c_int] * 7 + [_fp] * 6 + [_dp, _dp, ctypes.c_int])
+        L.tmref_forward_read.argtypes = ([ctypes.c_int] * 7 + [_fp] * 6 + [_dp, _dp, ctypes.c_int, ctypes.c_int])
         L.tmref_retrieve.argtypes = ([ctypes.c_int] * 6 + [_dp, _fp, _dp, ctypes.c_int])
         _lib = L
     return _lib
@@ -85,11 +86,16 @@ def mlp_grad(dim, depth, expansion, W, k, v):
     return G, float(loss[0])
 
 
+READ_MODES = {"after": 0, "before": 1}
+
+
 def forward(dim, depth, expansion, chunk, state, k, v, theta, eta, alpha, q=None,
-            n_threads=None):
+            n_threads=None, read="after"):
     """Store the call's tokens into ``state`` (fp64 [streams][2P], updated in
-    place); if ``q`` is given also return y [B][T][H][d] read chunk by chunk
-    through the freshly written memory.  k, v, q: [B][T][H][d]; gates [B][T][H]."""
+    place); if ``q`` is given also return y [B][T][H][d] read chunk by chunk,
+    through the memory after the chunk's write (read="after") or the memory
+    the chunk started with (read="before").  k, v, q: [B][T][H][d]; gates
+    [B][T][H]."""
     k, v, q = _f32(k), _f32(v), _f32(q)
     theta, eta, alpha = _f32(theta), _f32(eta), _f32(alpha)
     B, T, H, d = k.shape
@@ -97,9 +103,9 @@ def forward(dim, depth, expansion, chunk, state, k, v, theta, eta, alpha, q=None
     assert state.shape == (B * H, 2 * param_count(dim, depth, expansion))
     y = np.zeros((B, T, H, d), np.float64) if q is not None else None
     nt = n_threads or min(os.cpu_count() or 1, B * H)
-    rc = lib().tmref_forward(dim, depth, expansion, chunk, B, H, T, _f(k), _f(v), _f(q),
-                             _f(theta), _f(eta), _f(alpha), _d(state),
-                             _d(y) if y is not None else None, nt)
+    rc = lib().tmref_forward_read(dim, depth, expansion, chunk, B, H, T, _f(k), _f(v), _f(q),
+                                  _f(theta), _f(eta), _f(alpha), _d(state),
+                                  _d(y) if y is not None else None, READ_MODES[read], nt)
     if rc != 0:
         raise ValueError("tmref_forward failed: %d" % rc)
     return y

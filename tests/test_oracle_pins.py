@@ -354,6 +354,64 @@ def test_retrieval_reads_the_freshly_written_memory():
     assert np.array_equal(st, st2)
 
 
+def test_read_before_write_linear_closed_form():
+    # the queries read the memory before their chunk writes (the
+    # memory-as-context order).  Linear memory from W_0 = 0 with eta = alpha =
+    # 0: every gradient of chunk 1 is taken at W = 0, -2 k^T v, so after it
+    # W_1 = sum_t theta_t 2 k_t^T v_t; chunk 1's queries read W_0 (zeros),
+    # chunk 2's read W_1: y = q W_1 = sum_t 2 theta_t (q . k_t) v_t.  Read
+    # after the write, chunk 1's queries would see W_1 instead.
+    rng = np.random.default_rng(21)
+    d, b = 4, 3
+    k, v, q, (th, _, _) = rand_inputs(rng, 1, 2 * b, 1, d)
+    zeros = np.zeros_like(th)
+    st = np.zeros((1, 2 * d * d))
+    y = tmref.forward(d, 1, 1, b, st, k, v, th, zeros, zeros, q=q, read="before")
+    assert np.array_equal(y[0, :b], np.zeros((b, 1, d)))
+    K = k[0, :b, 0].astype(np.float64)
+    V = v[0, :b, 0].astype(np.float64)
+    t1 = th[0, :b, 0].astype(np.float64)
+    W1 = (2.0 * t1[:, None] * K).T @ V
+    for t in range(b, 2 * b):
+        np.testing.assert_allclose(y[0, t, 0], q[0, t, 0].astype(np.float64) @ W1, rtol=1e-12, atol=1e-14)
+    st_a = np.zeros((1, 2 * d * d))
+    y_a = tmref.forward(d, 1, 1, b, st_a, k, v, th, zeros, zeros, q=q, read="after")
+    np.testing.assert_allclose(y_a[0, :b, 0], q[0, :b, 0].astype(np.float64) @ W1, rtol=1e-12, atol=1e-14)
+    assert np.array_equal(st, st_a)   # the read order changes no write
+
+
+def test_read_before_write_sees_the_chunk_start_weights():
+    # read before the write: chunk c's queries equal a read-only retrieve
+    # on the memory after chunks 1..c-1 (the first chunk's on the initial
+    # memory, checked against torch), and without writes (theta = alpha = 0,
+    # S_0 = 0) both read orders agree exactly
+    rng = np.random.default_rng(22)
+    d, ex, depth, b, T = 4, 2, 2, 4, 16
+    dims = dims_of(d, depth, ex)
+    P = tmref.param_count(d, depth, ex)
+    k, v, q, (th, et, al) = rand_inputs(rng, 2, T, 1, d)
+    st0 = rand_state(rng, 2, P, 0.5, 0.1)
+    st = st0.copy()
+    y = tmref.forward(d, depth, ex, b, st, k, v, th, et, al, q=q, read="before")
+    for bi in range(2):
+        for t in range(b):
+            np.testing.assert_allclose(y[bi, t, 0], torch_fwd(st0[bi, :P], q[bi, t, 0].astype(np.float64), dims),
+                                       rtol=1e-12, atol=1e-13)
+    st2 = st0.copy()
+    for c0 in range(0, T, b):
+        s = slice(c0, c0 + b)
+        y2 = tmref.retrieve(d, depth, ex, st2, q[:, s])
+        assert np.array_equal(y[:, s], y2)
+        tmref.forward(d, depth, ex, b, st2, k[:, s], v[:, s], th[:, s], et[:, s], al[:, s])
+    assert np.array_equal(st, st2)
+    z = np.zeros_like(th)
+    sa = rand_state(rng, 2, P, 0.5, 0.0)
+    sb = sa.copy()
+    ya = tmref.forward(d, depth, ex, b, sa, k, v, z, et, z, q=q, read="after")
+    yb = tmref.forward(d, depth, ex, b, sb, k, v, z, et, z, q=q, read="before")
+    assert np.array_equal(ya, yb)
+
+
 def test_retrieve_is_read_only_and_is_a_forward_pass():
     rng = np.random.default_rng(12)
     d, ex, depth = 5, 2, 3
