@@ -149,11 +149,12 @@ def cpu_baseline(wl, params, ci, min_seconds=10.0):
                       "state), fp64 C oracle, one thread per stream, %.1f s" % (wl.name, reps, streams, tokens, dt)}
 
 
-def other_workload(name, steps, calls=None):
+def other_workload(name, steps, calls=None, read=None):
     """Throughput of another workload (tokens/s): state init + its calls in
     order, inputs resident in HBM, graph replay (each call's buffers repeat
     across steps).  calls: how many of the workload's calls to run (a prefix
-    of the stream; None = all)."""
+    of the stream; None = all).  read: the queries' read order
+    (tm_forward_ex), None for tm_forward."""
     import torch
     import test_trained_neural_amd as T
     from test_trained_neural_amd import inputs as I
@@ -177,7 +178,10 @@ def other_workload(name, steps, calls=None):
     def step():
         T.tm_state_init(ctx, state, Bn, H, init)
         for (k, v, q, th, et, al) in bufs:
-            T.tm_forward(ctx, state, k, v, q, th, et, al, y, ws)
+            if read is None:
+                T.tm_forward(ctx, state, k, v, q, th, et, al, y, ws)
+            else:
+                T.tm_forward_ex(ctx, state, k, v, q, th, et, al, y, ws, read)
 
     for _ in range(2):
         step()
@@ -190,7 +194,8 @@ def other_workload(name, steps, calls=None):
     T.tm_destroy(ctx)
     tokens = Bn * Tn * n_calls
     return {"tokens_per_s": tokens / dt, "ms_per_step": dt * 1e3, "steps": steps,
-            "step": "tm_state_init + %d tm_forward calls of (%d, %d) tokens, %d heads" % (n_calls, Bn, Tn, H),
+            "step": "tm_state_init + %d %s calls of (%d, %d) tokens, %d heads" % (
+                n_calls, "tm_forward" if read is None else "tm_forward_ex(read=%d)" % read, Bn, Tn, H),
             "sample": "whole workload" if n_calls == wl.calls else "first %d of %d calls" % (n_calls, wl.calls)}
 
 
@@ -344,6 +349,8 @@ def main():
             "mlp384_stream": other_workload("mlp384_stream", 3),
             "multihead1024": other_workload("multihead1024", 3),
             "deep512": other_workload("deep512", 2, calls=16),
+            # the same step with each chunk's queries read before its write
+            "mlp384_read_before_write": other_workload("mlp384", 20, read=1),
         }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, params, ci)

@@ -61,6 +61,12 @@ typedef enum {
 
 typedef enum { TM_F32 = 0, TM_BF16 = 1 } tm_dtype;
 
+/* When a chunk's queries read the memory in tm_forward_ex. */
+typedef enum {
+    TM_READ_AFTER_WRITE = 0,   /* through the memory after the chunk's write (tm_forward) */
+    TM_READ_BEFORE_WRITE = 1   /* through the memory the chunk started with */
+} tm_read;
+
 typedef struct tm_ctx tm_ctx;
 
 /* Memory configuration.  dim: per-head width, a multiple of 32, 32..1024;
@@ -111,6 +117,20 @@ tm_status tm_forward(const tm_ctx* ctx, void* state, const void* k, const void* 
                      const void* q, const float* theta, const float* eta,
                      const float* alpha, float* y, int batch, int heads,
                      int n_tokens, tm_dtype dtype, void* workspace, void* stream);
+
+/* tm_forward with the read order chosen.  TM_READ_BEFORE_WRITE: for each
+ * chunk c, chunk c's queries read the memory chunk c started with, then chunk
+ * c is stored (the memory-as-context order: "Attack of the Titans", memory as
+ * a context, and "Titans, explained" step 8, where a segment's tokens query
+ * the memory before it is updated).  Equivalent to alternating tm_retrieve
+ * and tm_store chunk by chunk; the state it leaves is bitwise that of
+ * tm_forward.  An unknown read value gives TM_ERR_INVALID; everything else as
+ * for tm_forward. */
+tm_status tm_forward_ex(const tm_ctx* ctx, void* state, const void* k, const void* v,
+                        const void* q, const float* theta, const float* eta,
+                        const float* alpha, float* y, int batch, int heads,
+                        int n_tokens, tm_dtype dtype, tm_read read, void* workspace,
+                        void* stream);
 
 /* Canonical fp32 copy of the state: dst is [batch*heads][2P], per stream
  * M_1..M_L then S_1..S_L, each W_l row-major [d_in][d_out]. */

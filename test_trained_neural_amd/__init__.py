@@ -20,11 +20,12 @@ LIB_PATH = os.path.join(HERE, "libtm.so")
 
 TM_OK, TM_ERR_INVALID, TM_ERR_SHAPE, TM_ERR_DTYPE, TM_ERR_STATE, TM_ERR_HIP = 0, -1, -2, -3, -4, -5
 TM_F32, TM_BF16 = 0, 1
+TM_READ_AFTER_WRITE, TM_READ_BEFORE_WRITE = 0, 1
 
 EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_workspace_bytes",
             "tm_state_init", "tm_store", "tm_retrieve", "tm_forward", "tm_state_export",
             "tm_state_import", "tm_state_check", "tm_status_str", "tm_timing_enable", "tm_timing_read",
-            "tm_graphs_enable", "tm_w1_split_enable")
+            "tm_graphs_enable", "tm_w1_split_enable", "tm_forward_ex")
 
 # kernel classes of tm_timing_enable / tm_timing_read
 K_SCAN, K_FWD, K_BWD, K_UPDATE, K_FIRST = 0, 1, 2, 3, 4
@@ -68,6 +69,8 @@ def lib():
         L.tm_retrieve.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
         L.tm_forward.restype = _i
         L.tm_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
+        L.tm_forward_ex.restype = _i
+        L.tm_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
         L.tm_state_export.restype = _i
         L.tm_state_export.argtypes = [_vp, _vp, _i, _i, _vp, _vp]
         L.tm_state_import.restype = _i
@@ -174,6 +177,15 @@ def tm_forward(ctx, state, k, v, q, theta, eta, alpha, y, workspace, stream=None
                                           _ptr(workspace), _stream(stream)))
 
 
+def tm_forward_ex(ctx, state, k, v, q, theta, eta, alpha, y, workspace, read, stream=None):
+    """read: TM_READ_AFTER_WRITE (as tm_forward) or TM_READ_BEFORE_WRITE."""
+    _tok(k, v, q, theta, eta, alpha, y)
+    B, T, H, _ = k.shape
+    _check("tm_forward_ex", lib().tm_forward_ex(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(q), _ptr(theta),
+                                                _ptr(eta), _ptr(alpha), _ptr(y), B, H, T, _dtype_code(k),
+                                                int(read), _ptr(workspace), _stream(stream)))
+
+
 def tm_state_export(ctx, state, batch, heads, dst, stream=None):
     _check("tm_state_export", lib().tm_state_export(ctx, _ptr(state), batch, heads, _ptr(dst),
                                                     _stream(stream)))
@@ -262,10 +274,12 @@ class NeuralMemory:
         tm_retrieve(self.ctx, state.buf, q, y, self.workspace(B, H, T))
         return y
 
-    def __call__(self, state, k, v, q, theta, eta, alpha):
+    def __call__(self, state, k, v, q, theta, eta, alpha, read=TM_READ_AFTER_WRITE):
+        """Store + retrieve; read: when each chunk's queries read the memory
+        (TM_READ_AFTER_WRITE, the default, or TM_READ_BEFORE_WRITE)."""
         B, T, H, d = k.shape
         y = torch.empty((B, T, H, d), dtype=torch.float32, device=self.device)
-        tm_forward(self.ctx, state.buf, k, v, q, theta, eta, alpha, y, self.workspace(B, H, T))
+        tm_forward_ex(self.ctx, state.buf, k, v, q, theta, eta, alpha, y, self.workspace(B, H, T), read)
         return y, state
 
     def export(self, state):

@@ -483,7 +483,8 @@ tm_status run_backward(const tm_ctx* c, char* state, long ns, const WsLayout& w,
 // the backward down to layer 1.  Step C only finishes chunk C-1.
 tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v, const void* q,
                     const float* theta, const float* eta, const float* alpha, float* y, int batch,
-                    int heads, int n_tokens, tm_dtype dtype, void* ws_v, hipStream_t st) {
+                    int heads, int n_tokens, tm_dtype dtype, void* ws_v, hipStream_t st,
+                    bool read_before = false) {
     char* state = static_cast<char*>(state_v);
     char* ws = static_cast<char*>(ws_v);
     const long ns = (long)batch * heads;
@@ -578,19 +579,24 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     }
 
     for (int ci = 0; ci <= C; ++ci) {
+        // queries: chunk ci-1's through the memory after its write (rows of
+        // step ci), or chunk ci's through the memory before its write (the
+        // same rows as chunk ci's keys)
+        const int cq = read_before ? ci : ci - 1;
+        const bool has_q = q && cq >= 0 && cq < C;
         a.do_update = ci >= 1;
         a.last_update = ci == C;
-        a.nq = (q && ci >= 1) ? b : 0;
+        a.nq = has_q ? b : 0;
         a.nk = ci < C ? b : 0;
         a.do_fwd = a.nq + a.nk > 0;
         a.chunk_prev = ci - 1;
         a.u.chunk = ci - 1;
-        a.tq0 = (ci - 1) * b;
+        a.tq0 = cq * b;
         a.tk0 = ci * b;
         // steps that skip a part still get valid addresses for its operands
         // (the step kernel loads them unconditionally and drops the values)
         const int cprev = ci >= 1 ? ci - 1 : 0;
-        a.xq = (q && ci >= 1) ? ws + w.xq + (size_t)(ci - 1) * w.xc * esz : nullptr;
+        a.xq = has_q ? ws + w.xq + (size_t)cq * w.xc * esz : nullptr;
         a.xk = ws + w.xk + (size_t)(ci < C ? ci : 0) * w.xc * esz;
         a.kt_prev = ws + w.kt + (size_t)cprev * c->dim * w.bp * esz;
         a.cc_prev = reinterpret_cast<const float*>(ws + w.cc) + cprev * b;
@@ -747,20 +753,31 @@ tm_status tm_store(const tm_ctx* c, void* state, const void* k, const void* v, c
     });
 }
 
-tm_status tm_forward(const tm_ctx* c, void* state, const void* k, const void* v, const void* q,
-                     const float* theta, const float* eta, const float* alpha, float* y, int batch,
-                     int heads, int n_tokens, tm_dtype dtype, void* ws, void* stream) {
+tm_status tm_forward_ex(const tm_ctx* c, void* state, const void* k, const void* v, const void* q,
+                        const float* theta, const float* eta, const float* alpha, float* y, int batch,
+                        int heads, int n_tokens, tm_dtype dtype, tm_read read, void* ws, void* stream) {
     tm_status rc = check_common(c, state, batch, heads, n_tokens, dtype, ws);
     if (rc != TM_OK) return rc;
+    if (read != TM_READ_AFTER_WRITE && read != TM_READ_BEFORE_WRITE) return TM_ERR_INVALID;
     if (n_tokens == 0) return TM_OK;
     if (!tok_ok(k) || !tok_ok(v) || !tok_ok(q) || !tok_ok(y) || !gate_ok(theta) || !gate_ok(eta) ||
         !gate_ok(alpha))
         return TM_ERR_INVALID;
     if (n_tokens % c->chunk != 0) return TM_ERR_SHAPE;
-    return with_graph(c, make_key(2, batch, heads, n_tokens, dtype, {state, k, v, q, theta, eta, alpha, y, ws}),
+    const bool before = read == TM_READ_BEFORE_WRITE;
+    return with_graph(c, make_key(before ? 4 : 2, batch, heads, n_tokens, dtype,
+                                  {state, k, v, q, theta, eta, alpha, y, ws}),
                       static_cast<hipStream_t>(stream), [&](hipStream_t st) {
-        return run_store(c, state, k, v, q, theta, eta, alpha, y, batch, heads, n_tokens, dtype, ws, st);
+        return run_store(c, state, k, v, q, theta, eta, alpha, y, batch, heads, n_tokens, dtype, ws, st,
+                         before);
     });
+}
+
+tm_status tm_forward(const tm_ctx* c, void* state, const void* k, const void* v, const void* q,
+                     const float* theta, const float* eta, const float* alpha, float* y, int batch,
+                     int heads, int n_tokens, tm_dtype dtype, void* ws, void* stream) {
+    return tm_forward_ex(c, state, k, v, q, theta, eta, alpha, y, batch, heads, n_tokens, dtype,
+                         TM_READ_AFTER_WRITE, ws, stream);
 }
 
 tm_status tm_retrieve(const tm_ctx* c, const void* state_v, const void* q, float* y, int batch,

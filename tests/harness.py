@@ -57,11 +57,15 @@ class GpuMemory:
             self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
         return self.ws
 
-    def forward(self, d):
+    def forward(self, d, read=None):
         B, Tn, H, dim = d["k"].shape
         y = torch.empty((B, Tn, H, dim), dtype=torch.float32, device="cuda")
-        T.tm_forward(self.ctx, self.state, d["k"], d["v"], d["q"], d["theta"], d["eta"], d["alpha"], y,
-                     self._ws(Tn))
+        if read is None:
+            T.tm_forward(self.ctx, self.state, d["k"], d["v"], d["q"], d["theta"], d["eta"], d["alpha"], y,
+                         self._ws(Tn))
+        else:
+            T.tm_forward_ex(self.ctx, self.state, d["k"], d["v"], d["q"], d["theta"], d["eta"], d["alpha"], y,
+                            self._ws(Tn), read)
         return y
 
     def store(self, d):
@@ -92,9 +96,10 @@ class GpuMemory:
         self.ctx = None
 
 
-def oracle_forward(wl: I.Workload, state: np.ndarray, ci: I.CallInputs, with_q=True, threads=None):
+def oracle_forward(wl: I.Workload, state: np.ndarray, ci: I.CallInputs, with_q=True, threads=None,
+                   read="after"):
     return tmref.forward(wl.dim, wl.depth, wl.expansion, wl.chunk, state, ci.k, ci.v, ci.theta, ci.eta,
-                         ci.alpha, q=ci.q if with_q else None, n_threads=threads)
+                         ci.alpha, q=ci.q if with_q else None, n_threads=threads, read=read)
 
 
 def compare_state(wl: I.Workload, gpu_state, ref_state):

@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     syms = declared_symbols()
-    assert len(syms) == 17
+    assert len(syms) == 18
     assert set(syms) == set(T.EXPORTED)
     L = ctypes.CDLL(T.LIB_PATH)
     for s in syms:
@@ -84,5 +84,12 @@ def test_call_validation_before_launch():
     assert L.tm_store(c, A, None, None, None, None, None, 1, 1, 0, T.TM_BF16, A, st) == T.TM_OK
     assert L.tm_forward(c, A, None, None, None, None, None, None, None, 1, 1, 0, T.TM_BF16, A, st) == T.TM_OK
     assert L.tm_retrieve(c, A, None, None, 1, 1, 0, T.TM_F32, A, st) == T.TM_OK
+    # the read order: only the two defined values
+    for bad in (-1, 2):
+        assert L.tm_forward_ex(c, A, A, A, A, G, G, G, A, 1, 1, 16, T.TM_BF16, bad, A, st) == T.TM_ERR_INVALID
+    assert L.tm_forward_ex(c, A, A, A, A, G, G, G, A, 1, 1, 17, T.TM_BF16, T.TM_READ_BEFORE_WRITE, A, st) == \
+        T.TM_ERR_SHAPE
+    assert L.tm_forward_ex(c, A, None, None, None, None, None, None, None, 1, 1, 0, T.TM_BF16,
+                           T.TM_READ_BEFORE_WRITE, A, st) == T.TM_OK
     assert L.tm_status_str(T.TM_ERR_SHAPE).decode().startswith("n_tokens")
     T.tm_destroy(c)

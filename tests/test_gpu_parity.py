@@ -323,3 +323,52 @@ def test_w1_split_matches_in_place(case):
     assert np.array_equal(sa, sb)
     for u, v in zip(ya, yb):
         assert np.array_equal(u, v)
+
+
+# queries read before their chunk's write (TM_READ_BEFORE_WRITE) against the
+# oracle's read-before-write order, on the small shapes and mlp384, two calls
+# carrying the state; the state matches the read-after-write call bitwise
+RB_CASES = [SMALL[0], SMALL[2], SMALL[3], SMALL[5], SMALL[2].replace(dtype="bf16", name="mlp96_bf16"),
+            SMALL[4].replace(dtype="bf16", name="deep32x4_bf16")]
+
+
+@pytest.mark.parametrize("wl", RB_CASES, ids=lambda w: w.name)
+def test_read_before_write_parity(wl):
+    import test_trained_neural_amd as T
+    say("case", wl)
+    p = I.make_params(wl)
+    g = GpuMemory(wl, p)
+    h = GpuMemory(wl, p)
+    ref = I.initial_state(wl, p)
+    tol = TOL[wl.dtype]
+    for j in range(2):
+        ci = I.make_call(wl, p, j)
+        d = dev_inputs(ci, wl.dtype)
+        y = g.forward(d, read=T.TM_READ_BEFORE_WRITE).cpu().numpy()
+        h.forward(d)
+        yr = oracle_forward(wl, ref, ci, read="before")
+        ey = relerr(y, yr)
+        em, es = compare_state(wl, g.export(), ref)
+        say("  call %d: y %.2e  M %.2e  S %.2e" % (j, ey, em, es))
+        assert ey < tol and em < tol and es < 2 * tol
+        assert np.array_equal(g.export(), h.export())
+    assert g.check() == (False, 2 * wl.seq)
+    g.close()
+    h.close()
+
+
+def test_read_before_write_mlp384():
+    import test_trained_neural_amd as T
+    wl = I.WORKLOADS["mlp384"]
+    say("case", wl)
+    p = I.make_params(wl)
+    ci = I.make_call(wl, p)
+    g = GpuMemory(wl, p)
+    y = g.forward(dev_inputs(ci, "bf16"), read=T.TM_READ_BEFORE_WRITE).cpu().numpy()
+    ref = I.initial_state(wl, p)
+    yr = oracle_forward(wl, ref, ci, read="before")
+    ey = relerr(y, yr)
+    em, es = compare_state(wl, g.export(), ref)
+    say("  y %.2e  M %.2e  S %.2e" % (ey, em, es))
+    assert ey < TOL["bf16"] and em < TOL["bf16"] and es < 2 * TOL["bf16"]
+    g.close()
