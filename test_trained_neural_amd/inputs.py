@@ -211,3 +211,31 @@ def initial_state(wl: Workload, params: Params, batch: int | None = None) -> np.
         for h in range(wl.heads):
             st[b * wl.heads + h, :P] = params.init_weights[h]
     return st
+
+
+@dataclasses.dataclass
+class PrologueInputs:
+    x: np.ndarray        # [B][T][D] float32 (bf16-exact for bf16 workloads)
+    w_kvq: np.ndarray    # [3][D][H*d] float32 (bf16-exact for bf16): W_K, W_V, W_Q
+    conv: np.ndarray     # [3][H*d][K] float32: per-channel taps, tap j for j tokens back
+    w_gate: np.ndarray   # [3][D][H] float32: theta, eta, alpha
+    gate_bias: np.ndarray  # [3] float32: the gate offsets
+
+
+def make_prologue(wl: Workload, params: Params, j: int = 0, seed: int = 0, conv_len: int = 4,
+                  tokens=None) -> PrologueInputs:
+    """The token vectors of call j (the same draws as make_call) with the
+    projection and gate weights of ``params``, and per-channel convolution
+    taps ~ N(0, 1/conv_len) from their own generator.  Draws only: the input
+    side's arithmetic is not done here."""
+    T = wl.tokens_per_call if tokens is None else tokens
+    B, D = wl.batch, wl.model_dim
+    rng = np.random.default_rng([seed, 1, j])
+    x = np.stack([rng.standard_normal((T, D), dtype=np.float64).astype(np.float32) for _ in range(B)])
+    w = np.stack([params.W_K, params.W_V, params.W_Q]).astype(np.float32)
+    crng = np.random.default_rng([seed, 2])
+    conv = (crng.standard_normal((3, D, conv_len)) / np.sqrt(conv_len)).astype(np.float32)
+    wg = np.stack(params.w_gate).astype(np.float32)
+    if wl.dtype == "bf16":
+        x, w = round_bf16(x), round_bf16(w)
+    return PrologueInputs(x, w, conv, wg, np.asarray(wl.offsets, np.float32))
