@@ -199,6 +199,59 @@ def other_workload(name, steps, calls=None, read=None):
             "sample": "whole workload" if n_calls == wl.calls else "first %d of %d calls" % (n_calls, wl.calls)}
 
 
+def input_side(name, steps):
+    """The input side (tm_project: x -> k, v, q and the gates, 4-tap
+    convolution) alone and chained with the memory step (tm_project +
+    tm_state_init + tm_forward), on the workload's first call; tokens/s."""
+    import numpy as np
+    import torch
+    import test_trained_neural_amd as T
+    from test_trained_neural_amd import inputs as I
+    wl = I.WORKLOADS[name]
+    params = I.make_params(wl, 0)
+    pi = I.make_prologue(wl, params, 0, 0, conv_len=4)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    Bn, Tn, H, d = wl.batch, wl.tokens_per_call, wl.heads, wl.dim
+    x = torch.from_numpy(pi.x).to(dev).to(tdt).contiguous()
+    w = torch.from_numpy(np.ascontiguousarray(pi.w_kvq.transpose(0, 2, 1))).to(dev).to(tdt).contiguous()
+    conv = torch.from_numpy(pi.conv).to(dev).contiguous()
+    wg = torch.from_numpy(np.ascontiguousarray(pi.w_gate.transpose(0, 2, 1))).to(dev).contiguous()
+    gb = torch.from_numpy(pi.gate_bias).to(dev).contiguous()
+    hist = torch.zeros((Bn, 3, 3, H * d), dtype=torch.float32, device=dev)
+    k, v, q = (torch.empty((Bn, Tn, H, d), dtype=tdt, device=dev) for _ in range(3))
+    g = [torch.empty((Bn, Tn, H), dtype=torch.float32, device=dev) for _ in range(3)]
+    ctx = T.tm_create(d, wl.depth, wl.expansion, wl.chunk)
+    state = torch.empty(T.tm_state_bytes(ctx, Bn, H), dtype=torch.uint8, device=dev)
+    ws = torch.empty(T.tm_workspace_bytes(ctx, Bn, H, Tn), dtype=torch.uint8, device=dev)
+    y = torch.empty((Bn, Tn, H, d), dtype=torch.float32, device=dev)
+    init = torch.from_numpy(params.init_weights).to(dev)
+
+    def project():
+        T.tm_project(ctx, x, w, conv, wg, gb, hist, k, v, q, g[0], g[1], g[2], H)
+
+    def chain():
+        project()
+        T.tm_state_init(ctx, state, Bn, H, init)
+        T.tm_forward(ctx, state, k, v, q, g[0], g[1], g[2], y, ws)
+
+    out = {}
+    for nm, fn in (("input_side", project), ("from_tokens", chain)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        out[nm] = {"tokens_per_s": Bn * Tn / dt, "ms_per_step": dt * 1e3, "steps": steps}
+    out["input_side"]["step"] = "tm_project of (%d, %d) tokens of width %d, 4-tap convolution" % (Bn, Tn, wl.model_dim)
+    out["from_tokens"]["step"] = "tm_project + tm_state_init + tm_forward of (%d, %d) tokens" % (Bn, Tn)
+    T.tm_destroy(ctx)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -352,6 +405,9 @@ def main():
             # the same step with each chunk's queries read before its write
             "mlp384_read_before_write": other_workload("mlp384", 20, read=1),
         }
+        side = input_side("mlp384", 20)
+        out["other_workloads"]["mlp384_input_side"] = side["input_side"]
+        out["other_workloads"]["mlp384_from_tokens"] = side["from_tokens"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, params, ci)
         out["cpu_baseline"]["gpu_over_cpu"] = out["value"] / out["cpu_baseline"]["value"]

@@ -132,6 +132,35 @@ tm_status tm_forward_ex(const tm_ctx* ctx, void* state, const void* k, const voi
                         int n_tokens, tm_dtype dtype, tm_read read, void* workspace,
                         void* stream);
 
+/* The memory's input side ("Titans, explained" steps 1, 4 and 5), from the
+ * tokens' model vectors to the keys, values, queries and gates that
+ * tm_store / tm_forward take:
+ *   p_i = x W_i^T for i = key, value, query (W_i: heads*dim output rows of
+ *   model_dim inputs, PyTorch's Linear layout), then a causal depthwise
+ *   convolution of every channel over the last conv_len tokens (tap j weighs
+ *   the projection j tokens back; no bias, no activation), then keys and
+ *   queries l2-normalised per head (norm clamped below at 1e-12); the gates
+ *   sigmoid(x w_g + b_g) per head for g = theta, eta, alpha.
+ * x: [batch][n_tokens][model_dim] of dtype, 16-byte aligned, model_dim a
+ *   multiple of 32.  w_kvq: [3][heads*dim][model_dim] of dtype, 16-byte
+ *   aligned.  conv: [3][heads*dim][conv_len] fp32, conv_len 1..4.  w_gate:
+ *   [3][heads][model_dim] fp32.  gate_bias: [3] fp32 (device).
+ * history: [batch][conv_len-1][3][heads*dim] fp32, the projections of the
+ *   stream's last conv_len-1 tokens before this call, oldest first (zeros at
+ *   a stream's start); read, then overwritten with those of this call's last
+ *   tokens, so consecutive calls equal one long call.  Ignored (may be null)
+ *   for conv_len 1.
+ * k, v, q: [batch][n_tokens][heads][dim] of dtype; theta, eta, alpha:
+ *   [batch][n_tokens][heads] fp32.  Every pointer is a device pointer owned by
+ *   the caller.  n_tokens == 0 is a no-op.  Bad sizes, null or misaligned
+ *   pointers give TM_ERR_INVALID, a bad dtype TM_ERR_DTYPE, all before any
+ *   launch.  Asynchronous on `stream`; three launches, no graph. */
+tm_status tm_project(const tm_ctx* ctx, const void* x, int model_dim, const void* w_kvq,
+                     const float* conv, int conv_len, const float* w_gate,
+                     const float* gate_bias, float* history, void* k, void* v, void* q,
+                     float* theta, float* eta, float* alpha, int batch, int heads,
+                     int n_tokens, tm_dtype dtype, void* stream);
+
 /* Canonical fp32 copy of the state: dst is [batch*heads][2P], per stream
  * M_1..M_L then S_1..S_L, each W_l row-major [d_in][d_out]. */
 tm_status tm_state_export(const tm_ctx* ctx, const void* state, int batch, int heads,

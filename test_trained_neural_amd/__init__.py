@@ -25,7 +25,7 @@ TM_READ_AFTER_WRITE, TM_READ_BEFORE_WRITE = 0, 1
 EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_workspace_bytes",
             "tm_state_init", "tm_store", "tm_retrieve", "tm_forward", "tm_state_export",
             "tm_state_import", "tm_state_check", "tm_status_str", "tm_timing_enable", "tm_timing_read",
-            "tm_graphs_enable", "tm_w1_split_enable", "tm_forward_ex")
+            "tm_graphs_enable", "tm_w1_split_enable", "tm_forward_ex", "tm_project")
 
 # kernel classes of tm_timing_enable / tm_timing_read
 K_SCAN, K_FWD, K_BWD, K_UPDATE, K_FIRST = 0, 1, 2, 3, 4
@@ -70,6 +70,9 @@ def lib():
         L.tm_forward.restype = _i
         L.tm_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
         L.tm_forward_ex.restype = _i
+        L.tm_project.restype = _i
+        L.tm_project.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _i, _i, _i, _i, _vp]
         L.tm_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
         L.tm_state_export.restype = _i
         L.tm_state_export.argtypes = [_vp, _vp, _i, _i, _vp, _vp]
@@ -184,6 +187,22 @@ def tm_forward_ex(ctx, state, k, v, q, theta, eta, alpha, y, workspace, read, st
     _check("tm_forward_ex", lib().tm_forward_ex(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(q), _ptr(theta),
                                                 _ptr(eta), _ptr(alpha), _ptr(y), B, H, T, _dtype_code(k),
                                                 int(read), _ptr(workspace), _stream(stream)))
+
+
+def tm_project(ctx, x, w_kvq, conv, w_gate, gate_bias, history, k, v, q, theta, eta, alpha, heads,
+               stream=None):
+    """The input side: x [B][T][D] -> k, v, q [B][T][H][d] (x's dtype) and
+    the gates [B][T][H] fp32; history [B][K-1][3][H*d] fp32 is read and
+    rewritten (None for K = 1)."""
+    _tok(x, w_kvq, conv, w_gate, gate_bias, k, v, q, theta, eta, alpha)
+    B, T, D = x.shape
+    K = conv.shape[-1]
+    if history is not None:
+        _tok(history)
+    _check("tm_project", lib().tm_project(ctx, _ptr(x), D, _ptr(w_kvq), _ptr(conv), K, _ptr(w_gate),
+                                          _ptr(gate_bias), _ptr(history) if history is not None else None,
+                                          _ptr(k), _ptr(v), _ptr(q), _ptr(theta), _ptr(eta), _ptr(alpha),
+                                          B, heads, T, _dtype_code(x), _stream(stream)))
 
 
 def tm_state_export(ctx, state, batch, heads, dst, stream=None):

@@ -773,6 +773,47 @@ tm_status tm_forward_ex(const tm_ctx* c, void* state, const void* k, const void*
     });
 }
 
+tm_status tm_project(const tm_ctx* c, const void* x, int model_dim, const void* w_kvq, const float* conv,
+                     int conv_len, const float* w_gate, const float* gate_bias, float* history, void* k,
+                     void* v, void* q, float* theta, float* eta, float* alpha, int batch, int heads,
+                     int n_tokens, tm_dtype dtype, void* stream) {
+    if (!c) return TM_ERR_INVALID;
+    if (dtype != TM_F32 && dtype != TM_BF16) return TM_ERR_DTYPE;
+    if (batch <= 0 || heads <= 0 || n_tokens < 0 || model_dim < 32 || model_dim % 32 != 0 ||
+        conv_len < 1 || conv_len > MAX_CONV || (long)batch * n_tokens > 0x7fffffffL ||
+        (long)heads * c->dim > 65536)
+        return TM_ERR_INVALID;
+    if (!tok_ok(x) || !tok_ok(w_kvq) || !gate_ok(conv) || !gate_ok(w_gate) || !gate_ok(gate_bias) ||
+        (conv_len > 1 && !gate_ok(history)))
+        return TM_ERR_INVALID;
+    if (n_tokens == 0) return TM_OK;
+    if (!tok_ok(k) || !tok_ok(v) || !tok_ok(q) || !gate_ok(theta) || !gate_ok(eta) || !gate_ok(alpha))
+        return TM_ERR_INVALID;
+    ProjArgs p;
+    memset(&p, 0, sizeof(p));
+    p.x = x;
+    p.w = w_kvq;
+    p.conv = conv;
+    p.wg = w_gate;
+    p.gb = gate_bias;
+    p.hist = history;
+    p.out[0] = k;
+    p.out[1] = v;
+    p.out[2] = q;
+    p.gate[0] = theta;
+    p.gate[1] = eta;
+    p.gate[2] = alpha;
+    p.B = batch;
+    p.T = n_tokens;
+    p.D = model_dim;
+    p.H = heads;
+    p.d = c->dim;
+    p.K = conv_len;
+    return launch_project(p, dtype == TM_F32 ? 1 : 0, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? TM_OK
+               : TM_ERR_HIP;
+}
+
 tm_status tm_forward(const tm_ctx* c, void* state, const void* k, const void* v, const void* q,
                      const float* theta, const float* eta, const float* alpha, float* y, int batch,
                      int heads, int n_tokens, tm_dtype dtype, void* ws, void* stream) {

@@ -250,7 +250,27 @@ struct ScanArgs {
     int bp, kt_f32;
 };
 
+// The input side ("Titans, explained" steps 1, 4, 5): per token x (width D)
+// the projections p_i = x W_i^T (i = key, value, query; W_i is [H*d][D], one
+// row per output channel), a causal depthwise convolution of each channel
+// over the last K <= 4 tokens (the tokens before the call come from the
+// history the previous call left: its last K-1 projections, oldest first),
+// l2-normalised keys and queries per head, and the gates sigmoid(x w_g + b_g).
+constexpr int MAX_CONV = 4;
+struct ProjArgs {
+    const void* x;            // [B][T][D]
+    const void* w;            // [3][H*d][D]
+    const float* conv;        // [3][H*d][K]
+    const float* wg;          // [3][H][D]
+    const float* gb;          // [3]
+    float* hist;              // [B][K-1][3][H*d] fp32, read by the projection kernel, then rewritten
+    void* out[3];             // k, v, q: [B][T][H][d]
+    float* gate[3];           // theta, eta, alpha: [B][T][H]
+    int B, T, D, H, d, K;
+};
+
 // ---- launchers (tm_kernels.hip) ----
+hipError_t launch_project(const ProjArgs& p, int f32, hipStream_t st);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
 // fwd: op = 0 bf16 (A bf16, B = bf16 transposed copy), op = 1 fp32 (A fp32,
 // B = fp32 master read with stride).  bwd: A fp32 deltas, B fp32 master.

@@ -1742,4 +1742,244 @@ hipError_t launch_header(StateHeader* h, uint64_t hash, int batch, int heads, hi
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Input side: projections + convolution + normalisation, gates, history.
+
+// One workgroup per (batch row b, tile of RT tokens, projection i, head h):
+// the head's d channels of projection i for tokens t0-3 .. t0+RT-1 on the
+// matrix cores (K = D; the 3 rows before the tile feed the convolution),
+// staged in LDS as fp32, then the convolution, the row norms (keys and
+// queries) and the store.  Before the call's first token the rows come from
+// the history.  Waves take 16-column blocks wave, wave + 8, ...; rows
+// outside the call multiply zeros.
+constexpr int PROJ_HALO = MAX_CONV - 1;
+
+template <class OP, int RT>
+__global__ __launch_bounds__(512) void project_kernel(ProjArgs a) {
+    typedef typename Frag<OP>::T F;
+    constexpr int NRB = (RT + PROJ_HALO + 15) / 16;   // row blocks of the staged tile
+    constexpr int G = 4;                              // column blocks per pass of a wave
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kofs = 8 * (lane >> 4);
+    const int b = blockIdx.z, i = blockIdx.y / a.H, h = blockIdx.y - i * a.H;
+    const int t0 = blockIdx.x * RT, d = a.d, D = a.D, HD = a.H * a.d;
+    const int ncb = d >> 4, nks = D >> 5;
+    const int DP = d + 4;                             // LDS row pitch (floats)
+    float* P = reinterpret_cast<float*>(lds);         // [NRB*16][DP]: projections of rows t0-3 ..
+    float* part = P + NRB * 16 * DP;                  // [8][RT]: per-wave partial sums of squares
+    const OP* x = reinterpret_cast<const OP*>(a.x) + (long)b * a.T * D;
+    const OP* w = reinterpret_cast<const OP*>(a.w) + ((long)i * HD + (long)h * d) * D;
+
+    // the staged rows (token t0 - 3 + r): clamped addresses, zeros outside the call
+    const OP* arow[NRB];
+    bool aok[NRB];
+#pragma unroll
+    for (int m = 0; m < NRB; ++m) {
+        const int u = t0 - PROJ_HALO + m * 16 + (lane & 15);
+        aok[m] = u >= 0 && u < a.T;
+        arow[m] = x + (long)min(max(u, 0), a.T - 1) * D + kofs;
+    }
+    for (int c0 = wave; c0 < ncb; c0 += 8 * G) {
+        f32x4 acc[NRB][G];
+        const OP* brow[G];
+        bool bok[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int cb = c0 + 8 * g;
+            bok[g] = cb < ncb;
+            brow[g] = w + (long)(min(cb, ncb - 1) * 16 + (lane & 15)) * D + kofs;
+#pragma unroll
+            for (int m = 0; m < NRB; ++m) acc[m][g] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+        // KC steps of loads per memory round trip; steps past K multiply zeros
+        constexpr int KC = sizeof(OP) == 2 ? 4 : 2;
+        for (int k0 = 0; k0 < nks; k0 += KC) {
+            F av[KC][NRB], bv[KC][G];
+#pragma unroll
+            for (int q = 0; q < KC; ++q) {
+                const int ks = min(k0 + q, nks - 1);
+                const bool live = k0 + q < nks;
+#pragma unroll
+                for (int m = 0; m < NRB; ++m) av[q][m] = keep_if(cvt<OP>(ld8(arow[m] + ks * 32)), aok[m] && live);
+#pragma unroll
+                for (int g = 0; g < G; ++g) bv[q][g] = cvt<OP>(ld8(brow[g] + ks * 32));
+            }
+            // keep every load of the round trip above the products (the
+            // scheduler would otherwise interleave them, one trip per step)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < KC; ++q)
+#pragma unroll
+                for (int m = 0; m < NRB; ++m)
+#pragma unroll
+                    for (int g = 0; g < G; ++g) mma(acc[m][g], av[q][m], bv[q][g]);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            if (bok[g])   // wave-uniform
+#pragma unroll
+                for (int m = 0; m < NRB; ++m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        P[(m * 16 + 4 * (lane >> 4) + e) * DP + (c0 + 8 * g) * 16 + (lane & 15)] = acc[m][g][e];
+    }
+    __syncthreads();
+    // rows before the call's first token: the history (projections of the
+    // previous call's last K-1 tokens, oldest first)
+    if (t0 < PROJ_HALO && a.K > 1) {
+        for (int idx = tid; idx < PROJ_HALO * d; idx += 512) {
+            const int r = idx / d, c = idx - r * d, u = t0 - PROJ_HALO + r;
+            if (u < 0 && u >= -(a.K - 1))
+                P[r * DP + c] = a.hist[(((long)b * (a.K - 1) + (a.K - 1 + u)) * 3 + i) * HD + (long)h * d + c];
+        }
+        __syncthreads();
+    }
+    // the convolution: thread -> channels tid and tid + 512, a window over
+    // the staged rows; then each wave's partial sums of squares per row
+    const int nrow = min(RT, a.T - t0);
+    float o[2][RT];
+    float ss[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) ss[r] = 0.f;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int c = tid + 512 * pass;
+        const bool on = c < d;
+        float tap[MAX_CONV];
+#pragma unroll
+        for (int j = 0; j < MAX_CONV; ++j)
+            tap[j] = (on && j < a.K) ? a.conv[((long)i * HD + (long)h * d + c) * a.K + j] : 0.f;
+        const int cc = on ? c : 0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < MAX_CONV; ++j) acc += tap[j] * P[(r + PROJ_HALO - j) * DP + cc];
+            o[pass][r] = acc;
+            ss[r] += acc * acc;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        float v = ss[r];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == 0) part[wave * RT + r] = v;
+    }
+    __syncthreads();
+    OP* out = reinterpret_cast<OP*>(a.out[i]) + ((long)b * a.T + t0) * a.H * d + (long)h * d;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        float scale = 1.f;
+        if (i != 1) {
+            float n2 = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < 8; ++wv) n2 += part[wv * RT + r];
+            scale = __builtin_amdgcn_rcpf(fmaxf(sqrtf(n2), 1e-12f));
+        }
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int c = tid + 512 * pass;
+            if (c < d && r < nrow) out[(long)r * a.H * d + c] = (OP)(o[pass][r] * scale);
+        }
+    }
+}
+
+// The gates: one wave per token, lanes split D; sigmoid(x w_g + b_g) for
+// every gate g and head.
+template <class OP>
+__global__ __launch_bounds__(256) void gates_kernel(ProjArgs a) {
+    const long tok = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (tok >= (long)a.B * a.T) return;   // wave-uniform
+    const OP* x = reinterpret_cast<const OP*>(a.x) + tok * a.D;
+    for (int gh = 0; gh < 3 * a.H; ++gh) {
+        const int g = gh / a.H, h = gh - g * a.H;
+        const float* wg = a.wg + ((long)g * a.H + h) * a.D;
+        float acc = 0.f;
+        for (int c = lane; c < a.D; c += 64) acc += (float)x[c] * wg[c];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if (lane == 0) a.gate[g][tok * a.H + h] = sigmoid(acc + a.gb[g]);
+    }
+}
+
+// The new history: per channel of each projection, the projections of the
+// call's last K-1 tokens (oldest first), or, where the call is shorter, the
+// old history moved up.  One wave per (batch row, projection, channel),
+// lanes split the width; each wave reads the old values it needs before it
+// writes, and waves own disjoint channels.
+template <class OP>
+__global__ __launch_bounds__(256) void history_kernel(ProjArgs a) {
+    const int HD = a.H * a.d, K1 = a.K - 1;
+    const long wv = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (wv >= (long)a.B * 3 * HD) return;   // wave-uniform
+    const int n = (int)(wv % HD), i = (int)((wv / HD) % 3), b = (int)(wv / (3L * HD));
+    float old[MAX_CONV - 1];
+#pragma unroll
+    for (int r = 0; r < MAX_CONV - 1; ++r)
+        old[r] = (r < K1) ? a.hist[(((long)b * K1 + r) * 3 + i) * HD + n] : 0.f;
+    const OP* w = reinterpret_cast<const OP*>(a.w) + ((long)i * HD + n) * a.D;
+    float nw[MAX_CONV - 1];
+#pragma unroll
+    for (int r = 0; r < MAX_CONV - 1; ++r) {
+        const int u = a.T - K1 + r;
+        float v = 0.f;
+        if (r < K1 && u >= 0) {   // wave-uniform
+            const OP* x = reinterpret_cast<const OP*>(a.x) + ((long)b * a.T + u) * a.D;
+            for (int c = lane; c < a.D; c += 64) v += (float)x[c] * (float)w[c];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        } else {
+#pragma unroll
+            for (int q = 0; q < MAX_CONV - 1; ++q)
+                if (q == r + a.T) v = old[q];
+        }
+        nw[r] = v;
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < MAX_CONV - 1; ++r)
+            if (r < K1) a.hist[(((long)b * K1 + r) * 3 + i) * HD + n] = nw[r];
+    }
+}
+
+template <class OP, int RT>
+static void launch_project_rt(const ProjArgs& p, hipStream_t st) {
+    constexpr int NRB = (RT + PROJ_HALO + 15) / 16;
+    const size_t lds = ((size_t)NRB * 16 * (p.d + 4) + 8 * RT) * 4;
+    if (lds > 64 * 1024)   // above the default dynamic LDS limit
+        (void)hipFuncSetAttribute((const void*)project_kernel<OP, RT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+    dim3 grid((p.T + RT - 1) / RT, 3 * p.H, p.B);
+    hipLaunchKernelGGL((project_kernel<OP, RT>), grid, dim3(512), lds, st, p);
+}
+
+hipError_t launch_project(const ProjArgs& p, int f32, hipStream_t st) {
+    if (p.T == 0 || p.B == 0) return hipSuccess;
+    if (p.d > 1024 || p.d % 32 != 0 || p.D % 32 != 0 || p.K < 1 || p.K > MAX_CONV) return hipErrorInvalidValue;
+    // tiles of 32 tokens; 16 for the widest heads (the staged rows fill LDS)
+    if (p.d <= 512) {
+        if (f32) launch_project_rt<float, 32>(p, st);
+        else launch_project_rt<bf16, 32>(p, st);
+    } else {
+        if (f32) launch_project_rt<float, 16>(p, st);
+        else launch_project_rt<bf16, 16>(p, st);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long toks = (long)p.B * p.T;
+    if (f32) hipLaunchKernelGGL(gates_kernel<float>, dim3((unsigned)((toks + 3) / 4)), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL(gates_kernel<bf16>, dim3((unsigned)((toks + 3) / 4)), dim3(256), 0, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess || p.K == 1) return e;
+    const long nw = (long)p.B * 3 * p.H * p.d;   // one wave each
+    if (f32) hipLaunchKernelGGL(history_kernel<float>, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL(history_kernel<bf16>, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
 }  // namespace tmk

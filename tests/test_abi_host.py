@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     syms = declared_symbols()
-    assert len(syms) == 18
+    assert len(syms) == 19
     assert set(syms) == set(T.EXPORTED)
     L = ctypes.CDLL(T.LIB_PATH)
     for s in syms:
@@ -91,5 +91,18 @@ def test_call_validation_before_launch():
         T.TM_ERR_SHAPE
     assert L.tm_forward_ex(c, A, None, None, None, None, None, None, None, 1, 1, 0, T.TM_BF16,
                            T.TM_READ_BEFORE_WRITE, A, st) == T.TM_OK
+    # the input side: sizes, dtype, alignment, all on the host
+    P = L.tm_project
+    assert P(c, A, 64, A, G, 4, G, G, G, A, A, A, G, G, G, 1, 1, 16, 7, st) == T.TM_ERR_DTYPE
+    assert P(c, A, 48, A, G, 4, G, G, G, A, A, A, G, G, G, 1, 1, 16, T.TM_BF16, st) == T.TM_ERR_INVALID
+    assert P(c, A, 64, A, G, 5, G, G, G, A, A, A, G, G, G, 1, 1, 16, T.TM_BF16, st) == T.TM_ERR_INVALID
+    assert P(c, A, 64, A, G, 0, G, G, G, A, A, A, G, G, G, 1, 1, 16, T.TM_BF16, st) == T.TM_ERR_INVALID
+    assert P(c, A, 64, A, G, 4, G, G, None, A, A, A, G, G, G, 1, 1, 16, T.TM_BF16, st) == T.TM_ERR_INVALID
+    assert P(c, ctypes.c_void_p((1 << 20) + 2), 64, A, G, 4, G, G, G, A, A, A, G, G, G, 1, 1, 16, T.TM_BF16,
+             st) == T.TM_ERR_INVALID
+    assert P(c, A, 64, A, G, 4, G, G, G, None, A, A, G, G, G, 1, 1, 16, T.TM_BF16, st) == T.TM_ERR_INVALID
+    assert P(c, A, 64, A, G, 4, G, G, G, A, A, A, G, G, G, 0, 1, 16, T.TM_BF16, st) == T.TM_ERR_INVALID
+    # empty: a no-op (outputs and, for one tap, the history may be null)
+    assert P(c, A, 64, A, G, 1, G, G, None, None, None, None, None, None, None, 1, 1, 0, T.TM_BF16, st) == T.TM_OK
     assert L.tm_status_str(T.TM_ERR_SHAPE).decode().startswith("n_tokens")
     T.tm_destroy(c)
