@@ -154,7 +154,8 @@ tm_status tm_forward_ex(const tm_ctx* ctx, void* state, const void* k, const voi
  *   [batch][n_tokens][heads] fp32.  Every pointer is a device pointer owned by
  *   the caller.  n_tokens == 0 is a no-op.  Bad sizes, null or misaligned
  *   pointers give TM_ERR_INVALID, a bad dtype TM_ERR_DTYPE, all before any
- *   launch.  Asynchronous on `stream`; three launches, no graph. */
+ *   launch.  Asynchronous on `stream` (two launches; graph replay as for the
+ *   calls below). */
 tm_status tm_project(const tm_ctx* ctx, const void* x, int model_dim, const void* w_kvq,
                      const float* conv, int conv_len, const float* w_gate,
                      const float* gate_bias, float* history, void* k, void* v, void* q,
@@ -180,11 +181,12 @@ tm_status tm_state_check(const tm_ctx* ctx, const void* state, int batch, int he
 const char* tm_status_str(tm_status status);
 
 /* Graph replay (on by default, process-wide).  A tm_state_init / tm_store /
- * tm_retrieve / tm_forward call whose device, pointers and sizes repeat an
- * earlier call's is captured once into a HIP graph (on a private stream of
- * the ctx) and from then on replayed on the caller's stream, which removes
- * most of the per-kernel launch cost of the chunk loop.  Each ctx keeps its
- * 16 most recent call shapes.  on = 0 launches every call directly. */
+ * tm_retrieve / tm_forward / tm_forward_ex / tm_project call whose device,
+ * pointers and sizes repeat an earlier call's is captured once into a HIP
+ * graph (on a private stream of the ctx) and from then on replayed on the
+ * caller's stream, which removes most of the per-kernel launch cost of the
+ * chunk loop.  Each ctx keeps its 16 most recent call shapes.  on = 0
+ * launches every call directly. */
 tm_status tm_graphs_enable(int on);
 
 /* Placement of W_1's update for depth-2 memories; the results are bitwise

@@ -20,8 +20,8 @@ using namespace tmk;
 // A call's launch sequence replayed as a HIP graph: keyed by everything the
 // kernels' arguments depend on (device, every pointer and every size).
 struct GraphEntry {
-    int dev, kind, batch, heads, n_tokens, dtype, opt;
-    const void* p[10];
+    int dev, kind, batch, heads, n_tokens, dtype, opt, extra;
+    const void* p[12];
     int seen;                    // sightings before capture
     hipGraphExec_t exec;
     unsigned long long last;     // LRU stamp
@@ -234,7 +234,7 @@ tm_status with_graph(const tm_ctx* cc, GraphEntry key, hipStream_t st, F&& launc
     GraphEntry* hit = nullptr;
     for (GraphEntry& e : *c->graphs) {
         if (e.dev == key.dev && e.kind == key.kind && e.batch == key.batch && e.heads == key.heads &&
-            e.n_tokens == key.n_tokens && e.dtype == key.dtype && e.opt == key.opt &&
+            e.n_tokens == key.n_tokens && e.dtype == key.dtype && e.opt == key.opt && e.extra == key.extra &&
             memcmp(e.p, key.p, sizeof(key.p)) == 0) {
             hit = &e;
             break;
@@ -789,6 +789,9 @@ tm_status tm_project(const tm_ctx* c, const void* x, int model_dim, const void* 
     if (n_tokens == 0) return TM_OK;
     if (!tok_ok(k) || !tok_ok(v) || !tok_ok(q) || !gate_ok(theta) || !gate_ok(eta) || !gate_ok(alpha))
         return TM_ERR_INVALID;
+    GraphEntry key = make_key(5, batch, heads, n_tokens, dtype, {x, w_kvq, conv, w_gate, gate_bias, history, k, v,
+                                                               q, theta, eta, alpha});
+    key.extra = model_dim * 8 + conv_len;
     ProjArgs p;
     memset(&p, 0, sizeof(p));
     p.x = x;
@@ -809,9 +812,9 @@ tm_status tm_project(const tm_ctx* c, const void* x, int model_dim, const void* 
     p.H = heads;
     p.d = c->dim;
     p.K = conv_len;
-    return launch_project(p, dtype == TM_F32 ? 1 : 0, static_cast<hipStream_t>(stream)) == hipSuccess
-               ? TM_OK
-               : TM_ERR_HIP;
+    return with_graph(c, key, static_cast<hipStream_t>(stream), [&](hipStream_t st) {
+        return launch_project(p, dtype == TM_F32 ? 1 : 0, st) == hipSuccess ? TM_OK : TM_ERR_HIP;
+    });
 }
 
 tm_status tm_forward(const tm_ctx* c, void* state, const void* k, const void* v, const void* q,
