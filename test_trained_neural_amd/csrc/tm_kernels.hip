@@ -672,13 +672,26 @@ __device__ __forceinline__ typename Frag<OP>::T tok8(const OP* p, int t0, int b)
     return v;
 }
 
-// tid: the thread's index among the tile's 256 threads.  A tile that is
-// not live (padding of a workgroup that carries two tiles) computes on a
-// valid tile and stores nothing; it still takes part in every barrier.
+// One tile's loaded operands and state, between tile_load and tile_finish.
 template <class OP>
-__device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool live, float (*UM)[65],
-                            float (*US)[65]) {
+struct TileIn {
     typedef typename Frag<OP>::T F;
+    int din, dout, i0, j0;
+    long off;
+    float pa, pe, s0;
+    bool aok[2], bok[2];
+    F fa[2][2], fc[2][2], fd[2][2];   // [k step][block]
+    f32x4 mreg[4], sreg[4];
+};
+
+// tid: the thread's index among the tile's 256 threads.  Every load of the
+// tile, in consumption order: the chunk scalars, the operand fragments (the
+// matrix work waits only for these), then the tile's M and S, whose latency
+// overlaps the matrix work and the LDS exchange.  Every load is
+// unconditional, from a clamped address, so the compiler waits for exactly
+// the loads each step needs; unused values are replaced by zeros.
+template <class OP>
+__device__ __forceinline__ void tile_load(TileIn<OP>& T, const UpdArgs& u, int s, int tile, int tid) {
     const int lane = tid & 63, wave = tid >> 6;
     // the tile's layer and its parameters, picked by compare and select (an
     // index computed at run time into the kernel arguments would become a
@@ -708,12 +721,16 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
         }
     tile -= tb;
     const int ti = tile / tjn, tj = tile - ti * tjn;
-    const int i0 = ti * 64, j0 = tj * 64;
+    T.din = din;
+    T.dout = dout;
+    T.off = off;
+    T.i0 = ti * 64;
+    T.j0 = tj * 64;
     const int b = u.b, bp = u.bp;
-    // the chunk scalars first: every load below is consumed in issue order
     const float* csp = u.cs + (long)s * u.cs_ss + (long)u.chunk * 4;
-    const float pa = csp[0], pe = csp[1], s0 = csp[2];
-
+    T.pa = csp[0];
+    T.pe = csp[1];
+    T.s0 = csp[2];
     // U_M, U_S on the matrix cores: 4 waves as 2 x 2, 32 x 32 each
     const int wi = wave & 1, wj = wave >> 1;
     const int kofs = 8 * (lane >> 4);
@@ -722,45 +739,49 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
     const OP* Bc = reinterpret_cast<const OP*>(dcp) + (long)s * dt_ss;
     const OP* Bd = reinterpret_cast<const OP*>(ddp) + (long)s * dt_ss;
     int ab[2], bb[2];
-    bool aok[2], bok[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-        ab[m] = (i0 >> 4) + wi * 2 + m;     // 16-row blocks of W (packed operand rows)
-        aok[m] = ab[m] * 16 < din;
-        if (!aok[m]) ab[m] = 0;
-        bb[m] = (j0 >> 4) + wj * 2 + m;
-        bok[m] = bb[m] * 16 < dout;
-        if (!bok[m]) bb[m] = 0;
+        ab[m] = (T.i0 >> 4) + wi * 2 + m;     // 16-row blocks of W (packed operand rows)
+        T.aok[m] = ab[m] * 16 < din;
+        if (!T.aok[m]) ab[m] = 0;
+        bb[m] = (T.j0 >> 4) + wj * 2 + m;
+        T.bok[m] = bb[m] * 16 < dout;
+        if (!T.bok[m]) bb[m] = 0;
     }
-    // operand fragments first (vector loads complete in issue order, so
-    // the matrix work below waits only for these), then this tile's M and
-    // S, whose latency overlaps the matrix work and the LDS exchange
-    // (every load is unconditional, from a clamped address, so the compiler
-    // can wait for exactly the loads each step needs; unused values are
-    // replaced by zeros)
-    F fa[2][2], fc[2][2], fd[2][2];   // [k step][block]
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int t0 = ks * 32 + kofs;
         const int kc = min(ks, nkb - 1);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            fa[ks][m] = tok8<OP>(A + pkf(ab[m], kc, nkb, lane), t0, b);
-            fc[ks][m] = tok8<OP>(Bc + pkf(bb[m], kc, nkb, lane), t0, b);
-            fd[ks][m] = tok8<OP>(Bd + pkf(bb[m], kc, nkb, lane), t0, b);
+            T.fa[ks][m] = tok8<OP>(A + pkf(ab[m], kc, nkb, lane), t0, b);
+            T.fc[ks][m] = tok8<OP>(Bc + pkf(bb[m], kc, nkb, lane), t0, b);
+            T.fd[ks][m] = tok8<OP>(Bd + pkf(bb[m], kc, nkb, lane), t0, b);
         }
     }
-    float* Mp = u.M + (long)s * u.P + off;
-    float* Sp = u.S + (long)s * u.P + off;
-    f32x4 mreg[4], sreg[4];
+    const float* Mp = u.M + (long)s * u.P + off;
+    const float* Sp = u.S + (long)s * u.P + off;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int idx = tid + 256 * q;
-        const int gi = min(i0 + (idx >> 4), din - 1), gj = min(j0 + (idx & 15) * 4, dout - 4);
+        const int gi = min(T.i0 + (idx >> 4), din - 1), gj = min(T.j0 + (idx & 15) * 4, dout - 4);
         const long o = (long)gi * dout + gj;
-        mreg[q] = *reinterpret_cast<const f32x4*>(Mp + o);   // outside the layer: not used
-        sreg[q] = *reinterpret_cast<const f32x4*>(Sp + o);
+        T.mreg[q] = *reinterpret_cast<const f32x4*>(Mp + o);   // outside the layer: not used
+        T.sreg[q] = *reinterpret_cast<const f32x4*>(Sp + o);
     }
+}
+
+// The tile's products, the momentum / forgetting write and the bf16 copy.
+// A tile that is not live (padding of a workgroup) computes on a valid tile
+// and stores nothing; it still takes part in every barrier.
+template <class OP>
+__device__ void tile_finish(const TileIn<OP>& T, const UpdArgs& u, int s, int tid, bool live,
+                            float (*UM)[65], float (*US)[65]) {
+    typedef typename Frag<OP>::T F;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wi = wave & 1, wj = wave >> 1;
+    const int nkb = u.bp >> 5;
+    const int din = T.din, dout = T.dout, i0 = T.i0, j0 = T.j0;
     f32x4 am[2][2], as[2][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -771,11 +792,11 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
         if (ks >= nkb) break;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const F av = aok[m] ? fa[ks][m] : zero_frag<OP>();
+            const F av = T.aok[m] ? T.fa[ks][m] : zero_frag<OP>();
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
-                mma(am[m][n], av, bok[n] ? fc[ks][n] : zero_frag<OP>());
-                mma(as[m][n], av, bok[n] ? fd[ks][n] : zero_frag<OP>());
+                mma(am[m][n], av, T.bok[n] ? T.fc[ks][n] : zero_frag<OP>());
+                mma(as[m][n], av, T.bok[n] ? T.fd[ks][n] : zero_frag<OP>());
             }
         }
     }
@@ -792,6 +813,8 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
             }
     __syncthreads();
 
+    float* Mp = u.M + (long)s * u.P + T.off;
+    float* Sp = u.S + (long)s * u.P + T.off;
     bool bad = false;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -800,12 +823,12 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
         const int gi = i0 + i, gj = j0 + j;
         if (live && gi < din && gj < dout) {
             const long o = (long)gi * dout + gj;
-            const f32x4 m = mreg[q], sv = sreg[q];
+            const f32x4 m = T.mreg[q], sv = T.sreg[q];
             f32x4 mn, sn;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                sn[e] = mom_s(pe, sv[e], US[i][j + e]);
-                mn[e] = mom_m(pa, m[e], s0, sv[e], UM[i][j + e]);
+                sn[e] = mom_s(T.pe, sv[e], US[i][j + e]);
+                mn[e] = mom_m(T.pa, m[e], T.s0, sv[e], UM[i][j + e]);
                 bad |= !__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn[e]);
                 UM[i][j + e] = mn[e];
             }
@@ -816,7 +839,7 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
     __syncthreads();
     // the tile of the bf16 forward copy Wt (packed [dout][din]): 4 column
     // blocks x 2 K steps x 64 lanes of 8 consecutive inputs, in memory order
-    bf16* Wp = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P + off;
+    bf16* Wp = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P + T.off;
     for (int idx = tid; idx < 512; idx += 256) {
         const int ln = idx & 63, kk = (idx >> 6) & 1, jb = idx >> 7;
         const int jl = jb * 16 + (ln & 15), il = kk * 32 + 8 * (ln >> 4);
@@ -827,6 +850,8 @@ __device__ void update_tile(const UpdArgs& u, int s, int tile, int tid, bool liv
             *reinterpret_cast<bf16x8*>(Wp + pkf((j0 >> 4) + jb, (i0 >> 5) + kk, din >> 5, ln)) = w;
         }
     }
+    // the LDS tiles are reused by the half's next tile
+    __syncthreads();
     if (__ballot(bad) != 0 && lane == 0 && live) atomicOr(u.flag, 1);
 }
 
@@ -838,7 +863,11 @@ constexpr int RPAD = 1;     // LDS row padding of the partial-sum tiles (floats)
 constexpr int FW = 8;       // waves of a first-layer workgroup
 
 constexpr int FRED = FW / 2;   // partial tiles kept in LDS (two-round reduction)
-constexpr size_t UPD_PAIR_LDS = 2 * 2 * 64 * 65 * 4;   // two update tiles: U_M, U_S each
+constexpr size_t UPD_PAIR_LDS = 2 * 2 * 64 * 65 * 4;   // the two halves' update tiles: U_M, U_S each
+// Update tiles per workgroup: two per half (both tiles' loads in flight
+// together) where the register budget holds them, one per half in the
+// half-occupancy (small) and fp32 variants.
+__host__ __device__ constexpr int upd_tpw(bool f32, bool small) { return (!f32 && !small) ? 4 : 2; }
 
 static size_t first_lds_bytes(int dim, int bp, int f32) {
     const size_t e = f32 ? 4 : 2;
@@ -1035,15 +1064,25 @@ void first_layer_kernel(FirstArgs a) {
             w1_rows<OP>(a, blockIdx.y, (int)blockIdx.x - a.nb1, lds);
             return;
         }
-        // the other layers' update tiles of chunk c-1, two per workgroup
-        // (threads 0..255 and 256..511, each half with its own LDS tiles);
-        // they touch nothing the first-layer blocks read or write
-        const int half = threadIdx.x >> 8;
-        int t = 2 * ((int)blockIdx.x - a.nb1) + half;
-        const bool live = t < a.upd_ntiles;
-        if (!live) t = a.upd_ntiles - 1;
-        float(*UM)[65] = reinterpret_cast<float(*)[65]>(lds) + half * 128;
-        update_tile<OP>(a.u, blockIdx.y, a.upd_tile0 + t, threadIdx.x & 255, live, UM, UM + 64);
+        // the other layers' update tiles of chunk c-1 (only launches that
+        // update a memory of depth three or more have them), TPW per
+        // workgroup: threads 0..255 and 256..511 each take TPW / 2 tiles with
+        // LDS tiles of their own, every tile's loads requested before the
+        // first is computed; they touch nothing the first-layer blocks read
+        // or write
+        if constexpr (UPD && DEEP) {
+            const int half = threadIdx.x >> 8, tid = threadIdx.x & 255;
+            constexpr int TPW = upd_tpw(sizeof(OP) == 4, SMALL);
+            const int t0 = TPW * ((int)blockIdx.x - a.nb1) + half;   // tiles t0, t0 + 2, ...
+            float(*UM)[65] = reinterpret_cast<float(*)[65]>(lds) + half * 128;
+            TileIn<OP> T[TPW / 2];
+#pragma unroll
+            for (int q = 0; q < TPW / 2; ++q)
+                tile_load<OP>(T[q], a.u, blockIdx.y, a.upd_tile0 + min(t0 + 2 * q, a.upd_ntiles - 1), tid);
+#pragma unroll
+            for (int q = 0; q < TPW / 2; ++q)
+                tile_finish<OP>(T[q], a.u, blockIdx.y, tid, t0 + 2 * q < a.upd_ntiles, UM, UM + 64);
+        }
         return;
     }
     const UpdArgs& u = a.u;
@@ -1488,6 +1527,12 @@ void first_layer_kernel(FirstArgs a) {
     if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
 }
 
+// The half-occupancy variant: bf16 with layer-0 and layer-1 widths within
+// SMALL_DIM (the fp32 operand set does not fit half the register file).
+static bool first_small(const FirstArgs& a, bool f32) {
+    return !f32 && a.dim <= SMALL_DIM && (a.u.L < 2 || a.u.dout[1] <= SMALL_DIM);
+}
+
 template <class OP, bool UPD, bool FWD>
 static void launch_first_as(const FirstArgs& a, dim3 grid, size_t lds, hipStream_t st) {
     if constexpr (UPD) {
@@ -1496,8 +1541,7 @@ static void launch_first_as(const FirstArgs& a, dim3 grid, size_t lds, hipStream
             return;
         }
     }
-    // (the fp32 operand set does not fit half the register file)
-    const bool small = sizeof(OP) == 2 && a.dim <= SMALL_DIM && (a.u.L < 2 || a.u.dout[1] <= SMALL_DIM);
+    const bool small = first_small(a, sizeof(OP) == 4);
     if constexpr (sizeof(OP) == 2) {
         if (small) {
             if (a.u.L >= 2)
@@ -1525,7 +1569,9 @@ hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st) {
     if (a.nw1 > 0 && (!a.do_update || a.u.L != 2 || a.upd_ntiles != 0 || a.nw1 % 8 != 0 ||
                       (long)(a.nw1 / 8) * W1_JPW < (a.nb1 + 7) / 8 || a.m1_rd == a.m1_wr))
         return hipErrorInvalidValue;
-    const int pairs = (a.upd_ntiles + 1) / 2;
+    if (a.upd_ntiles > 0 && (!a.do_update || a.u.L < 3)) return hipErrorInvalidValue;
+    const int tpw = upd_tpw(f32, first_small(a, f32));
+    const int pairs = (a.upd_ntiles + tpw - 1) / tpw;   // workgroups of update tiles
     dim3 grid(a.nb1 + (a.nw1 > 0 ? a.nw1 : pairs), ns);
     size_t lds = first_lds_bytes(a.dim, a.u.bp, f32);
     if (pairs > 0 && lds < UPD_PAIR_LDS) lds = UPD_PAIR_LDS;
