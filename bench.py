@@ -36,12 +36,16 @@ METRIC = "memory tokens/sec (store+retrieve) at dim 384, chunk 64; MFMA util %"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
-KERNEL_SOURCE = os.path.join(ROOT, "test_trained_neural_amd", "csrc", "tm_kernels.hip")
+# the sources of the chunk-step kernels: the device helpers, then the kernels
+KERNEL_SOURCES = [os.path.join(ROOT, "test_trained_neural_amd", "csrc", f) for f in ("tm_device.h", "tm_kernels.hip")]
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------
@@ -117,7 +121,7 @@ def read_traffic(kernel, workload):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"kernel source sha256\[:16\]: `([0-9a-f]+)`", text)
+    m = re.search(r"kernel source sha256\[:16\][^`]*`([0-9a-f]+)`", text)
     t = re.search(r"HBM bytes per launch: ([0-9.eE+]+)", text)
     if not m or not t or m.group(1) != kernel_source_hash():
         return None
