@@ -29,7 +29,12 @@
  *    weights after chunk c has been written (read mode 0), or, the variant in
  *    which the queries read the memory before the chunk writes to it ("Attack
  *    of the Titans", the memory-as-context architecture), through the weights
- *    chunk c started with (read mode 1).
+ *    chunk c started with (read mode 1).  Read mode 2 reads every query
+ *    through the memory right after its own token's write: inside a chunk the
+ *    weights still move token by token (only the gradients sit at the chunk
+ *    start), and query t sees them as they stand after token t, the way a
+ *    linear-attention output is a lookup in a matrix memory updated at every
+ *    step ("Attack of the Titans", the long-term memory section).
  *
  * Everything is fp64.  Inputs arrive as float32 arrays (bf16 inputs are passed
  * already widened, which is exact) and are widened to double on use.
@@ -182,7 +187,8 @@ typedef struct {
     double* state;
     double* y;            /* NULL: store only */
     int retrieve_only;
-    int read;                 /* 0: queries after the chunk's write; 1: before */
+    int read;                 /* 0: queries after the chunk's write; 1: before;
+                                 2: each after its own token's write */
     int tid, nthreads;
     int err;
 } job_t;
@@ -244,6 +250,12 @@ static void* run_streams(void* arg) {
                 double th = J->theta[row], et = J->eta[row], al = J->alpha[row];
                 for (long p = 0; p < P; p++) S[p] = et * S[p] - th * G[p];
                 for (long p = 0; p < P; p++) M[p] = (1.0 - al) * M[p] + S[p];
+                if (J->y && J->read == 2) {
+                    /* query t through the memory as token t left it */
+                    widen(kk, J->q + row * d, d);
+                    mlp_row_forward(m, M, kk, act, pre, out);
+                    memcpy(J->y + row * d, out, sizeof(double) * d);
+                }
             }
             if (J->y && J->read == 0) {
                 /* read the chunk's queries through the freshly written memory */
@@ -291,8 +303,9 @@ static int run(int dim, int depth, int expansion, int chunk, int batch, int head
 }
 
 /* Store the call's n_tokens into the memory (and, if y != NULL, read the
- * queries chunk by chunk: read = 0 through the memory after the chunk's
- * write, read = 1 through the memory the chunk started with).  state is
+ * queries: read = 0 chunk by chunk through the memory after the chunk's
+ * write, read = 1 through the memory the chunk started with, read = 2 each
+ * through the memory right after its own token's write).  state is
  * updated in place.  Returns 0, -1 (bad sizes or mode), -2 (out of memory),
  * -3 (n_tokens not a multiple of chunk). */
 int tmref_forward_read(int dim, int depth, int expansion, int chunk, int batch, int heads,
@@ -300,7 +313,7 @@ int tmref_forward_read(int dim, int depth, int expansion, int chunk, int batch, 
                        const float* theta, const float* eta, const float* alpha,
                        double* state, double* y, int read, int n_threads) {
     if (y && !q) return -1;
-    if (read != 0 && read != 1) return -1;
+    if (read < 0 || read > 2) return -1;
     return run(dim, depth, expansion, chunk, batch, heads, n_tokens, k, v, q,
                theta, eta, alpha, state, y, 0, read, n_threads);
 }

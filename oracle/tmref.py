@@ -86,7 +86,7 @@ def mlp_grad(dim, depth, expansion, W, k, v):
     return G, float(loss[0])
 
 
-READ_MODES = {"after": 0, "before": 1}
+READ_MODES = {"after": 0, "before": 1, "token": 2}
 
 
 def forward(dim, depth, expansion, chunk, state, k, v, theta, eta, alpha, q=None,
@@ -94,8 +94,9 @@ def forward(dim, depth, expansion, chunk, state, k, v, theta, eta, alpha, q=None
     """Store the call's tokens into ``state`` (fp64 [streams][2P], updated in
     place); if ``q`` is given also return y [B][T][H][d] read chunk by chunk,
     through the memory after the chunk's write (read="after") or the memory
-    the chunk started with (read="before").  k, v, q: [B][T][H][d]; gates
-    [B][T][H]."""
+    the chunk started with (read="before"), or each query through the memory
+    as its own token's write left it (read="token").  k, v, q: [B][T][H][d];
+    gates [B][T][H]."""
     k, v, q = _f32(k), _f32(v), _f32(q)
     theta, eta, alpha = _f32(theta), _f32(eta), _f32(alpha)
     B, T, H, d = k.shape

@@ -412,6 +412,116 @@ def test_read_before_write_sees_the_chunk_start_weights():
     assert np.array_equal(ya, yb)
 
 
+def chunk_coefficients(th, et, al):
+    """Brute-force coefficients of the memory after token t of a chunk whose
+    gradients all sit at the chunk-start weights (M_0, S_0), from unrolling
+    S_u = eta_u S_{u-1} - theta_u G_u and M_u = (1 - alpha_u) M_{u-1} + S_u:
+    M_t = pm[t] M_0 + ps[t] S_0 - sum_{i <= t} c[t, i] G_i, every product
+    written out (no recurrence)."""
+    b = len(th)
+    prod = lambda xs: float(np.prod(xs)) if len(xs) else 1.0
+    pm = np.array([prod(1.0 - al[:t + 1]) for t in range(b)])
+    ps = np.array([sum(prod(1.0 - al[u + 1:t + 1]) * prod(et[:u + 1]) for u in range(t + 1)) for t in range(b)])
+    c = np.zeros((b, b))
+    for t in range(b):
+        for i in range(t + 1):
+            c[t, i] = th[i] * sum(prod(1.0 - al[u + 1:t + 1]) * prod(et[i + 1:u + 1]) for u in range(i, t + 1))
+    return pm, ps, c
+
+
+def test_per_token_read_linear_dual_form():
+    # every query read right after its own token's write.  For the linear
+    # memory this is a causal, linear-attention-like sum over the chunk's
+    # earlier tokens and the token itself (the dual form): with
+    # G_i = 2 k_i^T (k_i M_0 - v_i) at the chunk-start weights,
+    #   y_t = pm_t q_t M_0 + ps_t q_t S_0 - sum_{i <= t} c_ti 2 (q_t . k_i)(k_i M_0 - v_i),
+    # coefficients from the brute-force products above.  Checked over three
+    # chunks with nonzero momentum, forgetting and S_0.
+    rng = np.random.default_rng(23)
+    d, b, C = 5, 4, 3
+    k, v, q, (th, et, al) = rand_inputs(rng, 1, b * C, 1, d)
+    st = rand_state(rng, 1, d * d, 0.5, 0.2)
+    M = st[0, :d * d].reshape(d, d).copy()
+    S = st[0, d * d:].reshape(d, d).copy()
+    y = tmref.forward(d, 1, 1, b, st, k, v, th, et, al, q=q, read="token")
+    for c0 in range(0, b * C, b):
+        K = k[0, c0:c0 + b, 0].astype(np.float64)
+        V = v[0, c0:c0 + b, 0].astype(np.float64)
+        Q = q[0, c0:c0 + b, 0].astype(np.float64)
+        pm, ps, cf = chunk_coefficients(*(g[0, c0:c0 + b, 0].astype(np.float64) for g in (th, et, al)))
+        E = K @ M - V
+        for t in range(b):
+            want = pm[t] * Q[t] @ M + ps[t] * Q[t] @ S
+            for i in range(t + 1):
+                want = want - cf[t, i] * 2.0 * float(Q[t] @ K[i]) * E[i]
+            np.testing.assert_allclose(y[0, c0 + t, 0], want, rtol=1e-11, atol=1e-13)
+        # the chunk's end state from the same coefficients (c at t = b-1 and
+        # the momentum's own products)
+        G = [2.0 * np.outer(K[i], E[i]) for i in range(b)]
+        pe = float(np.prod(et[0, c0:c0 + b, 0].astype(np.float64)))
+        dS = [float(th[0, c0 + i, 0]) * float(np.prod(et[0, c0 + i + 1:c0 + b, 0].astype(np.float64)))
+              for i in range(b)]
+        M, S = (pm[-1] * M + ps[-1] * S - sum(cf[-1, i] * G[i] for i in range(b)),
+                pe * S - sum(dS[i] * G[i] for i in range(b)))
+    np.testing.assert_allclose(st[0, :d * d].reshape(d, d), M, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(st[0, d * d:].reshape(d, d), S, rtol=1e-11, atol=1e-13)
+
+
+def test_per_token_read_delta_rule_special_case():
+    # eta = alpha = 0, S_0 = 0: the memory after token t of the chunk is
+    # M_0 - sum_{i <= t} theta_i G_i (the chunked delta rule), so
+    # y_t = q_t M_0 - sum_{i <= t} 2 theta_i (q_t . k_i)(k_i M_0 - v_i);
+    # token t's own write is included (i = t), later ones are not
+    rng = np.random.default_rng(24)
+    d, b = 4, 6
+    k, v, q, (th, _, _) = rand_inputs(rng, 1, b, 1, d)
+    z = np.zeros_like(th)
+    st = rand_state(rng, 1, d * d, 0.5, 0.0)
+    M0 = st[0, :d * d].reshape(d, d).copy()
+    y = tmref.forward(d, 1, 1, b, st, k, v, th, z, z, q=q, read="token")
+    K, V, Q = (a[0, :, 0].astype(np.float64) for a in (k, v, q))
+    for t in range(b):
+        want = Q[t] @ M0 - sum(2.0 * float(th[0, i, 0]) * float(Q[t] @ K[i]) * (K[i] @ M0 - V[i])
+                               for i in range(t + 1))
+        np.testing.assert_allclose(y[0, t, 0], want, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("depth", [2, 3])
+def test_per_token_read_mlp_against_autograd(depth):
+    # an MLP memory stepped token by token with torch.autograd gradients at
+    # each chunk's start weights, every query read through the weights right
+    # after its token; also: the read order changes no write, the last query
+    # of each chunk reads what the after-the-write order reads, and a chunk
+    # of one token makes the two orders the same
+    rng = np.random.default_rng(25 + depth)
+    d, ex, b, T = 4, 2, 4, 12
+    dims = dims_of(d, depth, ex)
+    P = tmref.param_count(d, depth, ex)
+    k, v, q, (th, et, al) = rand_inputs(rng, 1, T, 1, d)
+    st0 = rand_state(rng, 1, P, 0.5, 0.1)
+    st = st0.copy()
+    y = tmref.forward(d, depth, ex, b, st, k, v, th, et, al, q=q, read="token")
+    M, S = st0[0, :P].copy(), st0[0, P:].copy()
+    for c0 in range(0, T, b):
+        M0 = M.copy()
+        for t in range(c0, c0 + b):
+            G = torch_grad(M0, k[0, t, 0].astype(np.float64), v[0, t, 0].astype(np.float64), dims)
+            S = float(et[0, t, 0]) * S - float(th[0, t, 0]) * G
+            M = (1.0 - float(al[0, t, 0])) * M + S
+            np.testing.assert_allclose(y[0, t, 0], torch_fwd(M, q[0, t, 0].astype(np.float64), dims),
+                                       rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(st[0], np.concatenate([M, S]), rtol=1e-11, atol=1e-13)
+    sa = st0.copy()
+    ya = tmref.forward(d, depth, ex, b, sa, k, v, th, et, al, q=q, read="after")
+    assert np.array_equal(st, sa)
+    for c0 in range(0, T, b):
+        assert np.array_equal(y[:, c0 + b - 1], ya[:, c0 + b - 1])
+    s1, s2 = st0.copy(), st0.copy()
+    y1 = tmref.forward(d, depth, ex, 1, s1, k, v, th, et, al, q=q, read="token")
+    y2 = tmref.forward(d, depth, ex, 1, s2, k, v, th, et, al, q=q, read="after")
+    assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
+
+
 def test_retrieve_is_read_only_and_is_a_forward_pass():
     rng = np.random.default_rng(12)
     d, ex, depth = 5, 2, 3
