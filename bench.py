@@ -408,6 +408,8 @@ def main():
             "deep512": other_workload("deep512", 2, calls=16),
             # the same step with each chunk's queries read before its write
             "mlp384_read_before_write": other_workload("mlp384", 20, read=1),
+            # each query read right after its own token's write (the dual form)
+            "mlp384_read_per_token": other_workload("mlp384", 20, read=2),
         }
         side = input_side("mlp384", 20)
         out["other_workloads"]["mlp384_input_side"] = side["input_side"]

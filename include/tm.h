@@ -64,7 +64,8 @@ typedef enum { TM_F32 = 0, TM_BF16 = 1 } tm_dtype;
 /* When a chunk's queries read the memory in tm_forward_ex. */
 typedef enum {
     TM_READ_AFTER_WRITE = 0,   /* through the memory after the chunk's write (tm_forward) */
-    TM_READ_BEFORE_WRITE = 1   /* through the memory the chunk started with */
+    TM_READ_BEFORE_WRITE = 1,  /* through the memory the chunk started with */
+    TM_READ_PER_TOKEN = 2      /* each query through the memory right after its own token's write */
 } tm_read;
 
 typedef struct tm_ctx tm_ctx;
@@ -124,8 +125,17 @@ tm_status tm_forward(const tm_ctx* ctx, void* state, const void* k, const void* 
  * a context, and "Titans, explained" step 8, where a segment's tokens query
  * the memory before it is updated).  Equivalent to alternating tm_retrieve
  * and tm_store chunk by chunk; the state it leaves is bitwise that of
- * tm_forward.  An unknown read value gives TM_ERR_INVALID; everything else as
- * for tm_forward. */
+ * tm_forward.  TM_READ_PER_TOKEN: query t (of the chunk holding token t)
+ * reads the memory as token t's write left it, within the chunk too: the
+ * gradients stay at the chunk-start weights, but the momentum and forgetting
+ * have advanced token by token ("Attack of the Titans", the long-term memory
+ * section: a linear-attention output is a lookup in a memory updated at
+ * every step; Technical Details / Parallel training for the chunking).  It
+ * is computed by the dual form: the chunk start's products of the queries
+ * plus a causal b x b correction per layer, in 2 depth + 1 extra launches
+ * per chunk; W_1's update then stays in the first-layer blocks.  The last
+ * query of each chunk reads what TM_READ_AFTER_WRITE reads.  An unknown read
+ * value gives TM_ERR_INVALID; everything else as for tm_forward. */
 tm_status tm_forward_ex(const tm_ctx* ctx, void* state, const void* k, const void* v,
                         const void* q, const float* theta, const float* eta,
                         const float* alpha, float* y, int batch, int heads,
@@ -203,7 +213,8 @@ tm_status tm_w1_split_enable(int on);
  * Kernel classes: 0 coefficient scan (and key transpose), 1 chunk forward
  * products of layers 1.., 2 chunk backward products, 3 gradient reduction +
  * state update of layers 1.., 4 first-layer step (the first layer's update,
- * its in-place backward, and its forward).  While bit c of
+ * its in-place backward, and its forward), 5 the per-token read's products.
+ * While bit c of
  * class_mask is set, every launch of class c is bracketed by a pair of HIP
  * events recorded on its launch stream (mask 0 turns timing off).
  * tm_timing_read waits for the recorded launches and returns, for one class,

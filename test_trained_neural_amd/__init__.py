@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libtm.so")
 
 TM_OK, TM_ERR_INVALID, TM_ERR_SHAPE, TM_ERR_DTYPE, TM_ERR_STATE, TM_ERR_HIP = 0, -1, -2, -3, -4, -5
 TM_F32, TM_BF16 = 0, 1
-TM_READ_AFTER_WRITE, TM_READ_BEFORE_WRITE = 0, 1
+TM_READ_AFTER_WRITE, TM_READ_BEFORE_WRITE, TM_READ_PER_TOKEN = 0, 1, 2
 
 EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_workspace_bytes",
             "tm_state_init", "tm_store", "tm_retrieve", "tm_forward", "tm_state_export",
@@ -28,7 +28,7 @@ EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_w
             "tm_graphs_enable", "tm_w1_split_enable", "tm_forward_ex", "tm_project")
 
 # kernel classes of tm_timing_enable / tm_timing_read
-K_SCAN, K_FWD, K_BWD, K_UPDATE, K_FIRST = 0, 1, 2, 3, 4
+K_SCAN, K_FWD, K_BWD, K_UPDATE, K_FIRST, K_TOKEN_READ = 0, 1, 2, 3, 4, 5
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -181,7 +181,8 @@ def tm_forward(ctx, state, k, v, q, theta, eta, alpha, y, workspace, stream=None
 
 
 def tm_forward_ex(ctx, state, k, v, q, theta, eta, alpha, y, workspace, read, stream=None):
-    """read: TM_READ_AFTER_WRITE (as tm_forward) or TM_READ_BEFORE_WRITE."""
+    """read: TM_READ_AFTER_WRITE (as tm_forward), TM_READ_BEFORE_WRITE or
+    TM_READ_PER_TOKEN."""
     _tok(k, v, q, theta, eta, alpha, y)
     B, T, H, _ = k.shape
     _check("tm_forward_ex", lib().tm_forward_ex(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(q), _ptr(theta),
@@ -295,7 +296,8 @@ class NeuralMemory:
 
     def __call__(self, state, k, v, q, theta, eta, alpha, read=TM_READ_AFTER_WRITE):
         """Store + retrieve; read: when each chunk's queries read the memory
-        (TM_READ_AFTER_WRITE, the default, or TM_READ_BEFORE_WRITE)."""
+        (TM_READ_AFTER_WRITE, the default, TM_READ_BEFORE_WRITE or
+        TM_READ_PER_TOKEN)."""
         B, T, H, d = k.shape
         y = torch.empty((B, T, H, d), dtype=torch.float32, device=self.device)
         tm_forward_ex(self.ctx, state.buf, k, v, q, theta, eta, alpha, y, self.workspace(B, H, T), read)

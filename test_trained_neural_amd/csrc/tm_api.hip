@@ -65,8 +65,9 @@ StateLayout state_layout(const tm_ctx* c, long ns) {
 // sized in 4-byte elements so either operand type fits.
 struct WsLayout {
     size_t cc, dc, cs, act[MAXL], dsl[MAXL], dlp[MAXL], kt, xk, xq, ht[MAXL], dct[MAXL], ddt[MAXL], ht1[2],
-        m1x, ret[2], total;
-    long coef_ss, cs_ss, act_ss, dsl_ss, dlp_ss[MAXL], kt_ss, x_ss, xc, ht_ss, dt_ss[MAXL], ret_ss, ret_rows;
+        m1x, r3x[2], r3c, r3p, ret[2], total;
+    long coef_ss, cs_ss, act_ss, dsl_ss, dlp_ss[MAXL], kt_ss, x_ss, xc, ht_ss, dt_ss[MAXL], r3x_ss, r3c_ss, r3p_ss,
+        ret_ss, ret_rows;
     int bp, C;
 };
 
@@ -88,8 +89,9 @@ WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
         w.act[l] = o; o += al256((size_t)ns * w.act_ss * 4);
         w.dsl[l] = o; o += al256((size_t)ns * w.dsl_ss * 4);
     }
-    // Delta of layers 1.. (packed [b][dout]; layer 0's is formed in place)
-    for (int l = 1; l < c->L; ++l) {
+    // Delta of every layer (packed [b][dout]).  The store forms layer 0's
+    // in place; the per-token read writes it here.
+    for (int l = 0; l < c->L; ++l) {
         w.dlp_ss[l] = pk_size(b, c->dout[l]);
         w.dlp[l] = o; o += al256((size_t)ns * w.dlp_ss[l] * 4);
     }
@@ -122,6 +124,19 @@ WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
     if (c->L == 2) {
         w.m1x = o; o += al256((size_t)ns * c->din[1] * c->dout[1] * 4);
     }
+    // per-token read: the query rows' hidden layers (ping-pong, packed
+    // [b][h]), the correction's coefficient-scaled scores (packed [b][bp]) and
+    // the rows' pm_t, ps_t
+    if (c->L >= 2) {
+        w.r3x_ss = pk_size(b, h);
+        for (int i = 0; i < 2; ++i) {
+            w.r3x[i] = o; o += al256((size_t)ns * w.r3x_ss * 4);
+        }
+    }
+    w.r3c_ss = pk_size(b, w.bp);
+    w.r3c = o; o += al256((size_t)ns * w.r3c_ss * 4);
+    w.r3p_ss = 2 * b;
+    w.r3p = o; o += al256((size_t)ns * w.r3p_ss * 4);
     size_t fwd_total = o;
     // retrieve: ping-pong activations of up to RET_ROWS query rows (packed)
     w.ret_rows = T < RET_ROWS ? T : RET_ROWS;
@@ -163,7 +178,7 @@ hipError_t compute_units(int* out) {
 }
 
 // ---- optional per-launch timing (tm_timing_enable / tm_timing_read) ----
-enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_UPD = 3, K_FIRST = 4, K_CLASSES = 5 };
+enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_UPD = 3, K_FIRST = 4, K_R3 = 5, K_CLASSES = 6 };
 struct Timed {
     hipEvent_t a, b;
     int kind;
@@ -475,6 +490,108 @@ tm_status run_backward(const tm_ctx* c, char* state, long ns, const WsLayout& w,
     return TM_OK;
 }
 
+// Per-token read of chunk ci (every query through the memory as its own
+// token's write left it), between the chunk's forward / backward and the
+// step that writes it, so the state still holds the chunk-start weights:
+// layer 0's Delta of the keys, then per layer the coefficient-scaled scores
+// and the layer's rows (the last layer writes y).
+tm_status run_token_read(const tm_ctx* c, char* state, long ns, const WsLayout& w, char* ws,
+                         const TokLayout& tl, int ci, const void* v, const float* theta, const float* eta,
+                         const float* alpha, float* y, int n_tokens, int heads, bool f32, hipStream_t st) {
+    const int b = c->chunk;
+    const size_t esz = f32 ? 4 : 2;
+    StateLayout sl = state_layout(c, ns);
+    const float* Mst = reinterpret_cast<const float*>(state + sl.M);
+    const float* Sst = reinterpret_cast<const float*>(state + sl.S);
+    const char* xq = ws + w.xq + (size_t)ci * w.xc * esz;
+    const char* xk = ws + w.xk + (size_t)ci * w.xc * esz;
+    R3Args r;
+    memset(&r, 0, sizeof(r));
+    r.b = b;
+    r.bp = w.bp;
+    r.ms_ss = c->P;
+    r.tl = tl;
+    // Delta of layer 0 for the chunk's keys
+    if (c->L == 1) {
+        r.bl = BL_CF0;
+        r.K = c->dim;
+        r.N = c->dim;
+        r.a = xk;
+        r.a_ss = w.x_ss;
+        r.M = Mst;
+        r.v = v;
+        r.vt0 = ci * b;
+    } else {
+        r.bl = BL_CF1T;
+        r.K = c->dout[1];
+        r.N = c->dout[0];
+        r.a = ws + w.dlp[1];
+        r.a_ss = w.dlp_ss[1];
+        r.M = Mst + c->off[1];
+        r.dsl = reinterpret_cast<const float*>(ws + w.dsl[0]);
+        r.dsl_ss = w.dsl_ss;
+        r.dsl_ld = c->hidden;
+    }
+    r.out = ws + w.dlp[0];
+    r.out_ss = w.dlp_ss[0];
+    if (timed(K_R3, st, [&] { return launch_r3(r, R3_DELTA, (int)ns, f32 ? 1 : 0, st); }) != hipSuccess)
+        return TM_ERR_HIP;
+    float* pq = reinterpret_cast<float*>(ws + w.r3p);
+    for (int l = 0; l < c->L; ++l) {
+        memset(&r, 0, sizeof(r));
+        r.b = b;
+        r.bp = w.bp;
+        r.K = c->din[l];
+        r.N = c->dout[l];
+        r.tl = tl;
+        if (l == 0) {
+            r.a = xq;
+            r.a_ss = w.x_ss;
+            r.hk = xk;
+            r.hk_ss = w.x_ss;
+        } else {
+            // the keys' rows of the store's forward (no query rows: keys from row 0)
+            r.a = ws + w.r3x[(l - 1) & 1];
+            r.a_ss = w.r3x_ss;
+            r.hk = ws + w.act[l - 1];
+            r.hk_ss = w.act_ss;
+        }
+        // the coefficient-scaled scores (and, with layer 0, pm_t and ps_t)
+        r.theta = theta;
+        r.eta = eta;
+        r.alpha = alpha;
+        r.gl = TokLayout{n_tokens, heads, 1};
+        r.g0 = ci * b;
+        r.pq = l == 0 ? pq : nullptr;
+        r.pq_ss = w.r3p_ss;
+        r.out = ws + w.r3c;
+        r.out_ss = w.r3c_ss;
+        if (timed(K_R3, st, [&] { return launch_r3(r, R3_SCORE, (int)ns, f32 ? 1 : 0, st); }) != hipSuccess)
+            return TM_ERR_HIP;
+        // the layer's rows
+        r.bl = l == 0 ? BL_CF0 : l == 1 ? BL_CF1 : BL_ROW;
+        r.M = Mst + c->off[l];
+        r.S = Sst + c->off[l];
+        r.ms_ss = c->P;
+        r.sc = ws + w.r3c;
+        r.sc_ss = w.r3c_ss;
+        r.dl = ws + w.dlp[l];
+        r.dl_ss = w.dlp_ss[l];
+        r.pq = pq;
+        if (l + 1 < c->L) {
+            r.out = ws + w.r3x[l & 1];
+            r.out_ss = w.r3x_ss;
+        } else {
+            r.out = nullptr;
+            r.y = y;
+            r.yt0 = ci * b;
+        }
+        if (timed(K_R3, st, [&] { return launch_r3(r, R3_LAYER, (int)ns, f32 ? 1 : 0, st); }) != hipSuccess)
+            return TM_ERR_HIP;
+    }
+    return TM_OK;
+}
+
 // The call's chunk loop.  Step c (0..C) is one launch of the step kernel:
 // chunk c-1's update of every layer (the first layer's Delta formed in
 // place) and chunk c's first-layer forward of [queries of chunk c-1; keys of
@@ -484,7 +601,7 @@ tm_status run_backward(const tm_ctx* c, char* state, long ns, const WsLayout& w,
 tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v, const void* q,
                     const float* theta, const float* eta, const float* alpha, float* y, int batch,
                     int heads, int n_tokens, tm_dtype dtype, void* ws_v, hipStream_t st,
-                    bool read_before = false) {
+                    int read = TM_READ_AFTER_WRITE) {
     char* state = static_cast<char*>(state_v);
     char* ws = static_cast<char*>(ws_v);
     const long ns = (long)batch * heads;
@@ -570,7 +687,9 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     float* m1_ws = c->L == 2 ? reinterpret_cast<float*>(ws + w.m1x) : nullptr;
     const long p1 = c->L >= 2 ? (long)c->din[1] * c->dout[1] : 0;
     int nw1 = 0;
-    if (c->L == 2 && g_w1_split) {
+    // (the per-token read takes W_1's chunk-start M from the state, so its
+    // update stays in place there)
+    if (c->L == 2 && g_w1_split && read != TM_READ_PER_TOKEN) {
         // a multiple of 8 workgroups, W1_JPW row blocks each per XCD residue
         const int n1 = 8 * (((a.nb1 + 7) / 8 + W1_JPW - 1) / W1_JPW);
         int cus = 0;
@@ -582,8 +701,9 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         // queries: chunk ci-1's through the memory after its write (rows of
         // step ci), or chunk ci's through the memory before its write (the
         // same rows as chunk ci's keys)
-        const int cq = read_before ? ci : ci - 1;
-        const bool has_q = q && cq >= 0 && cq < C;
+        const int cq = read == TM_READ_BEFORE_WRITE ? ci : ci - 1;
+        // (per-token: the queries go through run_token_read, not these rows)
+        const bool has_q = q && read != TM_READ_PER_TOKEN && cq >= 0 && cq < C;
         a.do_update = ci >= 1;
         a.last_update = ci == C;
         a.nq = has_q ? b : 0;
@@ -643,6 +763,11 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         }
         if (ci < C && c->L >= 3) {
             tm_status rc = run_backward(c, state, ns, w, ws, tl, ci, f32, st);
+            if (rc != TM_OK) return rc;
+        }
+        if (ci < C && read == TM_READ_PER_TOKEN && q) {
+            tm_status rc = run_token_read(c, state, ns, w, ws, tl, ci, v, theta, eta, alpha, y, n_tokens, heads,
+                                          f32, st);
             if (rc != TM_OK) return rc;
         }
     }
@@ -758,18 +883,18 @@ tm_status tm_forward_ex(const tm_ctx* c, void* state, const void* k, const void*
                         int heads, int n_tokens, tm_dtype dtype, tm_read read, void* ws, void* stream) {
     tm_status rc = check_common(c, state, batch, heads, n_tokens, dtype, ws);
     if (rc != TM_OK) return rc;
-    if (read != TM_READ_AFTER_WRITE && read != TM_READ_BEFORE_WRITE) return TM_ERR_INVALID;
+    if (read != TM_READ_AFTER_WRITE && read != TM_READ_BEFORE_WRITE && read != TM_READ_PER_TOKEN)
+        return TM_ERR_INVALID;
     if (n_tokens == 0) return TM_OK;
     if (!tok_ok(k) || !tok_ok(v) || !tok_ok(q) || !tok_ok(y) || !gate_ok(theta) || !gate_ok(eta) ||
         !gate_ok(alpha))
         return TM_ERR_INVALID;
     if (n_tokens % c->chunk != 0) return TM_ERR_SHAPE;
-    const bool before = read == TM_READ_BEFORE_WRITE;
-    return with_graph(c, make_key(before ? 4 : 2, batch, heads, n_tokens, dtype,
-                                  {state, k, v, q, theta, eta, alpha, y, ws}),
+    const int kind = read == TM_READ_BEFORE_WRITE ? 4 : read == TM_READ_PER_TOKEN ? 6 : 2;
+    return with_graph(c, make_key(kind, batch, heads, n_tokens, dtype, {state, k, v, q, theta, eta, alpha, y, ws}),
                       static_cast<hipStream_t>(stream), [&](hipStream_t st) {
         return run_store(c, state, k, v, q, theta, eta, alpha, y, batch, heads, n_tokens, dtype, ws, st,
-                         before);
+                         (int)read);
     });
 }
 

@@ -85,9 +85,11 @@ def test_call_validation_before_launch():
     assert L.tm_forward(c, A, None, None, None, None, None, None, None, 1, 1, 0, T.TM_BF16, A, st) == T.TM_OK
     assert L.tm_retrieve(c, A, None, None, 1, 1, 0, T.TM_F32, A, st) == T.TM_OK
     # the read order: only the two defined values
-    for bad in (-1, 2):
+    for bad in (-1, 3):
         assert L.tm_forward_ex(c, A, A, A, A, G, G, G, A, 1, 1, 16, T.TM_BF16, bad, A, st) == T.TM_ERR_INVALID
     assert L.tm_forward_ex(c, A, A, A, A, G, G, G, A, 1, 1, 17, T.TM_BF16, T.TM_READ_BEFORE_WRITE, A, st) == \
+        T.TM_ERR_SHAPE
+    assert L.tm_forward_ex(c, A, A, A, A, G, G, G, A, 1, 1, 17, T.TM_F32, T.TM_READ_PER_TOKEN, A, st) == \
         T.TM_ERR_SHAPE
     assert L.tm_forward_ex(c, A, None, None, None, None, None, None, None, 1, 1, 0, T.TM_BF16,
                            T.TM_READ_BEFORE_WRITE, A, st) == T.TM_OK
