@@ -262,6 +262,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mlp384")
+    ap.add_argument("--read", choices=("after", "before", "token"), default="after",
+                    help="the queries' read order (after the chunk's write: tm_forward, the headline step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the other workloads' throughput")
     ap.add_argument("--calib-copy", action="store_true",
@@ -295,9 +297,14 @@ def main():
     ws = torch.empty(T.tm_workspace_bytes(ctx, Bn, H, Tn), dtype=torch.uint8, device=dev)
     y = torch.empty((Bn, Tn, H, d), dtype=torch.float32, device=dev)
 
+    read = {"after": None, "before": T.TM_READ_BEFORE_WRITE, "token": T.TM_READ_PER_TOKEN}[args.read]
+
     def step():
         T.tm_state_init(ctx, state, Bn, H, init)
-        T.tm_forward(ctx, state, k, v, q, th, et, al, y, ws)
+        if read is None:
+            T.tm_forward(ctx, state, k, v, q, th, et, al, y, ws)
+        else:
+            T.tm_forward_ex(ctx, state, k, v, q, th, et, al, y, ws, read)
 
     for _ in range(args.warmup):
         step()
@@ -394,7 +401,8 @@ def main():
         "data": "synthetic (seeded; shapes of the README example, gates with fixed logit offsets)",
         "config": {"workload": wl.name, "batch": Bn, "seq": Tn, "heads": H, "dim": d,
                    "hidden": wl.hidden, "depth": wl.depth, "chunk": wl.chunk,
-                   "step": "tm_state_init + tm_forward (store + retrieve)"},
+                   "step": "tm_state_init + tm_forward (store + retrieve)" if read is None else
+                           "tm_state_init + tm_forward_ex(read=%s) (store + retrieve)" % args.read},
         "roofline": roof,
         "kernels": kernels,
     }

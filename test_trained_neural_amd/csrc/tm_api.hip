@@ -66,8 +66,8 @@ StateLayout state_layout(const tm_ctx* c, long ns) {
 struct WsLayout {
     size_t cc, dc, cs, act[MAXL], dsl[MAXL], dlp[MAXL], kt, xk, xq, ht[MAXL], dct[MAXL], ddt[MAXL], ht1[2],
         m1x, r3x[2], r3c, r3p, ret[2], total;
-    long coef_ss, cs_ss, act_ss, dsl_ss, dlp_ss[MAXL], kt_ss, x_ss, xc, ht_ss, dt_ss[MAXL], r3x_ss, r3c_ss, r3p_ss,
-        ret_ss, ret_rows;
+    long coef_ss, cs_ss, act_ss, dsl_ss, dlp_ss[MAXL], kt_ss, x_ss, xc, ht_ss, dt_ss[MAXL], r3x_ss, r3c_ss, r3c_cs,
+        r3p_ss, ret_ss, ret_rows;
     int bp, C;
 };
 
@@ -89,9 +89,8 @@ WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
         w.act[l] = o; o += al256((size_t)ns * w.act_ss * 4);
         w.dsl[l] = o; o += al256((size_t)ns * w.dsl_ss * 4);
     }
-    // Delta of every layer (packed [b][dout]).  The store forms layer 0's
-    // in place; the per-token read writes it here.
-    for (int l = 0; l < c->L; ++l) {
+    // Delta of layers 1.. (packed [b][dout]; layer 0's is formed in place)
+    for (int l = 1; l < c->L; ++l) {
         w.dlp_ss[l] = pk_size(b, c->dout[l]);
         w.dlp[l] = o; o += al256((size_t)ns * w.dlp_ss[l] * 4);
     }
@@ -133,9 +132,12 @@ WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
             w.r3x[i] = o; o += al256((size_t)ns * w.r3x_ss * 4);
         }
     }
-    w.r3c_ss = pk_size(b, w.bp);
+    // C of layer 0 for every chunk of the call, then one more for the layer
+    // being read (fp32 [16 ceil(b/16)][bp] each); pm_t, ps_t of every chunk
+    w.r3c_cs = ((b + 15) / 16 * 16) * w.bp;
+    w.r3c_ss = (C + 1) * w.r3c_cs;
     w.r3c = o; o += al256((size_t)ns * w.r3c_ss * 4);
-    w.r3p_ss = 2 * b;
+    w.r3p_ss = C * 2 * b;
     w.r3p = o; o += al256((size_t)ns * w.r3p_ss * 4);
     size_t fwd_total = o;
     // retrieve: ping-pong activations of up to RET_ROWS query rows (packed)
@@ -490,54 +492,55 @@ tm_status run_backward(const tm_ctx* c, char* state, long ns, const WsLayout& w,
     return TM_OK;
 }
 
+// Per-token read, once per call: C of layer 0 and pm_t, ps_t for every
+// chunk (they depend on the inputs only).
+tm_status run_token_scores(const tm_ctx* c, long ns, const WsLayout& w, char* ws, const float* theta,
+                           const float* eta, const float* alpha, int n_tokens, int heads, bool f32,
+                           hipStream_t st) {
+    R3Args r;
+    memset(&r, 0, sizeof(r));
+    r.b = c->chunk;
+    r.bp = w.bp;
+    r.K = c->dim;
+    r.N = c->dout[0];
+    r.a = ws + w.xq;
+    r.a_ss = w.x_ss;
+    r.a_cs = w.xc;
+    r.hk = ws + w.xk;
+    r.hk_ss = w.x_ss;
+    r.hk_cs = w.xc;
+    r.sco = reinterpret_cast<float*>(ws + w.r3c);
+    r.sc_ss = w.r3c_ss;
+    r.sc_cs = w.r3c_cs;
+    r.theta = theta;
+    r.eta = eta;
+    r.alpha = alpha;
+    r.gl = TokLayout{n_tokens, heads, 1};
+    r.pq = reinterpret_cast<float*>(ws + w.r3p);
+    r.pq_ss = w.r3p_ss;
+    r.pq_cs = 2 * c->chunk;
+    if (timed(K_R3, st, [&] { return launch_r3_score(r, (int)ns, w.C, f32 ? 1 : 0, st); }) != hipSuccess)
+        return TM_ERR_HIP;
+    return TM_OK;
+}
+
 // Per-token read of chunk ci (every query through the memory as its own
 // token's write left it), between the chunk's forward / backward and the
-// step that writes it, so the state still holds the chunk-start weights:
-// layer 0's Delta of the keys, then per layer the coefficient-scaled scores
-// and the layer's rows (the last layer writes y).
+// step that writes it, so the state still holds the chunk-start weights: per
+// layer the rows (layer 0 forms its Delta in place), after the layer's C for
+// the layers past the first; the last layer writes y.
 tm_status run_token_read(const tm_ctx* c, char* state, long ns, const WsLayout& w, char* ws,
                          const TokLayout& tl, int ci, const void* v, const float* theta, const float* eta,
-                         const float* alpha, float* y, int n_tokens, int heads, bool f32, hipStream_t st) {
+                         const float* alpha, float* y, int n_tokens, int heads, const float* m1, long m1_ss,
+                         bool f32, hipStream_t st) {
     const int b = c->chunk;
     const size_t esz = f32 ? 4 : 2;
     StateLayout sl = state_layout(c, ns);
     const float* Mst = reinterpret_cast<const float*>(state + sl.M);
     const float* Sst = reinterpret_cast<const float*>(state + sl.S);
-    const char* xq = ws + w.xq + (size_t)ci * w.xc * esz;
-    const char* xk = ws + w.xk + (size_t)ci * w.xc * esz;
-    R3Args r;
-    memset(&r, 0, sizeof(r));
-    r.b = b;
-    r.bp = w.bp;
-    r.ms_ss = c->P;
-    r.tl = tl;
-    // Delta of layer 0 for the chunk's keys
-    if (c->L == 1) {
-        r.bl = BL_CF0;
-        r.K = c->dim;
-        r.N = c->dim;
-        r.a = xk;
-        r.a_ss = w.x_ss;
-        r.M = Mst;
-        r.v = v;
-        r.vt0 = ci * b;
-    } else {
-        r.bl = BL_CF1T;
-        r.K = c->dout[1];
-        r.N = c->dout[0];
-        r.a = ws + w.dlp[1];
-        r.a_ss = w.dlp_ss[1];
-        r.M = Mst + c->off[1];
-        r.dsl = reinterpret_cast<const float*>(ws + w.dsl[0]);
-        r.dsl_ss = w.dsl_ss;
-        r.dsl_ld = c->hidden;
-    }
-    r.out = ws + w.dlp[0];
-    r.out_ss = w.dlp_ss[0];
-    if (timed(K_R3, st, [&] { return launch_r3(r, R3_DELTA, (int)ns, f32 ? 1 : 0, st); }) != hipSuccess)
-        return TM_ERR_HIP;
-    float* pq = reinterpret_cast<float*>(ws + w.r3p);
+    float* cbuf = reinterpret_cast<float*>(ws + w.r3c);
     for (int l = 0; l < c->L; ++l) {
+        R3Args r;
         memset(&r, 0, sizeof(r));
         r.b = b;
         r.bp = w.bp;
@@ -545,48 +548,64 @@ tm_status run_token_read(const tm_ctx* c, char* state, long ns, const WsLayout& 
         r.N = c->dout[l];
         r.tl = tl;
         if (l == 0) {
-            r.a = xq;
+            r.a = ws + w.xq + (size_t)ci * w.xc * esz;
             r.a_ss = w.x_ss;
-            r.hk = xk;
+            r.hk = ws + w.xk + (size_t)ci * w.xc * esz;
             r.hk_ss = w.x_ss;
+            r.sc = cbuf + (size_t)ci * w.r3c_cs;
         } else {
             // the keys' rows of the store's forward (no query rows: keys from row 0)
             r.a = ws + w.r3x[(l - 1) & 1];
             r.a_ss = w.r3x_ss;
             r.hk = ws + w.act[l - 1];
             r.hk_ss = w.act_ss;
+            r.sco = cbuf + (size_t)w.C * w.r3c_cs;
+            r.sc_ss = w.r3c_ss;
+            r.theta = theta;
+            r.eta = eta;
+            r.alpha = alpha;
+            r.gl = TokLayout{n_tokens, heads, 1};
+            r.g0 = ci * b;
+            if (timed(K_R3, st, [&] { return launch_r3_score(r, (int)ns, 1, f32 ? 1 : 0, st); }) != hipSuccess)
+                return TM_ERR_HIP;
+            r.sc = r.sco;
         }
-        // the coefficient-scaled scores (and, with layer 0, pm_t and ps_t)
-        r.theta = theta;
-        r.eta = eta;
-        r.alpha = alpha;
-        r.gl = TokLayout{n_tokens, heads, 1};
-        r.g0 = ci * b;
-        r.pq = l == 0 ? pq : nullptr;
-        r.pq_ss = w.r3p_ss;
-        r.out = ws + w.r3c;
-        r.out_ss = w.r3c_ss;
-        if (timed(K_R3, st, [&] { return launch_r3(r, R3_SCORE, (int)ns, f32 ? 1 : 0, st); }) != hipSuccess)
-            return TM_ERR_HIP;
-        // the layer's rows
-        r.bl = l == 0 ? BL_CF0 : l == 1 ? BL_CF1 : BL_ROW;
-        r.M = Mst + c->off[l];
-        r.S = Sst + c->off[l];
-        r.ms_ss = c->P;
-        r.sc = ws + w.r3c;
         r.sc_ss = w.r3c_ss;
-        r.dl = ws + w.dlp[l];
-        r.dl_ss = w.dlp_ss[l];
-        r.pq = pq;
+        r.pq = reinterpret_cast<float*>(ws + w.r3p) + (size_t)ci * 2 * b;
+        r.pq_ss = w.r3p_ss;
+        r.bl = l == 0 ? BL_CF0 : l == 1 ? BL_CF1 : BL_ROW;
+        // (layer 1's M where this step's update wrote it)
+        r.M = l == 1 ? m1 : Mst + c->off[l];
+        r.m_ss = l == 1 ? m1_ss : c->P;
+        r.S = Sst + c->off[l];
+        r.s_ss = c->P;
+        if (l > 0) {
+            r.dk = R3D_BUF;
+            r.dl = ws + w.dlp[l];
+            r.dl_ss = w.dlp_ss[l];
+        } else if (c->L == 1) {
+            r.dk = R3D_OUT;
+            r.v = v;
+            r.vt0 = ci * b;
+        } else {
+            r.dk = R3D_BWD;
+            r.d1 = ws + w.dlp[1];
+            r.d1_ss = w.dlp_ss[1];
+            r.K1 = c->dout[1];
+            r.w1 = m1;
+            r.w1_ss = m1_ss;
+            r.dsl = reinterpret_cast<const float*>(ws + w.dsl[0]);
+            r.dsl_ss = w.dsl_ss;
+            r.dsl_ld = c->hidden;
+        }
         if (l + 1 < c->L) {
             r.out = ws + w.r3x[l & 1];
             r.out_ss = w.r3x_ss;
         } else {
-            r.out = nullptr;
             r.y = y;
             r.yt0 = ci * b;
         }
-        if (timed(K_R3, st, [&] { return launch_r3(r, R3_LAYER, (int)ns, f32 ? 1 : 0, st); }) != hipSuccess)
+        if (timed(K_R3, st, [&] { return launch_r3_layer(r, (int)ns, f32 ? 1 : 0, st); }) != hipSuccess)
             return TM_ERR_HIP;
     }
     return TM_OK;
@@ -637,6 +656,10 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     sa.bp = w.bp;
     sa.kt_f32 = f32 ? 1 : 0;
     if (timed(K_SCAN, st, [&] { return launch_scan(sa, st); }) != hipSuccess) return TM_ERR_HIP;
+    if (read == TM_READ_PER_TOKEN && q) {
+        tm_status rc = run_token_scores(c, ns, w, ws, theta, eta, alpha, n_tokens, heads, f32, st);
+        if (rc != TM_OK) return rc;
+    }
 
     FirstArgs a;
     memset(&a, 0, sizeof(a));
@@ -687,9 +710,7 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     float* m1_ws = c->L == 2 ? reinterpret_cast<float*>(ws + w.m1x) : nullptr;
     const long p1 = c->L >= 2 ? (long)c->din[1] * c->dout[1] : 0;
     int nw1 = 0;
-    // (the per-token read takes W_1's chunk-start M from the state, so its
-    // update stays in place there)
-    if (c->L == 2 && g_w1_split && read != TM_READ_PER_TOKEN) {
+    if (c->L == 2 && g_w1_split) {
         // a multiple of 8 workgroups, W1_JPW row blocks each per XCD residue
         const int n1 = 8 * (((a.nb1 + 7) / 8 + W1_JPW - 1) / W1_JPW);
         int cus = 0;
@@ -767,7 +788,7 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         }
         if (ci < C && read == TM_READ_PER_TOKEN && q) {
             tm_status rc = run_token_read(c, state, ns, w, ws, tl, ci, v, theta, eta, alpha, y, n_tokens, heads,
-                                          f32, st);
+                                          a.m1_wr, a.m1_wr_ss, f32, st);
             if (rc != TM_OK) return rc;
         }
     }

@@ -269,58 +269,69 @@ struct ProjArgs {
     int B, T, D, H, d, K;
 };
 
-// Per-token read of one chunk c (every query through the memory as its own
-// token's write left it), per stream s (blockIdx.y).  With every gradient of
-// the chunk at its start weights (M, S), the weights after token t are
+// Per-token read (every query through the memory as its own token's write
+// left it), per stream s (blockIdx.y).  With every gradient of chunk c at its
+// start weights (M, S), the weights after token t of the chunk are
 //     M_t = pm_t M + ps_t S - sum_{i <= t} c_ti G_i,   G_i = H_i^T Delta_i
 // per layer, so a query row's layer product is
-//     x_t M_t = pm_t x_t M + ps_t x_t S - sum_{i <= t} c_ti (x_t . H_i) Delta_i,
+//     x_t M_t = pm_t x_t M + ps_t x_t S - sum_{i <= t} C_ti Delta_i,
+//     C_ti = c_ti (x_t . H_i),
 // the chunk start's products plus a causal b x b correction (the dual form
-// of chunked linear attention).  Three kinds of launch per chunk:
-//   R3_DELTA  Delta of layer 0 for the chunk's keys (depth 1: 2 (k M - v);
-//             deeper: (Delta_1 W_1^T) . SiLU'(z_0)), packed [b][N];
-//   R3_SCORE  per layer: C[t][i] = c_ti (x_t . H_i) for i <= t < b, else 0,
-//             packed [b][bp]; with layer 0 also pm_t and ps_t;
-//   R3_LAYER  per layer: z = pm_t x M + ps_t x S - C Delta, then SiLU(z)
-//             (packed [b][N], the next layer's x) or y = z (the last layer).
+// of chunked linear attention).  Two kernels:
+//   score  C of one layer (fp32, [16 ceil(b/16)][bp] per chunk, zeros off
+//          the causal triangle and past the chunk) and, with layer 0, pm_t
+//          and ps_t; layer 0's depend on the inputs only, so one launch
+//          covers every chunk of the call (blockIdx.z = chunk);
+//   layer  one layer's rows: z = pm_t x M + ps_t x S - C Delta, then
+//          SiLU(z) (packed [b][N], the next layer's x) or y = z (the last
+//          layer).  Layer 0 forms its Delta in place: (Delta_1 W_1^T) .
+//          SiLU'(z_0) for depth >= 2, 2 (k M - v) for depth 1.
 // c_ti, pm_t, ps_t come from the chunk's gates by the recurrences of the
 // momentum and the forgetting (no ratios of running products).
-enum { R3_DELTA = 0, R3_SCORE = 1, R3_LAYER = 2 };
 enum { BL_CF0 = 0, BL_CF1 = 1, BL_ROW = 2, BL_CF1T = 3 };   // layout of an fp32 B operand
+enum { R3D_BUF = 0, R3D_BWD = 1, R3D_OUT = 2 };              // where a layer's Delta comes from
 struct R3Args {
     int b, bp, K, N;
-    int bl;                   // BL_*: layout of M and S (layer) or of the delta's weights
-    const void* a;            // A rows, packed [b][K] (operand type)
-    long a_ss;
-    const float* M;           // fp32 state matrices of the layer (stream stride ms_ss)
+    int bl;                   // BL_*: layout of the layer's M and S
+    int dk;                   // R3D_*: Delta from dl (BUF), formed from Delta_1 (BWD) or from k M - v (OUT)
+    const void* a;            // query rows, packed [b][K] (operand type); chunk z at a + z * a_cs
+    long a_ss, a_cs;
+    const void* hk;           // key rows of the layer's input, packed [b][K]
+    long hk_ss, hk_cs;
+    const float* M;           // fp32 M and S of the layer (stream strides m_ss, s_ss)
     const float* S;
-    long ms_ss;
-    const void* hk;           // score: the key rows' layer input, packed [b][K]
-    long hk_ss;
-    const void* sc;           // layer: C, packed [b][bp]
-    long sc_ss;
-    const void* dl;           // layer: the key rows' Delta, packed [b][N]
+    long m_ss, s_ss;
+    const float* sc;          // C, fp32 [16 ceil(b/16)][bp] (stream stride sc_ss, chunk stride sc_cs)
+    long sc_ss, sc_cs;
+    float* sco;               // score: where C is written (same strides)
+    const void* dl;           // BUF: the key rows' Delta, packed [b][N]
     long dl_ss;
-    const float* theta;       // score: gates of the chunk's tokens g0 .. g0 + b - 1
+    const void* d1;           // BWD: Delta_1 of the key rows, packed [b][K1]; W_1's M at w1
+    long d1_ss;
+    int K1;
+    const float* w1;
+    long w1_ss;
+    const float* dsl;         // BWD: SiLU'(z_0) of the key rows [b][dsl_ld]
+    long dsl_ss, dsl_ld;
+    const void* v;            // OUT: values of tokens vt0 + i
+    int vt0;
+    const float* theta;       // score: gates of tokens g0 + z b + t
     const float* eta;
     const float* alpha;
     TokLayout gl;
     int g0;
-    float* pq;                // pm_t (t < b) then ps_t, per stream (written by the layer-0 score)
-    long pq_ss;
-    void* out;                // packed output (delta, score, hidden layer), operand type
+    float* pq;                // pm_t (t < b) then ps_t, per stream and chunk
+    long pq_ss, pq_cs;
+    void* out;                // layer, hidden: SiLU(z), packed [b][N] (operand type)
     long out_ss;
-    float* y;                 // last layer: y of tokens yt0 + t
+    float* y;                 // layer, last: y of tokens yt0 + t
     TokLayout tl;
     int yt0;
-    const void* v;            // delta, depth 1: values of tokens vt0 + i
-    int vt0;
-    const float* dsl;         // delta, deeper: SiLU'(z_0) of the key rows [b][dsl_ld]
-    long dsl_ss, dsl_ld;
 };
 
 // ---- launchers (tm_r3.hip) ----
-hipError_t launch_r3(const R3Args& r, int kind, int ns, int f32, hipStream_t st);
+hipError_t launch_r3_score(const R3Args& r, int ns, int nchunks, int f32, hipStream_t st);
+hipError_t launch_r3_layer(const R3Args& r, int ns, int f32, hipStream_t st);
 
 // ---- launchers (tm_kernels.hip) ----
 hipError_t launch_project(const ProjArgs& p, int f32, hipStream_t st);
