@@ -17,6 +17,10 @@
 
 using namespace tmk;
 
+namespace tmk {
+thread_local LaunchEvents g_launch_ev;
+}
+
 // A call's launch sequence replayed as a HIP graph: keyed by everything the
 // kernels' arguments depend on (device, every pointer and every size).
 struct GraphEntry {
@@ -203,8 +207,12 @@ hipEvent_t pool_get() {
     return e;
 }
 
+// The launch inside `launch` records the pair with its own dispatch
+// (launch_k); a launch that turned out to be empty records nothing and is
+// not counted.
 template <class F>
 hipError_t timed(int kind, hipStream_t st, F&& launch) {
+    (void)st;
     bool on;
     {
         std::lock_guard<std::mutex> g(g_tmu);
@@ -218,13 +226,16 @@ hipError_t timed(int kind, hipStream_t st, F&& launch) {
         b = pool_get();
     }
     if (!a || !b) return hipErrorOutOfMemory;
-    hipError_t e = hipEventRecord(a, st);
-    if (e != hipSuccess) return e;
-    e = launch();
-    if (e != hipSuccess) return e;
-    e = hipEventRecord(b, st);
-    if (e != hipSuccess) return e;
+    g_launch_ev = LaunchEvents{a, b, false};
+    const hipError_t e = launch();
+    const bool used = g_launch_ev.used;
+    g_launch_ev = LaunchEvents{};
     std::lock_guard<std::mutex> g(g_tmu);
+    if (e != hipSuccess || !used) {
+        g_pool.push_back(a);
+        g_pool.push_back(b);
+        return e;
+    }
     g_pending.push_back(Timed{a, b, kind});
     return hipSuccess;
 }

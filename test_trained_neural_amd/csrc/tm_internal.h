@@ -2,11 +2,33 @@
 // kernels (tm_kernels.hip).  Not part of the public interface.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace tmk {
+
+// Event timing of launches (tm_timing_enable): while a timed call runs, its
+// launch records this pair with the kernel's own dispatch (hipExtLaunchKernel),
+// so the pair brackets the kernel's execution as the profiler sees it, not
+// the host-side launch around it.  Set and consumed on the calling thread.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+    bool used = false;
+};
+extern thread_local LaunchEvents g_launch_ev;
+
+template <class K, class... A>
+inline void launch_k(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, A... args) {
+    if (g_launch_ev.start && !g_launch_ev.used) {
+        g_launch_ev.used = true;
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, g_launch_ev.start, g_launch_ev.stop, 0u,
+                              args...);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+    }
+}
 
 constexpr int MAXL = 8;                 // deepest memory MLP supported
 constexpr int MAX_CHUNK = 64;           // one wave lane per token in the scan

@@ -375,7 +375,7 @@ template <class OP, class AT, class BT, int BM, int RT, int NR, int W>
 static void launch_one(const GemmArgs& g, int ns, hipStream_t st) {
     dim3 grid((g.N + NR * 16 - 1) / (NR * 16), (g.nrows + RT - 1) / RT, ns);
     const size_t lds = ((size_t)W * RT * (NR * 16 + 1) + 2 * RT) * 4;
-    hipLaunchKernelGGL((gemm_kernel<OP, AT, BT, BM, RT, NR, W>), grid, dim3(W * 64), lds, st, g);
+    launch_k((gemm_kernel<OP, AT, BT, BM, RT, NR, W>), grid, dim3(W * 64), lds, st, g);
 }
 
 template <class OP, class AT, class BT, int BM, int RT, int W>
@@ -536,7 +536,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t st) {
     const long blocks = (long)a.ns * a.C * ((a.ktl.d + SCAN_SLICE - 1) / SCAN_SLICE);
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffL || a.b > MAX_CHUNK || a.bp > MAX_CHUNK || a.ktl.d % 32 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    launch_k(scan_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -1428,7 +1428,7 @@ template <class OP, bool UPD, bool FWD>
 static void launch_first_as(const FirstArgs& a, dim3 grid, size_t lds, hipStream_t st) {
     if constexpr (UPD) {
         if (a.nw1 > 0) {
-            hipLaunchKernelGGL((first_layer_kernel<OP, true, FWD, true, true, false>), grid, dim3(FW * 64), lds, st, a);
+            launch_k((first_layer_kernel<OP, true, FWD, true, true, false>), grid, dim3(FW * 64), lds, st, a);
             return;
         }
     }
@@ -1436,16 +1436,16 @@ static void launch_first_as(const FirstArgs& a, dim3 grid, size_t lds, hipStream
     if constexpr (sizeof(OP) == 2) {
         if (small) {
             if (a.u.L >= 2)
-                hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, true, false, true>), grid, dim3(FW * 64), lds, st, a);
+                launch_k((first_layer_kernel<OP, UPD, FWD, true, false, true>), grid, dim3(FW * 64), lds, st, a);
             else
-                hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, false, false, true>), grid, dim3(FW * 64), lds, st, a);
+                launch_k((first_layer_kernel<OP, UPD, FWD, false, false, true>), grid, dim3(FW * 64), lds, st, a);
             return;
         }
     }
     if (a.u.L >= 2)
-        hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, true, false, false>), grid, dim3(FW * 64), lds, st, a);
+        launch_k((first_layer_kernel<OP, UPD, FWD, true, false, false>), grid, dim3(FW * 64), lds, st, a);
     else
-        hipLaunchKernelGGL((first_layer_kernel<OP, UPD, FWD, false, false, false>), grid, dim3(FW * 64), lds, st, a);
+        launch_k((first_layer_kernel<OP, UPD, FWD, false, false, false>), grid, dim3(FW * 64), lds, st, a);
 }
 
 template <class OP>
@@ -1620,12 +1620,12 @@ __global__ __launch_bounds__(256) void state_init_kernel(UpdArgs u, const float*
 
 hipError_t launch_state_init(const UpdArgs& u, int ntiles, int ns, const float* init, int H, StateHeader* h,
                              uint64_t hash, int batch, int heads, hipStream_t st) {
-    hipLaunchKernelGGL(state_init_kernel, dim3(ntiles, ns), dim3(256), 0, st, u, init, H, h, hash, batch, heads);
+    launch_k(state_init_kernel, dim3(ntiles, ns), dim3(256), 0, st, u, init, H, h, hash, batch, heads);
     return hipGetLastError();
 }
 
 hipError_t launch_shadow(const UpdArgs& u, int ntiles, int ns, hipStream_t st) {
-    hipLaunchKernelGGL(shadow_kernel, dim3(ntiles, ns), dim3(256), 0, st, u);
+    launch_k(shadow_kernel, dim3(ntiles, ns), dim3(256), 0, st, u);
     return hipGetLastError();
 }
 
@@ -1651,13 +1651,13 @@ __global__ void import_kernel(float* M, float* S, const float* src, long P, int 
 
 hipError_t launch_export(const float* M, const float* S, float* dst, long P, int ns, int d0, int h1, int d1,
                          hipStream_t st) {
-    hipLaunchKernelGGL(export_kernel, dim3(2048), dim3(256), 0, st, M, S, dst, P, ns, d0, h1, d1);
+    launch_k(export_kernel, dim3(2048), dim3(256), 0, st, M, S, dst, P, ns, d0, h1, d1);
     return hipGetLastError();
 }
 
 hipError_t launch_import(float* M, float* S, const float* src, long P, int ns, int d0, int h1, int d1,
                          hipStream_t st) {
-    hipLaunchKernelGGL(import_kernel, dim3(2048), dim3(256), 0, st, M, S, src, P, ns, d0, h1, d1);
+    launch_k(import_kernel, dim3(2048), dim3(256), 0, st, M, S, src, P, ns, d0, h1, d1);
     return hipGetLastError();
 }
 
@@ -1675,7 +1675,7 @@ __global__ void header_kernel(StateHeader* h, uint64_t hash, int batch, int head
 }
 
 hipError_t launch_header(StateHeader* h, uint64_t hash, int batch, int heads, hipStream_t st) {
-    hipLaunchKernelGGL(header_kernel, dim3(1), dim3(64), 0, st, h, hash, batch, heads);
+    launch_k(header_kernel, dim3(1), dim3(64), 0, st, h, hash, batch, heads);
     return hipGetLastError();
 }
 
@@ -1907,7 +1907,7 @@ static void launch_project_g(const ProjArgs& p, hipStream_t st) {
         (void)hipFuncSetAttribute((const void*)project_kernel<OP, RT, G>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     dim3 grid((p.T + RT - 1) / RT, 3 * p.H + 1, p.B);   // + one grid row for the gates
-    hipLaunchKernelGGL((project_kernel<OP, RT, G>), grid, dim3(512), lds, st, p);
+    launch_k((project_kernel<OP, RT, G>), grid, dim3(512), lds, st, p);
 }
 
 // G: column blocks a wave holds per pass, as few as cover the head in one
@@ -1935,8 +1935,8 @@ hipError_t launch_project(const ProjArgs& p, int f32, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.K == 1) return e;
     const long nw = (long)p.B * 3 * p.H * p.d;   // one wave each
-    if (f32) hipLaunchKernelGGL(history_kernel<float>, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL(history_kernel<bf16>, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, st, p);
+    if (f32) launch_k(history_kernel<float>, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, st, p);
+    else launch_k(history_kernel<bf16>, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

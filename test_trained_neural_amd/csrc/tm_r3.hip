@@ -417,18 +417,18 @@ hipError_t launch_r3_score(const R3Args& r, int ns, int nchunks, int f32, hipStr
     if (!r3_shape_ok(r, ns) || nchunks < 1 || nchunks > 65535) return hipErrorInvalidValue;
     const dim3 grid(r.bp / 16, ns, nchunks);
     if (r.K >= 1024) {
-        if (f32) hipLaunchKernelGGL((r3_score_kernel<float, 16>), grid, dim3(16 * 64), r3_score_lds(16), st, r);
-        else hipLaunchKernelGGL((r3_score_kernel<bf16, 16>), grid, dim3(16 * 64), r3_score_lds(16), st, r);
+        if (f32) launch_k((r3_score_kernel<float, 16>), grid, dim3(16 * 64), r3_score_lds(16), st, r);
+        else launch_k((r3_score_kernel<bf16, 16>), grid, dim3(16 * 64), r3_score_lds(16), st, r);
     } else {
-        if (f32) hipLaunchKernelGGL((r3_score_kernel<float, 8>), grid, dim3(8 * 64), r3_score_lds(8), st, r);
-        else hipLaunchKernelGGL((r3_score_kernel<bf16, 8>), grid, dim3(8 * 64), r3_score_lds(8), st, r);
+        if (f32) launch_k((r3_score_kernel<float, 8>), grid, dim3(8 * 64), r3_score_lds(8), st, r);
+        else launch_k((r3_score_kernel<bf16, 8>), grid, dim3(8 * 64), r3_score_lds(8), st, r);
     }
     return hipGetLastError();
 }
 
 template <class OP, int BL, int DK>
 static void launch_layer_as(const R3Args& r, int ns, hipStream_t st) {
-    hipLaunchKernelGGL((r3_layer_kernel<OP, BL, DK>), dim3(r.N / 16, ns), dim3(RW * 64), R3_LAYER_LDS, st, r);
+    launch_k((r3_layer_kernel<OP, BL, DK>), dim3(r.N / 16, ns), dim3(RW * 64), R3_LAYER_LDS, st, r);
 }
 
 template <class OP>
