@@ -13,6 +13,7 @@ import pytest
 
 from harness import GpuMemory, TOL, compare_state, dev_inputs, oracle_forward, relerr, say
 from test_gpu_parity import SMALL
+from test_gpu_workloads import MAX
 from test_trained_neural_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -50,6 +51,27 @@ def test_per_token_read_parity(wl):
     assert g.check() == (False, 2 * wl.seq)
     g.close()
     h.close()
+
+
+@pytest.mark.parametrize("wl", [w for w in MAX], ids=lambda w: w.name)
+def test_per_token_read_maximum_sizes(wl):
+    # the widest memory (dim 1024: layer 1's scores with K = 2048) and the
+    # deepest (8 weight matrices, six of them in the row-major layout)
+    import test_trained_neural_amd as T
+    say("case", wl)
+    p = I.make_params(wl)
+    ci = I.make_call(wl, p)
+    g = GpuMemory(wl, p)
+    y = g.forward(dev_inputs(ci, wl.dtype), read=T.TM_READ_PER_TOKEN).cpu().numpy()
+    ref = I.initial_state(wl, p)
+    yr = oracle_forward(wl, ref, ci, read="token")
+    ey = relerr(y, yr)
+    em, es = compare_state(wl, g.export(), ref)
+    say("  y %.2e  M %.2e  S %.2e" % (ey, em, es))
+    tol = TOL[wl.dtype]
+    assert np.all(np.isfinite(ref))
+    assert ey < tol and em < tol and es < 2 * tol
+    g.close()
 
 
 def test_per_token_read_mlp384():
