@@ -206,7 +206,7 @@ struct FirstArgs {
     UpdArgs u;                // layers, state, chunk scalars, flag
     int dim, h1, nb1;
     // update tiles [upd_tile0, upd_tile0 + upd_ntiles) of the other layers
-    // (chunk c-1), carried two per workgroup after the nb1 first-layer blocks
+    // (chunk c-1), carried two or four per workgroup after the nb1 first-layer blocks
     int upd_tile0, upd_ntiles;
     int do_update, do_fwd, nq, nk;
     int chunk_prev;

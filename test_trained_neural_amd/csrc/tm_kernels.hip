@@ -754,7 +754,7 @@ constexpr int RPAD = 1;     // LDS row padding of the partial-sum tiles (floats)
 constexpr int FW = 8;       // waves of a first-layer workgroup
 
 constexpr int FRED = FW / 2;   // partial tiles kept in LDS (two-round reduction)
-constexpr size_t UPD_PAIR_LDS = 2 * 2 * 64 * 65 * 4;   // the two halves' update tiles: U_M, U_S each
+constexpr size_t UPD_TILE_LDS = 2 * 2 * 64 * 65 * 4;   // the two halves' update tiles: U_M, U_S each
 // Update tiles per workgroup: two per half (both tiles' loads in flight
 // together) where the register budget holds them, one per half in the
 // half-occupancy (small) and fp32 variants.
@@ -1462,10 +1462,10 @@ hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st) {
         return hipErrorInvalidValue;
     if (a.upd_ntiles > 0 && (!a.do_update || a.u.L < 3)) return hipErrorInvalidValue;
     const int tpw = upd_tpw(f32, first_small(a, f32));
-    const int pairs = (a.upd_ntiles + tpw - 1) / tpw;   // workgroups of update tiles
-    dim3 grid(a.nb1 + (a.nw1 > 0 ? a.nw1 : pairs), ns);
+    const int nupd = (a.upd_ntiles + tpw - 1) / tpw;   // workgroups of update tiles
+    dim3 grid(a.nb1 + (a.nw1 > 0 ? a.nw1 : nupd), ns);
     size_t lds = first_lds_bytes(a.dim, a.u.bp, f32);
-    if (pairs > 0 && lds < UPD_PAIR_LDS) lds = UPD_PAIR_LDS;
+    if (nupd > 0 && lds < UPD_TILE_LDS) lds = UPD_TILE_LDS;
     if (a.nw1 > 0 && lds < W1_LDS) lds = W1_LDS;
     if (f32) launch_first_op<float>(a, grid, lds, st);
     else launch_first_op<bf16>(a, grid, lds, st);
