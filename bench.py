@@ -382,7 +382,7 @@ def main():
     roof["traffic"] = read_traffic(kernel_names[dom], wl.name)
     roof.update({"kernel": kernel_names[dom], "launches": dn, "avg_us": avg_s * 1e6,
                  ("bytes_per_launch" if kind == "hbm" else "flops_per_launch"): per_launch,
-                 "timing": "HIP events around each launch on its stream, second pass of the same steps",
+                 "timing": "HIP events recorded with each launch's own dispatch (hipExtLaunchKernel) on its stream, second pass of the same steps",
                  "kernel_source_sha256_16": kernel_source_hash()})
 
     tokens = Bn * Tn * args.steps
