@@ -115,6 +115,35 @@ def bwd_flops(wl, ns, T):
     return 2 * ns * T * sum(a * b for a, b in wl.layer_dims()[2:])
 
 
+def token_read_flops(wl, ns, T):
+    """Flops of the per-token read's products (tm_forward_ex, read per
+    token) over a call of T tokens: per chunk and stream, the scores
+    2 b^2 d_in of every layer, the query rows' products with M and S
+    (4 b d_in d_out) and the correction (2 b^2 d_out) of every layer, and
+    layer 0's Delta (2 b d_1 h, or 2 b d d for depth 1)."""
+    b = wl.chunk
+    dims = wl.layer_dims()
+    per = sum(2 * b * b * a + 4 * b * a * o + 2 * b * b * o for a, o in dims)
+    per += 2 * b * dims[1][1] * dims[0][1] if len(dims) >= 2 else 2 * b * dims[0][0] * dims[0][1]
+    return per * ns * (T // b)
+
+
+def project_flops(wl, Bn, T):
+    """Flops of the input side's projection kernel: k, v, q and the three
+    gates from every token's model vector."""
+    D, HD = wl.model_dim, wl.heads * wl.dim
+    return 2 * Bn * T * D * (3 * HD + 3 * wl.heads)
+
+
+def mfma_roofline(kind_flops, ms, n, dtype, kernel):
+    """An MFMA roofline entry from event-timed launches of one class."""
+    peak = BF16_PEAK_TFLOPS if dtype == "bf16" else FP32_PEAK_TFLOPS
+    achieved = kind_flops / (ms / 1e3) / 1e12
+    return {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+            "kernel": kernel, "launches": n, "avg_us": ms * 1e3 / max(n, 1),
+            "timing": "HIP events recorded with each launch's own dispatch, second pass of the same steps"}
+
+
 def read_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter summary, or None."""
     path = os.path.join(ROOT, "profiles", "%s_%s_pmc.md" % (kernel, workload))
@@ -153,7 +182,7 @@ def cpu_baseline(wl, params, ci, min_seconds=10.0):
                       "state), fp64 C oracle, one thread per stream, %.1f s" % (wl.name, reps, streams, tokens, dt)}
 
 
-def other_workload(name, steps, calls=None, read=None):
+def other_workload(name, steps, calls=None, read=None, oracle=False):
     """Throughput of another workload (tokens/s): state init + its calls in
     order, inputs resident in HBM, graph replay (each call's buffers repeat
     across steps).  calls: how many of the workload's calls to run (a prefix
@@ -195,15 +224,40 @@ def other_workload(name, steps, calls=None, read=None):
         step()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
-    T.tm_destroy(ctx)
     tokens = Bn * Tn * n_calls
-    return {"tokens_per_s": tokens / dt, "ms_per_step": dt * 1e3, "steps": steps,
-            "step": "tm_state_init + %d %s calls of (%d, %d) tokens, %d heads" % (
-                n_calls, "tm_forward" if read is None else "tm_forward_ex(read=%d)" % read, Bn, Tn, H),
-            "sample": "whole workload" if n_calls == wl.calls else "first %d of %d calls" % (n_calls, wl.calls)}
+    out = {"tokens_per_s": tokens / dt, "ms_per_step": dt * 1e3, "steps": steps,
+           "step": "tm_state_init + %d %s calls of (%d, %d) tokens, %d heads" % (
+               n_calls, "tm_forward" if read is None else "tm_forward_ex(read=%d)" % read, Bn, Tn, H),
+           "sample": "whole workload" if n_calls == wl.calls else "first %d of %d calls" % (n_calls, wl.calls)}
+    if read == T.TM_READ_PER_TOKEN:
+        # the read's own launches, event-timed in a second pass
+        T.tm_timing_enable(1 << T.K_TOKEN_READ)
+        T.tm_timing_read(T.K_TOKEN_READ)
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        T.tm_timing_enable(0)
+        ms, n = T.tm_timing_read(T.K_TOKEN_READ)
+        out["roofline"] = mfma_roofline(token_read_flops(wl, Bn * H, Tn) * n_calls * steps, ms, n, wl.dtype,
+                                        "r3_score_kernel + r3_layer_kernel")
+    T.tm_destroy(ctx)
+    if oracle:
+        # the oracle on the workload's first call, in the same read order
+        from oracle import tmref
+        ci = I.make_call(wl, params, 0, 0)
+        st = I.initial_state(wl, params)
+        nt = min(os.cpu_count() or 1, Bn * H)
+        t1 = time.perf_counter()
+        tmref.forward(wl.dim, wl.depth, wl.expansion, wl.chunk, st, ci.k, ci.v, ci.theta, ci.eta, ci.alpha,
+                      q=ci.q, n_threads=nt, read={None: "after", 1: "before", 2: "token"}[read])
+        odt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": Bn * Tn / odt, "unit": "tokens/s", "cores": nt, "kind": "oracle",
+                               "sample": "%s: one call (%d streams x %d tokens) from the initial state, fp64 C "
+                                         "oracle, %.1f s" % (wl.name, Bn * H, Tn, odt)}
+    return out
 
 
-def input_side(name, steps):
+def input_side(name, steps, oracle=False):
     """The input side (tm_project: x -> k, v, q and the gates, 4-tap
     convolution) alone and chained with the memory step (tm_project +
     tm_state_init + tm_forward), on the workload's first call; tokens/s."""
@@ -250,6 +304,25 @@ def input_side(name, steps):
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / steps
         out[nm] = {"tokens_per_s": Bn * Tn / dt, "ms_per_step": dt * 1e3, "steps": steps}
+    # the projection kernel, event-timed in a second pass
+    T.tm_timing_enable(1 << T.K_PROJECT)
+    T.tm_timing_read(T.K_PROJECT)
+    for _ in range(steps):
+        project()
+    torch.cuda.synchronize()
+    T.tm_timing_enable(0)
+    ms, n = T.tm_timing_read(T.K_PROJECT)
+    out["input_side"]["roofline"] = mfma_roofline(project_flops(wl, Bn, Tn) * steps, ms, n, wl.dtype,
+                                                  "project_kernel")
+    if oracle:
+        from oracle import prologue
+        t1 = time.perf_counter()
+        prologue.project(pi.x, pi.w_kvq, pi.conv, pi.w_gate, pi.gate_bias, H)
+        odt = time.perf_counter() - t1
+        out["input_side"]["cpu_baseline"] = {
+            "value": Bn * Tn / odt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%s input side: one call (%d x %d tokens of width %d), fp64 numpy oracle, %.2f s" % (
+                wl.name, Bn, Tn, wl.model_dim, odt)}
     out["input_side"]["step"] = "tm_project of (%d, %d) tokens of width %d, 4-tap convolution" % (Bn, Tn, wl.model_dim)
     out["from_tokens"]["step"] = "tm_project + tm_state_init + tm_forward of (%d, %d) tokens" % (Bn, Tn)
     T.tm_destroy(ctx)
@@ -415,11 +488,11 @@ def main():
             "multihead1024": other_workload("multihead1024", 3),
             "deep512": other_workload("deep512", 2, calls=16),
             # the same step with each chunk's queries read before its write
-            "mlp384_read_before_write": other_workload("mlp384", 20, read=1),
+            "mlp384_read_before_write": other_workload("mlp384", 20, read=1, oracle=not args.no_cpu_baseline),
             # each query read right after its own token's write (the dual form)
-            "mlp384_read_per_token": other_workload("mlp384", 20, read=2),
+            "mlp384_read_per_token": other_workload("mlp384", 20, read=2, oracle=not args.no_cpu_baseline),
         }
-        side = input_side("mlp384", 20)
+        side = input_side("mlp384", 20, oracle=not args.no_cpu_baseline)
         out["other_workloads"]["mlp384_input_side"] = side["input_side"]
         out["other_workloads"]["mlp384_from_tokens"] = side["from_tokens"]
     if not args.no_cpu_baseline:

@@ -213,8 +213,9 @@ tm_status tm_w1_split_enable(int on);
  * Kernel classes: 0 coefficient scan (and key transpose), 1 chunk forward
  * products of layers 1.., 2 chunk backward products, 3 gradient reduction +
  * state update of layers 1.., 4 first-layer step (the first layer's update,
- * its in-place backward, and its forward), 5 the per-token read's products.
- * While bit c of
+ * its in-place backward, and its forward), 5 the per-token read's products,
+ * 6 the input side's projection kernel (tm_project; its history kernel is
+ * not timed).  While bit c of
  * class_mask is set, every launch of class c is bracketed by a pair of HIP
  * events recorded on its launch stream (mask 0 turns timing off).
  * tm_timing_read waits for the recorded launches and returns, for one class,

@@ -184,7 +184,7 @@ hipError_t compute_units(int* out) {
 }
 
 // ---- optional per-launch timing (tm_timing_enable / tm_timing_read) ----
-enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_UPD = 3, K_FIRST = 4, K_R3 = 5, K_CLASSES = 6 };
+enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_UPD = 3, K_FIRST = 4, K_R3 = 5, K_PROJ = 6, K_CLASSES = 7 };
 struct Timed {
     hipEvent_t a, b;
     int kind;
@@ -970,7 +970,10 @@ tm_status tm_project(const tm_ctx* c, const void* x, int model_dim, const void* 
     p.d = c->dim;
     p.K = conv_len;
     return with_graph(c, key, static_cast<hipStream_t>(stream), [&](hipStream_t st) {
-        return launch_project(p, dtype == TM_F32 ? 1 : 0, st) == hipSuccess ? TM_OK : TM_ERR_HIP;
+        // (timed: the projection kernel, the first of the two launches)
+        return timed(K_PROJ, st, [&] { return launch_project(p, dtype == TM_F32 ? 1 : 0, st); }) == hipSuccess
+                   ? TM_OK
+                   : TM_ERR_HIP;
     });
 }
 
