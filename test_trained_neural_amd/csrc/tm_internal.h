@@ -355,8 +355,10 @@ struct R3Args {
 hipError_t launch_r3_score(const R3Args& r, int ns, int nchunks, int f32, hipStream_t st);
 hipError_t launch_r3_layer(const R3Args& r, int ns, int f32, hipStream_t st);
 
-// ---- launchers (tm_kernels.hip) ----
+// ---- launchers (tm_project.hip) ----
 hipError_t launch_project(const ProjArgs& p, int f32, hipStream_t st);
+
+// ---- launchers (tm_kernels.hip) ----
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
 // fwd: op = 0 bf16 (A bf16, B = bf16 transposed copy), op = 1 fp32 (A fp32,
 // B = fp32 master read with stride).  bwd: A fp32 deltas, B fp32 master.
