@@ -10,9 +10,10 @@ and Technical Details / Parallel training; "Titans, explained" steps 3-6.
 """
 import numpy as np
 import pytest
+import torch
 
 from harness import GpuMemory, TOL, compare_state, dev_inputs, oracle_forward, relerr, say
-from test_gpu_parity import SMALL
+from test_gpu_parity import SMALL, small
 from test_gpu_workloads import MAX
 from test_trained_neural_amd import inputs as I
 
@@ -89,3 +90,36 @@ def test_per_token_read_mlp384():
     say("  y %.2e  M %.2e  S %.2e" % (ey, em, es))
     assert ey < TOL["bf16"] and em < TOL["bf16"] and es < 2 * TOL["bf16"]
     g.close()
+
+
+@pytest.mark.parametrize("depth", [1, 2, 3])
+def test_per_token_read_graph_replay_matches_direct_launches(depth):
+    # repeated per-token calls on the same buffers replay as a HIP graph;
+    # every replay (eager work and syncs in between) equals the directly
+    # launched result bit for bit
+    import test_trained_neural_amd as T
+    wl = small("graph_r3_d%d" % depth, 64, depth, 2, 16, 2, 1, 64, "bf16")
+    say("case", wl)
+    p = I.make_params(wl)
+    d = dev_inputs(I.make_call(wl, p), "bf16")
+    g = GpuMemory(wl, p)
+    y = torch.empty((2, 64, 1, 64), dtype=torch.float32, device="cuda")
+    ws = torch.empty(T.tm_workspace_bytes(g.ctx, 2, 1, 64), dtype=torch.uint8, device="cuda")
+    args = (g.ctx, g.state, d["k"], d["v"], d["q"], d["theta"], d["eta"], d["alpha"], y, ws, T.TM_READ_PER_TOKEN)
+    try:
+        T.tm_graphs_enable(False)
+        T.tm_state_init(g.ctx, g.state, 2, 1, g.init)
+        T.tm_forward_ex(*args)
+        y_ref, s_ref = y.cpu().numpy().copy(), g.export()
+        T.tm_graphs_enable(True)
+        for rep in range(4):
+            y.fill_(float("nan"))
+            T.tm_state_init(g.ctx, g.state, 2, 1, g.init)
+            T.tm_forward_ex(*args)
+            torch.cuda.synchronize()
+            assert np.array_equal(y.cpu().numpy(), y_ref), rep
+            assert np.array_equal(g.export(), s_ref), rep
+            torch.cuda.synchronize()
+    finally:
+        T.tm_graphs_enable(True)
+        g.close()
