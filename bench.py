@@ -397,8 +397,9 @@ def main():
 
     # the same steps again with HIP events around every launch (events force
     # direct launches): per-kernel durations for the roofline
-    T.tm_timing_enable(0x1F)
-    for c in range(5):
+    classes = (T.K_SCAN, T.K_FWD, T.K_BWD, T.K_FIRST)
+    T.tm_timing_enable(sum(1 << c for c in classes))
+    for c in classes:
         T.tm_timing_read(c)
     torch.cuda.synchronize()
     e0 = time.perf_counter()
@@ -407,19 +408,17 @@ def main():
     torch.cuda.synchronize()
     e1 = time.perf_counter()
     T.tm_timing_enable(0)
-    names = {T.K_SCAN: "scan", T.K_FWD: "fwd", T.K_BWD: "bwd", T.K_UPDATE: "update", T.K_FIRST: "first"}
+    names = {T.K_SCAN: "scan", T.K_FWD: "fwd", T.K_BWD: "bwd", T.K_FIRST: "first"}
     per = {nm: T.tm_timing_read(c) for c, nm in names.items()}
 
     # algorithmic work per step of each class
     fl = first_layer_launches(wl, ns, Tn)
-    C = Tn // wl.chunk
     work = {
         "first": ("hbm", sum(fl)),
-        "update": ("hbm", update_launch_bytes(wl, ns) * (C if wl.depth >= 2 else 0)),
         "fwd": ("mfma", fwd_flops(wl, ns, Tn)),
         "bwd": ("mfma", bwd_flops(wl, ns, Tn)),
     }
-    kernel_names = {"first": "first_layer_kernel", "update": "update_kernel", "fwd": "gemm_kernel",
+    kernel_names = {"first": "first_layer_kernel", "fwd": "gemm_kernel",
                     "bwd": "gemm_kernel", "scan": "scan_kernel"}
     kernels = {}
     for nm, (ms, n) in per.items():

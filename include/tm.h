@@ -211,9 +211,11 @@ tm_status tm_w1_split_enable(int on);
 
 /* Instrumentation for measuring kernels in place (not part of the method).
  * Kernel classes: 0 coefficient scan (and key transpose), 1 chunk forward
- * products of layers 1.., 2 chunk backward products, 3 gradient reduction +
- * state update of layers 1.., 4 first-layer step (the first layer's update,
- * its in-place backward, and its forward), 5 the per-token read's products,
+ * products of layers 1.., 2 chunk backward products, 3 none (kept for
+ * numbering: the update of layers 1.. runs inside the first-layer step
+ * launch), 4 first-layer step (the first layer's update, its in-place
+ * backward, and its forward, with the other layers' updates riding in the
+ * same launch), 5 the per-token read's products,
  * 6 the input side's projection kernel (tm_project; its history kernel is
  * not timed).  While bit c of
  * class_mask is set, every launch of class c is bracketed by a pair of HIP

@@ -27,8 +27,8 @@ EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_w
             "tm_state_import", "tm_state_check", "tm_status_str", "tm_timing_enable", "tm_timing_read",
             "tm_graphs_enable", "tm_w1_split_enable", "tm_forward_ex", "tm_project")
 
-# kernel classes of tm_timing_enable / tm_timing_read
-K_SCAN, K_FWD, K_BWD, K_UPDATE, K_FIRST, K_TOKEN_READ, K_PROJECT = 0, 1, 2, 3, 4, 5, 6
+# kernel classes of tm_timing_enable / tm_timing_read (3 is unused)
+K_SCAN, K_FWD, K_BWD, K_FIRST, K_TOKEN_READ, K_PROJECT = 0, 1, 2, 4, 5, 6
 
 _lib = None
 _vp = ctypes.c_void_p

@@ -184,7 +184,8 @@ hipError_t compute_units(int* out) {
 }
 
 // ---- optional per-launch timing (tm_timing_enable / tm_timing_read) ----
-enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_UPD = 3, K_FIRST = 4, K_R3 = 5, K_PROJ = 6, K_CLASSES = 7 };
+// (class 3 is unused: the update of layers 1.. rides in the first-layer launch)
+enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_FIRST = 4, K_R3 = 5, K_PROJ = 6, K_CLASSES = 7 };
 struct Timed {
     hipEvent_t a, b;
     int kind;
