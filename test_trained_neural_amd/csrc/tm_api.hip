@@ -136,10 +136,10 @@ WsLayout ws_layout(const tm_ctx* c, long ns, long T) {
             w.r3x[i] = o; o += al256((size_t)ns * w.r3x_ss * 4);
         }
     }
-    // C of layer 0 for every chunk of the call, then one more for the layer
-    // being read (fp32 [16 ceil(b/16)][bp] each); pm_t, ps_t of every chunk
+    // C of layer 0 for every chunk of the call (fp32 [16 ceil(b/16)][bp]
+    // each; the other layers form theirs in place); pm_t, ps_t of every chunk
     w.r3c_cs = ((b + 15) / 16 * 16) * w.bp;
-    w.r3c_ss = (C + 1) * w.r3c_cs;
+    w.r3c_ss = C * w.r3c_cs;
     w.r3c = o; o += al256((size_t)ns * w.r3c_ss * 4);
     w.r3p_ss = C * 2 * b;
     w.r3p = o; o += al256((size_t)ns * w.r3p_ss * 4);
@@ -538,9 +538,10 @@ tm_status run_token_scores(const tm_ctx* c, long ns, const WsLayout& w, char* ws
 
 // Per-token read of chunk ci (every query through the memory as its own
 // token's write left it), between the chunk's forward / backward and the
-// step that writes it, so the state still holds the chunk-start weights: per
-// layer the rows (layer 0 forms its Delta in place), after the layer's C for
-// the layers past the first; the last layer writes y.
+// step that writes it, so the state still holds the chunk-start weights: one
+// launch per layer (layer 0 forms its Delta in place and reads its C from
+// the call's score launch; the layers past it form their C in place); the
+// last layer writes y.
 tm_status run_token_read(const tm_ctx* c, char* state, long ns, const WsLayout& w, char* ws,
                          const TokLayout& tl, int ci, const void* v, const float* theta, const float* eta,
                          const float* alpha, float* y, int n_tokens, int heads, const float* m1, long m1_ss,
@@ -566,21 +567,17 @@ tm_status run_token_read(const tm_ctx* c, char* state, long ns, const WsLayout& 
             r.hk_ss = w.x_ss;
             r.sc = cbuf + (size_t)ci * w.r3c_cs;
         } else {
-            // the keys' rows of the store's forward (no query rows: keys from row 0)
+            // the keys' rows of the store's forward (no query rows: keys from
+            // row 0); the layer forms its C in place from them and the gates
             r.a = ws + w.r3x[(l - 1) & 1];
             r.a_ss = w.r3x_ss;
             r.hk = ws + w.act[l - 1];
             r.hk_ss = w.act_ss;
-            r.sco = cbuf + (size_t)w.C * w.r3c_cs;
-            r.sc_ss = w.r3c_ss;
             r.theta = theta;
             r.eta = eta;
             r.alpha = alpha;
             r.gl = TokLayout{n_tokens, heads, 1};
             r.g0 = ci * b;
-            if (timed(K_R3, st, [&] { return launch_r3_score(r, (int)ns, 1, f32 ? 1 : 0, st); }) != hipSuccess)
-                return TM_ERR_HIP;
-            r.sc = r.sco;
         }
         r.sc_ss = w.r3c_ss;
         r.pq = reinterpret_cast<float*>(ws + w.r3p) + (size_t)ci * 2 * b;

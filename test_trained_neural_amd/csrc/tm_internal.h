@@ -300,18 +300,23 @@ struct ProjArgs {
 //     C_ti = c_ti (x_t . H_i),
 // the chunk start's products plus a causal b x b correction (the dual form
 // of chunked linear attention).  Two kernels:
-//   score  C of one layer (fp32, [16 ceil(b/16)][bp] per chunk, zeros off
-//          the causal triangle and past the chunk) and, with layer 0, pm_t
-//          and ps_t; layer 0's depend on the inputs only, so one launch
-//          covers every chunk of the call (blockIdx.z = chunk);
+//   score  C of layer 0 (fp32, [16 ceil(b/16)][bp] per chunk, zeros off
+//          the causal triangle and past the chunk) and pm_t, ps_t: they
+//          depend on the inputs only, so one launch covers every chunk of
+//          the call (blockIdx.z = chunk);
 //   layer  one layer's rows: z = pm_t x M + ps_t x S - C Delta, then
 //          SiLU(z) (packed [b][N], the next layer's x) or y = z (the last
 //          layer).  Layer 0 forms its Delta in place: (Delta_1 W_1^T) .
-//          SiLU'(z_0) for depth >= 2, 2 (k M - v) for depth 1.
+//          SiLU'(z_0) for depth >= 2, 2 (k M - v) for depth 1; the layers
+//          past it read Delta from the store's products and form their C in
+//          place (the scores ride in the same K steps as x M and x S).
 // c_ti, pm_t, ps_t come from the chunk's gates by the recurrences of the
 // momentum and the forgetting (no ratios of running products).
 enum { BL_CF0 = 0, BL_CF1 = 1, BL_ROW = 2, BL_CF1T = 3 };   // layout of an fp32 B operand
-enum { R3D_BUF = 0, R3D_BWD = 1, R3D_OUT = 2 };              // where a layer's Delta comes from
+// where a layer's Delta (and C) come from: BUF Delta from dl and C formed in
+// place (the layers past the first); BWD, OUT Delta formed in place and C
+// from sc (layer 0)
+enum { R3D_BUF = 0, R3D_BWD = 1, R3D_OUT = 2 };
 struct R3Args {
     int b, bp, K, N;
     int bl;                   // BL_*: layout of the layer's M and S
@@ -323,7 +328,7 @@ struct R3Args {
     const float* M;           // fp32 M and S of the layer (stream strides m_ss, s_ss)
     const float* S;
     long m_ss, s_ss;
-    const float* sc;          // C, fp32 [16 ceil(b/16)][bp] (stream stride sc_ss, chunk stride sc_cs)
+    const float* sc;          // layer 0: C, fp32 [16 ceil(b/16)][bp] (stream stride sc_ss, chunk stride sc_cs)
     long sc_ss, sc_cs;
     float* sco;               // score: where C is written (same strides)
     const void* dl;           // BUF: the key rows' Delta, packed [b][N]
@@ -337,7 +342,7 @@ struct R3Args {
     long dsl_ss, dsl_ld;
     const void* v;            // OUT: values of tokens vt0 + i
     int vt0;
-    const float* theta;       // score: gates of tokens g0 + z b + t
+    const float* theta;       // score, BUF: gates of tokens g0 + z b + t
     const float* eta;
     const float* alpha;
     TokLayout gl;

@@ -33,7 +33,9 @@ constexpr int RTP = 17;    // padded LDS row of a 16-column tile
 constexpr int RCP = 68;    // LDS row of C and of Delta transposed (16-byte aligned)
 constexpr int r3_score_lds(int sw) { return (sw * 64 * RTP + 3 * 64 + 64 * RTP) * 4; }
 constexpr int R3_STAGE = 1024;   // floats of a wave's staging area (W_1's M and S blocks of one K step)
-constexpr int R3_LAYER_LDS = (2 * RW * 64 * RTP + 64 * RCP + 16 * RCP + 2 * 64 + RW * R3_STAGE) * 4;
+constexpr int R3_NSC = RMR * (RMR + 1) / 2;   // score tiles on and below the diagonal
+constexpr int R3_LAYER_LDS = (2 * RW * 64 * RTP + RW * R3_STAGE + 64 * RCP + 16 * RCP + 2 * 64 + 3 * 64) * 4;
+static_assert(RW * 64 * RTP + RW * R3_STAGE >= (RW / 2) * R3_NSC * 256, "score reduction space");
 
 // 8 consecutive K values k0 .. k0 + 7 (k0 a multiple of 8) of column n of an
 // fp32 B operand held in a layer's state layout.
@@ -199,32 +201,44 @@ template <class OP, int BL, int DK>
 __global__ __launch_bounds__(RW * 64) void r3_layer_kernel(R3Args r) {
     typedef typename Frag<OP>::T F;
     // ring depth within the register budget (the row-major layout's strided
-    // loads carry an address per value)
-    constexpr int PF = (sizeof(OP) == 2 && DK != R3D_OUT && BL != BL_ROW) ? 3 : 2;
+    // loads carry an address per value; the key rows ride in the ring of the
+    // layers that form their scores in place)
+    constexpr int PF = sizeof(OP) == 2 ? ((DK == R3D_BWD && BL != BL_ROW) ? 3 : 2) : (DK == R3D_BUF ? 1 : 2);
     extern __shared__ __attribute__((aligned(16))) float lds[];
     float* zp = lds;                        // [RW][64][RTP]: pm x M + ps x S, per wave
     float* dp = zp + RW * 64 * RTP;         // [RW][64][RTP]: the Delta products, per wave
-    float* cT = dp + RW * 64 * RTP;         // [64][RCP]: C
+    float* stage = dp + RW * 64 * RTP;      // [RW][R3_STAGE]: W_1's blocks on their way to B fragments
+    float* sred = dp;                       // (after the products) the score tiles' reduction: dp, stage
+    float* cT = stage + RW * R3_STAGE;      // [64][RCP]: C
     float* dT = cT + 64 * RCP;              // [16][RCP]: Delta of the block's columns, transposed
     float* pmps = dT + 16 * RCP;            // pm_t, then ps_t
-    float* stage = pmps + 2 * 64;           // [RW][R3_STAGE]: W_1's blocks on their way to B fragments
+    float* gt = pmps + 2 * 64;              // BUF: theta, eta, alpha of the chunk's tokens
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = blockIdx.y, nb = blockIdx.x;
     const int n = nb * 16 + (lane & 15), kofs = 8 * (lane >> 4);
     const int b = r.b, mr = (b + 15) >> 4, nsk = r.K >> 5, nbp4 = r.bp >> 2;
 
-    // the epilogue's operands, requested first: pm_t, ps_t, C, and the
-    // Delta of the key rows (from memory for the layers past the first)
+    // the epilogue's operands, requested first: pm_t, ps_t, C (layer 0; the
+    // layers past it form C in place from the gates) and the Delta of the
+    // key rows (from memory for the layers past the first)
     if (tid < b) {
         pmps[tid] = r.pq[(long)s * r.pq_ss + tid];
         pmps[64 + tid] = r.pq[(long)s * r.pq_ss + b + tid];
+        if constexpr (DK == R3D_BUF) {
+            const long go = tok_off(r.gl, s, r.g0 + tid);
+            gt[tid] = r.theta[go];
+            gt[64 + tid] = r.eta[go];
+            gt[128 + tid] = r.alpha[go];
+        }
     }
-    const float* Cg = r.sc + (long)s * r.sc_ss;
     f32x4 cv[2];
+    if constexpr (DK != R3D_BUF) {
+        const float* Cg = r.sc + (long)s * r.sc_ss;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int idx = tid + q * RW * 64, t = idx / nbp4;
-        cv[q] = *reinterpret_cast<const f32x4*>(Cg + (long)(t < 16 * mr ? t : 0) * r.bp + (idx % nbp4) * 4);
+        for (int q = 0; q < 2; ++q) {
+            const int idx = tid + q * RW * 64, t = idx / nbp4;
+            cv[q] = *reinterpret_cast<const f32x4*>(Cg + (long)(t < 16 * mr ? t : 0) * r.bp + (idx % nbp4) * 4);
+        }
     }
     // (BWD, OUT: SiLU'(z_0) or v of the Delta epilogue's elements)
     float dv[2] = {0.f, 0.f};
@@ -261,7 +275,7 @@ __global__ __launch_bounds__(RW * 64) void r3_layer_kernel(R3Args r) {
         for (int m = 0; m < RMR; ++m) {
             const int mm = m < mr ? m : mr - 1;
             xa[p][m] = ld8(X + pkf(mm, k, nsk, lane));
-            if constexpr (DK == R3D_OUT) ha[p][m] = ld8(H + pkf(mm, k, nsk, lane));
+            if constexpr (DK != R3D_BWD) ha[p][m] = ld8(H + pkf(mm, k, nsk, lane));
         }
         if constexpr (BL == BL_CF1) {
             // the step's two 16 x 16 blocks (inputs 32k .. 32k+31, the
@@ -293,9 +307,11 @@ __global__ __launch_bounds__(RW * 64) void r3_layer_kernel(R3Args r) {
         wb[p] = ldB<BL_CF1T>(W1, k * 32 + kofs, n, r.K1, r.N);
     };
 
-    f32x4 aM[RMR], aS[RMR], aD[RMR];
+    f32x4 aM[RMR], aS[RMR], aD[RMR], aC[R3_NSC];
 #pragma unroll
     for (int m = 0; m < RMR; ++m) aM[m] = aS[m] = aD[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < R3_NSC; ++q) aC[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < PF; ++p) load(p, min(sl.kb + p, sl.klast));
     if constexpr (DK == R3D_BWD) {
@@ -332,6 +348,14 @@ __global__ __launch_bounds__(RW * 64) void r3_layer_kernel(R3Args r) {
                 mma(aS[m], xa[p][m], vs);
                 if constexpr (DK == R3D_OUT) mma(aD[m], ha[p][m], vm);
             }
+            if constexpr (DK == R3D_BUF) {
+                // the scores x_t . H_i of query block m and key block j <= m
+                const F* kf = ha[p];
+#pragma unroll
+                for (int m = 0; m < RMR; ++m)
+#pragma unroll
+                    for (int j = 0; j <= m; ++j) mma(aC[m * (m + 1) / 2 + j], xa[p][m], keep_if(kf[j], live));
+            }
             load(p, min(k + p + PF, sl.klast));
         }
     }
@@ -347,17 +371,80 @@ __global__ __launch_bounds__(RW * 64) void r3_layer_kernel(R3Args r) {
         }
     }
 
-    // C and the loaded Delta to LDS
+    // C (or, formed in place, the score tiles) and the loaded Delta to LDS
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int idx = tid + q * RW * 64, t = idx / nbp4, c4 = (idx % nbp4) * 4;
-        if (t < 16 * mr) {
+        if constexpr (DK != R3D_BUF) {
+            if (t < 16 * mr) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) cT[t * RCP + c4 + e] = cv[q][e];
+                for (int e = 0; e < 4; ++e) cT[t * RCP + c4 + e] = cv[q][e];
+            }
         }
         if constexpr (DK == R3D_BUF) dT[(idx & 15) * RCP + (idx >> 4)] = dv[q];
     }
-    __syncthreads();   // pm_t, ps_t visible
+    __syncthreads();   // pm_t, ps_t, the gates visible; every wave past its products
+    if constexpr (DK == R3D_BUF) {
+        // the score tiles summed over the waves in two rounds (waves 4..7
+        // store, waves 0..3 add theirs; the slots sum in wave order below),
+        // while wave 4 walks the coefficient rows into C's place
+        f32x4* slot = reinterpret_cast<f32x4*>(sred) + (wave % (RW / 2)) * R3_NSC * 64 + lane;
+        if (wave >= RW / 2) {
+#pragma unroll
+            for (int q = 0; q < R3_NSC; ++q) slot[q * 64] = aC[q];
+        }
+        __syncthreads();
+        if (wave < RW / 2) {
+#pragma unroll
+            for (int q = 0; q < R3_NSC; ++q) {
+                const f32x4 o = slot[q * 64];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) aC[q][e] += o[e];
+                slot[q * 64] = aC[q];
+            }
+        } else if (wave == RW / 2) {
+            // row t: c_ti = theta_i w_i, w_i = A_i + eta_{i+1} w_{i+1},
+            // A_i = prod_{i < j <= t} (1 - alpha_j), from w_t = A_t = 1
+            // down; every lane takes the same steps (rows above t hold the
+            // start value) and stores in groups of 16
+            const int t = lane;
+            float Ap = 1.f, wv = 1.f;
+#pragma unroll
+            for (int i0 = 48; i0 >= 0; i0 -= 16) {
+                float cr[16];
+#pragma unroll
+                for (int e = 15; e >= 0; --e) {
+                    const int i = i0 + e;
+                    if (i + 1 < 64) {
+                        const float ap = Ap * (1.0f - gt[128 + i + 1]);
+                        const float w = __builtin_fmaf(gt[64 + i + 1], wv, ap);
+                        Ap = i < t ? ap : 1.0f;
+                        wv = i < t ? w : 1.0f;
+                    }
+                    cr[e] = gt[i] * wv;
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e) cT[t * RCP + i0 + e] = cr[e];
+            }
+        }
+        __syncthreads();
+        // C = c_ti (x_t . H_i) on and below the diagonal inside the chunk,
+        // zeros elsewhere (a select: rows past the chunk are not defined)
+        for (int idx = tid; idx < 64 * 64; idx += RW * 64) {
+            const int t = idx >> 6, i = idx & 63;
+            float v = 0.f;
+            if (t < b && i <= t) {
+                const int q = (t >> 4) * ((t >> 4) + 1) / 2 + (i >> 4);
+                const int ln = (i & 15) + 16 * ((t & 15) >> 2), e = t & 3;
+                float sc = 0.f;
+#pragma unroll
+                for (int w = 0; w < RW / 2; ++w) sc += sred[((w * R3_NSC + q) * 64 + ln) * 4 + e];
+                v = cT[t * RCP + i] * sc;
+            }
+            cT[t * RCP + i] = v;
+        }
+        // (the next barrier orders these writes before the correction)
+    }
     float* zm = zp + wave * 64 * RTP;
     float* dm = dp + wave * 64 * RTP;
 #pragma unroll
