@@ -132,9 +132,9 @@ tm_status tm_forward(const tm_ctx* ctx, void* state, const void* k, const void* 
  * section: a linear-attention output is a lookup in a memory updated at
  * every step; Technical Details / Parallel training for the chunking).  It
  * is computed by the dual form: the chunk start's products of the queries
- * plus a causal b x b correction per layer, in 2 depth + 1 extra launches
- * per chunk; W_1's update then stays in the first-layer blocks.  The last
- * query of each chunk reads what TM_READ_AFTER_WRITE reads.  An unknown read
+ * plus a causal b x b correction per layer, one extra launch per layer and
+ * chunk (and one per call for layer 0's scores).  The last query of each
+ * chunk reads what TM_READ_AFTER_WRITE reads.  An unknown read
  * value gives TM_ERR_INVALID; everything else as for tm_forward. */
 tm_status tm_forward_ex(const tm_ctx* ctx, void* state, const void* k, const void* v,
                         const void* q, const float* theta, const float* eta,
