@@ -395,6 +395,18 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    # per-step spread: the same steps again, each between two events on the
+    # stream (graph replay as above)
+    step_ms = []
+    for _ in range(args.steps):
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record()
+        step()
+        eb.record()
+        eb.synchronize()
+        step_ms.append(ea.elapsed_time(eb))
+    step_ms.sort()
+
     # the same steps again with HIP events around every launch (events force
     # direct launches): per-kernel durations for the roofline
     classes = (T.K_SCAN, T.K_FWD, T.K_BWD, T.K_FIRST)
@@ -466,6 +478,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": elapsed / args.steps * 1e3,
+        "step_ms": {"min": step_ms[0], "median": step_ms[len(step_ms) // 2],
+                    "timing": "events around each step on its stream, a separate pass of the same steps"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
