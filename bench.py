@@ -257,6 +257,65 @@ def other_workload(name, steps, calls=None, read=None, oracle=False):
     return out
 
 
+def retrieval(name, steps, oracle=False):
+    """Read-only retrieval (tm_retrieve: every query through the current
+    memory, no write) of the workload's first call's queries, after storing
+    that call; tokens/s and the products' MFMA roofline."""
+    import torch
+    import test_trained_neural_amd as T
+    from test_trained_neural_amd import inputs as I
+    wl = I.WORKLOADS[name]
+    Bn, Tn, H, d = wl.batch, wl.tokens_per_call, wl.heads, wl.dim
+    params = I.make_params(wl, 0)
+    ci = I.make_call(wl, params, 0, 0)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    k, v, q = (torch.from_numpy(x).to(dev).to(tdt) for x in (ci.k, ci.v, ci.q))
+    th, et, al = (torch.from_numpy(x).to(dev) for x in (ci.theta, ci.eta, ci.alpha))
+    ctx = T.tm_create(d, wl.depth, wl.expansion, wl.chunk)
+    state = torch.empty(T.tm_state_bytes(ctx, Bn, H), dtype=torch.uint8, device=dev)
+    ws = torch.empty(T.tm_workspace_bytes(ctx, Bn, H, Tn), dtype=torch.uint8, device=dev)
+    y = torch.empty((Bn, Tn, H, d), dtype=torch.float32, device=dev)
+    T.tm_state_init(ctx, state, Bn, H, torch.from_numpy(params.init_weights).to(dev))
+    T.tm_store(ctx, state, k, v, th, et, al, ws)
+
+    def step():
+        T.tm_retrieve(ctx, state, q, y, ws)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    T.tm_timing_enable(1 << T.K_FWD)
+    T.tm_timing_read(T.K_FWD)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    T.tm_timing_enable(0)
+    ms, n = T.tm_timing_read(T.K_FWD)
+    flops = 2 * Bn * H * Tn * sum(a * b for a, b in wl.layer_dims()) * steps
+    out = {"tokens_per_s": Bn * Tn / dt, "ms_per_step": dt * 1e3, "steps": steps,
+           "step": "tm_retrieve of (%d, %d) queries through the memory after storing them" % (Bn, Tn),
+           "roofline": mfma_roofline(flops, ms, n, wl.dtype, "gemm_kernel")}
+    T.tm_destroy(ctx)
+    if oracle:
+        from oracle import tmref
+        st = I.initial_state(wl, params)
+        tmref.forward(wl.dim, wl.depth, wl.expansion, wl.chunk, st, ci.k, ci.v, ci.theta, ci.eta, ci.alpha)
+        nt = min(os.cpu_count() or 1, Bn * H)
+        t1 = time.perf_counter()
+        tmref.retrieve(wl.dim, wl.depth, wl.expansion, st, ci.q, n_threads=nt)
+        odt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": Bn * Tn / odt, "unit": "tokens/s", "cores": nt, "kind": "oracle",
+                               "sample": "%s: retrieve of one call's queries (%d streams x %d tokens), fp64 C "
+                                         "oracle, %.2f s" % (wl.name, Bn * H, Tn, odt)}
+    return out
+
+
 def input_side(name, steps, oracle=False):
     """The input side (tm_project: x -> k, v, q and the gates, 4-tap
     convolution) alone and chained with the memory step (tm_project +
@@ -504,6 +563,8 @@ def main():
             "mlp384_read_before_write": other_workload("mlp384", 20, read=1, oracle=not args.no_cpu_baseline),
             # each query read right after its own token's write (the dual form)
             "mlp384_read_per_token": other_workload("mlp384", 20, read=2, oracle=not args.no_cpu_baseline),
+            # read-only retrieval of the call's queries through the stored memory
+            "mlp384_retrieve": retrieval("mlp384", 20, oracle=not args.no_cpu_baseline),
         }
         side = input_side("mlp384", 20, oracle=not args.no_cpu_baseline)
         out["other_workloads"]["mlp384_input_side"] = side["input_side"]

@@ -48,6 +48,7 @@ struct tm_ctx {
 namespace {
 
 constexpr long RET_ROWS = 2048;   // query rows per stream per retrieve pass
+constexpr int RET_TILED_ROWS = 256;   // from this many rows a retrieve pass uses the tiled product
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -457,7 +458,11 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
                 g.coef_ss = w.coef_ss;
             }
         }
-        hipError_t e = timed(K_FWD, st, [&] { return launch_fwd(g, (int)ns, f32 ? 1 : 0, st); });
+        // (a retrieve pass of many rows: a plain tiled product, no split K)
+        const bool big = retrieve && !f32 && rows >= RET_TILED_ROWS;
+        hipError_t e = timed(K_FWD, st, [&] {
+            return big ? launch_rows(g, (int)ns, st) : launch_fwd(g, (int)ns, f32 ? 1 : 0, st);
+        });
         if (e != hipSuccess) return TM_ERR_HIP;
     }
     return TM_OK;

@@ -360,6 +360,12 @@ struct R3Args {
 hipError_t launch_r3_score(const R3Args& r, int ns, int nchunks, int f32, hipStream_t st);
 hipError_t launch_r3_layer(const R3Args& r, int ns, int f32, hipStream_t st);
 
+// ---- launchers (tm_retrieve.hip) ----
+// A retrieve pass's product of many query rows (bf16: tokens or packed rows
+// times the packed bf16 copy; EPI_HIDDEN without SiLU' and transposes, or
+// EPI_OUT with query rows only).
+hipError_t launch_rows(const GemmArgs& g, int ns, hipStream_t st);
+
 // ---- launchers (tm_project.hip) ----
 hipError_t launch_project(const ProjArgs& p, int f32, hipStream_t st);
 

@@ -169,6 +169,40 @@ def test_retrieve_is_read_only_and_matches_oracle():
         g.close()
 
 
+# retrieve passes of many query rows (the tiled product): a full pass of 2048
+# rows and a short second pass, a ragged row count inside one pass, a hidden
+# width that is not a multiple of 64, depth 1 to 3
+RET_CASES = [
+    small("ret_rows_2pass", 64, 2, 4, 16, 1, 2, 2100, "bf16"),
+    small("ret_rows_ragged", 96, 3, 3, 16, 2, 1, 1000, "bf16"),
+    small("ret_rows_lin", 128, 1, 1, 16, 1, 1, 512, "bf16"),
+]
+
+
+@pytest.mark.parametrize("wl", RET_CASES, ids=lambda w: w.name)
+def test_retrieve_many_rows(wl):
+    say("case", wl)
+    p = I.make_params(wl)
+    g = GpuMemory(wl, p)
+    ci = I.make_call(wl, p)
+    d = dev_inputs(ci, "bf16")
+    # store a first chunk-aligned prefix, then read every query
+    n = (min(wl.seq, 256) // wl.chunk) * wl.chunk
+    pre = {k: v[:, :n].contiguous() for k, v in d.items()}
+    g.store(pre)
+    ref = I.initial_state(wl, p)
+    cp = I.CallInputs(*(np.ascontiguousarray(getattr(ci, f)[:, :n]) for f in ("k", "v", "q", "theta", "eta", "alpha")))
+    oracle_forward(wl, ref, cp, with_q=False)
+    before = g.export()
+    y = g.retrieve(d["q"]).cpu().numpy()
+    assert np.array_equal(before, g.export())
+    yr = tmref.retrieve(wl.dim, wl.depth, wl.expansion, ref, ci.q)
+    e = relerr(y, yr)
+    say("  y %.2e" % e)
+    assert np.all(np.isfinite(y)) and e < TOL["bf16"]
+    g.close()
+
+
 def test_call_split_and_determinism():
     wl = small("split", 64, 2, 2, 16, 2, 1, 96, "bf16")
     say("case", wl)
