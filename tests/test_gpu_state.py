@@ -37,3 +37,26 @@ def test_state_header_mismatch_is_refused():
     finally:
         T.tm_destroy(other)
         g.close()
+
+
+def test_nan_input_sets_the_nonfinite_flag():
+    # a NaN in one key poisons the memory; the step kernels raise the sticky
+    # non-finite flag, as the oracle's state turns non-finite too
+    import test_trained_neural_amd as T
+    from harness import dev_inputs, oracle_forward
+    wl = small("nanflag", 64, 2, 2, 16, 1, 1, 64, "f32")
+    say("case", wl)
+    p = I.make_params(wl)
+    ci = I.make_call(wl, p)
+    ci.k[0, 20, 0, 3] = np.nan
+    g = GpuMemory(wl, p)
+    g.forward(dev_inputs(ci, "f32"))
+    nf, pos = g.check()
+    ref = I.initial_state(wl, p)
+    oracle_forward(wl, ref, ci)
+    assert not np.all(np.isfinite(ref))
+    assert nf and pos == 64
+    # the flag is sticky: a clean call after it leaves it set
+    g.forward(dev_inputs(I.make_call(wl, p, 1), "f32"))
+    assert g.check()[0]
+    g.close()
