@@ -172,6 +172,37 @@ tm_status tm_project(const tm_ctx* ctx, const void* x, int model_dim, const void
                      float* theta, float* eta, float* alpha, int batch, int heads,
                      int n_tokens, tm_dtype dtype, void* stream);
 
+/* Memory-side wiring of memory as a context (MAC: "Titans, explained" step
+ * 8; "Attack of the Titans", Technical Details, memory as a context).  A
+ * segment's tokens query the memory (tm_retrieve through the memory before
+ * the segment is written); the recalled vectors sit between the persistent
+ * tokens and the segment in the window attention runs over; the attention
+ * output y is written into the memory (tm_project of y, then tm_store) and
+ * gates the final output through the memory's read of it (tm_retrieve of y's
+ * queries after the write).  Attention and the persistent tokens' values are
+ * the caller's.  These two calls are the wiring the memory's own calls do
+ * not cover; both only move and multiply elements.
+ *
+ * tm_mac_window: window [batch][n_persist + 2 seg_len][model_dim] (dtype) =
+ *   persistent [n_persist][model_dim] (dtype; shared over the batch), then
+ *   recalled [batch][seg_len][model_dim] (fp32, the memory's read of the
+ *   segment, rounded to dtype to nearest even), then segment
+ *   [batch][seg_len][model_dim] (dtype).  n_persist may be 0 (persistent
+ *   may then be null).
+ * tm_mac_gate: out [batch][seg_len][model_dim] fp32 = y * mem element-wise,
+ *   y the attention output for the segment's positions (dtype), mem the
+ *   memory's fp32 read of y.  The pages fix no form for this gate; the
+ *   element-wise product of the output and the memory's read of it is the
+ *   plainest.
+ * model_dim: a positive multiple of 32; seg_len > 0, batch > 0; pointers
+ * 16-byte aligned (else TM_ERR_INVALID, bad dtype TM_ERR_DTYPE), all on the
+ * host before any launch.  Asynchronous on `stream`; one launch each. */
+tm_status tm_mac_window(const void* persistent, int n_persist, const float* recalled,
+                        const void* segment, void* window, int batch, int seg_len, int model_dim,
+                        tm_dtype dtype, void* stream);
+tm_status tm_mac_gate(const void* y, const float* mem, float* out, int batch, int seg_len,
+                      int model_dim, tm_dtype dtype, void* stream);
+
 /* Canonical fp32 copy of the state: dst is [batch*heads][2P], per stream
  * M_1..M_L then S_1..S_L, each W_l row-major [d_in][d_out]. */
 tm_status tm_state_export(const tm_ctx* ctx, const void* state, int batch, int heads,

@@ -25,7 +25,8 @@ TM_READ_AFTER_WRITE, TM_READ_BEFORE_WRITE, TM_READ_PER_TOKEN = 0, 1, 2
 EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_workspace_bytes",
             "tm_state_init", "tm_store", "tm_retrieve", "tm_forward", "tm_state_export",
             "tm_state_import", "tm_state_check", "tm_status_str", "tm_timing_enable", "tm_timing_read",
-            "tm_graphs_enable", "tm_w1_split_enable", "tm_forward_ex", "tm_project")
+            "tm_graphs_enable", "tm_w1_split_enable", "tm_forward_ex", "tm_project", "tm_mac_window",
+            "tm_mac_gate")
 
 # kernel classes of tm_timing_enable / tm_timing_read (3 is unused)
 K_SCAN, K_FWD, K_BWD, K_FIRST, K_TOKEN_READ, K_PROJECT = 0, 1, 2, 4, 5, 6
@@ -74,6 +75,10 @@ def lib():
         L.tm_project.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _i, _i, _i, _i, _vp]
         L.tm_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
+        L.tm_mac_window.restype = _i
+        L.tm_mac_window.argtypes = [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
+        L.tm_mac_gate.restype = _i
+        L.tm_mac_gate.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp]
         L.tm_state_export.restype = _i
         L.tm_state_export.argtypes = [_vp, _vp, _i, _i, _vp, _vp]
         L.tm_state_import.restype = _i
@@ -190,6 +195,26 @@ def tm_forward_ex(ctx, state, k, v, q, theta, eta, alpha, y, workspace, read, st
                                                 int(read), _ptr(workspace), _stream(stream)))
 
 
+def tm_mac_window(persistent, recalled, segment, window, stream=None):
+    """window [B][P+2S][D] = [persistent [P][D]; recalled [B][S][D] (fp32,
+    rounded to the segment's dtype); segment [B][S][D]]."""
+    _tok(recalled, segment, window)
+    if persistent is not None:
+        _tok(persistent)
+    B, S, D = segment.shape
+    P = 0 if persistent is None else persistent.shape[0]
+    _check("tm_mac_window", lib().tm_mac_window(_ptr(persistent), P, _ptr(recalled), _ptr(segment), _ptr(window),
+                                                B, S, D, _dtype_code(segment), _stream(stream)))
+
+
+def tm_mac_gate(y, mem, out, stream=None):
+    """out [B][S][D] fp32 = y * mem element-wise."""
+    _tok(y, mem, out)
+    B, S, D = y.shape
+    _check("tm_mac_gate", lib().tm_mac_gate(_ptr(y), _ptr(mem), _ptr(out), B, S, D, _dtype_code(y),
+                                            _stream(stream)))
+
+
 def tm_project(ctx, x, w_kvq, conv, w_gate, gate_bias, history, k, v, q, theta, eta, alpha, heads,
                stream=None):
     """The input side: x [B][T][D] -> k, v, q [B][T][H][d] (x's dtype) and
@@ -253,6 +278,40 @@ class MemState:
     def __init__(self, mem, batch, heads, device):
         self.batch, self.heads = batch, heads
         self.buf = torch.empty(tm_state_bytes(mem.ctx, batch, heads), dtype=torch.uint8, device=device)
+
+
+def mac_segment(mem, state, x, persistent, attention, w_kvq, conv, w_gate, gate_bias, heads, hist_x=None,
+                hist_y=None):
+    """One segment of memory as a context, on the memory's side (argument
+    marshalling over the C calls).  x [B][S][D] (D = heads * dim; S a
+    multiple of the chunk) is the segment's model vectors; ``attention`` is
+    the caller's: window [B][P+2S][D] (x's dtype) -> y [B][S][D] for the
+    segment's positions, x's dtype.  The segment's queries (projections of x)
+    read the memory before the segment is written; y is written (its keys,
+    values and gates from the same projections) and read back through its
+    queries to gate y.  Returns (out [B][S][D] fp32, state).  hist_x, hist_y:
+    the two projection streams' convolution histories (see tm_project)."""
+    B, S, D = x.shape
+    dev, dt, d = x.device, x.dtype, mem.dim
+    P = 0 if persistent is None else persistent.shape[0]
+
+    def project(src, hist):
+        k, v, q = (torch.empty((B, S, heads, d), dtype=dt, device=dev) for _ in range(3))
+        g = [torch.empty((B, S, heads), dtype=torch.float32, device=dev) for _ in range(3)]
+        tm_project(mem.ctx, src, w_kvq, conv, w_gate, gate_bias, hist, k, v, q, g[0], g[1], g[2], heads)
+        return k, v, q, g
+
+    _, _, qx, _ = project(x, hist_x)
+    recalled = mem.retrieve(state, qx).view(B, S, D)
+    window = torch.empty((B, P + 2 * S, D), dtype=dt, device=dev)
+    tm_mac_window(persistent, recalled, x, window)
+    y = attention(window).contiguous()
+    ky, vy, qy, gy = project(y, hist_y)
+    mem.store(state, ky, vy, gy[0], gy[1], gy[2])
+    my = mem.retrieve(state, qy).view(B, S, D)
+    out = torch.empty((B, S, D), dtype=torch.float32, device=dev)
+    tm_mac_gate(y, my, out)
+    return out, state
 
 
 class NeuralMemory:

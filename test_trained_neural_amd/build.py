@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, f) for f in ("tm_kernels.hip", "tm_r3.hip", "tm_retrieve.hip", "tm_project.hip", "tm_api.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("tm_kernels.hip", "tm_r3.hip", "tm_retrieve.hip", "tm_project.hip", "tm_mac.hip", "tm_api.hip")]
 HEADERS = [os.path.join(CSRC, "tm_internal.h"), os.path.join(CSRC, "tm_device.h"), os.path.join(ROOT, "include", "tm.h")]
 LIB = os.path.join(HERE, "libtm.so")
 

@@ -1017,6 +1017,29 @@ tm_status tm_retrieve(const tm_ctx* c, const void* state_v, const void* q, float
     });
 }
 
+tm_status tm_mac_window(const void* persistent, int n_persist, const float* recalled, const void* segment,
+                        void* window, int batch, int seg_len, int model_dim, tm_dtype dtype, void* stream) {
+    if (dtype != TM_F32 && dtype != TM_BF16) return TM_ERR_DTYPE;
+    if (batch <= 0 || seg_len <= 0 || n_persist < 0 || model_dim < 32 || model_dim % 32 != 0 ||
+        (long)batch * (n_persist + 2L * seg_len) * model_dim > (1L << 40))
+        return TM_ERR_INVALID;
+    if (!tok_ok(recalled) || !tok_ok(segment) || !tok_ok(window) || (n_persist > 0 && !tok_ok(persistent)))
+        return TM_ERR_INVALID;
+    MacArgs a{persistent, recalled, segment, window, batch, seg_len, n_persist, model_dim};
+    return hip_status(launch_mac_window(a, dtype == TM_F32 ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
+tm_status tm_mac_gate(const void* y, const float* mem, float* out, int batch, int seg_len, int model_dim,
+                      tm_dtype dtype, void* stream) {
+    if (dtype != TM_F32 && dtype != TM_BF16) return TM_ERR_DTYPE;
+    if (batch <= 0 || seg_len <= 0 || model_dim < 32 || model_dim % 32 != 0 ||
+        (long)batch * seg_len * model_dim > (1L << 40))
+        return TM_ERR_INVALID;
+    if (!tok_ok(y) || !tok_ok(mem) || !tok_ok(out)) return TM_ERR_INVALID;
+    MacArgs a{nullptr, mem, y, out, batch, seg_len, 0, model_dim};
+    return hip_status(launch_mac_gate(a, dtype == TM_F32 ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
 tm_status tm_state_export(const tm_ctx* c, const void* state, int batch, int heads, float* dst,
                           void* stream) {
     if (!c || !state || !dst || batch <= 0 || heads <= 0) return TM_ERR_INVALID;

@@ -366,6 +366,20 @@ hipError_t launch_r3_layer(const R3Args& r, int ns, int f32, hipStream_t st);
 // EPI_OUT with query rows only).
 hipError_t launch_rows(const GemmArgs& g, int ns, hipStream_t st);
 
+// Memory-as-context wiring (tm_mac.hip).  Window: out [B][P+2S][D] (operand
+// type) = [persistent [P][D]; recalled [B][S][D] fp32, rounded; segment
+// [B][S][D]].  Gate: out [B][S][D] fp32 = segment (the attention output y,
+// operand type) * recalled (the memory's fp32 read of y).
+struct MacArgs {
+    const void* persistent;
+    const float* recalled;
+    const void* segment;
+    void* out;
+    int B, S, P, D;
+};
+hipError_t launch_mac_window(const MacArgs& a, int f32, hipStream_t st);
+hipError_t launch_mac_gate(const MacArgs& a, int f32, hipStream_t st);
+
 // ---- launchers (tm_project.hip) ----
 hipError_t launch_project(const ProjArgs& p, int f32, hipStream_t st);
 

@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     syms = declared_symbols()
-    assert len(syms) == 19
+    assert len(syms) == 21
     assert set(syms) == set(T.EXPORTED)
     L = ctypes.CDLL(T.LIB_PATH)
     for s in syms:
@@ -106,5 +106,16 @@ def test_call_validation_before_launch():
     assert P(c, A, 64, A, G, 4, G, G, G, A, A, A, G, G, G, 0, 1, 16, T.TM_BF16, st) == T.TM_ERR_INVALID
     # empty: a no-op (outputs and, for one tap, the history may be null)
     assert P(c, A, 64, A, G, 1, G, G, None, None, None, None, None, None, None, 1, 1, 0, T.TM_BF16, st) == T.TM_OK
+    # the memory-as-context wiring: sizes, dtype, alignment, all on the host
+    W, G = L.tm_mac_window, L.tm_mac_gate
+    assert W(A, 2, A, A, A, 1, 4, 64, 7, st) == T.TM_ERR_DTYPE
+    assert W(A, 2, A, A, A, 1, 4, 48, T.TM_BF16, st) == T.TM_ERR_INVALID
+    assert W(A, -1, A, A, A, 1, 4, 64, T.TM_BF16, st) == T.TM_ERR_INVALID
+    assert W(None, 2, A, A, A, 1, 4, 64, T.TM_BF16, st) == T.TM_ERR_INVALID
+    assert W(A, 2, A, A, A, 1, 0, 64, T.TM_BF16, st) == T.TM_ERR_INVALID
+    assert W(A, 2, ctypes.c_void_p((1 << 20) + 4), A, A, 1, 4, 64, T.TM_BF16, st) == T.TM_ERR_INVALID
+    assert G(A, A, A, 1, 4, 64, 7, st) == T.TM_ERR_DTYPE
+    assert G(A, A, None, 1, 4, 64, T.TM_F32, st) == T.TM_ERR_INVALID
+    assert G(A, A, A, 0, 4, 64, T.TM_F32, st) == T.TM_ERR_INVALID
     assert L.tm_status_str(T.TM_ERR_SHAPE).decode().startswith("n_tokens")
     T.tm_destroy(c)
