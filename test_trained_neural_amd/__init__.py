@@ -29,7 +29,7 @@ EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_w
             "tm_mac_gate")
 
 # kernel classes of tm_timing_enable / tm_timing_read (3 is unused)
-K_SCAN, K_FWD, K_BWD, K_FIRST, K_TOKEN_READ, K_PROJECT = 0, 1, 2, 4, 5, 6
+K_SCAN, K_FWD, K_BWD, K_FIRST, K_TOKEN_READ, K_PROJECT, K_MAC = 0, 1, 2, 4, 5, 6, 7
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -130,6 +130,32 @@ def _tok(*ts):
                 raise ValueError("token and gate tensors must be contiguous device tensors")
 
 
+def _same(dtype, *named):
+    """Each (name, tensor) pair holds ``dtype`` (None tensors are skipped)."""
+    for name, t in named:
+        if t is not None and t.dtype != dtype:
+            raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def _shape(name, t, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _memory_call(k, v, q, theta, eta, alpha, y):
+    """The token, gate and output tensors of a memory call: k, v, q
+    [B][T][H][d] of one operand type, the gates [B][T][H] and y [B][T][H][d]
+    fp32."""
+    lead = k if k is not None else q
+    _dtype_code(lead)
+    _same(lead.dtype, ("v", v), ("q", q), ("k", k))
+    _same(torch.float32, ("theta", theta), ("eta", eta), ("alpha", alpha), ("y", y))
+    for name, t in (("v", v), ("q", q), ("y", y)):
+        _shape(name, t, lead.shape)
+    for name, t in (("theta", theta), ("eta", eta), ("alpha", alpha)):
+        _shape(name, t, lead.shape[:3])
+
+
 # ---------------------------------------------------------------------------
 # the C calls, one to one
 
@@ -156,13 +182,14 @@ def tm_workspace_bytes(ctx, batch, heads, n_tokens):
 
 
 def tm_state_init(ctx, state, batch, heads, init_weights, stream=None):
+    _same(torch.float32, ("init_weights", init_weights))
     _tok(init_weights)
-    assert init_weights.dtype == torch.float32
     _check("tm_state_init", lib().tm_state_init(ctx, _ptr(state), batch, heads, _ptr(init_weights),
                                                 _stream(stream)))
 
 
 def tm_store(ctx, state, k, v, theta, eta, alpha, workspace, stream=None):
+    _memory_call(k, v, None, theta, eta, alpha, None)
     _tok(k, v, theta, eta, alpha)
     B, T, H, _ = k.shape
     _check("tm_store", lib().tm_store(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta),
@@ -171,6 +198,7 @@ def tm_store(ctx, state, k, v, theta, eta, alpha, workspace, stream=None):
 
 
 def tm_retrieve(ctx, state, q, y, workspace, stream=None):
+    _memory_call(None, None, q, None, None, None, y)
     _tok(q, y)
     B, T, H, _ = q.shape
     _check("tm_retrieve", lib().tm_retrieve(ctx, _ptr(state), _ptr(q), _ptr(y), B, H, T,
@@ -178,6 +206,7 @@ def tm_retrieve(ctx, state, q, y, workspace, stream=None):
 
 
 def tm_forward(ctx, state, k, v, q, theta, eta, alpha, y, workspace, stream=None):
+    _memory_call(k, v, q, theta, eta, alpha, y)
     _tok(k, v, q, theta, eta, alpha, y)
     B, T, H, _ = k.shape
     _check("tm_forward", lib().tm_forward(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(q), _ptr(theta),
@@ -188,6 +217,7 @@ def tm_forward(ctx, state, k, v, q, theta, eta, alpha, y, workspace, stream=None
 def tm_forward_ex(ctx, state, k, v, q, theta, eta, alpha, y, workspace, read, stream=None):
     """read: TM_READ_AFTER_WRITE (as tm_forward), TM_READ_BEFORE_WRITE or
     TM_READ_PER_TOKEN."""
+    _memory_call(k, v, q, theta, eta, alpha, y)
     _tok(k, v, q, theta, eta, alpha, y)
     B, T, H, _ = k.shape
     _check("tm_forward_ex", lib().tm_forward_ex(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(q), _ptr(theta),
@@ -198,17 +228,27 @@ def tm_forward_ex(ctx, state, k, v, q, theta, eta, alpha, y, workspace, read, st
 def tm_mac_window(persistent, recalled, segment, window, stream=None):
     """window [B][P+2S][D] = [persistent [P][D]; recalled [B][S][D] (fp32,
     rounded to the segment's dtype); segment [B][S][D]]."""
+    _dtype_code(segment)
+    _same(segment.dtype, ("persistent", persistent), ("window", window))
+    _same(torch.float32, ("recalled", recalled))
+    B, S, D = segment.shape
+    P = 0 if persistent is None else persistent.shape[0]
+    _shape("persistent", persistent, (P, D))
+    _shape("recalled", recalled, (B, S, D))
+    _shape("window", window, (B, P + 2 * S, D))
     _tok(recalled, segment, window)
     if persistent is not None:
         _tok(persistent)
-    B, S, D = segment.shape
-    P = 0 if persistent is None else persistent.shape[0]
     _check("tm_mac_window", lib().tm_mac_window(_ptr(persistent), P, _ptr(recalled), _ptr(segment), _ptr(window),
                                                 B, S, D, _dtype_code(segment), _stream(stream)))
 
 
 def tm_mac_gate(y, mem, out, stream=None):
     """out [B][S][D] fp32 = y * mem element-wise."""
+    _dtype_code(y)
+    _same(torch.float32, ("mem", mem), ("out", out))
+    _shape("mem", mem, y.shape)
+    _shape("out", out, y.shape)
     _tok(y, mem, out)
     B, S, D = y.shape
     _check("tm_mac_gate", lib().tm_mac_gate(_ptr(y), _ptr(mem), _ptr(out), B, S, D, _dtype_code(y),
@@ -220,9 +260,21 @@ def tm_project(ctx, x, w_kvq, conv, w_gate, gate_bias, history, k, v, q, theta, 
     """The input side: x [B][T][D] -> k, v, q [B][T][H][d] (x's dtype) and
     the gates [B][T][H] fp32; history [B][K-1][3][H*d] fp32 is read and
     rewritten (None for K = 1)."""
-    _tok(x, w_kvq, conv, w_gate, gate_bias, k, v, q, theta, eta, alpha)
+    _dtype_code(x)
+    _same(x.dtype, ("w_kvq", w_kvq))
+    _same(torch.float32, ("conv", conv), ("w_gate", w_gate), ("gate_bias", gate_bias), ("history", history))
     B, T, D = x.shape
     K = conv.shape[-1]
+    HD = w_kvq.shape[1]
+    _shape("w_kvq", w_kvq, (3, HD, D))
+    _shape("conv", conv, (3, HD, K))
+    _shape("w_gate", w_gate, (3, heads, D))
+    _shape("gate_bias", gate_bias, (3,))
+    if K > 1:
+        _shape("history", history, (B, K - 1, 3, HD))
+    _memory_call(k, v, q, theta, eta, alpha, None)
+    _shape("k", k, (B, T, heads, HD // heads))
+    _tok(x, w_kvq, conv, w_gate, gate_bias, k, v, q, theta, eta, alpha)
     if history is not None:
         _tok(history)
     _check("tm_project", lib().tm_project(ctx, _ptr(x), D, _ptr(w_kvq), _ptr(conv), K, _ptr(w_gate),
@@ -232,11 +284,13 @@ def tm_project(ctx, x, w_kvq, conv, w_gate, gate_bias, history, k, v, q, theta, 
 
 
 def tm_state_export(ctx, state, batch, heads, dst, stream=None):
+    _same(torch.float32, ("dst", dst))
     _check("tm_state_export", lib().tm_state_export(ctx, _ptr(state), batch, heads, _ptr(dst),
                                                     _stream(stream)))
 
 
 def tm_state_import(ctx, state, batch, heads, src, stream=None):
+    _same(torch.float32, ("src", src))
     _check("tm_state_import", lib().tm_state_import(ctx, _ptr(state), batch, heads, _ptr(src),
                                                     _stream(stream)))
 

@@ -119,3 +119,39 @@ def test_call_validation_before_launch():
     assert G(A, A, A, 0, 4, 64, T.TM_F32, st) == T.TM_ERR_INVALID
     assert L.tm_status_str(T.TM_ERR_SHAPE).decode().startswith("n_tokens")
     T.tm_destroy(c)
+
+
+def test_binding_checks_dtypes_and_shapes():
+    """The binding refuses tensors of the wrong element type or shape before
+    it passes any pointer on (the C calls take untyped pointers)."""
+    import torch
+    import test_trained_neural_amd as T
+    bf, f32, f64 = torch.bfloat16, torch.float32, torch.float64
+    B, S, D, P = 2, 4, 32, 1
+    seg = torch.zeros((B, S, D), dtype=bf)
+    with pytest.raises(TypeError, match="recalled"):
+        T.tm_mac_window(torch.zeros((P, D), dtype=bf), torch.zeros((B, S, D), dtype=f64), seg,
+                        torch.zeros((B, P + 2 * S, D), dtype=bf))
+    with pytest.raises(TypeError, match="window"):
+        T.tm_mac_window(None, torch.zeros((B, S, D)), seg, torch.zeros((B, 2 * S, D), dtype=f32))
+    with pytest.raises(ValueError, match="window"):
+        T.tm_mac_window(None, torch.zeros((B, S, D)), seg, torch.zeros((B, 2 * S + 1, D), dtype=bf))
+    with pytest.raises(TypeError, match="mem"):
+        T.tm_mac_gate(seg, torch.zeros((B, S, D), dtype=bf), torch.zeros((B, S, D)))
+    with pytest.raises(ValueError, match="out"):
+        T.tm_mac_gate(seg, torch.zeros((B, S, D)), torch.zeros((B, S, D + 1)))
+    k = torch.zeros((1, 8, 2, 32), dtype=bf)
+    g = torch.zeros((1, 8, 2))
+    y = torch.zeros((1, 8, 2, 32))
+    with pytest.raises(TypeError, match="theta"):
+        T.tm_forward(None, None, k, k, k, g.double(), g, g, y, None)
+    with pytest.raises(TypeError, match="q"):
+        T.tm_forward(None, None, k, k, k.float(), g, g, g, y, None)
+    with pytest.raises(TypeError, match="y"):
+        T.tm_retrieve(None, None, k, y.to(bf), None)
+    with pytest.raises(ValueError, match="alpha"):
+        T.tm_store(None, None, k, k, g, g, g[:, :4], None)
+    with pytest.raises(TypeError, match="bfloat16 or float32"):
+        T.tm_store(None, None, k.half(), k.half(), g, g, g, None)
+    with pytest.raises(TypeError, match="init_weights"):
+        T.tm_state_init(None, None, 1, 2, torch.zeros((2, 10), dtype=f64))

@@ -96,3 +96,32 @@ def test_mac_segments_chain():
         say("  segment %d: out %.2e" % (sgi, e))
         assert np.all(np.isfinite(want)) and e < TOL["bf16"]
     assert mem.check(st) == (False, 2 * S)
+
+
+def test_mac_timing_class():
+    """Both wiring kernels are counted under their timing class, and the
+    timed launches give the same bytes."""
+    import test_trained_neural_amd as T
+    B, S, D, P = 2, 16, 64, 3
+    g = torch.Generator().manual_seed(4)
+    pers_c = torch.randn((P, D), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    rec_c = torch.randn((B, S, D), generator=g, dtype=torch.float32)
+    seg_c = torch.randn((B, S, D), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    want_w = torch.cat([pers_c[None].expand(B, P, D), rec_c.to(torch.bfloat16), seg_c], dim=1)
+    want_o = seg_c.float() * rec_c
+    pers, rec, seg = pers_c.cuda(), rec_c.cuda(), seg_c.cuda()
+    for mask in (0, 1 << T.K_MAC):
+        T.tm_timing_enable(mask)
+        T.tm_timing_read(T.K_MAC)
+        w = torch.empty((B, P + 2 * S, D), dtype=torch.bfloat16, device="cuda")
+        o = torch.empty((B, S, D), dtype=torch.float32, device="cuda")
+        T.tm_mac_window(pers, rec, seg, w)
+        T.tm_mac_gate(seg, rec, o)
+        torch.cuda.synchronize()
+        ms, n = T.tm_timing_read(T.K_MAC)
+        T.tm_timing_enable(0)
+        assert n == (2 if mask else 0) and (ms > 0) == bool(mask)
+        bw = (w.cpu() != want_w).nonzero().tolist()
+        bo = (o.cpu() != want_o).nonzero().tolist()
+        say("mask %d: window mismatches %d %s, gate mismatches %d %s" % (mask, len(bw), bw[:4], len(bo), bo[:4]))
+        assert not bw and not bo

@@ -14,7 +14,16 @@ import torch
 from oracle import tmref
 from test_trained_neural_amd import inputs as I
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _float64_default():
+    """torch's default dtype is float64 inside these pins, and restored
+    after each (other modules build float32 tensors by default)."""
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
 
 
 # --------------------------------------------------------------------------
