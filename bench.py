@@ -374,10 +374,12 @@ def input_side(name, steps, oracle=False):
     out["input_side"]["roofline"] = mfma_roofline(project_flops(wl, Bn, Tn) * steps, ms, n, wl.dtype,
                                                   "project_kernel")
     if oracle:
+        from threadpoolctl import threadpool_limits
         from oracle import prologue
-        t1 = time.perf_counter()
-        prologue.project(pi.x, pi.w_kvq, pi.conv, pi.w_gate, pi.gate_bias, H)
-        odt = time.perf_counter() - t1
+        with threadpool_limits(1):          # numpy's BLAS on one thread, as reported
+            t1 = time.perf_counter()
+            prologue.project(pi.x, pi.w_kvq, pi.conv, pi.w_gate, pi.gate_bias, H)
+            odt = time.perf_counter() - t1
         out["input_side"]["cpu_baseline"] = {
             "value": Bn * Tn / odt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": "%s input side: one call (%d x %d tokens of width %d), fp64 numpy oracle, %.2f s" % (
@@ -385,6 +387,103 @@ def input_side(name, steps, oracle=False):
     out["input_side"]["step"] = "tm_project of (%d, %d) tokens of width %d, 4-tap convolution" % (Bn, Tn, wl.model_dim)
     out["from_tokens"]["step"] = "tm_project + tm_state_init + tm_forward of (%d, %d) tokens" % (Bn, Tn)
     T.tm_destroy(ctx)
+    return out
+
+
+def mac_wiring(name, steps, seg=128, n_persist=4, oracle=False):
+    """The memory's side of memory as a context over the workload's first
+    call, segment by segment from the initial state: the segment's
+    projections (tm_project), its queries read before the write
+    (tm_retrieve), the window (tm_mac_window), the caller's attention (here
+    the segment's own rows passed through, one copy), the output's
+    projections, its write (tm_store) and read (tm_retrieve), and the gate
+    (tm_mac_gate); tokens/s, and the window kernel's HBM roofline."""
+    import numpy as np
+    import torch
+    import test_trained_neural_amd as T
+    from test_trained_neural_amd import inputs as I
+    wl = I.WORKLOADS[name]
+    params = I.make_params(wl, 0)
+    pi = I.make_prologue(wl, params, 0, 0, conv_len=4)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    Bn, Tn, H, d = wl.batch, wl.tokens_per_call, wl.heads, wl.dim
+    D, S, P = H * d, seg, n_persist
+    assert Tn % S == 0 and S % wl.chunk == 0
+    x = torch.from_numpy(pi.x).to(dev).to(tdt).contiguous()
+    w = torch.from_numpy(np.ascontiguousarray(pi.w_kvq.transpose(0, 2, 1))).to(dev).to(tdt).contiguous()
+    conv = torch.from_numpy(pi.conv).to(dev).contiguous()
+    wg = torch.from_numpy(np.ascontiguousarray(pi.w_gate.transpose(0, 2, 1))).to(dev).contiguous()
+    gb = torch.from_numpy(pi.gate_bias).to(dev).contiguous()
+    pers = torch.from_numpy(np.random.default_rng(3).standard_normal((P, D)).astype(np.float32)).to(dev).to(tdt)
+    hx = torch.zeros((Bn, 3, 3, D), dtype=torch.float32, device=dev)
+    hy = torch.zeros_like(hx)
+    mem = T.NeuralMemory(d, wl.depth, wl.expansion, wl.chunk, device=dev)
+    init = torch.from_numpy(params.init_weights).to(dev)
+    st = mem.init_state(Bn, H, init)
+    segs = [x[:, i * S:(i + 1) * S].contiguous() for i in range(Tn // S)]
+
+    def attention(window):
+        return window[:, P + S:]
+
+    def step():
+        hx.zero_()
+        hy.zero_()
+        T.tm_state_init(mem.ctx, st.buf, Bn, H, init)
+        for xs in segs:
+            T.mac_segment(mem, st, xs, pers, attention, w, conv, wg, gb, H, hx, hy)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    out = {"tokens_per_s": Bn * Tn / dt, "ms_per_step": dt * 1e3, "steps": steps}
+    # the window kernel alone, event-timed
+    rec = torch.randn((Bn, S, D), dtype=torch.float32, device=dev)
+    win = torch.empty((Bn, P + 2 * S, D), dtype=tdt, device=dev)
+    T.tm_timing_enable(1 << T.K_MAC)
+    T.tm_timing_read(T.K_MAC)
+    n_win = 20 * steps
+    for _ in range(n_win):
+        T.tm_mac_window(pers, rec, segs[0], win)
+    torch.cuda.synchronize()
+    T.tm_timing_enable(0)
+    ms, n = T.tm_timing_read(T.K_MAC)
+    es = 2 if wl.dtype == "bf16" else 4
+    per_launch = Bn * S * D * 4 + Bn * S * D * es + P * D * es + Bn * (P + 2 * S) * D * es
+    achieved = per_launch * n / (ms / 1e3) / 1e9
+    out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "mac_window_kernel",
+                       "launches": n, "avg_us": ms * 1e3 / max(n, 1), "bytes_per_launch": per_launch,
+                       "timing": "HIP events recorded with each launch's own dispatch"}
+    if oracle:
+        from threadpoolctl import threadpool_limits
+        from oracle import mac, prologue, tmref
+        xs = pi.x[:, :S].astype(np.float64)
+        ref = I.initial_state(wl, params)
+        lim = threadpool_limits(1)          # numpy's BLAS on one thread, as reported
+        t1 = time.perf_counter()
+        _, _, q, _, _, _, _ = prologue.project(xs, pi.w_kvq, pi.conv, pi.w_gate, pi.gate_bias, H)
+        r = tmref.retrieve(d, wl.depth, wl.expansion, ref, q.astype(np.float32), n_threads=1)
+        win_o = mac.window(pers.float().cpu().numpy(), r.reshape(Bn, S, D), xs, wl.dtype == "bf16")
+        y = win_o[:, P + S:]
+        k2, v2, q2, th, et, al, _ = prologue.project(y, pi.w_kvq, pi.conv, pi.w_gate, pi.gate_bias, H)
+        tmref.forward(d, wl.depth, wl.expansion, wl.chunk, ref, k2, v2, th, et, al, n_threads=1)
+        m2 = tmref.retrieve(d, wl.depth, wl.expansion, ref, q2.astype(np.float32), n_threads=1)
+        mac.gate(y, m2.reshape(Bn, S, D))
+        odt = time.perf_counter() - t1
+        lim.restore_original_limits()
+        out["cpu_baseline"] = {
+            "value": Bn * S / odt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%s memory-as-context wiring: the first segment (%d x %d tokens), fp64 oracles "
+                      "(input side, memory, wiring), one thread, %.2f s" % (wl.name, Bn, S, odt)}
+    out["step"] = ("%d segments of %d tokens x %d streams, %d persistent tokens: tm_project, tm_retrieve, "
+                   "tm_mac_window, pass-through attention, tm_project, tm_store, tm_retrieve, tm_mac_gate"
+                   % (Tn // S, S, Bn, P))
     return out
 
 
@@ -569,6 +668,8 @@ def main():
         side = input_side("mlp384", 20, oracle=not args.no_cpu_baseline)
         out["other_workloads"]["mlp384_input_side"] = side["input_side"]
         out["other_workloads"]["mlp384_from_tokens"] = side["from_tokens"]
+        # the memory's side of memory as a context, segment by segment
+        out["other_workloads"]["mlp384_mac"] = mac_wiring("mlp384", 10, oracle=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, params, ci)
         out["cpu_baseline"]["gpu_over_cpu"] = out["value"] / out["cpu_baseline"]["value"]

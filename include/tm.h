@@ -248,7 +248,8 @@ tm_status tm_w1_split_enable(int on);
  * backward, and its forward, with the other layers' updates riding in the
  * same launch), 5 the per-token read's products,
  * 6 the input side's projection kernel (tm_project; its history kernel is
- * not timed).  While bit c of
+ * not timed), 7 the memory-as-context window and gate kernels
+ * (tm_mac_window, tm_mac_gate).  While bit c of
  * class_mask is set, every launch of class c is bracketed by a pair of HIP
  * events recorded on its launch stream (mask 0 turns timing off).
  * tm_timing_read waits for the recorded launches and returns, for one class,

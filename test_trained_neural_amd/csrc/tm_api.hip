@@ -186,7 +186,7 @@ hipError_t compute_units(int* out) {
 
 // ---- optional per-launch timing (tm_timing_enable / tm_timing_read) ----
 // (class 3 is unused: the update of layers 1.. rides in the first-layer launch)
-enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_FIRST = 4, K_R3 = 5, K_PROJ = 6, K_CLASSES = 7 };
+enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_FIRST = 4, K_R3 = 5, K_PROJ = 6, K_MAC = 7, K_CLASSES = 8 };
 struct Timed {
     hipEvent_t a, b;
     int kind;
@@ -1026,7 +1026,8 @@ tm_status tm_mac_window(const void* persistent, int n_persist, const float* reca
     if (!tok_ok(recalled) || !tok_ok(segment) || !tok_ok(window) || (n_persist > 0 && !tok_ok(persistent)))
         return TM_ERR_INVALID;
     MacArgs a{persistent, recalled, segment, window, batch, seg_len, n_persist, model_dim};
-    return hip_status(launch_mac_window(a, dtype == TM_F32 ? 1 : 0, static_cast<hipStream_t>(stream)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(timed(K_MAC, st, [&] { return launch_mac_window(a, dtype == TM_F32 ? 1 : 0, st); }));
 }
 
 tm_status tm_mac_gate(const void* y, const float* mem, float* out, int batch, int seg_len, int model_dim,
@@ -1037,7 +1038,8 @@ tm_status tm_mac_gate(const void* y, const float* mem, float* out, int batch, in
         return TM_ERR_INVALID;
     if (!tok_ok(y) || !tok_ok(mem) || !tok_ok(out)) return TM_ERR_INVALID;
     MacArgs a{nullptr, mem, y, out, batch, seg_len, 0, model_dim};
-    return hip_status(launch_mac_gate(a, dtype == TM_F32 ? 1 : 0, static_cast<hipStream_t>(stream)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(timed(K_MAC, st, [&] { return launch_mac_gate(a, dtype == TM_F32 ? 1 : 0, st); }));
 }
 
 tm_status tm_state_export(const tm_ctx* c, const void* state, int batch, int heads, float* dst,
