@@ -154,7 +154,8 @@ tm_status tm_forward_ex(const tm_ctx* ctx, void* state, const void* k, const voi
  * x: [batch][n_tokens][model_dim] of dtype, 16-byte aligned, model_dim a
  *   multiple of 32.  w_kvq: [3][heads*dim][model_dim] of dtype, 16-byte
  *   aligned.  conv: [3][heads*dim][conv_len] fp32, conv_len 1..4.  w_gate:
- *   [3][heads][model_dim] fp32.  gate_bias: [3] fp32 (device).
+ *   [3][heads][model_dim] fp32, 16-byte aligned.  gate_bias: [3] fp32
+ *   (device).
  * history: [batch][conv_len-1][3][heads*dim] fp32, the projections of the
  *   stream's last conv_len-1 tokens before this call, oldest first (zeros at
  *   a stream's start); read, then overwritten with those of this call's last

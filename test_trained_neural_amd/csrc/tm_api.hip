@@ -943,7 +943,7 @@ tm_status tm_project(const tm_ctx* c, const void* x, int model_dim, const void* 
         conv_len < 1 || conv_len > MAX_CONV || (long)batch * n_tokens > 0x7fffffffL ||
         (long)heads * c->dim > 65536)
         return TM_ERR_INVALID;
-    if (!tok_ok(x) || !tok_ok(w_kvq) || !gate_ok(conv) || !gate_ok(w_gate) || !gate_ok(gate_bias) ||
+    if (!tok_ok(x) || !tok_ok(w_kvq) || !gate_ok(conv) || !tok_ok(w_gate) || !gate_ok(gate_bias) ||
         (conv_len > 1 && !gate_ok(history)))
         return TM_ERR_INVALID;
     if (n_tokens == 0) return TM_OK;

@@ -17,23 +17,61 @@ namespace tmk {
 // outside the call multiply zeros.
 constexpr int PROJ_HALO = MAX_CONV - 1;
 
-// The gates of RT tokens of batch row b: one wave per token at a time, lanes
-// split D; sigmoid(x w_g + b_g) for every gate g and head.
+// The gates of RT tokens of batch row b: sigmoid(x w_g + b_g) for every
+// gate g and head.  Wave w owns the RT/8 consecutive tokens from t0 + w*RT/8;
+// a lane takes 8 consecutive inputs of each 512-input chunk of D.  The steps
+// (gate-head gh, chunk) run in order and each issues the next step's loads
+// before its own arithmetic and reduction, so a step costs about one load
+// round trip; the two register buffers alternate by explicit unrolling.
 template <class OP, int RT>
 __device__ void gates_tile(const ProjArgs& a, int b, int t0) {
+    constexpr int TPW = RT / 8;
+    struct Buf {
+        f32x8 w;
+        f32x8 x[TPW];
+    };
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int t = t0 + wave; t < min(t0 + RT, a.T); t += 8) {
-        const long tok = (long)b * a.T + t;
-        const OP* x = reinterpret_cast<const OP*>(a.x) + tok * a.D;
-        for (int gh = 0; gh < 3 * a.H; ++gh) {
-            const int g = gh / a.H, h = gh - g * a.H;
-            const float* wg = a.wg + ((long)g * a.H + h) * a.D;
-            float acc = 0.f;
-            for (int c = lane; c < a.D; c += 64) acc += (float)x[c] * wg[c];
+    const int tw = t0 + wave * TPW;
+    const int nch = (a.D + 511) >> 9;
+    const int nit = 3 * a.H * nch;
+    const OP* xb = reinterpret_cast<const OP*>(a.x) + (long)b * a.T * a.D;
+    auto load = [&](int it, Buf& o) {
+        const int gh = it / nch, c = (it - gh * nch) * 512 + lane * 8;
+        const bool ok = c < a.D;                     // D is a multiple of 8
+        const int cc = ok ? c : 0;
+        o.w = keep_if(ld8(a.wg + (long)gh * a.D + cc), ok);
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-            if (lane == 0) a.gate[g][tok * a.H + h] = sigmoid(acc + a.gb[g]);
+        for (int t = 0; t < TPW; ++t)
+            o.x[t] = keep_if(to_f32v(ld8(xb + (long)min(tw + t, a.T - 1) * a.D + cc)), ok);
+    };
+    float acc[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) acc[t] = 0.f;
+    auto step = [&](int it, const Buf& cur, Buf& nxt) {
+        if (it + 1 < nit) load(it + 1, nxt);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[t] += cur.x[t][e] * cur.w[e];
+        const int gh = it / nch;
+        if (it - gh * nch == nch - 1) {              // the gate's last chunk (wave-uniform)
+            const int g = gh / a.H, h = gh - g * a.H;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) acc[t] += __shfl_xor(acc[t], off, 64);
+                const int tok = tw + t;
+                if (lane == 0 && tok < min(t0 + RT, a.T))
+                    a.gate[g][((long)b * a.T + tok) * a.H + h] = sigmoid(acc[t] + a.gb[g]);
+                acc[t] = 0.f;
+            }
         }
+    };
+    Buf A, B;
+    load(0, A);
+    for (int it = 0; it < nit; it += 2) {
+        step(it, A, B);
+        if (it + 1 < nit) step(it + 1, B, A);
     }
 }
 
