@@ -49,8 +49,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError("libtm.so is not built (run __graft_entry__.build() or "
-                              "python -m test_trained_neural_amd.build)")
+            raise ImportError("libtm.so is not built (run python -m test_trained_neural_amd.build)")
         L = ctypes.CDLL(LIB_PATH)
         L.tm_create.restype = _i
         L.tm_create.argtypes = [_i, _i, _i, _i, ctypes.POINTER(_vp)]
