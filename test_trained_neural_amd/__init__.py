@@ -343,27 +343,36 @@ def mac_segment(mem, state, x, persistent, attention, w_kvq, conv, w_gate, gate_
     read the memory before the segment is written; y is written (its keys,
     values and gates from the same projections) and read back through its
     queries to gate y.  Returns (out [B][S][D] fp32, state).  hist_x, hist_y:
-    the two projection streams' convolution histories (see tm_project)."""
+    the two projection streams' convolution histories (see tm_project).
+    The window handed to ``attention`` and the other intermediates are
+    buffers the memory keeps and reuses: calls on one memory run on one
+    stream at a time (as its state does), and ``attention`` keeps no
+    reference to the window past its call."""
     B, S, D = x.shape
     dev, dt, d = x.device, x.dtype, mem.dim
     P = 0 if persistent is None else persistent.shape[0]
+    # the intermediates live in buffers the memory keeps for its last
+    # segment shape (reused in stream order); only the output is new
+    key = (B, S, D, P, heads, dt, str(dev))
+    if mem._mac is None or mem._mac[0] != key:
+        f32 = torch.float32
+        kvq = [torch.empty((B, S, heads, d), dtype=dt, device=dev) for _ in range(3)]
+        g = [torch.empty((B, S, heads), dtype=f32, device=dev) for _ in range(3)]
+        reads = [torch.empty((B, S, heads, d), dtype=f32, device=dev) for _ in range(2)]
+        window = torch.empty((B, P + 2 * S, D), dtype=dt, device=dev)
+        mem._mac = (key, kvq, g, reads, window)
+    _, (k, v, q), g, (recalled, my), window = mem._mac
+    ws = mem.workspace(B, heads, S)
 
-    def project(src, hist):
-        k, v, q = (torch.empty((B, S, heads, d), dtype=dt, device=dev) for _ in range(3))
-        g = [torch.empty((B, S, heads), dtype=torch.float32, device=dev) for _ in range(3)]
-        tm_project(mem.ctx, src, w_kvq, conv, w_gate, gate_bias, hist, k, v, q, g[0], g[1], g[2], heads)
-        return k, v, q, g
-
-    _, _, qx, _ = project(x, hist_x)
-    recalled = mem.retrieve(state, qx).view(B, S, D)
-    window = torch.empty((B, P + 2 * S, D), dtype=dt, device=dev)
-    tm_mac_window(persistent, recalled, x, window)
+    tm_project(mem.ctx, x, w_kvq, conv, w_gate, gate_bias, hist_x, k, v, q, g[0], g[1], g[2], heads)
+    tm_retrieve(mem.ctx, state.buf, q, recalled, ws)
+    tm_mac_window(persistent, recalled.view(B, S, D), x, window)
     y = attention(window).contiguous()
-    ky, vy, qy, gy = project(y, hist_y)
-    mem.store(state, ky, vy, gy[0], gy[1], gy[2])
-    my = mem.retrieve(state, qy).view(B, S, D)
+    tm_project(mem.ctx, y, w_kvq, conv, w_gate, gate_bias, hist_y, k, v, q, g[0], g[1], g[2], heads)
+    tm_store(mem.ctx, state.buf, k, v, g[0], g[1], g[2], ws)
+    tm_retrieve(mem.ctx, state.buf, q, my, ws)
     out = torch.empty((B, S, D), dtype=torch.float32, device=dev)
-    tm_mac_gate(y, my, out)
+    tm_mac_gate(y, my.view(B, S, D), out)
     return out, state
 
 
@@ -374,6 +383,7 @@ class NeuralMemory:
         self.ctx = tm_create(dim, depth, expansion, chunk)
         self.params = tm_param_count(self.ctx)
         self._ws = None
+        self._mac = None   # mac_segment's intermediates for its last segment shape
 
     def __del__(self):
         try:
