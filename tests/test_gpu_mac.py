@@ -125,3 +125,49 @@ def test_mac_timing_class():
         bo = (o.cpu() != want_o).nonzero().tolist()
         say("mask %d: window mismatches %d %s, gate mismatches %d %s" % (mask, len(bw), bw[:4], len(bo), bo[:4]))
         assert not bw and not bo
+
+
+def test_mac_segment_buffers():
+    """mac_segment reuses the memory's buffers across segments: an output
+    it returned is untouched by the next segment, a change of segment length
+    takes new buffers, and every segment equals the same segment run by a
+    memory with no buffers kept (the state carried alike)."""
+    import test_trained_neural_amd as T
+    wl = small("macbuf", 64, 2, 2, 16, 2, 2, 64, "bf16", offsets=(-4.5, 1.0, -6.0))
+    H, d, P = wl.heads, wl.dim, 2
+    D = H * d
+    p = I.make_params(wl)
+    pi = I.make_prologue(wl, p, conv_len=2)
+    dev, bf = "cuda", torch.bfloat16
+    x = torch.from_numpy(pi.x).to(dev).to(bf)
+    w_kvq = torch.from_numpy(np.ascontiguousarray(pi.w_kvq.transpose(0, 2, 1))).to(dev).to(bf)
+    conv = torch.from_numpy(pi.conv).to(dev)
+    wg = torch.from_numpy(np.ascontiguousarray(pi.w_gate.transpose(0, 2, 1))).to(dev)
+    gb = torch.from_numpy(pi.gate_bias).to(dev)
+    pers = torch.from_numpy(np.random.default_rng(2).standard_normal((P, D)).astype(np.float32)).to(dev).to(bf)
+    init = torch.from_numpy(p.init_weights)
+
+    def attention(window):
+        S = (window.shape[1] - P) // 2
+        return window[:, P + S:] * 0.5 + window[:, P:P + S] * 0.25
+
+    mem = T.NeuralMemory(d, wl.depth, wl.expansion, wl.chunk, device=dev)
+    st = mem.init_state(wl.batch, H, init)
+    hx = torch.zeros((wl.batch, 1, 3, D), dtype=torch.float32, device=dev)
+    hy = torch.zeros_like(hx)
+    ref_st = mem.init_state(wl.batch, H, init)
+    rhx, rhy = torch.zeros_like(hx), torch.zeros_like(hx)
+    outs, keep, t = [], [], 0
+    for S in (32, 16, 16):
+        xs = x[:, t:t + S].contiguous()
+        t += S
+        out, st = T.mac_segment(mem, st, xs, pers, attention, w_kvq, conv, wg, gb, H, hx, hy)
+        outs.append(out)
+        keep.append(out.clone())
+        fresh = T.NeuralMemory(d, wl.depth, wl.expansion, wl.chunk, device=dev)   # no buffers kept
+        want, ref_st = T.mac_segment(fresh, ref_st, xs, pers, attention, w_kvq, conv, wg, gb, H, rhx, rhy)
+        assert torch.equal(out, want)
+    torch.cuda.synchronize()
+    for o, k in zip(outs, keep):
+        assert torch.equal(o, k)
+    assert mem.check(st) == (False, 64)
