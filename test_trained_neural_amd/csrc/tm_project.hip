@@ -288,7 +288,10 @@ hipError_t launch_project(const ProjArgs& p, int f32, hipStream_t st) {
     if (p.T == 0 || p.B == 0) return hipSuccess;
     if (p.d > 1024 || p.d % 32 != 0 || p.D % 32 != 0 || p.K < 1 || p.K > MAX_CONV) return hipErrorInvalidValue;
     // tiles of 32 tokens; 16 for the widest heads (the staged rows fill LDS)
-    if (p.d <= 512) {
+    // and for calls whose 32-token grid would not cover the 256 compute
+    // units (short calls: more, shorter workgroups finish sooner)
+    const long grid32 = (long)((p.T + 31) / 32) * (3 * p.H + 1) * p.B;
+    if (p.d <= 512 && grid32 >= 256) {
         if (f32) launch_project_rt<float, 32>(p, st);
         else launch_project_rt<bf16, 32>(p, st);
     } else {
