@@ -55,7 +55,8 @@ typedef enum {
     TM_ERR_INVALID = -1,  /* null/misaligned pointer, non-positive or unsupported size */
     TM_ERR_SHAPE = -2,    /* n_tokens not a multiple of the chunk size */
     TM_ERR_DTYPE = -3,    /* unknown tm_dtype */
-    TM_ERR_STATE = -4,    /* state header does not match the ctx / batch / heads */
+    TM_ERR_STATE = -4,    /* state not set up (tm_state_init / tm_state_import) for this
+                             configuration, batch and heads, or its header does not match */
     TM_ERR_HIP = -5       /* a HIP runtime call or launch failed */
 } tm_status;
 
@@ -81,6 +82,10 @@ void tm_destroy(tm_ctx* ctx);
 /* Weights per stream (P). */
 size_t tm_param_count(const tm_ctx* ctx);
 
+/* The configuration ctx was created with (depth 1 reports expansion 1).
+ * Any output pointer may be null.  TM_ERR_INVALID for a null ctx. */
+tm_status tm_config(const tm_ctx* ctx, int* dim, int* depth, int* expansion, int* chunk);
+
 /* Size in bytes of the opaque state blob for batch*heads streams (fp32 M and
  * S, a bf16 copy of M for the matrix cores, and a header).  0 on bad args. */
 size_t tm_state_bytes(const tm_ctx* ctx, int batch, int heads);
@@ -91,7 +96,13 @@ size_t tm_workspace_bytes(const tm_ctx* ctx, int batch, int heads, int n_tokens)
 
 /* M = init_weights (device fp32 [heads][P], canonical layer order, broadcast
  * over the batch), S = 0, position = 0, flag cleared.  state: 256-byte
- * aligned, tm_state_bytes(ctx, batch, heads) bytes. */
+ * aligned, tm_state_bytes(ctx, batch, heads) bytes.  The library records on
+ * the host, per state address, the configuration, batch and heads it was set
+ * up for (tm_state_import records them too); tm_store, tm_retrieve,
+ * tm_forward, tm_forward_ex and tm_state_export refuse, with TM_ERR_STATE and
+ * before any launch, a state address that was never set up or was set up
+ * for another configuration, batch or head count.  The record is
+ * process-wide, so a state may be used with any ctx of its configuration. */
 tm_status tm_state_init(const tm_ctx* ctx, void* state, int batch, int heads,
                         const float* init_weights, void* stream);
 

@@ -26,7 +26,7 @@ EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_w
             "tm_state_init", "tm_store", "tm_retrieve", "tm_forward", "tm_state_export",
             "tm_state_import", "tm_state_check", "tm_status_str", "tm_timing_enable", "tm_timing_read",
             "tm_graphs_enable", "tm_w1_split_enable", "tm_forward_ex", "tm_project", "tm_mac_window",
-            "tm_mac_gate")
+            "tm_mac_gate", "tm_config")
 
 # kernel classes of tm_timing_enable / tm_timing_read (3 is unused)
 K_SCAN, K_FWD, K_BWD, K_FIRST, K_TOKEN_READ, K_PROJECT, K_MAC = 0, 1, 2, 4, 5, 6, 7
@@ -57,6 +57,8 @@ def lib():
         L.tm_destroy.argtypes = [_vp]
         L.tm_param_count.restype = ctypes.c_size_t
         L.tm_param_count.argtypes = [_vp]
+        L.tm_config.restype = _i
+        L.tm_config.argtypes = [_vp] + [ctypes.POINTER(_i)] * 4
         L.tm_state_bytes.restype = ctypes.c_size_t
         L.tm_state_bytes.argtypes = [_vp, _i, _i]
         L.tm_workspace_bytes.restype = ctypes.c_size_t
@@ -141,6 +143,31 @@ def _shape(name, t, shape):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _blob(name, t, need):
+    """t is a contiguous device tensor of at least ``need`` bytes (the state
+    blob and the workspace are untyped bytes the kernels index by the call's
+    sizes: a short buffer would be read or written past its end)."""
+    if t is None or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous device tensor" % name)
+    if need == 0 or _nbytes(t) < need:
+        raise ValueError("%s holds %d bytes; this call needs %d" % (name, _nbytes(t), need))
+
+
+def _memory_sizes(ctx, state, workspace, B, H, T, d):
+    """The token width matches the memory's dim; the state and workspace
+    hold what tm_state_bytes / tm_workspace_bytes give for this call."""
+    dim = tm_config(ctx)[0]
+    if d != dim:
+        raise ValueError("token vectors are %d wide; the memory's dim is %d" % (d, dim))
+    _blob("state", state, tm_state_bytes(ctx, B, H))
+    if workspace is not False:
+        _blob("workspace", workspace, tm_workspace_bytes(ctx, B, H, T))
+
+
 def _memory_call(k, v, q, theta, eta, alpha, y):
     """The token, gate and output tensors of a memory call: k, v, q
     [B][T][H][d] of one operand type, the gates [B][T][H] and y [B][T][H][d]
@@ -172,6 +199,13 @@ def tm_param_count(ctx):
     return lib().tm_param_count(ctx)
 
 
+def tm_config(ctx):
+    """(dim, depth, expansion, chunk) of the memory configuration."""
+    v = [_i(0) for _ in range(4)]
+    _check("tm_config", lib().tm_config(ctx, *[ctypes.byref(x) for x in v]))
+    return tuple(int(x.value) for x in v)
+
+
 def tm_state_bytes(ctx, batch, heads):
     return lib().tm_state_bytes(ctx, batch, heads)
 
@@ -183,6 +217,10 @@ def tm_workspace_bytes(ctx, batch, heads, n_tokens):
 def tm_state_init(ctx, state, batch, heads, init_weights, stream=None):
     _same(torch.float32, ("init_weights", init_weights))
     _tok(init_weights)
+    _blob("state", state, tm_state_bytes(ctx, batch, heads))
+    if init_weights.numel() != heads * tm_param_count(ctx):
+        raise ValueError("init_weights must hold heads * P = %d values, got %d"
+                         % (heads * tm_param_count(ctx), init_weights.numel()))
     _check("tm_state_init", lib().tm_state_init(ctx, _ptr(state), batch, heads, _ptr(init_weights),
                                                 _stream(stream)))
 
@@ -190,7 +228,8 @@ def tm_state_init(ctx, state, batch, heads, init_weights, stream=None):
 def tm_store(ctx, state, k, v, theta, eta, alpha, workspace, stream=None):
     _memory_call(k, v, None, theta, eta, alpha, None)
     _tok(k, v, theta, eta, alpha)
-    B, T, H, _ = k.shape
+    B, T, H, d = k.shape
+    _memory_sizes(ctx, state, workspace, B, H, T, d)
     _check("tm_store", lib().tm_store(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(theta), _ptr(eta),
                                       _ptr(alpha), B, H, T, _dtype_code(k), _ptr(workspace),
                                       _stream(stream)))
@@ -199,7 +238,8 @@ def tm_store(ctx, state, k, v, theta, eta, alpha, workspace, stream=None):
 def tm_retrieve(ctx, state, q, y, workspace, stream=None):
     _memory_call(None, None, q, None, None, None, y)
     _tok(q, y)
-    B, T, H, _ = q.shape
+    B, T, H, d = q.shape
+    _memory_sizes(ctx, state, workspace, B, H, T, d)
     _check("tm_retrieve", lib().tm_retrieve(ctx, _ptr(state), _ptr(q), _ptr(y), B, H, T,
                                             _dtype_code(q), _ptr(workspace), _stream(stream)))
 
@@ -207,7 +247,8 @@ def tm_retrieve(ctx, state, q, y, workspace, stream=None):
 def tm_forward(ctx, state, k, v, q, theta, eta, alpha, y, workspace, stream=None):
     _memory_call(k, v, q, theta, eta, alpha, y)
     _tok(k, v, q, theta, eta, alpha, y)
-    B, T, H, _ = k.shape
+    B, T, H, d = k.shape
+    _memory_sizes(ctx, state, workspace, B, H, T, d)
     _check("tm_forward", lib().tm_forward(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(q), _ptr(theta),
                                           _ptr(eta), _ptr(alpha), _ptr(y), B, H, T, _dtype_code(k),
                                           _ptr(workspace), _stream(stream)))
@@ -218,7 +259,8 @@ def tm_forward_ex(ctx, state, k, v, q, theta, eta, alpha, y, workspace, read, st
     TM_READ_PER_TOKEN."""
     _memory_call(k, v, q, theta, eta, alpha, y)
     _tok(k, v, q, theta, eta, alpha, y)
-    B, T, H, _ = k.shape
+    B, T, H, d = k.shape
+    _memory_sizes(ctx, state, workspace, B, H, T, d)
     _check("tm_forward_ex", lib().tm_forward_ex(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(q), _ptr(theta),
                                                 _ptr(eta), _ptr(alpha), _ptr(y), B, H, T, _dtype_code(k),
                                                 int(read), _ptr(workspace), _stream(stream)))
@@ -272,7 +314,10 @@ def tm_project(ctx, x, w_kvq, conv, w_gate, gate_bias, history, k, v, q, theta, 
     if K > 1:
         _shape("history", history, (B, K - 1, 3, HD))
     _memory_call(k, v, q, theta, eta, alpha, None)
-    _shape("k", k, (B, T, heads, HD // heads))
+    dim = tm_config(ctx)[0]
+    if HD != heads * dim:
+        raise ValueError("w_kvq has %d output rows; heads * dim is %d" % (HD, heads * dim))
+    _shape("k", k, (B, T, heads, dim))
     _tok(x, w_kvq, conv, w_gate, gate_bias, k, v, q, theta, eta, alpha)
     if history is not None:
         _tok(history)
@@ -282,19 +327,30 @@ def tm_project(ctx, x, w_kvq, conv, w_gate, gate_bias, history, k, v, q, theta, 
                                           B, heads, T, _dtype_code(x), _stream(stream)))
 
 
+def _canonical(name, t, ctx, batch, heads):
+    n = batch * heads * 2 * tm_param_count(ctx)
+    if t is None or not t.is_cuda or not t.is_contiguous() or t.numel() != n:
+        raise ValueError("%s must be a contiguous device tensor of batch * heads * 2P = %d values" % (name, n))
+
+
 def tm_state_export(ctx, state, batch, heads, dst, stream=None):
     _same(torch.float32, ("dst", dst))
+    _canonical("dst", dst, ctx, batch, heads)
+    _blob("state", state, tm_state_bytes(ctx, batch, heads))
     _check("tm_state_export", lib().tm_state_export(ctx, _ptr(state), batch, heads, _ptr(dst),
                                                     _stream(stream)))
 
 
 def tm_state_import(ctx, state, batch, heads, src, stream=None):
     _same(torch.float32, ("src", src))
+    _canonical("src", src, ctx, batch, heads)
+    _blob("state", state, tm_state_bytes(ctx, batch, heads))
     _check("tm_state_import", lib().tm_state_import(ctx, _ptr(state), batch, heads, _ptr(src),
                                                     _stream(stream)))
 
 
 def tm_state_check(ctx, state, batch, heads, stream=None):
+    _blob("state", state, 256)   # the header
     nf = _i(0)
     pos = ctypes.c_longlong(0)
     _check("tm_state_check", lib().tm_state_check(ctx, _ptr(state), batch, heads, ctypes.byref(nf),

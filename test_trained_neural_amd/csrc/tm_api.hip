@@ -9,7 +9,10 @@
 // row-major form.
 #include <mutex>
 #include <new>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/tm.h"
@@ -167,6 +170,48 @@ uint64_t fnv(uint64_t h, uint64_t x) {
 
 tm_status hip_status(hipError_t e) { return e == hipSuccess ? TM_OK : TM_ERR_HIP; }
 
+// Host-side record of every state blob that tm_state_init or
+// tm_state_import set up in this process: the configuration hash, batch and
+// heads its header holds.  The compute calls look their state up here before
+// launching anything, so a blob made for another configuration, batch or
+// head count (or never set up) is refused with TM_ERR_STATE instead of being
+// read or written past its end on the device.  Keyed by the device address
+// (unique across devices); a blob set up again under another shape replaces
+// its record.
+struct StateRec {
+    uint64_t hash;
+    int batch, heads;
+};
+std::mutex g_smu;
+std::unordered_map<uintptr_t, StateRec>* g_states = nullptr;
+
+void state_register(const tm_ctx* c, const void* st, int batch, int heads) {
+    std::lock_guard<std::mutex> g(g_smu);
+    if (!g_states) g_states = new std::unordered_map<uintptr_t, StateRec>;
+    (*g_states)[(uintptr_t)st] = StateRec{c->hash, batch, heads};
+}
+
+// TM_OK if `st` was set up for this configuration, batch and heads.
+tm_status state_lookup(const tm_ctx* c, const void* st, int batch, int heads) {
+    std::lock_guard<std::mutex> g(g_smu);
+    if (!g_states) return TM_ERR_STATE;
+    auto it = g_states->find((uintptr_t)st);
+    if (it == g_states->end()) return TM_ERR_STATE;
+    const StateRec& r = it->second;
+    return r.hash == c->hash && r.batch == batch && r.heads == heads ? TM_OK : TM_ERR_STATE;
+}
+
+// TM_LOG=1 prints each call's configuration and launch plan to stderr once
+// per distinct call shape; TM_LOG=2 also prints graph captures and replays.
+int log_level() {
+    static int lvl = -1;
+    if (lvl < 0) {
+        const char* e = getenv("TM_LOG");
+        lvl = e ? atoi(e) : 0;
+    }
+    return lvl;
+}
+
 // compute units of the current device (queried once per device)
 hipError_t compute_units(int* out) {
     static std::mutex mu;
@@ -242,6 +287,31 @@ hipError_t timed(int kind, hipStream_t st, F&& launch) {
     return hipSuccess;
 }
 
+// ---- TM_LOG diagnostics ----
+thread_local bool g_log_plan = false;   // the running launch sequence prints its plan
+
+const char* kind_name(int kind) {
+    switch (kind) {
+        case 0: return "tm_state_init";
+        case 1: return "tm_store";
+        case 2: return "tm_forward";
+        case 3: return "tm_retrieve";
+        case 4: return "tm_forward_ex(read before write)";
+        case 5: return "tm_project";
+        case 6: return "tm_forward_ex(read per token)";
+        case 7: return "tm_backward";
+    }
+    return "?";
+}
+
+void log_call(const tm_ctx* c, const GraphEntry& k) {
+    fprintf(stderr,
+            "[tm] new call shape: %s, memory dim %d depth %d expansion %d chunk %d (P = %ld), batch %d, heads %d, "
+            "n_tokens %d, %s\n",
+            kind_name(k.kind), c->dim, c->depth, c->expansion, c->chunk, c->P, k.batch, k.heads, k.n_tokens,
+            k.dtype == TM_BF16 ? "bf16" : "fp32");
+}
+
 // ---- graph replay of repeated calls ----
 bool g_graphs = true;
 bool g_w1_split = true;   // tm_w1_split_enable
@@ -260,6 +330,7 @@ tm_status with_graph(const tm_ctx* cc, GraphEntry key, hipStream_t st, F&& launc
     }
     if (!g_graphs || timing) return launch(st);
     if (hipGetDevice(&key.dev) != hipSuccess) return TM_ERR_HIP;
+    const int lvl = log_level();
     std::unique_lock<std::mutex> lk(*c->gmu);
     GraphEntry* hit = nullptr;
     for (GraphEntry& e : *c->graphs) {
@@ -283,9 +354,16 @@ tm_status with_graph(const tm_ctx* cc, GraphEntry key, hipStream_t st, F&& launc
         key.last = ++c->stamp;
         c->graphs->push_back(key);
         lk.unlock();
-        return launch(st);
+        if (lvl >= 1) log_call(c, key);
+        g_log_plan = lvl >= 1;
+        tm_status rc = launch(st);
+        g_log_plan = false;
+        return rc;
     }
     hit->last = ++c->stamp;
+    if (lvl >= 2)
+        fprintf(stderr, "[tm] %s call %s (batch %d, heads %d, n_tokens %d)\n", hit->exec ? "replay" : "capture",
+                kind_name(key.kind), key.batch, key.heads, key.n_tokens);
     if (!hit->exec) {
         hipStream_t cs = nullptr;
         for (auto& pr : *c->capture_streams)
@@ -732,6 +810,15 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         if ((ns * (a.nb1 + n1) + cus - 1) / cus <= (ns * a.nb1 + cus - 1) / cus) nw1 = n1;
     }
 
+    if (g_log_plan)
+        fprintf(stderr,
+                "[tm] plan: %d chunks of %d over %ld streams; 1 scan launch%s, then %d steps of 1 first-layer "
+                "launch (%d blocks/stream, %d W_1 blocks/stream, %d update tiles of layers 2..) + %d product "
+                "launches + %d backward launches%s; workspace %zu bytes\n",
+                C, b, ns, read == TM_READ_PER_TOKEN && q ? " + 1 score launch" : "", C + 1, a.nb1, nw1, ntile_rest,
+                c->L - 1, c->L >= 3 ? c->L - 2 : 0, read == TM_READ_PER_TOKEN && q ? " + L read launches" : "",
+                w.total);
+
     for (int ci = 0; ci <= C; ++ci) {
         // queries: chunk ci-1's through the memory after its write (rows of
         // step ci), or chunk ci's through the memory before its write (the
@@ -872,6 +959,15 @@ void tm_destroy(tm_ctx* ctx) {
 
 size_t tm_param_count(const tm_ctx* c) { return c ? (size_t)c->P : 0; }
 
+tm_status tm_config(const tm_ctx* c, int* dim, int* depth, int* expansion, int* chunk) {
+    if (!c) return TM_ERR_INVALID;
+    if (dim) *dim = c->dim;
+    if (depth) *depth = c->depth;
+    if (expansion) *expansion = c->expansion;
+    if (chunk) *chunk = c->chunk;
+    return TM_OK;
+}
+
 size_t tm_state_bytes(const tm_ctx* c, int batch, int heads) {
     if (!c || batch <= 0 || heads <= 0) return 0;
     return state_layout(c, (long)batch * heads).total;
@@ -889,12 +985,14 @@ tm_status tm_state_init(const tm_ctx* c, void* state, int batch, int heads, cons
     if (!aligned(state, 256) || !aligned(init, 4)) return TM_ERR_INVALID;
     const long ns = (long)batch * heads;
     char* s = static_cast<char*>(state);
-    return with_graph(c, make_key(0, batch, heads, 0, 0, {state, init}), static_cast<hipStream_t>(stream),
-                      [&](hipStream_t st) {
+    tm_status rc = with_graph(c, make_key(0, batch, heads, 0, 0, {state, init}), static_cast<hipStream_t>(stream),
+                              [&](hipStream_t st) {
         UpdArgs u = base_upd(c, s, ns);
         return hip_status(launch_state_init(u, c->tbase[c->L], (int)ns, init, heads,
                                             reinterpret_cast<StateHeader*>(s), c->hash, batch, heads, st));
     });
+    if (rc == TM_OK) state_register(c, state, batch, heads);
+    return rc;
 }
 
 tm_status tm_store(const tm_ctx* c, void* state, const void* k, const void* v, const float* theta,
@@ -906,6 +1004,7 @@ tm_status tm_store(const tm_ctx* c, void* state, const void* k, const void* v, c
     if (!tok_ok(k) || !tok_ok(v) || !gate_ok(theta) || !gate_ok(eta) || !gate_ok(alpha))
         return TM_ERR_INVALID;
     if (n_tokens % c->chunk != 0) return TM_ERR_SHAPE;
+    if (state_lookup(c, state, batch, heads) != TM_OK) return TM_ERR_STATE;
     return with_graph(c, make_key(1, batch, heads, n_tokens, dtype, {state, k, v, theta, eta, alpha, ws}),
                       static_cast<hipStream_t>(stream), [&](hipStream_t st) {
         return run_store(c, state, k, v, nullptr, theta, eta, alpha, nullptr, batch, heads, n_tokens,
@@ -925,6 +1024,7 @@ tm_status tm_forward_ex(const tm_ctx* c, void* state, const void* k, const void*
         !gate_ok(alpha))
         return TM_ERR_INVALID;
     if (n_tokens % c->chunk != 0) return TM_ERR_SHAPE;
+    if (state_lookup(c, state, batch, heads) != TM_OK) return TM_ERR_STATE;
     const int kind = read == TM_READ_BEFORE_WRITE ? 4 : read == TM_READ_PER_TOKEN ? 6 : 2;
     return with_graph(c, make_key(kind, batch, heads, n_tokens, dtype, {state, k, v, q, theta, eta, alpha, y, ws}),
                       static_cast<hipStream_t>(stream), [&](hipStream_t st) {
@@ -993,6 +1093,7 @@ tm_status tm_retrieve(const tm_ctx* c, const void* state_v, const void* q, float
     if (rc != TM_OK) return rc;
     if (n_tokens == 0) return TM_OK;
     if (!tok_ok(q) || !tok_ok(y)) return TM_ERR_INVALID;
+    if (state_lookup(c, state_v, batch, heads) != TM_OK) return TM_ERR_STATE;
     char* state = const_cast<char*>(static_cast<const char*>(state_v));   // read only below
     char* ws = static_cast<char*>(ws_v);
     const long ns = (long)batch * heads;
@@ -1046,6 +1147,7 @@ tm_status tm_state_export(const tm_ctx* c, const void* state, int batch, int hea
                           void* stream) {
     if (!c || !state || !dst || batch <= 0 || heads <= 0) return TM_ERR_INVALID;
     if (!aligned(state, 256) || !aligned(dst, 4)) return TM_ERR_INVALID;
+    if (state_lookup(c, state, batch, heads) != TM_OK) return TM_ERR_STATE;
     const long ns = (long)batch * heads;
     StateLayout sl = state_layout(c, ns);
     const char* s = static_cast<const char*>(state);
@@ -1068,7 +1170,9 @@ tm_status tm_state_import(const tm_ctx* c, void* state, int batch, int heads, co
     if (launch_import(u.M, u.S, src, c->P, (int)ns, c->din[0], c->dout[0], c->L > 1 ? c->dout[1] : 0, st) !=
         hipSuccess)
         return TM_ERR_HIP;
-    return hip_status(launch_shadow(u, c->tbase[c->L], (int)ns, st));
+    if (launch_shadow(u, c->tbase[c->L], (int)ns, st) != hipSuccess) return TM_ERR_HIP;
+    state_register(c, state, batch, heads);
+    return TM_OK;
 }
 
 tm_status tm_state_check(const tm_ctx* c, const void* state, int batch, int heads, int* nonfinite,

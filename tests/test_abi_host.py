@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     syms = declared_symbols()
-    assert len(syms) == 21
+    assert len(syms) == 22
     assert set(syms) == set(T.EXPORTED)
     L = ctypes.CDLL(T.LIB_PATH)
     for s in syms:
@@ -118,7 +118,25 @@ def test_call_validation_before_launch():
     assert G(A, A, None, 1, 4, 64, T.TM_F32, st) == T.TM_ERR_INVALID
     assert G(A, A, A, 0, 4, 64, T.TM_F32, st) == T.TM_ERR_INVALID
     assert L.tm_status_str(T.TM_ERR_SHAPE).decode().startswith("n_tokens")
+    # every argument valid, but the state was never set up by tm_state_init /
+    # tm_state_import: refused before any launch
+    assert L.tm_store(c, A, A, A, G, G, G, 1, 1, 16, T.TM_BF16, A, st) == T.TM_ERR_STATE
+    assert L.tm_forward(c, A, A, A, A, G, G, G, A, 1, 1, 16, T.TM_F32, A, st) == T.TM_ERR_STATE
+    assert L.tm_forward_ex(c, A, A, A, A, G, G, G, A, 1, 1, 16, T.TM_BF16, T.TM_READ_PER_TOKEN, A, st) == \
+        T.TM_ERR_STATE
+    assert L.tm_retrieve(c, A, A, A, 1, 1, 5, T.TM_BF16, A, st) == T.TM_ERR_STATE
+    assert L.tm_state_export(c, A, 1, 1, A, st) == T.TM_ERR_STATE
     T.tm_destroy(c)
+
+
+def test_config_getter():
+    c = T.tm_create(128, 3, 2, 32)
+    assert T.tm_config(c) == (128, 3, 2, 32)
+    c1 = T.tm_create(64, 1, 7, 16)
+    assert T.tm_config(c1) == (64, 1, 1, 16)
+    assert T.lib().tm_config(None, None, None, None, None) == T.TM_ERR_INVALID
+    T.tm_destroy(c)
+    T.tm_destroy(c1)
 
 
 def test_binding_checks_dtypes_and_shapes():

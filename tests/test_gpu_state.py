@@ -60,3 +60,57 @@ def test_nan_input_sets_the_nonfinite_flag():
     g.forward(dev_inputs(I.make_call(wl, p, 1), "f32"))
     assert g.check()[0]
     g.close()
+
+
+def test_compute_calls_refuse_a_mismatched_state():
+    # a state set up for batch 1 passed with batch 2 (or another head count,
+    # or another configuration) is refused on the host with TM_ERR_STATE,
+    # nothing launched: the state's bytes and the output stay as they were
+    import ctypes
+    import test_trained_neural_amd as T
+    from harness import dev_inputs
+    wl = small("mismatch", 64, 2, 2, 16, 1, 1, 32, "bf16")
+    say("case", wl)
+    p = I.make_params(wl)
+    g = GpuMemory(wl, p)                      # batch 1
+    d = dev_inputs(I.make_call(wl.replace(batch=2), p), "bf16")   # inputs of batch 2
+    L = T.lib()
+    y = torch.full((2, 32, 1, 64), 7.0, device="cuda")
+    ws = torch.empty(T.tm_workspace_bytes(g.ctx, 2, 1, 32), dtype=torch.uint8, device="cuda")
+    before = g.state.clone()
+    torch.cuda.synchronize()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args = (ptr(d["k"]), ptr(d["v"]), ptr(d["q"]), ptr(d["theta"]), ptr(d["eta"]), ptr(d["alpha"]), ptr(y))
+    assert L.tm_forward(g.ctx, ptr(g.state), *args, 2, 1, 32, T.TM_BF16, ptr(ws), st) == T.TM_ERR_STATE
+    assert L.tm_forward_ex(g.ctx, ptr(g.state), *args, 1, 2, 32, T.TM_BF16, T.TM_READ_BEFORE_WRITE, ptr(ws),
+                           st) == T.TM_ERR_STATE
+    assert L.tm_store(g.ctx, ptr(g.state), *args[:2], *args[3:6], 2, 1, 32, T.TM_BF16, ptr(ws), st) == \
+        T.TM_ERR_STATE
+    assert L.tm_retrieve(g.ctx, ptr(g.state), args[2], ptr(y), 2, 1, 32, T.TM_BF16, ptr(ws), st) == T.TM_ERR_STATE
+    other = T.tm_create(64, 2, 2, 32)        # same widths, another chunk: another configuration
+    assert L.tm_retrieve(other, ptr(g.state), args[2], ptr(y), 1, 1, 32, T.TM_BF16, ptr(ws), st) == \
+        T.TM_ERR_STATE
+    torch.cuda.synchronize()
+    assert torch.equal(g.state, before)
+    assert bool((y == 7.0).all())
+    # the binding refuses a short workspace or state before calling the library
+    d1 = dev_inputs(I.make_call(wl, p), "bf16")
+    y1 = torch.empty((1, 32, 1, 64), device="cuda")
+    short = torch.empty(T.tm_workspace_bytes(g.ctx, 1, 1, 32) - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="workspace"):
+        T.tm_forward(g.ctx, g.state, d1["k"], d1["v"], d1["q"], d1["theta"], d1["eta"], d1["alpha"], y1, short)
+    with pytest.raises(ValueError, match="state"):
+        T.tm_forward(g.ctx, g.state[:-256], d1["k"], d1["v"], d1["q"], d1["theta"], d1["eta"], d1["alpha"], y1,
+                     ws)
+    with pytest.raises(ValueError, match="dim"):
+        T.tm_retrieve(g.ctx, g.state, d1["q"][..., :32].contiguous(), y1[..., :32].contiguous(), ws)
+    torch.cuda.synchronize()
+    assert torch.equal(g.state, before)
+    # a state set up again for batch 2 is taken with batch 2 (its record replaced)
+    big = torch.empty(T.tm_state_bytes(g.ctx, 2, 1), dtype=torch.uint8, device="cuda")
+    T.tm_state_init(g.ctx, big, 2, 1, g.init)
+    T.tm_forward(g.ctx, big, d["k"], d["v"], d["q"], d["theta"], d["eta"], d["alpha"], y, ws)
+    assert T.tm_state_check(g.ctx, big, 2, 1) == (False, 32)
+    T.tm_destroy(other)
+    g.close()
