@@ -57,7 +57,9 @@ typedef enum {
     TM_ERR_DTYPE = -3,    /* unknown tm_dtype */
     TM_ERR_STATE = -4,    /* state not set up (tm_state_init / tm_state_import) for this
                              configuration, batch and heads, or its header does not match */
-    TM_ERR_HIP = -5       /* a HIP runtime call or launch failed */
+    TM_ERR_HIP = -5,      /* a HIP runtime call or launch failed */
+    TM_ERR_SCRATCH = -6   /* tm_forward_noalloc: the call needs more workspace than the
+                             library's scratch array holds */
 } tm_status;
 
 typedef enum { TM_F32 = 0, TM_BF16 = 1 } tm_dtype;
@@ -129,6 +131,23 @@ tm_status tm_forward(const tm_ctx* ctx, void* state, const void* k, const void* 
                      const void* q, const float* theta, const float* eta,
                      const float* alpha, float* y, int batch, int heads,
                      int n_tokens, tm_dtype dtype, void* workspace, void* stream);
+
+/* tm_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results as tm_forward, bitwise, but the workspace is
+ * a scratch array the library holds in device memory, 32 MiB per GPU, kept
+ * from the first call on that GPU until the process ends; the caller passes
+ * only the state, inputs and outputs.  A call whose tm_workspace_bytes
+ * exceeds 32 MiB (e.g. more than 2 streams of 1024 tokens at dim 384, chunk
+ * 64) returns TM_ERR_SCRATCH before any launch.  No hipMalloc, hipFree or
+ * other allocating call is made, and calls are launched directly (no graph
+ * replay).  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (on different streams, or from several threads) race and must
+ * be serialised by the caller.  Everything else as for tm_forward. */
+tm_status tm_forward_noalloc(const tm_ctx* ctx, void* state, const void* k, const void* v,
+                             const void* q, const float* theta, const float* eta,
+                             const float* alpha, float* y, int batch, int heads,
+                             int n_tokens, tm_dtype dtype, void* stream);
 
 /* tm_forward with the read order chosen.  TM_READ_BEFORE_WRITE: for each
  * chunk c, chunk c's queries read the memory chunk c started with, then chunk

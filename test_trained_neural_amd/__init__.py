@@ -18,7 +18,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtm.so")
 
-TM_OK, TM_ERR_INVALID, TM_ERR_SHAPE, TM_ERR_DTYPE, TM_ERR_STATE, TM_ERR_HIP = 0, -1, -2, -3, -4, -5
+TM_OK, TM_ERR_INVALID, TM_ERR_SHAPE, TM_ERR_DTYPE, TM_ERR_STATE, TM_ERR_HIP, TM_ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6
 TM_F32, TM_BF16 = 0, 1
 TM_READ_AFTER_WRITE, TM_READ_BEFORE_WRITE, TM_READ_PER_TOKEN = 0, 1, 2
 
@@ -26,7 +26,7 @@ EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_w
             "tm_state_init", "tm_store", "tm_retrieve", "tm_forward", "tm_state_export",
             "tm_state_import", "tm_state_check", "tm_status_str", "tm_timing_enable", "tm_timing_read",
             "tm_graphs_enable", "tm_w1_split_enable", "tm_forward_ex", "tm_project", "tm_mac_window",
-            "tm_mac_gate", "tm_config")
+            "tm_mac_gate", "tm_config", "tm_forward_noalloc")
 
 # kernel classes of tm_timing_enable / tm_timing_read (3 is unused)
 K_SCAN, K_FWD, K_BWD, K_FIRST, K_TOKEN_READ, K_PROJECT, K_MAC = 0, 1, 2, 4, 5, 6, 7
@@ -72,6 +72,8 @@ def lib():
         L.tm_forward.restype = _i
         L.tm_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
         L.tm_forward_ex.restype = _i
+        L.tm_forward_noalloc.restype = _i
+        L.tm_forward_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
         L.tm_project.restype = _i
         L.tm_project.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _i, _i, _i, _i, _vp]
@@ -252,6 +254,18 @@ def tm_forward(ctx, state, k, v, q, theta, eta, alpha, y, workspace, stream=None
     _check("tm_forward", lib().tm_forward(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(q), _ptr(theta),
                                           _ptr(eta), _ptr(alpha), _ptr(y), B, H, T, _dtype_code(k),
                                           _ptr(workspace), _stream(stream)))
+
+
+def tm_forward_noalloc(ctx, state, k, v, q, theta, eta, alpha, y, stream=None):
+    """tm_forward with the library's own scratch array as the workspace (no
+    device allocation; calls on one GPU must not overlap)."""
+    _memory_call(k, v, q, theta, eta, alpha, y)
+    _tok(k, v, q, theta, eta, alpha, y)
+    B, T, H, d = k.shape
+    _memory_sizes(ctx, state, False, B, H, T, d)
+    _check("tm_forward_noalloc", lib().tm_forward_noalloc(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(q), _ptr(theta),
+                                                          _ptr(eta), _ptr(alpha), _ptr(y), B, H, T,
+                                                          _dtype_code(k), _stream(stream)))
 
 
 def tm_forward_ex(ctx, state, k, v, q, theta, eta, alpha, y, workspace, read, stream=None):

@@ -24,6 +24,15 @@ namespace tmk {
 thread_local LaunchEvents g_launch_ev;
 }
 
+// Workspace of tm_forward_noalloc, for callers that cannot allocate device
+// memory: a file-scope device array of SCRATCH_BYTES, one copy per GPU the
+// library runs on, held until the process ends.  In host code `scratch` only
+// names the symbol; its device address on the current GPU comes from
+// hipGetSymbolAddress (scratch_address below) and is the only form passed to
+// kernels.
+constexpr size_t SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
 // A call's launch sequence replayed as a HIP graph: keyed by everything the
 // kernels' arguments depend on (device, every pointer and every size).
 struct GraphEntry {
@@ -226,6 +235,27 @@ hipError_t compute_units(int* out) {
         if (e != hipSuccess) return e;
     }
     *out = cache[dev];
+    return hipSuccess;
+}
+
+// Device address of `scratch` on the current GPU, looked up once per device
+// (with that device current) and kept.
+hipError_t scratch_address(void** out) {
+    static std::mutex mu;
+    static void* addr[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
     return hipSuccess;
 }
 
@@ -1087,6 +1117,28 @@ tm_status tm_forward(const tm_ctx* c, void* state, const void* k, const void* v,
                          TM_READ_AFTER_WRITE, ws, stream);
 }
 
+tm_status tm_forward_noalloc(const tm_ctx* c, void* state, const void* k, const void* v, const void* q,
+                             const float* theta, const float* eta, const float* alpha, float* y, int batch,
+                             int heads, int n_tokens, tm_dtype dtype, void* stream) {
+    if (!c || !state) return TM_ERR_INVALID;
+    if (batch <= 0 || heads <= 0 || n_tokens < 0) return TM_ERR_INVALID;
+    if ((long)batch * heads > 65535) return TM_ERR_INVALID;
+    if (dtype != TM_F32 && dtype != TM_BF16) return TM_ERR_DTYPE;
+    if (!aligned(state, 256)) return TM_ERR_INVALID;
+    if (n_tokens == 0) return TM_OK;
+    if (!tok_ok(k) || !tok_ok(v) || !tok_ok(q) || !tok_ok(y) || !gate_ok(theta) || !gate_ok(eta) ||
+        !gate_ok(alpha))
+        return TM_ERR_INVALID;
+    if (n_tokens % c->chunk != 0) return TM_ERR_SHAPE;
+    if (state_lookup(c, state, batch, heads) != TM_OK) return TM_ERR_STATE;
+    if (ws_layout(c, (long)batch * heads, n_tokens).total > SCRATCH_BYTES) return TM_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return TM_ERR_HIP;
+    // direct launches (no graph capture: instantiating a graph may allocate)
+    return run_store(c, state, k, v, q, theta, eta, alpha, y, batch, heads, n_tokens, dtype, ws,
+                     static_cast<hipStream_t>(stream));
+}
+
 tm_status tm_retrieve(const tm_ctx* c, const void* state_v, const void* q, float* y, int batch,
                       int heads, int n_tokens, tm_dtype dtype, void* ws_v, void* stream) {
     tm_status rc = check_common(c, state_v, batch, heads, n_tokens, dtype, ws_v);
@@ -1249,6 +1301,7 @@ const char* tm_status_str(tm_status s) {
         case TM_ERR_DTYPE: return "unknown dtype";
         case TM_ERR_STATE: return "state header does not match the memory configuration";
         case TM_ERR_HIP: return "HIP runtime error";
+        case TM_ERR_SCRATCH: return "the call needs more workspace than the library's scratch array holds";
     }
     return "unknown status";
 }
