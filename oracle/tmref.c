@@ -48,6 +48,20 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* Loops over independent elements (the output columns of a product, the
+ * rows of an outer product, the weights in the momentum and forgetting
+ * updates) may be split over `n` threads when the library is built with
+ * OpenMP: every element is still computed by one thread with its terms
+ * summed in the order written, so the results are bitwise those of one
+ * thread.  This only lets a workload with fewer streams than cores use the
+ * spare cores; without OpenMP the pragma is ignored. */
+#define TMREF_PRAGMA(x) _Pragma(#x)
+#ifdef _OPENMP
+#define PAR_FOR(n) TMREF_PRAGMA(omp parallel for schedule(static) num_threads(n) if ((n) > 1))
+#else
+#define PAR_FOR(n)
+#endif
+
 typedef struct {
     int dim, depth, expansion;
     int L;
@@ -74,9 +88,11 @@ static double sigm(double z) { return 1.0 / (1.0 + exp(-z)); }
 
 /* Forward one row through the MLP.  act must hold (L+1)*maxw doubles and
  * pre must hold L*maxw doubles: act[l] is the input of layer l (act[0] = x),
- * pre[l] is layer l's pre-activation z.  Returns the output in out[dim]. */
+ * pre[l] is layer l's pre-activation z.  Returns the output in out[dim].
+ * nth: threads over blocks of output columns (each z[j] sums its inputs
+ * i = 0, 1, ... in order either way). */
 static void mlp_row_forward(const mlp_t* m, const double* W, const double* x,
-                            double* act, double* pre, double* out) {
+                            double* act, double* pre, double* out, int nth) {
     int w = m->maxw;
     memcpy(act, x, sizeof(double) * m->dim);
     for (int l = 0; l < m->L; l++) {
@@ -84,11 +100,15 @@ static void mlp_row_forward(const mlp_t* m, const double* W, const double* x,
         const double* a = act + (long)l * w;
         double* z = pre + (long)l * w;
         int di = m->din[l], dn = m->dout[l];
-        for (int j = 0; j < dn; j++) z[j] = 0.0;
-        for (int i = 0; i < di; i++) {
-            double ai = a[i];
-            const double* row = Wl + (long)i * dn;
-            for (int j = 0; j < dn; j++) z[j] += ai * row[j];
+        PAR_FOR(nth)
+        for (int j0 = 0; j0 < dn; j0 += 64) {
+            int j1 = j0 + 64 < dn ? j0 + 64 : dn;
+            for (int j = j0; j < j1; j++) z[j] = 0.0;
+            for (int i = 0; i < di; i++) {
+                double ai = a[i];
+                const double* row = Wl + (long)i * dn;
+                for (int j = j0; j < j1; j++) z[j] += ai * row[j];
+            }
         }
         double* nxt = act + (long)(l + 1) * w;
         if (l < m->L - 1) {
@@ -101,13 +121,14 @@ static void mlp_row_forward(const mlp_t* m, const double* W, const double* x,
 }
 
 /* Gradient of ||M(k) - v||^2 w.r.t. all weights, written to G (P doubles).
- * Scratch: act (L+1)*maxw, pre L*maxw, d0/d1 maxw each. */
+ * Scratch: act (L+1)*maxw, pre L*maxw, d0/d1 maxw each.  nth: threads over
+ * rows (independent elements), as in mlp_row_forward. */
 static double mlp_row_grad(const mlp_t* m, const double* W, const double* k,
                            const double* v, double* G, double* act, double* pre,
-                           double* d0, double* d1) {
+                           double* d0, double* d1, int nth) {
     int w = m->maxw;
     double* out = d1;
-    mlp_row_forward(m, W, k, act, pre, out);
+    mlp_row_forward(m, W, k, act, pre, out, nth);
     double loss = 0.0;
     /* dl/dy = 2 (y - v) */
     for (int j = 0; j < m->dim; j++) {
@@ -121,6 +142,7 @@ static double mlp_row_grad(const mlp_t* m, const double* W, const double* k,
         const double* a = act + (long)l * w;       /* input of layer l */
         int di = m->din[l], dn = m->dout[l];
         double* Gl = G + m->off[l];
+        PAR_FOR(nth)
         for (int i = 0; i < di; i++) {
             double ai = a[i];
             double* row = Gl + (long)i * dn;
@@ -130,6 +152,7 @@ static double mlp_row_grad(const mlp_t* m, const double* W, const double* k,
             /* dl/dh_{l-1} = delta W_l^T, then through SiLU'(z_{l-1}) */
             const double* Wl = W + m->off[l];
             const double* z = pre + (long)(l - 1) * w;
+            PAR_FOR(nth)
             for (int i = 0; i < di; i++) {
                 const double* row = Wl + (long)i * dn;
                 double s = 0.0;
@@ -158,7 +181,7 @@ int tmref_mlp_forward(int dim, int depth, int expansion, const double* W,
     double* act = malloc(sizeof(double) * (size_t)(m.L + 1) * m.maxw);
     double* pre = malloc(sizeof(double) * (size_t)m.L * m.maxw);
     if (!act || !pre) { free(act); free(pre); return -2; }
-    mlp_row_forward(&m, W, x, act, pre, y);
+    mlp_row_forward(&m, W, x, act, pre, y, 1);
     free(act); free(pre);
     return 0;
 }
@@ -172,7 +195,7 @@ int tmref_mlp_grad(int dim, int depth, int expansion, const double* W,
     double* d0 = malloc(sizeof(double) * (size_t)m.maxw);
     double* d1 = malloc(sizeof(double) * (size_t)m.maxw);
     if (!act || !pre || !d0 || !d1) { free(act); free(pre); free(d0); free(d1); return -2; }
-    double l = mlp_row_grad(&m, W, k, v, G, act, pre, d0, d1);
+    double l = mlp_row_grad(&m, W, k, v, G, act, pre, d0, d1, 1);
     if (loss) *loss = l;
     free(act); free(pre); free(d0); free(d1);
     return 0;
@@ -190,6 +213,7 @@ typedef struct {
     int read;                 /* 0: queries after the chunk's write; 1: before;
                                  2: each after its own token's write */
     int tid, nthreads;
+    int inner;                /* threads per stream for its element loops */
     int err;
 } job_t;
 
@@ -202,7 +226,7 @@ static void* run_streams(void* arg) {
     const mlp_t* m = J->m;
     long P = m->off[m->L];
     int d = m->dim, H = J->heads, T = J->n_tokens, b = J->chunk;
-    int w = m->maxw;
+    int w = m->maxw, nth = J->inner;
     double* M0 = malloc(sizeof(double) * (size_t)P);
     double* G = malloc(sizeof(double) * (size_t)P);
     double* act = malloc(sizeof(double) * (size_t)(m->L + 1) * w);
@@ -224,7 +248,7 @@ static void* run_streams(void* arg) {
             for (int t = 0; t < T; t++) {
                 size_t row = ((size_t)bi * T + t) * H + hi;
                 widen(kk, J->q + row * d, d);
-                mlp_row_forward(m, M, kk, act, pre, out);
+                mlp_row_forward(m, M, kk, act, pre, out, nth);
                 memcpy(J->y + row * d, out, sizeof(double) * d);
             }
             continue;
@@ -238,7 +262,7 @@ static void* run_streams(void* arg) {
                 for (int t = c0; t < c0 + b; t++) {
                     size_t row = ((size_t)bi * T + t) * H + hi;
                     widen(kk, J->q + row * d, d);
-                    mlp_row_forward(m, M, kk, act, pre, out);
+                    mlp_row_forward(m, M, kk, act, pre, out, nth);
                     memcpy(J->y + row * d, out, sizeof(double) * d);
                 }
             }
@@ -246,14 +270,16 @@ static void* run_streams(void* arg) {
                 size_t row = ((size_t)bi * T + t) * H + hi;
                 widen(kk, J->k + row * d, d);
                 widen(vv, J->v + row * d, d);
-                mlp_row_grad(m, M0, kk, vv, G, act, pre, d0, d1);
+                mlp_row_grad(m, M0, kk, vv, G, act, pre, d0, d1, nth);
                 double th = J->theta[row], et = J->eta[row], al = J->alpha[row];
+                PAR_FOR(nth)
                 for (long p = 0; p < P; p++) S[p] = et * S[p] - th * G[p];
+                PAR_FOR(nth)
                 for (long p = 0; p < P; p++) M[p] = (1.0 - al) * M[p] + S[p];
                 if (J->y && J->read == 2) {
                     /* query t through the memory as token t left it */
                     widen(kk, J->q + row * d, d);
-                    mlp_row_forward(m, M, kk, act, pre, out);
+                    mlp_row_forward(m, M, kk, act, pre, out, nth);
                     memcpy(J->y + row * d, out, sizeof(double) * d);
                 }
             }
@@ -262,7 +288,7 @@ static void* run_streams(void* arg) {
                 for (int t = c0; t < c0 + b; t++) {
                     size_t row = ((size_t)bi * T + t) * H + hi;
                     widen(kk, J->q + row * d, d);
-                    mlp_row_forward(m, M, kk, act, pre, out);
+                    mlp_row_forward(m, M, kk, act, pre, out, nth);
                     memcpy(J->y + row * d, out, sizeof(double) * d);
                 }
             }
@@ -284,13 +310,15 @@ static int run(int dim, int depth, int expansion, int chunk, int batch, int head
     if (!retrieve_only && n_tokens % chunk) return -3;
     int ns = batch * heads;
     if (n_threads <= 0) n_threads = 1;
+    /* one worker per stream; threads left over split each stream's loops */
+    int inner = n_threads / (n_threads < ns ? n_threads : ns);
     if (n_threads > ns) n_threads = ns;
     job_t* jobs = calloc((size_t)n_threads, sizeof(job_t));
     pthread_t* th = calloc((size_t)n_threads, sizeof(pthread_t));
     if (!jobs || !th) { free(jobs); free(th); return -2; }
     for (int i = 0; i < n_threads; i++) {
         job_t J = {&m, chunk, batch, heads, n_tokens, k, v, q, theta, eta, alpha,
-                   state, y, retrieve_only, read, i, n_threads, 0};
+                   state, y, retrieve_only, read, i, n_threads, inner, 0};
         jobs[i] = J;
     }
     for (int i = 1; i < n_threads; i++) pthread_create(&th[i], NULL, run_streams, &jobs[i]);

@@ -25,7 +25,7 @@ def build() -> str:
     """Compile the oracle with gcc (plain -O2: no fast-math, so every sum runs
     in the order written)."""
     tmp = _LIB + ".tmp%d" % os.getpid()
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall",
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-fopenmp",
                            "-o", tmp, _SRC, "-lm", "-lpthread"])
     os.replace(tmp, _LIB)
     return _LIB
@@ -89,6 +89,13 @@ def mlp_grad(dim, depth, expansion, W, k, v):
 READ_MODES = {"after": 0, "before": 1, "token": 2}
 
 
+def default_threads():
+    """Threads for the oracle: the host's cores, at most 16 (a GPU host's
+    share per device).  Streams get a thread each; spare threads split each
+    stream's element loops (bitwise the same results)."""
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
 def forward(dim, depth, expansion, chunk, state, k, v, theta, eta, alpha, q=None,
             n_threads=None, read="after"):
     """Store the call's tokens into ``state`` (fp64 [streams][2P], updated in
@@ -103,7 +110,7 @@ def forward(dim, depth, expansion, chunk, state, k, v, theta, eta, alpha, q=None
     assert d == dim and state.dtype == np.float64 and state.flags.c_contiguous
     assert state.shape == (B * H, 2 * param_count(dim, depth, expansion))
     y = np.zeros((B, T, H, d), np.float64) if q is not None else None
-    nt = n_threads or min(os.cpu_count() or 1, B * H)
+    nt = n_threads or default_threads()
     rc = lib().tmref_forward_read(dim, depth, expansion, chunk, B, H, T, _f(k), _f(v), _f(q),
                                   _f(theta), _f(eta), _f(alpha), _d(state),
                                   _d(y) if y is not None else None, READ_MODES[read], nt)
@@ -118,7 +125,7 @@ def retrieve(dim, depth, expansion, state, q, n_threads=None):
     B, T, H, d = q.shape
     state = np.ascontiguousarray(state, np.float64)
     y = np.zeros((B, T, H, d), np.float64)
-    nt = n_threads or min(os.cpu_count() or 1, B * H)
+    nt = n_threads or default_threads()
     rc = lib().tmref_retrieve(dim, depth, expansion, B, H, T, _d(state), _f(q), _d(y), nt)
     if rc != 0:
         raise ValueError("tmref_retrieve failed: %d" % rc)

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from harness import TOL, relerr, say
+from harness import TOL, relerr, say, yerr
 from oracle import mac, prologue, tmref
 from test_gpu_parity import small
 from test_trained_neural_amd import inputs as I
@@ -92,7 +92,7 @@ def test_mac_segments_chain():
         tmref.forward(d, wl.depth, wl.expansion, wl.chunk, ref, ky, vy, th, et, al)
         my = tmref.retrieve(d, wl.depth, wl.expansion, ref, qy.astype(np.float32)).reshape(wl.batch, S, D)
         want = mac.gate(y, my)
-        e = relerr(out.cpu().numpy(), want)
+        e = yerr(out.cpu().numpy(), want)
         say("  segment %d: out %.2e" % (sgi, e))
         assert np.all(np.isfinite(want)) and e < TOL["bf16"]
     assert mem.check(st) == (False, 2 * S)

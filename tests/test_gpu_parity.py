@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from harness import GpuMemory, TOL, compare_state, dev_inputs, oracle_forward, relerr, say
+from harness import GpuMemory, TOL, compare_state, dev_inputs, oracle_forward, relerr, say, yerr
 from oracle import tmref
 from test_trained_neural_amd import inputs as I
 
@@ -58,7 +58,7 @@ def test_small_parity(wl):
     say("case", wl)
     ys_g, ys_r, st, ref, nf, pos = run_pair(wl)
     tol = TOL[wl.dtype]
-    ey = relerr(ys_g[0], ys_r[0])
+    ey = yerr(ys_g[0], ys_r[0])
     em, es = compare_state(wl, st, ref)
     say("  y %.2e  M %.2e  S %.2e" % (ey, em, es))
     assert not nf and pos == wl.seq
@@ -165,7 +165,7 @@ def test_retrieve_is_read_only_and_matches_oracle():
         after = g.export()
         assert np.array_equal(before, after) and np.array_equal(y, y2)
         yr = tmref.retrieve(wl.dim, wl.depth, wl.expansion, ref, ci.q)
-        assert relerr(y, yr) < TOL[dtype]
+        assert yerr(y, yr) < TOL[dtype]
         g.close()
 
 
@@ -197,7 +197,7 @@ def test_retrieve_many_rows(wl):
     y = g.retrieve(d["q"]).cpu().numpy()
     assert np.array_equal(before, g.export())
     yr = tmref.retrieve(wl.dim, wl.depth, wl.expansion, ref, ci.q)
-    e = relerr(y, yr)
+    e = yerr(y, yr)
     say("  y %.2e" % e)
     assert np.all(np.isfinite(y)) and e < TOL["bf16"]
     g.close()
@@ -252,7 +252,7 @@ def test_linear64_workload():
     wl = I.WORKLOADS["linear64"]
     say("case", wl)
     ys_g, ys_r, st, ref, nf, pos = run_pair(wl)
-    ey = relerr(ys_g[0], ys_r[0])
+    ey = yerr(ys_g[0], ys_r[0])
     em, es = compare_state(wl, st, ref)
     say("  y %.2e  M %.2e  S %.2e" % (ey, em, es))
     assert ey < 1e-4 and em < 1e-4 and es < 1e-4
@@ -264,7 +264,7 @@ def test_mlp384_workload(dtype):
     wl = I.WORKLOADS["mlp384"].replace(dtype=dtype)
     say("case", wl)
     ys_g, ys_r, st, ref, nf, pos = run_pair(wl)
-    ey = relerr(ys_g[0], ys_r[0])
+    ey = yerr(ys_g[0], ys_r[0])
     em, es = compare_state(wl, st, ref)
     say("  y %.2e  M %.2e  S %.2e" % (ey, em, es))
     assert not nf and pos == 1024
@@ -381,7 +381,7 @@ def test_read_before_write_parity(wl):
         y = g.forward(d, read=T.TM_READ_BEFORE_WRITE).cpu().numpy()
         h.forward(d)
         yr = oracle_forward(wl, ref, ci, read="before")
-        ey = relerr(y, yr)
+        ey = yerr(y, yr)
         em, es = compare_state(wl, g.export(), ref)
         say("  call %d: y %.2e  M %.2e  S %.2e" % (j, ey, em, es))
         assert ey < tol and em < tol and es < 2 * tol
@@ -401,7 +401,7 @@ def test_read_before_write_mlp384():
     y = g.forward(dev_inputs(ci, "bf16"), read=T.TM_READ_BEFORE_WRITE).cpu().numpy()
     ref = I.initial_state(wl, p)
     yr = oracle_forward(wl, ref, ci, read="before")
-    ey = relerr(y, yr)
+    ey = yerr(y, yr)
     em, es = compare_state(wl, g.export(), ref)
     say("  y %.2e  M %.2e  S %.2e" % (ey, em, es))
     assert ey < TOL["bf16"] and em < TOL["bf16"] and es < 2 * TOL["bf16"]

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import test_trained_neural_amd as T
-from harness import GpuMemory, TOL, compare_state, relerr, say
+from harness import GpuMemory, TOL, compare_state, relerr, say, yerr
 from oracle import prologue as PR
 from oracle import tmref
 from test_trained_neural_amd import inputs as I
@@ -58,6 +58,11 @@ CASES = [
     (wl_of("p1024", 1, 48, 1, 1024, "f32"), 4),
     # one tap: no convolution
     (wl_of("p_k1", 1, 33, 2, 64, "bf16"), 1),
+    # calls long enough for the 32-token tiles (their grid covers the compute
+    # units): 8 heads of 128 with a ragged last tile; fp32 with two heads and
+    # a ragged last tile
+    (wl_of("p8x128_long", 2, 340, 8, 128, "bf16"), 4),
+    (wl_of("p_f32_long", 4, 1000, 2, 64, "f32"), 3),
 ]
 
 
@@ -72,7 +77,7 @@ def test_project_parity(case):
     ref = PR.project(pi.x, pi.w_kvq, pi.conv, pi.w_gate, pi.gate_bias, wl.heads)
     tol = TOL[wl.dtype]
     for n, a, r in zip(("k", "v", "q", "theta", "eta", "alpha"), got, ref[:6]):
-        e = relerr(a, r)
+        e = yerr(a, r)
         say("  %s %.2e" % (n, e))
         assert e < (tol if n in ("k", "v", "q") else 1e-4), n
     if K > 1:
@@ -82,17 +87,22 @@ def test_project_parity(case):
     T.tm_destroy(g.ctx)
 
 
-def test_project_history_across_calls():
-    # calls of 37, 2 (shorter than the history) and 57 tokens equal one call
-    wl = wl_of("p_hist", 2, 96, 2, 64, "f32")
-    say("case", wl)
+@pytest.mark.parametrize("wl,cuts", [
+    # calls of 37, 2 (shorter than the history) and 57 tokens (16-token tiles)
+    (wl_of("p_hist", 2, 96, 2, 64, "f32"), (0, 37, 39, 96)),
+    # calls of 300, 2 and 405 tokens: the long ones on 32-token tiles
+    (wl_of("p_hist_long", 4, 707, 2, 64, "f32"), (0, 300, 302, 707)),
+], ids=lambda x: x.name if hasattr(x, "name") else "")
+def test_project_history_across_calls(wl, cuts):
+    # consecutive calls equal one call
+    say("case", wl, cuts)
     p = I.make_params(wl)
     pi = I.make_prologue(wl, p, conv_len=4)
     ref = PR.project(pi.x, pi.w_kvq, pi.conv, pi.w_gate, pi.gate_bias, wl.heads)
     g = GpuProject(wl, pi)
-    parts = [g(pi.x[:, a:b]) for a, b in ((0, 37), (37, 39), (39, 96))]
+    parts = [g(pi.x[:, a:b]) for a, b in zip(cuts[:-1], cuts[1:])]
     for i, n in enumerate(("k", "v", "q", "theta", "eta", "alpha")):
-        e = relerr(np.concatenate([pp[i] for pp in parts], axis=1), ref[i])
+        e = yerr(np.concatenate([pp[i] for pp in parts], axis=1), ref[i])
         say("  %s %.2e" % (n, e))
         assert e < 1e-4, n
     assert relerr(g.hist.cpu().numpy(), ref[6]) < 1e-4
@@ -124,7 +134,7 @@ def test_tokens_to_memory_output():
     ref = I.initial_state(wl, p)
     yr = tmref.forward(wl.dim, wl.depth, wl.expansion, wl.chunk, ref, ci.k, ci.v, ci.theta, ci.eta, ci.alpha,
                        q=ci.q)
-    ey = relerr(y, yr)
+    ey = yerr(y, yr)
     em, es = compare_state(wl, mem.export(), ref)
     say("  y %.2e  M %.2e  S %.2e" % (ey, em, es))
     assert ey < TOL["bf16"] and em < TOL["bf16"] and es < 2 * TOL["bf16"]

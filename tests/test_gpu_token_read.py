@@ -1,7 +1,8 @@
 """Per-token read (TM_READ_PER_TOKEN: every query through the memory as its
 own token's write left it, the gradients at the chunk start) against the
-oracle's per-token order, element by element on y and on the state after
-each call.  The small shapes span ragged chunks (5, 24 tokens), a chunk of
+oracle's per-token order on y (per tensor, per token row and per element:
+harness.yerr) and on the state after each call (per weight matrix and per
+element: harness.compare_state).  The small shapes span ragged chunks (5, 24 tokens), a chunk of
 one token, several streams and heads, depth 1 to 4, and both operand types;
 mlp384 runs at full size.
 
@@ -12,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from harness import GpuMemory, TOL, compare_state, dev_inputs, oracle_forward, relerr, say
+from harness import GpuMemory, TOL, compare_state, dev_inputs, oracle_forward, relerr, say, yerr
 from test_gpu_parity import SMALL, small
 from test_gpu_workloads import MAX
 from test_trained_neural_amd import inputs as I
@@ -39,7 +40,7 @@ def test_per_token_read_parity(wl):
         y = g.forward(d, read=T.TM_READ_PER_TOKEN).cpu().numpy()
         h.forward(d)
         yr = oracle_forward(wl, ref, ci, read="token")
-        ey = relerr(y, yr)
+        ey = yerr(y, yr)
         em, es = compare_state(wl, g.export(), ref)
         ed = relerr(g.export(), h.export())
         say("  call %d: y %.2e  M %.2e  S %.2e  state vs read-after-write %.2e" % (j, ey, em, es, ed))
@@ -66,7 +67,7 @@ def test_per_token_read_maximum_sizes(wl):
     y = g.forward(dev_inputs(ci, wl.dtype), read=T.TM_READ_PER_TOKEN).cpu().numpy()
     ref = I.initial_state(wl, p)
     yr = oracle_forward(wl, ref, ci, read="token")
-    ey = relerr(y, yr)
+    ey = yerr(y, yr)
     em, es = compare_state(wl, g.export(), ref)
     say("  y %.2e  M %.2e  S %.2e" % (ey, em, es))
     tol = TOL[wl.dtype]
@@ -85,7 +86,7 @@ def test_per_token_read_mlp384():
     y = g.forward(dev_inputs(ci, "bf16"), read=T.TM_READ_PER_TOKEN).cpu().numpy()
     ref = I.initial_state(wl, p)
     yr = oracle_forward(wl, ref, ci, read="token")
-    ey = relerr(y, yr)
+    ey = yerr(y, yr)
     em, es = compare_state(wl, g.export(), ref)
     say("  y %.2e  M %.2e  S %.2e" % (ey, em, es))
     assert ey < TOL["bf16"] and em < TOL["bf16"] and es < 2 * TOL["bf16"]
