@@ -132,6 +132,42 @@ tm_status tm_forward(const tm_ctx* ctx, void* state, const void* k, const void* 
                      const float* alpha, float* y, int batch, int heads,
                      int n_tokens, tm_dtype dtype, void* workspace, void* stream);
 
+/* The backward through the store: gradients of an outer loss through one
+ * call of tm_forward (read = TM_READ_AFTER_WRITE) or tm_forward_ex with
+ * TM_READ_BEFORE_WRITE, for training a model around the memory
+ * ("titans-pytorch analysis", Editorial conclusion: the loss must
+ * backpropagate through the memory state; "Titans, explained", step 6: the
+ * chunked form is what makes the memory trainable in parallel).  For
+ *     L = sum(dy * y) + <dM, M_after> + <dS, S_after>,
+ * with y and the state after the call as that call produces them from
+ * `state` (the state blob as it was BEFORE the call; read only) and the
+ * same k, v, q and gates, it writes
+ *     dk, dv, dq = dL/dk, dL/dv, dL/dq   ([batch][n_tokens][heads][dim] fp32),
+ *     dtheta, deta, dalpha               ([batch][n_tokens][heads] fp32),
+ * and replaces dstate -- on entry (dM, dS), the gradient with respect to
+ * the state after the call, canonical fp32 [batch*heads][2P] as
+ * tm_state_export lays it out (zeros if the loss does not see that state) --
+ * with the gradient with respect to the state before the call, so that a
+ * stream of calls is differentiated by calling tm_backward on them in
+ * reverse order with one dstate buffer.  dy is fp32 in the token layout.
+ * The call recomputes the forward from `state` (every chunk-start state is
+ * kept in the workspace) and sweeps the chunks in reverse; all its
+ * arithmetic is fp32, whatever dtype k, v, q have (the gradient of the
+ * exact function at the given inputs).  workspace: tm_backward_workspace_bytes
+ * bytes, 256-byte aligned.  TM_READ_PER_TOKEN gives TM_ERR_INVALID.  Errors
+ * as for tm_forward (dstate null or not 16-byte aligned: TM_ERR_INVALID);
+ * n_tokens == 0 leaves dstate as it is (the call is the identity). */
+tm_status tm_backward(const tm_ctx* ctx, const void* state, const void* k, const void* v,
+                      const void* q, const float* theta, const float* eta, const float* alpha,
+                      const float* dy, float* dstate, float* dk, float* dv, float* dq,
+                      float* dtheta, float* deta, float* dalpha, int batch, int heads,
+                      int n_tokens, tm_dtype dtype, tm_read read, void* workspace, void* stream);
+
+/* Workspace bytes of tm_backward for a call of n_tokens per stream: the
+ * chunk-start states (n_tokens / chunk + 1 of them, 8P bytes per stream
+ * each), the key rows' activations per chunk and the sweep's scratch. */
+size_t tm_backward_workspace_bytes(const tm_ctx* ctx, int batch, int heads, int n_tokens);
+
 /* tm_forward for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same kernels and results as tm_forward, bitwise, but the workspace is

@@ -26,10 +26,12 @@ EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_w
             "tm_state_init", "tm_store", "tm_retrieve", "tm_forward", "tm_state_export",
             "tm_state_import", "tm_state_check", "tm_status_str", "tm_timing_enable", "tm_timing_read",
             "tm_graphs_enable", "tm_w1_split_enable", "tm_forward_ex", "tm_project", "tm_mac_window",
-            "tm_mac_gate", "tm_config", "tm_forward_noalloc")
+            "tm_mac_gate", "tm_config", "tm_forward_noalloc", "tm_backward", "tm_backward_workspace_bytes")
 
-# kernel classes of tm_timing_enable / tm_timing_read (3 is unused)
+# kernel classes of tm_timing_enable / tm_timing_read (3 is unused); 8 and 9
+# are tm_backward's state-streaming launches and its other launches
 K_SCAN, K_FWD, K_BWD, K_FIRST, K_TOKEN_READ, K_PROJECT, K_MAC = 0, 1, 2, 4, 5, 6, 7
+K_BACKWARD_STATE, K_BACKWARD_REST = 8, 9
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -72,6 +74,10 @@ def lib():
         L.tm_forward.restype = _i
         L.tm_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
         L.tm_forward_ex.restype = _i
+        L.tm_backward.restype = _i
+        L.tm_backward.argtypes = [_vp] * 16 + [_i, _i, _i, _i, _i, _vp, _vp]
+        L.tm_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.tm_backward_workspace_bytes.argtypes = [_vp, _i, _i, _i]
         L.tm_forward_noalloc.restype = _i
         L.tm_forward_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
         L.tm_project.restype = _i
@@ -254,6 +260,35 @@ def tm_forward(ctx, state, k, v, q, theta, eta, alpha, y, workspace, stream=None
     _check("tm_forward", lib().tm_forward(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(q), _ptr(theta),
                                           _ptr(eta), _ptr(alpha), _ptr(y), B, H, T, _dtype_code(k),
                                           _ptr(workspace), _stream(stream)))
+
+
+def tm_backward_workspace_bytes(ctx, batch, heads, n_tokens):
+    return lib().tm_backward_workspace_bytes(ctx, batch, heads, n_tokens)
+
+
+def tm_backward(ctx, state, k, v, q, theta, eta, alpha, dy, dstate, dk, dv, dq, dtheta, deta, dalpha, workspace,
+                read=TM_READ_AFTER_WRITE, stream=None):
+    """Gradients through one tm_forward call (see include/tm.h): ``state``
+    is the state blob as it was before the call (read only); dy [B][T][H][d]
+    fp32; dstate [B*H][2P] fp32, on entry the gradient with respect to the
+    state after the call, on return the one with respect to the state
+    before it; dk, dv, dq, dtheta, deta, dalpha are written."""
+    _memory_call(k, v, q, theta, eta, alpha, None)
+    _same(torch.float32, ("dy", dy), ("dk", dk), ("dv", dv), ("dq", dq), ("dtheta", dtheta), ("deta", deta),
+          ("dalpha", dalpha), ("dstate", dstate))
+    for name, t in (("dy", dy), ("dk", dk), ("dv", dv), ("dq", dq)):
+        _shape(name, t, k.shape)
+    for name, t in (("dtheta", dtheta), ("deta", deta), ("dalpha", dalpha)):
+        _shape(name, t, k.shape[:3])
+    _tok(k, v, q, theta, eta, alpha, dy, dk, dv, dq, dtheta, deta, dalpha)
+    B, T, H, d = k.shape
+    _memory_sizes(ctx, state, False, B, H, T, d)
+    _canonical("dstate", dstate, ctx, B, H)
+    _blob("workspace", workspace, tm_backward_workspace_bytes(ctx, B, H, T))
+    _check("tm_backward", lib().tm_backward(ctx, _ptr(state), _ptr(k), _ptr(v), _ptr(q), _ptr(theta), _ptr(eta),
+                                            _ptr(alpha), _ptr(dy), _ptr(dstate), _ptr(dk), _ptr(dv), _ptr(dq),
+                                            _ptr(dtheta), _ptr(deta), _ptr(dalpha), B, H, T, _dtype_code(k),
+                                            int(read), _ptr(workspace), _stream(stream)))
 
 
 def tm_forward_noalloc(ctx, state, k, v, q, theta, eta, alpha, y, stream=None):

@@ -37,7 +37,7 @@ static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
 // kernels' arguments depend on (device, every pointer and every size).
 struct GraphEntry {
     int dev, kind, batch, heads, n_tokens, dtype, opt, extra;
-    const void* p[12];
+    const void* p[16];
     int seen;                    // sightings before capture
     hipGraphExec_t exec;
     unsigned long long last;     // LRU stamp
@@ -261,7 +261,12 @@ hipError_t scratch_address(void** out) {
 
 // ---- optional per-launch timing (tm_timing_enable / tm_timing_read) ----
 // (class 3 is unused: the update of layers 1.. rides in the first-layer launch)
-enum { K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_FIRST = 4, K_R3 = 5, K_PROJ = 6, K_MAC = 7, K_CLASSES = 8 };
+enum {
+    K_SCAN = 0, K_FWD = 1, K_BWD = 2, K_FIRST = 4, K_R3 = 5, K_PROJ = 6, K_MAC = 7,
+    K_BSTATE = 8,   // tm_backward: the launches that stream the state (recompute's write, adjoint update)
+    K_BREST = 9,    // tm_backward: its other products, element-wise steps and coefficients
+    K_CLASSES = 10
+};
 struct Timed {
     hipEvent_t a, b;
     int kind;
@@ -926,6 +931,361 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     return TM_OK;
 }
 
+// ---- the backward through the store (tm_backward) ----
+// Workspace: every chunk-start state (canonical fp32, [chunk][stream][2P],
+// C + 1 of them), the chunks' coefficients, each (stream, chunk)'s key-row
+// record from the recompute, the reverse sweep's per-stream scratch, and
+// the partial sums behind the gates' gradients.  Sizes in 4-byte elements.
+struct BwdLayout {
+    size_t tape, cc, dc, cs, key, scr, pgp, pad, total;
+    long tape_cs;               // elements per chunk slot (ns * 2P)
+    long rec;                   // elements of one (stream, chunk) key record
+    long hk[MAXL], zk[MAXL], dk[MAXL], gk[MAXL];   // offsets inside a record
+    long scr_ss;                // per-stream elements of the sweep's scratch
+    long hq[MAXL], zq[MAXL], dq[MAXL], db[MAXL], hb[MAXL], u[MAXL], zb[MAXL];
+    int ngp, nad, gpbase[MAXL], adbase[MAXL];
+    int C;
+};
+
+BwdLayout bwd_layout(const tm_ctx* c, long ns, long T) {
+    BwdLayout w;
+    memset(&w, 0, sizeof(w));
+    const long b = c->chunk, C = T / b;
+    w.C = (int)C;
+    size_t o = 0;
+    w.tape_cs = ns * 2 * c->P;
+    w.tape = o; o += al256((size_t)(C + 1) * w.tape_cs * 4);
+    w.cc = o; o += al256((size_t)ns * T * 4);
+    w.dc = o; o += al256((size_t)ns * T * 4);
+    w.cs = o; o += al256((size_t)ns * C * 16);
+    // key record: h_l (l >= 1; h_0 is the keys themselves), z_l, Delta_l,
+    // and g_l = Delta_l W_l^T (l >= 1), each [b][width] row-major
+    long r = 0;
+    for (int l = 0; l < c->L; ++l) {
+        if (l >= 1) { w.hk[l] = r; r += b * c->din[l]; }
+        w.zk[l] = r; r += b * c->dout[l];
+        w.dk[l] = r; r += b * c->dout[l];
+        if (l >= 1) { w.gk[l] = r; r += b * c->din[l]; }
+    }
+    w.rec = r;
+    w.key = o; o += al256((size_t)ns * C * r * 4);
+    // sweep scratch per stream: the queries' h, z and backpropagated delta,
+    // and the key rows' Deltabar, hbar (from the surprise's adjoint), u and zbar
+    r = 0;
+    for (int l = 0; l < c->L; ++l) {
+        if (l >= 1) { w.hq[l] = r; r += b * c->din[l]; }
+        if (l + 1 < c->L) { w.zq[l] = r; r += b * c->dout[l]; w.dq[l] = r; r += b * c->dout[l]; }
+        w.db[l] = r; r += b * c->dout[l];
+        w.hb[l] = r; r += b * c->din[l];
+        if (l >= 1) { w.u[l] = r; r += b * c->din[l]; }
+        w.zb[l] = r; r += b * c->dout[l];
+    }
+    w.scr_ss = r;
+    w.scr = o; o += al256((size_t)ns * r * 4);
+    for (int l = 0; l < c->L; ++l) {
+        w.gpbase[l] = w.ngp;
+        w.ngp += (c->dout[l] + 63) / 64;
+        w.adbase[l] = w.nad;
+        w.nad += ((c->din[l] + 63) / 64) * ((c->dout[l] + 63) / 64);
+    }
+    w.pgp = o; o += al256((size_t)ns * C * w.ngp * 128 * 4);
+    w.pad = o; o += al256((size_t)ns * C * w.nad * 3 * 4);
+    w.total = o > 0 ? o : 256;
+    return w;
+}
+
+BMat rowm(const void* p, long ss, long ld) {
+    BMat m;
+    memset(&m, 0, sizeof(m));
+    m.p = p;
+    m.ss = ss;
+    m.ld = ld;
+    return m;
+}
+BMat tokm(const void* p, int t0, int bf) {
+    BMat m;
+    memset(&m, 0, sizeof(m));
+    m.p = p;
+    m.tok = 1;
+    m.t0 = t0;
+    m.bf = bf;
+    return m;
+}
+
+tm_status run_bwd(const tm_ctx* c, const void* state, const void* k, const void* v, const void* q,
+                  const float* theta, const float* eta, const float* alpha, const float* dy, float* dst,
+                  float* dk, float* dv, float* dq, float* dth, float* det, float* dal, int batch, int heads,
+                  int T, tm_dtype dtype, int read, void* ws_v, hipStream_t st) {
+    const long ns = (long)batch * heads, P = c->P;
+    const int b = c->chunk, C = T / b, L = c->L;
+    const int bf = dtype == TM_BF16 ? 1 : 0;
+    BwdLayout w = bwd_layout(c, ns, T);
+    char* ws = static_cast<char*>(ws_v);
+    float* tape = reinterpret_cast<float*>(ws + w.tape);
+    float* cc = reinterpret_cast<float*>(ws + w.cc);
+    float* dc = reinterpret_cast<float*>(ws + w.dc);
+    float* cs = reinterpret_cast<float*>(ws + w.cs);
+    float* key = reinterpret_cast<float*>(ws + w.key);
+    float* scr = reinterpret_cast<float*>(ws + w.scr);
+    float* pgp = reinterpret_cast<float*>(ws + w.pgp);
+    float* pad = reinterpret_cast<float*>(ws + w.pad);
+    const TokLayout tl{T, heads, c->dim};
+    const TokLayout gl{T, heads, 1};
+    if (g_log_plan)
+        fprintf(stderr,
+                "[tm] backward plan: %d chunks of %d over %ld streams; recompute 3L-1 = %d launches per chunk, "
+                "reverse sweep about 9L = %d per chunk; workspace %zu bytes\n",
+                C, b, ns, 3 * L - 1, 9 * L, w.total * 1);
+
+    auto gemm = [&](const BGemm& g, int kind) -> bool {
+        return timed(kind, st, [&] { return launch_bgemm(g, (int)ns, st); }) == hipSuccess;
+    };
+    auto base = [&](int m, int n, int kk, int ta, int tb, int epi) {
+        BGemm g;
+        memset(&g, 0, sizeof(g));
+        g.m = m;
+        g.n = n;
+        g.k = kk;
+        g.ta = ta;
+        g.tb = tb;
+        g.epi = epi;
+        g.tl = tl;
+        return g;
+    };
+    // layer l of a chunk-start state slot: M (S = 1: S), [din][dout] row-major
+    auto slot = [&](int ci, int l, int S) {
+        return rowm(tape + (size_t)ci * w.tape_cs + (S ? P : 0) + c->off[l], 2 * P, c->dout[l]);
+    };
+    auto adj = [&](int l, int S) { return rowm(dst + (S ? P : 0) + c->off[l], 2 * P, c->dout[l]); };
+    auto rec = [&](int ci, long off, int width) { return rowm(key + (size_t)ci * w.rec + off, (long)C * w.rec, width); };
+    auto sc = [&](long off, int width) { return rowm(scr + off, w.scr_ss, width); };
+    auto keys = [&](int ci) { return tokm(k, ci * b, bf); };
+    auto hkey = [&](int ci, int l) { return l == 0 ? keys(ci) : rec(ci, w.hk[l], c->din[l]); };
+
+    // the starting state, canonical, into slot 0
+    {
+        StateLayout sl = state_layout(c, ns);
+        const char* s8 = static_cast<const char*>(state);
+        if (timed(K_BREST, st, [&] {
+                return launch_export(reinterpret_cast<const float*>(s8 + sl.M), reinterpret_cast<const float*>(s8 + sl.S),
+                                     tape, P, (int)ns, c->din[0], c->dout[0], L > 1 ? c->dout[1] : 0, st);
+            }) != hipSuccess)
+            return TM_ERR_HIP;
+    }
+    // every chunk's coefficients
+    BCoef co;
+    memset(&co, 0, sizeof(co));
+    co.mode = BC_FWD;
+    co.b = b;
+    co.C = C;
+    co.theta = theta;
+    co.eta = eta;
+    co.alpha = alpha;
+    co.gl = gl;
+    co.cc = cc;
+    co.dc = dc;
+    co.coef_ss = T;
+    co.cs = cs;
+    co.cs_ss = (long)C * 4;
+    if (timed(K_BREST, st, [&] { return launch_bcoef(co, (int)ns, st); }) != hipSuccess) return TM_ERR_HIP;
+
+    // ---- recompute: chunk by chunk, keeping every chunk-start state ----
+    for (int ci = 0; ci < C; ++ci) {
+        // the key rows' forward at M_0 (z, h; the last layer's Delta = 2 (z - v))
+        for (int l = 0; l < L; ++l) {
+            const bool last = l + 1 == L;
+            BGemm g = base(b, c->dout[l], c->din[l], 0, 0, last ? BE_OUTK : BE_HID);
+            g.A = hkey(ci, l);
+            g.B = slot(ci, l, 0);
+            g.c0 = rec(ci, w.zk[l], c->dout[l]);
+            g.c1 = last ? rec(ci, w.dk[l], c->dout[l]) : rec(ci, w.hk[l + 1], c->din[l + 1]);
+            if (last) g.x0 = tokm(v, ci * b, bf);
+            if (!gemm(g, K_BREST)) return TM_ERR_HIP;
+        }
+        // their backward: g_l = Delta_l W_l^T, Delta_{l-1} = g_l * SiLU'(z_{l-1})
+        for (int l = L - 1; l >= 1; --l) {
+            BGemm g = base(b, c->din[l], c->dout[l], 0, 1, BE_BWDK);
+            g.A = rec(ci, w.dk[l], c->dout[l]);
+            g.B = slot(ci, l, 0);
+            g.c0 = rec(ci, w.gk[l], c->din[l]);
+            g.c1 = rec(ci, w.dk[l - 1], c->dout[l - 1]);
+            g.x0 = rec(ci, w.zk[l - 1], c->dout[l - 1]);
+            if (!gemm(g, K_BREST)) return TM_ERR_HIP;
+        }
+        // the write: M_end = p_alpha M_0 + s0 S_0 - H^T diag(c) Delta,
+        // S_end = p_eta S_0 - H^T diag(d) Delta, into the next slot
+        for (int l = 0; l < L; ++l) {
+            BGemm g = base(c->din[l], c->dout[l], b, 1, 0, BE_UPD);
+            g.dual = 2;
+            g.A = hkey(ci, l);
+            g.B = rec(ci, w.dk[l], c->dout[l]);
+            g.sk0 = cc + (size_t)ci * b;
+            g.sk1 = dc + (size_t)ci * b;
+            g.sk_ss = T;
+            g.x0 = slot(ci, l, 0);
+            g.x1 = slot(ci, l, 1);
+            g.c0 = slot(ci + 1, l, 0);
+            g.c1 = slot(ci + 1, l, 1);
+            g.cs = cs + (size_t)ci * 4;
+            g.cs_ss = (long)C * 4;
+            if (!gemm(g, K_BSTATE)) return TM_ERR_HIP;
+        }
+    }
+
+    // ---- reverse sweep ----
+    // the queries of chunk ci read slot wq: forward of their rows, backprop
+    // of dy down to dq, and their weights' gradient added to Mbar
+    auto query_steps = [&](int ci, int wq) -> bool {
+        for (int l = 0; l + 1 < L; ++l) {
+            BGemm g = base(b, c->dout[l], c->din[l], 0, 0, BE_HID);
+            g.A = l == 0 ? tokm(q, ci * b, bf) : sc(w.hq[l], c->din[l]);
+            g.B = slot(wq, l, 0);
+            g.c0 = sc(w.zq[l], c->dout[l]);
+            g.c1 = sc(w.hq[l + 1], c->din[l + 1]);
+            if (!gemm(g, K_BREST)) return false;
+        }
+        auto dqm = [&](int l) { return l == L - 1 ? tokm(dy, ci * b, 0) : sc(w.dq[l], c->dout[l]); };
+        for (int l = L - 1; l >= 0; --l) {
+            BGemm g = base(b, c->din[l], c->dout[l], 0, 1, l > 0 ? BE_QB : BE_STORE);
+            g.A = dqm(l);
+            g.B = slot(wq, l, 0);
+            if (l > 0) {
+                g.c0 = sc(w.dq[l - 1], c->dout[l - 1]);
+                g.x0 = sc(w.zq[l - 1], c->dout[l - 1]);
+            } else {
+                g.c0 = tokm(dq, ci * b, 0);
+            }
+            if (!gemm(g, K_BREST)) return false;
+        }
+        for (int l = 0; l < L; ++l) {
+            BGemm g = base(c->din[l], c->dout[l], b, 1, 0, BE_ACC);
+            g.A = l == 0 ? tokm(q, ci * b, bf) : sc(w.hq[l], c->din[l]);
+            g.B = dqm(l);
+            g.c0 = adj(l, 0);
+            if (!gemm(g, K_BREST)) return false;
+        }
+        return true;
+    };
+
+    for (int ci = C - 1; ci >= 0; --ci) {
+        if (read == TM_READ_AFTER_WRITE && !query_steps(ci, ci + 1)) return TM_ERR_HIP;
+        // the surprise's adjoint Gbar_i = -(c_i Mbar + d_i Sbar), through
+        // G_l = h_l^T Delta_l: Deltabar_l = -(c h_l Mbar_l + d h_l Sbar_l) (with
+        // the row sums behind cbar, dbar), hbar_l = -(c Delta_l Mbar_l^T + d Delta_l Sbar_l^T)
+        for (int l = 0; l < L; ++l) {
+            BGemm g = base(b, c->dout[l], c->din[l], 0, 0, BE_GP);
+            g.dual = 1;
+            g.A = hkey(ci, l);
+            g.B = adj(l, 0);
+            g.B2 = adj(l, 1);
+            g.rs0 = cc + (size_t)ci * b;
+            g.rs1 = dc + (size_t)ci * b;
+            g.sk_ss = T;
+            g.x0 = rec(ci, w.dk[l], c->dout[l]);
+            g.c0 = sc(w.db[l], c->dout[l]);
+            g.part = pgp + (size_t)ci * w.ngp * 128;
+            g.part_ss = (long)C * w.ngp * 128;
+            g.tile0 = w.gpbase[l];
+            if (!gemm(g, K_BREST)) return TM_ERR_HIP;
+            BGemm h = base(b, c->din[l], c->dout[l], 0, 1, BE_GQ);
+            h.dual = 1;
+            h.A = rec(ci, w.dk[l], c->dout[l]);
+            h.B = adj(l, 0);
+            h.B2 = adj(l, 1);
+            h.rs0 = cc + (size_t)ci * b;
+            h.rs1 = dc + (size_t)ci * b;
+            h.sk_ss = T;
+            h.c0 = sc(w.hb[l], c->din[l]);
+            if (!gemm(h, K_BREST)) return TM_ERR_HIP;
+        }
+        // back through the key rows' backward (layers 1 .. L-1 in order)
+        for (int l = 1; l < L; ++l) {
+            BElem e;
+            memset(&e, 0, sizeof(e));
+            e.mode = BW_U;
+            e.b = b;
+            e.n = c->din[l];
+            e.db = scr + w.db[l - 1];
+            e.z = key + (size_t)ci * w.rec + w.zk[l - 1];
+            e.g = key + (size_t)ci * w.rec + w.gk[l];
+            e.u = scr + w.u[l];
+            e.zb = scr + w.zb[l - 1];
+            e.ss = w.scr_ss;
+            e.rss = (long)C * w.rec;
+            // then Deltabar_l += u_l W_l (from g_l = Delta_l W_l^T)
+            BGemm g = base(b, c->dout[l], c->din[l], 0, 0, BE_ACC);
+            g.A = sc(w.u[l], c->din[l]);
+            g.B = slot(ci, l, 0);
+            g.c0 = sc(w.db[l], c->dout[l]);
+            if (timed(K_BREST, st, [&] { return launch_belem(e, (int)ns, st); }) != hipSuccess) return TM_ERR_HIP;
+            if (!gemm(g, K_BREST)) return TM_ERR_HIP;
+        }
+        {
+            BElem e;
+            memset(&e, 0, sizeof(e));
+            e.mode = BW_OUT;
+            e.b = b;
+            e.n = c->dout[L - 1];
+            e.db = scr + w.db[L - 1];
+            e.zb = scr + w.zb[L - 1];
+            e.ss = w.scr_ss;
+            e.dv = dv;
+            e.tl = tl;
+            e.t0 = ci * b;
+            if (timed(K_BREST, st, [&] { return launch_belem(e, (int)ns, st); }) != hipSuccess) return TM_ERR_HIP;
+        }
+        // back through the key rows' forward (layers L-1 .. 0): hbar_l =
+        // hbar_l(surprise) + zbar_l W_l^T, zbar_{l-1} += hbar_l SiLU'(z_{l-1}); dk
+        for (int l = L - 1; l >= 0; --l) {
+            BGemm g = base(b, c->din[l], c->dout[l], 0, 1, l > 0 ? BE_HB : BE_ADDSTORE);
+            g.A = sc(w.zb[l], c->dout[l]);
+            g.B = slot(ci, l, 0);
+            g.x0 = sc(w.hb[l], c->din[l]);
+            if (l > 0) {
+                g.x1 = rec(ci, w.zk[l - 1], c->dout[l - 1]);
+                g.c1 = sc(w.zb[l - 1], c->dout[l - 1]);
+            } else {
+                g.c0 = tokm(dk, ci * b, 0);
+            }
+            if (!gemm(g, K_BREST)) return TM_ERR_HIP;
+        }
+        // Mbar_0 = p_alpha Mbar + h^T zbar + u^T Delta, Sbar_0 = p_eta Sbar + s0 Mbar,
+        // with the sums behind the chunk scalars' adjoints
+        for (int l = 0; l < L; ++l) {
+            BGemm g = base(c->din[l], c->dout[l], b, 1, 0, BE_ADJ);
+            g.A = hkey(ci, l);
+            g.B = sc(w.zb[l], c->dout[l]);
+            if (l >= 1) {
+                g.k2 = b;
+                g.A2 = sc(w.u[l], c->din[l]);
+                g.Bs2 = rec(ci, w.dk[l], c->dout[l]);
+            }
+            g.c0 = adj(l, 0);
+            g.c1 = adj(l, 1);
+            g.x0 = slot(ci, l, 0);
+            g.x1 = slot(ci, l, 1);
+            g.cs = cs + (size_t)ci * 4;
+            g.cs_ss = (long)C * 4;
+            g.part = pad + (size_t)ci * w.nad * 3;
+            g.part_ss = (long)C * w.nad * 3;
+            g.tile0 = w.adbase[l];
+            if (!gemm(g, K_BSTATE)) return TM_ERR_HIP;
+        }
+        if (read == TM_READ_BEFORE_WRITE && !query_steps(ci, ci)) return TM_ERR_HIP;
+    }
+    // the gates' gradients, every chunk
+    co.mode = BC_BWD;
+    co.pgp = pgp;
+    co.ngp = w.ngp;
+    co.pad = pad;
+    co.nad = w.nad;
+    co.dtheta = dth;
+    co.deta = det;
+    co.dalpha = dal;
+    if (timed(K_BREST, st, [&] { return launch_bcoef(co, (int)ns, st); }) != hipSuccess) return TM_ERR_HIP;
+    return TM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1115,6 +1475,35 @@ tm_status tm_forward(const tm_ctx* c, void* state, const void* k, const void* v,
                      int heads, int n_tokens, tm_dtype dtype, void* ws, void* stream) {
     return tm_forward_ex(c, state, k, v, q, theta, eta, alpha, y, batch, heads, n_tokens, dtype,
                          TM_READ_AFTER_WRITE, ws, stream);
+}
+
+size_t tm_backward_workspace_bytes(const tm_ctx* c, int batch, int heads, int n_tokens) {
+    if (!c || batch <= 0 || heads <= 0 || n_tokens < 0) return 0;
+    return bwd_layout(c, (long)batch * heads, n_tokens).total;
+}
+
+tm_status tm_backward(const tm_ctx* c, const void* state, const void* k, const void* v, const void* q,
+                      const float* theta, const float* eta, const float* alpha, const float* dy, float* dstate,
+                      float* dk, float* dv, float* dq, float* dtheta, float* deta, float* dalpha, int batch,
+                      int heads, int n_tokens, tm_dtype dtype, tm_read read, void* ws, void* stream) {
+    tm_status rc = check_common(c, state, batch, heads, n_tokens, dtype, ws);
+    if (rc != TM_OK) return rc;
+    if (read != TM_READ_AFTER_WRITE && read != TM_READ_BEFORE_WRITE) return TM_ERR_INVALID;
+    if (!dstate || !aligned(dstate, 16)) return TM_ERR_INVALID;
+    if (n_tokens == 0) return TM_OK;   // the call is the identity on the state
+    if (!tok_ok(k) || !tok_ok(v) || !tok_ok(q) || !tok_ok(dy) || !tok_ok(dk) || !tok_ok(dv) || !tok_ok(dq) ||
+        !gate_ok(theta) || !gate_ok(eta) || !gate_ok(alpha) || !gate_ok(dtheta) || !gate_ok(deta) ||
+        !gate_ok(dalpha))
+        return TM_ERR_INVALID;
+    if (n_tokens % c->chunk != 0) return TM_ERR_SHAPE;
+    if (state_lookup(c, state, batch, heads) != TM_OK) return TM_ERR_STATE;
+    GraphEntry key = make_key(7, batch, heads, n_tokens, dtype,
+                              {state, k, v, q, theta, eta, alpha, dy, dstate, dk, dv, dq, dtheta, deta, dalpha, ws});
+    key.extra = (int)read;
+    return with_graph(c, key, static_cast<hipStream_t>(stream), [&](hipStream_t st) {
+        return run_bwd(c, state, k, v, q, theta, eta, alpha, dy, dstate, dk, dv, dq, dtheta, deta, dalpha, batch,
+                       heads, n_tokens, dtype, (int)read, ws, st);
+    });
 }
 
 tm_status tm_forward_noalloc(const tm_ctx* c, void* state, const void* k, const void* v, const void* q,

@@ -356,6 +356,112 @@ struct R3Args {
     int yt0;
 };
 
+// ---- the backward through the store (tm_bwd.hip) ----
+// Gradients of an outer loss through a call of tm_forward: a forward
+// recompute that keeps every chunk-start state (canonical fp32 row-major
+// layers, [c][stream][M_1..M_L, S_1..S_L]) and the key rows' activations,
+// then a reverse sweep over the chunks.  All arithmetic is fp32.
+//
+// One matrix operand: element (r, c) of stream s is at
+//   p + s * ss + r * ld + c                  (tok = 0, row-major fp32)
+//   p + tok_off(tl, s, t0 + r) + c           (tok = 1, token layout; bf16
+//                                             storage if bf, else fp32)
+struct BMat {
+    const void* p;
+    long ss, ld;
+    int tok, t0, bf;
+};
+// C[m][n] = sum_k A'[m][k] B'[k][n] per stream (blockIdx.z), with
+// A' = A^T (A stored [k][m]) if ta, B' = B^T (B stored [n][k]) if tb.
+//   dual 1: a second accumulator from B2 (same shape and transposition);
+//   dual 2: both accumulators from B, row k scaled by sk0[k] and sk1[k].
+// A second K segment (k2 > 0) adds sum_k A2'[m][k] B2s'[k][n] (same
+// transpositions) to the first accumulator.  The epilogue (BE_*) combines
+// the accumulators with the auxiliary operands x0, x1 into c0, c1.
+enum {
+    BE_STORE = 0,   // c0 = acc0
+    BE_ACC,         // c0 += acc0
+    BE_HID,         // c0 = z = acc0, c1 = SiLU(z)
+    BE_OUTK,        // c0 = z = acc0, c1 = 2 (z - x0)
+    BE_BWDK,        // c0 = g = acc0, c1 = g * SiLU'(x0)
+    BE_QB,          // c0 = acc0 * SiLU'(x0)
+    BE_ADDSTORE,    // c0 = acc0 + x0
+    BE_HB,          // c1 += (acc0 + x0) * SiLU'(x1)
+    BE_GP,          // c0 = -(rs0[r] acc0 + rs1[r] acc1); row partials of acc0 . x0, acc1 . x0
+    BE_GQ,          // c0 = -(rs0[r] acc0 + rs1[r] acc1)
+    BE_UPD,         // c0 = pa x0 + s0 x1 - acc0, c1 = pe x1 - acc1 (chunk scalars cs)
+    BE_ADJ          // c0 = pa c0 + acc0, c1 = pe c1 + s0 c0 (old values); tile partials of
+                    // <c0, x0>, <c1, x1>, <c0, x1> (old c0, c1)
+};
+struct BGemm {
+    int m, n, k, k2;
+    int ta, tb, dual, epi;
+    TokLayout tl;
+    BMat A, B, B2, A2, Bs2;
+    BMat c0, c1, x0, x1;
+    const float* sk0;         // dual 2: per-k scales (sk0 + s * sk_ss + k)
+    const float* sk1;
+    long sk_ss;
+    const float* rs0;         // BE_GP, BE_GQ: per-row scales (rs0 + s * sk_ss + r)
+    const float* rs1;
+    const float* cs;          // chunk scalars of the stream: cs + s * cs_ss (pa, pe, s0)
+    long cs_ss;
+    float* part;              // BE_GP: [s][nt_part][2][64] at part + s * part_ss + (tile0 + bx) * 128
+    long part_ss;             // BE_ADJ: [s][nt_part][3] at part + s * part_ss + (tile0 + tile) * 3
+    int tile0;
+};
+hipError_t launch_bgemm(const BGemm& g, int ns, hipStream_t st);
+
+// Element-wise steps of the reverse sweep over one chunk's b rows of width n
+// (row-major [b][n]):
+//   BW_U  : u = db * SiLU'(z), zb = db * g * SiLU''(z)
+//   BW_OUT: zb = 2 db, dv (token layout) = -2 db
+enum { BW_U = 0, BW_OUT = 1 };
+struct BElem {
+    int mode, b, n;
+    const float* db;          // db, u, zb: per-stream stride ss
+    const float* z;           // z, g: per-stream stride rss
+    const float* g;
+    float* u;
+    float* zb;
+    long ss, rss;
+    float* dv;                // BW_OUT: token layout tl, tokens t0 ..
+    TokLayout tl;
+    int t0;
+};
+hipError_t launch_belem(const BElem& e, int ns, hipStream_t st);
+
+// Per (stream, chunk): the chunk's coefficients from its gates (BC_FWD):
+//   A_i = prod_{j>i} (1 - alpha_j), E_i = prod_{j>i} eta_j,
+//   r_i = A_i + eta_{i+1} r_{i+1} (r_{b-1} = 1),
+//   c_i = theta_i r_i, d_i = theta_i E_i, (p_alpha, p_eta, s0) =
+//   ((1 - alpha_0) A_0, eta_0 E_0, eta_0 r_0);
+// or (BC_BWD) the adjoint of those definitions: from the partial sums of
+// cbar_i = -<Mbar_end, G_i>, dbar_i = -<Sbar_end, G_i>, pbar_alpha =
+// <Mbar_end, M_0>, pbar_eta = <Sbar_end, S_0>, s0bar = <Mbar_end, S_0> to
+// the gradients of theta, eta, alpha.
+enum { BC_FWD = 0, BC_BWD = 1 };
+struct BCoef {
+    int mode, b, C;
+    const float* theta;
+    const float* eta;
+    const float* alpha;
+    TokLayout gl;             // gates: d = 1
+    float* cc;                // [s][T]
+    float* dc;
+    long coef_ss;
+    float* cs;                // [s][C][4]
+    long cs_ss;
+    const float* pgp;         // BC_BWD: row partials [s][c][ngp][2][64]
+    int ngp;
+    const float* pad;         // BC_BWD: tile partials [s][c][nad][3]
+    int nad;
+    float* dtheta;            // BC_BWD: gradients, gate layout
+    float* deta;
+    float* dalpha;
+};
+hipError_t launch_bcoef(const BCoef& a, int ns, hipStream_t st);
+
 // ---- launchers (tm_r3.hip) ----
 hipError_t launch_r3_score(const R3Args& r, int ns, int nchunks, int f32, hipStream_t st);
 hipError_t launch_r3_layer(const R3Args& r, int ns, int f32, hipStream_t st);

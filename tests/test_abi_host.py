@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     syms = declared_symbols()
-    assert len(syms) == 23
+    assert len(syms) == 25
     assert set(syms) == set(T.EXPORTED)
     L = ctypes.CDLL(T.LIB_PATH)
     for s in syms:
@@ -173,3 +173,21 @@ def test_binding_checks_dtypes_and_shapes():
         T.tm_store(None, None, k.half(), k.half(), g, g, g, None)
     with pytest.raises(TypeError, match="init_weights"):
         T.tm_state_init(None, None, 1, 2, torch.zeros((2, 10), dtype=f64))
+
+
+def test_backward_validation_before_launch():
+    L = T.lib()
+    c = T.tm_create(64, 2, 2, 16)
+    A = ctypes.c_void_p(1 << 20)
+    G = ctypes.c_void_p((1 << 20) + 4096)
+    st = ctypes.c_void_p(None)
+    args = lambda n, read, dstate=A: (c, A, A, A, A, G, G, G, A, dstate, A, A, A, G, G, G, 1, 1, n, T.TM_F32, read,
+                                      A, st)
+    assert L.tm_backward(*args(16, T.TM_READ_PER_TOKEN)) == T.TM_ERR_INVALID
+    assert L.tm_backward(*args(16, 5)) == T.TM_ERR_INVALID
+    assert L.tm_backward(*args(16, T.TM_READ_AFTER_WRITE, None)) == T.TM_ERR_INVALID
+    assert L.tm_backward(*args(17, T.TM_READ_AFTER_WRITE)) == T.TM_ERR_SHAPE
+    assert L.tm_backward(*args(16, T.TM_READ_BEFORE_WRITE)) == T.TM_ERR_STATE   # never set up
+    assert L.tm_backward(*args(0, T.TM_READ_AFTER_WRITE)) == T.TM_OK             # the identity
+    assert T.tm_backward_workspace_bytes(c, 2, 1, 64) > T.tm_backward_workspace_bytes(c, 2, 1, 32) > 0
+    T.tm_destroy(c)
