@@ -157,6 +157,20 @@ def read_traffic(kernel, workload):
     return float(t.group(1))
 
 
+def host_info():
+    """The host the CPU baselines ran on: logical CPUs and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
 def cpu_baseline(wl, params, ci, min_seconds=10.0):
     """The fp64 oracle on a bounded sample of the same workload: the whole
     step (store + retrieve of every stream's tokens from the initial state),
@@ -179,10 +193,20 @@ def cpu_baseline(wl, params, ci, min_seconds=10.0):
             break
     return {"value": reps * wl.batch * tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%s: %d x the whole step (%d streams x %d tokens, store + retrieve from the initial "
-                      "state), fp64 C oracle, one thread per stream, %.1f s" % (wl.name, reps, streams, tokens, dt)}
+                      "state), fp64 C oracle, one thread per stream, %.1f s" % (wl.name, reps, streams, tokens, dt),
+            "host": host_info()}
 
 
-def other_workload(name, steps, calls=None, read=None, oracle=False):
+def scan_bytes(wl, ns, T):
+    """Bytes of the coefficient scan over a call of T tokens: the three gates
+    read and c, d written (20 B per token), the chunk scalars (16 B per
+    chunk), the keys and queries read once (2 d e) and written packed (rows
+    of both and the keys transposed, 3 d e), per stream."""
+    e = 2 if wl.dtype == "bf16" else 4
+    return ns * (T * (20 + 5 * wl.dim * e) + (T // wl.chunk) * 16)
+
+
+def other_workload(name, steps, calls=None, read=None, oracle=False, kernel_roof=False):
     """Throughput of another workload (tokens/s): state init + its calls in
     order, inputs resident in HBM, graph replay (each call's buffers repeat
     across steps).  calls: how many of the workload's calls to run (a prefix
@@ -229,6 +253,25 @@ def other_workload(name, steps, calls=None, read=None, oracle=False):
            "step": "tm_state_init + %d %s calls of (%d, %d) tokens, %d heads" % (
                n_calls, "tm_forward" if read is None else "tm_forward_ex(read=%d)" % read, Bn, Tn, H),
            "sample": "whole workload" if n_calls == wl.calls else "first %d of %d calls" % (n_calls, wl.calls)}
+    if kernel_roof:
+        # the coefficient scan and the chunk-step kernel, event-timed in a
+        # second pass: their HBM rooflines at this workload's scale
+        T.tm_timing_enable((1 << T.K_SCAN) | (1 << T.K_FIRST))
+        T.tm_timing_read(T.K_SCAN)
+        T.tm_timing_read(T.K_FIRST)
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        T.tm_timing_enable(0)
+        kin = {}
+        for nm, cls, kern, amount in (
+                ("scan", T.K_SCAN, "scan_kernel", scan_bytes(wl, Bn * H, Tn) * n_calls),
+                ("first", T.K_FIRST, "first_layer_kernel", sum(first_layer_launches(wl, Bn * H, Tn)) * n_calls)):
+            ms, n = T.tm_timing_read(cls)
+            gbs = amount * steps / (ms / 1e3) / 1e9
+            kin[nm] = {"kernel": kern, "launches_per_step": n / steps, "us_per_launch": ms * 1e3 / max(n, 1),
+                       "bytes_per_launch": amount * steps / max(n, 1), "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+        out["kernels"] = kin
     if read == T.TM_READ_PER_TOKEN:
         # the read's own launches, event-timed in a second pass
         T.tm_timing_enable(1 << T.K_TOKEN_READ)
@@ -253,7 +296,136 @@ def other_workload(name, steps, calls=None, read=None, oracle=False):
         odt = time.perf_counter() - t1
         out["cpu_baseline"] = {"value": Bn * Tn / odt, "unit": "tokens/s", "cores": nt, "kind": "oracle",
                                "sample": "%s: one call (%d streams x %d tokens) from the initial state, fp64 C "
-                                         "oracle, %.1f s" % (wl.name, Bn * H, Tn, odt)}
+                                         "oracle, %.1f s" % (wl.name, Bn * H, Tn, odt), "host": host_info()}
+    return out
+
+
+def backward_bytes(wl, ns, T):
+    """Bytes of tm_backward's state-streaming launches over a call of T
+    tokens, per layer and chunk: the recompute's write (M_0, S_0 read, M_end,
+    S_end written: 16 B per weight; the key rows' layer input, Delta and the
+    coefficients read) and the adjoint update (Mbar, Sbar read and written,
+    M_0, S_0 read: 24 B per weight; the products' operands read)."""
+    b = wl.chunk
+    e = 2 if wl.dtype == "bf16" else 4
+    per = 0
+    for l, (din, dout) in enumerate(wl.layer_dims()):
+        eh = e if l == 0 else 4
+        per += 16 * din * dout + b * din * eh + b * dout * 4 + 8 * b
+        per += 24 * din * dout + b * din * eh + b * dout * 4 + (8 * b * (din + dout) // 2 if l >= 1 else 0)
+    return ns * (T // b) * per
+
+
+def backward_flops(wl, ns, T):
+    """Flops of tm_backward's other products over a call of T tokens (per
+    chunk and stream: the key rows' forward and backward, the queries'
+    forward, backprop and weight gradient, the surprise's adjoint (two
+    accumulators, both directions), back through the key rows' backward and
+    forward)."""
+    b = wl.chunk
+    P = wl.params
+    dims = wl.layer_dims()
+    P0, PL = dims[0][0] * dims[0][1], dims[-1][0] * dims[-1][1]
+    per = 2 * b * (P + (P - P0) + (P - PL) + P + P + 2 * P + 2 * P + (P - P0) + P)
+    return ns * (T // b) * per
+
+
+def backward_line(name, steps, oracle=False):
+    """tm_backward over the workload's first call (the gradient of a random
+    outer loss on y; no gradient on the state after the call), inputs
+    resident in HBM, graph replay; tokens/s, the dominant class's roofline,
+    and the backward oracle on a bounded sample."""
+    import numpy as np
+    import torch
+    import test_trained_neural_amd as T
+    from test_trained_neural_amd import inputs as I
+    wl = I.WORKLOADS[name]
+    Bn, Tn, H, d = wl.batch, wl.tokens_per_call, wl.heads, wl.dim
+    ns = Bn * H
+    params = I.make_params(wl, 0)
+    ci = I.make_call(wl, params, 0, 0)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    k, v, q = (torch.from_numpy(x).to(dev).to(tdt) for x in (ci.k, ci.v, ci.q))
+    th, et, al = (torch.from_numpy(x).to(dev) for x in (ci.theta, ci.eta, ci.alpha))
+    dy_np = np.random.default_rng(11).standard_normal(ci.k.shape).astype(np.float32)
+    dy = torch.from_numpy(dy_np).to(dev)
+    ctx = T.tm_create(d, wl.depth, wl.expansion, wl.chunk)
+    state = torch.empty(T.tm_state_bytes(ctx, Bn, H), dtype=torch.uint8, device=dev)
+    T.tm_state_init(ctx, state, Bn, H, torch.from_numpy(params.init_weights).to(dev))
+    ws = torch.empty(T.tm_backward_workspace_bytes(ctx, Bn, H, Tn), dtype=torch.uint8, device=dev)
+    dstate = torch.zeros((ns, 2 * wl.params), dtype=torch.float32, device=dev)
+    dk, dv, dq = (torch.empty((Bn, Tn, H, d), dtype=torch.float32, device=dev) for _ in range(3))
+    dth, det, dal = (torch.empty((Bn, Tn, H), dtype=torch.float32, device=dev) for _ in range(3))
+
+    def step():
+        dstate.zero_()
+        T.tm_backward(ctx, state, k, v, q, th, et, al, dy, dstate, dk, dv, dq, dth, det, dal, ws)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    out = {"tokens_per_s": Bn * Tn / dt, "ms_per_step": dt * 1e3, "steps": steps,
+           "step": "tm_backward of one tm_forward call of (%d, %d) tokens from the initial state (dstate "
+                   "cleared first): recompute with every chunk-start state kept, reverse sweep, gate gradients"
+                   % (Bn, Tn)}
+    T.tm_timing_enable((1 << T.K_BACKWARD_STATE) | (1 << T.K_BACKWARD_REST))
+    T.tm_timing_read(T.K_BACKWARD_STATE)
+    T.tm_timing_read(T.K_BACKWARD_REST)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    T.tm_timing_enable(0)
+    ms_s, n_s = T.tm_timing_read(T.K_BACKWARD_STATE)
+    ms_r, n_r = T.tm_timing_read(T.K_BACKWARD_REST)
+    by = backward_bytes(wl, ns, Tn) * steps
+    fl = backward_flops(wl, ns, Tn) * steps
+    gbs = by / (ms_s / 1e3) / 1e9
+    tfl = fl / (ms_r / 1e3) / 1e12
+    out["kernels"] = {
+        "state_streaming": {"kernel": "bgemm_kernel (the write and adjoint-update epilogues)",
+                            "launches_per_step": n_s / steps, "ms_per_step": ms_s / steps,
+                            "us_per_launch": ms_s * 1e3 / max(n_s, 1), "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS},
+        "products_and_rest": {"kernel": "bgemm_kernel (other epilogues), belem_kernel, bcoef_kernel, export_kernel",
+                              "launches_per_step": n_r / steps, "ms_per_step": ms_r / steps,
+                              "us_per_launch": ms_r * 1e3 / max(n_r, 1), "tflops": tfl,
+                              "fp32_frac": tfl / FP32_PEAK_TFLOPS},
+    }
+    if ms_s >= ms_r:
+        out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": gbs / HBM_PEAK_GBS, "kernel": "bgemm_kernel (state streaming)",
+                           "launches": n_s, "avg_us": ms_s * 1e3 / max(n_s, 1), "bytes_per_launch": by / max(n_s, 1)}
+    else:
+        out["roofline"] = {"bound": "alu", "achieved": tfl, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tfl / FP32_PEAK_TFLOPS, "kernel": "bgemm_kernel (products, fp32 FMA)",
+                           "launches": n_r, "avg_us": ms_r * 1e3 / max(n_r, 1), "flops_per_launch": fl / max(n_r, 1)}
+    out["roofline"]["timing"] = "HIP events recorded with each launch's own dispatch, second pass of the same steps"
+    T.tm_destroy(ctx)
+    if oracle:
+        # the backward oracle on one stream's first 128 tokens, repeated for
+        # at least 10 s
+        import torch as _t
+        from oracle import backward as BW
+        n = min(128, Tn)
+        sub = lambda a: np.ascontiguousarray(a[:1, :n, :1])
+        st = I.initial_state(wl, params, batch=1)[:1]
+        reps, t1 = 0, time.perf_counter()
+        while True:
+            BW.forward_backward(wl.dim, wl.depth, wl.expansion, wl.chunk, st, sub(ci.k), sub(ci.v), sub(ci.q),
+                                sub(ci.theta), sub(ci.eta), sub(ci.alpha), sub(dy_np))
+            reps += 1
+            odt = time.perf_counter() - t1
+            if odt >= 10.0:
+                break
+        out["cpu_baseline"] = {"value": reps * n / odt, "unit": "tokens/s", "cores": _t.get_num_threads(),
+                               "kind": "oracle", "host": host_info(),
+                               "sample": "%s backward: %d x one stream's first %d tokens (float64 autograd through "
+                                         "the literal recurrence, PyTorch CPU), %.1f s" % (wl.name, reps, n, odt)}
     return out
 
 
@@ -300,7 +472,8 @@ def retrieval(name, steps, oracle=False):
     flops = 2 * Bn * H * Tn * sum(a * b for a, b in wl.layer_dims()) * steps
     out = {"tokens_per_s": Bn * Tn / dt, "ms_per_step": dt * 1e3, "steps": steps,
            "step": "tm_retrieve of (%d, %d) queries through the memory after storing them" % (Bn, Tn),
-           "roofline": mfma_roofline(flops, ms, n, wl.dtype, "gemm_kernel")}
+           "roofline": mfma_roofline(flops, ms, n, wl.dtype,
+                                     "rows_kernel" if wl.dtype == "bf16" and min(Tn, 2048) >= 256 else "gemm_kernel")}
     T.tm_destroy(ctx)
     if oracle:
         from oracle import tmref
@@ -312,7 +485,7 @@ def retrieval(name, steps, oracle=False):
         odt = time.perf_counter() - t1
         out["cpu_baseline"] = {"value": Bn * Tn / odt, "unit": "tokens/s", "cores": nt, "kind": "oracle",
                                "sample": "%s: retrieve of one call's queries (%d streams x %d tokens), fp64 C "
-                                         "oracle, %.2f s" % (wl.name, Bn * H, Tn, odt)}
+                                         "oracle, %.2f s" % (wl.name, Bn * H, Tn, odt), "host": host_info()}
     return out
 
 
@@ -383,7 +556,7 @@ def input_side(name, steps, oracle=False):
         out["input_side"]["cpu_baseline"] = {
             "value": Bn * Tn / odt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": "%s input side: one call (%d x %d tokens of width %d), fp64 numpy oracle, %.2f s" % (
-                wl.name, Bn, Tn, wl.model_dim, odt)}
+                wl.name, Bn, Tn, wl.model_dim, odt), "host": host_info()}
     out["input_side"]["step"] = "tm_project of (%d, %d) tokens of width %d, 4-tap convolution" % (Bn, Tn, wl.model_dim)
     out["from_tokens"]["step"] = "tm_project + tm_state_init + tm_forward of (%d, %d) tokens" % (Bn, Tn)
     T.tm_destroy(ctx)
@@ -442,6 +615,38 @@ def mac_wiring(name, steps, seg=128, n_persist=4, oracle=False):
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
     out = {"tokens_per_s": Bn * Tn / dt, "ms_per_step": dt * 1e3, "steps": steps}
+    # every kernel class of the step, event-timed in a second pass (direct
+    # launches): where a step's time goes, and what the launches leave to
+    # the host (the ctypes calls and launch gaps)
+    cls = {"project_kernel": T.K_PROJECT, "scan_kernel": T.K_SCAN, "first_layer_kernel": T.K_FIRST,
+           "gemm_kernel": T.K_FWD, "mac_window/gate_kernel": T.K_MAC}
+    T.tm_timing_enable(sum(1 << c for c in cls.values()))
+    for c in cls.values():
+        T.tm_timing_read(c)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    T.tm_timing_enable(0)
+    brk = {}
+    for nm, c in cls.items():
+        ms, n = T.tm_timing_read(c)
+        brk[nm] = {"ms_per_step": ms / steps, "launches_per_step": n / steps, "us_per_launch": ms * 1e3 / max(n, 1)}
+    kern_ms = sum(v["ms_per_step"] for v in brk.values())
+    out["kernels"] = brk
+    out["host_share"] = {"kernel_ms_per_step": kern_ms, "step_ms": dt * 1e3,
+                         "host_frac": max(0.0, 1.0 - kern_ms / (dt * 1e3)),
+                         "note": "1 - (summed event-timed kernel time) / (graph-replay step time)"}
+    dom = max(brk, key=lambda nm: brk[nm]["ms_per_step"])
+    nseg = Tn // S
+    if dom == "project_kernel":
+        flops = project_flops(wl, Bn, S) * 2 * nseg * steps
+        out["roofline"] = mfma_roofline(flops, brk[dom]["ms_per_step"] * steps, brk[dom]["launches_per_step"] * steps,
+                                        wl.dtype, dom)
+    elif dom == "gemm_kernel":
+        Pw = wl.params
+        flops = (2 * 2 * Bn * H * S * Pw + 2 * Bn * H * S * sum(a * b for a, b in wl.layer_dims()[1:])) * nseg * steps
+        out["roofline"] = mfma_roofline(flops, brk[dom]["ms_per_step"] * steps, brk[dom]["launches_per_step"] * steps,
+                                        wl.dtype, dom)
     # the window kernel alone, event-timed
     rec = torch.randn((Bn, S, D), dtype=torch.float32, device=dev)
     win = torch.empty((Bn, P + 2 * S, D), dtype=tdt, device=dev)
@@ -456,10 +661,12 @@ def mac_wiring(name, steps, seg=128, n_persist=4, oracle=False):
     es = 2 if wl.dtype == "bf16" else 4
     per_launch = Bn * S * D * 4 + Bn * S * D * es + P * D * es + Bn * (P + 2 * S) * D * es
     achieved = per_launch * n / (ms / 1e3) / 1e9
-    out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "mac_window_kernel",
-                       "launches": n, "avg_us": ms * 1e3 / max(n, 1), "bytes_per_launch": per_launch,
-                       "timing": "HIP events recorded with each launch's own dispatch"}
+    win_roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "mac_window_kernel",
+                "launches": n, "avg_us": ms * 1e3 / max(n, 1), "bytes_per_launch": per_launch,
+                "timing": "HIP events recorded with each launch's own dispatch"}
+    out["window_kernel"] = win_roof
+    out.setdefault("roofline", win_roof)
     if oracle:
         from threadpoolctl import threadpool_limits
         from oracle import mac, prologue, tmref
@@ -480,7 +687,8 @@ def mac_wiring(name, steps, seg=128, n_persist=4, oracle=False):
         out["cpu_baseline"] = {
             "value": Bn * S / odt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": "%s memory-as-context wiring: the first segment (%d x %d tokens), fp64 oracles "
-                      "(input side, memory, wiring), one thread, %.2f s" % (wl.name, Bn, S, odt)}
+                      "(input side, memory, wiring), one thread, %.2f s" % (wl.name, Bn, S, odt),
+            "host": host_info()}
     out["step"] = ("%d segments of %d tokens x %d streams, %d persistent tokens: tm_project, tm_retrieve, "
                    "tm_mac_window, pass-through attention, tm_project, tm_store, tm_retrieve, tm_mac_gate"
                    % (Tn // S, S, Bn, P))
@@ -656,7 +864,7 @@ def main():
         # the headline value is the workload above)
         out["other_workloads"] = {
             "mlp384_stream": other_workload("mlp384_stream", 3),
-            "multihead1024": other_workload("multihead1024", 3),
+            "multihead1024": other_workload("multihead1024", 3, kernel_roof=True),
             "deep512": other_workload("deep512", 2, calls=16),
             # the same step with each chunk's queries read before its write
             "mlp384_read_before_write": other_workload("mlp384", 20, read=1, oracle=not args.no_cpu_baseline),
@@ -664,6 +872,10 @@ def main():
             "mlp384_read_per_token": other_workload("mlp384", 20, read=2, oracle=not args.no_cpu_baseline),
             # read-only retrieval of the call's queries through the stored memory
             "mlp384_retrieve": retrieval("mlp384", 20, oracle=not args.no_cpu_baseline),
+            # ... and at the multi-head workload's scale (64 streams x 32768 queries)
+            "multihead1024_retrieve": retrieval("multihead1024", 3),
+            # the backward through the store (gradients through one tm_forward call)
+            "mlp384_backward": backward_line("mlp384", 10, oracle=not args.no_cpu_baseline),
         }
         side = input_side("mlp384", 20, oracle=not args.no_cpu_baseline)
         out["other_workloads"]["mlp384_input_side"] = side["input_side"]

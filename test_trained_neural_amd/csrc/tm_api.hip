@@ -937,7 +937,7 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
 // record from the recompute, the reverse sweep's per-stream scratch, and
 // the partial sums behind the gates' gradients.  Sizes in 4-byte elements.
 struct BwdLayout {
-    size_t tape, cc, dc, cs, key, scr, pgp, pad, total;
+    size_t tape, cc, dc, cs, key, scr, pgp, pad, acc, total;
     long tape_cs;               // elements per chunk slot (ns * 2P)
     long rec;                   // elements of one (stream, chunk) key record
     long hk[MAXL], zk[MAXL], dk[MAXL], gk[MAXL];   // offsets inside a record
@@ -990,6 +990,18 @@ BwdLayout bwd_layout(const tm_ctx* c, long ns, long T) {
     }
     w.pgp = o; o += al256((size_t)ns * C * w.ngp * 128 * 4);
     w.pad = o; o += al256((size_t)ns * C * w.nad * 3 * 4);
+    // split-K partial tiles of the largest split product (b rows by a layer
+    // width, either direction; the queries' weight gradient, K = b)
+    long acc = 0;
+    for (int l = 0; l < c->L; ++l) {
+        const int di = c->din[l], dn = c->dout[l];
+        const int shapes[3][3] = {{(int)b, dn, di}, {(int)b, di, dn}, {di, dn, (int)b}};
+        for (const auto& sh : shapes) {
+            const long f = bgemm_acc_floats(sh[0], sh[1], (int)ns, bgemm_splitk(sh[0], sh[1], sh[2], 0, BE_STORE, (int)ns));
+            acc = f > acc ? f : acc;
+        }
+    }
+    w.acc = o; o += al256((size_t)acc * 4);
     w.total = o > 0 ? o : 256;
     return w;
 }
@@ -1037,7 +1049,10 @@ tm_status run_bwd(const tm_ctx* c, const void* state, const void* k, const void*
                 "reverse sweep about 9L = %d per chunk; workspace %zu bytes\n",
                 C, b, ns, 3 * L - 1, 9 * L, w.total * 1);
 
-    auto gemm = [&](const BGemm& g, int kind) -> bool {
+    float* accbuf = reinterpret_cast<float*>(ws + w.acc);
+    auto gemm = [&](BGemm g, int kind) -> bool {
+        g.splitk = bgemm_splitk(g.m, g.n, g.k, g.k2, g.epi, (int)ns);
+        g.acc = accbuf;
         return timed(kind, st, [&] { return launch_bgemm(g, (int)ns, st); }) == hipSuccess;
     };
     auto base = [&](int m, int n, int kk, int ta, int tb, int epi) {

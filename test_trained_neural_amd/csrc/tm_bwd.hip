@@ -26,6 +26,8 @@ namespace {
 constexpr int BT = 64;    // output tile: BT x BT, 256 threads of 4 x 4
 constexpr int BKS = 16;   // K per LDS stage
 constexpr int BPAD = 4;
+constexpr int NST = 4;    // K steps whose loads are in flight together
+constexpr int MAXSPLIT = 8;   // most K slices of a split product
 
 __device__ __forceinline__ float silu_d(float z) {
     const float s = sigmoid(z);
@@ -40,89 +42,210 @@ __device__ __forceinline__ float silu_dd(float z) {
 __device__ __forceinline__ long moff(const BMat& M, const TokLayout& tl, int s, int r, int c) {
     return M.tok ? tok_off(tl, s, M.t0 + r) + c : (long)s * M.ss + (long)r * M.ld + c;
 }
-__device__ __forceinline__ float mload(const BMat& M, const TokLayout& tl, int s, int r, int c) {
-    const long o = moff(M, tl, s, r, c);
-    return M.bf ? (float)reinterpret_cast<const bf16*>(M.p)[o] : reinterpret_cast<const float*>(M.p)[o];
-}
 __device__ __forceinline__ float* mptr(const BMat& M, const TokLayout& tl, int s, int r, int c) {
     return const_cast<float*>(reinterpret_cast<const float*>(M.p)) + moff(M, tl, s, r, c);
 }
+// 4 consecutive elements of a row (every contiguous dimension here is a
+// multiple of 32, so a group of 4 is in bounds as a whole)
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 ld4(const BMat& M, const TokLayout& tl, int s, int r, int c) {
+    const long o = moff(M, tl, s, r, c);
+    if (M.bf) {
+        const bf16x4 v = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(M.p) + o);
+        return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    }
+    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(M.p) + o);
+}
+__device__ __forceinline__ void st4(const BMat& M, const TokLayout& tl, int s, int r, int c, f32x4 v) {
+    *reinterpret_cast<f32x4*>(mptr(M, tl, s, r, c)) = v;
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-__global__ __launch_bounds__(256) void bgemm_kernel(BGemm g) {
-    __shared__ float As[BKS][BT + BPAD];
-    __shared__ float Bs[2][BKS][BT + BPAD];
-    __shared__ float red[4][3];
-    const int s = blockIdx.z;
-    const int n0 = blockIdx.x * BT, m0 = blockIdx.y * BT;
-    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    float acc0[4][4], acc1[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc0[i][j] = acc1[i][j] = 0.f;
-
-    const int nseg = g.k2 > 0 ? 2 : 1;
-    for (int seg = 0; seg < nseg; ++seg) {
-        const BMat& A = seg ? g.A2 : g.A;
-        const BMat& B = seg ? g.Bs2 : g.B;
-        const int K = seg ? g.k2 : g.k;
-        const bool two = seg == 0 && g.dual != 0;
-        for (int k0 = 0; k0 < K; k0 += BKS) {
-            for (int e = tid; e < BT * BKS; e += 256) {
-                int mm, kk;
-                if (g.ta) { mm = e & (BT - 1); kk = e / BT; }       // A stored [k][m]: m contiguous
-                else { kk = e & (BKS - 1); mm = e / BKS; }          // A stored [m][k]: k contiguous
-                const int gm = m0 + mm, gk = k0 + kk;
-                float v = 0.f;
-                if (gm < g.m && gk < K) v = g.ta ? mload(A, g.tl, s, gk, gm) : mload(A, g.tl, s, gm, gk);
-                As[kk][mm] = v;
+// Register stage of one K step: A's and B's (and B2's) float4 for this
+// thread.  TA = 0: A stored [m][k] (thread: row t/4, k quad t%4); TA = 1:
+// A stored [k][m] (k row t/16, m quad t%16); likewise TB for B.
+template <int TA, int TB>
+struct Stage {
+    f32x4 a, b0, b1;
+    __device__ __forceinline__ void load(const BGemm& g, const BMat& A, const BMat& B, bool second, int s, int m0,
+                                         int n0, int k0, int ke) {
+        const int t = threadIdx.x;
+        if (TA == 0) {
+            const int gm = m0 + (t >> 2), gk = k0 + (t & 3) * 4;
+            a = gm < g.m && gk < ke ? ld4(A, g.tl, s, gm, gk) : zero4();
+        } else {
+            const int gk = k0 + (t >> 4), gm = m0 + (t & 15) * 4;
+            a = gk < ke && gm < g.m ? ld4(A, g.tl, s, gk, gm) : zero4();
+        }
+        const bool two = !second && g.dual != 0;
+        if (TB == 0) {
+            const int gk = k0 + (t >> 4), gn = n0 + (t & 15) * 4;
+            const bool ok = gk < ke && gn < g.n;
+            b0 = ok ? ld4(B, g.tl, s, gk, gn) : zero4();
+            b1 = zero4();
+            if (two && ok) {
+                if (g.dual == 1) {
+                    b1 = ld4(g.B2, g.tl, s, gk, gn);
+                } else {
+                    const float c0 = g.sk0[(long)s * g.sk_ss + gk], c1 = g.sk1[(long)s * g.sk_ss + gk];
+                    b1 = b0 * c1;
+                    b0 = b0 * c0;
+                }
             }
-            for (int e = tid; e < BT * BKS; e += 256) {
-                int nn, kk;
-                if (g.tb) { kk = e & (BKS - 1); nn = e / BKS; }     // B stored [n][k]
-                else { nn = e & (BT - 1); kk = e / BT; }            // B stored [k][n]
-                const int gn = n0 + nn, gk = k0 + kk;
-                float v = 0.f, v2 = 0.f;
-                if (gn < g.n && gk < K) {
-                    v = g.tb ? mload(B, g.tl, s, gn, gk) : mload(B, g.tl, s, gk, gn);
-                    if (seg == 0 && g.dual == 1)
-                        v2 = g.tb ? mload(g.B2, g.tl, s, gn, gk) : mload(g.B2, g.tl, s, gk, gn);
-                    if (seg == 0 && g.dual == 2) {
-                        v2 = v * g.sk1[(long)s * g.sk_ss + gk];
-                        v *= g.sk0[(long)s * g.sk_ss + gk];
+        } else {
+            const int gn = n0 + (t >> 2), gk = k0 + (t & 3) * 4;
+            const bool ok = gn < g.n && gk < ke;
+            b0 = ok ? ld4(B, g.tl, s, gn, gk) : zero4();
+            b1 = zero4();
+            if (two && ok) {
+                if (g.dual == 1) {
+                    b1 = ld4(g.B2, g.tl, s, gn, gk);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float c0 = g.sk0[(long)s * g.sk_ss + gk + j], c1 = g.sk1[(long)s * g.sk_ss + gk + j];
+                        b1[j] = b0[j] * c1;
+                        b0[j] = b0[j] * c0;
                     }
                 }
-                Bs[0][kk][nn] = v;
-                Bs[1][kk][nn] = v2;
             }
-            __syncthreads();
-#pragma unroll 4
-            for (int kk = 0; kk < BKS; ++kk) {
-                float a[4], b0[4];
+        }
+    }
+    __device__ __forceinline__ void store(float (*As)[BT + BPAD], float (*Bs0)[BT + BPAD], float (*Bs1)[BT + BPAD],
+                                          bool two) {
+        const int t = threadIdx.x;
+        if (TA == 0) {
+            const int mm = t >> 2, kq = (t & 3) * 4;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+            for (int j = 0; j < 4; ++j) As[kq + j][mm] = a[j];
+        } else {
+            *reinterpret_cast<f32x4*>(&As[t >> 4][(t & 15) * 4]) = a;
+        }
+        if (TB == 0) {
+            *reinterpret_cast<f32x4*>(&Bs0[t >> 4][(t & 15) * 4]) = b0;
+            if (two) *reinterpret_cast<f32x4*>(&Bs1[t >> 4][(t & 15) * 4]) = b1;
+        } else {
+            const int nn = t >> 2, kq = (t & 3) * 4;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) b0[j] = Bs[0][kk][tx * 4 + j];
+            for (int j = 0; j < 4; ++j) Bs0[kq + j][nn] = b0[j];
+            if (two)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < 4; ++j) Bs1[kq + j][nn] = b1[j];
+        }
+    }
+};
+
+// phase 0: the whole product and the epilogue; phase 1: one K slice of a
+// split product (blockIdx.z = stream * splitk + slice), raw accumulators to
+// g.acc; phase 2: the slices summed in order, then the epilogue.
+// PRE (the state-streaming epilogues BE_UPD, BE_ADJ): the epilogue's state
+// operands are requested before the K loop, so their HBM reads overlap the
+// product instead of following it.
+template <int TA, int TB, bool PRE, int PHASE>
+__global__ __launch_bounds__(256) void bgemm_kernel(BGemm g) {
+    constexpr int phase = PHASE;
+    __shared__ __attribute__((aligned(16))) float As[BKS][BT + BPAD];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BKS][BT + BPAD];
+    __shared__ float red[4][3];
+    const int split = phase == 1 ? g.splitk : 1;
+    const int s = blockIdx.z / split, slice = blockIdx.z - s * split;
+    const int n0 = blockIdx.x * BT, m0 = blockIdx.y * BT;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const long tiles = (long)gridDim.x * gridDim.y, tile = (long)blockIdx.y * gridDim.x + blockIdx.x;
+    f32x4 acc0[4], acc1[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc0[i][j] = __builtin_fmaf(a[i], b0[j], acc0[i][j]);
-                if (two) {
-                    float b1[4];
+    for (int i = 0; i < 4; ++i) acc0[i] = acc1[i] = zero4();
+    // PRE: x0, x1 (and c0, c1 for the adjoint) of this thread's 4 x 4 block
+    f32x4 px0[4], px1[4], pc0[4], pc1[4];
+    if (PRE) {
+        const int rb = m0 + ty * 4, cb = n0 + tx * 4;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) b1[j] = Bs[1][kk][tx * 4 + j];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) acc1[i][j] = __builtin_fmaf(a[i], b1[j], acc1[i][j]);
-                }
-            }
-            __syncthreads();
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = rb + i < g.m && cb < g.n;
+            px0[i] = ok ? ld4(g.x0, g.tl, s, rb + i, cb) : zero4();
+            px1[i] = ok ? ld4(g.x1, g.tl, s, rb + i, cb) : zero4();
+            pc0[i] = ok && g.epi == BE_ADJ ? ld4(g.c0, g.tl, s, rb + i, cb) : zero4();
+            pc1[i] = ok && g.epi == BE_ADJ ? ld4(g.c1, g.tl, s, rb + i, cb) : zero4();
         }
     }
 
+    if constexpr (PHASE == 2) {
+        // the slices' partial tiles, summed in slice order; up to MAXSPLIT
+        // slices' loads are requested before the first sum
+        f32x4 p0[MAXSPLIT][4], p1[MAXSPLIT][4];
+#pragma unroll
+        for (int sl = 0; sl < MAXSPLIT; ++sl)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float* p = g.acc + ((long)(s * g.splitk + min(sl, g.splitk - 1)) * tiles + tile) * 8192 +
+                                 (ty * 4 + i) * 64 + tx * 4;
+                p0[sl][i] = sl < g.splitk ? *reinterpret_cast<const f32x4*>(p) : zero4();
+                p1[sl][i] = sl < g.splitk && g.dual ? *reinterpret_cast<const f32x4*>(p + 4096) : zero4();
+            }
+#pragma unroll
+        for (int sl = 0; sl < MAXSPLIT; ++sl)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc0[i] += p0[sl][i];
+                acc1[i] += p1[sl][i];
+            }
+    } else {
+        // one K segment: A'B' over [kb, ke) of K (the second segment, if
+        // any, takes A2, Bs2 and never the second accumulator)
+        auto segment = [&](const BMat A, const BMat B, int K, bool second) __attribute__((always_inline)) {
+            int kb = 0, ke = K;
+            if (phase == 1) {
+                const int len = ((K + split - 1) / split + BKS - 1) / BKS * BKS;
+                kb = slice * len;
+                ke = min(K, kb + len);
+            }
+            const bool two = !second && g.dual != 0;
+            // NST steps of K at a time: every load of the group is requested
+            // before the first step is consumed, so a group costs one memory
+            // round trip rather than one per step
+            Stage<TA, TB> st[NST];
+            for (int g0 = kb; g0 < ke; g0 += NST * BKS) {
+#pragma unroll
+                for (int i = 0; i < NST; ++i)
+                    if (g0 + i * BKS < ke) st[i].load(g, A, B, second, s, m0, n0, g0 + i * BKS, ke);
+#pragma unroll
+                for (int i = 0; i < NST; ++i) {
+                    if (g0 + i * BKS >= ke) continue;   // (uniform: the whole workgroup skips)
+                    st[i].store(As, Bs[0], Bs[1], two);
+                    __syncthreads();
+#pragma unroll 4
+                    for (int kk = 0; kk < BKS; ++kk) {
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(&As[kk][ty * 4]);
+                        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&Bs[0][kk][tx * 4]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc0[j] += a[j] * b0;
+                        if (two) {
+                            const f32x4 b1 = *reinterpret_cast<const f32x4*>(&Bs[1][kk][tx * 4]);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) acc1[j] += a[j] * b1;
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+        };
+        segment(g.A, g.B, g.k, false);
+        if (g.k2 > 0) segment(g.A2, g.Bs2, g.k2, true);
+        if constexpr (PHASE == 1) {
+            float* p = g.acc + ((long)(s * g.splitk + slice) * tiles + tile) * 8192;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                *reinterpret_cast<f32x4*>(p + (ty * 4 + i) * 64 + tx * 4) = acc0[i];
+                if (g.dual) *reinterpret_cast<f32x4*>(p + 4096 + (ty * 4 + i) * 64 + tx * 4) = acc1[i];
+            }
+            return;
+        }
+    }
+
+    // ---- epilogue: rows rb .. rb+3, columns cb .. cb+3 (all in bounds or all out)
     const TokLayout& tl = g.tl;
     const int rb = m0 + ty * 4, cb = n0 + tx * 4;
+    const bool colok = cb < g.n;
     if (g.epi == BE_GP) {
         // the tile holds rows 0 .. b-1 (m <= 64): each row's dot products of
         // the two accumulators with x0 over the tile's columns, reduced over
@@ -132,17 +255,17 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm g) {
         for (int i = 0; i < 4; ++i) {
             pc[i] = pd[i] = 0.f;
             const int r = rb + i;
-            if (r >= g.m) continue;
+            if (r >= g.m || !colok) continue;
             const float cr = g.rs0[(long)s * g.sk_ss + r], dr = g.rs1[(long)s * g.sk_ss + r];
+            const f32x4 x = ld4(g.x0, tl, s, r, cb);
+            f32x4 o;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int n = cb + j;
-                if (n >= g.n) continue;
-                const float x = mload(g.x0, tl, s, r, n);
-                pc[i] = __builtin_fmaf(acc0[i][j], x, pc[i]);
-                pd[i] = __builtin_fmaf(acc1[i][j], x, pd[i]);
-                *mptr(g.c0, tl, s, r, n) = -__builtin_fmaf(cr, acc0[i][j], dr * acc1[i][j]);
+                pc[i] = __builtin_fmaf(acc0[i][j], x[j], pc[i]);
+                pd[i] = __builtin_fmaf(acc1[i][j], x[j], pd[i]);
+                o[j] = -__builtin_fmaf(cr, acc0[i][j], dr * acc1[i][j]);
             }
+            st4(g.c0, tl, s, r, cb, o);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -168,21 +291,20 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rb + i;
-            if (r >= g.m) continue;
+            if (r >= g.m || !colok) continue;
+            const f32x4 mb = PRE ? pc0[i] : ld4(g.c0, tl, s, r, cb), sb = PRE ? pc1[i] : ld4(g.c1, tl, s, r, cb);
+            const f32x4 mv = PRE ? px0[i] : ld4(g.x0, tl, s, r, cb), sv = PRE ? px1[i] : ld4(g.x1, tl, s, r, cb);
+            f32x4 mo, so;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int n = cb + j;
-                if (n >= g.n) continue;
-                float* pm = mptr(g.c0, tl, s, r, n);
-                float* ps = mptr(g.c1, tl, s, r, n);
-                const float mb = *pm, sb = *ps;
-                const float mv = mload(g.x0, tl, s, r, n), sv = mload(g.x1, tl, s, r, n);
-                d0 = __builtin_fmaf(mb, mv, d0);
-                d1 = __builtin_fmaf(sb, sv, d1);
-                d2 = __builtin_fmaf(mb, sv, d2);
-                *pm = __builtin_fmaf(pa, mb, acc0[i][j]);
-                *ps = __builtin_fmaf(pe, sb, s0 * mb);
+                d0 = __builtin_fmaf(mb[j], mv[j], d0);
+                d1 = __builtin_fmaf(sb[j], sv[j], d1);
+                d2 = __builtin_fmaf(mb[j], sv[j], d2);
+                mo[j] = __builtin_fmaf(pa, mb[j], acc0[i][j]);
+                so[j] = __builtin_fmaf(pe, sb[j], s0 * mb[j]);
             }
+            st4(g.c0, tl, s, r, cb, mo);
+            st4(g.c1, tl, s, r, cb, so);
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -198,57 +320,78 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm g) {
         }
         __syncthreads();
         if (tid == 0) {
-            float* o = g.part + (long)s * g.part_ss + (long)(g.tile0 + blockIdx.y * gridDim.x + blockIdx.x) * 3;
+            float* o = g.part + (long)s * g.part_ss + (long)(g.tile0 + tile) * 3;
 #pragma unroll
             for (int q = 0; q < 3; ++q) o[q] = (red[0][q] + red[1][q]) + (red[2][q] + red[3][q]);
         }
         return;
     }
+    if (!colok) return;
     const float* cs = g.epi == BE_UPD ? g.cs + (long)s * g.cs_ss : nullptr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = rb + i;
         if (r >= g.m) continue;
-        float cr = 0.f, dr = 0.f;
-        if (g.epi == BE_GQ) {
-            cr = g.rs0[(long)s * g.sk_ss + r];
-            dr = g.rs1[(long)s * g.sk_ss + r];
-        }
+        const f32x4 a0 = acc0[i];
+        f32x4 o, o1;
+        switch (g.epi) {
+            case BE_STORE: st4(g.c0, tl, s, r, cb, a0); break;
+            case BE_ACC: st4(g.c0, tl, s, r, cb, ld4(g.c0, tl, s, r, cb) + a0); break;
+            case BE_HID:
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = cb + j;
-            if (n >= g.n) continue;
-            const float a0 = acc0[i][j];
-            switch (g.epi) {
-                case BE_STORE: *mptr(g.c0, tl, s, r, n) = a0; break;
-                case BE_ACC: *mptr(g.c0, tl, s, r, n) += a0; break;
-                case BE_HID:
-                    *mptr(g.c0, tl, s, r, n) = a0;
-                    *mptr(g.c1, tl, s, r, n) = a0 * sigmoid(a0);
-                    break;
-                case BE_OUTK:
-                    *mptr(g.c0, tl, s, r, n) = a0;
-                    *mptr(g.c1, tl, s, r, n) = 2.f * (a0 - mload(g.x0, tl, s, r, n));
-                    break;
-                case BE_BWDK:
-                    *mptr(g.c0, tl, s, r, n) = a0;
-                    *mptr(g.c1, tl, s, r, n) = a0 * silu_d(mload(g.x0, tl, s, r, n));
-                    break;
-                case BE_QB: *mptr(g.c0, tl, s, r, n) = a0 * silu_d(mload(g.x0, tl, s, r, n)); break;
-                case BE_ADDSTORE: *mptr(g.c0, tl, s, r, n) = a0 + mload(g.x0, tl, s, r, n); break;
-                case BE_HB:
-                    *mptr(g.c1, tl, s, r, n) +=
-                        (a0 + mload(g.x0, tl, s, r, n)) * silu_d(mload(g.x1, tl, s, r, n));
-                    break;
-                case BE_GQ: *mptr(g.c0, tl, s, r, n) = -__builtin_fmaf(cr, a0, dr * acc1[i][j]); break;
-                case BE_UPD: {
-                    const float mv = mload(g.x0, tl, s, r, n), sv = mload(g.x1, tl, s, r, n);
-                    *mptr(g.c0, tl, s, r, n) = __builtin_fmaf(cs[0], mv, __builtin_fmaf(cs[2], sv, -a0));
-                    *mptr(g.c1, tl, s, r, n) = __builtin_fmaf(cs[1], sv, -acc1[i][j]);
-                    break;
-                }
-                default: break;
+                for (int j = 0; j < 4; ++j) o[j] = a0[j] * sigmoid(a0[j]);
+                st4(g.c0, tl, s, r, cb, a0);
+                st4(g.c1, tl, s, r, cb, o);
+                break;
+            case BE_OUTK: {
+                const f32x4 x = ld4(g.x0, tl, s, r, cb);
+                st4(g.c0, tl, s, r, cb, a0);
+                st4(g.c1, tl, s, r, cb, 2.f * (a0 - x));
+                break;
             }
+            case BE_BWDK: {
+                const f32x4 z = ld4(g.x0, tl, s, r, cb);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = a0[j] * silu_d(z[j]);
+                st4(g.c0, tl, s, r, cb, a0);
+                st4(g.c1, tl, s, r, cb, o);
+                break;
+            }
+            case BE_QB: {
+                const f32x4 z = ld4(g.x0, tl, s, r, cb);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = a0[j] * silu_d(z[j]);
+                st4(g.c0, tl, s, r, cb, o);
+                break;
+            }
+            case BE_ADDSTORE: st4(g.c0, tl, s, r, cb, a0 + ld4(g.x0, tl, s, r, cb)); break;
+            case BE_HB: {
+                const f32x4 h = a0 + ld4(g.x0, tl, s, r, cb), z = ld4(g.x1, tl, s, r, cb);
+                o = ld4(g.c1, tl, s, r, cb);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] += h[j] * silu_d(z[j]);
+                st4(g.c1, tl, s, r, cb, o);
+                break;
+            }
+            case BE_GQ: {
+                const float cr = g.rs0[(long)s * g.sk_ss + r], dr = g.rs1[(long)s * g.sk_ss + r];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = -__builtin_fmaf(cr, a0[j], dr * acc1[i][j]);
+                st4(g.c0, tl, s, r, cb, o);
+                break;
+            }
+            case BE_UPD: {
+                const f32x4 mv = PRE ? px0[i] : ld4(g.x0, tl, s, r, cb), sv = PRE ? px1[i] : ld4(g.x1, tl, s, r, cb);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    o[j] = __builtin_fmaf(cs[0], mv[j], __builtin_fmaf(cs[2], sv[j], -a0[j]));
+                    o1[j] = __builtin_fmaf(cs[1], sv[j], -acc1[i][j]);
+                }
+                st4(g.c0, tl, s, r, cb, o);
+                st4(g.c1, tl, s, r, cb, o1);
+                break;
+            }
+            default: break;
         }
     }
 }
@@ -374,11 +517,52 @@ __global__ __launch_bounds__(64) void bcoef_kernel(BCoef a) {
 
 }  // namespace
 
+int bgemm_splitk(int m, int n, int k, int k2, int epi, int ns) {
+    // the state-streaming products have workgroups enough (a tile per 64 x
+    // 64 weights); the others are b rows by a layer width, a few dozen
+    // tiles walking a long K: split K until the grid covers the chip
+    if (epi == BE_UPD || epi == BE_ADJ || k2 > 0 || k <= NST * BKS) return 1;
+    const long tiles = (long)((n + BT - 1) / BT) * ((m + BT - 1) / BT) * ns;
+    // slices of NST steps (one round trip each), as long as the grid stays
+    // within a few workgroups per compute unit
+    long sk = (k + NST * BKS - 1) / (NST * BKS);
+    if (sk > MAXSPLIT) sk = MAXSPLIT;
+    if (tiles * sk > 2048) sk = 2048 / tiles;
+    if (sk * ns > 65535) sk = 65535 / ns;
+    return sk > 1 ? (int)sk : 1;
+}
+
+long bgemm_acc_floats(int m, int n, int ns, int splitk) {
+    return splitk > 1 ? (long)((n + BT - 1) / BT) * ((m + BT - 1) / BT) * ns * splitk * 8192 : 0;
+}
+
+template <int TA, int TB>
+static void launch_tt(const BGemm& g, int ns, hipStream_t st) {
+    const dim3 grid((unsigned)((g.n + BT - 1) / BT), (unsigned)((g.m + BT - 1) / BT), (unsigned)ns);
+    if (g.splitk > 1) {
+        if (g_launch_ev.start && !g_launch_ev.used) g_launch_ev.parts = 2;   // timed: both kernels
+        launch_k(bgemm_kernel<TA, TB, false, 1>, dim3(grid.x, grid.y, grid.z * g.splitk), dim3(256), 0, st, g);
+        launch_k(bgemm_kernel<0, 0, false, 2>, grid, dim3(256), 0, st, g);
+    } else if (TA == 1 && TB == 0 && (g.epi == BE_UPD || g.epi == BE_ADJ)) {
+        launch_k(bgemm_kernel<1, 0, true, 0>, grid, dim3(256), 0, st, g);
+    } else {
+        launch_k(bgemm_kernel<TA, TB, false, 0>, grid, dim3(256), 0, st, g);
+    }
+}
+
 hipError_t launch_bgemm(const BGemm& g, int ns, hipStream_t st) {
     if (g.m <= 0 || g.n <= 0 || ns <= 0) return hipSuccess;
     if (g.epi == BE_GP && g.m > BT) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((g.n + BT - 1) / BT), (unsigned)((g.m + BT - 1) / BT), (unsigned)ns);
-    launch_k(bgemm_kernel, grid, dim3(256), 0, st, g);
+    if (g.splitk > 1 && (!g.acc || g.k2 > 0 || g.epi == BE_UPD || g.epi == BE_ADJ || g.splitk > MAXSPLIT))
+        return hipErrorInvalidValue;
+    if ((long)ns * (g.splitk > 1 ? g.splitk : 1) > 65535) return hipErrorInvalidValue;
+    if (g.ta) {
+        if (g.tb) launch_tt<1, 1>(g, ns, st);
+        else launch_tt<1, 0>(g, ns, st);
+    } else {
+        if (g.tb) launch_tt<0, 1>(g, ns, st);
+        else launch_tt<0, 0>(g, ns, st);
+    }
     return hipGetLastError();
 }
 

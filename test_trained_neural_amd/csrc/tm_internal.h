@@ -13,18 +13,24 @@ namespace tmk {
 // launch records this pair with the kernel's own dispatch (hipExtLaunchKernel),
 // so the pair brackets the kernel's execution as the profiler sees it, not
 // the host-side launch around it.  Set and consumed on the calling thread.
+// A timed launch made of several kernels (a split product and its
+// reduction) sets `parts` first: the start event goes with the first
+// kernel's dispatch, the stop event with the last one's.
 struct LaunchEvents {
     hipEvent_t start = nullptr, stop = nullptr;
     bool used = false;
+    int parts = 1, seen = 0;
 };
 extern thread_local LaunchEvents g_launch_ev;
 
 template <class K, class... A>
 inline void launch_k(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, A... args) {
     if (g_launch_ev.start && !g_launch_ev.used) {
-        g_launch_ev.used = true;
-        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, g_launch_ev.start, g_launch_ev.stop, 0u,
-                              args...);
+        const int k = ++g_launch_ev.seen;
+        const bool last = k >= g_launch_ev.parts;
+        if (last) g_launch_ev.used = true;
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, k == 1 ? g_launch_ev.start : nullptr,
+                              last ? g_launch_ev.stop : nullptr, 0u, args...);
     } else {
         hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
     }
@@ -409,7 +415,17 @@ struct BGemm {
     float* part;              // BE_GP: [s][nt_part][2][64] at part + s * part_ss + (tile0 + bx) * 128
     long part_ss;             // BE_ADJ: [s][nt_part][3] at part + s * part_ss + (tile0 + tile) * 3
     int tile0;
+    // split K (single-segment products only): splitk workgroups per tile
+    // each sum a slice of K into acc (raw accumulators, 2 x 64 x 64 per
+    // tile and slice); a second launch sums the slices in order and runs the
+    // epilogue.  acc must hold bgemm_acc_floats(m, n, ns, splitk) floats.
+    int splitk;
+    float* acc;
 };
+long bgemm_acc_floats(int m, int n, int ns, int splitk);
+// The split-K factor launch_bgemm will use for a product of this shape
+// (1: no split).
+int bgemm_splitk(int m, int n, int k, int k2, int epi, int ns);
 hipError_t launch_bgemm(const BGemm& g, int ns, hipStream_t st);
 
 // Element-wise steps of the reverse sweep over one chunk's b rows of width n
