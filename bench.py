@@ -705,6 +705,8 @@ def main():
                     help="the queries' read order (after the chunk's write: tm_forward, the headline step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the other workloads' throughput")
+    ap.add_argument("--lines", default=None,
+                    help="comma-separated names of the other workloads' lines to run (default: all)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="finish with a plain 256 MiB device copy (scale reference for HBM counters)")
     args = ap.parse_args()
@@ -862,26 +864,35 @@ def main():
     if not args.no_other:
         # the other workloads of the pages' shapes, a few steps each (context;
         # the headline value is the workload above)
-        out["other_workloads"] = {
-            "mlp384_stream": other_workload("mlp384_stream", 3),
-            "multihead1024": other_workload("multihead1024", 3, kernel_roof=True),
-            "deep512": other_workload("deep512", 2, calls=16),
+        orc = not args.no_cpu_baseline
+        lines = {
+            "mlp384_stream": lambda: other_workload("mlp384_stream", 3),
+            "multihead1024": lambda: other_workload("multihead1024", 3, kernel_roof=True),
+            "deep512": lambda: other_workload("deep512", 2, calls=16),
             # the same step with each chunk's queries read before its write
-            "mlp384_read_before_write": other_workload("mlp384", 20, read=1, oracle=not args.no_cpu_baseline),
+            "mlp384_read_before_write": lambda: other_workload("mlp384", 20, read=1, oracle=orc),
             # each query read right after its own token's write (the dual form)
-            "mlp384_read_per_token": other_workload("mlp384", 20, read=2, oracle=not args.no_cpu_baseline),
+            "mlp384_read_per_token": lambda: other_workload("mlp384", 20, read=2, oracle=orc),
             # read-only retrieval of the call's queries through the stored memory
-            "mlp384_retrieve": retrieval("mlp384", 20, oracle=not args.no_cpu_baseline),
+            "mlp384_retrieve": lambda: retrieval("mlp384", 20, oracle=orc),
             # ... and at the multi-head workload's scale (64 streams x 32768 queries)
-            "multihead1024_retrieve": retrieval("multihead1024", 3),
+            "multihead1024_retrieve": lambda: retrieval("multihead1024", 3),
             # the backward through the store (gradients through one tm_forward call)
-            "mlp384_backward": backward_line("mlp384", 10, oracle=not args.no_cpu_baseline),
+            "mlp384_backward": lambda: backward_line("mlp384", 10, oracle=orc),
+            # the input side alone and chained with the memory (two lines)
+            "mlp384_input_side": lambda: input_side("mlp384", 20, oracle=orc),
+            # the memory's side of memory as a context, segment by segment
+            "mlp384_mac": lambda: mac_wiring("mlp384", 10, oracle=orc),
         }
-        side = input_side("mlp384", 20, oracle=not args.no_cpu_baseline)
-        out["other_workloads"]["mlp384_input_side"] = side["input_side"]
-        out["other_workloads"]["mlp384_from_tokens"] = side["from_tokens"]
-        # the memory's side of memory as a context, segment by segment
-        out["other_workloads"]["mlp384_mac"] = mac_wiring("mlp384", 10, oracle=not args.no_cpu_baseline)
+        want = list(lines) if args.lines is None else args.lines.split(",")
+        out["other_workloads"] = {}
+        for nm in want:
+            r = lines[nm]()
+            if nm == "mlp384_input_side":
+                out["other_workloads"]["mlp384_input_side"] = r["input_side"]
+                out["other_workloads"]["mlp384_from_tokens"] = r["from_tokens"]
+            else:
+                out["other_workloads"][nm] = r
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, params, ci)
         out["cpu_baseline"]["gpu_over_cpu"] = out["value"] / out["cpu_baseline"]["value"]

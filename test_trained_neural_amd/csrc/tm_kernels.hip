@@ -201,16 +201,19 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     for (int k = kb; k < kb + spw; k += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
-            const bool live = k + p < ke;   // wave-uniform
-            F av[MR], bv[NR];
+            // steps past the wave's slice issue no matrix instruction
+            // (wave-uniform; their ring slots still reload a valid address)
+            if (k + p < ke) {
+                F av[MR], bv[NR];
 #pragma unroll
-            for (int m = 0; m < MR; ++m) av[m] = aok[m] ? cvt<OP>(a[p][m]) : zero_frag<OP>();
+                for (int m = 0; m < MR; ++m) av[m] = aok[m] ? cvt<OP>(a[p][m]) : zero_frag<OP>();
 #pragma unroll
-            for (int n = 0; n < NR; ++n) bv[n] = (live && bok[n]) ? cvt<OP>(bb[p][n]) : zero_frag<OP>();
+                for (int n = 0; n < NR; ++n) bv[n] = bok[n] ? cvt<OP>(bb[p][n]) : zero_frag<OP>();
 #pragma unroll
-            for (int m = 0; m < MR; ++m)
+                for (int m = 0; m < MR; ++m)
 #pragma unroll
-                for (int n = 0; n < NR; ++n) mma(acc[m][n], av[m], bv[n]);
+                    for (int n = 0; n < NR; ++n) mma(acc[m][n], av[m], bv[n]);
+            }
             load_step(p, min(k + p + PF, klast));
         }
     }
