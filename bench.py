@@ -206,7 +206,7 @@ def scan_bytes(wl, ns, T):
     return ns * (T * (20 + 5 * wl.dim * e) + (T // wl.chunk) * 16)
 
 
-def other_workload(name, steps, calls=None, read=None, oracle=False, kernel_roof=False):
+def other_workload(name, steps, calls=None, read=None, oracle=False, kernel_roof=False, oracle_tokens=None):
     """Throughput of another workload (tokens/s): state init + its calls in
     order, inputs resident in HBM, graph replay (each call's buffers repeat
     across steps).  calls: how many of the workload's calls to run (a prefix
@@ -285,18 +285,22 @@ def other_workload(name, steps, calls=None, read=None, oracle=False, kernel_roof
                                         "r3_score_kernel + r3_layer_kernel")
     T.tm_destroy(ctx)
     if oracle:
-        # the oracle on the workload's first call, in the same read order
+        # the oracle on the workload's first call (or its first oracle_tokens
+        # tokens), in the same read order, one thread per stream
         from oracle import tmref
-        ci = I.make_call(wl, params, 0, 0)
+        on = Tn if oracle_tokens is None else min(oracle_tokens, Tn)
+        ci = I.make_call(wl, params, 0, 0, tokens=on)
         st = I.initial_state(wl, params)
         nt = min(os.cpu_count() or 1, Bn * H)
         t1 = time.perf_counter()
         tmref.forward(wl.dim, wl.depth, wl.expansion, wl.chunk, st, ci.k, ci.v, ci.theta, ci.eta, ci.alpha,
                       q=ci.q, n_threads=nt, read={None: "after", 1: "before", 2: "token"}[read])
         odt = time.perf_counter() - t1
-        out["cpu_baseline"] = {"value": Bn * Tn / odt, "unit": "tokens/s", "cores": nt, "kind": "oracle",
-                               "sample": "%s: one call (%d streams x %d tokens) from the initial state, fp64 C "
-                                         "oracle, %.1f s" % (wl.name, Bn * H, Tn, odt), "host": host_info()}
+        out["cpu_baseline"] = {"value": Bn * on / odt, "unit": "tokens/s", "cores": nt, "kind": "oracle",
+                               "sample": "%s: %s (%d streams x %d tokens) from the initial state, fp64 C oracle, one "
+                                         "thread per stream, %.1f s" % (wl.name, "one call" if on == Tn else
+                                                                       "the first call's first %d tokens" % on,
+                                                                       Bn * H, on, odt), "host": host_info()}
     return out
 
 
@@ -866,9 +870,11 @@ def main():
         # the headline value is the workload above)
         orc = not args.no_cpu_baseline
         lines = {
-            "mlp384_stream": lambda: other_workload("mlp384_stream", 3),
-            "multihead1024": lambda: other_workload("multihead1024", 3, kernel_roof=True),
-            "deep512": lambda: other_workload("deep512", 2, calls=16),
+            "linear64": lambda: other_workload("linear64", 20, oracle=orc),
+            "mlp384_stream": lambda: other_workload("mlp384_stream", 3, oracle=orc),
+            "multihead1024": lambda: other_workload("multihead1024", 3, kernel_roof=True, oracle=orc,
+                                                    oracle_tokens=128),
+            "deep512": lambda: other_workload("deep512", 2, calls=16, oracle=orc, oracle_tokens=64),
             # the same step with each chunk's queries read before its write
             "mlp384_read_before_write": lambda: other_workload("mlp384", 20, read=1, oracle=orc),
             # each query read right after its own token's write (the dual form)

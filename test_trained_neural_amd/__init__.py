@@ -200,26 +200,50 @@ def tm_create(dim, depth, expansion, chunk):
 
 
 def tm_destroy(ctx):
+    _forget(ctx)
     lib().tm_destroy(ctx)
 
 
 def tm_param_count(ctx):
-    return lib().tm_param_count(ctx)
+    return _cached(ctx, ("params",), lambda: lib().tm_param_count(ctx))
 
 
 def tm_config(ctx):
     """(dim, depth, expansion, chunk) of the memory configuration."""
-    v = [_i(0) for _ in range(4)]
-    _check("tm_config", lib().tm_config(ctx, *[ctypes.byref(x) for x in v]))
-    return tuple(int(x.value) for x in v)
+    def query():
+        v = [_i(0) for _ in range(4)]
+        _check("tm_config", lib().tm_config(ctx, *[ctypes.byref(x) for x in v]))
+        return tuple(int(x.value) for x in v)
+    return _cached(ctx, ("config",), query)
+
+
+# The size queries and tm_config are pure functions of a ctx's (immutable)
+# configuration and their arguments: the binding's argument checks, made on
+# every call, remember them per ctx (forgotten by tm_destroy, so an address
+# reused by a later ctx starts afresh).
+_memo = {}
+
+
+def _cached(ctx, key, fn):
+    k = (ctx.value if isinstance(ctx, ctypes.c_void_p) else ctx,) + key
+    v = _memo.get(k)
+    if v is None:
+        v = _memo[k] = fn()
+    return v
+
+
+def _forget(ctx):
+    c = ctx.value if isinstance(ctx, ctypes.c_void_p) else ctx
+    for k in [k for k in _memo if k[0] == c]:
+        del _memo[k]
 
 
 def tm_state_bytes(ctx, batch, heads):
-    return lib().tm_state_bytes(ctx, batch, heads)
+    return _cached(ctx, ("state", batch, heads), lambda: lib().tm_state_bytes(ctx, batch, heads))
 
 
 def tm_workspace_bytes(ctx, batch, heads, n_tokens):
-    return lib().tm_workspace_bytes(ctx, batch, heads, n_tokens)
+    return _cached(ctx, ("ws", batch, heads, n_tokens), lambda: lib().tm_workspace_bytes(ctx, batch, heads, n_tokens))
 
 
 def tm_state_init(ctx, state, batch, heads, init_weights, stream=None):
@@ -263,7 +287,8 @@ def tm_forward(ctx, state, k, v, q, theta, eta, alpha, y, workspace, stream=None
 
 
 def tm_backward_workspace_bytes(ctx, batch, heads, n_tokens):
-    return lib().tm_backward_workspace_bytes(ctx, batch, heads, n_tokens)
+    return _cached(ctx, ("bws", batch, heads, n_tokens),
+                   lambda: lib().tm_backward_workspace_bytes(ctx, batch, heads, n_tokens))
 
 
 def tm_backward(ctx, state, k, v, q, theta, eta, alpha, dy, dstate, dk, dv, dq, dtheta, deta, dalpha, workspace,
