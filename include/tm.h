@@ -303,8 +303,9 @@ tm_status tm_graphs_enable(int on);
  * update runs in workgroups of its own beside the first-layer blocks, and M_1
  * alternates with a second buffer in the workspace over a call's updates; the
  * state holds the final M_1 when the call ends.  on = 0 keeps it in the
- * first-layer blocks, in place.  Process-wide; calls captured into graphs
- * before a change keep the setting they were captured with. */
+ * first-layer blocks, in place.  fp32 calls always update W_1 in place.
+ * Process-wide; calls captured into graphs before a change keep the setting
+ * they were captured with. */
 tm_status tm_w1_split_enable(int on);
 
 /* Instrumentation for measuring kernels in place (not part of the method).

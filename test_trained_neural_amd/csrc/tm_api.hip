@@ -837,7 +837,7 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
     float* m1_ws = c->L == 2 ? reinterpret_cast<float*>(ws + w.m1x) : nullptr;
     const long p1 = c->L >= 2 ? (long)c->din[1] * c->dout[1] : 0;
     int nw1 = 0;
-    if (c->L == 2 && g_w1_split) {
+    if (c->L == 2 && g_w1_split && !f32) {
         // a multiple of 8 workgroups, W1_JPW row blocks each per XCD residue
         const int n1 = 8 * (((a.nb1 + 7) / 8 + W1_JPW - 1) / W1_JPW);
         int cus = 0;

@@ -230,7 +230,11 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm g) {
             }
         };
         segment(g.A, g.B, g.k, false);
-        if (g.k2 > 0) segment(g.A2, g.Bs2, g.k2, true);
+        // (a second K segment only in the state-streaming instantiation, the
+        // one launch that has it: the adjoint update)
+        if constexpr (PRE) {
+            if (g.k2 > 0) segment(g.A2, g.Bs2, g.k2, true);
+        }
         if constexpr (PHASE == 1) {
             float* p = g.acc + ((long)(s * g.splitk + slice) * tiles + tile) * 8192;
 #pragma unroll
@@ -556,9 +560,11 @@ hipError_t launch_bgemm(const BGemm& g, int ns, hipStream_t st) {
     if (g.splitk > 1 && (!g.acc || g.k2 > 0 || g.epi == BE_UPD || g.epi == BE_ADJ || g.splitk > MAXSPLIT))
         return hipErrorInvalidValue;
     if ((long)ns * (g.splitk > 1 ? g.splitk : 1) > 65535) return hipErrorInvalidValue;
+    const bool streaming = g.ta && !g.tb && (g.epi == BE_UPD || g.epi == BE_ADJ);
+    if (g.k2 > 0 && !streaming) return hipErrorInvalidValue;
     if (g.ta) {
-        if (g.tb) launch_tt<1, 1>(g, ns, st);
-        else launch_tt<1, 0>(g, ns, st);
+        if (g.tb) return hipErrorInvalidValue;   // no product of the sweep needs both transposed
+        launch_tt<1, 0>(g, ns, st);
     } else {
         if (g.tb) launch_tt<0, 1>(g, ns, st);
         else launch_tt<0, 0>(g, ns, st);

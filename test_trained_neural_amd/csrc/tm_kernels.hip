@@ -1429,7 +1429,9 @@ static bool first_small(const FirstArgs& a, bool f32) {
 
 template <class OP, bool UPD, bool FWD>
 static void launch_first_as(const FirstArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-    if constexpr (UPD) {
+    // (W_1's workgroups of their own: bf16 only; with fp32 operands that
+    // variant's register set would spill)
+    if constexpr (UPD && sizeof(OP) == 2) {
         if (a.nw1 > 0) {
             launch_k((first_layer_kernel<OP, true, FWD, true, true, false>), grid, dim3(FW * 64), lds, st, a);
             return;
@@ -1460,7 +1462,7 @@ static void launch_first_op(const FirstArgs& a, dim3 grid, size_t lds, hipStream
 
 hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st) {
     if (!a.do_update && !a.do_fwd) return hipSuccess;
-    if (a.nw1 > 0 && (!a.do_update || a.u.L != 2 || a.upd_ntiles != 0 || a.nw1 % 8 != 0 ||
+    if (a.nw1 > 0 && (f32 || !a.do_update || a.u.L != 2 || a.upd_ntiles != 0 || a.nw1 % 8 != 0 ||
                       (long)(a.nw1 / 8) * W1_JPW < (a.nb1 + 7) / 8 || a.m1_rd == a.m1_wr))
         return hipErrorInvalidValue;
     if (a.upd_ntiles > 0 && (!a.do_update || a.u.L < 3)) return hipErrorInvalidValue;
