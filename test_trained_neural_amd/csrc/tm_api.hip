@@ -350,6 +350,16 @@ void log_call(const tm_ctx* c, const GraphEntry& k) {
 // ---- graph replay of repeated calls ----
 bool g_graphs = true;
 bool g_w1_split = true;   // tm_w1_split_enable
+// TM_XCD_STREAMS=0 turns the first-layer blocks' grouping by XCD off (for
+// comparing the two mappings; the results are bitwise the same)
+bool xcd_streams_on() {
+    static int on = -1;
+    if (on < 0) {
+        const char* e = getenv("TM_XCD_STREAMS");
+        on = e && e[0] == '0' ? 0 : 1;
+    }
+    return on == 1;
+}
 constexpr size_t MAX_GRAPHS = 16;
 
 // Runs `launch(stream)`.  A call whose key has been seen before is captured
@@ -573,6 +583,7 @@ tm_status run_forward_layers(const tm_ctx* c, char* state, long ns, const WsLayo
         }
         // (a retrieve pass of many rows: a plain tiled product, no split K)
         const bool big = retrieve && !f32 && rows >= RET_TILED_ROWS;
+        g.xcd_streams = xcd_streams_on() && ns % 8 == 0 && ns >= 8 ? 1 : 0;
         hipError_t e = timed(K_FWD, st, [&] {
             return big ? launch_rows(g, (int)ns, st) : launch_fwd(g, (int)ns, f32 ? 1 : 0, st);
         });
@@ -616,6 +627,7 @@ tm_status run_backward(const tm_ctx* c, char* state, long ns, const WsLayout& w,
         g.cc = reinterpret_cast<const float*>(ws + w.cc) + ci * b;
         g.dc = reinterpret_cast<const float*>(ws + w.dc) + ci * b;
         g.coef_ss = w.coef_ss;
+        g.xcd_streams = xcd_streams_on() && ns % 8 == 0 && ns >= 8 ? 1 : 0;
         hipError_t e = timed(K_BWD, st, [&] { return launch_bwd(g, (int)ns, f32 ? 1 : 0, st); });
         if (e != hipSuccess) return TM_ERR_HIP;
     }
@@ -889,11 +901,15 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
         // the other layers (independent of each other)
         a.upd_tile0 = tile2;
         a.upd_ntiles = a.do_update ? ntile_rest : 0;
+        // many streams, no workgroups of other roles: each stream's blocks on
+        // one XCD (its shared operands fetched into one L2)
+        a.xcd_streams = xcd_streams_on() && ns % 8 == 0 && ns >= 8 && a.upd_ntiles == 0 ? 1 : 0;
         a.m1_rd = m1_state;
         a.m1_wr = m1_state;
         a.m1_rd_ss = a.m1_wr_ss = c->P;
         a.nw1 = 0;
         if (nw1 > 0 && a.do_update && (ci >= 2 || C % 2 == 0)) {
+            a.xcd_streams = 0;
             const bool to_ws = (C - ci + 1) % 2 == 0;   // updates left, this one included
             a.nw1 = nw1;
             a.m1_rd = to_ws ? m1_state : m1_ws;

@@ -154,6 +154,7 @@ struct GemmArgs {
     const float* cc;          // c_t of the chunk's tokens: cc[s*coef_ss + t]
     const float* dc;
     long coef_ss;
+    int xcd_streams;          // 1: each stream's tiles on one XCD (ns % 8 == 0)
 };
 
 // The theta-weighted gradient reduction of one chunk and the fused
@@ -250,6 +251,7 @@ struct FirstArgs {
     float* m1_wr;
     long m1_wr_ss;
     int nw1;                  // > 0: W_1's update in workgroups of its own
+    int xcd_streams;          // 1: each stream's blocks on one XCD (grid (nb1, ns), ns % 8 == 0)
 };
 
 // Per call: the coefficient scan of every (stream, chunk); every chunk's

@@ -74,9 +74,20 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     extern __shared__ float red[];          // [W][RT][NTP], then the tile's c, d coefficients
     float* coefs = red + W * RT * NTP;      // [2][RT]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int s = blockIdx.z;
-    const int row0 = blockIdx.y * RT;
-    const int col0 = blockIdx.x * NT;
+    // the workgroup's stream and tile: the grid's own coordinates, or
+    // (xcd_streams) remapped so that all tiles of a stream run on one XCD
+    // (workgroups go to the 8 XCDs round-robin by linear id): the stream's
+    // activations and weights are then fetched into one L2, not several
+    int s = blockIdx.z, ty = blockIdx.y, tx = blockIdx.x;
+    if (g.xcd_streams) {
+        const int per = gridDim.x * gridDim.y;
+        const int lin = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x, q = lin >> 3;
+        s = (q / per) * 8 + (lin & 7);
+        ty = (q % per) / gridDim.x;
+        tx = (q % per) % gridDim.x;
+    }
+    const int row0 = ty * RT;
+    const int col0 = tx * NT;
     const int nsteps = g.K >> 5;
     const int spw = (nsteps + W - 1) / W;   // steps per wave
     const int kb = wave * spw;
@@ -391,6 +402,7 @@ static void launch_nr(const GemmArgs& g, int ns, int nr, hipStream_t st) {
 template <class OP, class AT, class BT, int BM>
 static hipError_t launch_gemm(const GemmArgs& g, int ns, hipStream_t st) {
     if (g.nrows <= 0 || g.N <= 0) return hipSuccess;
+    if (g.xcd_streams && ns % 8 != 0) return hipErrorInvalidValue;
     const GemmShape sh = pick<AT, BT>(g, ns);
     if (sh.rt == 64) {
         if (sh.w == 8) launch_nr<OP, AT, BT, BM, 64, 8>(g, ns, sh.nr, st);
@@ -980,11 +992,23 @@ void first_layer_kernel(FirstArgs a) {
         return;
     }
     const UpdArgs& u = a.u;
-    const int s = blockIdx.y;
+    // the workgroup's stream and column block: the grid's own coordinates,
+    // or (xcd_streams) remapped so that all blocks of a stream run on one
+    // XCD: the dispatcher deals workgroups to the 8 XCDs round-robin by
+    // linear id, so XCD x gets the linear ids x, x + 8, ...; they are given
+    // streams x, x + 8, ... (all nb1 blocks of each), and the operands every
+    // block of a stream reads (the chunk's keys and rows, layer 1's Delta)
+    // are fetched into one L2 instead of eight.
+    int s = blockIdx.y, bx = blockIdx.x;
+    if (a.xcd_streams) {
+        const int lin = blockIdx.y * gridDim.x + blockIdx.x, q = lin >> 3;
+        s = (q / a.nb1) * 8 + (lin & 7);
+        bx = q % a.nb1;
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kofs = 8 * (lane >> 4), g4 = 4 * (lane >> 4);
     const int d = a.dim, h1 = a.h1, b = u.b, bp = u.bp;
-    const int j0 = blockIdx.x * JW;
+    const int j0 = bx * JW;
     const int jl = lane & 15, j = j0 + jl;   // the lane's column (h1 is a multiple of 16)
     const int WP = d + WPAD, RP = JW + RPAD;
     constexpr int DP = MAX_CHUNK + WPAD;     // rows hold every token slot of a chunk
@@ -1055,7 +1079,7 @@ void first_layer_kernel(FirstArgs a) {
     const int mineB = (nrb - wave + FW - 1) / FW;
     // (the lane's 4 values of a 16 x 16 block of M or S are one float4 at
     // mso(rbk), the wave's block 1 KB contiguous)
-    auto mso = [&](int rbk) { return ((long)(blockIdx.x * nrb + rbk) * 64 + lane) * 4; };
+    auto mso = [&](int rbk) { return ((long)(bx * nrb + rbk) * 64 + lane) * 4; };
     F kf[PB][2];
     f32x4 mr[PB], sr[PB];
     auto load_rb = [&](int p, int n) {
@@ -1121,7 +1145,7 @@ void first_layer_kernel(FirstArgs a) {
     const float* M1r = DEEP ? a.m1_rd + (long)s * a.m1_rd_ss : nullptr;
     float* M1w = DEEP ? a.m1_wr + (long)s * a.m1_wr_ss : nullptr;
     float* S1 = u.S + (long)s * u.P + (DEEP ? u.off[1] : 0);
-    auto mso1 = [&](int nb) { return ((long)(blockIdx.x * ncb1 + nb) * 64 + lane) * 4; };
+    auto mso1 = [&](int nb) { return ((long)(bx * ncb1 + nb) * 64 + lane) * 4; };
     auto load_w1 = [&](int p, int n) {
         const int nb = min(wave + FW * n, ncb1 - 1);
 #pragma unroll
@@ -1138,7 +1162,7 @@ void first_layer_kernel(FirstArgs a) {
     auto issue1 = [&]() {
         if constexpr (W1) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) h1f[ks] = cvt<OP>(ld8(at1 + pkf(blockIdx.x, min(ks, nkb - 1), nkb, lane)));
+            for (int ks = 0; ks < 2; ++ks) h1f[ks] = cvt<OP>(ld8(at1 + pkf(bx, min(ks, nkb - 1), nkb, lane)));
 #pragma unroll
             for (int p = 0; p < PN; ++p) load_w1(p, p);
         }
@@ -1466,6 +1490,7 @@ hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st) {
                       (long)(a.nw1 / 8) * W1_JPW < (a.nb1 + 7) / 8 || a.m1_rd == a.m1_wr))
         return hipErrorInvalidValue;
     if (a.upd_ntiles > 0 && (!a.do_update || a.u.L < 3)) return hipErrorInvalidValue;
+    if (a.xcd_streams && (a.nw1 > 0 || a.upd_ntiles > 0 || ns % 8 != 0)) return hipErrorInvalidValue;
     const int tpw = upd_tpw(f32, first_small(a, f32));
     const int nupd = (a.upd_ntiles + tpw - 1) / tpw;   // workgroups of update tiles
     dim3 grid(a.nb1 + (a.nw1 > 0 ? a.nw1 : nupd), ns);

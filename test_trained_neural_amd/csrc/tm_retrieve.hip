@@ -24,9 +24,20 @@ __global__ __launch_bounds__(RB_WAVES * 64) void rows_kernel(GemmArgs g) {
     constexpr int NC = NR * 16;
     __shared__ float tile[RB_WAVES][16][NC + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int s = blockIdx.z;
-    const int r0 = blockIdx.y * (RB_WAVES * 16) + wave * 16;   // the wave's first row
-    const int c0 = blockIdx.x * NC;
+    // the stream and tile: the grid's coordinates, or (xcd_streams) remapped
+    // so that all tiles of a stream run on one XCD (workgroups go to the 8
+    // XCDs round-robin by linear id): a row block's operand rows and the
+    // stream's weights are then fetched into one L2, not several
+    int s = blockIdx.z, by = blockIdx.y, bx = blockIdx.x;
+    if (g.xcd_streams) {
+        const int per = gridDim.x * gridDim.y;
+        const int lin = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x, q = lin >> 3;
+        s = (q / per) * 8 + (lin & 7);
+        by = (q % per) / gridDim.x;
+        bx = (q % per) % gridDim.x;
+    }
+    const int r0 = by * (RB_WAVES * 16) + wave * 16;   // the wave's first row
+    const int c0 = bx * NC;
     const int nsteps = g.K >> 5;
     const int kofs = 8 * (lane >> 4);
 
@@ -114,7 +125,7 @@ hipError_t launch_rows(const GemmArgs& g, int ns, hipStream_t st) {
     // packed bf16 copy; N a multiple of 32, K of 32
     if (g.nrows <= 0) return hipSuccess;
     if (g.bmode != B_PACKED || (g.amode != A_TOKENS && g.amode != A_PACKED) || g.n0 != g.nrows ||
-        g.N % 32 != 0 || g.K % 32 != 0 || g.K <= 0 || ns < 1 || ns > 65535)
+        g.N % 32 != 0 || g.K % 32 != 0 || g.K <= 0 || ns < 1 || ns > 65535 || (g.xcd_streams && ns % 8 != 0))
         return hipErrorInvalidValue;
     const bool last = g.epi == EPI_OUT;
     if (!last && g.epi != EPI_HIDDEN) return hipErrorInvalidValue;
