@@ -476,8 +476,7 @@ def retrieval(name, steps, oracle=False):
     flops = 2 * Bn * H * Tn * sum(a * b for a, b in wl.layer_dims()) * steps
     out = {"tokens_per_s": Bn * Tn / dt, "ms_per_step": dt * 1e3, "steps": steps,
            "step": "tm_retrieve of (%d, %d) queries through the memory after storing them" % (Bn, Tn),
-           "roofline": mfma_roofline(flops, ms, n, wl.dtype,
-                                     "rows_kernel" if wl.dtype == "bf16" and min(Tn, 2048) >= 256 else "gemm_kernel")}
+           "roofline": mfma_roofline(flops, ms, n, wl.dtype, retrieve_kernel(wl, Tn))}
     T.tm_destroy(ctx)
     if oracle:
         from oracle import tmref
@@ -491,6 +490,16 @@ def retrieval(name, steps, oracle=False):
                                "sample": "%s: retrieve of one call's queries (%d streams x %d tokens), fp64 C "
                                          "oracle, %.2f s" % (wl.name, Bn * H, Tn, odt), "host": host_info()}
     return out
+
+
+def retrieve_kernel(wl, n_tokens):
+    """The kernel tm_retrieve launches for this memory: both layers in one
+    launch (depth 2, bf16, width <= 128, hidden a multiple of 64), else one
+    launch per layer, tiled from 256 rows a pass."""
+    h = wl.dim * wl.expansion
+    if wl.dtype == "bf16" and wl.depth == 2 and wl.dim <= 128 and h % 64 == 0:
+        return "mlp2_kernel"
+    return "rows_kernel" if wl.dtype == "bf16" and min(n_tokens, 2048) >= 256 else "gemm_kernel"
 
 
 def input_side(name, steps, oracle=False):

@@ -119,7 +119,11 @@ tm_status tm_store(const tm_ctx* ctx, void* state, const void* k, const void* v,
                    void* workspace, void* stream);
 
 /* y = M(q) for every query through the current weights (step 5).  The state
- * is not written.  Any n_tokens >= 0 (0: a no-op, as for tm_store). */
+ * is not written.  Any n_tokens >= 0 (0: a no-op, as for tm_store).  With
+ * bf16 operands, depth 2, dim <= 128 and a hidden width that is a multiple
+ * of 64, both layers run in one launch and the workspace is not touched;
+ * otherwise passes of up to 2048 rows per stream go layer by layer through
+ * it. */
 tm_status tm_retrieve(const tm_ctx* ctx, const void* state, const void* q, float* y,
                       int batch, int heads, int n_tokens, tm_dtype dtype,
                       void* workspace, void* stream);

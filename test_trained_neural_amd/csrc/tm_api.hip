@@ -1573,6 +1573,23 @@ tm_status tm_retrieve(const tm_ctx* c, const void* state_v, const void* q, float
                       static_cast<hipStream_t>(stream), [&](hipStream_t st) {
         WsLayout w = ws_layout(c, ns, n_tokens);
         TokLayout tl{n_tokens, heads, c->dim};
+        if (dtype == TM_BF16 && c->L == 2 && mlp2_fits(c->dim, c->hidden)) {
+            // both layers in one launch over every query row (no workspace)
+            StateLayout sl = state_layout(c, ns);
+            Mlp2Args a{};
+            a.q = q;
+            a.y = y;
+            a.w = state + sl.Wt;
+            a.w_ss = c->P;
+            a.off1 = c->off[1];
+            a.tl = tl;
+            a.t0 = 0;
+            a.nrows = n_tokens;
+            a.d = c->dim;
+            a.h = c->hidden;
+            a.xcd_streams = xcd_streams_on() && ns % 8 == 0 && ns >= 8 ? 1 : 0;
+            return hip_status(timed(K_FWD, st, [&] { return launch_mlp2(a, (int)ns, st); }));
+        }
         for (long p0 = 0; p0 < n_tokens; p0 += w.ret_rows) {
             FwdRows fr{};
             fr.nq = (int)((n_tokens - p0) < w.ret_rows ? (n_tokens - p0) : w.ret_rows);

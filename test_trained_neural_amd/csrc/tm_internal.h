@@ -490,6 +490,22 @@ hipError_t launch_r3_layer(const R3Args& r, int ns, int f32, hipStream_t st);
 // EPI_OUT with query rows only).
 hipError_t launch_rows(const GemmArgs& g, int ns, hipStream_t st);
 
+// Read-only retrieval of a depth-2 memory of width d <= 128 (bf16 operands),
+// both layers in one launch: y = SiLU(q W_0) W_1 for rows t0 .. t0+nrows-1
+// of every stream.  w: the stream's packed bf16 weights (W_0 packed [h][d],
+// W_1 packed [d][h] at w + off1), stream stride w_ss elements.
+struct Mlp2Args {
+    const void* q;
+    float* y;
+    const void* w;
+    long w_ss, off1;
+    TokLayout tl;
+    int t0, nrows, d, h;
+    int xcd_streams;
+};
+bool mlp2_fits(int d, int h);
+hipError_t launch_mlp2(const Mlp2Args& a, int ns, hipStream_t st);
+
 // Memory-as-context wiring (tm_mac.hip).  Window: out [B][P+2S][D] (operand
 // type) = [persistent [P][D]; recalled [B][S][D] fp32, rounded; segment
 // [B][S][D]].  Gate: out [B][S][D] fp32 = segment (the attention output y,

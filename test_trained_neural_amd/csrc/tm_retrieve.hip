@@ -10,7 +10,9 @@
 // layer's packed activations (through a per-wave LDS tile, so the stores
 // are 16-byte pieces of 8 consecutive columns), or writes y.  The chunk
 // step's products (a few dozen rows per stream) use the split-K kernel in
-// tm_kernels.hip instead.
+// tm_kernels.hip instead.  A memory of depth 2 and width up to 128 takes
+// mlp2_kernel below instead: both layers in one launch, no activations in
+// memory.
 #include "tm_device.h"
 
 namespace tmk {
@@ -135,6 +137,228 @@ hipError_t launch_rows(const GemmArgs& g, int ns, hipStream_t st) {
     } else {
         if (last) launch_rows_as<2, true>(g, ns, st);
         else launch_rows_as<2, false>(g, ns, st);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Read-only retrieval of a depth-2 memory of width d <= 128 in one launch:
+// y = SiLU(q W_0) W_1 with the hidden activations kept in registers.
+//
+// Both layers run transposed, H^T = W_0^T q^T and y^T = W_1^T H^T.  A lane's
+// share of a layer-0 result tile is 4 consecutive hidden units of one token,
+// and two such tiles (hidden 32k .. 32k+15 and 32k+16 .. 32k+31) make the
+// lane's 8 values of a layer-1 B fragment for the 32-deep step k, in the K
+// order {4g .. 4g+3, 16+4g .. 16+4g+3} for lane group g.  The order inside a
+// step is free as long as A and B use the same one, so W_1's fragments are
+// put into LDS in that order and nothing is moved between the layers.
+//
+// A workgroup owns WAVES x TB 16-token blocks of one stream; a wave keeps its
+// TB blocks of queries as B fragments (all d/32 steps) and TB x d/16
+// accumulator tiles of y.  The weights stream through LDS in 64-hidden
+// chunks, double buffered: chunk c+1's loads are in flight while chunk c
+// computes, and each fragment read from LDS serves TB matrix instructions.
+template <int D, int TB, int WAVES, int HC, bool PIPE>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mlp2_kernel(Mlp2Args a) {
+    constexpr int KS = D / 32, NB = D / 16, NT = WAVES * 64, SPC = HC / 32;
+    constexpr int W0P = (HC / 16) * KS * 64;   // 16-byte pieces of a chunk's W_0 fragments
+    constexpr int W1P = NB * SPC * 64;         // ... and of its W_1 fragments
+    constexpr int CP = W0P + W1P;
+    constexpr int RND = (CP + NT - 1) / NT;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    extern __shared__ __attribute__((aligned(16))) char lds[];   // 2 chunks of CP pieces
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, col = lane & 15;
+    // the stream and row block: the grid's coordinates, or (xcd_streams) all
+    // row blocks of a stream on one XCD, so its weights are fetched into one L2
+    int s = blockIdx.y, bx = blockIdx.x;
+    if (a.xcd_streams) {
+        const int lin = blockIdx.y * gridDim.x + blockIdx.x, q8 = lin >> 3;
+        s = (q8 / gridDim.x) * 8 + (lin & 7);
+        bx = q8 % gridDim.x;
+    }
+    const bf16* w0 = reinterpret_cast<const bf16*>(a.w) + (long)s * a.w_ss;
+    const bf16* w1 = w0 + a.off1;
+    const int nks1 = a.h >> 5, nch = a.h / HC;
+    const int r0 = (bx * WAVES + wave) * (TB * 16);   // the wave's first row
+
+    // the wave's queries: B fragments of layer 0 (rows past the call are
+    // clamped to a valid row and their results dropped)
+    bf16x8 qf[TB][KS];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const int t = min(r0 + 16 * tb + col, a.nrows - 1);
+        const bf16* qp = reinterpret_cast<const bf16*>(a.q) + tok_off(a.tl, s, a.t0 + t) + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[tb][ks] = ld8(qp + 32 * ks);
+    }
+
+    // chunk c of the weights: W_0's fragments of hidden blocks (HC/16)c ..
+    // (contiguous in the packed copy), then W_1's fragments of the chunk's
+    // K steps for every output block, each piece split in two halves that go
+    // to the lanes of the permuted K order
+    bf16x8 stg[RND];
+    auto fetch = [&](int c) {
+#pragma unroll
+        for (int p = 0; p < RND; ++p) {
+            const int o = p * NT + tid;
+            if (o < W0P) {
+                stg[p] = ld8(w0 + (long)c * (W0P * 8) + o * 8);
+            } else if (o < CP) {
+                const int o1 = o - W0P, f = o1 >> 6;
+                stg[p] = ld8(w1 + pkf(f / SPC, SPC * c + f % SPC, nks1, o1 & 63));
+            }
+        }
+    };
+    auto put = [&](char* buf) {
+#pragma unroll
+        for (int p = 0; p < RND; ++p) {
+            const int o = p * NT + tid;
+            if (o < W0P) {
+                *reinterpret_cast<bf16x8*>(buf + o * 16) = stg[p];
+            } else if (o < CP) {
+                // the piece holds inputs 8gp .. 8gp+7 of output row n: the
+                // first four go to lane group 2(gp&1), the last four to the
+                // group after it, in slots 0..3 (gp < 2) or 4..7
+                const int o1 = o - W0P, L = o1 & 63, n = L & 15, gp = L >> 4;
+                const int ga = 2 * (gp & 1), half = (gp >> 1) * 8;
+                char* fb = buf + W0P * 16 + (o1 >> 6) * 1024;
+                const bf16x8 v = stg[p];
+                *reinterpret_cast<bf16x4*>(fb + (n + 16 * ga) * 16 + half) = (bf16x4){v[0], v[1], v[2], v[3]};
+                *reinterpret_cast<bf16x4*>(fb + (n + 16 * (ga + 1)) * 16 + half) = (bf16x4){v[4], v[5], v[6], v[7]};
+            }
+        }
+    };
+
+    f32x4 yacc[NB][TB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) yacc[nb][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // A 32-hidden step: layer 0's fragments are read from LDS before its
+    // products (all at once, so one LDS round trip per step), then step st-1's
+    // layer-1 products (independent of this step's results), then this
+    // step's SiLU, in stages across its 8 TB values per lane so that the
+    // exponentials and reciprocals of different values overlap.
+    auto layer0 = [&](const char* cur, int st, f32x4 (&hacc)[2][TB]) {
+        bf16x8 w[2][KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+                w[hb][ks] = *reinterpret_cast<const bf16x8*>(cur + (((2 * st + hb) * KS + ks) * 64 + lane) * 16);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) hacc[hb][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) mma(hacc[hb][tb], w[hb][ks], qf[tb][ks]);
+    };
+    auto silu = [&](const f32x4 (&hacc)[2][TB], bf16x8 (&hf)[TB]) {
+        constexpr int NV = 8 * TB;
+        float z[NV], e[NV];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                z[8 * tb + i] = hacc[0][tb][i];
+                z[8 * tb + 4 + i] = hacc[1][tb][i];
+            }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) e[v] = __expf(-z[v]);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) e[v] = __builtin_amdgcn_rcpf(1.0f + e[v]);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) hf[tb][i] = (bf16)(z[8 * tb + i] * e[8 * tb + i]);
+    };
+    auto layer1 = [&](const char* l1, int st, const bf16x8 (&hf)[TB]) {
+        bf16x8 w[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            w[nb] = *reinterpret_cast<const bf16x8*>(l1 + ((nb * SPC + st) * 64 + lane) * 16);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) mma(yacc[nb][tb], w[nb], hf[tb]);
+    };
+    fetch(0);
+    put(lds);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const char* cur = lds + (c & 1) * (CP * 16);
+        if (c + 1 < nch) fetch(c + 1);
+        const char* l1 = cur + W0P * 16;
+        if constexpr (PIPE) {
+            bf16x8 hf[2][TB];
+#pragma unroll
+            for (int st = 0; st < SPC; ++st) {
+                f32x4 hacc[2][TB];
+                layer0(cur, st, hacc);
+                if (st > 0) layer1(l1, st - 1, hf[(st - 1) & 1]);
+                silu(hacc, hf[st & 1]);
+            }
+            layer1(l1, SPC - 1, hf[(SPC - 1) & 1]);
+        } else {
+#pragma unroll
+            for (int st = 0; st < SPC; ++st) {
+                f32x4 hacc[2][TB];
+                bf16x8 hf[TB];
+                layer0(cur, st, hacc);
+                silu(hacc, hf);
+                layer1(l1, st, hf);
+            }
+        }
+        if (c + 1 < nch) put(lds + ((c + 1) & 1) * (CP * 16));
+        __syncthreads();
+    }
+    // y: a lane holds outputs 16nb + 4g .. +3 of token r0 + 16tb + col
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const int t = r0 + 16 * tb + col;
+        if (t < a.nrows) {
+            float* yp = a.y + tok_off(a.tl, s, a.t0 + t) + 4 * g;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4*>(yp + 16 * nb) = yacc[nb][tb];
+        }
+    }
+}
+
+bool mlp2_fits(int d, int h) { return d >= 32 && d <= 128 && d % 32 == 0 && h >= 64 && h % 64 == 0; }
+
+template <int D, int TB, int WAVES, int HC, bool PIPE>
+static void launch_mlp2_as(const Mlp2Args& a, int ns, hipStream_t st) {
+    constexpr int CP = (HC / 16) * (D / 32) * 64 + (D / 16) * (HC / 32) * 64;
+    const dim3 grid((a.nrows + WAVES * TB * 16 - 1) / (WAVES * TB * 16), ns);
+    launch_k((mlp2_kernel<D, TB, WAVES, HC, PIPE>), grid, dim3(WAVES * 64), 2 * CP * 16, st, a);
+}
+
+// 4 waves of 2 token blocks (128 rows) per workgroup, 64-hidden chunks,
+// layer 1 of a step behind layer 0 of the next: 2 workgroups per compute unit
+// (232 registers a lane, 64 KB of LDS).  Measured on 64 streams of
+// 128 -> 512 -> 128 over 32768 rows: 767 us; without the step pipelining
+// 778 us; 8 waves with 128-hidden chunks 809 us; 4 token blocks a wave (one
+// wave a SIMD) 1171 us.
+template <int D>
+static void launch_mlp2_d(const Mlp2Args& a, int ns, hipStream_t st) {
+    launch_mlp2_as<D, 2, 4, 64, true>(a, ns, st);
+}
+
+hipError_t launch_mlp2(const Mlp2Args& a, int ns, hipStream_t st) {
+    if (a.nrows <= 0) return hipSuccess;
+    if (!mlp2_fits(a.d, a.h) || a.tl.d != a.d || ns < 1 || ns > 65535 || (a.xcd_streams && ns % 8 != 0))
+        return hipErrorInvalidValue;
+    switch (a.d) {
+        case 32: launch_mlp2_d<32>(a, ns, st); break;
+        case 64: launch_mlp2_d<64>(a, ns, st); break;
+        case 96: launch_mlp2_d<96>(a, ns, st); break;
+        default: launch_mlp2_d<128>(a, ns, st); break;
     }
     return hipGetLastError();
 }

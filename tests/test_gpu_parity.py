@@ -176,6 +176,14 @@ RET_CASES = [
     small("ret_rows_2pass", 64, 2, 4, 16, 1, 2, 2100, "bf16"),
     small("ret_rows_ragged", 96, 3, 3, 16, 2, 1, 1000, "bf16"),
     small("ret_rows_lin", 128, 1, 1, 16, 1, 1, 512, "bf16"),
+    # depth 2 at widths up to 128: both layers in one launch (mlp2_kernel):
+    # widths 32 to 128, hidden 64 (one 64-unit weight chunk), 192 (an odd
+    # number of chunks) and 512, row counts with a ragged last row block or
+    # under one 16-row block, 8 streams (grouped by XCD) and fewer
+    small("ret_mlp2_d128", 128, 2, 4, 64, 2, 4, 600, "bf16"),
+    small("ret_mlp2_d64_h192", 64, 2, 3, 16, 1, 2, 300, "bf16"),
+    small("ret_mlp2_d96", 96, 2, 2, 16, 2, 1, 77, "bf16"),
+    small("ret_mlp2_d32_h64", 32, 2, 2, 4, 1, 1, 5, "bf16"),
 ]
 
 

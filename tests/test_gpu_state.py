@@ -114,3 +114,27 @@ def test_compute_calls_refuse_a_mismatched_state():
     assert T.tm_state_check(g.ctx, big, 2, 1) == (False, 32)
     T.tm_destroy(other)
     g.close()
+
+
+def test_tm_log_prints_the_call_shape_and_plan():
+    # TM_LOG=1: a new call shape and its launch plan are printed (stderr);
+    # TM_LOG=2 also prints the capture and the replays
+    import os
+    import subprocess
+    import sys
+    code = ("import sys, os\n"
+            "sys.path.insert(0, %r)\n"
+            "from test_trained_neural_amd import inputs as I\n"
+            "from tests.harness import GpuMemory, dev_inputs\n"
+            "wl = I.Workload('log', batch=1, seq=32, heads=1, dim=32, depth=2, expansion=2, chunk=16, dtype='bf16',"
+            " offsets=(-4.0, 1.0, -4.0))\n"
+            "p = I.make_params(wl); g = GpuMemory(wl, p); d = dev_inputs(I.make_call(wl, p), 'bf16')\n"
+            "for _ in range(3): g.forward(d)\n"
+            "import torch; torch.cuda.synchronize()\n") % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for lvl, want in (("1", ["[tm] new call shape: tm_forward", "[tm] plan: 2 chunks of 16"]),
+                      ("2", ["[tm] capture call tm_forward", "[tm] replay call tm_forward"])):
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                           env=dict(os.environ, TM_LOG=lvl))
+        assert r.returncode == 0, r.stderr[-2000:]
+        for w in want:
+            assert w in r.stderr, (lvl, w, r.stderr[-2000:])

@@ -115,7 +115,8 @@ def test_multihead1024_workload():
     # 8 x 32768 tokens, 8 heads of dim 128 = 64 streams.  Oracle: all 64
     # streams over the first 2048 tokens (y and state), then the last chunk's
     # retrieval of every stream against the oracle's read of the GPU's final
-    # state; the whole call as one call and as 2048 + 30720 (bitwise identical)
+    # state; the whole call as one call and as 2048 + 30720 (bitwise
+    # identical); a read-only retrieval of the whole call from the final state
     wl = I.WORKLOADS["multihead1024"]
     say("case", wl)
     p = I.make_params(wl)
@@ -144,8 +145,23 @@ def test_multihead1024_workload():
     y_one = h.forward(d).cpu().numpy()
     assert np.array_equal(h.export(), st)
     assert np.array_equal(y_one, y_full)
-    g.close()
     h.close()
+    # read-only retrieval of the whole call's queries (64 streams x 32768
+    # rows, one launch) from the final state: every stream at 144 sampled
+    # rows (128 random, the last 16) against the oracle's read of that state
+    y_ret = g.retrieve(d["q"]).cpu().numpy()
+    assert np.all(np.isfinite(y_ret))
+    rng = np.random.default_rng(11)
+    worst = 0.0
+    for (bi, hi) in every:
+        s = bi * wl.heads + hi
+        rows = np.concatenate([np.sort(rng.choice(wl.seq - 16, 128, replace=False)), np.arange(wl.seq - 16, wl.seq)])
+        q = np.ascontiguousarray(ci.q[bi:bi + 1, rows, hi:hi + 1])
+        yr = tmref.retrieve(wl.dim, wl.depth, wl.expansion, st[s:s + 1].astype(np.float64), q)
+        worst = max(worst, yerr(y_ret[bi:bi + 1, rows, hi:hi + 1], yr))
+    say("  retrieve of the whole call, every stream at 144 rows: y %.2e" % worst)
+    assert worst < TOL["bf16"]
+    g.close()
 
 
 def test_deep512_prefix():
