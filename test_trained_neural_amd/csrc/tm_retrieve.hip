@@ -146,12 +146,14 @@ hipError_t launch_rows(const GemmArgs& g, int ns, hipStream_t st) {
 // y = SiLU(q W_0) W_1 with the hidden activations kept in registers.
 //
 // Both layers run transposed, H^T = W_0^T q^T and y^T = W_1^T H^T.  A lane's
-// share of a layer-0 result tile is 4 consecutive hidden units of one token,
-// and two such tiles (hidden 32k .. 32k+15 and 32k+16 .. 32k+31) make the
-// lane's 8 values of a layer-1 B fragment for the 32-deep step k, in the K
-// order {4g .. 4g+3, 16+4g .. 16+4g+3} for lane group g.  The order inside a
-// step is free as long as A and B use the same one, so W_1's fragments are
-// put into LDS in that order and nothing is moved between the layers.
+// share of a layer-0 result tile is 4 rows of one token, and a layer-1 B
+// fragment wants 8 consecutive hidden units of one token (lane group g of
+// the 32-deep step: units 8g .. 8g+7).  So the two layer-0 tiles of a step
+// take the step's hidden units in the order 8(i/4) + 4hb + i%4 for row i of
+// tile hb: lane group g then holds units 8g .. 8g+3 in tile 0 and 8g+4 ..
+// 8g+7 in tile 1, exactly its B fragment.  Only the rows of W_0's fragments
+// are gathered in that order when the chunk is loaded; W_1's fragments are
+// copied as they are stored, and nothing moves between the layers.
 //
 // A workgroup owns WAVES x TB 16-token blocks of one stream; a wave keeps its
 // TB blocks of queries as B fragments (all d/32 steps) and TB x d/16
@@ -166,7 +168,6 @@ void mlp2_kernel(Mlp2Args a) {
     constexpr int W1P = NB * SPC * 64;         // ... and of its W_1 fragments
     constexpr int CP = W0P + W1P;
     constexpr int RND = (CP + NT - 1) / NT;
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     extern __shared__ __attribute__((aligned(16))) char lds[];   // 2 chunks of CP pieces
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, col = lane & 15;
@@ -204,7 +205,12 @@ void mlp2_kernel(Mlp2Args a) {
         for (int p = 0; p < RND; ++p) {
             const int o = p * NT + tid;
             if (o < W0P) {
-                stg[p] = ld8(w0 + (long)c * (W0P * 8) + o * 8);
+                // A-fragment row i of the step's hidden block hb is hidden
+                // unit 8(i/4) + 4hb + i%4 of the step: 8 consecutive inputs
+                // of one hidden unit, contiguous in the packed copy
+                const int f0 = o >> 6, L = o & 63, hbl = f0 / KS, ks = f0 % KS, i = L & 15;
+                const int j = c * HC + 32 * (hbl >> 1) + 8 * (i >> 2) + 4 * (hbl & 1) + (i & 3);
+                stg[p] = ld8(w0 + pk(j, 32 * ks + 8 * (L >> 4), KS));
             } else if (o < CP) {
                 const int o1 = o - W0P, f = o1 >> 6;
                 stg[p] = ld8(w1 + pkf(f / SPC, SPC * c + f % SPC, nks1, o1 & 63));
@@ -215,19 +221,7 @@ void mlp2_kernel(Mlp2Args a) {
 #pragma unroll
         for (int p = 0; p < RND; ++p) {
             const int o = p * NT + tid;
-            if (o < W0P) {
-                *reinterpret_cast<bf16x8*>(buf + o * 16) = stg[p];
-            } else if (o < CP) {
-                // the piece holds inputs 8gp .. 8gp+7 of output row n: the
-                // first four go to lane group 2(gp&1), the last four to the
-                // group after it, in slots 0..3 (gp < 2) or 4..7
-                const int o1 = o - W0P, L = o1 & 63, n = L & 15, gp = L >> 4;
-                const int ga = 2 * (gp & 1), half = (gp >> 1) * 8;
-                char* fb = buf + W0P * 16 + (o1 >> 6) * 1024;
-                const bf16x8 v = stg[p];
-                *reinterpret_cast<bf16x4*>(fb + (n + 16 * ga) * 16 + half) = (bf16x4){v[0], v[1], v[2], v[3]};
-                *reinterpret_cast<bf16x4*>(fb + (n + 16 * (ga + 1)) * 16 + half) = (bf16x4){v[4], v[5], v[6], v[7]};
-            }
+            if (o < CP) *reinterpret_cast<bf16x8*>(buf + o * 16) = stg[p];
         }
     };
 
