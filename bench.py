@@ -405,8 +405,8 @@ def backward_line(name, steps, oracle=False):
                            "frac": gbs / HBM_PEAK_GBS, "kernel": "bgemm_kernel (state streaming)",
                            "launches": n_s, "avg_us": ms_s * 1e3 / max(n_s, 1), "bytes_per_launch": by / max(n_s, 1)}
     else:
-        out["roofline"] = {"bound": "alu", "achieved": tfl, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": tfl / FP32_PEAK_TFLOPS, "kernel": "bgemm_kernel (products, fp32 FMA)",
+        out["roofline"] = {"bound": "mfma", "achieved": tfl, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tfl / FP32_PEAK_TFLOPS, "kernel": "bgemm_kernel (products, fp32 matrix cores)",
                            "launches": n_r, "avg_us": ms_r * 1e3 / max(n_r, 1), "flops_per_launch": fl / max(n_r, 1)}
     out["roofline"]["timing"] = "HIP events recorded with each launch's own dispatch, second pass of the same steps"
     T.tm_destroy(ctx)

@@ -26,7 +26,8 @@ namespace {
 constexpr int BT = 64;    // output tile: BT x BT, 256 threads of 4 x 4
 constexpr int BKS = 16;   // K per LDS stage
 constexpr int BPAD = 4;
-constexpr int NST = 4;    // K steps whose loads are in flight together
+constexpr int NST = 4;    // K steps whose loads are in flight together (even: consumed in pairs)
+static_assert(NST % 2 == 0, "K steps are consumed in pairs");
 constexpr int MAXSPLIT = 8;   // most K slices of a split product
 
 __device__ __forceinline__ float silu_d(float z) {
@@ -144,8 +145,14 @@ struct Stage {
 template <int TA, int TB, bool PRE, int PHASE>
 __global__ __launch_bounds__(256) void bgemm_kernel(BGemm g) {
     constexpr int phase = PHASE;
-    __shared__ __attribute__((aligned(16))) float As[BKS][BT + BPAD];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BKS][BT + BPAD];
+    // the K stages' A and B tiles; after the K loop the same memory holds
+    // the matrix instructions' accumulator tiles on their way to the
+    // epilogue's layout
+    // (two K steps of BKS per barrier: rows 0 .. BKS-1 and BKS .. 2 BKS-1)
+    __shared__ __attribute__((aligned(16))) float lds_raw[2 * BT * (BT + 1)];
+    static_assert(3 * 2 * BKS * (BT + BPAD) <= 2 * BT * (BT + 1), "stage tiles fit the transfer tiles");
+    float(*As)[BT + BPAD] = reinterpret_cast<float(*)[BT + BPAD]>(lds_raw);
+    float(*Bs)[2 * BKS][BT + BPAD] = reinterpret_cast<float(*)[2 * BKS][BT + BPAD]>(lds_raw + 2 * BKS * (BT + BPAD));
     __shared__ float red[4][3];
     const int split = phase == 1 ? g.splitk : 1;
     const int s = blockIdx.z / split, slice = blockIdx.z - s * split;
@@ -190,6 +197,18 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm g) {
                 acc1[i] += p1[sl][i];
             }
     } else {
+        // the products on the matrix cores (fp32 16 x 16 x 4): wave w owns
+        // the 32 x 32 quarter (w / 2, w % 2) of the tile as 2 x 2 blocks; a
+        // lane supplies A[row l % 16][k l / 16] and B[k l / 16][column l % 16]
+        // of each 4-deep step and holds rows 4 (l / 16) .. +3 of column l % 16
+        // of each block
+        const int lane = tid & 63, wave = tid >> 6;
+        const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32, lr = lane & 15, lk = lane >> 4;
+        f32x4 mc0[2][2], mc1[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mc0[i][j] = mc1[i][j] = zero4();
         // one K segment: A'B' over [kb, ke) of K (the second segment, if
         // any, takes A2, Bs2 and never the second accumulator)
         auto segment = [&](const BMat A, const BMat B, int K, bool second) __attribute__((always_inline)) {
@@ -208,23 +227,35 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm g) {
 #pragma unroll
                 for (int i = 0; i < NST; ++i)
                     if (g0 + i * BKS < ke) st[i].load(g, A, B, second, s, m0, n0, g0 + i * BKS, ke);
+                auto steps = [&](int kb0) __attribute__((always_inline)) {
 #pragma unroll
-                for (int i = 0; i < NST; ++i) {
-                    if (g0 + i * BKS >= ke) continue;   // (uniform: the whole workgroup skips)
-                    st[i].store(As, Bs[0], Bs[1], two);
-                    __syncthreads();
-#pragma unroll 4
-                    for (int kk = 0; kk < BKS; ++kk) {
-                        const f32x4 a = *reinterpret_cast<const f32x4*>(&As[kk][ty * 4]);
-                        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&Bs[0][kk][tx * 4]);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) acc0[j] += a[j] * b0;
+                    for (int k4 = 0; k4 < BKS; k4 += 4) {
+                        const int kr = kb0 + k4 + lk;
+                        const float a0 = As[kr][wm + lr], a1 = As[kr][wm + 16 + lr];
+                        const float b0 = Bs[0][kr][wn + lr], b1 = Bs[0][kr][wn + 16 + lr];
+                        mc0[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, mc0[0][0], 0, 0, 0);
+                        mc0[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, mc0[0][1], 0, 0, 0);
+                        mc0[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, mc0[1][0], 0, 0, 0);
+                        mc0[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, mc0[1][1], 0, 0, 0);
                         if (two) {
-                            const f32x4 b1 = *reinterpret_cast<const f32x4*>(&Bs[1][kk][tx * 4]);
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) acc1[j] += a[j] * b1;
+                            const float c0 = Bs[1][kr][wn + lr], c1 = Bs[1][kr][wn + 16 + lr];
+                            mc1[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, c0, mc1[0][0], 0, 0, 0);
+                            mc1[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, c1, mc1[0][1], 0, 0, 0);
+                            mc1[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, c0, mc1[1][0], 0, 0, 0);
+                            mc1[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, c1, mc1[1][1], 0, 0, 0);
                         }
                     }
+                };
+                // two K steps per pair of barriers
+#pragma unroll
+                for (int i = 0; i < NST; i += 2) {
+                    if (g0 + i * BKS >= ke) continue;   // (uniform: the whole workgroup skips)
+                    const bool pair = g0 + (i + 1) * BKS < ke;
+                    st[i].store(As, Bs[0], Bs[1], two);
+                    if (pair) st[i + 1].store(As + BKS, Bs[0] + BKS, Bs[1] + BKS, two);
+                    __syncthreads();
+                    steps(0);
+                    if (pair) steps(BKS);
                     __syncthreads();
                 }
             }
@@ -235,6 +266,29 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm g) {
         if constexpr (PRE) {
             if (g.k2 > 0) segment(g.A2, g.Bs2, g.k2, true);
         }
+        // the accumulator tiles through LDS into the epilogue's layout
+        // (thread: rows ty*4 .. +3, columns tx*4 .. +3); the K loop ended
+        // with a barrier, so the stage tiles are free
+        float(*Cs)[BT][BT + 1] = reinterpret_cast<float(*)[BT][BT + 1]>(lds_raw);
+        const bool dual = g.dual != 0;
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = wm + 16 * bi + 4 * lk + e, c = wn + 16 * bj + lr;
+                    Cs[0][r][c] = mc0[bi][bj][e];
+                    if (dual) Cs[1][r][c] = mc1[bi][bj][e];
+                }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc0[i][j] = Cs[0][ty * 4 + i][tx * 4 + j];
+                acc1[i][j] = dual ? Cs[1][ty * 4 + i][tx * 4 + j] : 0.f;
+            }
         if constexpr (PHASE == 1) {
             float* p = g.acc + ((long)(s * g.splitk + slice) * tiles + tile) * 8192;
 #pragma unroll
