@@ -768,29 +768,29 @@ constexpr int WPAD = 8;     // LDS row padding (elements)
 constexpr int RPAD = 1;     // LDS row padding of the partial-sum tiles (floats)
 constexpr int FW = 8;       // waves of a first-layer workgroup
 
-constexpr int FRED = FW / 2;   // partial tiles kept in LDS (two-round reduction)
+// (a workgroup of NW waves keeps NW / 2 partial tiles in LDS: two-round reduction)
 constexpr size_t UPD_TILE_LDS = 2 * 2 * 64 * 65 * 4;   // the two halves' update tiles: U_M, U_S each
 // Update tiles per workgroup: two per half (both tiles' loads in flight
 // together) where the register budget holds them, one per half in the
 // half-occupancy (small) and fp32 variants.
 __host__ __device__ constexpr int upd_tpw(bool f32, bool small) { return (!f32 && !small) ? 4 : 2; }
 
-static size_t first_lds_bytes(int dim, int bp, int f32) {
+static size_t first_lds_bytes(int dim, int bp, int f32, int nw) {
     const size_t e = f32 ? 4 : 2;
     (void)bp;
     return (size_t)JW * (dim + WPAD) * e + 2 * (size_t)JW * (MAX_CHUNK + WPAD) * e +
-           (size_t)FRED * 128 * (JW + RPAD) * 4;
+           (size_t)(nw / 2) * 128 * (JW + RPAD) * 4;
 }
 
-// The waves' partial tiles acc (nb row blocks of 16 x JW) summed into FRED
-// LDS slots in two rounds: waves FRED.. store theirs, waves 0..FRED-1 add
-// their own.  Ends with a barrier; the caller sums the FRED slots.
-template <int NB>
+// The waves' partial tiles acc (nb row blocks of 16 x JW) summed into FR
+// LDS slots in two rounds: waves FR.. store theirs, waves 0..FR-1 add
+// their own.  Ends with a barrier; the caller sums the FR slots.
+template <int NB, int FR>
 __device__ __forceinline__ void partial_tiles(float* red, const f32x4* acc, int nb, int rows, int wave, int lane,
                                               int RP) {
     const int g4 = 4 * (lane >> 4), jl = lane & 15;
-    float* slot = red + (wave % FRED) * rows * RP;
-    if (wave >= FRED) {
+    float* slot = red + (wave % FR) * rows * RP;
+    if (wave >= FR) {
 #pragma unroll
         for (int m = 0; m < NB; ++m)
             if (m < nb)
@@ -798,7 +798,7 @@ __device__ __forceinline__ void partial_tiles(float* red, const f32x4* acc, int 
                 for (int e = 0; e < 4; ++e) slot[(16 * m + g4 + e) * RP + jl] = acc[m][e];
     }
     __syncthreads();
-    if (wave < FRED) {
+    if (wave < FR) {
 #pragma unroll
         for (int m = 0; m < NB; ++m)
             if (m < nb)
@@ -811,13 +811,16 @@ __device__ __forceinline__ void partial_tiles(float* red, const f32x4* acc, int 
 // Prefetch depths (in K steps or row blocks) of the first-layer workgroup:
 // everything a wave needs is requested at kernel start when it fits the
 // register file, so each phase waits for at most one round of memory.
-// SMALL (dim and layer 1's outputs at most 128): every wave has one K step
-// or row block per phase, so depth 1 everywhere and two workgroups per
-// compute unit (the register budget halves).
-template <class OP, bool SMALL> struct FirstDepth;
-template <> struct FirstDepth<bf16, false> { static constexpr int A = 2, B = 3, C = 2, N = 3; };
-template <> struct FirstDepth<float, false> { static constexpr int A = 1, B = 2, C = 1, N = 3; };
-template <class OP> struct FirstDepth<OP, true> { static constexpr int A = 1, B = 1, C = 1, N = 1; };
+// SMALL (dim and layer 1's outputs at most 128): with 8 waves every wave has
+// one K step or row block per phase, so depth 1 everywhere and two
+// workgroups per compute unit (the register budget halves); with 4 waves
+// (launches without other roles) two row blocks and two W_1 blocks per
+// wave, one K step, three workgroups per compute unit.
+template <class OP, bool SMALL, int NW> struct FirstDepth;
+template <> struct FirstDepth<bf16, false, 8> { static constexpr int A = 2, B = 3, C = 2, N = 3; };
+template <> struct FirstDepth<float, false, 8> { static constexpr int A = 1, B = 2, C = 1, N = 3; };
+template <class OP> struct FirstDepth<OP, true, 8> { static constexpr int A = 1, B = 1, C = 1, N = 1; };
+template <class OP> struct FirstDepth<OP, true, 4> { static constexpr int A = 1, B = 2, C = 1, N = 2; };
 constexpr int SMALL_DIM = 128;
 
 // W_1's update as a workgroup role of its own (depth 2, with workgroups to
@@ -957,12 +960,14 @@ __device__ void w1_rows(const FirstArgs& a, int s, int wg, char* lds) {
 // top in consumption order: a load whose only use sits behind a run-time
 // branch would be moved down to that use, and a branch or loop around a use
 // makes the compiler wait for every load in flight.
-template <class OP, bool UPD, bool FWD, bool DEEP, bool SPLIT, bool SMALL>
-__global__ __launch_bounds__(FW * 64) __attribute__((amdgpu_waves_per_eu(SMALL ? 4 : 1)))
+template <class OP, bool UPD, bool FWD, bool DEEP, bool SPLIT, bool SMALL, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(SMALL ? (NW == 4 ? 3 : 4) : 1)))
 void first_layer_kernel(FirstArgs a) {
     typedef typename Frag<OP>::T F;
-    constexpr int PA = FirstDepth<OP, SMALL>::A, PB = FirstDepth<OP, SMALL>::B, PC = FirstDepth<OP, SMALL>::C;
-    constexpr int NT = FW * 64;
+    static_assert(NW == 8 || (NW == 4 && SMALL && !SPLIT), "4-wave workgroups: small dims, no other roles");
+    constexpr int PA = FirstDepth<OP, SMALL, NW>::A, PB = FirstDepth<OP, SMALL, NW>::B, PC = FirstDepth<OP, SMALL, NW>::C;
+    constexpr int NT = NW * 64;
+    constexpr int FR = NW / 2;   // partial tiles kept in LDS
     constexpr bool BWD = UPD && DEEP;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     if ((int)blockIdx.x >= a.nb1) {
@@ -976,7 +981,7 @@ void first_layer_kernel(FirstArgs a) {
         // LDS tiles of their own, every tile's loads requested before the
         // first is computed; they touch nothing the first-layer blocks read
         // or write
-        if constexpr (UPD && DEEP) {
+        if constexpr (UPD && DEEP && NW == 8) {
             const int half = threadIdx.x >> 8, tid = threadIdx.x & 255;
             constexpr int TPW = upd_tpw(sizeof(OP) == 4, SMALL);
             const int t0 = TPW * ((int)blockIdx.x - a.nb1) + half;   // tiles t0, t0 + 2, ...
@@ -1015,7 +1020,7 @@ void first_layer_kernel(FirstArgs a) {
     OP* Wn = reinterpret_cast<OP*>(lds);   // [JW][WP]: the block's columns of W_0, K-contiguous
     OP* DcT = Wn + JW * WP;                 // [JW][DP]: (c Delta_0)^T of chunk c-1
     OP* DdT = DcT + JW * DP;
-    float* red = reinterpret_cast<float*>(DdT + JW * DP);   // [FRED][rows][RP] partial tiles
+    float* red = reinterpret_cast<float*>(DdT + JW * DP);   // [FR][rows][RP] partial tiles
     float* M0 = u.M + (long)s * u.P;
     float* S0 = u.S + (long)s * u.P;
     bf16* Wt0 = reinterpret_cast<bf16*>(u.Wt) + (long)s * u.P;
@@ -1036,7 +1041,7 @@ void first_layer_kernel(FirstArgs a) {
     }
     // (1) the in-place backward's operands: Delta_1 rows (4 token blocks) and
     //     the lane's column of W_1, K split over the waves
-    const int nsA = BWD ? u.dout[1] >> 5 : 1, qA = (nsA + FW - 1) / FW;
+    const int nsA = BWD ? u.dout[1] >> 5 : 1, qA = (nsA + NW - 1) / NW;
     const int kbA = wave * qA, keA = min(nsA, kbA + qA), klA = max(keA - 1, 0);
     const OP* Ad[4];
     const float* Bm = nullptr;
@@ -1074,16 +1079,16 @@ void first_layer_kernel(FirstArgs a) {
             dv[q] = a.dc_prev[(long)s * a.coef_ss + t];
         }
     }
-    // (3) the update's row blocks of this wave (block wave + FW * p): keys^T
+    // (3) the update's row blocks of this wave (block wave + NW * p): keys^T
     //     fragments, M and S; blocks past the matrix are clamped and dropped
-    const int mineB = (nrb - wave + FW - 1) / FW;
+    const int mineB = (nrb - wave + NW - 1) / NW;
     // (the lane's 4 values of a 16 x 16 block of M or S are one float4 at
     // mso(rbk), the wave's block 1 KB contiguous)
     auto mso = [&](int rbk) { return ((long)(bx * nrb + rbk) * 64 + lane) * 4; };
     F kf[PB][2];
     f32x4 mr[PB], sr[PB];
     auto load_rb = [&](int p, int n) {
-        const int rbk = min(wave + FW * n, nrb - 1);
+        const int rbk = min(wave + NW * n, nrb - 1);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             kf[p][ks] = keep_if(cvt<OP>(ld8(kt + pkf(rbk, min(ks, nkb - 1), nkb, lane))), ks < nkb);
@@ -1102,7 +1107,7 @@ void first_layer_kernel(FirstArgs a) {
     //     free (issued earlier, the prefetched set would not fit the register
     //     file), and still have the whole update phase to arrive.
     const int R = a.nq + a.nk;
-    const int nsC = d >> 5, qC = (nsC + FW - 1) / FW;
+    const int nsC = d >> 5, qC = (nsC + NW - 1) / NW;
     const int kbC = wave * qC, keC = min(nsC, kbC + qC), klC = max(keC - 1, 0);
     const OP* Ax[8];
     bool rok[8];
@@ -1129,14 +1134,14 @@ void first_layer_kernel(FirstArgs a) {
     // (5) chunk c-1's update of rows j0 .. j0+15 of W_1 (depth >= 2), its
     //     operands requested once the forward's registers are free.  It is
     //     computed transposed, U^T = (c Delta_1)^T H_1 (rows: layer 1's
-    //     outputs n in 16-blocks nb = wave, wave + FW, ...; columns: the
+    //     outputs n in 16-blocks nb = wave, wave + NW, ...; columns: the
     //     block's inputs j; K: tokens), so a lane's 4 results are outputs
     //     n .. n+3 of one input j: one float4 of M and S in their accumulator
     //     order.
     constexpr bool W1 = UPD && DEEP && !SPLIT;
-    constexpr int PN = FirstDepth<OP, SMALL>::N;   // n-blocks per wave held in registers
+    constexpr int PN = FirstDepth<OP, SMALL, NW>::N;   // n-blocks per wave held in registers
     const int d1 = DEEP ? u.dout[1] : 16, ncb1 = d1 >> 4;
-    const int mine1 = (ncb1 - wave + FW - 1) / FW;
+    const int mine1 = (ncb1 - wave + NW - 1) / NW;
     F h1f[2], c1f[PN][2], d1f[PN][2];
     f32x4 m1r[PN], s1r[PN];
     const OP* at1 = DEEP ? reinterpret_cast<const OP*>(u.at[1]) + (long)s * u.at_ss[1] : nullptr;
@@ -1147,7 +1152,7 @@ void first_layer_kernel(FirstArgs a) {
     float* S1 = u.S + (long)s * u.P + (DEEP ? u.off[1] : 0);
     auto mso1 = [&](int nb) { return ((long)(bx * ncb1 + nb) * 64 + lane) * 4; };
     auto load_w1 = [&](int p, int n) {
-        const int nb = min(wave + FW * n, ncb1 - 1);
+        const int nb = min(wave + NW * n, ncb1 - 1);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int kc = min(ks, nkb - 1), t0 = ks * 32 + kofs;
@@ -1168,7 +1173,7 @@ void first_layer_kernel(FirstArgs a) {
         }
     };
     auto update1 = [&](int p, int n, bool live) {
-        const int nb = min(wave + FW * n, ncb1 - 1);
+        const int nb = min(wave + NW * n, ncb1 - 1);
         f32x4 um = (f32x4){0.f, 0.f, 0.f, 0.f}, us = um;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -1230,14 +1235,14 @@ void first_layer_kernel(FirstArgs a) {
                 for (int m = 0; m < 4; ++m) mma(acc[m], tok[m] ? av[m] : zero_frag<OP>(), bv);
             }
             issue_rows();
-            partial_tiles<4>(red, acc, 4, 64, wave, lane, RP);
+            partial_tiles<4, FR>(red, acc, 4, 64, wave, lane, RP);
             // theta-weighted, into LDS (token slots past the chunk get zeros)
 #pragma unroll
             for (int q = 0; q < EA; ++q) {
                 const int idx = tid + NT * q, t = idx / JW, cl = idx % JW;
                 float z = 0.f;
 #pragma unroll
-                for (int w = 0; w < FRED; ++w) z += red[(w * 64 + t) * RP + cl];
+                for (int w = 0; w < FR; ++w) z += red[(w * 64 + t) * RP + cl];
                 const float dl = t < b ? z * sl[q] : 0.f;
                 DcT[cl * DP + t] = (OP)(cv[q] * dl);
                 DdT[cl * DP + t] = (OP)(dv[q] * dl);
@@ -1262,7 +1267,7 @@ void first_layer_kernel(FirstArgs a) {
         __syncthreads();
 
         // U = K^T diag(c) Delta_0 and the momentum / forgetting write, 16-row
-        // blocks (block w, w+FW, ... for wave w)
+        // blocks (block w, w+NW, ... for wave w)
         F bc[2], bd[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -1271,7 +1276,7 @@ void first_layer_kernel(FirstArgs a) {
             bd[ks] = on ? *reinterpret_cast<const F*>(&DdT[jl * DP + ks * 32 + kofs]) : zero_frag<OP>();
         }
         auto update_rb = [&](int p, int n, bool live) {
-            const int rbk = min(wave + FW * n, nrb - 1), ib = 16 * rbk;
+            const int rbk = min(wave + NW * n, nrb - 1), ib = 16 * rbk;
             f32x4 um = (f32x4){0.f, 0.f, 0.f, 0.f}, us = um;
             mma(um, kf[p][0], bc[0]);
             mma(us, kf[p][0], bd[0]);
@@ -1302,7 +1307,7 @@ void first_layer_kernel(FirstArgs a) {
                 }
             }
         };
-        // the prefetched row blocks, then (dim above 16 * FW * PB only) the
+        // the prefetched row blocks, then (dim above 16 * NW * PB only) the
         // rest, each loaded and used
 #pragma unroll
         for (int p = 0; p < PB; ++p) update_rb(p, p, p < mineB);
@@ -1360,7 +1365,7 @@ void first_layer_kernel(FirstArgs a) {
             for (int m = 0; m < 8; ++m) mma(acc[m], rok[m] ? xv[m] : zero_frag<OP>(), bv);
         }
         issue1();   // layer 1's rows: operands now, the update after the epilogue
-        partial_tiles<8>(red, acc, 8, 128, wave, lane, RP);
+        partial_tiles<8, FR>(red, acc, 8, 128, wave, lane, RP);
     }
     if constexpr (DEEP) {
         // z of every (row, column), summed from the partial tiles (slot
@@ -1378,7 +1383,7 @@ void first_layer_kernel(FirstArgs a) {
             for (int e = 0; e < 4; ++e) {
                 float z = 0.f;
 #pragma unroll
-                for (int w = 0; w < FRED; ++w) z += red[(w * 128 + r) * RP + c4 + e];
+                for (int w = 0; w < FR; ++w) z += red[(w * 128 + r) * RP + c4 + e];
                 const float sg = sigmoid(z);
                 hv[e] = (OP)(z * sg);
                 sd[e] = sg * (1.0f + z * (1.0f - sg));
@@ -1407,7 +1412,7 @@ void first_layer_kernel(FirstArgs a) {
             const int r = idx / JW, cl = idx - r * JW;
             float z = 0.f;
 #pragma unroll
-            for (int w = 0; w < FRED; ++w) z += red[(w * 128 + r) * RP + cl];
+            for (int w = 0; w < FR; ++w) z += red[(w * 128 + r) * RP + cl];
             red[r * RP + cl] = z;
         }
         __syncthreads();
@@ -1445,10 +1450,21 @@ void first_layer_kernel(FirstArgs a) {
     if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
 }
 
+static bool first_nw4_on() {
+    static const int v = getenv("TM_FIRST4") ? atoi(getenv("TM_FIRST4")) : 1;
+    return v != 0;
+}
+
 // The half-occupancy variant: bf16 with layer-0 and layer-1 widths within
 // SMALL_DIM (the fp32 operand set does not fit half the register file).
 static bool first_small(const FirstArgs& a, bool f32) {
     return !f32 && a.dim <= SMALL_DIM && (a.u.L < 2 || a.u.dout[1] <= SMALL_DIM);
+}
+
+// The small-dim variant with 4-wave workgroups: launches without workgroups
+// of other roles (no W_1 workgroups, no update tiles).
+static bool first_small4(const FirstArgs& a, bool f32) {
+    return first_small(a, f32) && a.nw1 == 0 && a.upd_ntiles == 0 && first_nw4_on();
 }
 
 template <class OP, bool UPD, bool FWD>
@@ -1457,24 +1473,31 @@ static void launch_first_as(const FirstArgs& a, dim3 grid, size_t lds, hipStream
     // variant's register set would spill)
     if constexpr (UPD && sizeof(OP) == 2) {
         if (a.nw1 > 0) {
-            launch_k((first_layer_kernel<OP, true, FWD, true, true, false>), grid, dim3(FW * 64), lds, st, a);
+            launch_k((first_layer_kernel<OP, true, FWD, true, true, false, 8>), grid, dim3(FW * 64), lds, st, a);
             return;
         }
     }
     const bool small = first_small(a, sizeof(OP) == 4);
     if constexpr (sizeof(OP) == 2) {
+        if (small && first_small4(a, false)) {
+            if (a.u.L >= 2)
+                launch_k((first_layer_kernel<OP, UPD, FWD, true, false, true, 4>), grid, dim3(4 * 64), lds, st, a);
+            else
+                launch_k((first_layer_kernel<OP, UPD, FWD, false, false, true, 4>), grid, dim3(4 * 64), lds, st, a);
+            return;
+        }
         if (small) {
             if (a.u.L >= 2)
-                launch_k((first_layer_kernel<OP, UPD, FWD, true, false, true>), grid, dim3(FW * 64), lds, st, a);
+                launch_k((first_layer_kernel<OP, UPD, FWD, true, false, true, 8>), grid, dim3(FW * 64), lds, st, a);
             else
-                launch_k((first_layer_kernel<OP, UPD, FWD, false, false, true>), grid, dim3(FW * 64), lds, st, a);
+                launch_k((first_layer_kernel<OP, UPD, FWD, false, false, true, 8>), grid, dim3(FW * 64), lds, st, a);
             return;
         }
     }
     if (a.u.L >= 2)
-        launch_k((first_layer_kernel<OP, UPD, FWD, true, false, false>), grid, dim3(FW * 64), lds, st, a);
+        launch_k((first_layer_kernel<OP, UPD, FWD, true, false, false, 8>), grid, dim3(FW * 64), lds, st, a);
     else
-        launch_k((first_layer_kernel<OP, UPD, FWD, false, false, false>), grid, dim3(FW * 64), lds, st, a);
+        launch_k((first_layer_kernel<OP, UPD, FWD, false, false, false, 8>), grid, dim3(FW * 64), lds, st, a);
 }
 
 template <class OP>
@@ -1494,7 +1517,7 @@ hipError_t launch_first(const FirstArgs& a, int ns, int f32, hipStream_t st) {
     const int tpw = upd_tpw(f32, first_small(a, f32));
     const int nupd = (a.upd_ntiles + tpw - 1) / tpw;   // workgroups of update tiles
     dim3 grid(a.nb1 + (a.nw1 > 0 ? a.nw1 : nupd), ns);
-    size_t lds = first_lds_bytes(a.dim, a.u.bp, f32);
+    size_t lds = first_lds_bytes(a.dim, a.u.bp, f32, first_small4(a, f32) ? 4 : 8);
     if (nupd > 0 && lds < UPD_TILE_LDS) lds = UPD_TILE_LDS;
     if (a.nw1 > 0 && lds < W1_LDS) lds = W1_LDS;
     if (f32) launch_first_op<float>(a, grid, lds, st);
