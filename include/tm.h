@@ -38,6 +38,12 @@
  *     argument checks run on the host before anything is launched, so a call
  *     that returns an error has not touched the state.  Non-finite values are
  *     not call errors: they set a sticky flag read by tm_state_check.
+ *   - Environment (read once per process): TM_LOG=1 prints each new call
+ *     shape's configuration and launch plan to stderr, TM_LOG=2 also graph
+ *     captures and replays; TM_XCD_STREAMS=0 and TM_FIRST4=0 turn off,
+ *     for comparison, the grouping of a stream's workgroups on one XCD and
+ *     the 4-wave first-layer workgroups of small widths (results agree to
+ *     rounding).
  *   - A state blob may be used by one stream at a time; a ctx is immutable
  *     and may be shared between threads.
  */
