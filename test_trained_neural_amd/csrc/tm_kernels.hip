@@ -1172,7 +1172,13 @@ void first_layer_kernel(FirstArgs a) {
             for (int p = 0; p < PN; ++p) load_w1(p, p);
         }
     };
-    auto update1 = [&](int p, int n, bool live) {
+    // the bf16 copy of the prefetched output blocks leaves through a
+    // per-wave LDS tile in the partial-tile area (free once W_1's update
+    // runs): a lane holds 4 outputs of one input, the copy stores 8
+    // consecutive inputs of one output per 16 bytes
+    constexpr int TR1 = 24;   // tile row pitch (elements): rows stay 16-byte aligned
+    bf16* t1 = reinterpret_cast<bf16*>(red) + wave * (16 * PN * TR1);
+    auto update1 = [&](int p, int n, bool live, bool tiled) {
         const int nb = min(wave + NW * n, ncb1 - 1);
         f32x4 um = (f32x4){0.f, 0.f, 0.f, 0.f}, us = um;
 #pragma unroll
@@ -1193,18 +1199,29 @@ void first_layer_kernel(FirstArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 bad |= !__builtin_isfinite(mn[e]) || !__builtin_isfinite(sn[e]);
-                Wt1[pk(n0 + e, j, h1 >> 5)] = (bf16)mn[e];
+                if (tiled) t1[(16 * p + g4 + e) * TR1 + jl] = (bf16)mn[e];
+                else Wt1[pk(n0 + e, j, h1 >> 5)] = (bf16)mn[e];
             }
         }
     };
     auto run1 = [&]() {
         if constexpr (W1) {
 #pragma unroll
-            for (int p = 0; p < PN; ++p) update1(p, p, p < mine1);
-            if constexpr (!SMALL)   // (SMALL: one output block per wave)
+            for (int p = 0; p < PN; ++p) update1(p, p, p < mine1, true);
+            // the tile's rows as whole 16-byte pieces (the LDS operations of
+            // one wave complete in order: no barrier)
+            for (int c = lane; c < PN * 32; c += 64) {
+                const int row = c >> 1, half = c & 1, p = row >> 4;
+                if (p < mine1) {
+                    const int nb = min(wave + NW * p, ncb1 - 1);
+                    const bf16x8 v = *reinterpret_cast<const bf16x8*>(&t1[row * TR1 + 8 * half]);
+                    *reinterpret_cast<bf16x8*>(Wt1 + pk(nb * 16 + (row & 15), j0 + 8 * half, h1 >> 5)) = v;
+                }
+            }
+            if constexpr (!SMALL)   // (SMALL: every output block prefetched)
             for (int n = PN; n < mine1; ++n) {
                 load_w1(0, n);
-                update1(0, n, true);
+                update1(0, n, true, false);
             }
         }
     };
@@ -1446,6 +1463,7 @@ void first_layer_kernel(FirstArgs a) {
             }
         }
     }
+    if (a.nk == 0) __syncthreads();   // (uniform) the epilogue's reads of the partial tiles are done
     run1();
     if (__ballot(bad) != 0 && lane == 0) atomicOr(u.flag, 1);
 }
