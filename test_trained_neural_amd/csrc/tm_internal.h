@@ -196,7 +196,8 @@ struct UpdArgs {
 //     keys of chunk c] through the freshly written columns;
 //   * if do_update and depth >= 2: chunk c-1's update of rows j of W_1 (and
 //     of their bf16 copy).
-// K is split over the workgroup's 8 waves for the backward and the forward
+// K is split over the workgroup's waves (8; 4 for small widths in launches
+// without workgroups of other roles) for the backward and the forward
 // products (partial tiles summed in LDS), so no wave walks a long chain of
 // dependent loads.
 // Depth 2 with workgroups to spare: W_1's update moves to nw1 workgroups

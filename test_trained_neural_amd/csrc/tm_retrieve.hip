@@ -160,7 +160,7 @@ hipError_t launch_rows(const GemmArgs& g, int ns, hipStream_t st) {
 // accumulator tiles of y.  The weights stream through LDS in 64-hidden
 // chunks, double buffered: chunk c+1's loads are in flight while chunk c
 // computes, and each fragment read from LDS serves TB matrix instructions.
-template <int D, int TB, int WAVES, int HC, bool PIPE>
+template <int D, int TB, int WAVES, int HC>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mlp2_kernel(Mlp2Args a) {
     constexpr int KS = D / 32, NB = D / 16, NT = WAVES * 64, SPC = HC / 32;
@@ -195,10 +195,9 @@ void mlp2_kernel(Mlp2Args a) {
         for (int ks = 0; ks < KS; ++ks) qf[tb][ks] = ld8(qp + 32 * ks);
     }
 
-    // chunk c of the weights: W_0's fragments of hidden blocks (HC/16)c ..
-    // (contiguous in the packed copy), then W_1's fragments of the chunk's
-    // K steps for every output block, each piece split in two halves that go
-    // to the lanes of the permuted K order
+    // chunk c of the weights: W_0's fragments of the chunk's hidden units
+    // (rows gathered in the order above), then W_1's fragments of the
+    // chunk's K steps for every output block, as stored
     bf16x8 stg[RND];
     auto fetch = [&](int c) {
 #pragma unroll
@@ -289,26 +288,18 @@ void mlp2_kernel(Mlp2Args a) {
         const char* cur = lds + (c & 1) * (CP * 16);
         if (c + 1 < nch) fetch(c + 1);
         const char* l1 = cur + W0P * 16;
-        if constexpr (PIPE) {
-            bf16x8 hf[2][TB];
+        // step st's layer-0 products go out before step st-1's layer-1
+        // products, so the SiLU between the layers of a step waits behind
+        // independent matrix work
+        bf16x8 hf[2][TB];
 #pragma unroll
-            for (int st = 0; st < SPC; ++st) {
-                f32x4 hacc[2][TB];
-                layer0(cur, st, hacc);
-                if (st > 0) layer1(l1, st - 1, hf[(st - 1) & 1]);
-                silu(hacc, hf[st & 1]);
-            }
-            layer1(l1, SPC - 1, hf[(SPC - 1) & 1]);
-        } else {
-#pragma unroll
-            for (int st = 0; st < SPC; ++st) {
-                f32x4 hacc[2][TB];
-                bf16x8 hf[TB];
-                layer0(cur, st, hacc);
-                silu(hacc, hf);
-                layer1(l1, st, hf);
-            }
+        for (int st = 0; st < SPC; ++st) {
+            f32x4 hacc[2][TB];
+            layer0(cur, st, hacc);
+            if (st > 0) layer1(l1, st - 1, hf[(st - 1) & 1]);
+            silu(hacc, hf[st & 1]);
         }
+        layer1(l1, SPC - 1, hf[(SPC - 1) & 1]);
         if (c + 1 < nch) put(lds + ((c + 1) & 1) * (CP * 16));
         __syncthreads();
     }
@@ -326,11 +317,11 @@ void mlp2_kernel(Mlp2Args a) {
 
 bool mlp2_fits(int d, int h) { return d >= 32 && d <= 128 && d % 32 == 0 && h >= 64 && h % 64 == 0; }
 
-template <int D, int TB, int WAVES, int HC, bool PIPE>
+template <int D, int TB, int WAVES, int HC>
 static void launch_mlp2_as(const Mlp2Args& a, int ns, hipStream_t st) {
     constexpr int CP = (HC / 16) * (D / 32) * 64 + (D / 16) * (HC / 32) * 64;
     const dim3 grid((a.nrows + WAVES * TB * 16 - 1) / (WAVES * TB * 16), ns);
-    launch_k((mlp2_kernel<D, TB, WAVES, HC, PIPE>), grid, dim3(WAVES * 64), 2 * CP * 16, st, a);
+    launch_k((mlp2_kernel<D, TB, WAVES, HC>), grid, dim3(WAVES * 64), 2 * CP * 16, st, a);
 }
 
 // 4 waves of 2 token blocks (128 rows) per workgroup, 64-hidden chunks,
@@ -341,7 +332,7 @@ static void launch_mlp2_as(const Mlp2Args& a, int ns, hipStream_t st) {
 // wave a SIMD) 1171 us.
 template <int D>
 static void launch_mlp2_d(const Mlp2Args& a, int ns, hipStream_t st) {
-    launch_mlp2_as<D, 2, 4, 64, true>(a, ns, st);
+    launch_mlp2_as<D, 2, 4, 64>(a, ns, st);
 }
 
 hipError_t launch_mlp2(const Mlp2Args& a, int ns, hipStream_t st) {
