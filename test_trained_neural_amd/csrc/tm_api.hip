@@ -47,6 +47,14 @@ struct tm_ctx {
     std::mutex* gmu;
     std::vector<GraphEntry>* graphs;
     std::vector<std::pair<int, hipStream_t>>* capture_streams;
+    // the backward's second stream per device, with its fork and join
+    // events (independent products of a chunk run on both)
+    struct Side {
+        int dev;
+        hipStream_t s;
+        hipEvent_t fork, join;
+    };
+    std::vector<Side>* sides;
     unsigned long long stamp;
     int dim, depth, expansion, chunk, hidden, L;
     int din[MAXL], dout[MAXL];
@@ -953,7 +961,7 @@ tm_status run_store(const tm_ctx* c, void* state_v, const void* k, const void* v
 // record from the recompute, the reverse sweep's per-stream scratch, and
 // the partial sums behind the gates' gradients.  Sizes in 4-byte elements.
 struct BwdLayout {
-    size_t tape, cc, dc, cs, key, scr, pgp, pad, acc, total;
+    size_t tape, cc, dc, cs, key, scr, pgp, pad, acc, acc2, total;
     long tape_cs;               // elements per chunk slot (ns * 2P)
     long rec;                   // elements of one (stream, chunk) key record
     long hk[MAXL], zk[MAXL], dk[MAXL], gk[MAXL];   // offsets inside a record
@@ -1018,6 +1026,7 @@ BwdLayout bwd_layout(const tm_ctx* c, long ns, long T) {
         }
     }
     w.acc = o; o += al256((size_t)acc * 4);
+    w.acc2 = o; o += al256((size_t)acc * 4);   // the second stream's
     w.total = o > 0 ? o : 256;
     return w;
 }
@@ -1066,10 +1075,48 @@ tm_status run_bwd(const tm_ctx* c, const void* state, const void* k, const void*
                 C, b, ns, 3 * L - 1, 9 * L, w.total * 1);
 
     float* accbuf = reinterpret_cast<float*>(ws + w.acc);
-    auto gemm = [&](BGemm g, int kind) -> bool {
+    float* accbuf2 = reinterpret_cast<float*>(ws + w.acc2);
+    // the second stream (default priority) and its fork / join events; under
+    // graph capture the fork joins it to the capture and the products on
+    // it become parallel branches of the graph
+    tm_ctx::Side side{-1, nullptr, nullptr, nullptr};
+    {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return TM_ERR_HIP;
+        tm_ctx* cm = const_cast<tm_ctx*>(c);
+        // (a lock of its own: the graph cache's lock is held while a call is
+        // captured)
+        static std::mutex side_mu;
+        std::lock_guard<std::mutex> lk(side_mu);
+        for (auto& sd : *cm->sides)
+            if (sd.dev == dev) side = sd;
+        if (side.dev < 0) {
+            tm_ctx::Side sd{dev, nullptr, nullptr, nullptr};
+            if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) return TM_ERR_HIP;
+            if (hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
+                hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
+                if (sd.fork) (void)hipEventDestroy(sd.fork);
+                (void)hipStreamDestroy(sd.s);
+                return TM_ERR_HIP;
+            }
+            cm->sides->push_back(sd);
+            side = sd;
+        }
+    }
+    hipStream_t s2 = side.s;
+    auto fork = [&]() -> bool {
+        return hipEventRecord(side.fork, st) == hipSuccess && hipStreamWaitEvent(s2, side.fork, 0) == hipSuccess;
+    };
+    auto join = [&]() -> bool {
+        return hipEventRecord(side.join, s2) == hipSuccess && hipStreamWaitEvent(st, side.join, 0) == hipSuccess;
+    };
+    // a product on the main stream, or (second) on the second stream with
+    // its own split-K partial tiles
+    auto gemm = [&](BGemm g, int kind, bool second = false) -> bool {
         g.splitk = bgemm_splitk(g.m, g.n, g.k, g.k2, g.epi, (int)ns);
-        g.acc = accbuf;
-        return timed(kind, st, [&] { return launch_bgemm(g, (int)ns, st); }) == hipSuccess;
+        g.acc = second ? accbuf2 : accbuf;
+        hipStream_t gs = second ? s2 : st;
+        return timed(kind, gs, [&] { return launch_bgemm(g, (int)ns, gs); }) == hipSuccess;
     };
     auto base = [&](int m, int n, int kk, int ta, int tb, int epi) {
         BGemm g;
@@ -1144,7 +1191,9 @@ tm_status run_bwd(const tm_ctx* c, const void* state, const void* k, const void*
             if (!gemm(g, K_BREST)) return TM_ERR_HIP;
         }
         // the write: M_end = p_alpha M_0 + s0 S_0 - H^T diag(c) Delta,
-        // S_end = p_eta S_0 - H^T diag(d) Delta, into the next slot
+        // S_end = p_eta S_0 - H^T diag(d) Delta, into the next slot (the
+        // layers' writes are independent: odd layers on the second stream)
+        if (L > 1 && !fork()) return TM_ERR_HIP;
         for (int l = 0; l < L; ++l) {
             BGemm g = base(c->din[l], c->dout[l], b, 1, 0, BE_UPD);
             g.dual = 2;
@@ -1159,8 +1208,9 @@ tm_status run_bwd(const tm_ctx* c, const void* state, const void* k, const void*
             g.c1 = slot(ci + 1, l, 1);
             g.cs = cs + (size_t)ci * 4;
             g.cs_ss = (long)C * 4;
-            if (!gemm(g, K_BSTATE)) return TM_ERR_HIP;
+            if (!gemm(g, K_BSTATE, (l & 1) != 0)) return TM_ERR_HIP;
         }
+        if (L > 1 && !join()) return TM_ERR_HIP;
     }
 
     // ---- reverse sweep ----
@@ -1188,21 +1238,26 @@ tm_status run_bwd(const tm_ctx* c, const void* state, const void* k, const void*
             }
             if (!gemm(g, K_BREST)) return false;
         }
+        // (each layer's gradient goes to its own Mbar: odd layers on the
+        // second stream)
+        if (L > 1 && !fork()) return false;
         for (int l = 0; l < L; ++l) {
             BGemm g = base(c->din[l], c->dout[l], b, 1, 0, BE_ACC);
             g.A = l == 0 ? tokm(q, ci * b, bf) : sc(w.hq[l], c->din[l]);
             g.B = dqm(l);
             g.c0 = adj(l, 0);
-            if (!gemm(g, K_BREST)) return false;
+            if (!gemm(g, K_BREST, (l & 1) != 0)) return false;
         }
-        return true;
+        return L == 1 || join();
     };
 
     for (int ci = C - 1; ci >= 0; --ci) {
         if (read == TM_READ_AFTER_WRITE && !query_steps(ci, ci + 1)) return TM_ERR_HIP;
         // the surprise's adjoint Gbar_i = -(c_i Mbar + d_i Sbar), through
         // G_l = h_l^T Delta_l: Deltabar_l = -(c h_l Mbar_l + d h_l Sbar_l) (with
-        // the row sums behind cbar, dbar), hbar_l = -(c Delta_l Mbar_l^T + d Delta_l Sbar_l^T)
+        // the row sums behind cbar, dbar), hbar_l = -(c Delta_l Mbar_l^T + d Delta_l Sbar_l^T);
+        // the hbar products (independent of the Deltabar ones) on the second stream
+        if (!fork()) return TM_ERR_HIP;
         for (int l = 0; l < L; ++l) {
             BGemm g = base(b, c->dout[l], c->din[l], 0, 0, BE_GP);
             g.dual = 1;
@@ -1227,8 +1282,9 @@ tm_status run_bwd(const tm_ctx* c, const void* state, const void* k, const void*
             h.rs1 = dc + (size_t)ci * b;
             h.sk_ss = T;
             h.c0 = sc(w.hb[l], c->din[l]);
-            if (!gemm(h, K_BREST)) return TM_ERR_HIP;
+            if (!gemm(h, K_BREST, true)) return TM_ERR_HIP;
         }
+        if (!join()) return TM_ERR_HIP;
         // back through the key rows' backward (layers 1 .. L-1 in order)
         for (int l = 1; l < L; ++l) {
             BElem e;
@@ -1281,7 +1337,9 @@ tm_status run_bwd(const tm_ctx* c, const void* state, const void* k, const void*
             if (!gemm(g, K_BREST)) return TM_ERR_HIP;
         }
         // Mbar_0 = p_alpha Mbar + h^T zbar + u^T Delta, Sbar_0 = p_eta Sbar + s0 Mbar,
-        // with the sums behind the chunk scalars' adjoints
+        // with the sums behind the chunk scalars' adjoints (layers
+        // independent: odd layers on the second stream)
+        if (L > 1 && !fork()) return TM_ERR_HIP;
         for (int l = 0; l < L; ++l) {
             BGemm g = base(c->din[l], c->dout[l], b, 1, 0, BE_ADJ);
             g.A = hkey(ci, l);
@@ -1300,8 +1358,9 @@ tm_status run_bwd(const tm_ctx* c, const void* state, const void* k, const void*
             g.part = pad + (size_t)ci * w.nad * 3;
             g.part_ss = (long)C * w.nad * 3;
             g.tile0 = w.adbase[l];
-            if (!gemm(g, K_BSTATE)) return TM_ERR_HIP;
+            if (!gemm(g, K_BSTATE, (l & 1) != 0)) return TM_ERR_HIP;
         }
+        if (L > 1 && !join()) return TM_ERR_HIP;
         if (read == TM_READ_BEFORE_WRITE && !query_steps(ci, ci)) return TM_ERR_HIP;
     }
     // the gates' gradients, every chunk
@@ -1334,10 +1393,12 @@ tm_status tm_create(int dim, int depth, int expansion, int chunk, tm_ctx** out) 
     c->gmu = new (std::nothrow) std::mutex;
     c->graphs = new (std::nothrow) std::vector<GraphEntry>;
     c->capture_streams = new (std::nothrow) std::vector<std::pair<int, hipStream_t>>;
-    if (!c->gmu || !c->graphs || !c->capture_streams) {
+    c->sides = new (std::nothrow) std::vector<tm_ctx::Side>;
+    if (!c->gmu || !c->graphs || !c->capture_streams || !c->sides) {
         delete c->gmu;
         delete c->graphs;
         delete c->capture_streams;
+        delete c->sides;
         delete c;
         return TM_ERR_INVALID;
     }
@@ -1372,8 +1433,14 @@ void tm_destroy(tm_ctx* ctx) {
     for (GraphEntry& e : *ctx->graphs)
         if (e.exec) (void)hipGraphExecDestroy(e.exec);
     for (auto& pr : *ctx->capture_streams) (void)hipStreamDestroy(pr.second);
+    for (auto& sd : *ctx->sides) {
+        (void)hipEventDestroy(sd.fork);
+        (void)hipEventDestroy(sd.join);
+        (void)hipStreamDestroy(sd.s);
+    }
     delete ctx->graphs;
     delete ctx->capture_streams;
+    delete ctx->sides;
     delete ctx->gmu;
     delete ctx;
 }
