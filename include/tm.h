@@ -43,7 +43,8 @@
  *     captures and replays; TM_XCD_STREAMS=0 and TM_FIRST4=0 turn off,
  *     for comparison, the grouping of a stream's workgroups on one XCD and
  *     the 4-wave first-layer workgroups of small widths (results agree to
- *     rounding).
+ *     rounding); TM_STORE_GROUPS=1, 2, 4 or 8 sets the number of batch
+ *     groups (tm_store_groups_enable) where the batch divides by it.
  *   - A state blob may be used by one stream at a time; a ctx is immutable
  *     and may be shared between threads.
  */
@@ -99,7 +100,8 @@ tm_status tm_config(const tm_ctx* ctx, int* dim, int* depth, int* expansion, int
 size_t tm_state_bytes(const tm_ctx* ctx, int batch, int heads);
 
 /* Scratch bytes tm_store / tm_retrieve / tm_forward need for a call of
- * n_tokens tokens per stream.  The workspace holds no data between calls. */
+ * n_tokens tokens per stream (enough for the call's batch groups, see
+ * tm_store_groups_enable).  The workspace holds no data between calls. */
 size_t tm_workspace_bytes(const tm_ctx* ctx, int batch, int heads, int n_tokens);
 
 /* M = init_weights (device fp32 [heads][P], canonical layer order, broadcast
@@ -317,6 +319,19 @@ tm_status tm_graphs_enable(int on);
  * Process-wide; calls captured into graphs before a change keep the setting
  * they were captured with. */
 tm_status tm_w1_split_enable(int on);
+
+/* Batch groups of the chunk loop (tm_store, tm_forward, tm_forward_ex); the
+ * results are bitwise identical either way.  With on = 1 (the default), a
+ * call of at least 16 streams with an even batch runs its two batch halves
+ * as two independent chunk chains, one on the caller's stream and one on a
+ * second stream of the ctx (per device and host thread, default priority,
+ * forked from and joined back to the caller's stream, so the call stays
+ * ordered on `stream`), and each half uses its own half of the workspace:
+ * one chain's launches fill the compute units the other's leave idle.
+ * on = 0 runs one chain.  tm_forward_noalloc always runs one chain.
+ * Process-wide; calls captured into graphs before a change keep the setting
+ * they were captured with. */
+tm_status tm_store_groups_enable(int on);
 
 /* Instrumentation for measuring kernels in place (not part of the method).
  * Kernel classes: 0 coefficient scan (and key transpose), 1 chunk forward

@@ -25,8 +25,9 @@ TM_READ_AFTER_WRITE, TM_READ_BEFORE_WRITE, TM_READ_PER_TOKEN = 0, 1, 2
 EXPORTED = ("tm_create", "tm_destroy", "tm_param_count", "tm_state_bytes", "tm_workspace_bytes",
             "tm_state_init", "tm_store", "tm_retrieve", "tm_forward", "tm_state_export",
             "tm_state_import", "tm_state_check", "tm_status_str", "tm_timing_enable", "tm_timing_read",
-            "tm_graphs_enable", "tm_w1_split_enable", "tm_forward_ex", "tm_project", "tm_mac_window",
-            "tm_mac_gate", "tm_config", "tm_forward_noalloc", "tm_backward", "tm_backward_workspace_bytes")
+            "tm_graphs_enable", "tm_w1_split_enable", "tm_store_groups_enable", "tm_forward_ex", "tm_project",
+            "tm_mac_window", "tm_mac_gate", "tm_config", "tm_forward_noalloc", "tm_backward",
+            "tm_backward_workspace_bytes")
 
 # kernel classes of tm_timing_enable / tm_timing_read (3 is unused); 8 and 9
 # are tm_backward's state-streaming launches and its other launches
@@ -103,6 +104,8 @@ def lib():
         L.tm_graphs_enable.argtypes = [_i]
         L.tm_w1_split_enable.restype = _i
         L.tm_w1_split_enable.argtypes = [_i]
+        L.tm_store_groups_enable.restype = _i
+        L.tm_store_groups_enable.argtypes = [_i]
         L.tm_status_str.restype = ctypes.c_char_p
         L.tm_status_str.argtypes = [_i]
         _lib = L
@@ -438,6 +441,10 @@ def tm_graphs_enable(on):
 
 def tm_w1_split_enable(on):
     _check("tm_w1_split_enable", lib().tm_w1_split_enable(1 if on else 0))
+
+
+def tm_store_groups_enable(on):
+    _check("tm_store_groups_enable", lib().tm_store_groups_enable(1 if on else 0))
 
 
 def tm_timing_enable(class_mask):

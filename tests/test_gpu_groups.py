@@ -1,0 +1,78 @@
+"""A store whose batches run as G chunk chains on G streams at once
+(TM_STORE_GROUPS=2 or 4) gives bitwise the results of one chain
+(TM_STORE_GROUPS=1): the chains own disjoint streams of the state and
+disjoint slices of the workspace, and each runs the launches of one chain
+over its own streams.  Checked over a run of calls that goes through the
+first (direct), second (captured) and later (replayed) call of a shape, in
+each read order and for a store, with the position counted once per call:
+8 streams (4 x 2 heads) of 128 -> 512 -> 128, chunk 64, 256 tokens, bf16,
+and 2 streams of the dim-384 MLP over an odd number of chunks."""
+import os
+import subprocess
+import sys
+import tempfile
+
+import numpy as np
+import pytest
+
+from harness import say
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+RUN = r"""
+import sys
+sys.path.insert(0, %(root)r); sys.path.insert(0, %(tests)r)
+import numpy as np, torch
+import test_trained_neural_amd as T
+from harness import GpuMemory, dev_inputs
+from test_trained_neural_amd import inputs as I
+wl = I.Workload("groups", batch=%(batch)d, seq=%(seq)d, heads=%(heads)d, dim=%(dim)d, depth=2, expansion=4, chunk=64,
+                dtype="bf16", offsets=(-7.0, 2.0, -7.0))
+p = I.make_params(wl)
+ci = I.make_call(wl, p)
+g = GpuMemory(wl, p)
+d = dev_inputs(ci, "bf16")
+out = {}
+for i in range(3):
+    out["y%%d" %% i] = g.forward(d).cpu().numpy()
+for i in range(2):
+    out["b%%d" %% i] = g.forward(d, read=T.TM_READ_BEFORE_WRITE).cpu().numpy()
+    out["t%%d" %% i] = g.forward(d, read=T.TM_READ_PER_TOKEN).cpu().numpy()
+    g.store(d)
+torch.cuda.synchronize()
+nf, pos = T.tm_state_check(g.ctx, g.state, g.B, g.H)
+out["pos"] = np.array([pos, int(nf)])
+out["st"] = g.export()
+np.savez(%(out)r, **out)
+"""
+
+CASES = [dict(batch=4, seq=256, heads=2, dim=128), dict(batch=2, seq=192, heads=1, dim=384)]
+
+
+def run_groups(env, case):
+    with tempfile.TemporaryDirectory() as td:
+        out = os.path.join(td, "out.npz")
+        code = RUN % dict(case, root=ROOT, tests=os.path.join(ROOT, "tests"), out=out)
+        res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                             env=dict(os.environ, **env))
+        assert res.returncode == 0, res.stderr[-2000:]
+        z = np.load(out)
+        return {k: z[k] for k in z.files}
+
+
+@pytest.mark.parametrize("case", CASES, ids=["dim128_heads2", "dim384"])
+def test_chains_match_one(case):
+    say("case", case)
+    one = run_groups({"TM_STORE_GROUPS": "1"}, case)
+    seq = case["seq"]
+    assert one["pos"][0] == 9 * seq and one["pos"][1] == 0
+    for G in (2, 4):
+        if case["batch"] % G:
+            continue
+        got = run_groups({"TM_STORE_GROUPS": str(G)}, case)
+        assert sorted(one) == sorted(got)
+        for k in sorted(one):
+            assert np.array_equal(one[k], got[k]), (G, k)
+        say("  %d chains: %d outputs and the state bitwise equal; position %d" % (G, len(one) - 2, got["pos"][0]))
