@@ -329,8 +329,8 @@ tm_status tm_w1_split_enable(int on);
  * ordered on `stream`), and each half uses its own half of the workspace:
  * one chain's launches fill the compute units the other's leave idle.
  * on = 0 runs one chain.  tm_forward_noalloc always runs one chain.
- * Process-wide; calls captured into graphs before a change keep the setting
- * they were captured with. */
+ * Process-wide; the setting is part of a call shape's graph key, so a change
+ * captures a graph of its own. */
 tm_status tm_store_groups_enable(int on);
 
 /* Instrumentation for measuring kernels in place (not part of the method).

@@ -8,6 +8,7 @@
 // [d_out][d_in].  Export and import convert to and from the canonical
 // row-major form.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <new>
 #include <stdio.h>
@@ -236,12 +237,12 @@ tm_status state_lookup(const tm_ctx* c, const void* st, int batch, int heads) {
 
 // TM_LOG=1 prints each call's configuration and launch plan to stderr once
 // per distinct call shape; TM_LOG=2 also prints graph captures and replays.
+// (each switch is read once, by a thread-safe static initialisation)
 int log_level() {
-    static int lvl = -1;
-    if (lvl < 0) {
+    static const int lvl = [] {
         const char* e = getenv("TM_LOG");
-        lvl = e ? atoi(e) : 0;
-    }
+        return e ? atoi(e) : 0;
+    }();
     return lvl;
 }
 
@@ -372,17 +373,18 @@ void log_call(const tm_ctx* c, const GraphEntry& k) {
 }
 
 // ---- graph replay of repeated calls ----
-bool g_graphs = true;
-bool g_w1_split = true;   // tm_w1_split_enable
+// process-wide switches, set by the *_enable calls from any thread
+std::atomic<bool> g_graphs{true};
+std::atomic<bool> g_w1_split{true};       // tm_w1_split_enable
+std::atomic<bool> g_store_groups{true};   // tm_store_groups_enable
 // TM_XCD_STREAMS=0 turns the first-layer blocks' grouping by XCD off (for
 // comparing the two mappings; the results are bitwise the same)
 bool xcd_streams_on() {
-    static int on = -1;
-    if (on < 0) {
+    static const bool on = [] {
         const char* e = getenv("TM_XCD_STREAMS");
-        on = e && e[0] == '0' ? 0 : 1;
-    }
-    return on == 1;
+        return !(e && e[0] == '0');
+    }();
+    return on;
 }
 constexpr size_t MAX_GRAPHS = 16;
 
@@ -467,7 +469,7 @@ GraphEntry make_key(int kind, int batch, int heads, int n_tokens, int dtype,
     k.heads = heads;
     k.n_tokens = n_tokens;
     k.dtype = dtype;
-    k.opt = g_w1_split ? 1 : 0;
+    k.opt = (g_w1_split ? 1 : 0) | (g_store_groups ? 2 : 0);   // the switches that change the launches
     int i = 0;
     for (const void* p : ptrs) k.p[i++] = p;
     return k;
@@ -1016,13 +1018,11 @@ tm_status run_chain(const tm_ctx* c, void* state_v, const void* k, const void* v
 // dim-128 memory: +9% tokens/s with two chains, -5% with four.
 // TM_STORE_GROUPS=1, 2, 4 or 8 overrides the choice (for comparison).
 constexpr int MAX_GROUPS = 8;
-bool g_store_groups = true;   // tm_store_groups_enable
 int store_groups(int batch, int heads) {
-    static int env = -2;
-    if (env == -2) {
+    static const int env = [] {
         const char* e = getenv("TM_STORE_GROUPS");
-        env = e && (e[0] == '1' || e[0] == '2' || e[0] == '4' || e[0] == '8') && e[1] == 0 ? e[0] - '0' : -1;
-    }
+        return e && (e[0] == '1' || e[0] == '2' || e[0] == '4' || e[0] == '8') && e[1] == 0 ? e[0] - '0' : -1;
+    }();
     if (!g_store_groups) return 1;
     const int G = env > 0 ? env : ((long)batch * heads >= 16 ? 2 : 1);
     return batch % G == 0 ? G : 1;
