@@ -1053,10 +1053,25 @@ tm_status run_store(const tm_ctx* c, void* state, const void* k, const void* v, 
     tm_ctx::Side side[MAX_GROUPS - 1];
     for (int g = 1; g < G; ++g)
         if (side_stream(c, &side[g - 1], g - 1) != TM_OK) return TM_ERR_HIP;
-    for (int g = 1; g < G; ++g)
-        if (hipEventRecord(side[g - 1].fork, st) != hipSuccess ||
-            hipStreamWaitEvent(side[g - 1].s, side[g - 1].fork, 0) != hipSuccess)
-            return TM_ERR_HIP;
+    // the extra streams forked so far are joined back on every path (a
+    // capture must end with every stream it reached joined)
+    int forked = 1;
+    auto join = [&]() {
+        bool ok = true;
+        for (int g = 1; g < forked; ++g)
+            ok = hipEventRecord(side[g - 1].join, side[g - 1].s) == hipSuccess &&
+                 hipStreamWaitEvent(st, side[g - 1].join, 0) == hipSuccess && ok;
+        return ok;
+    };
+    for (int g = 1; g < G; ++g) {
+        if (hipEventRecord(side[g - 1].fork, st) != hipSuccess) break;
+        if (hipStreamWaitEvent(side[g - 1].s, side[g - 1].fork, 0) != hipSuccess) break;
+        forked = g + 1;
+    }
+    if (forked < G) {
+        (void)join();
+        return TM_ERR_HIP;
+    }
     const int bg = batch / G;
     const size_t esz = dtype == TM_F32 ? 4 : 2;
     const size_t tok = (size_t)n_tokens * heads * c->dim, gate = (size_t)n_tokens * heads;
@@ -1074,11 +1089,7 @@ tm_status run_store(const tm_ctx* c, void* state, const void* k, const void* v, 
                        y ? y + b0 * tok : nullptr, bg, heads, n_tokens, dtype, static_cast<char*>(ws_v) + g * wsg,
                        g == 0 ? st : side[g - 1].s, read, g == 0);
     }
-    // (joined on every path: a capture must end with the extra streams joined)
-    bool joined = true;
-    for (int g = 1; g < G; ++g)
-        joined = hipEventRecord(side[g - 1].join, side[g - 1].s) == hipSuccess &&
-                 hipStreamWaitEvent(st, side[g - 1].join, 0) == hipSuccess && joined;
+    const bool joined = join();
     if (rc != TM_OK) return rc;
     return joined ? TM_OK : TM_ERR_HIP;
 }
