@@ -6,9 +6,10 @@ over its own streams.  Checked over a run of calls that goes through the
 first (direct), second (captured) and later (replayed) call of a shape, in
 each read order and for a store, with the position counted once per call:
 8 streams (4 x 2 heads) of 128 -> 512 -> 128, chunk 64, 256 tokens, bf16;
-2 streams of the dim-384 MLP over an odd number of chunks; and 16 streams
+2 streams of the dim-384 MLP over an odd number of chunks; 16 streams
 (4 x 4 heads) of 64 -> 256 -> 64 in fp32 (token offsets of 4-byte inputs;
-16 streams also take two chains by default)."""
+16 streams also take two chains by default); and 16 streams of depth 3
+(bf16) and depth 4 (fp32, chunk 32)."""
 import os
 import subprocess
 import sys
@@ -30,8 +31,8 @@ import numpy as np, torch
 import test_trained_neural_amd as T
 from harness import GpuMemory, dev_inputs
 from test_trained_neural_amd import inputs as I
-wl = I.Workload("groups", batch=%(batch)d, seq=%(seq)d, heads=%(heads)d, dim=%(dim)d, depth=2, expansion=4, chunk=64,
-                dtype=%(dtype)r, offsets=%(offsets)r)
+wl = I.Workload("groups", batch=%(batch)d, seq=%(seq)d, heads=%(heads)d, dim=%(dim)d, depth=%(depth)d,
+                expansion=%(expansion)d, chunk=%(chunk)d, dtype=%(dtype)r, offsets=%(offsets)r)
 p = I.make_params(wl)
 ci = I.make_call(wl, p)
 g = GpuMemory(wl, p)
@@ -52,9 +53,16 @@ np.savez(%(out)r, **out)
 
 # (theta, eta, alpha offsets: the dim-64 memory diverges over these 9 calls
 # with eta's offset at 2 -- in the oracle too -- so it takes -3)
-CASES = [dict(batch=4, seq=256, heads=2, dim=128, dtype="bf16", offsets=(-7.0, 2.0, -7.0)),
-         dict(batch=2, seq=192, heads=1, dim=384, dtype="bf16", offsets=(-7.0, 2.0, -7.0)),
-         dict(batch=4, seq=128, heads=4, dim=64, dtype="f32", offsets=(-7.0, -3.0, -7.0))]
+D2 = dict(depth=2, expansion=4, chunk=64)
+CASES = [dict(D2, batch=4, seq=256, heads=2, dim=128, dtype="bf16", offsets=(-7.0, 2.0, -7.0)),
+         dict(D2, batch=2, seq=192, heads=1, dim=384, dtype="bf16", offsets=(-7.0, 2.0, -7.0)),
+         dict(D2, batch=4, seq=128, heads=4, dim=64, dtype="f32", offsets=(-7.0, -3.0, -7.0)),
+         # deeper memories: layers 2.. updated by the step launch's update
+         # tiles, and the backward launches down to layer 1, per chain
+         dict(batch=4, seq=128, heads=4, dim=64, depth=3, expansion=2, chunk=64, dtype="bf16",
+              offsets=(-7.0, -3.0, -7.0)),
+         dict(batch=2, seq=96, heads=8, dim=32, depth=4, expansion=2, chunk=32, dtype="f32",
+              offsets=(-7.0, -3.0, -7.0))]
 
 
 def run_groups(env, case):
@@ -68,7 +76,8 @@ def run_groups(env, case):
         return {k: z[k] for k in z.files}
 
 
-@pytest.mark.parametrize("case", CASES, ids=["dim128_heads2", "dim384", "f32_dim64_heads4"])
+@pytest.mark.parametrize("case", CASES, ids=["dim128_heads2", "dim384", "f32_dim64_heads4", "depth3_dim64",
+                                             "f32_depth4_dim32"])
 def test_chains_match_one(case):
     say("case", case)
     one = run_groups({"TM_STORE_GROUPS": "1"}, case)
