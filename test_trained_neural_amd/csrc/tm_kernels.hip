@@ -496,22 +496,39 @@ __device__ void scan_rows(const ScanArgs& a, int s, int c, int f0, char* lds) {
     T(*tile)[SCAN_TP] = reinterpret_cast<T(*)[SCAN_TP]>(lds);   // [token][feature of the slice]
     const int d = a.ktl.d, b = a.b, nks = d >> 5, nkb = a.bp >> 5;
     const int nf = min(SCAN_SLICE, d - f0), nbt = (b + 15) >> 4;
-    const int items = nbt * (nf >> 5) * 64;   // 16 B pieces per tensor (fragment order)
+    const int items = nbt * (nf >> 5) * 64;   // 8-feature pieces per tensor (fragment order)
+    // every piece of the thread (at most PER: a chunk of 64 tokens, a slice
+    // of 128 features) is requested before any is stored: loads and stores
+    // interleaved in a loop would wait a memory round trip per piece, the
+    // compiler unable to move a load above a store that might alias it.
+    // Keys first, then queries.
+    constexpr int PER = (MAX_CHUNK / 16) * (SCAN_SLICE / 32) * 64 / 256;
+    int po[PER], pt[PER], pf[PER];
+    long ps[PER];
+    bool live[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int idx = threadIdx.x + 256 * u;
+        const int ln = idx & 63, f = idx >> 6, ksl = f % (nf >> 5), tb = f / (nf >> 5);
+        const int t = tb * 16 + (ln & 15), fl = ksl * 32 + 8 * (ln >> 4);
+        live[u] = idx < items && t < b;
+        // pieces past the chunk or the slice read a valid row and are zeroed
+        ps[u] = tok_off(a.ktl, s, c * b + min(t, b - 1)) + f0 + (idx < items ? fl : 0);
+        po[u] = idx < items ? pkf(tb, (f0 >> 5) + ksl, nks, ln) : -1;
+        pt[u] = t;
+        pf[u] = fl;
+    }
     for (int kq = 0; kq < (a.q ? 2 : 1); ++kq) {
         const T* src = reinterpret_cast<const T*>(kq ? a.q : a.k);
         T* dst = reinterpret_cast<T*>(kq ? a.xq : a.xk) + ((long)s * a.C + c) * a.xc;
-        for (int idx = threadIdx.x; idx < items; idx += 256) {
-            const int ln = idx & 63, f = idx >> 6, ksl = f % (nf >> 5), tb = f / (nf >> 5);
-            const int t = tb * 16 + (ln & 15), fl = ksl * 32 + 8 * (ln >> 4);
-            V v;
-            if (t < b) {
-                v = ld8(src + tok_off(a.ktl, s, c * b + t) + f0 + fl);
-            } else {
+        V v[PER];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = (T)0.0f;
-            }
-            *reinterpret_cast<V*>(dst + pkf(tb, (f0 >> 5) + ksl, nks, ln)) = v;
-            if (kq == 0 && t < MAX_CHUNK) *reinterpret_cast<V*>(&tile[t][fl]) = v;
+        for (int u = 0; u < PER; ++u) v[u] = keep_if(ld8(src + ps[u]), live[u]);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            if (po[u] < 0) continue;
+            *reinterpret_cast<V*>(dst + po[u]) = v[u];
+            if (kq == 0 && pt[u] < MAX_CHUNK) *reinterpret_cast<V*>(&tile[pt[u]][pf[u]]) = v[u];
         }
     }
     // rows of the tile past the packed ones (tokens up to bp) are zero
